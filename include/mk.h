@@ -1,0 +1,222 @@
+/* mk.h -- C ABI of the persistent-megakernel decode library (libmk.so), MI355X / gfx950.
+ *
+ * One transformer decode step of a Llama-family model (RMSNorm, QKV projection,
+ * RoPE, KV-cache write, split-KV decode attention, output projection, SwiGLU
+ * FFN, final RMSNorm, LM head, argmax) runs as ONE resident grid: one
+ * workgroup per compute unit executes a static queue of tile instructions that
+ * the host planned once, and tile-level event counters in device memory replace
+ * kernel boundaries.  The design follows the pages this library was written
+ * from: the MegaRTP article (tahou.com), sections 3-4 (host-generated
+ * instruction queues [num_CUs, max_len, 32] int32 with NoOp padding, event
+ * counters with thresholds, an operand pointer table [num_ops, 16] u64, worker
+ * roles, recycled shared-memory pages); the CMU 15-779 lecture 7 notes
+ * (semidirectx.com), sections 4-6 (worker loop: prefetch weights before waiting
+ * on counters; per-layer task partition; MPK task graph); the MPK internals
+ * notes (dpshk.com) for gcd/lcm event partitioning and linearization.
+ *
+ * Conventions shared by every call:
+ *  - No exception crosses the ABI.  Every call returns an mk_status; on failure
+ *    mk_last_error() gives a thread-local message for the last failing call.
+ *  - "host" pointers are CPU memory read during the call only; "device"
+ *    pointers are HIP device memory that must stay valid until the stream work
+ *    that uses them has completed.  The caller owns weights, KV cache, token
+ *    ids and streams; a plan owns its queues, counters, workspace and outputs.
+ *  - One in-flight run per plan (counters and workspace belong to the plan);
+ *    distinct plans are independent.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+
+typedef enum {
+  MK_OK = 0,
+  MK_E_INVALID = -1,     /* bad pointer, size or state of an argument */
+  MK_E_UNSUPPORTED = -2, /* a shape or option outside what the library supports */
+  MK_E_NOMEM = -3,       /* host or device allocation failed */
+  MK_E_HIP = -4,         /* a HIP runtime call failed (message has hipGetErrorString) */
+  MK_E_TIMEOUT = -5,     /* a device-side wait exceeded its bound (watchdog record filled) */
+  MK_E_STATE = -6        /* the call does not apply to this plan (e.g. running a graph-only plan) */
+} mk_status;
+
+typedef struct mk_plan mk_plan; /* opaque */
+
+/* Thread-local text for the last failing call on this thread ("" if none). */
+const char* mk_last_error(void);
+int mk_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Model description.  Plain data, copied by mk_plan_build.
+ * arch: MK_ARCH_LLAMA (RMSNorm, GQA attention, SwiGLU) or MK_ARCH_QWEN3 (adds a
+ * per-head RMSNorm of q and k before RoPE, weights q_norm/k_norm, same eps).
+ * weight_dtype: MK_BF16 (row-major [out, in], PyTorch Linear layout).
+ * max_kv_len: rows per sequence in the KV cache (capacity); kv_len[b] + 1 <= it.
+ * RoPE is rotate-half with angle pos * rope_theta^(-2i/head_dim).
+ * ------------------------------------------------------------------------- */
+enum { MK_ARCH_LLAMA = 1, MK_ARCH_QWEN3 = 2 };
+enum { MK_BF16 = 0 };
+
+typedef struct {
+  uint32_t abi_version; /* MK_ABI_VERSION */
+  uint32_t struct_size; /* sizeof(mk_model_desc) */
+  int32_t arch;
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t tied_lm_head; /* 1: the LM head is the embedding matrix */
+  int32_t qk_norm;      /* 1 for MK_ARCH_QWEN3 */
+  int32_t weight_dtype; /* MK_BF16 */
+  int32_t max_kv_len;   /* KV-cache capacity per sequence (rows) */
+  float rms_eps, rope_theta;
+} mk_model_desc;
+
+/* Planning options; pass NULL (or 0 in a field) for the defaults.
+ * num_cus: workgroups of the persistent grid = queues (default: the device's CU
+ *   count; the plan can be built without a GPU when it is given).
+ * gemv_rows: weight rows per QKV / O / LM-head tile (default 32768 / hidden,
+ *   clamped to [4, 16]); gateup_outs: FFN outputs per gate/up tile (default
+ *   gemv_rows / 2); down_rows: rows per down tile (default 32768 / ffn,
+ *   clamped to [1, 16]); lm_rows: LM-head rows per tile (default gemv_rows);
+ * attn_splits: KV splits per (sequence, kv head) (default from the longest
+ *   sequence: ceil((kv+1)/64) clamped to [1, 32], raised until one split's
+ *   K and V rows fit in 64 KiB);
+ * timeout_ms: bound of every device-side wait (default 200). */
+typedef struct {
+  int32_t num_cus, gemv_rows, gateup_outs, down_rows, lm_rows, attn_splits;
+  int32_t timeout_ms;
+  int32_t reserved[5];
+} mk_plan_opts;
+
+/* Build the static tile plan of one decode step (host-only arithmetic; uploads
+ * nothing until the first run).  kv_len: host int32[batch], prior rows per
+ * sequence; the step writes row kv_len[b] and attends rows 0..kv_len[b].  The
+ * planner cuts every operator into tiles, derives events by gcd partition of
+ * each producer/consumer edge (lcm-normalized at forks and joins), drops
+ * residual edges implied transitively, linearizes tasks so each event's
+ * successors are contiguous, and places task t in queue t % num_cus at slot
+ * t / num_cus.  Deterministic: equal inputs give bit-identical plans.
+ * Errors: MK_E_INVALID (null/size/abi mismatch), MK_E_UNSUPPORTED (head_dim not
+ * 64 or 128, hidden or ffn not a multiple of 8 or above 12288, more than 4 query
+ * heads per kv head, kv_len[b] + 1 > max_kv_len, batch other than 1, tiles that
+ * do not fit the 144 KiB LDS page ring). */
+mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* kv_len,
+                        const mk_plan_opts* opts, mk_plan** out);
+
+/* Plan an arbitrary operator graph with the same rules (no payloads; the result
+ * can be exported but not run: mk_run returns MK_E_STATE).  ops[i].grid holds
+ * up to three axis extents; edges must go from a lower to a higher op index;
+ * out_map / in_map give, per grid axis, the tensor dimension (0..3) it
+ * partitions or -1; when has_extent is set, extent/ptile/ctile (elements) let
+ * the planner reject gcd slices that do not cut the tensor at the same places
+ * on both sides (ragged tiles). */
+typedef struct {
+  int32_t opcode, spec, layer;
+  int32_t grid[3];
+} mk_graph_op;
+typedef struct {
+  int32_t prod, cons;
+  int32_t out_map[3], in_map[3];
+  int32_t has_extent;
+  int32_t extent[4], ptile[4], ctile[4];
+} mk_graph_edge;
+mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_edge* edges, int32_t n_edges,
+                        int32_t num_cus, mk_plan** out);
+
+/* Host views of the plan's schedule metadata, valid until mk_plan_free.
+ * queue: int32 [num_cus][max_len][32] (word layout: 0 opcode, 1 spec_id,
+ *   2 operand row, 3 wait count, 4 wait event, 5 wait target per run, 6 signal
+ *   count, 7 signal event, 8 signal increment, 9 task id, 10 layer, 11-13 grid
+ *   coordinates, 14-23 op payload, 24-31 zero; NoOp rows are all zero).
+ * event_target/first/last: per event, triggers per run and the [first, last)
+ *   task-id range of its successors.  task_trigger/task_wait: per task, the
+ *   event it triggers / waits on, or -1.  op_table: int32 [num_ops][8] rows
+ *   (opcode, spec, layer, grid x, y, z, tasks, 0).  edge_kept: per input edge, 0
+ *   when dropped as residual. */
+typedef struct {
+  int32_t num_cus, max_len, num_tasks, num_events, num_ops, num_edges;
+  const int32_t* queue;
+  const uint32_t* event_target;
+  const int32_t* event_first;
+  const int32_t* event_last;
+  const int32_t* task_trigger;
+  const int32_t* task_wait;
+  const int32_t* op_table;
+  const uint8_t* edge_kept;
+} mk_plan_view;
+mk_status mk_plan_export(const mk_plan* plan, mk_plan_view* out);
+
+/* Weights: device pointers.  layer_ptrs is a HOST array of n_layers * 11 device
+ * pointers in slot order (attn_norm, wq, wk, wv, q_norm, k_norm, wo, ffn_norm,
+ * w_gate, w_up, w_down); q_norm/k_norm may be NULL without qk_norm.  embed and
+ * final_norm are required; lm_head is ignored when tied.  All bf16. */
+#define MK_LAYER_SLOTS 11
+typedef struct {
+  const void* const* layer_ptrs;
+  const void* embed;
+  const void* final_norm;
+  const void* lm_head;
+} mk_weights;
+
+/* Run one decode step as the persistent megakernel: ONE launch of 'num_cus'
+ * workgroups on 'stream' (a hipStream_t; NULL = default stream).
+ * kv_cache: device bf16 [n_layers][2][batch][n_kv_heads][max_kv_len][head_dim];
+ *   row kv_len[b] of every (layer, K|V, b, head) is written, rows < kv_len[b]
+ *   are read, nothing else is touched, so repeated runs are idempotent.
+ * tokens: device int32 [batch], input token ids (ids outside [0, vocab) are
+ *   clamped into it on the device).
+ * Results stay in the plan (see mk_plan_output).  Only enqueues work; the
+ * first call uploads the plan; pointer changes rewrite the operand table.
+ * A device wait that exceeds the plan's bound makes the grid exit early and is
+ * reported by mk_plan_check.  Errors: MK_E_INVALID, MK_E_STATE (graph-only
+ * plan), MK_E_HIP. */
+mk_status mk_run(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens, void* stream);
+
+/* The same step with one kernel launch per operator (stream order replaces the
+ * event counters; same tiles and tile arithmetic, weights read straight from
+ * memory).  The baseline the megakernel is measured against. */
+mk_status mk_run_layerwise(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens,
+                           void* stream);
+
+/* Device pointer and size of a plan output:
+ * MK_OUT_LOGITS fp32 [batch][vocab]; MK_OUT_NEXT_TOKEN int32 [batch];
+ * MK_OUT_QKV fp32 [n_layers][batch][n_kv_heads][(n_q/n_kv + 2) * head_dim]
+ *   (per kv head: its q heads, then k, then v, before RoPE);
+ * MK_OUT_HIDDEN fp32 [n_layers][2][batch][hidden] (residual stream after the
+ *   attention block and after the FFN block of each layer). */
+enum { MK_OUT_LOGITS = 0, MK_OUT_NEXT_TOKEN = 1, MK_OUT_QKV = 2, MK_OUT_HIDDEN = 3 };
+mk_status mk_plan_output(const mk_plan* plan, int32_t which, void** dev_ptr, size_t* bytes);
+/* Enqueue a device-to-device copy of output 'which' into dst (device, at least
+ * 'bytes' = the output's size) on 'stream'. */
+mk_status mk_plan_copy_output(const mk_plan* plan, int32_t which, void* dst, size_t bytes, void* stream);
+
+/* Synchronize the stream, then read back the device state of the last run:
+ * counters_ok = 1 when every event counter equals epoch * target; err_* is the
+ * watchdog record (err_kind 0 = none, 1 = event wait, 2 = page wait, 3 = ready
+ * wait, 4 = drain wait).  Returns MK_E_TIMEOUT when the record is set. */
+typedef struct {
+  uint32_t epoch;
+  int32_t counters_ok;
+  int32_t bad_counters;
+  int32_t err_kind, err_cu, err_slot, err_event;
+  uint32_t err_value, err_target;
+} mk_check;
+mk_status mk_plan_check(mk_plan* plan, void* stream, mk_check* out);
+
+/* Per-instruction timestamps of the next mk_run calls (enable=1) or none
+ * (enable=0).  mk_plan_trace copies the last run's trace to host memory:
+ * uint64 [num_cus][max_len][4] = (event satisfied, compute start, compute end,
+ * signalled), in ticks of 'ticks_per_us'. */
+mk_status mk_plan_set_trace(mk_plan* plan, int32_t enable);
+mk_status mk_plan_trace(mk_plan* plan, void* stream, uint64_t* host_out, size_t bytes, double* ticks_per_us);
+
+void mk_plan_free(mk_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -38,6 +38,8 @@ Readings where the pages are silent (each listed in the design notes):
 from math import gcd
 from itertools import product
 
+import numpy as np
+
 WORDS = 32
 MAX_DIMS = 4
 
@@ -333,10 +335,10 @@ def plan_graph(ops, edges, num_cus):
     # --- 6. placement and encoding -------------------------------------------
     T = len(tasks)
     max_len = max(1, ceil_div(T, num_cus))
-    queue = [[[0] * WORDS for _ in range(max_len)] for _ in range(num_cus)]
+    queue = np.zeros((num_cus, max_len, WORDS), dtype=np.int32)
     for t, (o, x, y, z) in enumerate(tasks):
         op = ops[o]
-        w = queue[t % num_cus][t // num_cus]
+        w = queue[t % num_cus, t // num_cus]
         w[W_OPCODE] = op.opcode
         w[W_SPEC] = op.spec
         w[W_OPROW] = o
@@ -368,11 +370,33 @@ def plan_graph(ops, edges, num_cus):
 # ---------------------------------------------------------------------------
 # Llama-family decode step as an operator DAG
 # ---------------------------------------------------------------------------
-DEFAULT_OPTS = dict(num_cus=256, gemv_rows=16, gateup_outs=8, down_rows=4, lm_rows=16, attn_splits=0)
+DEFAULT_OPTS = dict(num_cus=256, gemv_rows=0, gateup_outs=0, down_rows=0, lm_rows=0, attn_splits=0)
 
 
-def default_splits(max_pos_plus_1):
-    return max(1, min(32, ceil_div(max_pos_plus_1, 64)))
+def resolve_opts(desc, batch, kv_len, opts=None):
+    """Fill the 0 (default) fields: tiles of about 64 KiB of bf16 weights.
+    gemv_rows = clamp(32768 // hidden, 4, 16); gateup_outs = gemv_rows // 2;
+    down_rows = clamp(32768 // ffn, 1, 16); lm_rows = gemv_rows;
+    attn_splits = clamp(ceil((max kv + 1) / 64), 1, 32), then raised until one
+    split's K and V rows (2 * rows * head_dim * 2 bytes) fit in 64 KiB."""
+    o = dict(DEFAULT_OPTS)
+    o.update({k: v for k, v in (opts or {}).items() if v})
+    H, F, hd = desc["hidden"], desc["ffn"], desc["head_dim"]
+    if not o["gemv_rows"]:
+        o["gemv_rows"] = max(4, min(16, 32768 // H))
+    if not o["gateup_outs"]:
+        o["gateup_outs"] = max(1, o["gemv_rows"] // 2)
+    if not o["down_rows"]:
+        o["down_rows"] = max(1, min(16, 32768 // F))
+    if not o["lm_rows"]:
+        o["lm_rows"] = o["gemv_rows"]
+    if not o["attn_splits"]:
+        n = int(max(kv_len)) + 1
+        S = max(1, min(32, ceil_div(n, 64)))
+        while ceil_div(n, S) * hd * 4 > 65536:
+            S += 1
+        o["attn_splits"] = S
+    return o
 
 
 def split_range(pos, S, s):
@@ -385,8 +409,7 @@ def split_range(pos, S, s):
 
 
 def model_graph(desc, batch, kv_len, opts=None):
-    o = dict(DEFAULT_OPTS)
-    o.update(opts or {})
+    o = resolve_opts(desc, batch, kv_len, opts)
     H, nq, nkv, hd = desc["hidden"], desc["n_q_heads"], desc["n_kv_heads"], desc["head_dim"]
     F, V, L = desc["ffn"], desc["vocab"], desc["n_layers"]
     B = batch
@@ -395,7 +418,7 @@ def model_graph(desc, batch, kv_len, opts=None):
     R, GU, DR, LR = o["gemv_rows"], o["gateup_outs"], o["down_rows"], o["lm_rows"]
     assert RPG % R == 0 and hd % R == 0
     T_qkv, T_o, T_f, T_d, T_v = RPG // R, ceil_div(H, R), ceil_div(F, GU), ceil_div(H, DR), ceil_div(V, LR)
-    S = o["attn_splits"] or default_splits(int(max(kv_len)) + 1)
+    S = o["attn_splits"]
     spec = 1 if B > 4 else 0
     ops, edges = [], []
 
@@ -431,8 +454,7 @@ def model_graph(desc, batch, kv_len, opts=None):
 
 
 def plan_model(desc, batch, kv_len, opts=None):
-    o = dict(DEFAULT_OPTS)
-    o.update(opts or {})
+    o = resolve_opts(desc, batch, kv_len, opts)
     ops, edges, info = model_graph(desc, batch, kv_len, o)
     pl = plan_graph(ops, edges, o["num_cus"])
     pl.info = info

@@ -1,0 +1,273 @@
+"""Python binding of libmk.so (include/mk.h): argument marshalling only.
+
+Every step of the decode path runs in the library's HIP kernels; PyTorch is
+used for device memory and streams.  Importing this package loads the
+in-tree ``libmk.so`` and raises if it is missing -- there is no fallback.
+
+    import persistent_megakernel_decode_amd as mk
+    plan = mk.Plan.build(desc, batch, kv_len)       # mk_plan_build
+    plan.run(weights, kv_cache, tokens)             # mk_run (one persistent launch)
+    plan.run_layerwise(weights, kv_cache, tokens)   # mk_run_layerwise (one launch per op)
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmk.so")
+
+MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_TIMEOUT, MK_E_STATE = 0, -1, -2, -3, -4, -5, -6
+MK_ABI_VERSION = 1
+MK_ARCH_LLAMA, MK_ARCH_QWEN3 = 1, 2
+MK_BF16 = 0
+MK_LAYER_SLOTS = 11
+MK_OUT_LOGITS, MK_OUT_NEXT_TOKEN, MK_OUT_QKV, MK_OUT_HIDDEN = 0, 1, 2, 3
+LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_plan_export", "mk_run",
+            "mk_run_layerwise", "mk_plan_output", "mk_plan_copy_output", "mk_plan_check", "mk_plan_set_trace",
+            "mk_plan_trace", "mk_plan_free")
+
+i32, u32, f32, vp, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("abi_version", u32), ("struct_size", u32), ("arch", i32), ("n_layers", i32), ("hidden", i32),
+                ("n_q_heads", i32), ("n_kv_heads", i32), ("head_dim", i32), ("ffn", i32), ("vocab", i32),
+                ("tied_lm_head", i32), ("qk_norm", i32), ("weight_dtype", i32), ("max_kv_len", i32),
+                ("rms_eps", f32), ("rope_theta", f32)]
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("num_cus", i32), ("gemv_rows", i32), ("gateup_outs", i32), ("down_rows", i32), ("lm_rows", i32),
+                ("attn_splits", i32), ("timeout_ms", i32), ("reserved", i32 * 5)]
+
+
+class GraphOp(ctypes.Structure):
+    _fields_ = [("opcode", i32), ("spec", i32), ("layer", i32), ("grid", i32 * 3)]
+
+
+class GraphEdge(ctypes.Structure):
+    _fields_ = [("prod", i32), ("cons", i32), ("out_map", i32 * 3), ("in_map", i32 * 3), ("has_extent", i32),
+                ("extent", i32 * 4), ("ptile", i32 * 4), ("ctile", i32 * 4)]
+
+
+class PlanView(ctypes.Structure):
+    _fields_ = [("num_cus", i32), ("max_len", i32), ("num_tasks", i32), ("num_events", i32), ("num_ops", i32),
+                ("num_edges", i32), ("queue", vp), ("event_target", vp), ("event_first", vp), ("event_last", vp),
+                ("task_trigger", vp), ("task_wait", vp), ("op_table", vp), ("edge_kept", vp)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("layer_ptrs", vp), ("embed", vp), ("final_norm", vp), ("lm_head", vp)]
+
+
+class Check(ctypes.Structure):
+    _fields_ = [("epoch", u32), ("counters_ok", i32), ("bad_counters", i32), ("err_kind", i32), ("err_cu", i32),
+                ("err_slot", i32), ("err_event", i32), ("err_value", u32), ("err_target", u32)]
+
+
+class MKError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s (status %d)" % (msg, status))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libmk.so (built by ``python -m persistent_megakernel_decode_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmk.so is not built: run python -m persistent_megakernel_decode_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.mk_last_error.restype = ctypes.c_char_p
+        L.mk_abi_version.restype = ctypes.c_int
+        L.mk_plan_build.argtypes = [P(ModelDesc), i32, vp, P(PlanOpts), P(vp)]
+        L.mk_graph_plan.argtypes = [vp, i32, vp, i32, i32, P(vp)]
+        L.mk_plan_export.argtypes = [vp, P(PlanView)]
+        L.mk_run.argtypes = [vp, P(Weights), vp, vp, vp]
+        L.mk_run_layerwise.argtypes = [vp, P(Weights), vp, vp, vp]
+        L.mk_plan_output.argtypes = [vp, i32, P(vp), P(sz)]
+        L.mk_plan_copy_output.argtypes = [vp, i32, vp, sz, vp]
+        L.mk_plan_check.argtypes = [vp, vp, P(Check)]
+        L.mk_plan_set_trace.argtypes = [vp, i32]
+        L.mk_plan_trace.argtypes = [vp, vp, vp, sz, P(ctypes.c_double)]
+        L.mk_plan_free.argtypes = [vp]
+        L.mk_plan_free.restype = None
+        for n in EXPORTED:
+            if n not in ("mk_last_error", "mk_abi_version", "mk_plan_free"):
+                getattr(L, n).restype = ctypes.c_int
+        if L.mk_abi_version() != MK_ABI_VERSION:
+            raise ImportError("libmk.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(st):
+    if st != MK_OK:
+        raise MKError(st, lib().mk_last_error().decode())
+
+
+def model_desc(cfg, max_kv_len):
+    """mk_model_desc from a workload dict (synth.config format)."""
+    return ModelDesc(MK_ABI_VERSION, ctypes.sizeof(ModelDesc),
+                     MK_ARCH_QWEN3 if cfg.get("qk_norm") else MK_ARCH_LLAMA, cfg["n_layers"], cfg["hidden"],
+                     cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn"], cfg["vocab"],
+                     int(cfg["tied"]), int(cfg["qk_norm"]), MK_BF16, int(max_kv_len), cfg["rms_eps"],
+                     cfg["rope_theta"])
+
+
+def _arr(view_ptr, n, dtype):
+    if n == 0:
+        return np.zeros(0, dtype=dtype)
+    buf = (ctypes.c_char * (n * np.dtype(dtype).itemsize)).from_address(view_ptr)
+    return np.frombuffer(buf, dtype=dtype).copy()
+
+
+class Plan:
+    """An mk_plan: static schedule plus the device buffers it owns."""
+
+    def __init__(self, handle, batch=None, vocab=None):
+        self._h = vp(handle)
+        self.batch, self.vocab = batch, vocab
+        self._keep = None
+
+    @classmethod
+    def build(cls, cfg, batch, kv_len, max_kv_len, **opts):
+        desc = model_desc(cfg, max_kv_len)
+        kv = np.ascontiguousarray(kv_len, dtype=np.int32)
+        o = PlanOpts()
+        for k, v in opts.items():
+            setattr(o, k, int(v))
+        h = vp()
+        _check(lib().mk_plan_build(ctypes.byref(desc), int(batch), kv.ctypes.data, ctypes.byref(o), ctypes.byref(h)))
+        return cls(h.value, batch, cfg["vocab"])
+
+    @classmethod
+    def graph(cls, ops, edges, num_cus):
+        """ops: [(opcode, grid[, spec, layer])],
+        edges: [(prod, cons, out_map, in_map, extent|None, ptile, ctile)]"""
+        OA = (GraphOp * max(1, len(ops)))()
+        for i, op in enumerate(ops):
+            opcode, grid = op[0], op[1]
+            spec, layer = (op[2], op[3]) if len(op) > 2 else (0, 0)
+            g = tuple(grid) + (1,) * (3 - len(grid))
+            OA[i] = GraphOp(opcode, spec, layer, (i32 * 3)(*g))
+        EA = (GraphEdge * max(1, len(edges)))()
+        for i, (p, c, om, im, ext, pt, ct) in enumerate(edges):
+            om = tuple(om) + (-1,) * (3 - len(om))
+            im = tuple(im) + (-1,) * (3 - len(im))
+            e = GraphEdge(p, c, (i32 * 3)(*om), (i32 * 3)(*im), 1 if ext is not None else 0)
+            if ext is not None:
+                pad = lambda v: tuple(v) + (1,) * (4 - len(v))
+                e.extent, e.ptile, e.ctile = (i32 * 4)(*pad(ext)), (i32 * 4)(*pad(pt)), (i32 * 4)(*pad(ct))
+            EA[i] = e
+        h = vp()
+        _check(lib().mk_graph_plan(OA, len(ops), EA, len(edges), num_cus, ctypes.byref(h)))
+        return cls(h.value)
+
+    def export(self):
+        v = PlanView()
+        _check(lib().mk_plan_export(self._h, ctypes.byref(v)))
+        C, L, T, E = v.num_cus, v.max_len, v.num_tasks, v.num_events
+        return dict(num_cus=C, max_len=L, num_tasks=T, num_events=E,
+                    queue=_arr(v.queue, C * L * 32, np.int32).reshape(C, L, 32),
+                    event_target=_arr(v.event_target, E, np.uint32), event_first=_arr(v.event_first, E, np.int32),
+                    event_last=_arr(v.event_last, E, np.int32), task_trigger=_arr(v.task_trigger, T, np.int32),
+                    task_wait=_arr(v.task_wait, T, np.int32),
+                    op_table=_arr(v.op_table, v.num_ops * 8, np.int32).reshape(v.num_ops, 8),
+                    edge_kept=_arr(v.edge_kept, v.num_edges, np.uint8))
+
+    def run(self, weights, kv_cache, tokens, stream=None, layerwise=False):
+        w = weights.struct if isinstance(weights, DeviceWeights) else weights
+        s = vp(stream.cuda_stream if stream is not None else current_stream())
+        fn = lib().mk_run_layerwise if layerwise else lib().mk_run
+        _check(fn(self._h, ctypes.byref(w), vp(kv_cache.data_ptr()), vp(tokens.data_ptr()), s))
+
+    def run_layerwise(self, weights, kv_cache, tokens, stream=None):
+        self.run(weights, kv_cache, tokens, stream, layerwise=True)
+
+    def output(self, which):
+        """Copy an output into a new torch tensor (on the current stream)."""
+        import torch
+        p, n = vp(), sz()
+        _check(lib().mk_plan_output(self._h, which, ctypes.byref(p), ctypes.byref(n)))
+        dt = torch.int32 if which == MK_OUT_NEXT_TOKEN else torch.float32
+        out = torch.empty(n.value // 4, dtype=dt, device="cuda")
+        _check(lib().mk_plan_copy_output(self._h, which, vp(out.data_ptr()), n.value, vp(current_stream())))
+        return out
+
+    def check(self, stream=None):
+        c = Check()
+        st = lib().mk_plan_check(self._h, vp(stream.cuda_stream if stream is not None else current_stream()),
+                                 ctypes.byref(c))
+        return st, c
+
+    def set_trace(self, enable):
+        _check(lib().mk_plan_set_trace(self._h, 1 if enable else 0))
+
+    def trace(self, stream=None):
+        ex = self.export()
+        out = np.zeros((ex["num_cus"], ex["max_len"], 4), dtype=np.uint64)
+        tpu = ctypes.c_double()
+        _check(lib().mk_plan_trace(self._h, vp(stream.cuda_stream if stream is not None else current_stream()),
+                                   out.ctypes.data, out.nbytes, ctypes.byref(tpu)))
+        return out, tpu.value
+
+    def free(self):
+        if self._h:
+            lib().mk_plan_free(self._h)
+            self._h = vp()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def current_stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class DeviceWeights:
+    """Upload host weights (synth.make_weights format: uint16 bf16 bits) to the
+    current GPU as bf16 tensors and hold the mk_weights pointer table."""
+
+    def __init__(self, host_weights, cfg):
+        import torch
+
+        def dev(a):
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+            return t.to("cuda", non_blocking=False)
+
+        self.tensors = []
+        L = cfg["n_layers"]
+        self.table = (vp * (L * MK_LAYER_SLOTS))()
+        for l in range(L):
+            for s, name in enumerate(LAYER_SLOTS):
+                a = host_weights["layers"][l].get(name)
+                if a is not None:
+                    t = dev(a)
+                    self.tensors.append(t)
+                    self.table[l * MK_LAYER_SLOTS + s] = t.data_ptr()
+        self.embed = dev(host_weights["embed"])
+        self.final_norm = dev(host_weights["final_norm"])
+        self.lm_head = dev(host_weights["lm_head"]) if "lm_head" in host_weights else None
+        self.struct = Weights(ctypes.cast(self.table, vp), self.embed.data_ptr(), self.final_norm.data_ptr(),
+                              self.lm_head.data_ptr() if self.lm_head is not None else None)
+
+
+def kv_to_device(kv_host):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(kv_host).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def tokens_to_device(tokens):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to("cuda")

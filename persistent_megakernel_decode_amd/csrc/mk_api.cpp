@@ -1,0 +1,583 @@
+// C ABI of libmk.so (declared in include/mk.h): plan lifecycle, device
+// buffers, the operand pointer table, launches, checks and traces.
+//
+// The operand pointer table follows the MegaRTP article, section 4
+// "KernelPlan": one row of 16 u64 per operator, shared by all of its tile
+// instructions, so that rebinding weights, KV cache or workspace rewrites the
+// table but never the instruction queues.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mk.h"
+#include "mk_device.hpp"
+#include "plan.hpp"
+
+namespace mk {
+hipError_t launch_megakernel(const mkd::KArgs& a, int num_cus, hipStream_t s);
+hipError_t launch_layer(const mkd::KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s);
+hipError_t megakernel_occupancy(int hd, int* blocks_per_cu);
+}  // namespace mk
+
+namespace {
+thread_local std::string g_err;
+
+mk_status fail(mk_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+mk_status hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return MK_E_HIP;
+}
+#define HIPCHK(x, what)                          \
+  do {                                           \
+    hipError_t e_ = (x);                         \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+}  // namespace
+
+struct mk_plan {
+  bool graph_only = false;
+  mk::Plan P;
+  mk_model_desc desc{};
+  int batch = 0;
+  std::vector<int32_t> kv_len;
+  mk::ModelOpts opts{};
+  std::vector<mk::GraphOp> ops;
+  std::vector<int> op_first, op_count;
+  mkd::Consts c{};
+  int num_cus = 0;
+  unsigned long long timeout_ticks = 0;
+  // device state
+  int device = -1;
+  bool uploaded = false;
+  int* d_queue = nullptr;
+  unsigned* d_counters = nullptr;
+  unsigned* d_err = nullptr;
+  uint64_t* d_optab = nullptr;
+  float* d_rope = nullptr;
+  char* d_ws = nullptr;
+  size_t ws_bytes = 0;
+  unsigned long long* d_trace = nullptr;
+  bool trace_on = false;
+  unsigned epoch = 0;
+  bool need_reset = false;
+  std::vector<uint64_t> h_optab;
+  // workspace offsets (bytes)
+  size_t off_qkv = 0, off_part = 0, off_ao = 0, off_hidden = 0, off_act = 0, off_logits = 0, off_lmmax = 0,
+         off_next = 0;
+  size_t sz_qkv = 0, sz_part = 0, sz_ao = 0, sz_act = 0;
+};
+
+extern "C" {
+
+const char* mk_last_error(void) { return g_err.c_str(); }
+int mk_abi_version(void) { return MK_ABI_VERSION; }
+
+static mk_status finish_plan_common(mk_plan* p) {
+  // tasks of every op must be contiguous for the layerwise launches
+  const int n_ops = (int)p->ops.size();
+  p->op_first.assign(n_ops, -1);
+  p->op_count.assign(n_ops, 0);
+  for (int t = 0; t < p->P.num_tasks; ++t) {
+    int o = p->P.tasks[t][0];
+    if (p->op_first[o] < 0) p->op_first[o] = t;
+    if (p->op_first[o] + p->op_count[o] != t) p->op_first[o] = -2;  // not contiguous
+    p->op_count[o]++;
+  }
+  return MK_OK;
+}
+
+mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* kv_len, const mk_plan_opts* opts,
+                        mk_plan** out) {
+  g_err.clear();
+  if (!desc || !kv_len || !out) return fail(MK_E_INVALID, "null argument");
+  *out = nullptr;
+  if (desc->abi_version != MK_ABI_VERSION || desc->struct_size != sizeof(mk_model_desc))
+    return fail(MK_E_INVALID, "mk_model_desc abi_version/struct_size mismatch");
+  const mk_model_desc& d = *desc;
+  if (d.arch != MK_ARCH_LLAMA && d.arch != MK_ARCH_QWEN3) return fail(MK_E_UNSUPPORTED, "unknown arch");
+  if (d.weight_dtype != MK_BF16) return fail(MK_E_UNSUPPORTED, "only bf16 weights are supported");
+  if (d.n_layers < 1 || d.hidden < 32 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.ffn < 32 || d.vocab < 1)
+    return fail(MK_E_INVALID, "model sizes must be positive");
+  if (d.head_dim != 64 && d.head_dim != 128) return fail(MK_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d.n_q_heads % d.n_kv_heads) return fail(MK_E_UNSUPPORTED, "n_q_heads must be a multiple of n_kv_heads");
+  if (d.n_q_heads / d.n_kv_heads > mkd::kNW) return fail(MK_E_UNSUPPORTED, "at most 4 query heads per kv head");
+  if (d.hidden % 8 || d.ffn % 8)
+    return fail(MK_E_UNSUPPORTED, "hidden and ffn must be multiples of 8");
+  if (d.hidden > 8 * mkd::kNW * 64 * mkd::kMaxChunks || d.ffn > 8 * mkd::kNW * 64 * mkd::kMaxChunks ||
+      d.n_q_heads * d.head_dim > 8 * mkd::kNW * 64 * mkd::kMaxChunks)
+    return fail(MK_E_UNSUPPORTED, "hidden, ffn and n_q_heads*head_dim must be <= 12288");
+  if ((d.arch == MK_ARCH_QWEN3) != (d.qk_norm != 0)) return fail(MK_E_INVALID, "qk_norm must match arch");
+  if (!(d.rms_eps > 0.f) || !(d.rope_theta > 0.f)) return fail(MK_E_INVALID, "rms_eps and rope_theta must be > 0");
+  if (batch != 1) return fail(MK_E_UNSUPPORTED, "batch must be 1 in this build");
+  std::vector<int32_t> kl(kv_len, kv_len + batch);
+  for (int b = 0; b < batch; ++b)
+    if (kl[b] < 0 || kl[b] + 1 > d.max_kv_len) return fail(MK_E_UNSUPPORTED, "kv_len[b] + 1 must be <= max_kv_len");
+
+  auto* p = new mk_plan();
+  p->desc = d;
+  p->batch = batch;
+  p->kv_len = kl;
+  mk::ModelOpts o{};
+  int timeout_ms = 200;
+  if (opts) {
+    o.num_cus = opts->num_cus;
+    o.gemv_rows = opts->gemv_rows;
+    o.gateup_outs = opts->gateup_outs;
+    o.down_rows = opts->down_rows;
+    o.lm_rows = opts->lm_rows;
+    o.attn_splits = opts->attn_splits;
+    if (opts->timeout_ms > 0) timeout_ms = opts->timeout_ms;
+  }
+  if (o.num_cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      delete p;
+      return fail(MK_E_INVALID, "num_cus not given and no device to query");
+    }
+    o.num_cus = n;
+  }
+  mk::ModelShape ms{d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab};
+  mk::resolve_opts(ms, kl, &o);
+  if (o.gemv_rows > mkd::kMaxRows || 2 * o.gateup_outs > mkd::kMaxRows || o.down_rows > mkd::kMaxRows ||
+      o.lm_rows > mkd::kMaxRows) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "tile rows must be <= 16");
+  }
+  // every tile's weight bytes must fit the LDS page ring
+  auto r1k = [](long v) { return (v + 1023) / 1024 * 1024; };
+  const long ring = (long)mkd::kNumPages * mkd::kPage;
+  const int Smax = o.attn_splits;
+  const int maxpos = *std::max_element(kl.begin(), kl.end()) + 1;
+  const long attn_rows = mk::ceil_div(maxpos, Smax);
+  if ((long)o.gemv_rows * d.hidden * 2 > ring || r1k((long)o.gateup_outs * d.hidden * 2) * 2 > ring ||
+      (long)o.down_rows * d.ffn * 2 > ring || (long)o.gemv_rows * d.n_q_heads * d.head_dim * 2 > ring ||
+      (long)o.lm_rows * d.hidden * 2 > ring || r1k(attn_rows * d.head_dim * 2) * 2 > ring) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "a tile does not fit the 144 KiB LDS page ring; use smaller tiles");
+  }
+  if (attn_rows + 1 > (mkd::kScratch - 3 * d.head_dim)) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "too many positions per attention split; raise attn_splits");
+  }
+  p->opts = o;
+  std::vector<mk::GraphEdge> edges;
+  std::string err = mk::model_graph(ms, batch, kl, o, &p->ops, &edges);
+  if (err.empty()) err = mk::plan_graph(p->ops, edges, o.num_cus, &p->kv_len, &p->P);
+  if (!err.empty()) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "planner: " + err);
+  }
+  finish_plan_common(p);
+  for (size_t k = 0; k < p->ops.size(); ++k)
+    if (p->op_first[k] < 0) {
+      delete p;
+      return fail(MK_E_UNSUPPORTED, "planner: an operator's tasks are not contiguous");
+    }
+  p->num_cus = o.num_cus;
+  const int hpg = d.n_q_heads / d.n_kv_heads;
+  mkd::Consts& c = p->c;
+  c.H = d.hidden;
+  c.nq = d.n_q_heads;
+  c.nkv = d.n_kv_heads;
+  c.hd = d.head_dim;
+  c.F = d.ffn;
+  c.V = d.vocab;
+  c.L = d.n_layers;
+  c.B = batch;
+  c.cap = d.max_kv_len;
+  c.hpg = hpg;
+  c.RPG = (hpg + 2) * d.head_dim;
+  c.S = o.attn_splits;
+  c.T_v = mk::ceil_div(d.vocab, o.lm_rows);
+  c.qk_norm = d.qk_norm;
+  c.eps = d.rms_eps;
+  c.inv_sqrt_hd = (float)(1.0 / std::sqrt((double)d.head_dim));
+  p->timeout_ticks = (unsigned long long)timeout_ms * 100000ull;  // 100 MHz constant clock
+  // workspace layout (fp32 everywhere)
+  const size_t B = batch, L = d.n_layers;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o2 = off;
+    off += (bytes + 255) / 256 * 256;
+    return o2;
+  };
+  p->sz_qkv = B * c.nkv * c.RPG * 4;
+  p->sz_part = B * c.nkv * c.S * hpg * (c.hd + 2) * 4;
+  p->sz_ao = B * c.nq * c.hd * 4;
+  p->sz_act = B * c.F * 4;
+  p->off_qkv = take(p->sz_qkv * L);
+  p->off_part = take(p->sz_part * L);
+  p->off_ao = take(p->sz_ao * L);
+  p->off_hidden = take(B * c.H * 4 * 2 * L);
+  p->off_act = take(p->sz_act * L);
+  p->off_logits = take(B * c.V * 4);
+  p->off_lmmax = take(B * c.T_v * 8);
+  p->off_next = take(B * 4);
+  p->ws_bytes = off;
+  *out = p;
+  return MK_OK;
+}
+
+mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_edge* edges, int32_t n_edges,
+                        int32_t num_cus, mk_plan** out) {
+  g_err.clear();
+  if (!out || (n_ops > 0 && !ops) || (n_edges > 0 && !edges) || n_ops < 0 || n_edges < 0)
+    return fail(MK_E_INVALID, "null argument");
+  *out = nullptr;
+  auto* p = new mk_plan();
+  p->graph_only = true;
+  std::vector<mk::GraphEdge> ge;
+  for (int i = 0; i < n_ops; ++i) {
+    mk::GraphOp op;
+    op.opcode = ops[i].opcode;
+    op.spec = ops[i].spec;
+    op.layer = ops[i].layer;
+    op.grid = {{ops[i].grid[0], ops[i].grid[1], ops[i].grid[2]}};
+    p->ops.push_back(op);
+  }
+  for (int i = 0; i < n_edges; ++i) {
+    mk::GraphEdge e;
+    e.prod = edges[i].prod;
+    e.cons = edges[i].cons;
+    for (int a = 0; a < 3; ++a) {
+      e.out_map[a] = edges[i].out_map[a];
+      e.in_map[a] = edges[i].in_map[a];
+    }
+    e.has_extent = edges[i].has_extent != 0;
+    for (int k = 0; k < 4; ++k) {
+      e.extent[k] = edges[i].extent[k];
+      e.ptile[k] = edges[i].ptile[k];
+      e.ctile[k] = edges[i].ctile[k];
+    }
+    ge.push_back(e);
+  }
+  std::string err = mk::plan_graph(p->ops, ge, num_cus, nullptr, &p->P);
+  if (!err.empty()) {
+    delete p;
+    return fail(MK_E_INVALID, "planner: " + err);
+  }
+  finish_plan_common(p);
+  p->num_cus = num_cus;
+  *out = p;
+  return MK_OK;
+}
+
+mk_status mk_plan_export(const mk_plan* p, mk_plan_view* v) {
+  g_err.clear();
+  if (!p || !v) return fail(MK_E_INVALID, "null argument");
+  v->num_cus = p->P.num_cus;
+  v->max_len = p->P.max_len;
+  v->num_tasks = p->P.num_tasks;
+  v->num_events = p->P.num_events;
+  v->num_ops = (int32_t)p->ops.size();
+  v->num_edges = (int32_t)p->P.edge_kept.size();
+  v->queue = p->P.queue.data();
+  v->event_target = p->P.event_target.data();
+  v->event_first = p->P.event_first.data();
+  v->event_last = p->P.event_last.data();
+  v->task_trigger = p->P.task_trigger.data();
+  v->task_wait = p->P.task_wait.data();
+  v->op_table = p->P.op_table.data();
+  v->edge_kept = p->P.edge_kept.data();
+  return MK_OK;
+}
+
+static mk_status ensure_device(mk_plan* p) {
+  if (p->uploaded) {
+    int dev = -1;
+    HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+    if (dev != p->device) return fail(MK_E_STATE, "plan was uploaded to another device");
+    return MK_OK;
+  }
+  HIPCHK(hipGetDevice(&p->device), "hipGetDevice");
+  int ncu = 0;
+  HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, p->device), "hipDeviceGetAttribute");
+  int occ = 0;
+  HIPCHK(mk::megakernel_occupancy(p->c.hd, &occ), "occupancy");
+  if (p->num_cus > ncu || occ < 1)
+    return fail(MK_E_UNSUPPORTED, "the persistent grid (" + std::to_string(p->num_cus) + " workgroups) cannot be co-resident on " +
+                                      std::to_string(ncu) + " CUs");
+  const size_t qbytes = p->P.queue.size() * 4, ebytes = (size_t)std::max(1, p->P.num_events) * 4;
+  HIPCHK(hipMalloc(&p->d_queue, qbytes), "hipMalloc queue");
+  HIPCHK(hipMalloc(&p->d_counters, ebytes), "hipMalloc counters");
+  HIPCHK(hipMalloc(&p->d_err, 64), "hipMalloc err");
+  HIPCHK(hipMalloc(&p->d_optab, p->ops.size() * 16 * 8), "hipMalloc optab");
+  HIPCHK(hipMalloc(&p->d_rope, (size_t)p->batch * p->c.hd * 4), "hipMalloc rope");
+  HIPCHK(hipMalloc(&p->d_ws, p->ws_bytes), "hipMalloc workspace");
+  HIPCHK(hipMemcpy(p->d_queue, p->P.queue.data(), qbytes, hipMemcpyHostToDevice), "upload queue");
+  HIPCHK(hipMemset(p->d_counters, 0, ebytes), "zero counters");
+  HIPCHK(hipMemset(p->d_err, 0, 64), "zero err");
+  HIPCHK(hipMemset(p->d_ws, 0xFF, p->ws_bytes), "poison workspace");  // NaN until written
+  // RoPE table (cos, sin) at each sequence's new position, computed in fp64
+  std::vector<float> rope((size_t)p->batch * p->c.hd);
+  const int half = p->c.hd / 2;
+  for (int b = 0; b < p->batch; ++b)
+    for (int i = 0; i < half; ++i) {
+      double ang = (double)p->kv_len[b] * std::pow((double)p->desc.rope_theta, -2.0 * i / p->c.hd);
+      rope[(size_t)b * p->c.hd + 2 * i] = (float)std::cos(ang);
+      rope[(size_t)b * p->c.hd + 2 * i + 1] = (float)std::sin(ang);
+    }
+  HIPCHK(hipMemcpy(p->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice), "upload rope");
+  p->uploaded = true;
+  p->epoch = 0;
+  return MK_OK;
+}
+
+static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const void* tokens, hipStream_t s) {
+  const mk_model_desc& d = p->desc;
+  const int L = d.n_layers;
+  if (!w || !w->layer_ptrs || !w->embed || !w->final_norm || !kv || !tokens)
+    return fail(MK_E_INVALID, "null weight, KV-cache or token pointer");
+  if (!d.tied_lm_head && !w->lm_head) return fail(MK_E_INVALID, "lm_head is required when not tied");
+  for (int l = 0; l < L; ++l)
+    for (int sidx = 0; sidx < MK_LAYER_SLOTS; ++sidx) {
+      bool need = !(sidx == 4 || sidx == 5) || d.qk_norm;
+      if (need && !w->layer_ptrs[l * MK_LAYER_SLOTS + sidx]) return fail(MK_E_INVALID, "null layer weight pointer");
+    }
+  const size_t B = p->batch, hpg = p->c.hpg;
+  auto u = [](const void* q) { return (uint64_t)(uintptr_t)q; };
+  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(p->d_ws + off); };
+  const size_t hid = B * p->c.H * 4;
+  auto xa = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l) * hid); };
+  auto xb = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l + 1) * hid); };
+  const size_t kvlayer = (size_t)2 * B * d.n_kv_heads * d.max_kv_len * d.head_dim * 2;
+  std::vector<uint64_t> t(p->ops.size() * 16, 0);
+  for (size_t o = 0; o < p->ops.size(); ++o) {
+    const auto& op = p->ops[o];
+    uint64_t* r = &t[o * 16];
+    const int l = op.layer;
+    const void* const* W = l < L ? w->layer_ptrs + (size_t)l * MK_LAYER_SLOTS : nullptr;
+    switch (op.opcode) {
+      case mk::kQkv:
+        r[mkd::QkvWq] = u(W[1]);
+        r[mkd::QkvWk] = u(W[2]);
+        r[mkd::QkvWv] = u(W[3]);
+        r[mkd::QkvNorm] = u(W[0]);
+        r[mkd::QkvX] = l ? xb(l - 1) : 0;
+        r[mkd::QkvEmbed] = u(w->embed);
+        r[mkd::QkvTokens] = u(tokens);
+        r[mkd::QkvOut] = ws(p->off_qkv + l * p->sz_qkv);
+        break;
+      case mk::kAttn:
+        r[mkd::AttnQkv] = ws(p->off_qkv + l * p->sz_qkv);
+        r[mkd::AttnK] = u((const char*)kv + l * kvlayer);
+        r[mkd::AttnV] = u((const char*)kv + l * kvlayer + kvlayer / 2);
+        r[mkd::AttnRope] = u(p->d_rope);
+        r[mkd::AttnOut] = ws(p->off_part + l * p->sz_part);
+        r[mkd::AttnQn] = d.qk_norm ? u(W[4]) : 0;
+        r[mkd::AttnKn] = d.qk_norm ? u(W[5]) : 0;
+        break;
+      case mk::kCombine:
+        r[mkd::CombPart] = ws(p->off_part + l * p->sz_part);
+        r[mkd::CombOut] = ws(p->off_ao + l * p->sz_ao);
+        break;
+      case mk::kOproj:
+        r[mkd::OWo] = u(W[6]);
+        r[mkd::OIn] = ws(p->off_ao + l * p->sz_ao);
+        r[mkd::OX] = l ? xb(l - 1) : 0;
+        r[mkd::OEmbed] = u(w->embed);
+        r[mkd::OTokens] = u(tokens);
+        r[mkd::OOut] = xa(l);
+        break;
+      case mk::kGateUp:
+        r[mkd::GuWg] = u(W[8]);
+        r[mkd::GuWu] = u(W[9]);
+        r[mkd::GuNorm] = u(W[7]);
+        r[mkd::GuIn] = xa(l);
+        r[mkd::GuOut] = ws(p->off_act + l * p->sz_act);
+        break;
+      case mk::kDown:
+        r[mkd::DnW] = u(W[10]);
+        r[mkd::DnIn] = ws(p->off_act + l * p->sz_act);
+        r[mkd::DnRes] = xa(l);
+        r[mkd::DnOut] = xb(l);
+        break;
+      case mk::kLmHead:
+        r[mkd::LmW] = u(d.tied_lm_head ? w->embed : w->lm_head);
+        r[mkd::LmNorm] = u(w->final_norm);
+        r[mkd::LmIn] = xb(L - 1);
+        r[mkd::LmLogits] = ws(p->off_logits);
+        r[mkd::LmMax] = ws(p->off_lmmax);
+        break;
+      case mk::kArgmax:
+        r[mkd::AmMax] = ws(p->off_lmmax);
+        r[mkd::AmOut] = ws(p->off_next);
+        break;
+      default:
+        break;
+    }
+  }
+  (void)hpg;
+  if (t != p->h_optab) {
+    p->h_optab = t;
+    HIPCHK(hipMemcpyAsync(p->d_optab, p->h_optab.data(), t.size() * 8, hipMemcpyHostToDevice, s), "upload operand table");
+    HIPCHK(hipStreamSynchronize(s), "operand table sync");
+  }
+  return MK_OK;
+}
+
+static mkd::KArgs kargs(const mk_plan* p) {
+  mkd::KArgs a{};
+  a.queue = p->d_queue;
+  a.optab = p->d_optab;
+  a.counters = p->d_counters;
+  a.err = p->d_err;
+  a.trace = p->trace_on ? p->d_trace : nullptr;
+  a.max_len = p->P.max_len;
+  a.epoch = p->epoch;
+  a.timeout_ticks = p->timeout_ticks;
+  a.c = p->c;
+  return a;
+}
+
+mk_status mk_run(mk_plan* p, const mk_weights* w, void* kv_cache, const void* tokens, void* stream) {
+  g_err.clear();
+  if (!p) return fail(MK_E_INVALID, "null plan");
+  if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
+  hipStream_t s = (hipStream_t)stream;
+  mk_status st = ensure_device(p);
+  if (st != MK_OK) return st;
+  st = bind_operands(p, w, kv_cache, tokens, s);
+  if (st != MK_OK) return st;
+  if (p->need_reset) {
+    HIPCHK(hipMemsetAsync(p->d_counters, 0, (size_t)std::max(1, p->P.num_events) * 4, s), "reset counters");
+    p->epoch = 0;
+    p->need_reset = false;
+  }
+  p->epoch += 1;
+  if (p->epoch == 0) p->epoch = 1;  // 0 marks "no error" in the watchdog record
+  if (p->trace_on) HIPCHK(hipMemsetAsync(p->d_trace, 0, (size_t)p->num_cus * p->P.max_len * 32, s), "clear trace");
+  HIPCHK(mk::launch_megakernel(kargs(p), p->num_cus, s), "megakernel launch");
+  return MK_OK;
+}
+
+mk_status mk_run_layerwise(mk_plan* p, const mk_weights* w, void* kv_cache, const void* tokens, void* stream) {
+  g_err.clear();
+  if (!p) return fail(MK_E_INVALID, "null plan");
+  if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
+  hipStream_t s = (hipStream_t)stream;
+  mk_status st = ensure_device(p);
+  if (st != MK_OK) return st;
+  st = bind_operands(p, w, kv_cache, tokens, s);
+  if (st != MK_OK) return st;
+  mkd::KArgs a = kargs(p);
+  a.trace = nullptr;
+  for (size_t o = 0; o < p->ops.size(); ++o)
+    HIPCHK(mk::launch_layer(a, p->num_cus, p->op_first[o], p->op_count[o], s), "layer launch");
+  return MK_OK;
+}
+
+mk_status mk_plan_output(const mk_plan* p, int32_t which, void** dev_ptr, size_t* bytes) {
+  g_err.clear();
+  if (!p || !dev_ptr || !bytes) return fail(MK_E_INVALID, "null argument");
+  if (p->graph_only || !p->uploaded) return fail(MK_E_STATE, "the plan has not run");
+  const size_t B = p->batch;
+  switch (which) {
+    case MK_OUT_LOGITS:
+      *dev_ptr = p->d_ws + p->off_logits;
+      *bytes = B * p->c.V * 4;
+      return MK_OK;
+    case MK_OUT_NEXT_TOKEN:
+      *dev_ptr = p->d_ws + p->off_next;
+      *bytes = B * 4;
+      return MK_OK;
+    case MK_OUT_QKV:
+      *dev_ptr = p->d_ws + p->off_qkv;
+      *bytes = p->sz_qkv * p->c.L;
+      return MK_OK;
+    case MK_OUT_HIDDEN:
+      *dev_ptr = p->d_ws + p->off_hidden;
+      *bytes = B * p->c.H * 4 * 2 * p->c.L;
+      return MK_OK;
+    default:
+      return fail(MK_E_INVALID, "unknown output");
+  }
+}
+
+mk_status mk_plan_copy_output(const mk_plan* p, int32_t which, void* dst, size_t bytes, void* stream) {
+  void* src = nullptr;
+  size_t n = 0;
+  mk_status st = mk_plan_output(p, which, &src, &n);
+  if (st != MK_OK) return st;
+  if (!dst || bytes < n) return fail(MK_E_INVALID, "destination missing or too small");
+  HIPCHK(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, (hipStream_t)stream), "copy output");
+  return MK_OK;
+}
+
+mk_status mk_plan_check(mk_plan* p, void* stream, mk_check* out) {
+  g_err.clear();
+  if (!p || !out) return fail(MK_E_INVALID, "null argument");
+  std::memset(out, 0, sizeof(*out));
+  if (p->graph_only || !p->uploaded) return fail(MK_E_STATE, "the plan has not run");
+  HIPCHK(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  std::vector<uint32_t> ctr(std::max(1, p->P.num_events));
+  uint32_t err[16];
+  HIPCHK(hipMemcpy(ctr.data(), p->d_counters, ctr.size() * 4, hipMemcpyDeviceToHost), "read counters");
+  HIPCHK(hipMemcpy(err, p->d_err, 64, hipMemcpyDeviceToHost), "read err");
+  out->epoch = p->epoch;
+  int bad = 0;
+  for (int e = 0; e < p->P.num_events; ++e)
+    if (ctr[e] != p->epoch * p->P.event_target[e]) ++bad;
+  out->bad_counters = bad;
+  out->counters_ok = bad == 0;
+  if (err[0] != 0 && err[0] == p->epoch) {
+    out->err_kind = (int32_t)err[1];
+    out->err_cu = (int32_t)err[2];
+    out->err_slot = (int32_t)err[3];
+    out->err_event = (int32_t)err[4];
+    out->err_value = err[5];
+    out->err_target = err[6];
+    p->need_reset = true;
+    return fail(MK_E_TIMEOUT, "a device wait timed out (kind " + std::to_string(err[1]) + ", cu " + std::to_string(err[2]) +
+                                  ", slot " + std::to_string(err[3]) + ")");
+  }
+  if (bad) p->need_reset = true;
+  return MK_OK;
+}
+
+mk_status mk_plan_set_trace(mk_plan* p, int32_t enable) {
+  g_err.clear();
+  if (!p) return fail(MK_E_INVALID, "null plan");
+  if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
+  if (enable && !p->d_trace) {
+    HIPCHK(hipMalloc(&p->d_trace, (size_t)p->num_cus * p->P.max_len * 32), "hipMalloc trace");
+  }
+  p->trace_on = enable != 0;
+  return MK_OK;
+}
+
+mk_status mk_plan_trace(mk_plan* p, void* stream, uint64_t* host_out, size_t bytes, double* ticks_per_us) {
+  g_err.clear();
+  if (!p || !host_out || !ticks_per_us) return fail(MK_E_INVALID, "null argument");
+  const size_t need = (size_t)p->num_cus * p->P.max_len * 32;
+  if (!p->d_trace) return fail(MK_E_STATE, "tracing was never enabled");
+  if (bytes < need) return fail(MK_E_INVALID, "host buffer too small");
+  HIPCHK(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  HIPCHK(hipMemcpy(host_out, p->d_trace, need, hipMemcpyDeviceToHost), "read trace");
+  *ticks_per_us = 100.0;
+  return MK_OK;
+}
+
+void mk_plan_free(mk_plan* p) {
+  if (!p) return;
+  if (p->uploaded) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(p->d_queue);
+    (void)hipFree(p->d_counters);
+    (void)hipFree(p->d_err);
+    (void)hipFree(p->d_optab);
+    (void)hipFree(p->d_rope);
+    (void)hipFree(p->d_ws);
+  }
+  if (p->d_trace) (void)hipFree(p->d_trace);
+  delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,383 @@
+// Persistent megakernel interpreter and layerwise kernels for gfx950 (MI355X).
+//
+// Megakernel: one workgroup per compute unit walks its static queue of tile
+// instructions.  The worker loop is the one of the CMU 15-779 lecture 7 notes,
+// section 4.1 (fetch the task, prefetch its weights without waiting on any
+// dependency, wait for the counters, read activations and compute, bump the
+// trigger counter), split over wavefront roles as in the MegaRTP article,
+// section 3 (controller / loader / consumer / storer warps) and section 4
+// ("Device-side execution", "shared-memory paging"):
+//   wave 0    controller: waits for each instruction's event counter
+//             (agent-scope acquire) and publishes "ready" in LDS;
+//   wave 1    storer: after the compute waves finish an instruction, an
+//             agent-scope release and one atomic add on its trigger counter;
+//   waves 2-3 weight loaders: stream every instruction's weight (or K/V) bytes
+//             HBM -> LDS with LDS-DMA (global_load_lds_dwordx4), alternating
+//             16 KiB pages of a 9-page ring; they never wait on events, only on
+//             free pages, so weights stream while activations are not ready;
+//   waves 4-7 compute: one quarter of K each (GEMV) or one query head each
+//             (attention); the last of them to finish runs the epilogue.
+// Every wait is bounded (watchdog): on timeout the wave records
+// {cu, slot, event, value, target} and the workgroup drains and exits.
+#include <hip/hip_runtime.h>
+
+#include "mk_device.hpp"
+
+using namespace mkd;
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct Ctrl {
+  int ready_seq, done_seq, abort_flag, pad;
+  int slot_full[16];   // generation + 1 of the data in each ring slot (loaders -> compute)
+  int slot_freed[16];  // times each slot was released (compute -> loaders)
+  int slot_rel[16];    // compute waves done with the slot's current page
+  int arrive[4];       // compute waves done with instruction i (slot i % 4)
+  float part[4][kNW][kMaxRows];
+  float ssp[4][kNW];
+  float scratch[kNW][kScratch];
+};
+struct __attribute__((aligned(16))) Lds {
+  char ring[kNumPages][kPage];
+  Ctrl c;
+};
+
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)p);
+}
+// LDS flag access for the loader waves, in inline asm so that the compiler
+// does not put a vmcnt(0) wait (for the wave's own pending LDS-DMA) in front.
+__device__ __forceinline__ int lds_ld_asm(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ void lds_st_asm(uint32_t addr, int v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ int lds_load_acq(int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+__device__ __forceinline__ void lds_store_rel(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+
+enum { ErrEvent = 1, ErrPage = 2, ErrReady = 3, ErrDrain = 4, ErrFree = 5 };
+
+// The record belongs to the run whose epoch is in err[0]; the first failing
+// wave of that run fills it.
+__device__ void record_error(const KArgs& a, Lds& L, int kind, int slot, int ev, unsigned val, unsigned tgt) {
+  if (lane_id() == 0) {
+    unsigned old = __hip_atomic_load(&a.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old != a.epoch && __hip_atomic_compare_exchange_strong(&a.err[0], &old, a.epoch, __ATOMIC_RELAXED,
+                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+      a.err[1] = kind;
+      a.err[2] = blockIdx.x;
+      a.err[3] = slot;
+      a.err[4] = ev;
+      a.err[5] = val;
+      a.err[6] = tgt;
+    }
+    __hip_atomic_store(&L.c.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+__device__ __forceinline__ bool aborted(Lds& L) {
+  return __hip_atomic_load(&L.c.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+}
+
+// Wait until *p >= v (LDS, workgroup acquire), bounded.
+__device__ bool wait_lds_ge(const KArgs& a, Lds& L, int* p, int v, int kind, int slot) {
+  if (lds_load_acq(p) >= v) return true;
+  const unsigned long long t0 = now_ticks();
+  for (unsigned it = 0;; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    if (lds_load_acq(p) >= v) return true;
+    if ((it & 31) == 31) {
+      if (aborted(L)) return false;
+      if (now_ticks() - t0 > a.timeout_ticks) {
+        record_error(a, L, kind, slot, -1, (unsigned)lds_load_acq(p), (unsigned)v);
+        return false;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ const int* instr(const KArgs& a, int i) {
+  return a.queue + ((size_t)blockIdx.x * a.max_len + i) * 32;
+}
+
+// ---------------------------------------------------------------------------
+__device__ void controller(const KArgs& a, Lds& L) {
+  for (int i = 0; i < a.max_len; ++i) {
+    const int* ins = instr(a, i);
+    if (ins[WOpcode] == OpNoop) break;
+    if (ins[WWaitCnt]) {
+      const unsigned tgt = a.epoch * (unsigned)ins[WWaitTgt];
+      unsigned* ctr = a.counters + ins[WWaitEv];
+      unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int)(v - tgt) < 0) {
+        const unsigned long long t0 = now_ticks();
+        for (unsigned it = 0;; ++it) {
+          __builtin_amdgcn_s_sleep(1);
+          v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((int)(v - tgt) >= 0) break;
+          if ((it & 63) == 63) {
+            if (aborted(L) || __hip_atomic_load(&a.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
+              if (lane_id() == 0) __hip_atomic_store(&L.c.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              return;
+            }
+            if (now_ticks() - t0 > a.timeout_ticks) {
+              record_error(a, L, ErrEvent, i, ins[WWaitEv], v, tgt);
+              return;
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    if (a.trace && lane_id() == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 0] = now_ticks();
+    if (lane_id() == 0) lds_store_rel(&L.c.ready_seq, i + 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+__device__ void storer(const KArgs& a, Lds& L) {
+  for (int i = 0; i < a.max_len; ++i) {
+    const int* ins = instr(a, i);
+    if (ins[WOpcode] == OpNoop) break;
+    if (!wait_lds_ge(a, L, &L.c.done_seq, i + 1, ErrDrain, i)) return;
+    if (ins[WSigCnt] && lane_id() == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(a.counters + ins[WSigEv], (unsigned)ins[WSigInc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (a.trace && lane_id() == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 3] = now_ticks();
+  }
+}
+
+// ---------------------------------------------------------------------------
+__device__ void loader(const KArgs& a, Lds& L, int parity) {
+  const int lane = lane_id();
+  const uint32_t full_base = lds_addr(&L.c.slot_full[0]);
+  const uint32_t freed_base = lds_addr(&L.c.slot_freed[0]);
+  // issued-but-unpublished pages (oldest first); scalars, never indexed
+  int q0 = 0, q1 = 0, q2 = 0, npend = 0;
+  auto publish = [&](int sq) { lds_st_asm(full_base + 4 * (sq % kNumPages), sq / kNumPages + 1); };
+  auto publish_all = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (npend > 0) publish(q0);
+    if (npend > 1) publish(q1);
+    if (npend > 2) publish(q2);
+    npend = 0;
+  };
+  int seq = 0;
+  for (int i = 0; i < a.max_len; ++i) {
+    const int* ins = instr(a, i);
+    if (ins[WOpcode] == OpNoop) break;
+    const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
+    const Tile t = tile_info(ins, orow, a.c);
+    const char* dummy = t.len0 > 0 ? t.p0 : t.p1;
+    for (int pg = 0; pg < t.npages; ++pg, ++seq) {
+      if ((seq & 1) != parity) continue;
+      const int slot = seq % kNumPages, gen = seq / kNumPages;
+      if (lds_ld_asm(freed_base + 4 * slot) < gen) {
+        publish_all();
+        const unsigned long long t0 = now_ticks();
+        for (unsigned it = 0;; ++it) {
+          __builtin_amdgcn_s_sleep(1);
+          if (lds_ld_asm(freed_base + 4 * slot) >= gen) break;
+          if ((it & 31) == 31) {
+            if (aborted(L)) return;
+            if (now_ticks() - t0 > a.timeout_ticks) {
+              record_error(a, L, ErrFree, i, slot, 0, gen);
+              return;
+            }
+          }
+        }
+      }
+      char* dst = L.ring[slot];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int toff = pg * kPage + j * 1024 + lane * 16;
+        const char* src = dummy;
+        if (toff < t.len0)
+          src = t.p0 + toff;
+        else if (toff >= t.off1 && toff < t.off1 + t.len1)
+          src = t.p1 + (toff - t.off1);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
+      }
+      if (npend == 0) {
+        q0 = seq;
+      } else if (npend == 1) {
+        q1 = seq;
+      } else {
+        q2 = seq;
+      }
+      ++npend;
+      if (npend == 3) {
+        asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+        publish(q0);
+        q0 = q1;
+        q1 = q2;
+        npend = 2;
+      }
+    }
+  }
+  publish_all();
+}
+
+// ---------------------------------------------------------------------------
+template <int HD>
+__device__ void compute(const KArgs& a, Lds& L, int cw) {
+  const int lane = lane_id();
+  int seq = 0;
+  int act_row = -1;
+  Act act;
+  float act_ss = 0.f;
+  for (int i = 0; i < a.max_len; ++i) {
+    const int* ins = instr(a, i);
+    const int op = ins[WOpcode];
+    if (op == OpNoop) break;
+    const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
+    const Tile t = tile_info(ins, orow, a.c);
+    const int first = seq;
+    seq += t.npages;
+    if (!wait_lds_ge(a, L, &L.c.ready_seq, i + 1, ErrReady, i)) return;
+    if (!wait_lds_ge(a, L, &L.c.done_seq, i - 3, ErrDrain, i)) return;
+    for (int pg = 0; pg < t.npages; ++pg) {
+      const int sq = first + pg;
+      if (!wait_lds_ge(a, L, &L.c.slot_full[sq % kNumPages], sq / kNumPages + 1, ErrPage, i)) return;
+    }
+    if (cw == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 1] = now_ticks();
+    LdsSrc src;
+    src.ring = L.ring[0];
+    src.first_slot = first % kNumPages;
+    src.off1 = t.off1;
+    const int sl = i & 3;
+    const bool gemv = op == OpQkv || op == OpOproj || op == OpGateUp || op == OpDown || op == OpLmHead;
+    if (gemv) {
+      const GemvIn gi = gemv_input(ins, orow, a.c);
+      if (ins[WOpRow] != act_row) {
+        load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
+        act_ss = wave_sum(act.ss);
+        act_row = ins[WOpRow];
+      }
+      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L.c.part[sl][cw]);
+      if (lane == 0) L.c.ssp[sl][cw] = act_ss;
+    } else if (op == OpAttn) {
+      attn_wave<HD>(src, ins, orow, a.c, cw, L.c.scratch[cw], cw == 0);
+    } else if (op == OpCombine) {
+      combine_wave<HD>(ins, orow, a.c, cw);
+    } else if (op == OpArgmax) {
+      if (cw == 0) argmax_wave(ins, orow, a.c);
+    }
+    // release this tile's pages
+    for (int pg = 0; pg < t.npages; ++pg) {
+      const int sq = first + pg, slot = sq % kNumPages;
+      int old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(&L.c.slot_rel[slot], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __shfl(old, 0, 64);
+      if (old == kNW - 1 && lane == 0) {
+        __hip_atomic_store(&L.c.slot_rel[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        lds_store_rel(&L.c.slot_freed[slot], sq / kNumPages + 1);
+      }
+    }
+    // arrival; the last compute wave runs the epilogue and publishes completion
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(&L.c.arrive[sl], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __shfl(old, 0, 64);
+    if (old == kNW - 1) {
+      if (lane == 0) __hip_atomic_store(&L.c.arrive[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (gemv) gemv_epilogue(ins, orow, a.c, L.c.part[sl], L.c.ssp[sl]);
+      if (a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 2] = now_ticks();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) lds_store_rel(&L.c.done_seq, i + 1);
+    }
+  }
+}
+
+template <int HD>
+__global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
+  __shared__ Lds L;
+  {
+    int* c = (int*)&L.c;
+    const int n = (int)(sizeof(Ctrl) / 4);
+    for (int k = threadIdx.x; k < n; k += blockDim.x) c[k] = 0;
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6;
+  if (w == 0)
+    controller(a, L);
+  else if (w == 1)
+    storer(a, L);
+  else if (w < 4)
+    loader(a, L, w - 2);
+  else
+    compute<HD>(a, L, w - 4);
+}
+
+// ---------------------------------------------------------------------------
+// Layerwise: one launch per operator, one workgroup (4 waves) per tile.
+template <int HD>
+__global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int first_task) {
+  __shared__ float part[kNW][kMaxRows];
+  __shared__ float ssp[kNW];
+  __shared__ float scr[kNW][kScratch];
+  const int t = first_task + blockIdx.x;
+  const int* ins = a.queue + ((size_t)(t % num_cus) * a.max_len + t / num_cus) * 32;
+  const int cw = threadIdx.x >> 6, lane = lane_id();
+  const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
+  const Tile tl = tile_info(ins, orow, a.c);
+  GlbSrc src;
+  src.p0 = tl.p0;
+  src.p1 = tl.p1 ? tl.p1 : tl.p0;
+  const int op = ins[WOpcode];
+  if (op == OpQkv || op == OpOproj || op == OpGateUp || op == OpDown || op == OpLmHead) {
+    const GemvIn gi = gemv_input(ins, orow, a.c);
+    Act act;
+    load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
+    const float ss = wave_sum(act.ss);
+    gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw]);
+    if (lane == 0) ssp[cw] = ss;
+    __syncthreads();
+    if (cw == 0) gemv_epilogue(ins, orow, a.c, part, ssp);
+  } else if (op == OpAttn) {
+    attn_wave<HD>(src, ins, orow, a.c, cw, scr[cw], cw == 0);
+  } else if (op == OpCombine) {
+    combine_wave<HD>(ins, orow, a.c, cw);
+  } else if (op == OpArgmax) {
+    if (cw == 0) argmax_wave(ins, orow, a.c);
+  }
+}
+
+}  // namespace
+
+// ---- launch wrappers used by the host API ----------------------------------------
+namespace mk {
+
+hipError_t launch_megakernel(const KArgs& a, int num_cus, hipStream_t s) {
+  if (a.c.hd == 64) {
+    hipLaunchKernelGGL(mk_megakernel<64>, dim3(num_cus), dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(mk_megakernel<128>, dim3(num_cus), dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_layer(const KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s) {
+  if (a.c.hd == 64) {
+    hipLaunchKernelGGL(mk_layer_kernel<64>, dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
+  } else {
+    hipLaunchKernelGGL(mk_layer_kernel<128>, dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
+  }
+  return hipGetLastError();
+}
+
+hipError_t megakernel_occupancy(int hd, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, hd == 64 ? (const void*)mk_megakernel<64>
+                                                                               : (const void*)mk_megakernel<128>,
+                                                      512, 0);
+}
+
+}  // namespace mk

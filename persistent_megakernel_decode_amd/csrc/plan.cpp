@@ -1,0 +1,472 @@
+// Host-side tile planner (see plan.hpp for the rules and their sources).
+#include "plan.hpp"
+
+#include <algorithm>
+#include <map>
+#include <numeric>
+#include <set>
+
+namespace mk {
+
+namespace {
+
+std::array<int, kMaxDims> build_partition(const std::array<int, 3>& grid, const std::array<int, 3>& amap) {
+  std::array<int, kMaxDims> part{{1, 1, 1, 1}};
+  for (int a = 0; a < 3; ++a)
+    if (amap[a] >= 0) part[amap[a]] *= grid[a];
+  return part;
+}
+
+long lcm_l(long a, long b) { return a / std::gcd(a, b) * b; }
+
+enum Kind { kChain, kFork, kJoin, kMixed };
+
+// Op-specific payload words (instruction words 14..23) of task (x, y, z).
+void payload(const GraphOp& op, int x, int y, int z, const std::vector<int32_t>* kv_len, int32_t* w) {
+  (void)z;
+  const auto& p = op.p;
+  switch (op.kind) {
+    case kQkv:  // p0 = rows per tile
+      w[0] = y * p[0];
+      w[1] = p[0];
+      break;
+    case kAttn: {  // p0 = splits
+      int pos = (*kv_len)[x], lo, hi;
+      split_range(pos, p[0], z, &lo, &hi);
+      w[0] = lo;
+      w[1] = hi;
+      w[2] = pos;
+      break;
+    }
+    case kCombine:  // p0 = splits
+      w[0] = p[0];
+      break;
+    case kOproj:
+    case kLmHead:  // p0 = rows per tile, p1 = total rows
+    case kGateUp:  // p0 = outputs per tile, p1 = total outputs
+      w[0] = x * p[0];
+      w[1] = std::min(p[0], p[1] - x * p[0]);
+      break;
+    case kDown:  // p0 = rows per tile, p1 = total rows, p2 = K
+      w[0] = x * p[0];
+      w[1] = std::min(p[0], p[1] - x * p[0]);
+      w[2] = 0;
+      w[3] = p[2];
+      break;
+    case kArgmax:  // p0 = LM-head tiles
+      w[0] = p[0];
+      break;
+    default:
+      break;
+  }
+}
+
+}  // namespace
+
+std::string plan_graph(const std::vector<GraphOp>& ops, const std::vector<GraphEdge>& edges, int num_cus,
+                       const std::vector<int32_t>* kv_len, Plan* out) {
+  const int n_ops = (int)ops.size(), n_edges = (int)edges.size();
+  if (num_cus <= 0) return "num_cus must be positive";
+  for (const auto& op : ops)
+    for (int a = 0; a < 3; ++a)
+      if (op.grid[a] < 1) return "grid extents must be >= 1";
+  for (const auto& e : edges) {
+    if (e.prod < 0 || e.cons >= n_ops || e.prod >= e.cons) return "edges must go from a lower to a higher op index";
+    for (int a = 0; a < 3; ++a)
+      if (e.out_map[a] >= kMaxDims || e.in_map[a] >= kMaxDims || e.out_map[a] < -1 || e.in_map[a] < -1)
+        return "map entries must be -1..3";
+  }
+
+  // 1. per-edge gcd partition, with the ragged-alignment check
+  std::vector<std::array<int, kMaxDims>> evd(n_edges);
+  for (int i = 0; i < n_edges; ++i) {
+    const auto& e = edges[i];
+    auto pp = build_partition(ops[e.prod].grid, e.out_map);
+    auto cp = build_partition(ops[e.cons].grid, e.in_map);
+    for (int d = 0; d < kMaxDims; ++d) {
+      int g = std::gcd(pp[d], cp[d]);
+      if (e.has_extent && g > 1) {
+        for (int k = 1; k < g; ++k) {
+          long bp = std::min<long>((long)k * (pp[d] / g) * e.ptile[d], e.extent[d]);
+          long bc = std::min<long>((long)k * (cp[d] / g) * e.ctile[d], e.extent[d]);
+          if (bp != bc) {
+            g = 1;
+            break;
+          }
+        }
+      }
+      evd[i][d] = g;
+    }
+  }
+  auto whole = [&](int i) {
+    for (int d = 0; d < kMaxDims; ++d)
+      if (evd[i][d] != 1) return false;
+    return true;
+  };
+
+  // 2. residual stripping by full-dependency sets
+  std::vector<std::vector<int>> in_edges(n_ops);
+  for (int i = 0; i < n_edges; ++i) in_edges[edges[i].cons].push_back(i);
+  std::vector<std::set<int>> fd(n_ops);
+  std::vector<uint8_t> kept(n_edges, 1);
+  for (int c = 0; c < n_ops; ++c) {
+    for (int i : in_edges[c]) {
+      int p = edges[i].prod;
+      for (int j : in_edges[c]) {
+        if (j != i && edges[j].prod != p && fd[edges[j].prod].count(p)) {
+          kept[i] = 0;
+          break;
+        }
+      }
+    }
+    for (int i : in_edges[c]) {
+      if (!kept[i]) continue;
+      int x = edges[i].prod;
+      fd[c].insert(fd[x].begin(), fd[x].end());
+      if (whole(i)) fd[c].insert(x);
+    }
+  }
+
+  // 3. components of kept edges (edges sharing a producer or a consumer)
+  std::vector<int> parent(n_edges);
+  std::iota(parent.begin(), parent.end(), 0);
+  auto find = [&](int i) {
+    while (parent[i] != i) {
+      parent[i] = parent[parent[i]];
+      i = parent[i];
+    }
+    return i;
+  };
+  std::map<int, std::vector<int>> by_prod, by_cons;
+  for (int i = 0; i < n_edges; ++i)
+    if (kept[i]) {
+      by_prod[edges[i].prod].push_back(i);
+      by_cons[edges[i].cons].push_back(i);
+    }
+  auto unite = [&](const std::vector<int>& grp) {
+    for (size_t k = 1; k < grp.size(); ++k) {
+      int a = find(grp[0]), b = find(grp[k]);
+      if (a != b) parent[std::max(a, b)] = std::min(a, b);
+    }
+  };
+  for (auto& kv : by_prod) unite(kv.second);
+  for (auto& kv : by_cons) unite(kv.second);
+  std::map<int, std::vector<int>> comps;
+  for (int i = 0; i < n_edges; ++i)
+    if (kept[i]) comps[find(i)].push_back(i);
+  std::map<int, Kind> kind;
+  std::vector<int> comp_of_cons(n_ops, -1);
+  for (auto& kv : comps) {
+    const auto& es = kv.second;
+    std::set<int> prods, conss;
+    std::set<std::pair<int, int>> pairs;
+    for (int i : es) {
+      prods.insert(edges[i].prod);
+      conss.insert(edges[i].cons);
+      pairs.insert({edges[i].prod, edges[i].cons});
+    }
+    Kind k;
+    if (es.size() == 1) {
+      k = kChain;
+    } else if (pairs.size() != es.size()) {
+      k = kMixed;
+    } else if (prods.size() == 1 && std::all_of(conss.begin(), conss.end(), [&](int c) { return by_cons[c].size() == 1; })) {
+      k = kFork;
+    } else if (conss.size() == 1 && std::all_of(prods.begin(), prods.end(), [&](int p) { return by_prod[p].size() == 1; })) {
+      k = kJoin;
+    } else {
+      k = kMixed;
+    }
+    kind[kv.first] = k;
+    if (k == kMixed)
+      for (int i : es) evd[i] = {{1, 1, 1, 1}};
+    for (int c : conss) comp_of_cons[c] = kv.first;
+    if (*prods.rbegin() >= *conss.begin()) return "a component's producers must precede its consumers";
+  }
+
+  // 4. fork / join lcm normalization
+  for (auto& kv : comps) {
+    const auto& es = kv.second;
+    Kind k = kind[kv.first];
+    if (k != kFork && k != kJoin) continue;
+    const GraphOp& O = ops[k == kFork ? edges[es[0]].prod : edges[es[0]].cons];
+    for (int a = 0; a < 3; ++a) {
+      long Lx = 1;
+      for (int i : es) {
+        int d = k == kFork ? edges[i].out_map[a] : edges[i].in_map[a];
+        int ev = d >= 0 ? evd[i][d] : 1;
+        Lx = lcm_l(Lx, O.grid[a] / ev);
+      }
+      for (int i : es) {
+        int d = k == kFork ? edges[i].out_map[a] : edges[i].in_map[a];
+        if (d >= 0) evd[i][d] = (O.grid[a] % Lx == 0) ? (int)(O.grid[a] / Lx) : 1;
+      }
+    }
+  }
+
+  // 5. linearization
+  Plan& P = *out;
+  P = Plan();
+  std::map<std::array<int, 4>, int> task_of;
+  std::vector<uint8_t> emitted(n_ops, 0);
+  auto new_task = [&](int o, int x, int y, int z, int wait_ev) {
+    task_of[{{o, x, y, z}}] = (int)P.tasks.size();
+    P.tasks.push_back({{o, x, y, z}});
+    P.task_trigger.push_back(-1);
+    P.task_wait.push_back(wait_ev);
+  };
+  struct Slice {
+    int op;
+    std::array<int, 3> lo, hi;
+  };
+  // per-axis range of an op's tasks in the slice whose event index along tensor dim d is idx[d]
+  auto axis_slice = [&](int o, const std::array<int, 3>& amap, const std::array<int, kMaxDims>& ed,
+                        const std::array<int, kMaxDims>& idx) {
+    Slice s{o, {{0, 0, 0}}, {{0, 0, 0}}};
+    for (int a = 0; a < 3; ++a) {
+      int d = amap[a];
+      if (d >= 0 && ed[d] > 1) {
+        int span = ops[o].grid[a] / ed[d];
+        s.lo[a] = idx[d] * span;
+        s.hi[a] = (idx[d] + 1) * span;
+      } else {
+        s.lo[a] = 0;
+        s.hi[a] = ops[o].grid[a];
+      }
+    }
+    return s;
+  };
+  std::string err;
+  auto emit_event = [&](const std::vector<Slice>& cons, const std::vector<Slice>& prods) {
+    int eid = (int)P.event_first.size();
+    P.event_first.push_back((int)P.tasks.size());
+    for (const auto& s : cons)
+      for (int x = s.lo[0]; x < s.hi[0]; ++x)
+        for (int y = s.lo[1]; y < s.hi[1]; ++y)
+          for (int z = s.lo[2]; z < s.hi[2]; ++z) new_task(s.op, x, y, z, eid);
+    P.event_last.push_back((int)P.tasks.size());
+    uint32_t n = 0;
+    for (const auto& s : prods)
+      for (int x = s.lo[0]; x < s.hi[0]; ++x)
+        for (int y = s.lo[1]; y < s.hi[1]; ++y)
+          for (int z = s.lo[2]; z < s.hi[2]; ++z) {
+            int t = task_of.at({{s.op, x, y, z}});
+            if (P.task_trigger[t] != -1) err = "a task would trigger two events";
+            P.task_trigger[t] = eid;
+            ++n;
+          }
+    P.event_target.push_back(n);
+  };
+
+  for (int c = 0; c < n_ops; ++c) {
+    if (emitted[c]) continue;
+    const GraphOp& C = ops[c];
+    if (comp_of_cons[c] < 0) {
+      for (int x = 0; x < C.grid[0]; ++x)
+        for (int y = 0; y < C.grid[1]; ++y)
+          for (int z = 0; z < C.grid[2]; ++z) new_task(c, x, y, z, -1);
+      emitted[c] = 1;
+      continue;
+    }
+    int root = comp_of_cons[c];
+    const auto& es = comps[root];
+    Kind k = kind[root];
+    if (k == kChain || k == kJoin) {
+      int i0 = es[0];
+      std::array<int, 3> nev;
+      for (int a = 0; a < 3; ++a) {
+        int d = edges[i0].in_map[a];
+        nev[a] = d >= 0 ? evd[i0][d] : 1;
+      }
+      for (int ix = 0; ix < nev[0]; ++ix)
+        for (int iy = 0; iy < nev[1]; ++iy)
+          for (int iz = 0; iz < nev[2]; ++iz) {
+            std::array<int, 3> cidx{{ix, iy, iz}};
+            Slice cs{c, {{0, 0, 0}}, {{0, 0, 0}}};
+            for (int a = 0; a < 3; ++a) {
+              int span = C.grid[a] / nev[a];
+              cs.lo[a] = cidx[a] * span;
+              cs.hi[a] = (cidx[a] + 1) * span;
+            }
+            std::vector<Slice> prods;
+            for (int i : es) {
+              const auto& e = edges[i];
+              std::array<int, kMaxDims> idx{{0, 0, 0, 0}};
+              for (int a = 0; a < 3; ++a)
+                if (e.in_map[a] >= 0) idx[e.in_map[a]] = cidx[a];
+              prods.push_back(axis_slice(e.prod, e.out_map, evd[i], idx));
+            }
+            emit_event({cs}, prods);
+          }
+      emitted[c] = 1;
+    } else if (k == kFork) {
+      int p = edges[es[0]].prod;
+      const GraphOp& Pop = ops[p];
+      std::array<int, 3> nev;
+      for (int a = 0; a < 3; ++a) {
+        int d = edges[es[0]].out_map[a];
+        nev[a] = d >= 0 ? evd[es[0]][d] : 1;
+      }
+      std::vector<int> order(es.begin(), es.end());
+      std::stable_sort(order.begin(), order.end(), [&](int u, int v) { return edges[u].cons < edges[v].cons; });
+      for (int ix = 0; ix < nev[0]; ++ix)
+        for (int iy = 0; iy < nev[1]; ++iy)
+          for (int iz = 0; iz < nev[2]; ++iz) {
+            std::array<int, 3> pidx{{ix, iy, iz}};
+            Slice ps{p, {{0, 0, 0}}, {{0, 0, 0}}};
+            for (int a = 0; a < 3; ++a) {
+              int span = Pop.grid[a] / nev[a];
+              ps.lo[a] = pidx[a] * span;
+              ps.hi[a] = (pidx[a] + 1) * span;
+            }
+            std::vector<Slice> cons;
+            for (int i : order) {
+              const auto& e = edges[i];
+              std::array<int, kMaxDims> idx{{0, 0, 0, 0}};
+              for (int a = 0; a < 3; ++a)
+                if (e.out_map[a] >= 0) idx[e.out_map[a]] = pidx[a];
+              cons.push_back(axis_slice(e.cons, e.in_map, evd[i], idx));
+            }
+            emit_event(cons, {ps});
+          }
+      for (int i : es) emitted[edges[i].cons] = 1;
+    } else {
+      std::set<int> conss, prods;
+      for (int i : es) {
+        conss.insert(edges[i].cons);
+        prods.insert(edges[i].prod);
+      }
+      auto full = [&](int o) { return Slice{o, {{0, 0, 0}}, ops[o].grid}; };
+      std::vector<Slice> cs, ps;
+      for (int o : conss) cs.push_back(full(o));
+      for (int o : prods) ps.push_back(full(o));
+      emit_event(cs, ps);
+      for (int o : conss) emitted[o] = 1;
+    }
+    if (!err.empty()) return err;
+  }
+
+  // 6. placement and encoding
+  P.num_cus = num_cus;
+  P.num_tasks = (int)P.tasks.size();
+  P.num_events = (int)P.event_first.size();
+  P.max_len = std::max(1, ceil_div(P.num_tasks, num_cus));
+  P.queue.assign((size_t)num_cus * P.max_len * kWords, 0);
+  for (int t = 0; t < P.num_tasks; ++t) {
+    const auto& tk = P.tasks[t];
+    const GraphOp& op = ops[tk[0]];
+    int32_t* w = &P.queue[((size_t)(t % num_cus) * P.max_len + t / num_cus) * kWords];
+    w[kWOpcode] = op.opcode;
+    w[kWSpec] = op.spec;
+    w[kWOpRow] = tk[0];
+    if (P.task_wait[t] >= 0) {
+      w[kWWaitCnt] = 1;
+      w[kWWaitEv] = P.task_wait[t];
+      w[kWWaitTgt] = (int32_t)P.event_target[P.task_wait[t]];
+    }
+    if (P.task_trigger[t] >= 0) {
+      w[kWSigCnt] = 1;
+      w[kWSigEv] = P.task_trigger[t];
+      w[kWSigInc] = 1;
+    }
+    w[kWTask] = t;
+    w[kWLayer] = op.layer;
+    w[kWGx] = tk[1];
+    w[kWGy] = tk[2];
+    w[kWGz] = tk[3];
+    payload(op, tk[1], tk[2], tk[3], kv_len, w + kWPay);
+  }
+  P.op_table.assign((size_t)n_ops * 8, 0);
+  for (int o = 0; o < n_ops; ++o) {
+    int32_t* r = &P.op_table[(size_t)o * 8];
+    r[0] = ops[o].opcode;
+    r[1] = ops[o].spec;
+    r[2] = ops[o].layer;
+    r[3] = ops[o].grid[0];
+    r[4] = ops[o].grid[1];
+    r[5] = ops[o].grid[2];
+    r[6] = ops[o].grid[0] * ops[o].grid[1] * ops[o].grid[2];
+  }
+  P.edge_kept = kept;
+  return "";
+}
+
+void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, ModelOpts* o) {
+  if (!o->gemv_rows) o->gemv_rows = std::max(4, std::min(16, 32768 / m.hidden));
+  if (!o->gateup_outs) o->gateup_outs = std::max(1, o->gemv_rows / 2);
+  if (!o->down_rows) o->down_rows = std::max(1, std::min(16, 32768 / m.ffn));
+  if (!o->lm_rows) o->lm_rows = o->gemv_rows;
+  if (!o->attn_splits) {
+    int n = *std::max_element(kv_len.begin(), kv_len.end()) + 1;
+    int S = std::max(1, std::min(32, ceil_div(n, 64)));
+    while ((long)ceil_div(n, S) * m.head_dim * 4 > 65536) ++S;
+    o->attn_splits = S;
+  }
+}
+
+std::string model_graph(const ModelShape& m, int batch, const std::vector<int32_t>& kv_len, const ModelOpts& o,
+                        std::vector<GraphOp>* ops_out, std::vector<GraphEdge>* edges_out) {
+  const int H = m.hidden, nq = m.n_q_heads, nkv = m.n_kv_heads, hd = m.head_dim, F = m.ffn, V = m.vocab;
+  const int L = m.n_layers, B = batch;
+  const int hpg = nq / nkv, RPG = (hpg + 2) * hd;
+  const int R = o.gemv_rows, GU = o.gateup_outs, DR = o.down_rows, LR = o.lm_rows, S = o.attn_splits;
+  if (R <= 0 || GU <= 0 || DR <= 0 || LR <= 0 || S <= 0) return "tile options must be positive";
+  if (RPG % R || hd % R) return "gemv_rows must divide head_dim";
+  const int T_qkv = RPG / R, T_o = ceil_div(H, R), T_f = ceil_div(F, GU), T_d = ceil_div(H, DR),
+            T_v = ceil_div(V, LR);
+  const int spec = B > 4 ? 1 : 0;
+  auto& ops = *ops_out;
+  auto& edges = *edges_out;
+  ops.clear();
+  edges.clear();
+  auto add = [&](int opcode, std::array<int, 3> grid, int layer, int sp, std::array<int, 8> p) {
+    GraphOp op;
+    op.opcode = opcode;
+    op.kind = opcode;
+    op.grid = grid;
+    op.layer = layer;
+    op.spec = sp;
+    op.p = p;
+    ops.push_back(op);
+    return (int)ops.size() - 1;
+  };
+  auto edge = [&](int p, int c, std::array<int, 3> om, std::array<int, 3> im, std::array<int, 4> ext,
+                  std::array<int, 4> pt, std::array<int, 4> ct) {
+    GraphEdge e;
+    e.prod = p;
+    e.cons = c;
+    e.out_map = om;
+    e.in_map = im;
+    e.has_extent = true;
+    e.extent = ext;
+    e.ptile = pt;
+    e.ctile = ct;
+    edges.push_back(e);
+  };
+  const std::array<int, 3> none{{-1, -1, -1}};
+  int prev_down = -1;
+  for (int l = 0; l < L; ++l) {
+    int q = add(kQkv, {{nkv, T_qkv, 1}}, l, spec, {{R}});
+    int a = add(kAttn, {{B, nkv, S}}, l, 0, {{S}});
+    int c = add(kCombine, {{B, nkv, 1}}, l, 0, {{S}});
+    int op = add(kOproj, {{T_o, 1, 1}}, l, spec, {{R, H}});
+    int g = add(kGateUp, {{T_f, 1, 1}}, l, spec, {{GU, F}});
+    int d = add(kDown, {{T_d, 1, 1}}, l, spec, {{DR, H, F}});
+    if (prev_down >= 0) edge(prev_down, q, {{1, -1, -1}}, none, {{B, H, 1, 1}}, {{1, DR, 1, 1}}, {{1, H, 1, 1}});
+    edge(q, a, {{1, 2, -1}}, {{0, 1, -1}}, {{B, nkv, RPG, 1}}, {{B, 1, R, 1}}, {{1, 1, RPG, 1}});
+    edge(a, c, {{0, 1, 2}}, {{0, 1, -1}}, {{B, nkv, S, 1}}, {{1, 1, 1, 1}}, {{1, 1, S, 1}});
+    edge(c, op, {{0, 1, -1}}, none, {{B, nkv, 1, 1}}, {{1, 1, 1, 1}}, {{B, nkv, 1, 1}});
+    if (prev_down >= 0) edge(prev_down, op, {{1, -1, -1}}, none, {{B, H, 1, 1}}, {{1, DR, 1, 1}}, {{1, H, 1, 1}});
+    edge(op, g, {{1, -1, -1}}, none, {{B, H, 1, 1}}, {{1, R, 1, 1}}, {{1, H, 1, 1}});
+    edge(op, d, {{1, -1, -1}}, none, {{B, H, 1, 1}}, {{1, R, 1, 1}}, {{1, H, 1, 1}});
+    edge(g, d, {{1, -1, -1}}, none, {{B, F, 1, 1}}, {{1, GU, 1, 1}}, {{1, F, 1, 1}});
+    prev_down = d;
+  }
+  int lm = add(kLmHead, {{T_v, 1, 1}}, L, spec, {{LR, V}});
+  int am = add(kArgmax, {{B, 1, 1}}, L, 0, {{T_v}});
+  edge(prev_down, lm, {{1, -1, -1}}, none, {{B, H, 1, 1}}, {{1, DR, 1, 1}}, {{1, H, 1, 1}});
+  edge(lm, am, {{1, -1, -1}}, {{0, -1, -1}}, {{B, T_v, 1, 1}}, {{B, 1, 1, 1}}, {{1, T_v, 1, 1}});
+  return "";
+}
+
+}  // namespace mk

@@ -1,0 +1,88 @@
+// Host-side tile planner of the persistent megakernel (no HIP dependency).
+//
+// Operator DAG -> tasks (tiles) -> events -> linearized task order -> static
+// per-CU queues of 32-word instructions.  The rules follow the MPK internals
+// notes (dpshk.com), "fine-grained pipeline" (per-dimension gcd of producer
+// and consumer partitions), "handling fork producer" / "handling join
+// consumer" (lcm normalization) and "building the SM-level DAG"
+// (linearization: each event's successors are created contiguously), and the
+// MegaRTP article (tahou.com), section 4 "KernelPlan" (round-robin placement
+// into a fixed [num_CUs, max_len, 32] int32 tensor padded with NoOps).
+#pragma once
+#include <array>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace mk {
+
+constexpr int kWords = 32;
+constexpr int kMaxDims = 4;
+
+// instruction words
+enum : int {
+  kWOpcode = 0, kWSpec = 1, kWOpRow = 2, kWWaitCnt = 3, kWWaitEv = 4, kWWaitTgt = 5,
+  kWSigCnt = 6, kWSigEv = 7, kWSigInc = 8, kWTask = 9, kWLayer = 10, kWGx = 11, kWGy = 12, kWGz = 13,
+  kWPay = 14, kNPay = 10
+};
+
+// opcodes of the Llama-family decode step
+enum : int { kNoop = 0, kQkv = 1, kAttn = 2, kCombine = 3, kOproj = 4, kGateUp = 5, kDown = 6, kLmHead = 7, kArgmax = 8 };
+
+struct GraphOp {
+  int opcode = 0, spec = 0, layer = 0;
+  std::array<int, 3> grid{{1, 1, 1}};
+  // payload words of task (x, y, z); filled by the model builder (kind-specific)
+  int kind = 0;          // 0 = no payload, else opcode-specific rule
+  std::array<int, 8> p{};  // parameters of the payload rule
+};
+
+struct GraphEdge {
+  int prod = 0, cons = 0;
+  std::array<int, 3> out_map{{-1, -1, -1}}, in_map{{-1, -1, -1}};
+  bool has_extent = false;
+  std::array<int, kMaxDims> extent{{1, 1, 1, 1}}, ptile{{1, 1, 1, 1}}, ctile{{1, 1, 1, 1}};
+};
+
+struct Plan {
+  int num_cus = 0, max_len = 0, num_tasks = 0, num_events = 0;
+  std::vector<int32_t> queue;  // [num_cus][max_len][32]
+  std::vector<uint32_t> event_target;
+  std::vector<int32_t> event_first, event_last;
+  std::vector<int32_t> task_trigger, task_wait;
+  std::vector<std::array<int, 4>> tasks;  // (op, x, y, z)
+  std::vector<int32_t> op_table;          // [num_ops][8]
+  std::vector<uint8_t> edge_kept;
+};
+
+// Returns "" on success, else an error message.  'payload' callback encodes the
+// op-specific words of a task.
+std::string plan_graph(const std::vector<GraphOp>& ops, const std::vector<GraphEdge>& edges, int num_cus,
+                       const std::vector<int32_t>* kv_len, Plan* out);
+
+struct ModelShape {
+  int n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+};
+struct ModelOpts {
+  int num_cus, gemv_rows, gateup_outs, down_rows, lm_rows, attn_splits;
+};
+
+// Fill 0 fields with the defaults (tiles of about 64 KiB of bf16 weights).
+void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, ModelOpts* o);
+
+// Operator DAG of one Llama-family decode step, in topological order.
+std::string model_graph(const ModelShape& m, int batch, const std::vector<int32_t>& kv_len, const ModelOpts& o,
+                        std::vector<GraphOp>* ops, std::vector<GraphEdge>* edges);
+
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// positions [lo, hi) of split s when pos + 1 positions are cut into S splits
+inline void split_range(int pos, int S, int s, int* lo, int* hi) {
+  int n = pos + 1, sz = ceil_div(n, S);
+  int l = s * sz < n ? s * sz : n;
+  int h = l + sz < n ? l + sz : n;
+  *lo = l;
+  *hi = h;
+}
+
+}  // namespace mk

@@ -1,0 +1,120 @@
+"""CPU tests of the HIP library (no GPU): it loads, exports every symbol the
+header declares, rejects bad arguments, and its C++ planner reproduces the
+reference planner (oracle/planner.py) bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import planner as P
+
+mk = pytest.importorskip("persistent_megakernel_decode_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "mk.h")).read()
+    declared = set(re.findall(r"\b(mk_[a-z_]+)\s*\(", hdr))
+    assert {"mk_plan_build", "mk_run", "mk_run_layerwise"} <= declared
+    L = mk.lib()
+    for name in sorted(declared):
+        assert hasattr(L, name), name
+    assert set(mk.EXPORTED) == declared
+    assert L.mk_abi_version() == mk.MK_ABI_VERSION
+
+
+def _compare(lib_plan, ref):
+    ex = lib_plan.export()
+    assert ex["num_cus"] == ref.num_cus and ex["max_len"] == ref.max_len
+    assert ex["num_tasks"] == ref.num_tasks and ex["num_events"] == ref.num_events
+    assert np.array_equal(ex["queue"], np.asarray(ref.queue, dtype=np.int32))
+    assert ex["event_target"].tolist() == list(ref.event_target)
+    assert ex["event_first"].tolist() == list(ref.event_first)
+    assert ex["event_last"].tolist() == list(ref.event_last)
+    assert ex["task_trigger"].tolist() == list(ref.trigger)
+    assert ex["task_wait"].tolist() == list(ref.wait)
+    assert ex["edge_kept"].astype(bool).tolist() == list(ref.kept)
+    assert ex["op_table"].tolist() == P.op_table(ref)
+    return ex
+
+
+@pytest.mark.parametrize("name,overrides,num_cus,opts", [
+    ("tiny", {}, 256, {}),
+    ("tiny", {}, 37, dict(attn_splits=5)),
+    ("tiny", dict(kv_len=0), 64, {}),
+    ("tiny", dict(ffn=688 + 32, vocab=4100, kv_len=999), 100, {}),  # ragged FFN and vocab tails
+    ("tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128), 256, {}),
+    ("llama1b", {}, 256, {}),
+    ("llama1b", {}, 148, dict(gemv_rows=8, down_rows=8)),
+    ("qwen3_8b", {}, 256, {}),
+])
+def test_cpp_planner_matches_reference(name, overrides, num_cus, opts):
+    cfg = synth.config(name, **overrides)
+    kv = synth.kv_lengths(cfg)
+    cap = synth.kv_capacity(kv)
+    ref = P.plan_model(cfg, cfg["batch"], kv, dict(num_cus=num_cus, **opts))
+    plan = mk.Plan.build(cfg, cfg["batch"], kv, cap, num_cus=num_cus, **opts)
+    try:
+        _compare(plan, ref)
+    finally:
+        plan.free()
+
+
+def _graph_via_lib(ops, edges, num_cus):
+    lops = [(op.opcode, op.grid, op.spec, op.layer) for op in ops]
+    ledges = [(e.prod, e.cons, e.out_map, e.in_map, e.extent, e.ptile, e.ctile) for e in edges]
+    return mk.Plan.graph(lops, ledges, num_cus)
+
+
+def test_cpp_planner_matches_reference_on_page_examples():
+    from tests.test_planner_pins import demo_graph, megasim_layers
+    cases = [
+        ([P.Op("F", 1, (4,)), P.Op("A", 2, (4,)), P.Op("B", 3, (2,)), P.Op("G", 4, (4,))],
+         [P.Edge(0, 1, (0,), (0,)), P.Edge(0, 2, (0,), (0,)), P.Edge(1, 3, (0,), (0,)), P.Edge(2, 3, (0,), (0,))], 8),
+        demo_graph() + (6,),
+        megasim_layers(3) + (132,),
+        ([P.Op("t", 1, (732,))], [], 148),
+        # a mixed fork/join component (falls back to one event)
+        ([P.Op("A", 1, (4,)), P.Op("B", 2, (8,)), P.Op("C", 3, (2,)), P.Op("D", 4, (8,)), P.Op("E", 5, (4,))],
+         [P.Edge(0, 1, (0,), (0,)), P.Edge(0, 2, (0,), (0,)), P.Edge(1, 3, (0,), (0,)), P.Edge(1, 4, (0,), (0,)),
+          P.Edge(2, 4, (0,), (0,))], 16),
+    ]
+    for prod in (128,):
+        for cons in (128, 64, 1, 127):
+            cases.append(([P.Op("P", 1, (prod,)), P.Op("C", 2, (cons,))], [P.Edge(0, 1, (0,), (0,))], 256))
+    for ops, edges, C in cases:
+        ref = P.plan_graph(ops, edges, C)
+        plan = _graph_via_lib(ops, edges, C)
+        try:
+            _compare(plan, ref)
+        finally:
+            plan.free()
+
+
+def test_plan_build_rejects_bad_arguments():
+    cfg = synth.config("tiny")
+    with pytest.raises(mk.MKError) as e:
+        mk.Plan.build(cfg, 1, [200], 100, num_cus=8)  # kv_len + 1 > capacity
+    assert e.value.status == mk.MK_E_UNSUPPORTED
+    with pytest.raises(mk.MKError) as e:
+        mk.Plan.build(dict(cfg, head_dim=96), 1, [10], 100, num_cus=8)
+    assert e.value.status == mk.MK_E_UNSUPPORTED
+    d = mk.model_desc(cfg, 100)
+    d.struct_size = 4
+    h = ctypes.c_void_p()
+    kv = np.array([10], np.int32)
+    assert mk.lib().mk_plan_build(ctypes.byref(d), 1, kv.ctypes.data, None, ctypes.byref(h)) == mk.MK_E_INVALID
+    assert mk.lib().mk_plan_build(None, 1, kv.ctypes.data, None, ctypes.byref(h)) == mk.MK_E_INVALID
+    assert b"null" in mk.lib().mk_last_error()
+    # a graph-only plan cannot run
+    g = mk.Plan.graph([(1, (4,))], [], 4)
+    w = mk.Weights()
+    assert mk.lib().mk_run(g._h, ctypes.byref(w), None, None, None) == mk.MK_E_STATE
+    g.free()
+    # an edge that goes backwards is rejected
+    with pytest.raises(mk.MKError):
+        mk.Plan.graph([(1, (4,)), (2, (4,))], [(1, 0, (0,), (0,), None, None, None)], 4)
