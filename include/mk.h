@@ -209,8 +209,10 @@ mk_status mk_plan_check(mk_plan* plan, void* stream, mk_check* out);
 
 /* Per-instruction timestamps of the next mk_run calls (enable=1) or none
  * (enable=0).  mk_plan_trace copies the last run's trace to host memory:
- * uint64 [num_cus][max_len][4] = (event satisfied, compute start, compute end,
- * signalled), in ticks of 'ticks_per_us'. */
+ * uint64 [num_cus][max_len][16] = (event satisfied, compute start, compute end,
+ * signalled, first page DMA issued, last page landed in LDS, compute wave 0
+ * activation ready, 0, then per compute wave 0..3 its start and its
+ * pages-released time), in ticks of 'ticks_per_us'. */
 mk_status mk_plan_set_trace(mk_plan* plan, int32_t enable);
 mk_status mk_plan_trace(mk_plan* plan, void* stream, uint64_t* host_out, size_t bytes, double* ticks_per_us);
 

@@ -212,7 +212,7 @@ class Plan:
 
     def trace(self, stream=None):
         ex = self.export()
-        out = np.zeros((ex["num_cus"], ex["max_len"], 4), dtype=np.uint64)
+        out = np.zeros((ex["num_cus"], ex["max_len"], 16), dtype=np.uint64)
         tpu = ctypes.c_double()
         _check(lib().mk_plan_trace(self._h, vp(stream.cuda_stream if stream is not None else current_stream()),
                                    out.ctypes.data, out.nbytes, ctypes.byref(tpu)))

@@ -304,7 +304,7 @@ static mk_status ensure_device(mk_plan* p) {
   if (p->num_cus > ncu || occ < 1)
     return fail(MK_E_UNSUPPORTED, "the persistent grid (" + std::to_string(p->num_cus) + " workgroups) cannot be co-resident on " +
                                       std::to_string(ncu) + " CUs");
-  const size_t qbytes = p->P.queue.size() * 4, ebytes = (size_t)std::max(1, p->P.num_events) * 4;
+  const size_t qbytes = p->P.queue.size() * 4, ebytes = (size_t)std::max(1, p->P.num_events) * 4 * mkd::kCtrStride;
   HIPCHK(hipMalloc(&p->d_queue, qbytes), "hipMalloc queue");
   HIPCHK(hipMalloc(&p->d_counters, ebytes), "hipMalloc counters");
   HIPCHK(hipMalloc(&p->d_err, 64), "hipMalloc err");
@@ -447,13 +447,13 @@ mk_status mk_run(mk_plan* p, const mk_weights* w, void* kv_cache, const void* to
   st = bind_operands(p, w, kv_cache, tokens, s);
   if (st != MK_OK) return st;
   if (p->need_reset) {
-    HIPCHK(hipMemsetAsync(p->d_counters, 0, (size_t)std::max(1, p->P.num_events) * 4, s), "reset counters");
+    HIPCHK(hipMemsetAsync(p->d_counters, 0, (size_t)std::max(1, p->P.num_events) * 4 * mkd::kCtrStride, s), "reset counters");
     p->epoch = 0;
     p->need_reset = false;
   }
   p->epoch += 1;
   if (p->epoch == 0) p->epoch = 1;  // 0 marks "no error" in the watchdog record
-  if (p->trace_on) HIPCHK(hipMemsetAsync(p->d_trace, 0, (size_t)p->num_cus * p->P.max_len * 32, s), "clear trace");
+  if (p->trace_on) HIPCHK(hipMemsetAsync(p->d_trace, 0, (size_t)p->num_cus * p->P.max_len * mkd::kTraceWords * 8, s), "clear trace");
   HIPCHK(mk::launch_megakernel(kargs(p), p->num_cus, s), "megakernel launch");
   return MK_OK;
 }
@@ -517,14 +517,14 @@ mk_status mk_plan_check(mk_plan* p, void* stream, mk_check* out) {
   std::memset(out, 0, sizeof(*out));
   if (p->graph_only || !p->uploaded) return fail(MK_E_STATE, "the plan has not run");
   HIPCHK(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
-  std::vector<uint32_t> ctr(std::max(1, p->P.num_events));
+  std::vector<uint32_t> ctr((size_t)std::max(1, p->P.num_events) * mkd::kCtrStride);
   uint32_t err[16];
   HIPCHK(hipMemcpy(ctr.data(), p->d_counters, ctr.size() * 4, hipMemcpyDeviceToHost), "read counters");
   HIPCHK(hipMemcpy(err, p->d_err, 64, hipMemcpyDeviceToHost), "read err");
   out->epoch = p->epoch;
   int bad = 0;
   for (int e = 0; e < p->P.num_events; ++e)
-    if (ctr[e] != p->epoch * p->P.event_target[e]) ++bad;
+    if (ctr[(size_t)e * mkd::kCtrStride] != p->epoch * p->P.event_target[e]) ++bad;
   out->bad_counters = bad;
   out->counters_ok = bad == 0;
   if (err[0] != 0 && err[0] == p->epoch) {
@@ -547,7 +547,7 @@ mk_status mk_plan_set_trace(mk_plan* p, int32_t enable) {
   if (!p) return fail(MK_E_INVALID, "null plan");
   if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
   if (enable && !p->d_trace) {
-    HIPCHK(hipMalloc(&p->d_trace, (size_t)p->num_cus * p->P.max_len * 32), "hipMalloc trace");
+    HIPCHK(hipMalloc(&p->d_trace, (size_t)p->num_cus * p->P.max_len * mkd::kTraceWords * 8), "hipMalloc trace");
   }
   p->trace_on = enable != 0;
   return MK_OK;
@@ -556,7 +556,7 @@ mk_status mk_plan_set_trace(mk_plan* p, int32_t enable) {
 mk_status mk_plan_trace(mk_plan* p, void* stream, uint64_t* host_out, size_t bytes, double* ticks_per_us) {
   g_err.clear();
   if (!p || !host_out || !ticks_per_us) return fail(MK_E_INVALID, "null argument");
-  const size_t need = (size_t)p->num_cus * p->P.max_len * 32;
+  const size_t need = (size_t)p->num_cus * p->P.max_len * mkd::kTraceWords * 8;
   if (!p->d_trace) return fail(MK_E_STATE, "tracing was never enabled");
   if (bytes < need) return fail(MK_E_INVALID, "host buffer too small");
   HIPCHK(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");

@@ -5,6 +5,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// LDS (address space 3): device code reaches shared memory only through such
+// pointers so that every access is a ds_* instruction, never a flat access
+// that would queue in the vector-memory pipeline behind the page DMA.
+#define LDS __attribute__((address_space(3)))
+// Global memory (address space 1): pointers taken from the operand table are
+// cast to it so loads and stores are global_* (vmcnt only), not flat_*.
+#define GLB __attribute__((address_space(1)))
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 namespace mkd {
 
 // ---- instruction words (same layout as the host planner) -------------------
@@ -40,6 +51,8 @@ constexpr int kNW = 4;        // compute waves per workgroup (K split / one q he
 constexpr int kMaxRows = 16;  // weight rows per GEMV tile
 constexpr int kMaxChunks = 6; // 16-byte activation chunks per lane (K / (8 * kNW * 64))
 constexpr int kScratch = 512; // floats of per-compute-wave scratch
+constexpr int kTraceWords = 16; // timestamps per traced instruction
+constexpr int kCtrStride = 64;  // u32 words between event counters: one 256-byte line each
 
 struct Consts {
   int H, nq, nkv, hd, F, V, L, B, cap, hpg, RPG, S, T_v, qk_norm;
@@ -51,7 +64,7 @@ struct KArgs {
   const uint64_t* optab;      // [num_ops][16]
   unsigned* counters;         // [num_events]
   unsigned* err;              // watchdog record [8]
-  unsigned long long* trace;  // [C][max_len][4] or null
+  unsigned long long* trace;  // [C][max_len][kTraceWords] or null
   int max_len;
   unsigned epoch;
   unsigned long long timeout_ticks;
@@ -83,10 +96,23 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Data one compute unit writes for another within a step is stored agent-coherent
+// (a relaxed agent-scope atomic store: written through the XCD's L2), so a
+// producer never needs the L2 write-back that an agent-scope release fence
+// performs -- under full HBM load that write-back costs tens of microseconds.
+// The producer then only waits for its stores to complete before its counter
+// atomic; consumers still acquire.
+__device__ __forceinline__ void st_agent(GLB float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(GLB int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // token id of sequence 0, clamped into [0, vocab) so that a bad id cannot index
 // outside the embedding
 __device__ __forceinline__ int token0(const uint64_t tokens_ptr, int V) {
-  int t = ((const int*)tokens_ptr)[0];
+  int t = ((const GLB int*)tokens_ptr)[0];
   return t < 0 ? 0 : (t >= V ? V - 1 : t);
 }
 __device__ __forceinline__ int ld_word(const int* ins, int w) { return ins[w]; }
@@ -98,8 +124,8 @@ __device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amd
 // scalars (no arrays) so that nothing is indexed at run time and everything
 // stays in registers.
 struct Tile {
-  const char* p0;
-  const char* p1;
+  const GLB char* p0;
+  const GLB char* p1;
   int len0, off1, len1;
   int bytes, npages;
 };
@@ -117,29 +143,29 @@ __device__ inline Tile tile_info(const int* ins, const uint64_t* orow, const Con
       const int g = ins[WGx], row0 = ins[WPay], nrows = ins[WPay + 1];
       const int qrows = c.hpg * c.hd;
       if (row0 < qrows)
-        t.p0 = (const char*)orow[QkvWq] + ((size_t)g * qrows + row0) * c.H * 2;
+        t.p0 = (const GLB char*)orow[QkvWq] + ((size_t)g * qrows + row0) * c.H * 2;
       else if (row0 < qrows + c.hd)
-        t.p0 = (const char*)orow[QkvWk] + ((size_t)g * c.hd + row0 - qrows) * c.H * 2;
+        t.p0 = (const GLB char*)orow[QkvWk] + ((size_t)g * c.hd + row0 - qrows) * c.H * 2;
       else
-        t.p0 = (const char*)orow[QkvWv] + ((size_t)g * c.hd + row0 - qrows - c.hd) * c.H * 2;
+        t.p0 = (const GLB char*)orow[QkvWv] + ((size_t)g * c.hd + row0 - qrows - c.hd) * c.H * 2;
       t.len0 = nrows * c.H * 2;
       break;
     }
     case OpOproj:
-      t.p0 = (const char*)orow[OWo] + (size_t)ins[WPay] * c.nq * c.hd * 2;
+      t.p0 = (const GLB char*)orow[OWo] + (size_t)ins[WPay] * c.nq * c.hd * 2;
       t.len0 = ins[WPay + 1] * c.nq * c.hd * 2;
       break;
     case OpGateUp:
-      t.p0 = (const char*)orow[GuWg] + (size_t)ins[WPay] * c.H * 2;
-      t.p1 = (const char*)orow[GuWu] + (size_t)ins[WPay] * c.H * 2;
+      t.p0 = (const GLB char*)orow[GuWg] + (size_t)ins[WPay] * c.H * 2;
+      t.p1 = (const GLB char*)orow[GuWu] + (size_t)ins[WPay] * c.H * 2;
       t.len0 = t.len1 = ins[WPay + 1] * c.H * 2;
       break;
     case OpDown:
-      t.p0 = (const char*)orow[DnW] + (size_t)ins[WPay] * c.F * 2;
+      t.p0 = (const GLB char*)orow[DnW] + (size_t)ins[WPay] * c.F * 2;
       t.len0 = ins[WPay + 1] * c.F * 2;
       break;
     case OpLmHead:
-      t.p0 = (const char*)orow[LmW] + (size_t)ins[WPay] * c.H * 2;
+      t.p0 = (const GLB char*)orow[LmW] + (size_t)ins[WPay] * c.H * 2;
       t.len0 = ins[WPay + 1] * c.H * 2;
       break;
     case OpAttn: {
@@ -147,8 +173,8 @@ __device__ inline Tile tile_info(const int* ins, const uint64_t* orow, const Con
       int nk = (hi < pos ? hi : pos) - lo;
       if (nk < 0) nk = 0;
       const size_t base = (((size_t)b * c.nkv + g) * c.cap + lo) * c.hd * 2;
-      t.p0 = (const char*)orow[AttnK] + base;
-      t.p1 = (const char*)orow[AttnV] + base;
+      t.p0 = (const GLB char*)orow[AttnK] + base;
+      t.p1 = (const GLB char*)orow[AttnV] + base;
       t.len0 = t.len1 = nk * c.hd * 2;
       break;
     }
@@ -164,24 +190,30 @@ __device__ inline Tile tile_info(const int* ins, const uint64_t* orow, const Con
 // ---- weight sources -------------------------------------------------------------
 // LDS page ring: page j of the tile lives in ring slot (first + j) mod kNumPages.
 struct LdsSrc {
-  const char* ring;
+  const LDS char* ring;
   int first_slot;
   int off1;
-  __device__ __forceinline__ const char* at(int seg, int o) const {
+  __device__ __forceinline__ const LDS char* at(int seg, int o) const {
     const int t = (seg ? off1 : 0) + o;
     int slot = first_slot + (t >> 14);
     if (slot >= kNumPages) slot -= kNumPages;
     return ring + slot * kPage + (t & (kPage - 1));
   }
-  __device__ __forceinline__ uint4 ld16(int seg, int o) const { return *(const uint4*)at(seg, o); }
-  __device__ __forceinline__ uint16_t ld2(int seg, int o) const { return *(const uint16_t*)at(seg, o); }
+  __device__ __forceinline__ uint4 ld16(int seg, int o) const {
+    const u32x4 v = *(const LDS u32x4*)at(seg, o);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  __device__ __forceinline__ uint16_t ld2(int seg, int o) const { return *(const LDS uint16_t*)at(seg, o); }
 };
 // Straight from device memory (layerwise kernels).
 struct GlbSrc {
-  const char* p0;
-  const char* p1;
-  __device__ __forceinline__ uint4 ld16(int seg, int o) const { return *(const uint4*)((seg ? p1 : p0) + o); }
-  __device__ __forceinline__ uint16_t ld2(int seg, int o) const { return *(const uint16_t*)((seg ? p1 : p0) + o); }
+  const GLB char* p0;
+  const GLB char* p1;
+  __device__ __forceinline__ uint4 ld16(int seg, int o) const {
+    const u32x4 v = *(const GLB u32x4*)((seg ? p1 : p0) + o);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  __device__ __forceinline__ uint16_t ld2(int seg, int o) const { return *(const GLB uint16_t*)((seg ? p1 : p0) + o); }
 };
 
 // ---- activations of a GEMV tile ---------------------------------------------
@@ -194,53 +226,71 @@ struct Act {
   int nc;
 };
 
-// src: fp32 vector (xf) or a bf16 row (xb); nw: bf16 norm weight or null
-__device__ inline void load_act(Act& a, int K, int cw, const float* xf, const uint16_t* xb, const uint16_t* nw) {
+// src: fp32 vector (xf) or a bf16 row (xb); nw: bf16 norm weight or null.
+// All loads are issued before any is used (addresses of chunks outside the
+// wave's range are clamped to chunk 0 and their values zeroed afterwards).
+__device__ inline void load_act(Act& a, int K, int cw, const GLB float* xf, const GLB uint16_t* xb,
+                                const GLB uint16_t* nw) {
   const int lane = lane_id();
   const int nch = K / 8;                    // 16-byte chunks of bf16 weights per row
   const int cpw = (nch + kNW - 1) / kNW;    // chunks per wave (the last wave may get fewer)
   const int base = cw * cpw;
   a.nc = (cpw + 63) / 64;
-  a.ss = 0.f;
+  f32x4 x0[kMaxChunks], x1[kMaxChunks];
+  u32x4 xr[kMaxChunks], wr[kMaxChunks];
+  bool ok[kMaxChunks];
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
     const int ch = lane + 64 * j;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a.x[j][e] = 0.f;
-    if (j < a.nc && ch < cpw && base + ch < nch) {
-      const int k0 = (base + ch) * 8;
-      float v[8];
+    ok[j] = j < a.nc && ch < cpw && base + ch < nch;
+    const int k0 = (ok[j] ? base + ch : 0) * 8;
+    if (j < a.nc) {
       if (xf) {
-        float4 u0 = *(const float4*)(xf + k0), u1 = *(const float4*)(xf + k0 + 4);
-        v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w; v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+        x0[j] = *(const GLB f32x4*)(xf + k0);
+        x1[j] = *(const GLB f32x4*)(xf + k0 + 4);
       } else {
-        uint4 u = *(const uint4*)(xb + k0);
-        v[0] = bf16lo(u.x); v[1] = bf16hi(u.x); v[2] = bf16lo(u.y); v[3] = bf16hi(u.y);
-        v[4] = bf16lo(u.z); v[5] = bf16hi(u.z); v[6] = bf16lo(u.w); v[7] = bf16hi(u.w);
+        xr[j] = *(const GLB u32x4*)(xb + k0);
       }
-      float w[8];
+      if (nw) wr[j] = *(const GLB u32x4*)(nw + k0);
+    }
+  }
+  a.ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) {
+    float v[8], w[8];
+    if (j < a.nc) {
+      if (xf) {
+        v[0] = x0[j].x; v[1] = x0[j].y; v[2] = x0[j].z; v[3] = x0[j].w;
+        v[4] = x1[j].x; v[5] = x1[j].y; v[6] = x1[j].z; v[7] = x1[j].w;
+      } else {
+        v[0] = bf16lo(xr[j].x); v[1] = bf16hi(xr[j].x); v[2] = bf16lo(xr[j].y); v[3] = bf16hi(xr[j].y);
+        v[4] = bf16lo(xr[j].z); v[5] = bf16hi(xr[j].z); v[6] = bf16lo(xr[j].w); v[7] = bf16hi(xr[j].w);
+      }
       if (nw) {
-        uint4 u = *(const uint4*)(nw + k0);
-        w[0] = bf16lo(u.x); w[1] = bf16hi(u.x); w[2] = bf16lo(u.y); w[3] = bf16hi(u.y);
-        w[4] = bf16lo(u.z); w[5] = bf16hi(u.z); w[6] = bf16lo(u.w); w[7] = bf16hi(u.w);
+        w[0] = bf16lo(wr[j].x); w[1] = bf16hi(wr[j].x); w[2] = bf16lo(wr[j].y); w[3] = bf16hi(wr[j].y);
+        w[4] = bf16lo(wr[j].z); w[5] = bf16hi(wr[j].z); w[6] = bf16lo(wr[j].w); w[7] = bf16hi(wr[j].w);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) w[e] = 1.f;
       }
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        a.ss += v[e] * v[e];
-        a.x[j][e] = v[e] * w[e];
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float x = (j < a.nc && ok[j]) ? v[e] : 0.f;
+      a.ss = fmaf(x, x, a.ss);
+      a.x[j][e] = x * ((j < a.nc && ok[j]) ? w[e] : 0.f);
     }
   }
 }
 
 // Partial dot products of the wave's K range for 'nrows' rows of a tile; rows
-// r < n0 come from segment 0, the rest from segment 1 (row r - n0).  Row r's
-// partial lands in part[r] (lane 0 writes).
+// r < n0 come from segment 0, the rest from segment 1 (row r - n0).  The 16
+// per-lane accumulators are summed across the wave by a butterfly that halves
+// the rows kept at each exchange (xor 32, 16, 8, 4), then xor 2 and 1: 17
+// exchanges instead of 16 full reductions.  Lane l ends with the total of row
+// (l >> 2) & 15; lanes with (l & 3) == 0 write part[row].
 template <class Src>
-__device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, float* part) {
+__device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part) {
   const int lane = lane_id();
   const int nch = K / 8;
   const int cpw = (nch + kNW - 1) / kNW;
@@ -248,17 +298,26 @@ __device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, in
   float acc[kMaxRows];
 #pragma unroll
   for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.f;
+  // Rows past nrows re-read the last row and chunks outside the wave's range
+  // re-read chunk 0 (their activations are zero), so every row's load can be
+  // issued before any is used: one memory latency per chunk, not per row.
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
-    const int ch = lane + 64 * j;
-    if (j < a.nc && ch < cpw && base + ch < nch) {
-      const int cb = (base + ch) * 16;
+    if (j < a.nc) {
+      const int ch = lane + 64 * j;
+      const int cb = (ch < cpw && base + ch < nch ? base + ch : 0) * 16;
+      uint4 wv[kMaxRows];
 #pragma unroll
       for (int r = 0; r < kMaxRows; ++r) {
-        if (r < nrows) {
-          const int seg = r < n0 ? 0 : 1;
-          const int rr = r < n0 ? r : r - n0;
-          uint4 u = src.ld16(seg, rr * K * 2 + cb);
+        const int rc = r < nrows ? r : nrows - 1;
+        const int seg = rc < n0 ? 0 : 1;
+        const int rr = rc < n0 ? rc : rc - n0;
+        wv[r] = src.ld16(seg, rr * K * 2 + cb);
+      }
+#pragma unroll
+      for (int r = 0; r < kMaxRows; ++r) {
+        {
+          const uint4 u = wv[r];
           float s = acc[r];
           s = fmaf(bf16lo(u.x), a.x[j][0], s);
           s = fmaf(bf16hi(u.x), a.x[j][1], s);
@@ -273,20 +332,29 @@ __device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, in
       }
     }
   }
+  static_assert(kMaxRows == 16, "the butterfly below reduces 16 rows");
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) {
-    if (r < nrows) {
-      float v = wave_sum(acc[r]);
-      if (lane == 0) part[r] = v;
+  for (int half = 8, m = 32; half >= 1; half >>= 1, m >>= 1) {
+    const bool up = (lane & m) != 0;
+#pragma unroll
+    for (int r = 0; r < half; ++r) {
+      const float send = up ? acc[r] : acc[r + half];
+      const float keep = up ? acc[r + half] : acc[r];
+      acc[r] = keep + __shfl_xor(send, m, 64);
     }
   }
+  float v = acc[0];
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
+  const int row = (lane >> 2) & 15;
+  if ((lane & 3) == 0 && row < nrows) part[row] = v;
 }
 
 // Which activation and norm a GEMV op reads, and its K.
 struct GemvIn {
-  const float* xf;
-  const uint16_t* xb;
-  const uint16_t* nw;
+  const GLB float* xf;
+  const GLB uint16_t* xb;
+  const GLB uint16_t* nw;
   int K;
   int n0, nrows;  // rows in segment 0, total rows
 };
@@ -300,42 +368,57 @@ __device__ inline GemvIn gemv_input(const int* ins, const uint64_t* orow, const 
   switch (op) {
     case OpQkv:
       g.K = c.H;
-      g.nw = (const uint16_t*)orow[QkvNorm];
-      if (orow[QkvX]) g.xf = (const float*)orow[QkvX];
-      else g.xb = (const uint16_t*)orow[QkvEmbed] + (size_t)token0(orow[QkvTokens], c.V) * c.H;
+      g.nw = (const GLB uint16_t*)orow[QkvNorm];
+      if (orow[QkvX]) g.xf = (const GLB float*)orow[QkvX];
+      else g.xb = (const GLB uint16_t*)orow[QkvEmbed] + (size_t)token0(orow[QkvTokens], c.V) * c.H;
       g.n0 = g.nrows = ins[WPay + 1];
       break;
     case OpOproj:
       g.K = c.nq * c.hd;
-      g.xf = (const float*)orow[OIn];
+      g.xf = (const GLB float*)orow[OIn];
       g.n0 = g.nrows = ins[WPay + 1];
       break;
     case OpGateUp:
       g.K = c.H;
-      g.nw = (const uint16_t*)orow[GuNorm];
-      g.xf = (const float*)orow[GuIn];
+      g.nw = (const GLB uint16_t*)orow[GuNorm];
+      g.xf = (const GLB float*)orow[GuIn];
       g.n0 = ins[WPay + 1];
       g.nrows = 2 * ins[WPay + 1];
       break;
     case OpDown:
       g.K = c.F;
-      g.xf = (const float*)orow[DnIn];
+      g.xf = (const GLB float*)orow[DnIn];
       g.n0 = g.nrows = ins[WPay + 1];
       break;
     default:  // OpLmHead
       g.K = c.H;
-      g.nw = (const uint16_t*)orow[LmNorm];
-      g.xf = (const float*)orow[LmIn];
+      g.nw = (const GLB uint16_t*)orow[LmNorm];
+      g.xf = (const GLB float*)orow[LmIn];
       g.n0 = g.nrows = ins[WPay + 1];
       break;
   }
   return g;
 }
 
+// Residual input of a GEMV tile's rows (O projection: the residual stream or,
+// in layer 0, the embedding row; down projection: the post-attention stream),
+// one value per lane < nrows; loaded ahead of the epilogue.
+__device__ inline float gemv_residual(const int* ins, const uint64_t* orow, const Consts& c) {
+  const int lane = lane_id();
+  const int op = ins[WOpcode];
+  const int row0 = ins[WPay], nr = ins[WPay + 1];
+  const int rr = row0 + (lane < nr ? lane : 0);
+  if (op == OpOproj)
+    return orow[OX] ? ((const GLB float*)orow[OX])[rr]
+                    : bf16f(((const GLB uint16_t*)orow[OEmbed])[(size_t)token0(orow[OTokens], c.V) * c.H + rr]);
+  if (op == OpDown) return ((const GLB float*)orow[DnRes])[rr];
+  return 0.f;
+}
+
 // Epilogue of a GEMV tile, run by one wave once every compute wave's partials
 // (part[w][r]) and partial sums of squares (ssp[w]) are in LDS.
-__device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const Consts& c, const float (*part)[kMaxRows],
-                                     const float* ssp) {
+__device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const Consts& c,
+                                     const LDS float (*part)[kMaxRows], const LDS float* ssp, float res) {
   const int lane = lane_id();
   const int op = ins[WOpcode];
   const GemvIn g = gemv_input(ins, orow, c);
@@ -355,25 +438,21 @@ __device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const
   const int row0 = ins[WPay], nr = ins[WPay + 1];
   switch (op) {
     case OpQkv:
-      if (lane < nr) ((float*)orow[QkvOut])[(size_t)ins[WGx] * c.RPG + row0 + lane] = v;
+      if (lane < nr) st_agent((GLB float*)orow[QkvOut] + (size_t)ins[WGx] * c.RPG + row0 + lane, v);
       break;
     case OpOproj:
-      if (lane < nr) {
-        float res = orow[OX] ? ((const float*)orow[OX])[row0 + lane]
-                             : bf16f(((const uint16_t*)orow[OEmbed])[(size_t)token0(orow[OTokens], c.V) * c.H + row0 + lane]);
-        ((float*)orow[OOut])[row0 + lane] = res + v;
-      }
+      if (lane < nr) st_agent((GLB float*)orow[OOut] + row0 + lane, res + v);
       break;
     case OpGateUp: {
       float u = __shfl(v, lane + nr, 64);  // up row j sits at tile row nr + j
-      if (lane < nr) ((float*)orow[GuOut])[row0 + lane] = v / (1.f + __expf(-v)) * u;
+      if (lane < nr) st_agent((GLB float*)orow[GuOut] + row0 + lane, v / (1.f + __expf(-v)) * u);
       break;
     }
     case OpDown:
-      if (lane < nr) ((float*)orow[DnOut])[row0 + lane] = ((const float*)orow[DnRes])[row0 + lane] + v;
+      if (lane < nr) st_agent((GLB float*)orow[DnOut] + row0 + lane, res + v);
       break;
     case OpLmHead: {
-      if (lane < nr) ((float*)orow[LmLogits])[row0 + lane] = v;
+      if (lane < nr) ((GLB float*)orow[LmLogits])[row0 + lane] = v;
       // tile max, lowest row on ties
       float bv = lane < nr ? v : -INFINITY;
       int bi = lane < nr ? row0 + lane : 0x7FFFFFFF;
@@ -387,9 +466,9 @@ __device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const
         }
       }
       if (lane == 0) {
-        float* mx = (float*)orow[LmMax] + 2 * (size_t)ins[WGx];
-        mx[0] = bv;
-        ((int*)mx)[1] = bi;
+        GLB float* mx = (GLB float*)orow[LmMax] + 2 * (size_t)ins[WGx];
+        st_agent(mx, bv);
+        st_agent((GLB int*)mx + 1, bi);
       }
       break;
     }
@@ -398,117 +477,150 @@ __device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const
   }
 }
 
+__device__ __forceinline__ bool is_gemv(int op) {
+  return op == OpQkv || op == OpOproj || op == OpGateUp || op == OpDown || op == OpLmHead;
+}
+
 // ---- attention -----------------------------------------------------------------
 // One wave per query head of the kv group: RoPE (and Qwen3's q/k RMSNorm), the
 // new K/V row (written to the cache by wave 0 of the split that holds it),
 // scores over the split's positions, and the partial (max, sum, weighted V).
+// Every global input is loaded in one batch up front; the RoPE partner of
+// element d (d +- head_dim/2) is in the same lane for head_dim 128 and in
+// lane ^ 32 for head_dim 64.
 template <int HD, class Src>
 __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t* orow, const Consts& c, int cw,
-                                 float* scr, bool writer) {
+                                 LDS float* scr, bool writer) {
   const int lane = lane_id();
   const int b = ins[WGx], g = ins[WGy], s = ins[WGz];
   const int lo = ins[WPay], hi = ins[WPay + 1], pos = ins[WPay + 2];
   int nk = (hi < pos ? hi : pos) - lo;
   if (nk < 0) nk = 0;
   const bool has_new = pos >= lo && pos < hi;
-  const float* qkv = (const float*)orow[AttnQkv] + ((size_t)b * c.nkv + g) * c.RPG;
-  const float* rope = (const float*)orow[AttnRope] + (size_t)b * HD;  // (cos, sin) pairs
-  float* qs = scr;            // rotated q, HD floats
-  float* kn = scr + HD;       // new k (bf16-rounded), HD
-  float* vn = scr + 2 * HD;   // new v (bf16-rounded), HD
-  float* sc = scr + 3 * HD;   // scores
+  const bool active = cw < c.hpg;
   constexpr int HALF = HD / 2;
-  constexpr int PER = HD / 64;  // values per lane for a full head vector
+  constexpr int PER = HD / 64;  // head elements per lane: d = lane + 64 k
+  const GLB float* qkv = (const GLB float*)orow[AttnQkv] + ((size_t)b * c.nkv + g) * c.RPG;
+  const GLB float* rope = (const GLB float*)orow[AttnRope] + (size_t)b * HD;  // (cos, sin) pairs
+  const GLB uint16_t* qn = c.qk_norm ? (const GLB uint16_t*)orow[AttnQn] : nullptr;
+  const GLB uint16_t* knw = c.qk_norm ? (const GLB uint16_t*)orow[AttnKn] : nullptr;
+  LDS float* qs = scr;            // rotated q, HD floats
+  LDS float* kn = scr + HD;       // new k (bf16-rounded), HD
+  LDS float* vn = scr + 2 * HD;   // new v (bf16-rounded), HD
+  LDS float* sc = scr + 3 * HD;   // scores
 
-  // rotate-half RoPE of head vector src (fp32, optional per-head RMSNorm with weight nw)
-  auto rot = [&](const float* hv, const uint16_t* nw, float* out, bool round_bf16) {
-    float v[PER];
-    float ss = 0.f;
+  // ---- one batch of global loads
+  float qv[PER], kv[PER], vv[PER], cs[PER], sn[PER], wq[PER], wk[PER];
+  const int qh = active ? cw : 0;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      v[k] = hv[lane + 64 * k];
-      ss += v[k] * v[k];
-    }
-    if (nw) {
+  for (int k = 0; k < PER; ++k) {
+    const int d = lane + 64 * k;
+    const int ii = d < HALF ? d : d - HALF;
+    qv[k] = qkv[qh * HD + d];
+    kv[k] = qkv[c.hpg * HD + d];
+    vv[k] = qkv[(c.hpg + 1) * HD + d];
+    cs[k] = rope[2 * ii];
+    sn[k] = rope[2 * ii + 1];
+    wq[k] = qn ? bf16f(qn[d]) : 1.f;
+    wk[k] = knw ? bf16f(knw[d]) : 1.f;
+  }
+  // ---- per-head RMSNorm (Qwen3) and rotate-half RoPE, in registers
+  auto norm_rot = [&](float* v, const float* w, bool do_norm) {
+    if (do_norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) ss = fmaf(v[k], v[k], ss);
       ss = wave_sum(ss);
-      float inv = 1.f / sqrtf(ss / (float)HD + c.eps);
+      const float inv = 1.f / sqrtf(ss / (float)HD + c.eps);
 #pragma unroll
-      for (int k = 0; k < PER; ++k) v[k] = v[k] * inv * bf16f(nw[lane + 64 * k]);
+      for (int k = 0; k < PER; ++k) v[k] = v[k] * inv * w[k];
     }
-    // stage in out[], then rotate pairs (i, i + HALF)
-#pragma unroll
-    for (int k = 0; k < PER; ++k) out[lane + 64 * k] = v[k];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    float partner[PER];
+    if (PER == 1) {
+      partner[0] = __shfl_xor(v[0], 32, 64);
+    } else {
+      partner[0] = v[PER - 1];
+      partner[PER - 1] = v[0];
+    }
     float r[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int d = lane + 64 * k;
-      const int i = d < HALF ? d : d - HALF;
-      const float cs = rope[2 * i], sn = rope[2 * i + 1];
-      const float a = out[i], bb = out[i + HALF];
-      r[k] = d < HALF ? a * cs - bb * sn : bb * cs + a * sn;
+      r[k] = d < HALF ? v[k] * cs[k] - partner[k] * sn[k] : v[k] * cs[k] + partner[k] * sn[k];
     }
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int k = 0; k < PER; ++k) out[lane + 64 * k] = round_bf16 ? bf16f(f2bf(r[k])) : r[k];
-    __builtin_amdgcn_wave_barrier();
+    for (int k = 0; k < PER; ++k) v[k] = r[k];
   };
-
-  const bool active = cw < c.hpg;
-  if (active) {
-    rot(qkv + cw * HD, c.qk_norm ? (const uint16_t*)orow[AttnQn] : nullptr, qs, false);
-  }
-  if (has_new) {
-    // every wave computes the new row (cheap); the writer stores it
-    rot(qkv + c.hpg * HD, c.qk_norm ? (const uint16_t*)orow[AttnKn] : nullptr, kn, true);
+  norm_rot(qv, wq, c.qk_norm != 0);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) vn[lane + 64 * k] = bf16f(f2bf(qkv[(c.hpg + 1) * HD + lane + 64 * k]));
-    __builtin_amdgcn_wave_barrier();
+  for (int k = 0; k < PER; ++k) qs[lane + 64 * k] = qv[k];
+  if (has_new) {
+    norm_rot(kv, wk, c.qk_norm != 0);
+    uint16_t kb[PER], vb[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      kb[k] = f2bf(kv[k]);
+      vb[k] = f2bf(vv[k]);
+      kn[lane + 64 * k] = bf16f(kb[k]);
+      vn[lane + 64 * k] = bf16f(vb[k]);
+    }
     if (writer) {
-      size_t row = (((size_t)b * c.nkv + g) * c.cap + pos) * HD;
-      uint16_t* K = (uint16_t*)orow[AttnK] + row;
-      uint16_t* Vv = (uint16_t*)orow[AttnV] + row;
+      const size_t row = (((size_t)b * c.nkv + g) * c.cap + pos) * HD;
+      GLB uint16_t* K = (GLB uint16_t*)orow[AttnK] + row;
+      GLB uint16_t* Vv = (GLB uint16_t*)orow[AttnV] + row;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
-        K[lane + 64 * k] = f2bf(kn[lane + 64 * k]);
-        Vv[lane + 64 * k] = f2bf(vn[lane + 64 * k]);
+        K[lane + 64 * k] = kb[k];
+        Vv[lane + 64 * k] = vb[k];
       }
     }
   }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   if (!active) return;
   const int n = nk + (has_new ? 1 : 0);
-  float* outp = (float*)orow[AttnOut] + ((((size_t)b * c.nkv + g) * c.S + s) * c.hpg + cw) * (HD + 2);
+  GLB float* outp = (GLB float*)orow[AttnOut] + ((((size_t)b * c.nkv + g) * c.S + s) * c.hpg + cw) * (HD + 2);
   if (n == 0) {
     if (lane == 0) {
-      outp[0] = -INFINITY;
-      outp[1] = 0.f;
+      st_agent(outp, -INFINITY);
+      st_agent(outp + 1, 0.f);
     }
 #pragma unroll
-    for (int k = 0; k < PER; ++k) outp[2 + lane + 64 * k] = 0.f;
+    for (int k = 0; k < PER; ++k) st_agent(outp + 2 + lane + 64 * k, 0.f);
     return;
   }
-  // scores: LPP lanes per position, 8 dims (16 bytes) per lane
+  // ---- scores: LPP lanes per position, 8 dims (16 bytes) per lane, PPP
+  // positions per pass, 4 passes' loads issued together
   constexpr int LPP = HD / 8;
   constexpr int PPP = 64 / LPP;
   const int p_in = lane / LPP, cidx = lane % LPP;
-  float qv[8];
+  float qc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qv[e] = qs[cidx * 8 + e];
-  for (int j0 = 0; j0 < n; j0 += PPP) {
-    const int j = j0 + p_in;
-    float d = 0.f;
-    if (j < nk) {
-      uint4 u = src.ld16(0, j * HD * 2 + cidx * 16);
-      d = bf16lo(u.x) * qv[0] + bf16hi(u.x) * qv[1] + bf16lo(u.y) * qv[2] + bf16hi(u.y) * qv[3] +
-          bf16lo(u.z) * qv[4] + bf16hi(u.z) * qv[5] + bf16lo(u.w) * qv[6] + bf16hi(u.w) * qv[7];
-    } else if (j < n) {
+  for (int e = 0; e < 8; ++e) qc[e] = qs[cidx * 8 + e];
+  for (int j0 = 0; j0 < n; j0 += 4 * PPP) {
+    uint4 u[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d += kn[cidx * 8 + e] * qv[e];
+    for (int pss = 0; pss < 4; ++pss) {
+      int j = j0 + pss * PPP + p_in;
+      j = j < nk ? j : (nk > 0 ? nk - 1 : 0);
+      u[pss] = nk > 0 ? src.ld16(0, j * HD * 2 + cidx * 16) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int m = LPP / 2; m >= 1; m >>= 1) d += __shfl_xor(d, m, 64);
-    if (cidx == 0 && j < n) sc[j] = d * c.inv_sqrt_hd;
+    for (int pss = 0; pss < 4; ++pss) {
+      const int j = j0 + pss * PPP + p_in;
+      float d;
+      if (j < nk) {
+        d = bf16lo(u[pss].x) * qc[0] + bf16hi(u[pss].x) * qc[1] + bf16lo(u[pss].y) * qc[2] + bf16hi(u[pss].y) * qc[3] +
+            bf16lo(u[pss].z) * qc[4] + bf16hi(u[pss].z) * qc[5] + bf16lo(u[pss].w) * qc[6] + bf16hi(u[pss].w) * qc[7];
+      } else {
+        d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += kn[cidx * 8 + e] * qc[e];
+      }
+#pragma unroll
+      for (int m = LPP / 2; m >= 1; m >>= 1) d += __shfl_xor(d, m, 64);
+      if (cidx == 0 && j < n) sc[j] = d * c.inv_sqrt_hd;
+    }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -518,67 +630,114 @@ __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t*
   float l = 0.f, o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float p = __expf(sc[j] - m);
-    l += p;
+  // V rows, 8 positions per batch so the loads overlap
+  for (int j0 = 0; j0 < nk; j0 += 8) {
+    float vr[8][PER], pp[8];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int dd = lane + 64 * k;
-      const float vv = j < nk ? bf16f(src.ld2(1, (j * HD + dd) * 2)) : vn[dd];
-      o[k] = fmaf(p, vv, o[k]);
+    for (int u2 = 0; u2 < 8; ++u2) {
+      const int j = j0 + u2;
+      const int jc = j < nk ? j : nk - 1;
+      pp[u2] = j < nk ? __expf(sc[j] - m) : 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) vr[u2][k] = bf16f(src.ld2(1, (jc * HD + lane + 64 * k) * 2));
+    }
+#pragma unroll
+    for (int u2 = 0; u2 < 8; ++u2) {
+      l += pp[u2];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] = fmaf(pp[u2], vr[u2][k], o[k]);
     }
   }
+  if (has_new) {
+    const float p = __expf(sc[nk] - m);
+    l += p;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = fmaf(p, vn[lane + 64 * k], o[k]);
+  }
   if (lane == 0) {
-    outp[0] = m;
-    outp[1] = l;
+    st_agent(outp, m);
+    st_agent(outp + 1, l);
   }
 #pragma unroll
-  for (int k = 0; k < PER; ++k) outp[2 + lane + 64 * k] = o[k];
+  for (int k = 0; k < PER; ++k) st_agent(outp + 2 + lane + 64 * k, o[k]);
 }
 
-// Merge the S split partials of one query head (log-sum-exp).
+// Merge the S split partials of one query head (log-sum-exp).  Lane s reads
+// split s's (max, sum); the weighted outputs are read 8 splits at a time.
 template <int HD>
 __device__ inline void combine_wave(const int* ins, const uint64_t* orow, const Consts& c, int cw) {
   if (cw >= c.hpg) return;
   const int lane = lane_id();
   const int b = ins[WGx], g = ins[WGy];
   constexpr int PER = HD / 64;
-  const float* part = (const float*)orow[CombPart] + (((size_t)b * c.nkv + g) * c.S * c.hpg + cw) * (HD + 2);
+  const GLB float* part = (const GLB float*)orow[CombPart] + (((size_t)b * c.nkv + g) * c.S * c.hpg + cw) * (HD + 2);
   const size_t stride = (size_t)c.hpg * (HD + 2);
   float M = -INFINITY;
-  for (int s = 0; s < c.S; ++s) {
-    const float* p = part + s * stride;
-    if (p[1] > 0.f) M = fmaxf(M, p[0]);
+  for (int s0 = 0; s0 < c.S; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < c.S) {
+      const float ms = part[s * stride], ls = part[s * stride + 1];
+      if (ls > 0.f) M = fmaxf(M, ms);
+    }
   }
+  M = wave_max(M);
   float L = 0.f, o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int s = 0; s < c.S; ++s) {
-    const float* p = part + s * stride;
-    if (!(p[1] > 0.f)) continue;
-    const float w = __expf(p[0] - M);
-    L += w * p[1];
+  for (int s0 = 0; s0 < c.S; s0 += 8) {
+    float w[8], ov[8][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = fmaf(w, p[2 + lane + 64 * k], o[k]);
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      w[u] = 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) ov[u][k] = 0.f;
+      if (s < c.S) {
+        const GLB float* p = part + s * stride;
+        const float ls = p[1];
+        w[u] = ls > 0.f ? __expf(p[0] - M) : 0.f;
+        L = fmaf(w[u], ls > 0.f ? ls : 0.f, L);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) ov[u][k] = p[2 + lane + 64 * k];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] = fmaf(w[u], ov[u][k], o[k]);
   }
-  float* out = (float*)orow[CombOut] + (size_t)b * c.nq * HD + (size_t)(g * c.hpg + cw) * HD;
+  GLB float* out = (GLB float*)orow[CombOut] + (size_t)b * c.nq * HD + (size_t)(g * c.hpg + cw) * HD;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) out[lane + 64 * k] = o[k] / L;
+  for (int k = 0; k < PER; ++k) st_agent(out + lane + 64 * k, o[k] / L);
 }
 
 // Reduce the LM-head tile maxima of sequence b in tile order (lowest index on ties).
 __device__ inline void argmax_wave(const int* ins, const uint64_t* orow, const Consts& c) {
   const int lane = lane_id();
   const int b = ins[WGx], T = ins[WPay];
-  const float* mx = (const float*)orow[AmMax] + (size_t)b * 2 * T;
+  const GLB float* mx = (const GLB float*)orow[AmMax] + (size_t)b * 2 * T;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int t = lane; t < T; t += 64) {
-    float v = mx[2 * t];
-    int i = ((const int*)mx)[2 * t + 1];
-    if (v > bv || (v == bv && i < bi)) {
-      bv = v;
-      bi = i;
+  for (int t0 = 0; t0 < T; t0 += 64 * 16) {
+    float2 pr[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = t0 + u * 64 + lane;
+      if (t < T) {
+        const f32x2 q = ((const GLB f32x2*)mx)[t];
+        pr[u] = make_float2(q.x, q.y);
+      } else {
+        pr[u] = make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float v = pr[u].x;
+      const int i = __float_as_int(pr[u].y);
+      if (v > bv || (v == bv && i < bi)) {
+        bv = v;
+        bi = i;
+      }
     }
   }
 #pragma unroll
@@ -590,7 +749,7 @@ __device__ inline void argmax_wave(const int* ins, const uint64_t* orow, const C
       bi = oi;
     }
   }
-  if (lane == 0) ((int*)orow[AmOut])[b] = bi;
+  if (lane == 0) ((GLB int*)orow[AmOut])[b] = bi;
 }
 
 }  // namespace mkd

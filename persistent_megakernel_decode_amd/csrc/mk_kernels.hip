@@ -45,8 +45,8 @@ struct __attribute__((aligned(16))) Lds {
 };
 
 template <class T>
-__device__ __forceinline__ uint32_t lds_addr(T* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)p);
+__device__ __forceinline__ uint32_t lds_addr(LDS T* p) {
+  return (uint32_t)(uintptr_t)p;
 }
 // LDS flag access for the loader waves, in inline asm so that the compiler
 // does not put a vmcnt(0) wait (for the wave's own pending LDS-DMA) in front.
@@ -59,14 +59,14 @@ __device__ __forceinline__ void lds_st_asm(uint32_t addr, int v) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
 }
 
-__device__ __forceinline__ int lds_load_acq(int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-__device__ __forceinline__ void lds_store_rel(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+__device__ __forceinline__ int lds_load_acq(LDS int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+__device__ __forceinline__ void lds_store_rel(LDS int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
 
 enum { ErrEvent = 1, ErrPage = 2, ErrReady = 3, ErrDrain = 4, ErrFree = 5 };
 
 // The record belongs to the run whose epoch is in err[0]; the first failing
 // wave of that run fills it.
-__device__ void record_error(const KArgs& a, Lds& L, int kind, int slot, int ev, unsigned val, unsigned tgt) {
+__device__ void record_error(const KArgs& a, LDS Lds* L, int kind, int slot, int ev, unsigned val, unsigned tgt) {
   if (lane_id() == 0) {
     unsigned old = __hip_atomic_load(&a.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old != a.epoch && __hip_atomic_compare_exchange_strong(&a.err[0], &old, a.epoch, __ATOMIC_RELAXED,
@@ -78,16 +78,16 @@ __device__ void record_error(const KArgs& a, Lds& L, int kind, int slot, int ev,
       a.err[5] = val;
       a.err[6] = tgt;
     }
-    __hip_atomic_store(&L.c.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&L->c.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
-__device__ __forceinline__ bool aborted(Lds& L) {
-  return __hip_atomic_load(&L.c.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+__device__ __forceinline__ bool aborted(LDS Lds* L) {
+  return __hip_atomic_load(&L->c.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
 }
 
 // Wait until *p >= v (LDS, workgroup acquire), bounded.
-__device__ bool wait_lds_ge(const KArgs& a, Lds& L, int* p, int v, int kind, int slot) {
+__device__ bool wait_lds_ge(const KArgs& a, LDS Lds* L, LDS int* p, int v, int kind, int slot) {
   if (lds_load_acq(p) >= v) return true;
   const unsigned long long t0 = now_ticks();
   for (unsigned it = 0;; ++it) {
@@ -108,23 +108,23 @@ __device__ __forceinline__ const int* instr(const KArgs& a, int i) {
 }
 
 // ---------------------------------------------------------------------------
-__device__ void controller(const KArgs& a, Lds& L) {
+__device__ void controller(const KArgs& a, LDS Lds* L) {
   for (int i = 0; i < a.max_len; ++i) {
     const int* ins = instr(a, i);
     if (ins[WOpcode] == OpNoop) break;
     if (ins[WWaitCnt]) {
       const unsigned tgt = a.epoch * (unsigned)ins[WWaitTgt];
-      unsigned* ctr = a.counters + ins[WWaitEv];
+      unsigned* ctr = a.counters + (size_t)ins[WWaitEv] * kCtrStride;
       unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((int)(v - tgt) < 0) {
         const unsigned long long t0 = now_ticks();
         for (unsigned it = 0;; ++it) {
-          __builtin_amdgcn_s_sleep(1);
+          __builtin_amdgcn_s_sleep(4);
           v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if ((int)(v - tgt) >= 0) break;
-          if ((it & 63) == 63) {
+          if ((it & 15) == 15) {
             if (aborted(L) || __hip_atomic_load(&a.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
-              if (lane_id() == 0) __hip_atomic_store(&L.c.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              if (lane_id() == 0) __hip_atomic_store(&L->c.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
               return;
             }
             if (now_ticks() - t0 > a.timeout_ticks) {
@@ -136,38 +136,75 @@ __device__ void controller(const KArgs& a, Lds& L) {
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    if (a.trace && lane_id() == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 0] = now_ticks();
-    if (lane_id() == 0) lds_store_rel(&L.c.ready_seq, i + 1);
+    if (a.trace && lane_id() == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 0] = now_ticks();
+    if (lane_id() == 0) lds_store_rel(&L->c.ready_seq, i + 1);
   }
 }
 
 // ---------------------------------------------------------------------------
-__device__ void storer(const KArgs& a, Lds& L) {
+// Storer: per instruction, prefetch the residual, wait until every compute wave
+// has arrived, run the GEMV epilogue (reduce the partials in LDS, RMSNorm
+// scale, residual / SiLU, store), hand the LDS slot back, and signal.  A run of
+// consecutive instructions that trigger the same event is signalled once, at
+// its end, with the summed increment: a producer never depends on its own
+// trigger event, so deferring within the run cannot delay the event.
+__device__ void storer(const KArgs& a, LDS Lds* L) {
+  const int lane = lane_id();
+  unsigned pending = 0;
   for (int i = 0; i < a.max_len; ++i) {
     const int* ins = instr(a, i);
-    if (ins[WOpcode] == OpNoop) break;
-    if (!wait_lds_ge(a, L, &L.c.done_seq, i + 1, ErrDrain, i)) return;
-    if (ins[WSigCnt] && lane_id() == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(a.counters + ins[WSigEv], (unsigned)ins[WSigInc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int op = ins[WOpcode];
+    if (op == OpNoop) break;
+    const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
+    const int sl = i & 3;
+    const bool gemv = is_gemv(op);
+    // the residual may be read only once the instruction's event has been
+    // acquired (the controller publishes "ready" after its acquire)
+    if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
+    const float res = (op == OpOproj || op == OpDown) ? gemv_residual(ins, orow, a.c) : 0.f;
+    if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
+    if (gemv) gemv_epilogue(ins, orow, a.c, L->c.part[sl], L->c.ssp[sl], res);
+    if (lane == 0) {
+      __hip_atomic_store(&L->c.arrive[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      lds_store_rel(&L->c.done_seq, i + 1);
     }
-    if (a.trace && lane_id() == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 3] = now_ticks();
+    if (a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 2] = now_ticks();
+    if (ins[WSigCnt]) {
+      pending += (unsigned)ins[WSigInc];
+      const int* nx = i + 1 < a.max_len ? instr(a, i + 1) : nullptr;
+      const bool same_next = nx && nx[WOpcode] != OpNoop && nx[WSigCnt] && nx[WSigEv] == ins[WSigEv];
+      if (!same_next) {
+        // every output of the run was stored agent-coherent (by this wave or
+        // by the compute waves before they arrived): wait for completion, then count
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0)
+          __hip_atomic_fetch_add(a.counters + (size_t)ins[WSigEv] * kCtrStride, pending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pending = 0;
+      }
+    }
+    if (a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 3] = now_ticks();
   }
 }
 
 // ---------------------------------------------------------------------------
-__device__ void loader(const KArgs& a, Lds& L, int parity) {
+__device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
   const int lane = lane_id();
-  const uint32_t full_base = lds_addr(&L.c.slot_full[0]);
-  const uint32_t freed_base = lds_addr(&L.c.slot_freed[0]);
-  // issued-but-unpublished pages (oldest first); scalars, never indexed
-  int q0 = 0, q1 = 0, q2 = 0, npend = 0;
-  auto publish = [&](int sq) { lds_st_asm(full_base + 4 * (sq % kNumPages), sq / kNumPages + 1); };
+  const uint32_t full_base = lds_addr(&L->c.slot_full[0]);
+  const uint32_t freed_base = lds_addr(&L->c.slot_freed[0]);
+  // issued-but-unpublished pages (oldest first): page sequence number and, for
+  // the trace, the instruction whose last page it is (-1 otherwise); scalars,
+  // never indexed
+  int q0 = 0, q1 = 0, q2 = 0, l0 = -1, l1 = -1, l2 = -1, npend = 0;
+  auto publish = [&](int sq, int last_of) {
+    lds_st_asm(full_base + 4 * (sq % kNumPages), sq / kNumPages + 1);
+    if (a.trace && last_of >= 0 && lane == 0)
+      a.trace[((size_t)blockIdx.x * a.max_len + last_of) * kTraceWords + 5] = now_ticks();
+  };
   auto publish_all = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (npend > 0) publish(q0);
-    if (npend > 1) publish(q1);
-    if (npend > 2) publish(q2);
+    if (npend > 0) publish(q0, l0);
+    if (npend > 1) publish(q1, l1);
+    if (npend > 2) publish(q2, l2);
     npend = 0;
   };
   int seq = 0;
@@ -176,7 +213,7 @@ __device__ void loader(const KArgs& a, Lds& L, int parity) {
     if (ins[WOpcode] == OpNoop) break;
     const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
     const Tile t = tile_info(ins, orow, a.c);
-    const char* dummy = t.len0 > 0 ? t.p0 : t.p1;
+    const GLB char* dummy = t.len0 > 0 ? t.p0 : t.p1;
     for (int pg = 0; pg < t.npages; ++pg, ++seq) {
       if ((seq & 1) != parity) continue;
       const int slot = seq % kNumPages, gen = seq / kNumPages;
@@ -195,30 +232,37 @@ __device__ void loader(const KArgs& a, Lds& L, int parity) {
           }
         }
       }
-      char* dst = L.ring[slot];
+      if (pg == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 4] = now_ticks();
+      LDS char* dst = L->ring[slot];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int toff = pg * kPage + j * 1024 + lane * 16;
-        const char* src = dummy;
+        const GLB char* src = dummy;
         if (toff < t.len0)
           src = t.p0 + toff;
         else if (toff >= t.off1 && toff < t.off1 + t.len1)
           src = t.p1 + (toff - t.off1);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const GLB void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
       }
+      const int last_of = pg == t.npages - 1 ? i : -1;
       if (npend == 0) {
         q0 = seq;
+        l0 = last_of;
       } else if (npend == 1) {
         q1 = seq;
+        l1 = last_of;
       } else {
         q2 = seq;
+        l2 = last_of;
       }
       ++npend;
       if (npend == 3) {
         asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-        publish(q0);
+        publish(q0, l0);
         q0 = q1;
+        l0 = l1;
         q1 = q2;
+        l1 = l2;
         npend = 2;
       }
     }
@@ -228,7 +272,7 @@ __device__ void loader(const KArgs& a, Lds& L, int parity) {
 
 // ---------------------------------------------------------------------------
 template <int HD>
-__device__ void compute(const KArgs& a, Lds& L, int cw) {
+__device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
   const int lane = lane_id();
   int seq = 0;
   int act_row = -1;
@@ -240,21 +284,23 @@ __device__ void compute(const KArgs& a, Lds& L, int cw) {
     if (op == OpNoop) break;
     const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
     const Tile t = tile_info(ins, orow, a.c);
+    unsigned long long* tr = a.trace ? a.trace + ((size_t)blockIdx.x * a.max_len + i) * kTraceWords : nullptr;
     const int first = seq;
     seq += t.npages;
-    if (!wait_lds_ge(a, L, &L.c.ready_seq, i + 1, ErrReady, i)) return;
-    if (!wait_lds_ge(a, L, &L.c.done_seq, i - 3, ErrDrain, i)) return;
+    if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
+    if (!wait_lds_ge(a, L, &L->c.done_seq, i - 3, ErrDrain, i)) return;
     for (int pg = 0; pg < t.npages; ++pg) {
       const int sq = first + pg;
-      if (!wait_lds_ge(a, L, &L.c.slot_full[sq % kNumPages], sq / kNumPages + 1, ErrPage, i)) return;
+      if (!wait_lds_ge(a, L, &L->c.slot_full[sq % kNumPages], sq / kNumPages + 1, ErrPage, i)) return;
     }
-    if (cw == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 1] = now_ticks();
+    if (cw == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 1] = now_ticks();
+    if (tr && lane == 0) tr[8 + cw] = now_ticks();
     LdsSrc src;
-    src.ring = L.ring[0];
+    src.ring = L->ring[0];
     src.first_slot = first % kNumPages;
     src.off1 = t.off1;
     const int sl = i & 3;
-    const bool gemv = op == OpQkv || op == OpOproj || op == OpGateUp || op == OpDown || op == OpLmHead;
+    const bool gemv = is_gemv(op);
     if (gemv) {
       const GemvIn gi = gemv_input(ins, orow, a.c);
       if (ins[WOpRow] != act_row) {
@@ -262,10 +308,11 @@ __device__ void compute(const KArgs& a, Lds& L, int cw) {
         act_ss = wave_sum(act.ss);
         act_row = ins[WOpRow];
       }
-      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L.c.part[sl][cw]);
-      if (lane == 0) L.c.ssp[sl][cw] = act_ss;
+      if (cw == 0 && tr && lane == 0) tr[6] = now_ticks();
+      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw]);
+      if (lane == 0) L->c.ssp[sl][cw] = act_ss;
     } else if (op == OpAttn) {
-      attn_wave<HD>(src, ins, orow, a.c, cw, L.c.scratch[cw], cw == 0);
+      attn_wave<HD>(src, ins, orow, a.c, cw, L->c.scratch[cw], cw == 0);
     } else if (op == OpCombine) {
       combine_wave<HD>(ins, orow, a.c, cw);
     } else if (op == OpArgmax) {
@@ -274,34 +321,28 @@ __device__ void compute(const KArgs& a, Lds& L, int cw) {
     // release this tile's pages
     for (int pg = 0; pg < t.npages; ++pg) {
       const int sq = first + pg, slot = sq % kNumPages;
-      int old = 0;
-      if (lane == 0) old = __hip_atomic_fetch_add(&L.c.slot_rel[slot], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-      old = __shfl(old, 0, 64);
-      if (old == kNW - 1 && lane == 0) {
-        __hip_atomic_store(&L.c.slot_rel[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        lds_store_rel(&L.c.slot_freed[slot], sq / kNumPages + 1);
+      if (lane == 0) {
+        const int old = __hip_atomic_fetch_add(&L->c.slot_rel[slot], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (old == kNW - 1) {  // the last compute wave done with this page hands it to the loaders
+          __hip_atomic_store(&L->c.slot_rel[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          lds_store_rel(&L->c.slot_freed[slot], sq / kNumPages + 1);
+        }
       }
     }
-    // arrival; the last compute wave runs the epilogue and publishes completion
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(&L.c.arrive[sl], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    old = __shfl(old, 0, 64);
-    if (old == kNW - 1) {
-      if (lane == 0) __hip_atomic_store(&L.c.arrive[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (gemv) gemv_epilogue(ins, orow, a.c, L.c.part[sl], L.c.ssp[sl]);
-      if (a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * 4 + 2] = now_ticks();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) lds_store_rel(&L.c.done_seq, i + 1);
-    }
+    if (tr && lane == 0) tr[12 + cw] = now_ticks();
+    // arrival: GEMV partials are in LDS; other ops wrote global memory, which
+    // must be complete before the storer signals (workgroup release = vmcnt(0))
+    if (!gemv) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_fetch_add(&L->c.arrive[sl], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
 template <int HD>
 __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
-  __shared__ Lds L;
+  __shared__ Lds Ls;
+  LDS Lds* L = (LDS Lds*)&Ls;
   {
-    int* c = (int*)&L.c;
+    LDS int* c = (LDS int*)&L->c;
     const int n = (int)(sizeof(Ctrl) / 4);
     for (int k = threadIdx.x; k < n; k += blockDim.x) c[k] = 0;
   }
@@ -321,9 +362,12 @@ __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
 // Layerwise: one launch per operator, one workgroup (4 waves) per tile.
 template <int HD>
 __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int first_task) {
-  __shared__ float part[kNW][kMaxRows];
-  __shared__ float ssp[kNW];
-  __shared__ float scr[kNW][kScratch];
+  __shared__ float part_s[kNW][kMaxRows];
+  __shared__ float ssp_s[kNW];
+  __shared__ float scr_s[kNW][kScratch];
+  LDS float(*part)[kMaxRows] = (LDS float(*)[kMaxRows])part_s;
+  LDS float* ssp = (LDS float*)ssp_s;
+  LDS float(*scr)[kScratch] = (LDS float(*)[kScratch])scr_s;
   const int t = first_task + blockIdx.x;
   const int* ins = a.queue + ((size_t)(t % num_cus) * a.max_len + t / num_cus) * 32;
   const int cw = threadIdx.x >> 6, lane = lane_id();
@@ -333,7 +377,7 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   src.p0 = tl.p0;
   src.p1 = tl.p1 ? tl.p1 : tl.p0;
   const int op = ins[WOpcode];
-  if (op == OpQkv || op == OpOproj || op == OpGateUp || op == OpDown || op == OpLmHead) {
+  if (is_gemv(op)) {
     const GemvIn gi = gemv_input(ins, orow, a.c);
     Act act;
     load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
@@ -341,7 +385,7 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
     gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw]);
     if (lane == 0) ssp[cw] = ss;
     __syncthreads();
-    if (cw == 0) gemv_epilogue(ins, orow, a.c, part, ssp);
+    if (cw == 0) gemv_epilogue(ins, orow, a.c, part, ssp, gemv_residual(ins, orow, a.c));
   } else if (op == OpAttn) {
     attn_wave<HD>(src, ins, orow, a.c, cw, scr[cw], cw == 0);
   } else if (op == OpCombine) {

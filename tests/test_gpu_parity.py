@@ -69,9 +69,14 @@ class Case:
         for b, p in enumerate(self.inp["kv_len"]):
             mask[:, :, b, :, int(p), :] = True
         assert np.array_equal(r["kv"][~mask], kv0[~mask])
-        d = np.abs(r["kv"][mask].astype(np.int32) - kvr[mask].astype(np.int32))
-        assert d.max() <= 1, d.max()
-        assert (d > 0).mean() < 0.02
+        # new rows: fp32 vs fp64 arithmetic before the same bf16 rounding may
+        # land one bf16 step apart; near zero the step is tiny, so the slack is
+        # one step of the value plus 1e-4 of the row's RMS.
+        g = oracle.bf16_to_f64(r["kv"][mask]).reshape(-1, kv0.shape[-1])
+        o = oracle.bf16_to_f64(kvr[mask]).reshape(-1, kv0.shape[-1])
+        rms = np.sqrt(np.mean(o * o, axis=1, keepdims=True))
+        assert (np.abs(g - o) <= np.abs(o) * 2.0 ** -7 + 1e-4 * rms).all()
+        assert (g != o).mean() < 0.02
 
 
 _cases = {}
@@ -130,3 +135,27 @@ def test_gpu_llama1b_full_size():
     c = case("llama1b", "llama1b", norm_sigma=0.0)
     c.assert_parity(c.run())
     c.assert_parity(c.run(layerwise=True), layerwise=True)
+
+
+@pytest.mark.parametrize("key,name", [("tiny", "tiny"), ("llama1b", "llama1b")])
+def test_gpu_consecutive_runs_new_tokens(key, name):
+    """Consecutive runs on one plan with different token ids: each must match
+    its own oracle result, so no run can pass by reading an earlier run's
+    intermediates (data written across compute units must be visible within
+    the step that produced it)."""
+    mk = _mk()
+    c = case(key, name, norm_sigma=0.0 if name == "llama1b" else 0.1)
+    V = c.cfg["vocab"]
+    for trial, tok in enumerate([(int(c.inp["tokens"][0]) + 1 + 977 * t) % V for t in range(3)]):
+        inp = dict(c.inp, tokens=np.array([tok], dtype=np.int32))
+        ref = oracle.decode_step(inp)
+        kv = c.fresh_kv()
+        c.plan.run(c.w, kv, mk.tokens_to_device(inp["tokens"]))
+        torch.cuda.synchronize()
+        st, chk = c.plan.check()
+        assert st == mk.MK_OK and chk.counters_ok == 1
+        logits = c.plan.output(mk.MK_OUT_LOGITS).cpu().numpy().reshape(1, -1)
+        rel = np.linalg.norm(logits - ref["logits"]) / np.linalg.norm(ref["logits"])
+        print("  token %d rel-L2 %.3g" % (tok, rel), flush=True)
+        assert rel <= LOGIT_TOL
+        assert int(c.plan.output(mk.MK_OUT_NEXT_TOKEN).cpu()[0]) == int(ref["next"][0])
