@@ -85,11 +85,16 @@ typedef struct {
  * attn_splits: KV splits per (sequence, kv head) (default from the longest
  *   sequence: ceil((kv+1)/64) clamped to [1, 32], raised until one split's
  *   K and V rows fit in 64 KiB);
- * timeout_ms: bound of every device-side wait (default 200). */
+ * timeout_ms: bound of every device-side wait (default 200);
+ * dma_pages: 16 KiB pages each of the two weight-loader waves keeps in flight
+ *   (1 or 2, default 2): enough to cover HBM latency, few enough that the
+ *   latency-critical activation reads do not queue behind a deep DMA backlog.
+ *   Does not change the plan's schedule metadata. */
 typedef struct {
   int32_t num_cus, gemv_rows, gateup_outs, down_rows, lm_rows, attn_splits;
   int32_t timeout_ms;
-  int32_t reserved[5];
+  int32_t dma_pages;
+  int32_t reserved[4];
 } mk_plan_opts;
 
 /* Build the static tile plan of one decode step (host-only arithmetic; uploads

@@ -53,6 +53,7 @@ struct mk_plan {
   mkd::Consts c{};
   int num_cus = 0;
   unsigned long long timeout_ticks = 0;
+  int dma_pages = 2;
   // device state
   int device = -1;
   bool uploaded = false;
@@ -134,6 +135,11 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     o.lm_rows = opts->lm_rows;
     o.attn_splits = opts->attn_splits;
     if (opts->timeout_ms > 0) timeout_ms = opts->timeout_ms;
+    if (opts->dma_pages < 0 || opts->dma_pages > 2) {
+      delete p;
+      return fail(MK_E_INVALID, "dma_pages must be 0 (default), 1 or 2");
+    }
+    if (opts->dma_pages > 0) p->dma_pages = opts->dma_pages;
   }
   if (o.num_cus <= 0) {
     int dev = 0, n = 0;
@@ -162,9 +168,9 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     delete p;
     return fail(MK_E_UNSUPPORTED, "a tile does not fit the 144 KiB LDS page ring; use smaller tiles");
   }
-  if (attn_rows + 1 > (mkd::kScratch - 3 * d.head_dim)) {
+  if (o.attn_splits > 64) {
     delete p;
-    return fail(MK_E_UNSUPPORTED, "too many positions per attention split; raise attn_splits");
+    return fail(MK_E_UNSUPPORTED, "at most 64 attention splits");
   }
   p->opts = o;
   std::vector<mk::GraphEdge> edges;
@@ -431,6 +437,7 @@ static mkd::KArgs kargs(const mk_plan* p) {
   a.err = p->d_err;
   a.trace = p->trace_on ? p->d_trace : nullptr;
   a.max_len = p->P.max_len;
+  a.dma_pages = p->dma_pages;
   a.epoch = p->epoch;
   a.timeout_ticks = p->timeout_ticks;
   a.c = p->c;

@@ -66,6 +66,7 @@ struct KArgs {
   unsigned* err;              // watchdog record [8]
   unsigned long long* trace;  // [C][max_len][kTraceWords] or null
   int max_len;
+  int dma_pages;  // pages in flight per loader wave (1 or 2)
   unsigned epoch;
   unsigned long long timeout_ticks;
   Consts c;
@@ -84,15 +85,40 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+// Cross-lane reductions with DPP (register-to-register lane moves, no LDS):
+// quad_perm [1,0,3,2] and [2,3,0,1] (xor 1, xor 2), row_half_mirror (i -> 7-i
+// within 8 lanes), row_ror 4 / 8 (rotate within 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+enum : int { DppXor1 = 0xB1, DppXor2 = 0x4E, DppHalfMirror = 0x141, DppRor4 = 0x124, DppRor8 = 0x128 };
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// every lane of each 16-lane row ends with the row's sum
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dppf<DppXor1>(v);
+  v += dppf<DppXor2>(v);
+  v += dppf<DppRor4>(v);
+  v += dppf<DppRor8>(v);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dppf<DppXor1>(v));
+  v = fmaxf(v, dppf<DppXor2>(v));
+  v = fmaxf(v, dppf<DppRor4>(v));
+  v = fmaxf(v, dppf<DppRor8>(v));
   return v;
+}
+// wave-uniform sum / max of one value per lane
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max16(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -283,71 +309,71 @@ __device__ inline void load_act(Act& a, int K, int cw, const GLB float* xf, cons
   }
 }
 
-// Partial dot products of the wave's K range for 'nrows' rows of a tile; rows
-// r < n0 come from segment 0, the rest from segment 1 (row r - n0).  The 16
-// per-lane accumulators are summed across the wave by a butterfly that halves
-// the rows kept at each exchange (xor 32, 16, 8, 4), then xor 2 and 1: 17
-// exchanges instead of 16 full reductions.  Lane l ends with the total of row
-// (l >> 2) & 15; lanes with (l & 3) == 0 write part[row].
-template <class Src>
-__device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part) {
+// Partial dot products of the wave's K range for 'nrows' (<= NR) rows of a
+// tile; rows r < n0 come from segment 0, the rest from segment 1 (row r - n0).
+// Rows past nrows re-read the last row and chunks outside the wave's range
+// re-read chunk 0 (their activations are zero), so every row's load can be
+// issued before any is used: one memory latency per chunk, not per row.  The
+// NR per-lane accumulators are summed across the wave with DPP row sums and
+// scalar adds of the four 16-lane rows (no LDS traffic).
+template <int NR, class Src>
+__device__ inline void gemv_rows_t(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part) {
   const int lane = lane_id();
   const int nch = K / 8;
   const int cpw = (nch + kNW - 1) / kNW;
   const int base = cw * cpw;
-  float acc[kMaxRows];
+  float acc[NR];
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.f;
-  // Rows past nrows re-read the last row and chunks outside the wave's range
-  // re-read chunk 0 (their activations are zero), so every row's load can be
-  // issued before any is used: one memory latency per chunk, not per row.
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
     if (j < a.nc) {
       const int ch = lane + 64 * j;
       const int cb = (ch < cpw && base + ch < nch ? base + ch : 0) * 16;
-      uint4 wv[kMaxRows];
+      uint4 wv[NR];
 #pragma unroll
-      for (int r = 0; r < kMaxRows; ++r) {
+      for (int r = 0; r < NR; ++r) {
         const int rc = r < nrows ? r : nrows - 1;
         const int seg = rc < n0 ? 0 : 1;
         const int rr = rc < n0 ? rc : rc - n0;
         wv[r] = src.ld16(seg, rr * K * 2 + cb);
       }
 #pragma unroll
-      for (int r = 0; r < kMaxRows; ++r) {
-        {
-          const uint4 u = wv[r];
-          float s = acc[r];
-          s = fmaf(bf16lo(u.x), a.x[j][0], s);
-          s = fmaf(bf16hi(u.x), a.x[j][1], s);
-          s = fmaf(bf16lo(u.y), a.x[j][2], s);
-          s = fmaf(bf16hi(u.y), a.x[j][3], s);
-          s = fmaf(bf16lo(u.z), a.x[j][4], s);
-          s = fmaf(bf16hi(u.z), a.x[j][5], s);
-          s = fmaf(bf16lo(u.w), a.x[j][6], s);
-          s = fmaf(bf16hi(u.w), a.x[j][7], s);
-          acc[r] = s;
-        }
+      for (int r = 0; r < NR; ++r) {
+        const uint4 u = wv[r];
+        float s = acc[r];
+        s = fmaf(bf16lo(u.x), a.x[j][0], s);
+        s = fmaf(bf16hi(u.x), a.x[j][1], s);
+        s = fmaf(bf16lo(u.y), a.x[j][2], s);
+        s = fmaf(bf16hi(u.y), a.x[j][3], s);
+        s = fmaf(bf16lo(u.z), a.x[j][4], s);
+        s = fmaf(bf16hi(u.z), a.x[j][5], s);
+        s = fmaf(bf16lo(u.w), a.x[j][6], s);
+        s = fmaf(bf16hi(u.w), a.x[j][7], s);
+        acc[r] = s;
       }
     }
   }
-  static_assert(kMaxRows == 16, "the butterfly below reduces 16 rows");
+  // row sums with DPP within each 16-lane row, the four rows combined through
+  // scalar registers; row r's total is placed in lane r for one LDS write
+  float vout = 0.f;
 #pragma unroll
-  for (int half = 8, m = 32; half >= 1; half >>= 1, m >>= 1) {
-    const bool up = (lane & m) != 0;
-#pragma unroll
-    for (int r = 0; r < half; ++r) {
-      const float send = up ? acc[r] : acc[r + half];
-      const float keep = up ? acc[r + half] : acc[r];
-      acc[r] = keep + __shfl_xor(send, m, 64);
-    }
+  for (int r = 0; r < NR; ++r) {
+    const float t = row_sum16(acc[r]);
+    const float tot = (readlane_f(t, 0) + readlane_f(t, 16)) + (readlane_f(t, 32) + readlane_f(t, 48));
+    vout = lane == r ? tot : vout;
   }
-  float v = acc[0];
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 1, 64);
-  const int row = (lane >> 2) & 15;
-  if ((lane & 3) == 0 && row < nrows) part[row] = v;
+  if (lane < nrows) part[lane] = vout;
+}
+
+template <class Src>
+__device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part) {
+  if (nrows <= 4)
+    gemv_rows_t<4>(src, a, K, cw, n0, nrows, part);
+  else if (nrows <= 8)
+    gemv_rows_t<8>(src, a, K, cw, n0, nrows, part);
+  else
+    gemv_rows_t<16>(src, a, K, cw, n0, nrows, part);
 }
 
 // Which activation and norm a GEMV op reads, and its K.
@@ -490,7 +516,7 @@ __device__ __forceinline__ bool is_gemv(int op) {
 // lane ^ 32 for head_dim 64.
 template <int HD, class Src>
 __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t* orow, const Consts& c, int cw,
-                                 LDS float* scr, bool writer) {
+                                 LDS float* scr, bool writer, unsigned long long* tr = nullptr) {
   const int lane = lane_id();
   const int b = ins[WGx], g = ins[WGy], s = ins[WGz];
   const int lo = ins[WPay], hi = ins[WPay + 1], pos = ins[WPay + 2];
@@ -507,7 +533,6 @@ __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t*
   LDS float* qs = scr;            // rotated q, HD floats
   LDS float* kn = scr + HD;       // new k (bf16-rounded), HD
   LDS float* vn = scr + 2 * HD;   // new v (bf16-rounded), HD
-  LDS float* sc = scr + 3 * HD;   // scores
 
   // ---- one batch of global loads
   float qv[PER], kv[PER], vv[PER], cs[PER], sn[PER], wq[PER], wk[PER];
@@ -577,6 +602,7 @@ __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t*
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  if (tr && lane == 0) tr[6] = now_ticks();
   if (!active) return;
   const int n = nk + (has_new ? 1 : 0);
   GLB float* outp = (GLB float*)orow[AttnOut] + ((((size_t)b * c.nkv + g) * c.S + s) * c.hpg + cw) * (HD + 2);
@@ -589,122 +615,136 @@ __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t*
     for (int k = 0; k < PER; ++k) st_agent(outp + 2 + lane + 64 * k, 0.f);
     return;
   }
-  // ---- scores: LPP lanes per position, 8 dims (16 bytes) per lane, PPP
-  // positions per pass, 4 passes' loads issued together
+  // ---- one pass over the split's positions with an online softmax.  Lane
+  // (g, cidx) handles position j = j0 + g of each pass and dims cidx*8..+7:
+  // a 16-byte K chunk and a 16-byte V chunk per pass; the LPP lanes of a
+  // position sum their partial dot products; every lane keeps a running
+  // (max, sum, weighted V) for its positions, and the PPP groups are merged by
+  // log-sum-exp at the end.
   constexpr int LPP = HD / 8;
   constexpr int PPP = 64 / LPP;
-  const int p_in = lane / LPP, cidx = lane % LPP;
+  constexpr int U = 4;  // passes whose loads are issued together
+  const int gi = lane / LPP, cidx = lane % LPP;
   float qc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qc[e] = qs[cidx * 8 + e];
-  for (int j0 = 0; j0 < n; j0 += 4 * PPP) {
-    uint4 u[4];
+  float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
-    for (int pss = 0; pss < 4; ++pss) {
-      int j = j0 + pss * PPP + p_in;
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int j0 = 0; j0 < n; j0 += U * PPP) {
+    uint4 ku[U], vu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int j = j0 + u * PPP + gi;
       j = j < nk ? j : (nk > 0 ? nk - 1 : 0);
-      u[pss] = nk > 0 ? src.ld16(0, j * HD * 2 + cidx * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int pss = 0; pss < 4; ++pss) {
-      const int j = j0 + pss * PPP + p_in;
-      float d;
-      if (j < nk) {
-        d = bf16lo(u[pss].x) * qc[0] + bf16hi(u[pss].x) * qc[1] + bf16lo(u[pss].y) * qc[2] + bf16hi(u[pss].y) * qc[3] +
-            bf16lo(u[pss].z) * qc[4] + bf16hi(u[pss].z) * qc[5] + bf16lo(u[pss].w) * qc[6] + bf16hi(u[pss].w) * qc[7];
+      if (nk > 0) {
+        ku[u] = src.ld16(0, j * HD * 2 + cidx * 16);
+        vu[u] = src.ld16(1, j * HD * 2 + cidx * 16);
       } else {
-        d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d += kn[cidx * 8 + e] * qc[e];
+        ku[u] = vu[u] = make_uint4(0, 0, 0, 0);
       }
+    }
 #pragma unroll
-      for (int m = LPP / 2; m >= 1; m >>= 1) d += __shfl_xor(d, m, 64);
-      if (cidx == 0 && j < n) sc[j] = d * c.inv_sqrt_hd;
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * PPP + gi;
+      float kf[8], vf[8];
+      if (j < nk) {
+        kf[0] = bf16lo(ku[u].x); kf[1] = bf16hi(ku[u].x); kf[2] = bf16lo(ku[u].y); kf[3] = bf16hi(ku[u].y);
+        kf[4] = bf16lo(ku[u].z); kf[5] = bf16hi(ku[u].z); kf[6] = bf16lo(ku[u].w); kf[7] = bf16hi(ku[u].w);
+        vf[0] = bf16lo(vu[u].x); vf[1] = bf16hi(vu[u].x); vf[2] = bf16lo(vu[u].y); vf[3] = bf16hi(vu[u].y);
+        vf[4] = bf16lo(vu[u].z); vf[5] = bf16hi(vu[u].z); vf[6] = bf16lo(vu[u].w); vf[7] = bf16hi(vu[u].w);
+      } else {  // the new row (j == nk) or past the end (masked below)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kf[e] = kn[cidx * 8 + e];
+          vf[e] = vn[cidx * 8 + e];
+        }
+      }
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(kf[e], qc[e], d);
+      // sum over the LPP lanes of this position (8: half a DPP row, 16: a row)
+      d += dppf<DppXor1>(d);
+      d += dppf<DppXor2>(d);
+      d += dppf<DppHalfMirror>(d);
+      if (LPP == 16) d += dppf<DppRor8>(d);
+      if (j < n) {
+        const float sj = d * c.inv_sqrt_hd;
+        const float mn = fmaxf(m, sj);
+        const float al = __expf(m - mn);  // 0 when m = -inf
+        const float pj = __expf(sj - mn);
+        l = l * al + pj;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(pj, vf[e], o[e] * al);
+        m = mn;
+      }
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  float m = -INFINITY;
-  for (int j = lane; j < n; j += 64) m = fmaxf(m, sc[j]);
-  m = wave_max(m);
-  float l = 0.f, o[PER];
+  // merge the PPP position groups
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  // V rows, 8 positions per batch so the loads overlap
-  for (int j0 = 0; j0 < nk; j0 += 8) {
-    float vr[8][PER], pp[8];
+  for (int mm = LPP; mm < 64; mm <<= 1) {
+    const float m2 = __shfl_xor(m, mm, 64);
+    const float l2 = __shfl_xor(l, mm, 64);
+    float o2[8];
 #pragma unroll
-    for (int u2 = 0; u2 < 8; ++u2) {
-      const int j = j0 + u2;
-      const int jc = j < nk ? j : nk - 1;
-      pp[u2] = j < nk ? __expf(sc[j] - m) : 0.f;
+    for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[e], mm, 64);
+    const float M = fmaxf(m, m2);
+    const float a1 = m == -INFINITY ? 0.f : __expf(m - M);
+    const float a2 = m2 == -INFINITY ? 0.f : __expf(m2 - M);
+    l = l * a1 + l2 * a2;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) vr[u2][k] = bf16f(src.ld2(1, (jc * HD + lane + 64 * k) * 2));
-    }
-#pragma unroll
-    for (int u2 = 0; u2 < 8; ++u2) {
-      l += pp[u2];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = fmaf(pp[u2], vr[u2][k], o[k]);
-    }
-  }
-  if (has_new) {
-    const float p = __expf(sc[nk] - m);
-    l += p;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = fmaf(p, vn[lane + 64 * k], o[k]);
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+    m = M;
   }
   if (lane == 0) {
     st_agent(outp, m);
     st_agent(outp + 1, l);
   }
+  if (gi == 0) {
 #pragma unroll
-  for (int k = 0; k < PER; ++k) st_agent(outp + 2 + lane + 64 * k, o[k]);
+    for (int e = 0; e < 8; ++e) st_agent(outp + 2 + cidx * 8 + e, o[e]);
+  }
+  if (tr && lane == 0) tr[7] = now_ticks();
 }
 
 // Merge the S split partials of one query head (log-sum-exp).  Lane s reads
-// split s's (max, sum); the weighted outputs are read 8 splits at a time.
+// split s's (max, sum) and turns it into a weight; the weighted outputs are
+// read 16 splits per batch with clamped (branch-free) addresses so that each
+// batch's loads are issued together.
 template <int HD>
-__device__ inline void combine_wave(const int* ins, const uint64_t* orow, const Consts& c, int cw) {
+__device__ inline void combine_wave(const int* ins, const uint64_t* orow, const Consts& c, int cw,
+                                    unsigned long long* tr = nullptr) {
   if (cw >= c.hpg) return;
   const int lane = lane_id();
   const int b = ins[WGx], g = ins[WGy];
   constexpr int PER = HD / 64;
   const GLB float* part = (const GLB float*)orow[CombPart] + (((size_t)b * c.nkv + g) * c.S * c.hpg + cw) * (HD + 2);
   const size_t stride = (size_t)c.hpg * (HD + 2);
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < c.S; s0 += 64) {
-    const int s = s0 + lane;
-    if (s < c.S) {
-      const float ms = part[s * stride], ls = part[s * stride + 1];
-      if (ls > 0.f) M = fmaxf(M, ms);
-    }
-  }
-  M = wave_max(M);
-  float L = 0.f, o[PER];
+  const int S = c.S;  // <= 64 (checked at plan build)
+  const int sl = lane < S ? lane : S - 1;
+  const float ms = part[sl * stride], ls = part[sl * stride + 1];
+  const bool live = lane < S && ls > 0.f;
+  const float M = wave_max(live ? ms : -INFINITY);
+  const float wsp = live ? __expf(ms - M) : 0.f;
+  const float L = wave_sum(wsp * (live ? ls : 0.f));
+  if (tr && lane == 0) tr[6] = now_ticks();
+  float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int s0 = 0; s0 < c.S; s0 += 8) {
-    float w[8], ov[8][PER];
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float ov[16][PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      w[u] = 0.f;
+    for (int u = 0; u < 16; ++u) {
+      const int s = s0 + u < S ? s0 + u : S - 1;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) ov[u][k] = 0.f;
-      if (s < c.S) {
-        const GLB float* p = part + s * stride;
-        const float ls = p[1];
-        w[u] = ls > 0.f ? __expf(p[0] - M) : 0.f;
-        L = fmaf(w[u], ls > 0.f ? ls : 0.f, L);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) ov[u][k] = p[2 + lane + 64 * k];
-      }
+      for (int k = 0; k < PER; ++k) ov[u][k] = part[s * stride + 2 + lane + 64 * k];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u) {
+      const float w = __shfl(wsp, s0 + u < 64 ? s0 + u : 63, 64);  // 0 for splits >= S
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = fmaf(w[u], ov[u][k], o[k]);
+      for (int k = 0; k < PER; ++k) o[k] = fmaf(s0 + u < S ? w : 0.f, ov[u][k], o[k]);
+    }
   }
   GLB float* out = (GLB float*)orow[CombOut] + (size_t)b * c.nq * HD + (size_t)(g * c.hpg + cw) * HD;
 #pragma unroll

@@ -256,14 +256,18 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
         l2 = last_of;
       }
       ++npend;
-      if (npend == 3) {
-        asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+      // keep at most dma_pages pages in flight: wait for the oldest to land
+      if (npend > a.dma_pages) {
+        if (a.dma_pages == 1)
+          asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else  // 2: npend == 3 here, at most three entries (q0..q2) are ever held
+          asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
         publish(q0, l0);
         q0 = q1;
         l0 = l1;
         q1 = q2;
         l1 = l2;
-        npend = 2;
+        --npend;
       }
     }
   }
@@ -311,10 +315,11 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
       if (cw == 0 && tr && lane == 0) tr[6] = now_ticks();
       gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw]);
       if (lane == 0) L->c.ssp[sl][cw] = act_ss;
+      if (cw == 0 && tr && lane == 0) tr[7] = now_ticks();
     } else if (op == OpAttn) {
-      attn_wave<HD>(src, ins, orow, a.c, cw, L->c.scratch[cw], cw == 0);
+      attn_wave<HD>(src, ins, orow, a.c, cw, L->c.scratch[cw], cw == 0, cw == 0 ? tr : nullptr);
     } else if (op == OpCombine) {
-      combine_wave<HD>(ins, orow, a.c, cw);
+      combine_wave<HD>(ins, orow, a.c, cw, cw == 0 ? tr : nullptr);
     } else if (op == OpArgmax) {
       if (cw == 0) argmax_wave(ins, orow, a.c);
     }
