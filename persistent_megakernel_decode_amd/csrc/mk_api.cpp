@@ -295,6 +295,11 @@ mk_status mk_plan_export(const mk_plan* p, mk_plan_view* v) {
   return MK_OK;
 }
 
+// kCtrSub sub-counter lines per event
+static size_t counter_bytes(const mk_plan* p) {
+  return (size_t)mkd::kCtrSub * std::max(1, p->P.num_events) * mkd::kCtrStride * 4;
+}
+
 static mk_status ensure_device(mk_plan* p) {
   if (p->uploaded) {
     int dev = -1;
@@ -310,7 +315,7 @@ static mk_status ensure_device(mk_plan* p) {
   if (p->num_cus > ncu || occ < 1)
     return fail(MK_E_UNSUPPORTED, "the persistent grid (" + std::to_string(p->num_cus) + " workgroups) cannot be co-resident on " +
                                       std::to_string(ncu) + " CUs");
-  const size_t qbytes = p->P.queue.size() * 4, ebytes = (size_t)std::max(1, p->P.num_events) * 4 * mkd::kCtrStride;
+  const size_t qbytes = p->P.queue.size() * 4, ebytes = counter_bytes(p);
   HIPCHK(hipMalloc(&p->d_queue, qbytes), "hipMalloc queue");
   HIPCHK(hipMalloc(&p->d_counters, ebytes), "hipMalloc counters");
   HIPCHK(hipMalloc(&p->d_err, 64), "hipMalloc err");
@@ -434,6 +439,7 @@ static mkd::KArgs kargs(const mk_plan* p) {
   a.queue = p->d_queue;
   a.optab = p->d_optab;
   a.counters = p->d_counters;
+  a.num_events = std::max(1, p->P.num_events);
   a.err = p->d_err;
   a.trace = p->trace_on ? p->d_trace : nullptr;
   a.max_len = p->P.max_len;
@@ -454,7 +460,7 @@ mk_status mk_run(mk_plan* p, const mk_weights* w, void* kv_cache, const void* to
   st = bind_operands(p, w, kv_cache, tokens, s);
   if (st != MK_OK) return st;
   if (p->need_reset) {
-    HIPCHK(hipMemsetAsync(p->d_counters, 0, (size_t)std::max(1, p->P.num_events) * 4 * mkd::kCtrStride, s), "reset counters");
+    HIPCHK(hipMemsetAsync(p->d_counters, 0, counter_bytes(p), s), "reset counters");
     p->epoch = 0;
     p->need_reset = false;
   }
@@ -524,14 +530,17 @@ mk_status mk_plan_check(mk_plan* p, void* stream, mk_check* out) {
   std::memset(out, 0, sizeof(*out));
   if (p->graph_only || !p->uploaded) return fail(MK_E_STATE, "the plan has not run");
   HIPCHK(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
-  std::vector<uint32_t> ctr((size_t)std::max(1, p->P.num_events) * mkd::kCtrStride);
+  std::vector<uint32_t> ctr(counter_bytes(p) / 4);
   uint32_t err[16];
   HIPCHK(hipMemcpy(ctr.data(), p->d_counters, ctr.size() * 4, hipMemcpyDeviceToHost), "read counters");
   HIPCHK(hipMemcpy(err, p->d_err, 64, hipMemcpyDeviceToHost), "read err");
   out->epoch = p->epoch;
   int bad = 0;
-  for (int e = 0; e < p->P.num_events; ++e)
-    if (ctr[(size_t)e * mkd::kCtrStride] != p->epoch * p->P.event_target[e]) ++bad;
+  for (int e = 0; e < p->P.num_events; ++e) {
+    uint32_t sum = 0;  // modulo 2^32, as the device compares
+    for (int k = 0; k < mkd::kCtrSub; ++k) sum += ctr[mkd::ctr_word(e, k, p->P.num_events)];
+    if (sum != p->epoch * p->P.event_target[e]) ++bad;
+  }
   out->bad_counters = bad;
   out->counters_ok = bad == 0;
   if (err[0] != 0 && err[0] == p->epoch) {

@@ -12,6 +12,11 @@
 // Global memory (address space 1): pointers taken from the operand table are
 // cast to it so loads and stores are global_* (vmcnt only), not flat_*.
 #define GLB __attribute__((address_space(1)))
+// Constant address space (4): the instruction queue and the operand table are
+// never written while a kernel runs; reading them through such pointers gives
+// scalar loads (the scalar cache), which do not queue in the vector-memory
+// pipeline behind the weight stream.
+#define CST __attribute__((address_space(4)))
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -53,6 +58,14 @@ constexpr int kMaxChunks = 6; // 16-byte activation chunks per lane (K / (8 * kN
 constexpr int kScratch = 512; // floats of per-compute-wave scratch
 constexpr int kTraceWords = 16; // timestamps per traced instruction
 constexpr int kCtrStride = 64;  // u32 words between event counters: one 256-byte line each
+// Each event is counted in kCtrSub sub-counters (a producer on compute unit c
+// adds to sub-counter c mod kCtrSub; a waiter sums all of them), so the atomic
+// adds of one event's many producers do not all serialize on one line.
+// Sub-counter k of event e is word ctr_word(e, k, E) of the counter buffer.
+constexpr int kCtrSub = 16;
+__host__ __device__ inline size_t ctr_word(int e, int k, int num_events) {
+  return ((size_t)k * num_events + e) * kCtrStride;
+}
 
 struct Consts {
   int H, nq, nkv, hd, F, V, L, B, cap, hpg, RPG, S, T_v, qk_norm;
@@ -62,7 +75,8 @@ struct Consts {
 struct KArgs {
   const int* queue;           // [C][max_len][32]
   const uint64_t* optab;      // [num_ops][16]
-  unsigned* counters;         // [num_events]
+  unsigned* counters;         // [kCtrSub][num_events] lines (ctr_word)
+  int num_events;
   unsigned* err;              // watchdog record [8]
   unsigned long long* trace;  // [C][max_len][kTraceWords] or null
   int max_len;
@@ -111,6 +125,14 @@ __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, dppf<DppRor8>(v));
   return v;
 }
+// sum of lanes 0-15 (integer), wave-uniform
+__device__ __forceinline__ unsigned row0_sum_u32(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, DppXor1, 0xF, 0xF, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, DppXor2, 0xF, 0xF, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, DppRor4, 0xF, 0xF, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, DppRor8, 0xF, 0xF, false);
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 0);
+}
 // wave-uniform sum / max of one value per lane
 __device__ __forceinline__ float wave_sum(float v) {
   v = row_sum16(v);
@@ -141,8 +163,34 @@ __device__ __forceinline__ int token0(const uint64_t tokens_ptr, int V) {
   int t = ((const GLB int*)tokens_ptr)[0];
   return t < 0 ? 0 : (t >= V ? V - 1 : t);
 }
-__device__ __forceinline__ int ld_word(const int* ins, int w) { return ins[w]; }
 __device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// ---- instruction metadata ---------------------------------------------------------
+// An instruction's 32 words and its operand-table row (16 u64) form a 64-dword
+// record.  The interpreter's waves read it from a copy in LDS with one load per
+// lane (lane l holds dword l) and take fields out with v_readlane, which
+// returns them wave-uniform (in scalar registers) without further memory
+// round trips.  The loader reads the records straight from device memory.
+struct Meta {
+  uint32_t v;  // lane l < 32: instruction word l; lane 32 + j: dword j of the operand row
+  __device__ __forceinline__ int w(int k) const { return __builtin_amdgcn_readlane((int)v, k); }
+  __device__ __forceinline__ uint64_t q(int k) const {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)v, 33 + 2 * k) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)v, 32 + 2 * k);
+  }
+};
+__device__ __forceinline__ Meta load_meta(const LDS uint32_t* rec) {
+  Meta m;
+  m.v = rec[threadIdx.x & 63];
+  return m;
+}
+// The same fields through scalar loads from the queue and the operand table.
+struct GMeta {
+  const CST int* ins;
+  const CST uint64_t* row;
+  __device__ __forceinline__ int w(int k) const { return ins[k]; }
+  __device__ __forceinline__ uint64_t q(int k) const { return row[k]; }
+};
 
 // ---- tile byte layout ---------------------------------------------------------
 // A tile's weight bytes are one or two contiguous source segments placed one
@@ -158,49 +206,50 @@ struct Tile {
 
 __device__ __forceinline__ int round1k(int v) { return (v + 1023) & ~1023; }
 
-__device__ inline Tile tile_info(const int* ins, const uint64_t* orow, const Consts& c) {
+template <class M>
+__device__ inline Tile tile_info(const M& m, const Consts& c) {
   Tile t;
   t.p0 = nullptr;
   t.p1 = nullptr;
   t.len0 = t.off1 = t.len1 = 0;
-  const int op = ins[WOpcode];
+  const int op = m.w(WOpcode);
   switch (op) {
     case OpQkv: {
-      const int g = ins[WGx], row0 = ins[WPay], nrows = ins[WPay + 1];
+      const int g = m.w(WGx), row0 = m.w(WPay), nrows = m.w(WPay + 1);
       const int qrows = c.hpg * c.hd;
       if (row0 < qrows)
-        t.p0 = (const GLB char*)orow[QkvWq] + ((size_t)g * qrows + row0) * c.H * 2;
+        t.p0 = (const GLB char*)m.q(QkvWq) + ((size_t)g * qrows + row0) * c.H * 2;
       else if (row0 < qrows + c.hd)
-        t.p0 = (const GLB char*)orow[QkvWk] + ((size_t)g * c.hd + row0 - qrows) * c.H * 2;
+        t.p0 = (const GLB char*)m.q(QkvWk) + ((size_t)g * c.hd + row0 - qrows) * c.H * 2;
       else
-        t.p0 = (const GLB char*)orow[QkvWv] + ((size_t)g * c.hd + row0 - qrows - c.hd) * c.H * 2;
+        t.p0 = (const GLB char*)m.q(QkvWv) + ((size_t)g * c.hd + row0 - qrows - c.hd) * c.H * 2;
       t.len0 = nrows * c.H * 2;
       break;
     }
     case OpOproj:
-      t.p0 = (const GLB char*)orow[OWo] + (size_t)ins[WPay] * c.nq * c.hd * 2;
-      t.len0 = ins[WPay + 1] * c.nq * c.hd * 2;
+      t.p0 = (const GLB char*)m.q(OWo) + (size_t)m.w(WPay) * c.nq * c.hd * 2;
+      t.len0 = m.w(WPay + 1) * c.nq * c.hd * 2;
       break;
     case OpGateUp:
-      t.p0 = (const GLB char*)orow[GuWg] + (size_t)ins[WPay] * c.H * 2;
-      t.p1 = (const GLB char*)orow[GuWu] + (size_t)ins[WPay] * c.H * 2;
-      t.len0 = t.len1 = ins[WPay + 1] * c.H * 2;
+      t.p0 = (const GLB char*)m.q(GuWg) + (size_t)m.w(WPay) * c.H * 2;
+      t.p1 = (const GLB char*)m.q(GuWu) + (size_t)m.w(WPay) * c.H * 2;
+      t.len0 = t.len1 = m.w(WPay + 1) * c.H * 2;
       break;
     case OpDown:
-      t.p0 = (const GLB char*)orow[DnW] + (size_t)ins[WPay] * c.F * 2;
-      t.len0 = ins[WPay + 1] * c.F * 2;
+      t.p0 = (const GLB char*)m.q(DnW) + (size_t)m.w(WPay) * c.F * 2;
+      t.len0 = m.w(WPay + 1) * c.F * 2;
       break;
     case OpLmHead:
-      t.p0 = (const GLB char*)orow[LmW] + (size_t)ins[WPay] * c.H * 2;
-      t.len0 = ins[WPay + 1] * c.H * 2;
+      t.p0 = (const GLB char*)m.q(LmW) + (size_t)m.w(WPay) * c.H * 2;
+      t.len0 = m.w(WPay + 1) * c.H * 2;
       break;
     case OpAttn: {
-      const int b = ins[WGx], g = ins[WGy], lo = ins[WPay], hi = ins[WPay + 1], pos = ins[WPay + 2];
+      const int b = m.w(WGx), g = m.w(WGy), lo = m.w(WPay), hi = m.w(WPay + 1), pos = m.w(WPay + 2);
       int nk = (hi < pos ? hi : pos) - lo;
       if (nk < 0) nk = 0;
       const size_t base = (((size_t)b * c.nkv + g) * c.cap + lo) * c.hd * 2;
-      t.p0 = (const GLB char*)orow[AttnK] + base;
-      t.p1 = (const GLB char*)orow[AttnV] + base;
+      t.p0 = (const GLB char*)m.q(AttnK) + base;
+      t.p1 = (const GLB char*)m.q(AttnV) + base;
       t.len0 = t.len1 = nk * c.hd * 2;
       break;
     }
@@ -214,22 +263,36 @@ __device__ inline Tile tile_info(const int* ins, const uint64_t* orow, const Con
 }
 
 // ---- weight sources -------------------------------------------------------------
-// LDS page ring: page j of the tile lives in ring slot (first + j) mod kNumPages.
+// LDS page ring: page j of the tile lives in ring slot (first + j) mod kNumPages,
+// so tile byte t sits at ring offset (first * kPage + t) mod (kNumPages * kPage).
+// The tile spans at most kNumPages pages, so the modulo is one conditional
+// subtraction: min over unsigned of x and x - ring size (the second wraps to a
+// huge value while x is below the ring size).  The uniform part of x is scalar.
 struct LdsSrc {
-  const LDS char* ring;
-  int first_slot;
-  int off1;
-  __device__ __forceinline__ const LDS char* at(int seg, int o) const {
-    const int t = (seg ? off1 : 0) + o;
-    int slot = first_slot + (t >> 14);
-    if (slot >= kNumPages) slot -= kNumPages;
-    return ring + slot * kPage + (t & (kPage - 1));
+  uint32_t ring;   // LDS byte address of ring slot 0
+  uint32_t first;  // first * kPage
+  uint32_t off1;   // tile offset of segment 1
+  __device__ __forceinline__ uint32_t addr(int seg, uint32_t o) const {
+    const uint32_t x = first + (seg ? off1 : 0u) + o;
+    const uint32_t y = x - (uint32_t)(kNumPages * kPage);
+    return ring + (x < y ? x : y);
   }
   __device__ __forceinline__ uint4 ld16(int seg, int o) const {
-    const u32x4 v = *(const LDS u32x4*)at(seg, o);
+    const u32x4 v = *(const LDS u32x4*)(uintptr_t)addr(seg, (uint32_t)o);
     return make_uint4(v.x, v.y, v.z, v.w);
   }
-  __device__ __forceinline__ uint16_t ld2(int seg, int o) const { return *(const LDS uint16_t*)at(seg, o); }
+  __device__ __forceinline__ uint16_t ld2(int seg, int o) const {
+    return *(const LDS uint16_t*)(uintptr_t)addr(seg, (uint32_t)o);
+  }
+};
+// A tile whose pages do not wrap around the ring end: plain offsets.
+struct LdsLin {
+  uint32_t base;  // LDS byte address of the tile's first page
+  uint32_t off1;
+  __device__ __forceinline__ uint4 ld16(int seg, int o) const {
+    const u32x4 v = *(const LDS u32x4*)(uintptr_t)(base + (seg ? off1 : 0u) + (uint32_t)o);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
 };
 // Straight from device memory (layerwise kernels).
 struct GlbSrc {
@@ -244,8 +307,8 @@ struct GlbSrc {
 
 // ---- activations of a GEMV tile ---------------------------------------------
 // Each compute wave owns about K / kNW consecutive input elements; lane l holds the
-// 16-byte chunks l, l + 64, ... of that range as fp32 (times the RMSNorm
-// weight when the op fuses a norm), plus its partial sum of squares.
+// 16-byte chunks l, l + 64, ... of that range as fp32 (times the RMSNorm weight
+// when the op fuses a norm), plus its partial sum of squares.
 struct Act {
   float x[kMaxChunks][8];
   float ss;
@@ -309,19 +372,36 @@ __device__ inline void load_act(Act& a, int K, int cw, const GLB float* xf, cons
   }
 }
 
+// Cross-lane butterflies of gfx950: permlane32_swap exchanges the upper half
+// of x with the lower half of y, so the sum holds x's pairwise (l, l + 32) sums
+// in lanes 0-31 and y's in lanes 32-63; permlane16_swap exchanges the odd
+// 16-lane rows of x with the even rows of y, so the sum holds x's (row 0 + row
+// 1) in row 0, y's in row 1, x's (row 2 + row 3) in row 2 and y's in row 3.
+__device__ __forceinline__ float swap_sum32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Partial dot products of the wave's K range for 'nrows' (<= NR) rows of a
 // tile; rows r < n0 come from segment 0, the rest from segment 1 (row r - n0).
 // Rows past nrows re-read the last row and chunks outside the wave's range
-// re-read chunk 0 (their activations are zero), so every row's load can be
-// issued before any is used: one memory latency per chunk, not per row.  The
-// NR per-lane accumulators are summed across the wave with DPP row sums and
-// scalar adds of the four 16-lane rows (no LDS traffic).
+// re-read chunk 0 (their activations are zero), so every row's load is issued
+// before any is used.  The NR per-lane accumulators are summed across the wave
+// by halving butterflies: NR values per lane -> NR/2 (lane halves) -> NR/4
+// (16-lane rows) -> DPP sums within each row, after which row R of the wave
+// holds tile rows r + (NR/4) R, r < NR/4.
 template <int NR, class Src>
 __device__ inline void gemv_rows_t(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part) {
+  static_assert(NR == 4 || NR == 8 || NR == 16, "tile rows");
   const int lane = lane_id();
   const int nch = K / 8;
   const int cpw = (nch + kNW - 1) / kNW;
   const int base = cw * cpw;
+  const int rb = K * 2;
   float acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = 0.f;
@@ -336,7 +416,7 @@ __device__ inline void gemv_rows_t(const Src& src, const Act& a, int K, int cw, 
         const int rc = r < nrows ? r : nrows - 1;
         const int seg = rc < n0 ? 0 : 1;
         const int rr = rc < n0 ? rc : rc - n0;
-        wv[r] = src.ld16(seg, rr * K * 2 + cb);
+        wv[r] = src.ld16(seg, rr * rb + cb);
       }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -354,16 +434,18 @@ __device__ inline void gemv_rows_t(const Src& src, const Act& a, int K, int cw, 
       }
     }
   }
-  // row sums with DPP within each 16-lane row, the four rows combined through
-  // scalar registers; row r's total is placed in lane r for one LDS write
-  float vout = 0.f;
+  constexpr int H2 = NR / 2, P = NR / 4;
+  float u[H2], v[P];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const float t = row_sum16(acc[r]);
-    const float tot = (readlane_f(t, 0) + readlane_f(t, 16)) + (readlane_f(t, 32) + readlane_f(t, 48));
-    vout = lane == r ? tot : vout;
-  }
-  if (lane < nrows) part[lane] = vout;
+  for (int r = 0; r < H2; ++r) u[r] = swap_sum32(acc[r], acc[r + H2]);
+#pragma unroll
+  for (int r = 0; r < P; ++r) v[r] = row_sum16(swap_sum16(u[r], u[r + P]));
+  const int c = lane & 15, R = lane >> 4;
+  float o = v[0];
+#pragma unroll
+  for (int r = 1; r < P; ++r) o = c == r ? v[r] : o;
+  const int row = c + P * R;
+  if (c < P && row < nrows) part[row] = o;
 }
 
 template <class Src>
@@ -385,42 +467,42 @@ struct GemvIn {
   int n0, nrows;  // rows in segment 0, total rows
 };
 
-__device__ inline GemvIn gemv_input(const int* ins, const uint64_t* orow, const Consts& c) {
+__device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
   GemvIn g;
   g.xf = nullptr;
   g.xb = nullptr;
   g.nw = nullptr;
-  const int op = ins[WOpcode];
+  const int op = m.w(WOpcode);
   switch (op) {
     case OpQkv:
       g.K = c.H;
-      g.nw = (const GLB uint16_t*)orow[QkvNorm];
-      if (orow[QkvX]) g.xf = (const GLB float*)orow[QkvX];
-      else g.xb = (const GLB uint16_t*)orow[QkvEmbed] + (size_t)token0(orow[QkvTokens], c.V) * c.H;
-      g.n0 = g.nrows = ins[WPay + 1];
+      g.nw = (const GLB uint16_t*)m.q(QkvNorm);
+      if (m.q(QkvX)) g.xf = (const GLB float*)m.q(QkvX);
+      else g.xb = (const GLB uint16_t*)m.q(QkvEmbed) + (size_t)token0(m.q(QkvTokens), c.V) * c.H;
+      g.n0 = g.nrows = m.w(WPay + 1);
       break;
     case OpOproj:
       g.K = c.nq * c.hd;
-      g.xf = (const GLB float*)orow[OIn];
-      g.n0 = g.nrows = ins[WPay + 1];
+      g.xf = (const GLB float*)m.q(OIn);
+      g.n0 = g.nrows = m.w(WPay + 1);
       break;
     case OpGateUp:
       g.K = c.H;
-      g.nw = (const GLB uint16_t*)orow[GuNorm];
-      g.xf = (const GLB float*)orow[GuIn];
-      g.n0 = ins[WPay + 1];
-      g.nrows = 2 * ins[WPay + 1];
+      g.nw = (const GLB uint16_t*)m.q(GuNorm);
+      g.xf = (const GLB float*)m.q(GuIn);
+      g.n0 = m.w(WPay + 1);
+      g.nrows = 2 * m.w(WPay + 1);
       break;
     case OpDown:
       g.K = c.F;
-      g.xf = (const GLB float*)orow[DnIn];
-      g.n0 = g.nrows = ins[WPay + 1];
+      g.xf = (const GLB float*)m.q(DnIn);
+      g.n0 = g.nrows = m.w(WPay + 1);
       break;
     default:  // OpLmHead
       g.K = c.H;
-      g.nw = (const GLB uint16_t*)orow[LmNorm];
-      g.xf = (const GLB float*)orow[LmIn];
-      g.n0 = g.nrows = ins[WPay + 1];
+      g.nw = (const GLB uint16_t*)m.q(LmNorm);
+      g.xf = (const GLB float*)m.q(LmIn);
+      g.n0 = g.nrows = m.w(WPay + 1);
       break;
   }
   return g;
@@ -429,25 +511,25 @@ __device__ inline GemvIn gemv_input(const int* ins, const uint64_t* orow, const 
 // Residual input of a GEMV tile's rows (O projection: the residual stream or,
 // in layer 0, the embedding row; down projection: the post-attention stream),
 // one value per lane < nrows; loaded ahead of the epilogue.
-__device__ inline float gemv_residual(const int* ins, const uint64_t* orow, const Consts& c) {
+__device__ inline float gemv_residual(const Meta& m, const Consts& c) {
   const int lane = lane_id();
-  const int op = ins[WOpcode];
-  const int row0 = ins[WPay], nr = ins[WPay + 1];
+  const int op = m.w(WOpcode);
+  const int row0 = m.w(WPay), nr = m.w(WPay + 1);
   const int rr = row0 + (lane < nr ? lane : 0);
   if (op == OpOproj)
-    return orow[OX] ? ((const GLB float*)orow[OX])[rr]
-                    : bf16f(((const GLB uint16_t*)orow[OEmbed])[(size_t)token0(orow[OTokens], c.V) * c.H + rr]);
-  if (op == OpDown) return ((const GLB float*)orow[DnRes])[rr];
+    return m.q(OX) ? ((const GLB float*)m.q(OX))[rr]
+                    : bf16f(((const GLB uint16_t*)m.q(OEmbed))[(size_t)token0(m.q(OTokens), c.V) * c.H + rr]);
+  if (op == OpDown) return ((const GLB float*)m.q(DnRes))[rr];
   return 0.f;
 }
 
 // Epilogue of a GEMV tile, run by one wave once every compute wave's partials
 // (part[w][r]) and partial sums of squares (ssp[w]) are in LDS.
-__device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const Consts& c,
+__device__ inline void gemv_epilogue(const Meta& m, const Consts& c,
                                      const LDS float (*part)[kMaxRows], const LDS float* ssp, float res) {
   const int lane = lane_id();
-  const int op = ins[WOpcode];
-  const GemvIn g = gemv_input(ins, orow, c);
+  const int op = m.w(WOpcode);
+  const GemvIn g = gemv_input(m, c);
   float scale = 1.f;
   if (g.nw) {
     float ss = 0.f;
@@ -461,24 +543,24 @@ __device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const
     for (int w = 0; w < kNW; ++w) v += part[w][lane];
     v *= scale;
   }
-  const int row0 = ins[WPay], nr = ins[WPay + 1];
+  const int row0 = m.w(WPay), nr = m.w(WPay + 1);
   switch (op) {
     case OpQkv:
-      if (lane < nr) st_agent((GLB float*)orow[QkvOut] + (size_t)ins[WGx] * c.RPG + row0 + lane, v);
+      if (lane < nr) st_agent((GLB float*)m.q(QkvOut) + (size_t)m.w(WGx) * c.RPG + row0 + lane, v);
       break;
     case OpOproj:
-      if (lane < nr) st_agent((GLB float*)orow[OOut] + row0 + lane, res + v);
+      if (lane < nr) st_agent((GLB float*)m.q(OOut) + row0 + lane, res + v);
       break;
     case OpGateUp: {
       float u = __shfl(v, lane + nr, 64);  // up row j sits at tile row nr + j
-      if (lane < nr) st_agent((GLB float*)orow[GuOut] + row0 + lane, v / (1.f + __expf(-v)) * u);
+      if (lane < nr) st_agent((GLB float*)m.q(GuOut) + row0 + lane, v / (1.f + __expf(-v)) * u);
       break;
     }
     case OpDown:
-      if (lane < nr) st_agent((GLB float*)orow[DnOut] + row0 + lane, res + v);
+      if (lane < nr) st_agent((GLB float*)m.q(DnOut) + row0 + lane, res + v);
       break;
     case OpLmHead: {
-      if (lane < nr) ((GLB float*)orow[LmLogits])[row0 + lane] = v;
+      if (lane < nr) ((GLB float*)m.q(LmLogits))[row0 + lane] = v;
       // tile max, lowest row on ties
       float bv = lane < nr ? v : -INFINITY;
       int bi = lane < nr ? row0 + lane : 0x7FFFFFFF;
@@ -492,7 +574,7 @@ __device__ inline void gemv_epilogue(const int* ins, const uint64_t* orow, const
         }
       }
       if (lane == 0) {
-        GLB float* mx = (GLB float*)orow[LmMax] + 2 * (size_t)ins[WGx];
+        GLB float* mx = (GLB float*)m.q(LmMax) + 2 * (size_t)m.w(WGx);
         st_agent(mx, bv);
         st_agent((GLB int*)mx + 1, bi);
       }
@@ -515,21 +597,21 @@ __device__ __forceinline__ bool is_gemv(int op) {
 // element d (d +- head_dim/2) is in the same lane for head_dim 128 and in
 // lane ^ 32 for head_dim 64.
 template <int HD, class Src>
-__device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t* orow, const Consts& c, int cw,
+__device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c, int cw,
                                  LDS float* scr, bool writer, unsigned long long* tr = nullptr) {
   const int lane = lane_id();
-  const int b = ins[WGx], g = ins[WGy], s = ins[WGz];
-  const int lo = ins[WPay], hi = ins[WPay + 1], pos = ins[WPay + 2];
+  const int b = mt.w(WGx), g = mt.w(WGy), s = mt.w(WGz);
+  const int lo = mt.w(WPay), hi = mt.w(WPay + 1), pos = mt.w(WPay + 2);
   int nk = (hi < pos ? hi : pos) - lo;
   if (nk < 0) nk = 0;
   const bool has_new = pos >= lo && pos < hi;
   const bool active = cw < c.hpg;
   constexpr int HALF = HD / 2;
   constexpr int PER = HD / 64;  // head elements per lane: d = lane + 64 k
-  const GLB float* qkv = (const GLB float*)orow[AttnQkv] + ((size_t)b * c.nkv + g) * c.RPG;
-  const GLB float* rope = (const GLB float*)orow[AttnRope] + (size_t)b * HD;  // (cos, sin) pairs
-  const GLB uint16_t* qn = c.qk_norm ? (const GLB uint16_t*)orow[AttnQn] : nullptr;
-  const GLB uint16_t* knw = c.qk_norm ? (const GLB uint16_t*)orow[AttnKn] : nullptr;
+  const GLB float* qkv = (const GLB float*)mt.q(AttnQkv) + ((size_t)b * c.nkv + g) * c.RPG;
+  const GLB float* rope = (const GLB float*)mt.q(AttnRope) + (size_t)b * HD;  // (cos, sin) pairs
+  const GLB uint16_t* qn = c.qk_norm ? (const GLB uint16_t*)mt.q(AttnQn) : nullptr;
+  const GLB uint16_t* knw = c.qk_norm ? (const GLB uint16_t*)mt.q(AttnKn) : nullptr;
   LDS float* qs = scr;            // rotated q, HD floats
   LDS float* kn = scr + HD;       // new k (bf16-rounded), HD
   LDS float* vn = scr + 2 * HD;   // new v (bf16-rounded), HD
@@ -591,8 +673,8 @@ __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t*
     }
     if (writer) {
       const size_t row = (((size_t)b * c.nkv + g) * c.cap + pos) * HD;
-      GLB uint16_t* K = (GLB uint16_t*)orow[AttnK] + row;
-      GLB uint16_t* Vv = (GLB uint16_t*)orow[AttnV] + row;
+      GLB uint16_t* K = (GLB uint16_t*)mt.q(AttnK) + row;
+      GLB uint16_t* Vv = (GLB uint16_t*)mt.q(AttnV) + row;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         K[lane + 64 * k] = kb[k];
@@ -605,7 +687,7 @@ __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t*
   if (tr && lane == 0) tr[6] = now_ticks();
   if (!active) return;
   const int n = nk + (has_new ? 1 : 0);
-  GLB float* outp = (GLB float*)orow[AttnOut] + ((((size_t)b * c.nkv + g) * c.S + s) * c.hpg + cw) * (HD + 2);
+  GLB float* outp = (GLB float*)mt.q(AttnOut) + ((((size_t)b * c.nkv + g) * c.S + s) * c.hpg + cw) * (HD + 2);
   if (n == 0) {
     if (lane == 0) {
       st_agent(outp, -INFINITY);
@@ -712,13 +794,13 @@ __device__ inline void attn_wave(const Src& src, const int* ins, const uint64_t*
 // read 16 splits per batch with clamped (branch-free) addresses so that each
 // batch's loads are issued together.
 template <int HD>
-__device__ inline void combine_wave(const int* ins, const uint64_t* orow, const Consts& c, int cw,
+__device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
                                     unsigned long long* tr = nullptr) {
   if (cw >= c.hpg) return;
   const int lane = lane_id();
-  const int b = ins[WGx], g = ins[WGy];
+  const int b = m.w(WGx), g = m.w(WGy);
   constexpr int PER = HD / 64;
-  const GLB float* part = (const GLB float*)orow[CombPart] + (((size_t)b * c.nkv + g) * c.S * c.hpg + cw) * (HD + 2);
+  const GLB float* part = (const GLB float*)m.q(CombPart) + (((size_t)b * c.nkv + g) * c.S * c.hpg + cw) * (HD + 2);
   const size_t stride = (size_t)c.hpg * (HD + 2);
   const int S = c.S;  // <= 64 (checked at plan build)
   const int sl = lane < S ? lane : S - 1;
@@ -746,16 +828,16 @@ __device__ inline void combine_wave(const int* ins, const uint64_t* orow, const 
       for (int k = 0; k < PER; ++k) o[k] = fmaf(s0 + u < S ? w : 0.f, ov[u][k], o[k]);
     }
   }
-  GLB float* out = (GLB float*)orow[CombOut] + (size_t)b * c.nq * HD + (size_t)(g * c.hpg + cw) * HD;
+  GLB float* out = (GLB float*)m.q(CombOut) + (size_t)b * c.nq * HD + (size_t)(g * c.hpg + cw) * HD;
 #pragma unroll
   for (int k = 0; k < PER; ++k) st_agent(out + lane + 64 * k, o[k] / L);
 }
 
 // Reduce the LM-head tile maxima of sequence b in tile order (lowest index on ties).
-__device__ inline void argmax_wave(const int* ins, const uint64_t* orow, const Consts& c) {
+__device__ inline void argmax_wave(const Meta& m, const Consts& c) {
   const int lane = lane_id();
-  const int b = ins[WGx], T = ins[WPay];
-  const GLB float* mx = (const GLB float*)orow[AmMax] + (size_t)b * 2 * T;
+  const int b = m.w(WGx), T = m.w(WPay);
+  const GLB float* mx = (const GLB float*)m.q(AmMax) + (size_t)b * 2 * T;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
   for (int t0 = 0; t0 < T; t0 += 64 * 16) {
@@ -789,7 +871,7 @@ __device__ inline void argmax_wave(const int* ins, const uint64_t* orow, const C
       bi = oi;
     }
   }
-  if (lane == 0) ((GLB int*)orow[AmOut])[b] = bi;
+  if (lane == 0) ((GLB int*)m.q(AmOut))[b] = bi;
 }
 
 }  // namespace mkd

@@ -32,15 +32,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 struct Ctrl {
   int ready_seq, done_seq, abort_flag, pad;
   int slot_full[16];   // generation + 1 of the data in each ring slot (loaders -> compute)
-  int slot_freed[16];  // times each slot was released (compute -> loaders)
-  int slot_rel[16];    // compute waves done with the slot's current page
+  int slot_rel[16];    // compute-wave releases of each slot, cumulative (kNW per use)
   int arrive[4];       // compute waves done with instruction i (slot i % 4)
   float part[4][kNW][kMaxRows];
   float ssp[4][kNW];
   float scratch[kNW][kScratch];
 };
+// Copies of the instructions in flight (instruction i in slot i % kMeta) and of
+// their operand-table rows, staged by the controller.
+constexpr int kMeta = 8;
 struct __attribute__((aligned(16))) Lds {
   char ring[kNumPages][kPage];
+  uint32_t meta[kMeta][64];
   Ctrl c;
 };
 
@@ -103,24 +106,67 @@ __device__ bool wait_lds_ge(const KArgs& a, LDS Lds* L, LDS int* p, int v, int k
   }
 }
 
-__device__ __forceinline__ const int* instr(const KArgs& a, int i) {
-  return a.queue + ((size_t)blockIdx.x * a.max_len + i) * 32;
+__device__ __forceinline__ const CST int* instr(const KArgs& a, int i) {
+  return (const CST int*)(uintptr_t)a.queue + ((size_t)blockIdx.x * a.max_len + i) * 32;
+}
+__device__ __forceinline__ const CST uint64_t* oprow(const KArgs& a, int row) {
+  return (const CST uint64_t*)(uintptr_t)a.optab + (size_t)row * 16;
+}
+
+// Copy instruction j and its operand row into meta record j % kMeta (scalar
+// loads; lane 0 writes).  Past the end of the queue the record is a NoOp.
+__device__ void stage(const KArgs& a, LDS Lds* L, int j) {
+  LDS uint32_t* rec = L->meta[j % kMeta];
+  if (j >= a.max_len) {
+    if (lane_id() == 0) rec[WOpcode] = OpNoop;
+    return;
+  }
+  const CST uint32_t* g = (const CST uint32_t*)instr(a, j);
+  uint32_t w[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) w[k] = g[k];
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) rec[k] = w[k];
+  }
+  const CST uint32_t* gr = (const CST uint32_t*)oprow(a, (int)w[WOpRow]);
+#pragma unroll
+  for (int k = 0; k < 32; ++k) w[k] = gr[k];
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) rec[32 + k] = w[k];
+  }
 }
 
 // ---------------------------------------------------------------------------
 __device__ void controller(const KArgs& a, LDS Lds* L) {
+  stage(a, L, 0);
   for (int i = 0; i < a.max_len; ++i) {
-    const int* ins = instr(a, i);
-    if (ins[WOpcode] == OpNoop) break;
-    if (ins[WWaitCnt]) {
-      const unsigned tgt = a.epoch * (unsigned)ins[WWaitTgt];
-      unsigned* ctr = a.counters + (size_t)ins[WWaitEv] * kCtrStride;
-      unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const Meta m = load_meta(L->meta[i % kMeta]);
+    if (m.w(WOpcode) == OpNoop) {
+      // let the other waves read the NoOp and leave their loops
+      if (lane_id() == 0) lds_store_rel(&L->c.ready_seq, i + 1);
+      break;
+    }
+    // slot (i + 1) % kMeta last held instruction i + 1 - kMeta; the storer reads
+    // the slots of the instruction it is on and of the next one
+    if (i + 2 > kMeta && !wait_lds_ge(a, L, &L->c.done_seq, i + 2 - kMeta, ErrDrain, i)) return;
+    stage(a, L, i + 1);
+    if (m.w(WWaitCnt)) {
+      const unsigned tgt = a.epoch * (unsigned)m.w(WWaitTgt);
+      // lane k < kCtrSub reads sub-counter k; the event's count is their sum
+      const int k = lane_id() < kCtrSub ? lane_id() : 0;
+      unsigned* ctr = a.counters + ctr_word(m.w(WWaitEv), k, a.num_events);
+      auto count = [&]() {
+        const unsigned x = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return row0_sum_u32(lane_id() < kCtrSub ? x : 0u);
+      };
+      unsigned v = count();
       if ((int)(v - tgt) < 0) {
         const unsigned long long t0 = now_ticks();
         for (unsigned it = 0;; ++it) {
           __builtin_amdgcn_s_sleep(4);
-          v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v = count();
           if ((int)(v - tgt) >= 0) break;
           if ((it & 15) == 15) {
             if (aborted(L) || __hip_atomic_load(&a.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
@@ -128,7 +174,7 @@ __device__ void controller(const KArgs& a, LDS Lds* L) {
               return;
             }
             if (now_ticks() - t0 > a.timeout_ticks) {
-              record_error(a, L, ErrEvent, i, ins[WWaitEv], v, tgt);
+              record_error(a, L, ErrEvent, i, m.w(WWaitEv), v, tgt);
               return;
             }
           }
@@ -152,33 +198,34 @@ __device__ void storer(const KArgs& a, LDS Lds* L) {
   const int lane = lane_id();
   unsigned pending = 0;
   for (int i = 0; i < a.max_len; ++i) {
-    const int* ins = instr(a, i);
-    const int op = ins[WOpcode];
-    if (op == OpNoop) break;
-    const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
-    const int sl = i & 3;
-    const bool gemv = is_gemv(op);
     // the residual may be read only once the instruction's event has been
     // acquired (the controller publishes "ready" after its acquire)
     if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
-    const float res = (op == OpOproj || op == OpDown) ? gemv_residual(ins, orow, a.c) : 0.f;
+    const Meta m = load_meta(L->meta[i % kMeta]);
+    const int op = m.w(WOpcode);
+    if (op == OpNoop) break;
+    const int sl = i & 3;
+    const bool gemv = is_gemv(op);
+    const float res = (op == OpOproj || op == OpDown) ? gemv_residual(m, a.c) : 0.f;
     if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
-    if (gemv) gemv_epilogue(ins, orow, a.c, L->c.part[sl], L->c.ssp[sl], res);
+    if (gemv) gemv_epilogue(m, a.c, L->c.part[sl], L->c.ssp[sl], res);
     if (lane == 0) {
       __hip_atomic_store(&L->c.arrive[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       lds_store_rel(&L->c.done_seq, i + 1);
     }
     if (a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 2] = now_ticks();
-    if (ins[WSigCnt]) {
-      pending += (unsigned)ins[WSigInc];
-      const int* nx = i + 1 < a.max_len ? instr(a, i + 1) : nullptr;
-      const bool same_next = nx && nx[WOpcode] != OpNoop && nx[WSigCnt] && nx[WSigEv] == ins[WSigEv];
+    if (m.w(WSigCnt)) {
+      pending += (unsigned)m.w(WSigInc);
+      // the next instruction was staged before this one was published
+      const Meta nx = load_meta(L->meta[(i + 1) % kMeta]);
+      const bool same_next = nx.w(WOpcode) != OpNoop && nx.w(WSigCnt) && nx.w(WSigEv) == m.w(WSigEv);
       if (!same_next) {
         // every output of the run was stored agent-coherent (by this wave or
         // by the compute waves before they arrived): wait for completion, then count
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (lane == 0)
-          __hip_atomic_fetch_add(a.counters + (size_t)ins[WSigEv] * kCtrStride, pending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(a.counters + ctr_word(m.w(WSigEv), blockIdx.x % kCtrSub, a.num_events), pending,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         pending = 0;
       }
     }
@@ -190,7 +237,7 @@ __device__ void storer(const KArgs& a, LDS Lds* L) {
 __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
   const int lane = lane_id();
   const uint32_t full_base = lds_addr(&L->c.slot_full[0]);
-  const uint32_t freed_base = lds_addr(&L->c.slot_freed[0]);
+  const uint32_t rel_base = lds_addr(&L->c.slot_rel[0]);
   // issued-but-unpublished pages (oldest first): page sequence number and, for
   // the trace, the instruction whose last page it is (-1 otherwise); scalars,
   // never indexed
@@ -209,20 +256,24 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
   };
   int seq = 0;
   for (int i = 0; i < a.max_len; ++i) {
-    const int* ins = instr(a, i);
+    const CST int* ins = instr(a, i);
     if (ins[WOpcode] == OpNoop) break;
-    const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
-    const Tile t = tile_info(ins, orow, a.c);
+    GMeta gm;
+    gm.ins = ins;
+    gm.row = oprow(a, ins[WOpRow]);
+    const Tile t = tile_info(gm, a.c);
     const GLB char* dummy = t.len0 > 0 ? t.p0 : t.p1;
     for (int pg = 0; pg < t.npages; ++pg, ++seq) {
       if ((seq & 1) != parity) continue;
+      // the slot's previous page (gen uses ago) must have been released by
+      // every compute wave
       const int slot = seq % kNumPages, gen = seq / kNumPages;
-      if (lds_ld_asm(freed_base + 4 * slot) < gen) {
+      if (lds_ld_asm(rel_base + 4 * slot) < kNW * gen) {
         publish_all();
         const unsigned long long t0 = now_ticks();
         for (unsigned it = 0;; ++it) {
           __builtin_amdgcn_s_sleep(1);
-          if (lds_ld_asm(freed_base + 4 * slot) >= gen) break;
+          if (lds_ld_asm(rel_base + 4 * slot) >= kNW * gen) break;
           if ((it & 31) == 31) {
             if (aborted(L)) return;
             if (now_ticks() - t0 > a.timeout_ticks) {
@@ -234,15 +285,30 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
       }
       if (pg == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 4] = now_ticks();
       LDS char* dst = L->ring[slot];
+      // a page inside one segment streams from one base address; otherwise each
+      // 16-byte chunk picks its segment (chunks past the tile re-read a valid one)
+      const int pofs = pg * kPage;
+      const GLB char* whole = nullptr;
+      if (pofs + kPage <= t.len0)
+        whole = t.p0 + pofs;
+      else if (t.len1 && pofs >= t.off1 && pofs + kPage <= t.off1 + t.len1)
+        whole = t.p1 + (pofs - t.off1);
+      if (whole) {
+        const GLB char* src = whole + lane * 16;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int toff = pg * kPage + j * 1024 + lane * 16;
-        const GLB char* src = dummy;
-        if (toff < t.len0)
-          src = t.p0 + toff;
-        else if (toff >= t.off1 && toff < t.off1 + t.len1)
-          src = t.p1 + (toff - t.off1);
-        __builtin_amdgcn_global_load_lds((const GLB void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
+        for (int j = 0; j < 16; ++j)
+          __builtin_amdgcn_global_load_lds((const GLB void*)(src + j * 1024), (lds_void*)(dst + j * 1024), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int toff = pofs + j * 1024 + lane * 16;
+          const GLB char* src = dummy;
+          if (toff < t.len0)
+            src = t.p0 + toff;
+          else if (toff >= t.off1 && toff < t.off1 + t.len1)
+            src = t.p1 + (toff - t.off1);
+          __builtin_amdgcn_global_load_lds((const GLB void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
+        }
       }
       const int last_of = pg == t.npages - 1 ? i : -1;
       if (npend == 0) {
@@ -283,15 +349,14 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
   Act act;
   float act_ss = 0.f;
   for (int i = 0; i < a.max_len; ++i) {
-    const int* ins = instr(a, i);
-    const int op = ins[WOpcode];
+    if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
+    const Meta m = load_meta(L->meta[i % kMeta]);
+    const int op = m.w(WOpcode);
     if (op == OpNoop) break;
-    const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
-    const Tile t = tile_info(ins, orow, a.c);
+    const Tile t = tile_info(m, a.c);
     unsigned long long* tr = a.trace ? a.trace + ((size_t)blockIdx.x * a.max_len + i) * kTraceWords : nullptr;
     const int first = seq;
     seq += t.npages;
-    if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
     if (!wait_lds_ge(a, L, &L->c.done_seq, i - 3, ErrDrain, i)) return;
     for (int pg = 0; pg < t.npages; ++pg) {
       const int sq = first + pg;
@@ -300,38 +365,43 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
     if (cw == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 1] = now_ticks();
     if (tr && lane == 0) tr[8 + cw] = now_ticks();
     LdsSrc src;
-    src.ring = L->ring[0];
-    src.first_slot = first % kNumPages;
-    src.off1 = t.off1;
+    src.ring = lds_addr(&L->ring[0][0]);
+    src.first = (uint32_t)(first % kNumPages) * kPage;
+    src.off1 = (uint32_t)t.off1;
     const int sl = i & 3;
     const bool gemv = is_gemv(op);
     if (gemv) {
-      const GemvIn gi = gemv_input(ins, orow, a.c);
-      if (ins[WOpRow] != act_row) {
+      const GemvIn gi = gemv_input(m, a.c);
+      if (m.w(WOpRow) != act_row) {
         load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
         act_ss = wave_sum(act.ss);
-        act_row = ins[WOpRow];
+        act_row = m.w(WOpRow);
       }
       if (cw == 0 && tr && lane == 0) tr[6] = now_ticks();
-      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw]);
+      if (first % kNumPages + t.npages <= kNumPages) {
+        LdsLin lin;
+        lin.base = src.ring + src.first;
+        lin.off1 = src.off1;
+        gemv_rows(lin, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw]);
+      } else {
+        gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw]);
+      }
       if (lane == 0) L->c.ssp[sl][cw] = act_ss;
       if (cw == 0 && tr && lane == 0) tr[7] = now_ticks();
     } else if (op == OpAttn) {
-      attn_wave<HD>(src, ins, orow, a.c, cw, L->c.scratch[cw], cw == 0, cw == 0 ? tr : nullptr);
+      attn_wave<HD>(src, m, a.c, cw, L->c.scratch[cw], cw == 0, cw == 0 ? tr : nullptr);
     } else if (op == OpCombine) {
-      combine_wave<HD>(ins, orow, a.c, cw, cw == 0 ? tr : nullptr);
+      combine_wave<HD>(m, a.c, cw, cw == 0 ? tr : nullptr);
     } else if (op == OpArgmax) {
-      if (cw == 0) argmax_wave(ins, orow, a.c);
+      if (cw == 0) argmax_wave(m, a.c);
     }
-    // release this tile's pages
-    for (int pg = 0; pg < t.npages; ++pg) {
-      const int sq = first + pg, slot = sq % kNumPages;
-      if (lane == 0) {
-        const int old = __hip_atomic_fetch_add(&L->c.slot_rel[slot], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (old == kNW - 1) {  // the last compute wave done with this page hands it to the loaders
-          __hip_atomic_store(&L->c.slot_rel[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          lds_store_rel(&L->c.slot_freed[slot], sq / kNumPages + 1);
-        }
+    // release this tile's pages (every LDS read of them has returned: their
+    // values were used); non-returning adds, the loaders wait for kNW per use
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) {
+      for (int pg = 0; pg < t.npages; ++pg) {
+        const int slot = (first + pg) % kNumPages;
+        __hip_atomic_fetch_add(&L->c.slot_rel[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
     if (tr && lane == 0) tr[12 + cw] = now_ticks();
@@ -352,15 +422,21 @@ __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
     for (int k = threadIdx.x; k < n; k += blockDim.x) c[k] = 0;
   }
   __syncthreads();
+  // issue priority: compute and storer waves (the dependency chain) ahead of
+  // the controller, the controller ahead of the loaders
   const int w = threadIdx.x >> 6;
-  if (w == 0)
+  if (w == 0) {
+    __builtin_amdgcn_s_setprio(1);
     controller(a, L);
-  else if (w == 1)
+  } else if (w == 1) {
+    __builtin_amdgcn_s_setprio(2);
     storer(a, L);
-  else if (w < 4)
+  } else if (w < 4) {
     loader(a, L, w - 2);
-  else
+  } else {
+    __builtin_amdgcn_s_setprio(2);
     compute<HD>(a, L, w - 4);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -373,30 +449,37 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   LDS float(*part)[kMaxRows] = (LDS float(*)[kMaxRows])part_s;
   LDS float* ssp = (LDS float*)ssp_s;
   LDS float(*scr)[kScratch] = (LDS float(*)[kScratch])scr_s;
+  __shared__ uint32_t meta_s[64];
   const int t = first_task + blockIdx.x;
-  const int* ins = a.queue + ((size_t)(t % num_cus) * a.max_len + t / num_cus) * 32;
+  const CST uint32_t* gins = (const CST uint32_t*)(uintptr_t)a.queue + ((size_t)(t % num_cus) * a.max_len + t / num_cus) * 32;
+  const CST uint32_t* grow = (const CST uint32_t*)((const CST uint64_t*)(uintptr_t)a.optab + (size_t)gins[WOpRow] * 16);
+  if (threadIdx.x < 32)
+    meta_s[threadIdx.x] = gins[threadIdx.x];
+  else if (threadIdx.x < 64)
+    meta_s[threadIdx.x] = grow[threadIdx.x - 32];
+  __syncthreads();
+  const Meta m = load_meta((const LDS uint32_t*)meta_s);
   const int cw = threadIdx.x >> 6, lane = lane_id();
-  const uint64_t* orow = a.optab + (size_t)ins[WOpRow] * 16;
-  const Tile tl = tile_info(ins, orow, a.c);
+  const Tile tl = tile_info(m, a.c);
   GlbSrc src;
   src.p0 = tl.p0;
   src.p1 = tl.p1 ? tl.p1 : tl.p0;
-  const int op = ins[WOpcode];
+  const int op = m.w(WOpcode);
   if (is_gemv(op)) {
-    const GemvIn gi = gemv_input(ins, orow, a.c);
+    const GemvIn gi = gemv_input(m, a.c);
     Act act;
     load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
     const float ss = wave_sum(act.ss);
     gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw]);
     if (lane == 0) ssp[cw] = ss;
     __syncthreads();
-    if (cw == 0) gemv_epilogue(ins, orow, a.c, part, ssp, gemv_residual(ins, orow, a.c));
+    if (cw == 0) gemv_epilogue(m, a.c, part, ssp, gemv_residual(m, a.c));
   } else if (op == OpAttn) {
-    attn_wave<HD>(src, ins, orow, a.c, cw, scr[cw], cw == 0);
+    attn_wave<HD>(src, m, a.c, cw, scr[cw], cw == 0);
   } else if (op == OpCombine) {
-    combine_wave<HD>(ins, orow, a.c, cw);
+    combine_wave<HD>(m, a.c, cw);
   } else if (op == OpArgmax) {
-    if (cw == 0) argmax_wave(ins, orow, a.c);
+    if (cw == 0) argmax_wave(m, a.c);
   }
 }
 
