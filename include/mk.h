@@ -87,7 +87,7 @@ typedef struct {
  *   K and V rows fit in 64 KiB);
  * timeout_ms: bound of every device-side wait (default 200);
  * dma_pages: 16 KiB pages each of the two weight-loader waves keeps in flight
- *   (1 or 2, default 2): enough to cover HBM latency, few enough that the
+ *   (1 to 3, default 2): enough to cover HBM latency, few enough that the
  *   latency-critical activation reads do not queue behind a deep DMA backlog.
  *   Does not change the plan's schedule metadata. */
 typedef struct {

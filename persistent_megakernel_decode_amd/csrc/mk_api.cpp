@@ -135,9 +135,9 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     o.lm_rows = opts->lm_rows;
     o.attn_splits = opts->attn_splits;
     if (opts->timeout_ms > 0) timeout_ms = opts->timeout_ms;
-    if (opts->dma_pages < 0 || opts->dma_pages > 2) {
+    if (opts->dma_pages < 0 || opts->dma_pages > 3) {
       delete p;
-      return fail(MK_E_INVALID, "dma_pages must be 0 (default), 1 or 2");
+      return fail(MK_E_INVALID, "dma_pages must be 0 (default), 1, 2 or 3");
     }
     if (opts->dma_pages > 0) p->dma_pages = opts->dma_pages;
   }

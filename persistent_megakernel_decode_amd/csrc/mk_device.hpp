@@ -386,54 +386,14 @@ __device__ __forceinline__ float swap_sum16(float x, float y) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Partial dot products of the wave's K range for 'nrows' (<= NR) rows of a
-// tile; rows r < n0 come from segment 0, the rest from segment 1 (row r - n0).
-// Rows past nrows re-read the last row and chunks outside the wave's range
-// re-read chunk 0 (their activations are zero), so every row's load is issued
-// before any is used.  The NR per-lane accumulators are summed across the wave
-// by halving butterflies: NR values per lane -> NR/2 (lane halves) -> NR/4
-// (16-lane rows) -> DPP sums within each row, after which row R of the wave
-// holds tile rows r + (NR/4) R, r < NR/4.
-template <int NR, class Src>
-__device__ inline void gemv_rows_t(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part) {
+// Wave-wide sum of NR per-lane accumulators by halving butterflies: NR values
+// per lane -> NR/2 (lane halves) -> NR/4 (16-lane rows) -> DPP sums within each
+// row, after which row R of the wave holds tile rows r + (NR/4) R, r < NR/4;
+// rows < nrows are written to part[].
+template <int NR>
+__device__ inline void gemv_reduce(const float (&acc)[NR], int nrows, LDS float* part) {
   static_assert(NR == 4 || NR == 8 || NR == 16, "tile rows");
   const int lane = lane_id();
-  const int nch = K / 8;
-  const int cpw = (nch + kNW - 1) / kNW;
-  const int base = cw * cpw;
-  const int rb = K * 2;
-  float acc[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    if (j < a.nc) {
-      const int ch = lane + 64 * j;
-      const int cb = (ch < cpw && base + ch < nch ? base + ch : 0) * 16;
-      uint4 wv[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int rc = r < nrows ? r : nrows - 1;
-        const int seg = rc < n0 ? 0 : 1;
-        const int rr = rc < n0 ? rc : rc - n0;
-        wv[r] = src.ld16(seg, rr * rb + cb);
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const uint4 u = wv[r];
-        float s = acc[r];
-        s = fmaf(bf16lo(u.x), a.x[j][0], s);
-        s = fmaf(bf16hi(u.x), a.x[j][1], s);
-        s = fmaf(bf16lo(u.y), a.x[j][2], s);
-        s = fmaf(bf16hi(u.y), a.x[j][3], s);
-        s = fmaf(bf16lo(u.z), a.x[j][4], s);
-        s = fmaf(bf16hi(u.z), a.x[j][5], s);
-        s = fmaf(bf16lo(u.w), a.x[j][6], s);
-        s = fmaf(bf16hi(u.w), a.x[j][7], s);
-        acc[r] = s;
-      }
-    }
-  }
   constexpr int H2 = NR / 2, P = NR / 4;
   float u[H2], v[P];
 #pragma unroll
@@ -448,14 +408,100 @@ __device__ inline void gemv_rows_t(const Src& src, const Act& a, int K, int cw, 
   if (c < P && row < nrows) part[row] = o;
 }
 
-template <class Src>
-__device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part) {
-  if (nrows <= 4)
-    gemv_rows_t<4>(src, a, K, cw, n0, nrows, part);
-  else if (nrows <= 8)
-    gemv_rows_t<8>(src, a, K, cw, n0, nrows, part);
-  else
-    gemv_rows_t<16>(src, a, K, cw, n0, nrows, part);
+// Partial dot products of the wave's K range for 'nrows' (<= NR) rows of a
+// tile; rows r < n0 come from segment 0, the rest from segment 1 (row r - n0).
+// Rows past nrows re-read the last row and chunks outside the wave's range
+// re-read chunk 0 (their activations are zero), so every load is issued before
+// any is used.  When the wave's share of the tile (NR rows x NC chunks of 16
+// bytes per lane) fits in registers, it is read whole and rel() -- which hands
+// the tile's LDS pages back to the loaders -- runs before the arithmetic;
+// otherwise (NC == 0: any number of chunks, read chunk by chunk) after it.
+template <int NR, int NC, class Src, class Rel>
+__device__ inline void gemv_tile(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part,
+                                 const Rel& rel) {
+  const int lane = lane_id();
+  const int nch = K / 8;
+  const int cpw = (nch + kNW - 1) / kNW;
+  const int base = cw * cpw;
+  const int rb = K * 2;
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+  auto row_load = [&](int j, uint4 (&wv)[NR]) {
+    const int ch = lane + 64 * j;
+    const int cb = (ch < cpw && base + ch < nch ? base + ch : 0) * 16;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int rc = r < nrows ? r : nrows - 1;
+      const int seg = rc < n0 ? 0 : 1;
+      const int rr = rc < n0 ? rc : rc - n0;
+      wv[r] = src.ld16(seg, rr * rb + cb);
+    }
+  };
+  auto fma_rows = [&](int j, const uint4 (&wv)[NR]) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint4 u = wv[r];
+      float s = acc[r];
+      s = fmaf(bf16lo(u.x), a.x[j][0], s);
+      s = fmaf(bf16hi(u.x), a.x[j][1], s);
+      s = fmaf(bf16lo(u.y), a.x[j][2], s);
+      s = fmaf(bf16hi(u.y), a.x[j][3], s);
+      s = fmaf(bf16lo(u.z), a.x[j][4], s);
+      s = fmaf(bf16hi(u.z), a.x[j][5], s);
+      s = fmaf(bf16lo(u.w), a.x[j][6], s);
+      s = fmaf(bf16hi(u.w), a.x[j][7], s);
+      acc[r] = s;
+    }
+  };
+  if constexpr (NC > 0) {
+    uint4 wv[NC][NR];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) row_load(j, wv[j]);
+    rel();
+#pragma unroll
+    for (int j = 0; j < NC; ++j) fma_rows(j, wv[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j) {
+      if (j < a.nc) {
+        uint4 wv[NR];
+        row_load(j, wv);
+        fma_rows(j, wv);
+      }
+    }
+    rel();
+  }
+  gemv_reduce<NR>(acc, nrows, part);
+}
+
+// Tile shapes: NR = 4, 8 or 16 rows; the wave's share is read whole when
+// NR x chunks <= 16 (16 x 16 bytes per lane), which the default tile sizes
+// (rows x K <= 32768) always meet.
+template <class Src, class Rel>
+__device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part,
+                                 const Rel& rel) {
+  const int nc = a.nc;
+  if (nrows <= 4) {
+    switch (nc) {
+      case 1: gemv_tile<4, 1>(src, a, K, cw, n0, nrows, part, rel); break;
+      case 2: gemv_tile<4, 2>(src, a, K, cw, n0, nrows, part, rel); break;
+      case 3: gemv_tile<4, 3>(src, a, K, cw, n0, nrows, part, rel); break;
+      case 4: gemv_tile<4, 4>(src, a, K, cw, n0, nrows, part, rel); break;
+      default: gemv_tile<4, 0>(src, a, K, cw, n0, nrows, part, rel); break;
+    }
+  } else if (nrows <= 8) {
+    switch (nc) {
+      case 1: gemv_tile<8, 1>(src, a, K, cw, n0, nrows, part, rel); break;
+      case 2: gemv_tile<8, 2>(src, a, K, cw, n0, nrows, part, rel); break;
+      default: gemv_tile<8, 0>(src, a, K, cw, n0, nrows, part, rel); break;
+    }
+  } else {
+    if (nc == 1)
+      gemv_tile<16, 1>(src, a, K, cw, n0, nrows, part, rel);
+    else
+      gemv_tile<16, 0>(src, a, K, cw, n0, nrows, part, rel);
+  }
 }
 
 // Which activation and norm a GEMV op reads, and its K.
@@ -833,45 +879,67 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
   for (int k = 0; k < PER; ++k) st_agent(out + lane + 64 * k, o[k] / L);
 }
 
-// Reduce the LM-head tile maxima of sequence b in tile order (lowest index on ties).
-__device__ inline void argmax_wave(const Meta& m, const Consts& c) {
+// Reduce the LM-head tile maxima of sequence b in tile order, lowest index on
+// ties.  Compute wave cw scans the contiguous quarter cw of the T tile maxima,
+// 32 per lane per batch (every load of a batch issued before any is used), and
+// leaves its best (value, index) in out2[0..1]; argmax_final merges the quarters.
+__device__ __forceinline__ bool amax_better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+__device__ inline void argmax_part(const Meta& m, const Consts& c, int cw, LDS float* out2) {
   const int lane = lane_id();
   const int b = m.w(WGx), T = m.w(WPay);
-  const GLB float* mx = (const GLB float*)m.q(AmMax) + (size_t)b * 2 * T;
+  const GLB f32x2* mx = (const GLB f32x2*)m.q(AmMax) + (size_t)b * T;
+  const int per = (T + kNW - 1) / kNW;
+  const int lo = cw * per, hi = lo + per < T ? lo + per : T;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int t0 = 0; t0 < T; t0 += 64 * 16) {
-    float2 pr[16];
+  constexpr int U = 32;
+  for (int t0 = lo; t0 < hi; t0 += 64 * U) {
+    f32x2 pr[U];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int t = t0 + u * 64 + lane;
-      if (t < T) {
-        const f32x2 q = ((const GLB f32x2*)mx)[t];
-        pr[u] = make_float2(q.x, q.y);
-      } else {
-        pr[u] = make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
-      }
+      pr[u] = mx[t < hi ? t : lo];
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float v = pr[u].x;
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * 64 + lane;
       const int i = __float_as_int(pr[u].y);
-      if (v > bv || (v == bv && i < bi)) {
-        bv = v;
+      if (t < hi && amax_better(pr[u].x, i, bv, bi)) {
+        bv = pr[u].x;
         bi = i;
       }
     }
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    float ov = __shfl_xor(bv, m, 64);
-    int oi = __shfl_xor(bi, m, 64);
-    if (ov > bv || (ov == bv && oi < bi)) {
+  for (int msk = 32; msk >= 1; msk >>= 1) {
+    const float ov = __shfl_xor(bv, msk, 64);
+    const int oi = __shfl_xor(bi, msk, 64);
+    if (amax_better(ov, oi, bv, bi)) {
       bv = ov;
       bi = oi;
     }
   }
-  if (lane == 0) ((GLB int*)m.q(AmOut))[b] = bi;
+  if (lane == 0) {
+    out2[0] = bv;
+    out2[1] = __int_as_float(bi);
+  }
+}
+// part[w][0..1]: wave w's (value, index); one wave stores the winner.
+__device__ inline void argmax_final(const Meta& m, const LDS float (*part)[kMaxRows]) {
+  float bv = part[0][0];
+  int bi = __float_as_int(part[0][1]);
+#pragma unroll
+  for (int w = 1; w < kNW; ++w) {
+    const float v = part[w][0];
+    const int i = __float_as_int(part[w][1]);
+    if (amax_better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  if (lane_id() == 0) ((GLB int*)m.q(AmOut))[m.w(WGx)] = bi;
 }
 
 }  // namespace mkd

@@ -63,6 +63,8 @@ __device__ __forceinline__ void lds_st_asm(uint32_t addr, int v) {
 }
 
 __device__ __forceinline__ int lds_load_acq(LDS int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+// Publish an LDS flag: orders the wave's earlier LDS accesses only (a release
+// over all address spaces would also wait for the wave's global stores).
 __device__ __forceinline__ void lds_store_rel(LDS int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
 
 enum { ErrEvent = 1, ErrPage = 2, ErrReady = 3, ErrDrain = 4, ErrFree = 5 };
@@ -208,7 +210,10 @@ __device__ void storer(const KArgs& a, LDS Lds* L) {
     const bool gemv = is_gemv(op);
     const float res = (op == OpOproj || op == OpDown) ? gemv_residual(m, a.c) : 0.f;
     if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
-    if (gemv) gemv_epilogue(m, a.c, L->c.part[sl], L->c.ssp[sl], res);
+    if (gemv)
+      gemv_epilogue(m, a.c, L->c.part[sl], L->c.ssp[sl], res);
+    else if (op == OpArgmax)
+      argmax_final(m, L->c.part[sl]);
     if (lane == 0) {
       __hip_atomic_store(&L->c.arrive[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       lds_store_rel(&L->c.done_seq, i + 1);
@@ -241,7 +246,7 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
   // issued-but-unpublished pages (oldest first): page sequence number and, for
   // the trace, the instruction whose last page it is (-1 otherwise); scalars,
   // never indexed
-  int q0 = 0, q1 = 0, q2 = 0, l0 = -1, l1 = -1, l2 = -1, npend = 0;
+  int q0 = 0, q1 = 0, q2 = 0, q3 = 0, l0 = -1, l1 = -1, l2 = -1, l3 = -1, npend = 0;
   auto publish = [&](int sq, int last_of) {
     lds_st_asm(full_base + 4 * (sq % kNumPages), sq / kNumPages + 1);
     if (a.trace && last_of >= 0 && lane == 0)
@@ -252,6 +257,7 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
     if (npend > 0) publish(q0, l0);
     if (npend > 1) publish(q1, l1);
     if (npend > 2) publish(q2, l2);
+    if (npend > 3) publish(q3, l3);
     npend = 0;
   };
   int seq = 0;
@@ -317,22 +323,32 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
       } else if (npend == 1) {
         q1 = seq;
         l1 = last_of;
-      } else {
+      } else if (npend == 2) {
         q2 = seq;
         l2 = last_of;
+      } else {
+        q3 = seq;
+        l3 = last_of;
       }
       ++npend;
-      // keep at most dma_pages pages in flight: wait for the oldest to land
-      if (npend > a.dma_pages) {
-        if (a.dma_pages == 1)
+      // keep at most 'depth' (1..3) pages in flight: wait for the oldest to
+      // land (16 DMA instructions per page; npend == depth + 1 here, so at most
+      // four entries q0..q3 are ever held)
+      const int depth = a.dma_pages;
+      if (npend > depth) {
+        if (depth == 1)
           asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else  // 2: npend == 3 here, at most three entries (q0..q2) are ever held
+        else if (depth == 2)
           asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
         publish(q0, l0);
         q0 = q1;
         l0 = l1;
         q1 = q2;
         l1 = l2;
+        q2 = q3;
+        l2 = l3;
         --npend;
       }
     }
@@ -364,6 +380,17 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
     }
     if (cw == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 1] = now_ticks();
     if (tr && lane == 0) tr[8 + cw] = now_ticks();
+    // hand the tile's pages back to the loaders once every LDS read of them has
+    // returned (non-returning adds; the loaders wait for kNW per use of a slot)
+    auto release = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane == 0) {
+        for (int pg = 0; pg < t.npages; ++pg) {
+          const int slot = (first + pg) % kNumPages;
+          __hip_atomic_fetch_add(&L->c.slot_rel[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    };
     LdsSrc src;
     src.ring = lds_addr(&L->ring[0][0]);
     src.first = (uint32_t)(first % kNumPages) * kPage;
@@ -382,9 +409,9 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
         LdsLin lin;
         lin.base = src.ring + src.first;
         lin.off1 = src.off1;
-        gemv_rows(lin, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw]);
+        gemv_rows(lin, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw], release);
       } else {
-        gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw]);
+        gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw], release);
       }
       if (lane == 0) L->c.ssp[sl][cw] = act_ss;
       if (cw == 0 && tr && lane == 0) tr[7] = now_ticks();
@@ -393,20 +420,12 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
     } else if (op == OpCombine) {
       combine_wave<HD>(m, a.c, cw, cw == 0 ? tr : nullptr);
     } else if (op == OpArgmax) {
-      if (cw == 0) argmax_wave(m, a.c);
+      argmax_part(m, a.c, cw, L->c.part[sl][cw]);
     }
-    // release this tile's pages (every LDS read of them has returned: their
-    // values were used); non-returning adds, the loaders wait for kNW per use
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) {
-      for (int pg = 0; pg < t.npages; ++pg) {
-        const int slot = (first + pg) % kNumPages;
-        __hip_atomic_fetch_add(&L->c.slot_rel[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    }
+    if (!gemv) release();
     if (tr && lane == 0) tr[12 + cw] = now_ticks();
     // arrival: GEMV partials are in LDS; other ops wrote global memory, which
-    // must be complete before the storer signals (workgroup release = vmcnt(0))
+    // must be complete before the storer signals
     if (!gemv) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_fetch_add(&L->c.arrive[sl], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
@@ -470,7 +489,7 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
     Act act;
     load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
     const float ss = wave_sum(act.ss);
-    gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw]);
+    gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw], [] {});
     if (lane == 0) ssp[cw] = ss;
     __syncthreads();
     if (cw == 0) gemv_epilogue(m, a.c, part, ssp, gemv_residual(m, a.c));
@@ -479,7 +498,9 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   } else if (op == OpCombine) {
     combine_wave<HD>(m, a.c, cw);
   } else if (op == OpArgmax) {
-    if (cw == 0) argmax_wave(m, a.c);
+    argmax_part(m, a.c, cw, part[cw]);
+    __syncthreads();
+    if (cw == 0) argmax_final(m, part);
   }
 }
 
