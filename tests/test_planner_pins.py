@@ -18,36 +18,42 @@ examples and to brute-force region overlap.
   queues give [148, 5, 32] with 140 queues of 5 and 8 of 4.
 """
 import itertools
+import json
+import os
 
 import numpy as np
 import pytest
 
 from oracle import planner as P
 
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_examples.json")))
+
 
 def test_fork_then_join_worked_example():
     ops = [P.Op("F", 1, (4,)), P.Op("A", 2, (4,)), P.Op("B", 3, (2,)), P.Op("G", 4, (4,))]
     edges = [P.Edge(0, 1, (0,), (0,)), P.Edge(0, 2, (0,), (0,)), P.Edge(1, 3, (0,), (0,)), P.Edge(2, 3, (0,), (0,))]
     pl = P.plan_graph(ops, edges, num_cus=8)
-    assert [pl.evd[i][0] for i in range(4)] == [2, 2, 2, 2]
+    fk, jn = GOLD["fork_example"], GOLD["join_example"]
+    assert [pl.evd[i][0] for i in range(4)] == [fk["events_per_edge"]] * 2 + [jn["events"]] * 2
     assert pl.num_events == 4 and pl.num_tasks == 14
     names = [(ops[o].name, x) for (o, x, y, z) in pl.tasks]
     # fork event 0 releases A0, A1, B0; event 1 releases A2, A3, B1
-    assert names[pl.event_first[0]:pl.event_last[0]] == [("A", 0), ("A", 1), ("B", 0)]
-    assert names[pl.event_first[1]:pl.event_last[1]] == [("A", 2), ("A", 3), ("B", 1)]
+    assert names[pl.event_first[0]:pl.event_last[0]] == [tuple(v) for v in fk["event0_releases"]]
+    assert names[pl.event_first[1]:pl.event_last[1]] == [tuple(v) for v in fk["event1_releases"]]
     assert pl.event_target[0] == 2 and pl.event_target[1] == 2  # F tasks {0,1} and {2,3}
     # join events: 2 (A) + 1 (B) triggers, releasing G0-1 and G2-3
-    assert pl.event_target[2:] == [3, 3]
-    assert names[pl.event_first[2]:pl.event_last[2]] == [("G", 0), ("G", 1)]
-    assert names[pl.event_first[3]:pl.event_last[3]] == [("G", 2), ("G", 3)]
+    assert pl.event_target[2:] == [jn["triggers_per_event"]] * jn["events"]
+    for e, rel in enumerate(jn["event_releases"]):
+        assert names[pl.event_first[2 + e]:pl.event_last[2 + e]] == [("G", g) for g in rel]
     trig = {names[t]: pl.trigger[t] for t in range(pl.num_tasks)}
     assert trig[("F", 0)] == trig[("F", 1)] == 0 and trig[("F", 2)] == trig[("F", 3)] == 1
     assert trig[("A", 0)] == trig[("A", 1)] == trig[("B", 0)] == 2
     assert trig[("A", 2)] == trig[("A", 3)] == trig[("B", 1)] == 3
 
 
-@pytest.mark.parametrize("prod,cons,events,triggers", [(128, 128, 128, 1), (128, 64, 64, 2), (128, 1, 1, 128), (128, 127, 1, 128)])
-def test_gcd_examples(prod, cons, events, triggers):
+@pytest.mark.parametrize("prod,cons,events", [tuple(r) for r in GOLD["gcd_table"]["rows"]])
+def test_gcd_examples(prod, cons, events):
+    triggers = prod // events
     ops = [P.Op("P", 1, (prod,)), P.Op("C", 2, (cons,))]
     pl = P.plan_graph(ops, [P.Edge(0, 1, (0,), (0,))], num_cus=256)
     assert pl.num_events == events
@@ -126,10 +132,11 @@ def demo_graph():
 def test_lecture_demo_graph():
     ops, edges = demo_graph()
     pl = P.plan_graph(ops, edges, num_cus=6)
-    assert pl.num_tasks == 28
-    assert pl.num_events == 9
-    assert sum(len(_overlap_pairs(ops, e)) for e in edges) == 52
-    assert _check_happens_before(pl, ops, edges) == 52
+    g = GOLD["lecture_demo"]
+    assert pl.num_tasks == g["tasks"]
+    assert pl.num_events == g["events"]
+    assert sum(len(_overlap_pairs(ops, e)) for e in edges) == g["pairwise_edges"]
+    assert _check_happens_before(pl, ops, edges) == g["pairwise_edges"]
     # tanh task i waits for exactly the 3 GEMV tasks of its 24 elements
     for t, (o, x, y, z) in enumerate(pl.tasks):
         if o == 1:
@@ -167,21 +174,25 @@ def test_lecture_llama1b_layer_counts():
     pl = P.plan_graph(ops, edges, num_cus=132)
     mid = {i for i, op in enumerate(ops) if op.layer == 1}
     tasks = [t for t, (o, x, y, z) in enumerate(pl.tasks) if o in mid]
-    assert len(tasks) == 1984
+    g = GOLD["lecture_llama1b_layer"]
+    assert len(tasks) == g["tasks"]
     events = {pl.wait[t] for t in tasks}
-    assert len(events) == 15
+    assert len(events) == g["events"]
     edges_te = sum((pl.wait[t] >= 0) + (pl.trigger[t] >= 0) for t in tasks)
-    assert edges_te == 3968
-    # ~380K pairwise edges, counted by brute-force region overlap (layer 1's inputs)
+    assert edges_te == g["task_event_edges"]
+    # ~380K pairwise edges (the page gives the rounded figure), counted here by
+    # brute-force region overlap of layer 1's inputs
     pairwise = sum(len(_overlap_pairs(ops, e)) for e in edges if e.cons in mid and not e.name.endswith("_res"))
     assert pairwise == 379904
+    assert abs(pairwise - g["pairwise_edges_approx"]) / g["pairwise_edges_approx"] < 0.01
     assert not any(pl.kept[i] for i, e in enumerate(edges) if e.name.endswith("_res"))
 
 
 def test_round_robin_queue_shape():
-    pl = P.plan_graph([P.Op("t", 1, (732,))], [], num_cus=148)
+    g = GOLD["megartp_queue"]
+    pl = P.plan_graph([P.Op("t", 1, (g["tasks"],))], [], num_cus=g["num_cus"])
     q = np.array(pl.queue)
-    assert q.shape == (148, 5, 32)
+    assert q.shape == tuple(g["queue_shape"])
     valid = (q[:, :, P.W_OPCODE] != 0).sum(axis=1)
     assert list(valid[:140]) == [5] * 140 and list(valid[140:]) == [4] * 8
     assert (q[140:, 4] == 0).all()  # NoOp rows are all zero
