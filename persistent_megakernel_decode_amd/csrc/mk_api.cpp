@@ -156,6 +156,17 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     delete p;
     return fail(MK_E_UNSUPPORTED, "tile rows must be <= 16");
   }
+  // the GEMV tile shapes the kernels instantiate (rows per tile by K)
+  {
+    const int K_h = d.hidden, K_o = d.n_q_heads * d.head_dim, K_f = d.ffn;
+    if (o.gemv_rows > mkd::gemv_max_rows(K_h) || o.gemv_rows > mkd::gemv_max_rows(K_o) ||
+        2 * o.gateup_outs > mkd::gemv_max_rows(K_h) || o.down_rows > mkd::gemv_max_rows(K_f) ||
+        o.lm_rows > mkd::gemv_max_rows(K_h)) {
+      delete p;
+      return fail(MK_E_UNSUPPORTED, "GEMV tile rows exceed the limit for K (16 rows up to K 2048, 8 up to 4096, "
+                                    "4 beyond)");
+    }
+  }
   // every tile's weight bytes must fit the LDS page ring
   auto r1k = [](long v) { return (v + 1023) / 1024 * 1024; };
   const long ring = (long)mkd::kNumPages * mkd::kPage;

@@ -343,6 +343,7 @@ __device__ inline void load_act(Act& a, int K, int cw, const GLB float* xf, cons
       if (nw) wr[j] = *(const GLB u32x4*)(nw + k0);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // one memory latency for all of them
   a.ss = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
@@ -458,6 +459,10 @@ __device__ inline void gemv_tile(const Src& src, const Act& a, int K, int cw, in
     uint4 wv[NC][NR];
 #pragma unroll
     for (int j = 0; j < NC; ++j) row_load(j, wv[j]);
+    // keep every LDS read of the share in flight at once: without this
+    // boundary the scheduler interleaves each read with the previous row's
+    // FMAs and waits for it, paying the LDS latency once per row
+    __builtin_amdgcn_sched_barrier(0);
     rel();
 #pragma unroll
     for (int j = 0; j < NC; ++j) fma_rows(j, wv[j]);
@@ -467,6 +472,7 @@ __device__ inline void gemv_tile(const Src& src, const Act& a, int K, int cw, in
       if (j < a.nc) {
         uint4 wv[NR];
         row_load(j, wv);
+        __builtin_amdgcn_sched_barrier(0);
         fma_rows(j, wv);
       }
     }
@@ -475,33 +481,27 @@ __device__ inline void gemv_tile(const Src& src, const Act& a, int K, int cw, in
   gemv_reduce<NR>(acc, nrows, part);
 }
 
-// Tile shapes: NR = 4, 8 or 16 rows; the wave's share is read whole when
-// NR x chunks <= 16 (16 x 16 bytes per lane), which the default tile sizes
-// (rows x K <= 32768) always meet.
+// Tile shapes, by 16-byte chunks per lane nc = ceil(K / 2048): nc = 1 -> up to
+// 16 rows, nc = 2 -> up to 8, nc = 3..4 -> up to 4 (the wave's share, at most
+// 16 x 16 bytes per lane, is read whole); larger K -> up to 4 rows, chunk by
+// chunk.  Few shapes keep the interpreter's code within the instruction cache;
+// the plan builder rejects tiles with more rows (gemv_max_rows).
+__host__ __device__ inline int gemv_max_rows(int K) {
+  const int nc = (K + 2047) / 2048;
+  return nc <= 1 ? 16 : nc == 2 ? 8 : 4;
+}
 template <class Src, class Rel>
 __device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part,
                                  const Rel& rel) {
   const int nc = a.nc;
-  if (nrows <= 4) {
-    switch (nc) {
-      case 1: gemv_tile<4, 1>(src, a, K, cw, n0, nrows, part, rel); break;
-      case 2: gemv_tile<4, 2>(src, a, K, cw, n0, nrows, part, rel); break;
-      case 3: gemv_tile<4, 3>(src, a, K, cw, n0, nrows, part, rel); break;
-      case 4: gemv_tile<4, 4>(src, a, K, cw, n0, nrows, part, rel); break;
-      default: gemv_tile<4, 0>(src, a, K, cw, n0, nrows, part, rel); break;
-    }
-  } else if (nrows <= 8) {
-    switch (nc) {
-      case 1: gemv_tile<8, 1>(src, a, K, cw, n0, nrows, part, rel); break;
-      case 2: gemv_tile<8, 2>(src, a, K, cw, n0, nrows, part, rel); break;
-      default: gemv_tile<8, 0>(src, a, K, cw, n0, nrows, part, rel); break;
-    }
-  } else {
-    if (nc == 1)
-      gemv_tile<16, 1>(src, a, K, cw, n0, nrows, part, rel);
-    else
-      gemv_tile<16, 0>(src, a, K, cw, n0, nrows, part, rel);
-  }
+  if (nc == 1)
+    gemv_tile<16, 1>(src, a, K, cw, n0, nrows, part, rel);
+  else if (nc == 2)
+    gemv_tile<8, 2>(src, a, K, cw, n0, nrows, part, rel);
+  else if (nc <= 4)
+    gemv_tile<4, 4>(src, a, K, cw, n0, nrows, part, rel);
+  else
+    gemv_tile<4, 0>(src, a, K, cw, n0, nrows, part, rel);
 }
 
 // Which activation and norm a GEMV op reads, and its K.
@@ -772,6 +772,7 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
         ku[u] = vu[u] = make_uint4(0, 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // the batch's LDS reads stay in flight together
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * PPP + gi;
@@ -867,6 +868,7 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
 #pragma unroll
       for (int k = 0; k < PER; ++k) ov[u][k] = part[s * stride + 2 + lane + 64 * k];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const float w = __shfl(wsp, s0 + u < 64 ? s0 + u : 63, 64);  // 0 for splits >= S
@@ -902,6 +904,7 @@ __device__ inline void argmax_part(const Meta& m, const Consts& c, int cw, LDS f
       const int t = t0 + u * 64 + lane;
       pr[u] = mx[t < hi ? t : lo];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * 64 + lane;

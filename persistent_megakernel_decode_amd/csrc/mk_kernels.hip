@@ -405,14 +405,7 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
         act_row = m.w(WOpRow);
       }
       if (cw == 0 && tr && lane == 0) tr[6] = now_ticks();
-      if (first % kNumPages + t.npages <= kNumPages) {
-        LdsLin lin;
-        lin.base = src.ring + src.first;
-        lin.off1 = src.off1;
-        gemv_rows(lin, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw], release);
-      } else {
-        gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw], release);
-      }
+      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw], release);
       if (lane == 0) L->c.ssp[sl][cw] = act_ss;
       if (cw == 0 && tr && lane == 0) tr[7] = now_ticks();
     } else if (op == OpAttn) {

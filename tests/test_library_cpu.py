@@ -49,7 +49,7 @@ def _compare(lib_plan, ref):
     ("tiny", dict(ffn=688 + 32, vocab=4100, kv_len=999), 100, {}),  # ragged FFN and vocab tails
     ("tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128), 256, {}),
     ("llama1b", {}, 256, {}),
-    ("llama1b", {}, 148, dict(gemv_rows=8, down_rows=8)),
+    ("llama1b", {}, 148, dict(gemv_rows=8, down_rows=2)),
     ("qwen3_8b", {}, 256, {}),
 ])
 def test_cpp_planner_matches_reference(name, overrides, num_cus, opts):
@@ -103,6 +103,10 @@ def test_plan_build_rejects_bad_arguments():
     with pytest.raises(mk.MKError) as e:
         mk.Plan.build(dict(cfg, head_dim=96), 1, [10], 100, num_cus=8)
     assert e.value.status == mk.MK_E_UNSUPPORTED
+    # more GEMV rows than the tile shape for K allows (K = 8192: at most 4)
+    with pytest.raises(mk.MKError) as e:
+        mk.Plan.build(synth.config("llama1b"), 1, [10], 100, num_cus=8, down_rows=8)
+    assert e.value.status == mk.MK_E_UNSUPPORTED and b"rows" in mk.lib().mk_last_error()
     d = mk.model_desc(cfg, 100)
     d.struct_size = 4
     h = ctypes.c_void_p()
