@@ -26,6 +26,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-step latency (µs) + achieved HBM GB/s vs peak, Llama-1B-shape bs=1"
 PEAK_GBPS = 8000.0
+SHAPES = {"tiny": "tiny Llama-style", "llama1b": "Llama-3.2-1B-shaped", "llama1b_b16": "Llama-3.2-1B-shaped",
+          "qwen3_8b": "Qwen3-8B-shaped"}
 KERNEL_SOURCES = ["persistent_megakernel_decode_amd/csrc/mk_kernels.hip",
                   "persistent_megakernel_decode_amd/csrc/mk_device.hpp"]
 
@@ -173,8 +175,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 weights, fp32 accumulate",
         "data": "synthetic (seeded, random-init weights of the workload's shape)",
-        "config": {"workload": "%s: Llama-3.2-1B-shaped decode step, batch %d, KV %s, %d layers, hidden %d"
-                   % (args.workload, cfg["batch"], str(int(inp["kv_len"][0])), cfg["n_layers"], cfg["hidden"]),
+        "config": {"workload": "%s: %s decode step, batch %d, KV %s, %d layers, hidden %d"
+                   % (args.workload, SHAPES.get(args.workload, "Llama-family"), cfg["batch"],
+                      str(int(inp["kv_len"][0])) if cfg["batch"] == 1 else "%d..%d" % (min(inp["kv_len"]), max(inp["kv_len"])),
+                      cfg["n_layers"], cfg["hidden"]),
                    "batch": int(cfg["batch"]), "kv_len": [int(k) for k in inp["kv_len"]],
                    "persistent_grid": "%d workgroups x 512 threads" % plan.export()["num_cus"]},
         "algorithmic_bytes": nbytes,

@@ -107,8 +107,12 @@ typedef struct {
  * t / num_cus.  Deterministic: equal inputs give bit-identical plans.
  * Errors: MK_E_INVALID (null/size/abi mismatch), MK_E_UNSUPPORTED (head_dim not
  * 64 or 128, hidden or ffn not a multiple of 8 or above 12288, more than 4 query
- * heads per kv head, kv_len[b] + 1 > max_kv_len, batch other than 1, tiles that
- * do not fit the 144 KiB LDS page ring). */
+ * heads per kv head, kv_len[b] + 1 > max_kv_len, batch outside 1..16, GEMV
+ * tiles with more rows than their K allows (16 up to K 2048, 8 up to 4096, 4
+ * beyond), tiles that do not fit the LDS page ring: 144 KiB at batch 1, 128 KiB
+ * at batch 2..16).  Batch 1 runs fp32 vector GEMV tiles; batch 2..16 runs the
+ * same tiles on the matrix cores (16 weight rows x 16 sequences per MFMA block,
+ * activations entered as bf16 high and low parts). */
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* kv_len,
                         const mk_plan_opts* opts, mk_plan** out);
 

@@ -20,7 +20,8 @@
 namespace mk {
 hipError_t launch_megakernel(const mkd::KArgs& a, int num_cus, hipStream_t s);
 hipError_t launch_layer(const mkd::KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s);
-hipError_t megakernel_occupancy(int hd, int* blocks_per_cu);
+hipError_t megakernel_occupancy(int hd, int batch, int* blocks_per_cu);
+int ring_pages(int batch);
 }  // namespace mk
 
 namespace {
@@ -116,7 +117,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     return fail(MK_E_UNSUPPORTED, "hidden, ffn and n_q_heads*head_dim must be <= 12288");
   if ((d.arch == MK_ARCH_QWEN3) != (d.qk_norm != 0)) return fail(MK_E_INVALID, "qk_norm must match arch");
   if (!(d.rms_eps > 0.f) || !(d.rope_theta > 0.f)) return fail(MK_E_INVALID, "rms_eps and rope_theta must be > 0");
-  if (batch != 1) return fail(MK_E_UNSUPPORTED, "batch must be 1 in this build");
+  if (batch < 1 || batch > mkd::kMB) return fail(MK_E_UNSUPPORTED, "batch must be 1..16");
   std::vector<int32_t> kl(kv_len, kv_len + batch);
   for (int b = 0; b < batch; ++b)
     if (kl[b] < 0 || kl[b] + 1 > d.max_kv_len) return fail(MK_E_UNSUPPORTED, "kv_len[b] + 1 must be <= max_kv_len");
@@ -169,7 +170,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   }
   // every tile's weight bytes must fit the LDS page ring
   auto r1k = [](long v) { return (v + 1023) / 1024 * 1024; };
-  const long ring = (long)mkd::kNumPages * mkd::kPage;
+  const long ring = (long)mk::ring_pages(batch) * mkd::kPage;
   const int Smax = o.attn_splits;
   const int maxpos = *std::max_element(kl.begin(), kl.end()) + 1;
   const long attn_rows = mk::ceil_div(maxpos, Smax);
@@ -177,7 +178,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
       (long)o.down_rows * d.ffn * 2 > ring || (long)o.gemv_rows * d.n_q_heads * d.head_dim * 2 > ring ||
       (long)o.lm_rows * d.hidden * 2 > ring || r1k(attn_rows * d.head_dim * 2) * 2 > ring) {
     delete p;
-    return fail(MK_E_UNSUPPORTED, "a tile does not fit the 144 KiB LDS page ring; use smaller tiles");
+    return fail(MK_E_UNSUPPORTED, "a tile does not fit the LDS page ring (144 KiB, 128 KiB for batch > 1); use smaller tiles");
   }
   if (o.attn_splits > 64) {
     delete p;
@@ -322,7 +323,7 @@ static mk_status ensure_device(mk_plan* p) {
   int ncu = 0;
   HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, p->device), "hipDeviceGetAttribute");
   int occ = 0;
-  HIPCHK(mk::megakernel_occupancy(p->c.hd, &occ), "occupancy");
+  HIPCHK(mk::megakernel_occupancy(p->c.hd, p->batch, &occ), "occupancy");
   if (p->num_cus > ncu || occ < 1)
     return fail(MK_E_UNSUPPORTED, "the persistent grid (" + std::to_string(p->num_cus) + " workgroups) cannot be co-resident on " +
                                       std::to_string(ncu) + " CUs");

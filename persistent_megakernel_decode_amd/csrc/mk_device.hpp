@@ -54,6 +54,7 @@ constexpr int kPage = 16384;  // bytes per LDS page
 constexpr int kNumPages = 9;  // page ring of the interpreter: 144 KiB
 constexpr int kNW = 4;        // compute waves per workgroup (K split / one q head each)
 constexpr int kMaxRows = 16;  // weight rows per GEMV tile
+constexpr int kMB = 16;       // sequences per batched GEMV tile (the MFMA N dimension)
 constexpr int kMaxChunks = 6; // 16-byte activation chunks per lane (K / (8 * kNW * 64))
 constexpr int kScratch = 512; // floats of per-compute-wave scratch
 constexpr int kTraceWords = 16; // timestamps per traced instruction
@@ -159,6 +160,10 @@ __device__ __forceinline__ void st_agent(GLB int* p, int v) {
 }
 // token id of sequence 0, clamped into [0, vocab) so that a bad id cannot index
 // outside the embedding
+__device__ __forceinline__ int token_of(const GLB int* tokens, int b, int V) {
+  const int t = tokens[b];
+  return t < 0 ? 0 : (t >= V ? V - 1 : t);
+}
 __device__ __forceinline__ int token0(const uint64_t tokens_ptr, int V) {
   int t = ((const GLB int*)tokens_ptr)[0];
   return t < 0 ? 0 : (t >= V ? V - 1 : t);
@@ -272,9 +277,10 @@ struct LdsSrc {
   uint32_t ring;   // LDS byte address of ring slot 0
   uint32_t first;  // first * kPage
   uint32_t off1;   // tile offset of segment 1
+  uint32_t wrap;   // ring size in bytes
   __device__ __forceinline__ uint32_t addr(int seg, uint32_t o) const {
     const uint32_t x = first + (seg ? off1 : 0u) + o;
-    const uint32_t y = x - (uint32_t)(kNumPages * kPage);
+    const uint32_t y = x - wrap;
     return ring + (x < y ? x : y);
   }
   __device__ __forceinline__ uint4 ld16(int seg, int o) const {
@@ -509,6 +515,8 @@ struct GemvIn {
   const GLB float* xf;
   const GLB uint16_t* xb;
   const GLB uint16_t* nw;
+  const GLB uint16_t* emb;  // embedding table when the input is the token's row (xf null)
+  const GLB int* tok;       // token ids [B]
   int K;
   int n0, nrows;  // rows in segment 0, total rows
 };
@@ -518,13 +526,20 @@ __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
   g.xf = nullptr;
   g.xb = nullptr;
   g.nw = nullptr;
+  g.emb = nullptr;
+  g.tok = nullptr;
   const int op = m.w(WOpcode);
   switch (op) {
     case OpQkv:
       g.K = c.H;
       g.nw = (const GLB uint16_t*)m.q(QkvNorm);
-      if (m.q(QkvX)) g.xf = (const GLB float*)m.q(QkvX);
-      else g.xb = (const GLB uint16_t*)m.q(QkvEmbed) + (size_t)token0(m.q(QkvTokens), c.V) * c.H;
+      if (m.q(QkvX)) {
+        g.xf = (const GLB float*)m.q(QkvX);
+      } else {
+        g.emb = (const GLB uint16_t*)m.q(QkvEmbed);
+        g.tok = (const GLB int*)m.q(QkvTokens);
+        if (c.B == 1) g.xb = g.emb + (size_t)token0(m.q(QkvTokens), c.V) * c.H;
+      }
       g.n0 = g.nrows = m.w(WPay + 1);
       break;
     case OpOproj:
@@ -628,6 +643,215 @@ __device__ inline void gemv_epilogue(const Meta& m, const Consts& c,
     }
     default:
       break;
+  }
+}
+
+__device__ __forceinline__ bool amax_better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// ---- batched GEMV (B <= 16 sequences) on the matrix cores ----------------------
+// A tile is up to 16 weight rows x K; each compute wave takes a quarter of K in
+// steps of 32 and accumulates one v_mfma_f32_16x16x32_bf16 block: A = the 16
+// weight rows (lane l: row l % 16, k = 8 (l / 16) .. +7, one 16-byte LDS read),
+// B = the sequences' activations (lane l: sequence l % 16, the same 8 k), C =
+// 16 rows x 16 sequences (lane l: sequence l % 16, rows 4 (l / 16) .. +3).  The
+// fp32 activations (times the RMSNorm weight) enter as two bf16 parts, hi =
+// bf16(x) and lo = bf16(x - hi), one MFMA each: the weight x activation
+// products keep about 16 bits of the activation, as the fp32 path does to
+// within rounding.  Rows past nrows re-read the last row, sequences past B and
+// chunks past the wave's range read valid addresses and are zeroed.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+template <bool EMB, class Src, class Rel>
+__device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
+                                    LDS float* ssp, const Rel& rel) {
+  const int lane = lane_id();
+  const int K = gi.K, nch = K / 8, cpw = (nch + kNW - 1) / kNW, base = cw * cpw;
+  const int nks = (cpw + 3) / 4;  // k-steps of 4 chunks
+  const int r = lane & 15, q = lane >> 4;
+  const int rc = r < gi.nrows ? r : gi.nrows - 1;
+  const int seg = rc < gi.n0 ? 0 : 1, rr = rc < gi.n0 ? rc : rc - gi.n0;
+  const int arow = rr * K * 2;
+  const int b = lane & 15;
+  const bool bok = b < B;
+  const GLB float* xf = nullptr;
+  const GLB uint16_t* xb = nullptr;
+  if (EMB)
+    xb = gi.emb + (size_t)token_of(gi.tok, bok ? b : 0, V) * K;
+  else
+    xf = gi.xf + (size_t)(bok ? b : 0) * K;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  constexpr int NB = 4;  // k-steps whose loads are issued together
+  for (int ks0 = 0; ks0 < nks; ks0 += NB) {
+    u32x4 A[NB], xr[NB], wn[NB];
+    f32x4 x0[NB], x1[NB];
+    bool ok[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int ks = ks0 + u, ch = ks * 4 + q;
+      ok[u] = ks < nks && ch < cpw && base + ch < nch;
+      const int kk = (ok[u] ? base + ch : 0) * 8;
+      const uint4 w = src.ld16(seg, arow + kk * 2);
+      A[u] = u32x4{w.x, w.y, w.z, w.w};
+      if (EMB) {
+        xr[u] = *(const GLB u32x4*)(xb + kk);
+      } else {
+        x0[u] = *(const GLB f32x4*)(xf + kk);
+        x1[u] = *(const GLB f32x4*)(xf + kk + 4);
+      }
+      if (gi.nw) wn[u] = *(const GLB u32x4*)(gi.nw + kk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      float v[8];
+      if (EMB) {
+        v[0] = bf16lo(xr[u].x); v[1] = bf16hi(xr[u].x); v[2] = bf16lo(xr[u].y); v[3] = bf16hi(xr[u].y);
+        v[4] = bf16lo(xr[u].z); v[5] = bf16hi(xr[u].z); v[6] = bf16lo(xr[u].w); v[7] = bf16hi(xr[u].w);
+      } else {
+        v[0] = x0[u].x; v[1] = x0[u].y; v[2] = x0[u].z; v[3] = x0[u].w;
+        v[4] = x1[u].x; v[5] = x1[u].y; v[6] = x1[u].z; v[7] = x1[u].w;
+      }
+      const bool live = ok[u] && bok;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = live ? v[e] : 0.f;
+        ss = fmaf(v[e], v[e], ss);
+      }
+      if (gi.nw) {
+        v[0] *= bf16lo(wn[u].x); v[1] *= bf16hi(wn[u].x); v[2] *= bf16lo(wn[u].y); v[3] *= bf16hi(wn[u].y);
+        v[4] *= bf16lo(wn[u].z); v[5] *= bf16hi(wn[u].z); v[6] *= bf16lo(wn[u].w); v[7] *= bf16hi(wn[u].w);
+      }
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)v[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(v[e] - (float)h);
+      }
+      const bf16x8 av = __builtin_bit_cast(bf16x8, A[u]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lo, acc, 0, 0, 0);
+    }
+  }
+  rel();
+  // sequence b's sum of squares over the wave's range: lanes b, b+16, b+32, b+48
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  if (lane < kMB) ssp[lane] = ss;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[(4 * q + i) * kMB + b] = acc[i];
+}
+
+template <class Src, class Rel>
+__device__ inline void gemv_rows_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
+                                    LDS float* ssp, const Rel& rel) {
+  if (gi.xf)
+    gemv_tile_mb<false>(src, gi, B, V, cw, part, ssp, rel);
+  else
+    gemv_tile_mb<true>(src, gi, B, V, cw, part, ssp, rel);
+}
+
+// Residual inputs of the four (row, sequence) outputs lane l owns in the batched
+// epilogue: index idx = l + 64 j, row idx / 16, sequence idx % 16 = l % 16.
+__device__ inline f32x4 gemv_residual_mb(const Meta& m, const Consts& c) {
+  const int lane = lane_id();
+  const int op = m.w(WOpcode);
+  f32x4 r = {0.f, 0.f, 0.f, 0.f};
+  if (op != OpOproj && op != OpDown) return r;
+  const int row0 = m.w(WPay), nr = m.w(WPay + 1);
+  const int b = lane & 15, bb = b < c.B ? b : 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (lane + 64 * j) >> 4;
+    const int rr = row0 + (row < nr ? row : 0);
+    if (op == OpOproj) {
+      r[j] = m.q(OX) ? ((const GLB float*)m.q(OX))[(size_t)bb * c.H + rr]
+                     : bf16f(((const GLB uint16_t*)m.q(OEmbed))[(size_t)token_of((const GLB int*)m.q(OTokens), bb, c.V) *
+                                                                  c.H + rr]);
+    } else {
+      r[j] = ((const GLB float*)m.q(DnRes))[(size_t)bb * c.H + rr];
+    }
+  }
+  return r;
+}
+
+// Epilogue of a batched GEMV tile: part[w * 256 + row * 16 + b] are wave w's
+// partial sums, ssp[w * 16 + b] its sums of squares of sequence b.
+__device__ inline void gemv_epilogue_mb(const Meta& m, const Consts& c, const LDS float* part, const LDS float* ssp,
+                                        f32x4 res) {
+  const int lane = lane_id();
+  const int op = m.w(WOpcode);
+  const GemvIn g = gemv_input(m, c);
+  const int b = lane & 15;
+  const bool bok = b < c.B;
+  float scale = 1.f;
+  if (g.nw) {
+    float ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) ss += ssp[w * kMB + b];
+    scale = 1.f / sqrtf(ss / (float)g.K + c.eps);
+  }
+  const int row0 = m.w(WPay), nr = m.w(WPay + 1);
+  auto val = [&](int row) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) v += part[w * kMB * kMB + row * kMB + b];
+    return v * scale;
+  };
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (lane + 64 * j) >> 4;
+    const bool live = bok && row < nr;
+    switch (op) {
+      case OpQkv:
+        if (live) st_agent((GLB float*)m.q(QkvOut) + ((size_t)b * c.nkv + m.w(WGx)) * c.RPG + row0 + row, val(row));
+        break;
+      case OpOproj:
+        if (live) st_agent((GLB float*)m.q(OOut) + (size_t)b * c.H + row0 + row, res[j] + val(row));
+        break;
+      case OpGateUp:
+        if (live) {
+          const float gt = val(row), up = val(nr + row);  // up row j sits at tile row nr + j
+          st_agent((GLB float*)m.q(GuOut) + (size_t)b * c.F + row0 + row, gt / (1.f + __expf(-gt)) * up);
+        }
+        break;
+      case OpDown:
+        if (live) st_agent((GLB float*)m.q(DnOut) + (size_t)b * c.H + row0 + row, res[j] + val(row));
+        break;
+      case OpLmHead:
+        if (live) {
+          const float v = val(row);
+          ((GLB float*)m.q(LmLogits))[(size_t)b * c.V + row0 + row] = v;
+          if (amax_better(v, row0 + row, bv, bi)) {
+            bv = v;
+            bi = row0 + row;
+          }
+        }
+        break;
+      default:
+        break;
+    }
+  }
+  if (op == OpLmHead) {
+    // lanes b, b+16, b+32, b+48 hold sequence b's rows: the tile's (max, lowest index)
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk <<= 1) {
+      const float ov = __shfl_xor(bv, msk, 64);
+      const int oi = __shfl_xor(bi, msk, 64);
+      if (amax_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane < kMB && bok) {
+      GLB float* mx = (GLB float*)m.q(LmMax) + 2 * ((size_t)b * c.T_v + m.w(WGx));
+      st_agent(mx, bv);
+      st_agent((GLB int*)mx + 1, bi);
+    }
   }
 }
 
@@ -885,9 +1109,6 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
 // ties.  Compute wave cw scans the contiguous quarter cw of the T tile maxima,
 // 32 per lane per batch (every load of a batch issued before any is used), and
 // leaves its best (value, index) in out2[0..1]; argmax_final merges the quarters.
-__device__ __forceinline__ bool amax_better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
 __device__ inline void argmax_part(const Meta& m, const Consts& c, int cw, LDS float* out2) {
   const int lane = lane_id();
   const int b = m.w(WGx), T = m.w(WPay);
@@ -929,14 +1150,14 @@ __device__ inline void argmax_part(const Meta& m, const Consts& c, int cw, LDS f
     out2[1] = __int_as_float(bi);
   }
 }
-// part[w][0..1]: wave w's (value, index); one wave stores the winner.
-__device__ inline void argmax_final(const Meta& m, const LDS float (*part)[kMaxRows]) {
-  float bv = part[0][0];
-  int bi = __float_as_int(part[0][1]);
+// part[w * stride + 0..1]: wave w's (value, index); one wave stores the winner.
+__device__ inline void argmax_final(const Meta& m, const LDS float* part, int stride) {
+  float bv = part[0];
+  int bi = __float_as_int(part[1]);
 #pragma unroll
   for (int w = 1; w < kNW; ++w) {
-    const float v = part[w][0];
-    const int i = __float_as_int(part[w][1]);
+    const float v = part[w * stride];
+    const int i = __float_as_int(part[w * stride + 1]);
     if (amax_better(v, i, bv, bi)) {
       bv = v;
       bi = i;

@@ -29,22 +29,33 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-struct Ctrl {
-  int ready_seq, done_seq, abort_flag, pad;
+// PW / SW: partial-sum and sum-of-squares floats per compute wave per slot
+// (one value per tile row for batch 1; a 16 x 16 block of rows x sequences and
+// one value per sequence for the batched path)
+template <int PW, int SW>
+struct CtrlT {
+  int ready_seq, done_seq, abort_flag, meta_seq;  // meta_seq: meta records staged (instructions 0 .. meta_seq-1)
   int slot_full[16];   // generation + 1 of the data in each ring slot (loaders -> compute)
   int slot_rel[16];    // compute-wave releases of each slot, cumulative (kNW per use)
   int arrive[4];       // compute waves done with instruction i (slot i % 4)
-  float part[4][kNW][kMaxRows];
-  float ssp[4][kNW];
+  float part[4][kNW][PW];
+  float ssp[4][kNW][SW];
   float scratch[kNW][kScratch];
 };
 // Copies of the instructions in flight (instruction i in slot i % kMeta) and of
 // their operand-table rows, staged by the controller.
 constexpr int kMeta = 8;
-struct __attribute__((aligned(16))) Lds {
-  char ring[kNumPages][kPage];
+// Workgroup LDS.  MB: batched sequences (MFMA tiles) -- one page less in the
+// ring for the 16 x 16 partial blocks.
+template <bool MB_>
+struct __attribute__((aligned(16))) LdsT {
+  static constexpr bool MB = MB_;
+  static constexpr int NP = MB_ ? kNumPages - 1 : kNumPages;  // ring pages
+  static constexpr int PW = MB_ ? kMB * kMB : kMaxRows;
+  static constexpr int SW = MB_ ? kMB : 1;
+  char ring[NP][kPage];
   uint32_t meta[kMeta][64];
-  Ctrl c;
+  CtrlT<PW, SW> c;
 };
 
 template <class T>
@@ -71,7 +82,8 @@ enum { ErrEvent = 1, ErrPage = 2, ErrReady = 3, ErrDrain = 4, ErrFree = 5 };
 
 // The record belongs to the run whose epoch is in err[0]; the first failing
 // wave of that run fills it.
-__device__ void record_error(const KArgs& a, LDS Lds* L, int kind, int slot, int ev, unsigned val, unsigned tgt) {
+template <class LT>
+__device__ void record_error(const KArgs& a, LDS LT* L, int kind, int slot, int ev, unsigned val, unsigned tgt) {
   if (lane_id() == 0) {
     unsigned old = __hip_atomic_load(&a.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old != a.epoch && __hip_atomic_compare_exchange_strong(&a.err[0], &old, a.epoch, __ATOMIC_RELAXED,
@@ -87,12 +99,14 @@ __device__ void record_error(const KArgs& a, LDS Lds* L, int kind, int slot, int
   }
 }
 
-__device__ __forceinline__ bool aborted(LDS Lds* L) {
+template <class LT>
+__device__ __forceinline__ bool aborted(LDS LT* L) {
   return __hip_atomic_load(&L->c.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
 }
 
 // Wait until *p >= v (LDS, workgroup acquire), bounded.
-__device__ bool wait_lds_ge(const KArgs& a, LDS Lds* L, LDS int* p, int v, int kind, int slot) {
+template <class LT>
+__device__ bool wait_lds_ge(const KArgs& a, LDS LT* L, LDS int* p, int v, int kind, int slot) {
   if (lds_load_acq(p) >= v) return true;
   const unsigned long long t0 = now_ticks();
   for (unsigned it = 0;; ++it) {
@@ -117,7 +131,8 @@ __device__ __forceinline__ const CST uint64_t* oprow(const KArgs& a, int row) {
 
 // Copy instruction j and its operand row into meta record j % kMeta (scalar
 // loads; lane 0 writes).  Past the end of the queue the record is a NoOp.
-__device__ void stage(const KArgs& a, LDS Lds* L, int j) {
+template <class LT>
+__device__ void stage(const KArgs& a, LDS LT* L, int j) {
   LDS uint32_t* rec = L->meta[j % kMeta];
   if (j >= a.max_len) {
     if (lane_id() == 0) rec[WOpcode] = OpNoop;
@@ -141,7 +156,8 @@ __device__ void stage(const KArgs& a, LDS Lds* L, int j) {
 }
 
 // ---------------------------------------------------------------------------
-__device__ void controller(const KArgs& a, LDS Lds* L) {
+template <class LT>
+__device__ void controller(const KArgs& a, LDS LT* L) {
   stage(a, L, 0);
   for (int i = 0; i < a.max_len; ++i) {
     const Meta m = load_meta(L->meta[i % kMeta]);
@@ -196,7 +212,8 @@ __device__ void controller(const KArgs& a, LDS Lds* L) {
 // consecutive instructions that trigger the same event is signalled once, at
 // its end, with the summed increment: a producer never depends on its own
 // trigger event, so deferring within the run cannot delay the event.
-__device__ void storer(const KArgs& a, LDS Lds* L) {
+template <class LT>
+__device__ void storer(const KArgs& a, LDS LT* L) {
   const int lane = lane_id();
   unsigned pending = 0;
   for (int i = 0; i < a.max_len; ++i) {
@@ -208,12 +225,21 @@ __device__ void storer(const KArgs& a, LDS Lds* L) {
     if (op == OpNoop) break;
     const int sl = i & 3;
     const bool gemv = is_gemv(op);
-    const float res = (op == OpOproj || op == OpDown) ? gemv_residual(m, a.c) : 0.f;
-    if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
-    if (gemv)
-      gemv_epilogue(m, a.c, L->c.part[sl], L->c.ssp[sl], res);
-    else if (op == OpArgmax)
-      argmax_final(m, L->c.part[sl]);
+    if constexpr (LT::MB) {
+      const f32x4 res = gemv_residual_mb(m, a.c);
+      if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
+      if (gemv)
+        gemv_epilogue_mb(m, a.c, &L->c.part[sl][0][0], &L->c.ssp[sl][0][0], res);
+      else if (op == OpArgmax)
+        argmax_final(m, &L->c.part[sl][0][0], LT::PW);
+    } else {
+      const float res = (op == OpOproj || op == OpDown) ? gemv_residual(m, a.c) : 0.f;
+      if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
+      if (gemv)
+        gemv_epilogue(m, a.c, L->c.part[sl], &L->c.ssp[sl][0][0], res);
+      else if (op == OpArgmax)
+        argmax_final(m, &L->c.part[sl][0][0], LT::PW);
+    }
     if (lane == 0) {
       __hip_atomic_store(&L->c.arrive[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       lds_store_rel(&L->c.done_seq, i + 1);
@@ -239,7 +265,8 @@ __device__ void storer(const KArgs& a, LDS Lds* L) {
 }
 
 // ---------------------------------------------------------------------------
-__device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
+template <class LT>
+__device__ void loader(const KArgs& a, LDS LT* L, int parity) {
   const int lane = lane_id();
   const uint32_t full_base = lds_addr(&L->c.slot_full[0]);
   const uint32_t rel_base = lds_addr(&L->c.slot_rel[0]);
@@ -248,7 +275,7 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
   // never indexed
   int q0 = 0, q1 = 0, q2 = 0, q3 = 0, l0 = -1, l1 = -1, l2 = -1, l3 = -1, npend = 0;
   auto publish = [&](int sq, int last_of) {
-    lds_st_asm(full_base + 4 * (sq % kNumPages), sq / kNumPages + 1);
+    lds_st_asm(full_base + 4 * (sq % LT::NP), sq / LT::NP + 1);
     if (a.trace && last_of >= 0 && lane == 0)
       a.trace[((size_t)blockIdx.x * a.max_len + last_of) * kTraceWords + 5] = now_ticks();
   };
@@ -273,7 +300,7 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
       if ((seq & 1) != parity) continue;
       // the slot's previous page (gen uses ago) must have been released by
       // every compute wave
-      const int slot = seq % kNumPages, gen = seq / kNumPages;
+      const int slot = seq % LT::NP, gen = seq / LT::NP;
       if (lds_ld_asm(rel_base + 4 * slot) < kNW * gen) {
         publish_all();
         const unsigned long long t0 = now_ticks();
@@ -357,8 +384,8 @@ __device__ void loader(const KArgs& a, LDS Lds* L, int parity) {
 }
 
 // ---------------------------------------------------------------------------
-template <int HD>
-__device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
+template <int HD, class LT>
+__device__ void compute(const KArgs& a, LDS LT* L, int cw) {
   const int lane = lane_id();
   int seq = 0;
   int act_row = -1;
@@ -376,7 +403,7 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
     if (!wait_lds_ge(a, L, &L->c.done_seq, i - 3, ErrDrain, i)) return;
     for (int pg = 0; pg < t.npages; ++pg) {
       const int sq = first + pg;
-      if (!wait_lds_ge(a, L, &L->c.slot_full[sq % kNumPages], sq / kNumPages + 1, ErrPage, i)) return;
+      if (!wait_lds_ge(a, L, &L->c.slot_full[sq % LT::NP], sq / LT::NP + 1, ErrPage, i)) return;
     }
     if (cw == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 1] = now_ticks();
     if (tr && lane == 0) tr[8 + cw] = now_ticks();
@@ -386,18 +413,22 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (lane == 0) {
         for (int pg = 0; pg < t.npages; ++pg) {
-          const int slot = (first + pg) % kNumPages;
+          const int slot = (first + pg) % LT::NP;
           __hip_atomic_fetch_add(&L->c.slot_rel[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
       }
     };
     LdsSrc src;
     src.ring = lds_addr(&L->ring[0][0]);
-    src.first = (uint32_t)(first % kNumPages) * kPage;
+    src.first = (uint32_t)(first % LT::NP) * kPage;
     src.off1 = (uint32_t)t.off1;
+    src.wrap = (uint32_t)(LT::NP * kPage);
     const int sl = i & 3;
     const bool gemv = is_gemv(op);
-    if (gemv) {
+    if (gemv && LT::MB) {
+      const GemvIn gi = gemv_input(m, a.c);
+      gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, &L->c.part[sl][cw][0], &L->c.ssp[sl][cw][0], release);
+    } else if (gemv) {
       const GemvIn gi = gemv_input(m, a.c);
       if (m.w(WOpRow) != act_row) {
         load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
@@ -405,15 +436,15 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
         act_row = m.w(WOpRow);
       }
       if (cw == 0 && tr && lane == 0) tr[6] = now_ticks();
-      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, L->c.part[sl][cw], release);
-      if (lane == 0) L->c.ssp[sl][cw] = act_ss;
+      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, &L->c.part[sl][cw][0], release);
+      if (lane == 0) L->c.ssp[sl][cw][0] = act_ss;
       if (cw == 0 && tr && lane == 0) tr[7] = now_ticks();
     } else if (op == OpAttn) {
       attn_wave<HD>(src, m, a.c, cw, L->c.scratch[cw], cw == 0, cw == 0 ? tr : nullptr);
     } else if (op == OpCombine) {
       combine_wave<HD>(m, a.c, cw, cw == 0 ? tr : nullptr);
     } else if (op == OpArgmax) {
-      argmax_part(m, a.c, cw, L->c.part[sl][cw]);
+      argmax_part(m, a.c, cw, &L->c.part[sl][cw][0]);
     }
     if (!gemv) release();
     if (tr && lane == 0) tr[12 + cw] = now_ticks();
@@ -424,13 +455,14 @@ __device__ void compute(const KArgs& a, LDS Lds* L, int cw) {
   }
 }
 
-template <int HD>
+template <int HD, bool MB>
 __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
-  __shared__ Lds Ls;
-  LDS Lds* L = (LDS Lds*)&Ls;
+  typedef LdsT<MB> LT;
+  __shared__ LT Ls;
+  LDS LT* L = (LDS LT*)&Ls;
   {
     LDS int* c = (LDS int*)&L->c;
-    const int n = (int)(sizeof(Ctrl) / 4);
+    const int n = (int)(sizeof(L->c) / 4);
     for (int k = threadIdx.x; k < n; k += blockDim.x) c[k] = 0;
   }
   __syncthreads();
@@ -447,19 +479,20 @@ __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
     loader(a, L, w - 2);
   } else {
     __builtin_amdgcn_s_setprio(2);
-    compute<HD>(a, L, w - 4);
+    compute<HD, LT>(a, L, w - 4);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Layerwise: one launch per operator, one workgroup (4 waves) per tile.
-template <int HD>
+template <int HD, bool MB>
 __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int first_task) {
-  __shared__ float part_s[kNW][kMaxRows];
-  __shared__ float ssp_s[kNW];
+  constexpr int PW = MB ? kMB * kMB : kMaxRows, SW = MB ? kMB : 1;
+  __shared__ float part_s[kNW][PW];
+  __shared__ float ssp_s[kNW][SW];
   __shared__ float scr_s[kNW][kScratch];
-  LDS float(*part)[kMaxRows] = (LDS float(*)[kMaxRows])part_s;
-  LDS float* ssp = (LDS float*)ssp_s;
+  LDS float(*part)[PW] = (LDS float(*)[PW])part_s;
+  LDS float(*ssp)[SW] = (LDS float(*)[SW])ssp_s;
   LDS float(*scr)[kScratch] = (LDS float(*)[kScratch])scr_s;
   __shared__ uint32_t meta_s[64];
   const int t = first_task + blockIdx.x;
@@ -479,13 +512,19 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   const int op = m.w(WOpcode);
   if (is_gemv(op)) {
     const GemvIn gi = gemv_input(m, a.c);
-    Act act;
-    load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
-    const float ss = wave_sum(act.ss);
-    gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw], [] {});
-    if (lane == 0) ssp[cw] = ss;
-    __syncthreads();
-    if (cw == 0) gemv_epilogue(m, a.c, part, ssp, gemv_residual(m, a.c));
+    if constexpr (MB) {
+      gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {});
+      __syncthreads();
+      if (cw == 0) gemv_epilogue_mb(m, a.c, &part[0][0], &ssp[0][0], gemv_residual_mb(m, a.c));
+    } else {
+      Act act;
+      load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
+      const float ss = wave_sum(act.ss);
+      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw], [] {});
+      if (lane == 0) ssp[cw][0] = ss;
+      __syncthreads();
+      if (cw == 0) gemv_epilogue(m, a.c, part, &ssp[0][0], gemv_residual(m, a.c));
+    }
   } else if (op == OpAttn) {
     attn_wave<HD>(src, m, a.c, cw, scr[cw], cw == 0);
   } else if (op == OpCombine) {
@@ -493,37 +532,56 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   } else if (op == OpArgmax) {
     argmax_part(m, a.c, cw, part[cw]);
     __syncthreads();
-    if (cw == 0) argmax_final(m, part);
+    if (cw == 0) argmax_final(m, &part[0][0], PW);
   }
+}
+
+template <bool MB>
+const void* megakernel_fn(int hd) {
+  return hd == 64 ? (const void*)mk_megakernel<64, MB> : (const void*)mk_megakernel<128, MB>;
 }
 
 }  // namespace
 
 // ---- launch wrappers used by the host API ----------------------------------------
+// Batch 1 runs the fp32 GEMV path; batch 2..16 the matrix-core path.
 namespace mk {
 
 hipError_t launch_megakernel(const KArgs& a, int num_cus, hipStream_t s) {
-  if (a.c.hd == 64) {
-    hipLaunchKernelGGL(mk_megakernel<64>, dim3(num_cus), dim3(512), 0, s, a);
+  if (a.c.B == 1) {
+    if (a.c.hd == 64)
+      hipLaunchKernelGGL((mk_megakernel<64, false>), dim3(num_cus), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((mk_megakernel<128, false>), dim3(num_cus), dim3(512), 0, s, a);
   } else {
-    hipLaunchKernelGGL(mk_megakernel<128>, dim3(num_cus), dim3(512), 0, s, a);
+    if (a.c.hd == 64)
+      hipLaunchKernelGGL((mk_megakernel<64, true>), dim3(num_cus), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((mk_megakernel<128, true>), dim3(num_cus), dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_layer(const KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s) {
-  if (a.c.hd == 64) {
-    hipLaunchKernelGGL(mk_layer_kernel<64>, dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
+  if (a.c.B == 1) {
+    if (a.c.hd == 64)
+      hipLaunchKernelGGL((mk_layer_kernel<64, false>), dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
+    else
+      hipLaunchKernelGGL((mk_layer_kernel<128, false>), dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
   } else {
-    hipLaunchKernelGGL(mk_layer_kernel<128>, dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
+    if (a.c.hd == 64)
+      hipLaunchKernelGGL((mk_layer_kernel<64, true>), dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
+    else
+      hipLaunchKernelGGL((mk_layer_kernel<128, true>), dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
   }
   return hipGetLastError();
 }
 
-hipError_t megakernel_occupancy(int hd, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, hd == 64 ? (const void*)mk_megakernel<64>
-                                                                               : (const void*)mk_megakernel<128>,
-                                                      512, 0);
+hipError_t megakernel_occupancy(int hd, int batch, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, batch == 1 ? megakernel_fn<false>(hd) : megakernel_fn<true>(hd), 512, 0);
 }
+
+int ring_pages(int batch) { return batch == 1 ? LdsT<false>::NP : LdsT<true>::NP; }
 
 }  // namespace mk

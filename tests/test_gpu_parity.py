@@ -159,3 +159,49 @@ def test_gpu_consecutive_runs_new_tokens(key, name):
         print("  token %d rel-L2 %.3g" % (tok, rel), flush=True)
         assert rel <= LOGIT_TOL
         assert int(c.plan.output(mk.MK_OUT_NEXT_TOKEN).cpu()[0]) == int(ref["next"][0])
+
+
+@pytest.mark.timeout(900)
+def test_gpu_qwen3_8b_full_size():
+    """Qwen3-8B shape (36 layers, hidden 4096, head_dim 128, q/k RMSNorm, FFN
+    12288, untied 151936-row LM head), batch 1, KV 4096, in the default launch
+    configuration; megakernel and layerwise against the oracle."""
+    import gc
+    c = Case("qwen3_8b", norm_sigma=0.0)
+    try:
+        c.assert_parity(c.run())
+        c.assert_parity(c.run(layerwise=True), layerwise=True)
+    finally:
+        c.plan.free()
+        del c
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("key,name,overrides", [
+    ("b3", "tiny", dict(batch=3, kv_len=(0, 200), seed=11)),
+    ("b16", "tiny", dict(batch=16, kv_len=(100, 300), seed=12)),
+    ("b5_qwen", "tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128, batch=5, kv_len=(1, 90), seed=13)),
+])
+def test_gpu_batched(key, name, overrides):
+    """Batch 2..16 (matrix-core GEMV tiles, per-sequence attention lengths):
+    megakernel and layerwise against the oracle, every sequence's argmax."""
+    c = case(key, name, **overrides)
+    c.assert_parity(c.run())
+    c.assert_parity(c.run(layerwise=True), layerwise=True)
+
+
+@pytest.mark.timeout(900)
+def test_gpu_llama1b_batch16_full_size():
+    """Llama-3.2-1B shape at batch 16, per-sequence KV lengths uniform in
+    [512, 2048], default launch configuration."""
+    import gc
+    c = Case("llama1b_b16", norm_sigma=0.0)
+    try:
+        c.assert_parity(c.run())
+        c.assert_parity(c.run(layerwise=True), layerwise=True)
+    finally:
+        c.plan.free()
+        del c
+        gc.collect()
+        torch.cuda.empty_cache()

@@ -49,6 +49,8 @@ def _compare(lib_plan, ref):
     ("tiny", dict(ffn=688 + 32, vocab=4100, kv_len=999), 100, {}),  # ragged FFN and vocab tails
     ("tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128), 256, {}),
     ("llama1b", {}, 256, {}),
+    ("tiny", dict(batch=3, kv_len=(0, 200), seed=11), 37, {}),
+    ("llama1b_b16", {}, 256, {}),
     ("llama1b", {}, 148, dict(gemv_rows=8, down_rows=2)),
     ("qwen3_8b", {}, 256, {}),
 ])
