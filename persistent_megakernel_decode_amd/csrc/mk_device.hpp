@@ -311,38 +311,54 @@ struct GlbSrc {
   __device__ __forceinline__ uint16_t ld2(int seg, int o) const { return *(const GLB uint16_t*)((seg ? p1 : p0) + o); }
 };
 
+// Which activation and norm a GEMV op reads, and its K.
+struct GemvIn {
+  const GLB float* xf;
+  const GLB uint16_t* xb;
+  const GLB uint16_t* nw;
+  const GLB uint16_t* emb;  // embedding table when the input is the token's row (xf null)
+  const GLB int* tok;       // token ids [B]
+  int K;
+  int n0, nrows;  // rows in segment 0, total rows
+};
+
 // ---- activations of a GEMV tile ---------------------------------------------
 // Each compute wave owns about K / kNW consecutive input elements; lane l holds the
 // 16-byte chunks l, l + 64, ... of that range as fp32 (times the RMSNorm weight
 // when the op fuses a norm), plus its partial sum of squares.
 struct Act {
   float x[kMaxChunks][8];
-  float ss;
+  float ss;   // this lane's sum of squares of the (un-normed) inputs
+  float ssw;  // the wave's sum of ss
   int nc;
 };
 
 // src: fp32 vector (xf) or a bf16 row (xb); nw: bf16 norm weight or null.
 // All loads are issued before any is used (addresses of chunks outside the
-// wave's range are clamped to chunk 0 and their values zeroed afterwards).
-__device__ inline void load_act(Act& a, int K, int cw, const GLB float* xf, const GLB uint16_t* xb,
-                                const GLB uint16_t* nw) {
+// wave's range are clamped to chunk 0 and their values zeroed afterwards); the
+// fp32 input lands straight in a.x, so besides a the load holds only the norm
+// weights (and a bf16 input) in flight: it can run while a GEMV tile's weights
+// sit in registers.  MC: chunks per lane unrolled (at least a.nc).
+template <int MC>
+__device__ inline void load_act_t(Act& a, int K, int cw, const GLB float* xf, const GLB uint16_t* xb,
+                                  const GLB uint16_t* nw) {
   const int lane = lane_id();
   const int nch = K / 8;                    // 16-byte chunks of bf16 weights per row
   const int cpw = (nch + kNW - 1) / kNW;    // chunks per wave (the last wave may get fewer)
   const int base = cw * cpw;
   a.nc = (cpw + 63) / 64;
-  f32x4 x0[kMaxChunks], x1[kMaxChunks];
-  u32x4 xr[kMaxChunks], wr[kMaxChunks];
-  bool ok[kMaxChunks];
+  u32x4 xr[MC], wr[MC];
+  bool ok[MC];
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
+  for (int j = 0; j < MC; ++j) {
     const int ch = lane + 64 * j;
     ok[j] = j < a.nc && ch < cpw && base + ch < nch;
     const int k0 = (ok[j] ? base + ch : 0) * 8;
     if (j < a.nc) {
       if (xf) {
-        x0[j] = *(const GLB f32x4*)(xf + k0);
-        x1[j] = *(const GLB f32x4*)(xf + k0 + 4);
+        const f32x4 v0 = *(const GLB f32x4*)(xf + k0), v1 = *(const GLB f32x4*)(xf + k0 + 4);
+        a.x[j][0] = v0.x; a.x[j][1] = v0.y; a.x[j][2] = v0.z; a.x[j][3] = v0.w;
+        a.x[j][4] = v1.x; a.x[j][5] = v1.y; a.x[j][6] = v1.z; a.x[j][7] = v1.w;
       } else {
         xr[j] = *(const GLB u32x4*)(xb + k0);
       }
@@ -352,31 +368,31 @@ __device__ inline void load_act(Act& a, int K, int cw, const GLB float* xf, cons
   __builtin_amdgcn_sched_barrier(0);  // one memory latency for all of them
   a.ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    float v[8], w[8];
-    if (j < a.nc) {
-      if (xf) {
-        v[0] = x0[j].x; v[1] = x0[j].y; v[2] = x0[j].z; v[3] = x0[j].w;
-        v[4] = x1[j].x; v[5] = x1[j].y; v[6] = x1[j].z; v[7] = x1[j].w;
-      } else {
-        v[0] = bf16lo(xr[j].x); v[1] = bf16hi(xr[j].x); v[2] = bf16lo(xr[j].y); v[3] = bf16hi(xr[j].y);
-        v[4] = bf16lo(xr[j].z); v[5] = bf16hi(xr[j].z); v[6] = bf16lo(xr[j].w); v[7] = bf16hi(xr[j].w);
-      }
-      if (nw) {
-        w[0] = bf16lo(wr[j].x); w[1] = bf16hi(wr[j].x); w[2] = bf16lo(wr[j].y); w[3] = bf16hi(wr[j].y);
-        w[4] = bf16lo(wr[j].z); w[5] = bf16hi(wr[j].z); w[6] = bf16lo(wr[j].w); w[7] = bf16hi(wr[j].w);
-      } else {
+  for (int j = 0; j < MC; ++j) {
+    if (j < a.nc && !xf) {
+      a.x[j][0] = bf16lo(xr[j].x); a.x[j][1] = bf16hi(xr[j].x); a.x[j][2] = bf16lo(xr[j].y); a.x[j][3] = bf16hi(xr[j].y);
+      a.x[j][4] = bf16lo(xr[j].z); a.x[j][5] = bf16hi(xr[j].z); a.x[j][6] = bf16lo(xr[j].w); a.x[j][7] = bf16hi(xr[j].w);
+    }
+    float w[8];
+    if (j < a.nc && nw) {
+      w[0] = bf16lo(wr[j].x); w[1] = bf16hi(wr[j].x); w[2] = bf16lo(wr[j].y); w[3] = bf16hi(wr[j].y);
+      w[4] = bf16lo(wr[j].z); w[5] = bf16hi(wr[j].z); w[6] = bf16lo(wr[j].w); w[7] = bf16hi(wr[j].w);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = 1.f;
-      }
+      for (int e = 0; e < 8; ++e) w[e] = 1.f;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = (j < a.nc && ok[j]) ? v[e] : 0.f;
+      const float x = (j < a.nc && ok[j]) ? a.x[j][e] : 0.f;
       a.ss = fmaf(x, x, a.ss);
-      a.x[j][e] = x * ((j < a.nc && ok[j]) ? w[e] : 0.f);
+      a.x[j][e] = x * w[e];
     }
   }
+  a.ssw = wave_sum(a.ss);
+}
+__device__ inline void load_act(Act& a, int K, int cw, const GLB float* xf, const GLB uint16_t* xb,
+                                const GLB uint16_t* nw) {
+  load_act_t<kMaxChunks>(a, K, cw, xf, xb, nw);
 }
 
 // Cross-lane butterflies of gfx950: permlane32_swap exchanges the upper half
@@ -420,12 +436,20 @@ __device__ inline void gemv_reduce(const float (&acc)[NR], int nrows, LDS float*
 // Rows past nrows re-read the last row and chunks outside the wave's range
 // re-read chunk 0 (their activations are zero), so every load is issued before
 // any is used.  When the wave's share of the tile (NR rows x NC chunks of 16
-// bytes per lane) fits in registers, it is read whole and rel() -- which hands
-// the tile's LDS pages back to the loaders -- runs before the arithmetic;
-// otherwise (NC == 0: any number of chunks, read chunk by chunk) after it.
-template <int NR, int NC, class Src, class Rel>
-__device__ inline void gemv_tile(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part,
-                                 const Rel& rel) {
+// bytes per lane) fits in registers, it is read whole, rel() hands the tile's
+// LDS pages back to the loaders, and only then pre() waits for the tile's event
+// and the activations are loaded: the weights never wait for the event.
+// Otherwise (NC == 0: any number of chunks, read chunk by chunk) pre() runs
+// first and rel() after the arithmetic.
+template <int NR, int NC, class Src, class Rel, class Pre>
+__device__ inline void gemv_tile(const Src& src, Act& a, const GemvIn& gi, int cw, LDS float* part, const Rel& rel,
+                                 const Pre& pre) {
+  const int K = gi.K, n0 = gi.n0, nrows = gi.nrows;
+  // pre() waits for the tile's event and says whether the activations must be
+  // loaded (false when an earlier tile of the same op left them in a)
+  auto deps = [&]() {
+    if (pre()) load_act_t<(NC > 0 ? NC : kMaxChunks)>(a, K, cw, gi.xf, gi.xb, gi.nw);
+  };
   const int lane = lane_id();
   const int nch = K / 8;
   const int cpw = (nch + kNW - 1) / kNW;
@@ -470,9 +494,11 @@ __device__ inline void gemv_tile(const Src& src, const Act& a, int K, int cw, in
     // FMAs and waits for it, paying the LDS latency once per row
     __builtin_amdgcn_sched_barrier(0);
     rel();
+    deps();
 #pragma unroll
     for (int j = 0; j < NC; ++j) fma_rows(j, wv[j]);
   } else {
+    deps();
 #pragma unroll
     for (int j = 0; j < kMaxChunks; ++j) {
       if (j < a.nc) {
@@ -487,6 +513,12 @@ __device__ inline void gemv_tile(const Src& src, const Act& a, int K, int cw, in
   gemv_reduce<NR>(acc, nrows, part);
 }
 
+// 16-byte chunks per lane of a wave's K range (the Act chunk count)
+__host__ __device__ inline int gemv_chunks(int K) {
+  const int cpw = (K / 8 + kNW - 1) / kNW;
+  return (cpw + 63) / 64;
+}
+
 // Tile shapes, by 16-byte chunks per lane nc = ceil(K / 2048): nc = 1 -> up to
 // 16 rows, nc = 2 -> up to 8, nc = 3..4 -> up to 4 (the wave's share, at most
 // 16 x 16 bytes per lane, is read whole); larger K -> up to 4 rows, chunk by
@@ -496,30 +528,19 @@ __host__ __device__ inline int gemv_max_rows(int K) {
   const int nc = (K + 2047) / 2048;
   return nc <= 1 ? 16 : nc == 2 ? 8 : 4;
 }
-template <class Src, class Rel>
-__device__ inline void gemv_rows(const Src& src, const Act& a, int K, int cw, int n0, int nrows, LDS float* part,
-                                 const Rel& rel) {
-  const int nc = a.nc;
+template <class Src, class Rel, class Pre>
+__device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int cw, LDS float* part, const Rel& rel,
+                                 const Pre& pre) {
+  const int nc = gemv_chunks(gi.K);
   if (nc == 1)
-    gemv_tile<16, 1>(src, a, K, cw, n0, nrows, part, rel);
+    gemv_tile<16, 1>(src, a, gi, cw, part, rel, pre);
   else if (nc == 2)
-    gemv_tile<8, 2>(src, a, K, cw, n0, nrows, part, rel);
+    gemv_tile<8, 2>(src, a, gi, cw, part, rel, pre);
   else if (nc <= 4)
-    gemv_tile<4, 4>(src, a, K, cw, n0, nrows, part, rel);
+    gemv_tile<4, 4>(src, a, gi, cw, part, rel, pre);
   else
-    gemv_tile<4, 0>(src, a, K, cw, n0, nrows, part, rel);
+    gemv_tile<4, 0>(src, a, gi, cw, part, rel, pre);
 }
-
-// Which activation and norm a GEMV op reads, and its K.
-struct GemvIn {
-  const GLB float* xf;
-  const GLB uint16_t* xb;
-  const GLB uint16_t* nw;
-  const GLB uint16_t* emb;  // embedding table when the input is the token's row (xf null)
-  const GLB int* tok;       // token ids [B]
-  int K;
-  int n0, nrows;  // rows in segment 0, total rows
-};
 
 __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
   GemvIn g;

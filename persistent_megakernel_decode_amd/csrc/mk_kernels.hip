@@ -159,6 +159,7 @@ __device__ void stage(const KArgs& a, LDS LT* L, int j) {
 template <class LT>
 __device__ void controller(const KArgs& a, LDS LT* L) {
   stage(a, L, 0);
+  if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, 1);
   for (int i = 0; i < a.max_len; ++i) {
     const Meta m = load_meta(L->meta[i % kMeta]);
     if (m.w(WOpcode) == OpNoop) {
@@ -170,6 +171,7 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
     // the slots of the instruction it is on and of the next one
     if (i + 2 > kMeta && !wait_lds_ge(a, L, &L->c.done_seq, i + 2 - kMeta, ErrDrain, i)) return;
     stage(a, L, i + 1);
+    if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, i + 2);
     if (m.w(WWaitCnt)) {
       const unsigned tgt = a.epoch * (unsigned)m.w(WWaitTgt);
       // lane k < kCtrSub reads sub-counter k; the event's count is their sum
@@ -384,15 +386,19 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
 }
 
 // ---------------------------------------------------------------------------
+// Compute waves.  A batch-1 GEMV tile's weights do not depend on any event: as
+// soon as the instruction is staged and its pages have landed, each wave reads
+// its share into registers and hands the pages back, and only then waits for
+// the instruction's event (controller "ready") and loads the activations.
+// Other ops wait for "ready" first.
 template <int HD, class LT>
 __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
   const int lane = lane_id();
   int seq = 0;
   int act_row = -1;
   Act act;
-  float act_ss = 0.f;
   for (int i = 0; i < a.max_len; ++i) {
-    if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
+    if (!wait_lds_ge(a, L, &L->c.meta_seq, i + 1, ErrReady, i)) return;
     const Meta m = load_meta(L->meta[i % kMeta]);
     const int op = m.w(WOpcode);
     if (op == OpNoop) break;
@@ -400,12 +406,12 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
     unsigned long long* tr = a.trace ? a.trace + ((size_t)blockIdx.x * a.max_len + i) * kTraceWords : nullptr;
     const int first = seq;
     seq += t.npages;
+    // the partial-sum slot i % 4 was last used by instruction i - 4
     if (!wait_lds_ge(a, L, &L->c.done_seq, i - 3, ErrDrain, i)) return;
     for (int pg = 0; pg < t.npages; ++pg) {
       const int sq = first + pg;
       if (!wait_lds_ge(a, L, &L->c.slot_full[sq % LT::NP], sq / LT::NP + 1, ErrPage, i)) return;
     }
-    if (cw == 0 && a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 1] = now_ticks();
     if (tr && lane == 0) tr[8 + cw] = now_ticks();
     // hand the tile's pages back to the loaders once every LDS read of them has
     // returned (non-returning adds; the loaders wait for kNW per use of a slot)
@@ -425,31 +431,41 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
     src.wrap = (uint32_t)(LT::NP * kPage);
     const int sl = i & 3;
     const bool gemv = is_gemv(op);
-    if (gemv && LT::MB) {
+    if (gemv && !LT::MB) {
       const GemvIn gi = gemv_input(m, a.c);
-      gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, &L->c.part[sl][cw][0], &L->c.ssp[sl][cw][0], release);
-    } else if (gemv) {
-      const GemvIn gi = gemv_input(m, a.c);
-      if (m.w(WOpRow) != act_row) {
-        load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
-        act_ss = wave_sum(act.ss);
+      bool live = true;
+      auto pre = [&]() {
+        if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) {
+          live = false;
+          return false;
+        }
+        if (cw == 0 && tr && lane == 0) tr[1] = now_ticks();
+        const bool load = m.w(WOpRow) != act_row;
         act_row = m.w(WOpRow);
-      }
-      if (cw == 0 && tr && lane == 0) tr[6] = now_ticks();
-      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, &L->c.part[sl][cw][0], release);
-      if (lane == 0) L->c.ssp[sl][cw][0] = act_ss;
+        return load;
+      };
+      gemv_rows(src, act, gi, cw, &L->c.part[sl][cw][0], release, pre);
+      if (!live) return;
+      if (lane == 0) L->c.ssp[sl][cw][0] = act.ssw;
       if (cw == 0 && tr && lane == 0) tr[7] = now_ticks();
-    } else if (op == OpAttn) {
-      attn_wave<HD>(src, m, a.c, cw, L->c.scratch[cw], cw == 0, cw == 0 ? tr : nullptr);
-    } else if (op == OpCombine) {
-      combine_wave<HD>(m, a.c, cw, cw == 0 ? tr : nullptr);
-    } else if (op == OpArgmax) {
-      argmax_part(m, a.c, cw, &L->c.part[sl][cw][0]);
+    } else {
+      if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
+      if (cw == 0 && tr && lane == 0) tr[1] = now_ticks();
+      if (gemv) {
+        const GemvIn gi = gemv_input(m, a.c);
+        gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, &L->c.part[sl][cw][0], &L->c.ssp[sl][cw][0], release);
+      } else if (op == OpAttn) {
+        attn_wave<HD>(src, m, a.c, cw, L->c.scratch[cw], cw == 0, cw == 0 ? tr : nullptr);
+      } else if (op == OpCombine) {
+        combine_wave<HD>(m, a.c, cw, cw == 0 ? tr : nullptr);
+      } else if (op == OpArgmax) {
+        argmax_part(m, a.c, cw, &L->c.part[sl][cw][0]);
+      }
+      if (!gemv) release();
     }
-    if (!gemv) release();
     if (tr && lane == 0) tr[12 + cw] = now_ticks();
     // arrival: GEMV partials are in LDS; other ops wrote global memory, which
-    // must be complete before the storer signals
+    // must be complete before the storer signals (workgroup release = vmcnt(0))
     if (!gemv) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_fetch_add(&L->c.arrive[sl], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
@@ -518,10 +534,8 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
       if (cw == 0) gemv_epilogue_mb(m, a.c, &part[0][0], &ssp[0][0], gemv_residual_mb(m, a.c));
     } else {
       Act act;
-      load_act(act, gi.K, cw, gi.xf, gi.xb, gi.nw);
-      const float ss = wave_sum(act.ss);
-      gemv_rows(src, act, gi.K, cw, gi.n0, gi.nrows, part[cw], [] {});
-      if (lane == 0) ssp[cw][0] = ss;
+      gemv_rows(src, act, gi, cw, part[cw], [] {}, [] { return true; });
+      if (lane == 0) ssp[cw][0] = act.ssw;
       __syncthreads();
       if (cw == 0) gemv_epilogue(m, a.c, part, &ssp[0][0], gemv_residual(m, a.c));
     }
