@@ -158,6 +158,11 @@ __device__ void stage(const KArgs& a, LDS LT* L, int j) {
 // ---------------------------------------------------------------------------
 template <class LT>
 __device__ void controller(const KArgs& a, LDS LT* L) {
+  // the last event this wave saw at or past a target, and the count it read:
+  // counters only grow within a run, so a later instruction waiting on the same
+  // event for a target within that count needs neither a poll nor an acquire
+  int seen_ev = -1;
+  unsigned seen_val = 0;
   stage(a, L, 0);
   if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, 1);
   for (int i = 0; i < a.max_len; ++i) {
@@ -172,7 +177,7 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
     if (i + 2 > kMeta && !wait_lds_ge(a, L, &L->c.done_seq, i + 2 - kMeta, ErrDrain, i)) return;
     stage(a, L, i + 1);
     if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, i + 2);
-    if (m.w(WWaitCnt)) {
+    if (m.w(WWaitCnt) && !(m.w(WWaitEv) == seen_ev && (int)(seen_val - a.epoch * (unsigned)m.w(WWaitTgt)) >= 0)) {
       const unsigned tgt = a.epoch * (unsigned)m.w(WWaitTgt);
       // lane k < kCtrSub reads sub-counter k; the event's count is their sum
       const int k = lane_id() < kCtrSub ? lane_id() : 0;
@@ -201,6 +206,8 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      seen_ev = m.w(WWaitEv);
+      seen_val = v;
     }
     if (a.trace && lane_id() == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 0] = now_ticks();
     if (lane_id() == 0) lds_store_rel(&L->c.ready_seq, i + 1);
