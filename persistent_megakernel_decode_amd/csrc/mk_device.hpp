@@ -441,83 +441,121 @@ __device__ inline void gemv_reduce(const float (&acc)[NR], int nrows, LDS float*
 // and the activations are loaded: the weights never wait for the event.
 // Otherwise (NC == 0: any number of chunks, read chunk by chunk) pre() runs
 // first and rel() after the arithmetic.
-template <int NR, int NC, class Src, class Rel, class Pre>
-__device__ inline void gemv_tile(const Src& src, Act& a, const GemvIn& gi, int cw, LDS float* part, const Rel& rel,
-                                 const Pre& pre) {
-  const int K = gi.K, n0 = gi.n0, nrows = gi.nrows;
-  // pre() waits for the tile's event and says whether the activations must be
-  // loaded (false when an earlier tile of the same op left them in a)
-  auto deps = [&]() {
-    if (pre()) load_act_t<(NC > 0 ? NC : kMaxChunks)>(a, K, cw, gi.xf, gi.xb, gi.nw);
-  };
-  const int lane = lane_id();
-  const int nch = K / 8;
-  const int cpw = (nch + kNW - 1) / kNW;
-  const int base = cw * cpw;
-  const int rb = K * 2;
-  float acc[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-  auto row_load = [&](int j, uint4 (&wv)[NR]) {
-    const int ch = lane + 64 * j;
-    const int cb = (ch < cpw && base + ch < nch ? base + ch : 0) * 16;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int rc = r < nrows ? r : nrows - 1;
-      const int seg = rc < n0 ? 0 : 1;
-      const int rr = rc < n0 ? rc : rc - n0;
-      wv[r] = src.ld16(seg, rr * rb + cb);
-    }
-  };
-  auto fma_rows = [&](int j, const uint4 (&wv)[NR]) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint4 u = wv[r];
-      float s = acc[r];
-      s = fmaf(bf16lo(u.x), a.x[j][0], s);
-      s = fmaf(bf16hi(u.x), a.x[j][1], s);
-      s = fmaf(bf16lo(u.y), a.x[j][2], s);
-      s = fmaf(bf16hi(u.y), a.x[j][3], s);
-      s = fmaf(bf16lo(u.z), a.x[j][4], s);
-      s = fmaf(bf16hi(u.z), a.x[j][5], s);
-      s = fmaf(bf16lo(u.w), a.x[j][6], s);
-      s = fmaf(bf16hi(u.w), a.x[j][7], s);
-      acc[r] = s;
-    }
-  };
-  if constexpr (NC > 0) {
-    uint4 wv[NC][NR];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) row_load(j, wv[j]);
-    // keep every LDS read of the share in flight at once: without this
-    // boundary the scheduler interleaves each read with the previous row's
-    // FMAs and waits for it, paying the LDS latency once per row
-    __builtin_amdgcn_sched_barrier(0);
-    rel();
-    deps();
-#pragma unroll
-    for (int j = 0; j < NC; ++j) fma_rows(j, wv[j]);
-  } else {
-    deps();
-#pragma unroll
-    for (int j = 0; j < kMaxChunks; ++j) {
-      if (j < a.nc) {
-        uint4 wv[NR];
-        row_load(j, wv);
-        __builtin_amdgcn_sched_barrier(0);
-        fma_rows(j, wv);
-      }
-    }
-    rel();
-  }
-  gemv_reduce<NR>(acc, nrows, part);
-}
-
 // 16-byte chunks per lane of a wave's K range (the Act chunk count)
 __host__ __device__ inline int gemv_chunks(int K) {
   const int cpw = (K / 8 + kNW - 1) / kNW;
   return (cpw + 63) / 64;
 }
+
+// Weight share of one wave: NR rows (rows r < n0 from segment 0, the rest from
+// segment 1 as row r - n0) x the 16-byte chunks l, l + 64, ... of the wave's K
+// range.  Rows past nrows re-read the last row and chunks outside the range
+// re-read chunk 0 (their activations are zero), so every load is issued before
+// any is used.
+struct GemvGeom {
+  int nch, cpw, base, rb, n0, nrows;
+  __device__ GemvGeom(const GemvIn& gi, int cw)
+      : nch(gi.K / 8), cpw((gi.K / 8 + kNW - 1) / kNW), base(cw * ((gi.K / 8 + kNW - 1) / kNW)), rb(gi.K * 2),
+        n0(gi.n0), nrows(gi.nrows) {}
+};
+template <int NR, class Src>
+__device__ __forceinline__ void gemv_load_chunk(const Src& src, const GemvGeom& g, int j, uint4* wv) {
+  const int ch = lane_id() + 64 * j;
+  const int cb = (ch < g.cpw && g.base + ch < g.nch ? g.base + ch : 0) * 16;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int rc = r < g.nrows ? r : g.nrows - 1;
+    const int seg = rc < g.n0 ? 0 : 1;
+    const int rr = rc < g.n0 ? rc : rc - g.n0;
+    wv[r] = src.ld16(seg, rr * g.rb + cb);
+  }
+}
+template <int NR>
+__device__ __forceinline__ void gemv_fma_chunk(const Act& a, int j, const uint4* wv, float (&acc)[NR]) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint4 u = wv[r];
+    float s = acc[r];
+    s = fmaf(bf16lo(u.x), a.x[j][0], s);
+    s = fmaf(bf16hi(u.x), a.x[j][1], s);
+    s = fmaf(bf16lo(u.y), a.x[j][2], s);
+    s = fmaf(bf16hi(u.y), a.x[j][3], s);
+    s = fmaf(bf16lo(u.z), a.x[j][4], s);
+    s = fmaf(bf16hi(u.z), a.x[j][5], s);
+    s = fmaf(bf16lo(u.w), a.x[j][6], s);
+    s = fmaf(bf16hi(u.w), a.x[j][7], s);
+    acc[r] = s;
+  }
+}
+// the whole share (NR x NC <= 16 registers of 16 bytes) into wv
+template <int NR, int NC, class Src>
+__device__ __forceinline__ void gemv_pull(const Src& src, const GemvGeom& g, uint4 (&wv)[16]) {
+#pragma unroll
+  for (int j = 0; j < NC; ++j) gemv_load_chunk<NR>(src, g, j, &wv[j * NR]);
+}
+template <int NR, int NC>
+__device__ __forceinline__ void gemv_finish(const Act& a, const uint4 (&wv)[16], int nrows, LDS float* part) {
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) gemv_fma_chunk<NR>(a, j, &wv[j * NR], acc);
+  gemv_reduce<NR>(acc, nrows, part);
+}
+// any K, 4 rows, chunk by chunk (the activations are already loaded)
+template <class Src>
+__device__ inline void gemv_chunked(const Src& src, const Act& a, const GemvGeom& g, LDS float* part) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) {
+    if (j < a.nc) {
+      uint4 wv[4];
+      gemv_load_chunk<4>(src, g, j, wv);
+      __builtin_amdgcn_sched_barrier(0);
+      gemv_fma_chunk<4>(a, j, wv, acc);
+    }
+  }
+  gemv_reduce<4>(acc, g.nrows, part);
+}
+
+// One GEMV tile for one compute wave.  When its weight share fits in registers
+// (the tile shapes below), the share is read whole from LDS, rel() hands the
+// tile's pages back to the loaders, and only then pre() waits for the tile's
+// event and says whether the activations must be loaded (false when an earlier
+// tile of the same op left them in a): the weights never wait for the event.
+// Otherwise pre() runs first and rel() after the arithmetic.  The activation
+// load has one call site, so it is inlined once.
+template <class Src, class Rel, class Pre>
+__device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int cw, LDS float* part, const Rel& rel,
+                                 const Pre& pre) {
+  const GemvGeom g(gi, cw);
+  const int nc = gemv_chunks(gi.K);
+  const int shape = nc == 1 ? 0 : nc == 2 ? 1 : nc <= 4 ? 2 : 3;
+  uint4 wv[16];
+  if (shape == 0)
+    gemv_pull<16, 1>(src, g, wv);
+  else if (shape == 1)
+    gemv_pull<8, 2>(src, g, wv);
+  else if (shape == 2)
+    gemv_pull<4, 4>(src, g, wv);
+  // keep every LDS read of the share in flight at once: without this boundary
+  // the scheduler interleaves each read with the previous row's FMAs and waits
+  // for it, paying the LDS latency once per row
+  __builtin_amdgcn_sched_barrier(0);
+  if (shape != 3) rel();
+  if (pre()) load_act_t<kMaxChunks>(a, gi.K, cw, gi.xf, gi.xb, gi.nw);
+  if (shape == 0)
+    gemv_finish<16, 1>(a, wv, g.nrows, part);
+  else if (shape == 1)
+    gemv_finish<8, 2>(a, wv, g.nrows, part);
+  else if (shape == 2)
+    gemv_finish<4, 4>(a, wv, g.nrows, part);
+  else {
+    gemv_chunked(src, a, g, part);
+    rel();
+  }
+}
+
 
 // Tile shapes, by 16-byte chunks per lane nc = ceil(K / 2048): nc = 1 -> up to
 // 16 rows, nc = 2 -> up to 8, nc = 3..4 -> up to 4 (the wave's share, at most
@@ -527,19 +565,6 @@ __host__ __device__ inline int gemv_chunks(int K) {
 __host__ __device__ inline int gemv_max_rows(int K) {
   const int nc = (K + 2047) / 2048;
   return nc <= 1 ? 16 : nc == 2 ? 8 : 4;
-}
-template <class Src, class Rel, class Pre>
-__device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int cw, LDS float* part, const Rel& rel,
-                                 const Pre& pre) {
-  const int nc = gemv_chunks(gi.K);
-  if (nc == 1)
-    gemv_tile<16, 1>(src, a, gi, cw, part, rel, pre);
-  else if (nc == 2)
-    gemv_tile<8, 2>(src, a, gi, cw, part, rel, pre);
-  else if (nc <= 4)
-    gemv_tile<4, 4>(src, a, gi, cw, part, rel, pre);
-  else
-    gemv_tile<4, 0>(src, a, gi, cw, part, rel, pre);
 }
 
 __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
