@@ -38,6 +38,7 @@ struct CtrlT {
   int slot_full[16];   // generation + 1 of the data in each ring slot (loaders -> compute)
   int slot_rel[16];    // compute-wave releases of each slot, cumulative (kNW per use)
   int arrive[4];       // compute waves done with instruction i (slot i % 4)
+  int rel_sink[64];    // target of the zero adds of lanes that release no page
   float part[4][kNW][PW];
   float ssp[4][kNW][SW];
   float scratch[kNW][kScratch];
@@ -421,15 +422,15 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
     }
     if (tr && lane == 0) tr[8 + cw] = now_ticks();
     // hand the tile's pages back to the loaders once every LDS read of them has
-    // returned (non-returning adds; the loaders wait for kNW per use of a slot)
+    // returned (the loaders wait for kNW per use of a slot): one non-returning
+    // add per lane, lane p < npages releasing page p, the others adding zero to
+    // a word of their own (no divergent branch, so values held in registers
+    // across the loop need no copies here)
     auto release = [&]() {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (lane == 0) {
-        for (int pg = 0; pg < t.npages; ++pg) {
-          const int slot = (first + pg) % LT::NP;
-          __hip_atomic_fetch_add(&L->c.slot_rel[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-      }
+      const bool mine = lane < t.npages;
+      LDS int* p = mine ? &L->c.slot_rel[(first + lane) % LT::NP] : &L->c.rel_sink[lane];
+      __hip_atomic_fetch_add(p, mine ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
     LdsSrc src;
     src.ring = lds_addr(&L->ring[0][0]);
