@@ -83,8 +83,9 @@ typedef struct {
  *   gemv_rows / 2); down_rows: rows per down tile (default 32768 / ffn,
  *   clamped to [1, 16]); lm_rows: LM-head rows per tile (default gemv_rows);
  * attn_splits: KV splits per (sequence, kv head) (default from the longest
- *   sequence: ceil((kv+1)/64) clamped to [1, 32], raised until one split's
- *   K and V rows fit in 64 KiB);
+ *   sequence: ceil((kv+1)/64) clamped to [1, 32], lowered to
+ *   ceil(2 num_cus / (batch n_kv_heads)) when that is smaller, then raised
+ *   until one split's K and V rows fit in 64 KiB);
  * timeout_ms: bound of every device-side wait (default 200);
  * dma_pages: 16 KiB pages each of the two weight-loader waves keeps in flight
  *   (1 to 3, default 2): enough to cover HBM latency, few enough that the

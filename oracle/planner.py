@@ -377,8 +377,10 @@ def resolve_opts(desc, batch, kv_len, opts=None):
     """Fill the 0 (default) fields: tiles of about 64 KiB of bf16 weights.
     gemv_rows = clamp(32768 // hidden, 4, 16); gateup_outs = gemv_rows // 2;
     down_rows = clamp(32768 // ffn, 1, 16); lm_rows = gemv_rows;
-    attn_splits = clamp(ceil((max kv + 1) / 64), 1, 32), then raised until one
-    split's K and V rows (2 * rows * head_dim * 2 bytes) fit in 64 KiB."""
+    attn_splits = clamp(ceil((max kv + 1) / 64), 1, 32), lowered to
+    max(1, ceil(2 * num_cus / (batch * n_kv_heads))) if that is smaller (about two
+    attention tasks per compute unit), then raised until one split's K and V rows
+    (2 * rows * head_dim * 2 bytes) fit in 64 KiB."""
     o = dict(DEFAULT_OPTS)
     o.update({k: v for k, v in (opts or {}).items() if v})
     H, F, hd = desc["hidden"], desc["ffn"], desc["head_dim"]
@@ -393,6 +395,7 @@ def resolve_opts(desc, batch, kv_len, opts=None):
     if not o["attn_splits"]:
         n = int(max(kv_len)) + 1
         S = max(1, min(32, ceil_div(n, 64)))
+        S = min(S, max(1, ceil_div(2 * o["num_cus"], len(kv_len) * desc["n_kv_heads"])))
         while ceil_div(n, S) * hd * 4 > 65536:
             S += 1
         o["attn_splits"] = S

@@ -275,6 +275,11 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
 }
 
 // ---------------------------------------------------------------------------
+// Cache policy of the weight DMA: non-temporal (each weight byte is read once
+// per step), so the stream does not push the step's activations and partial
+// results out of the L2.
+constexpr int kDmaNT = 2;
+
 template <class LT>
 __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
   const int lane = lane_id();
@@ -340,7 +345,7 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
         const GLB char* src = whole + lane * 16;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          __builtin_amdgcn_global_load_lds((const GLB void*)(src + j * 1024), (lds_void*)(dst + j * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const GLB void*)(src + j * 1024), (lds_void*)(dst + j * 1024), 16, 0, kDmaNT);
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -350,7 +355,7 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
             src = t.p0 + toff;
           else if (toff >= t.off1 && toff < t.off1 + t.len1)
             src = t.p1 + (toff - t.off1);
-          __builtin_amdgcn_global_load_lds((const GLB void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const GLB void*)src, (lds_void*)(dst + j * 1024), 16, 0, kDmaNT);
         }
       }
       const int last_of = pg == t.npages - 1 ? i : -1;

@@ -399,6 +399,10 @@ void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, Model
   if (!o->attn_splits) {
     int n = *std::max_element(kv_len.begin(), kv_len.end()) + 1;
     int S = std::max(1, std::min(32, ceil_div(n, 64)));
+    // no more splits than give about two tasks per compute unit over all
+    // (sequence, kv head) pairs: every split pays its own q/k/v loads
+    const int pairs = (int)kv_len.size() * m.n_kv_heads;
+    S = std::min(S, std::max(1, ceil_div(2L * o->num_cus, pairs)));
     while ((long)ceil_div(n, S) * m.head_dim * 4 > 65536) ++S;
     o->attn_splits = S;
   }
