@@ -61,6 +61,9 @@ def _load():
         lib.synth_mix.restype = u64
         lib.synth_f32_to_bf16.argtypes = [ctypes.c_float]
         lib.synth_f32_to_bf16.restype = ctypes.c_uint16
+        lib.synth_fp8_weights.argtypes = [u64, u64, dbl, u64, u64, vp, vp]
+        lib.synth_e4m3_code.argtypes = [dbl]
+        lib.synth_e4m3_code.restype = ctypes.c_uint8
         _lib = lib
     return _lib
 
@@ -98,6 +101,19 @@ def f32_to_bf16_bits(f):
     return int(_load().synth_f32_to_bf16(float(f)))
 
 
+def fp8_weights(seed, tid, N, K, sigma=0.02):
+    """[N, K] OCP e4m3 codes (uint8) and [ceil(N/128), K/128] fp32 block scales."""
+    assert K % 128 == 0
+    codes = np.empty((N, K), dtype=np.uint8)
+    scales = np.empty(((N + 127) // 128, K // 128), dtype=np.float32)
+    _load().synth_fp8_weights(seed, tid, sigma, N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def e4m3_code(v):
+    return int(_load().synth_e4m3_code(float(v)))
+
+
 # --------------------------------------------------------------------------
 # Workload shapes
 # --------------------------------------------------------------------------
@@ -115,6 +131,72 @@ CONFIGS = {
                      ffn=12288, vocab=151936, tied=0, qk_norm=1, rms_eps=1e-5, rope_theta=1e4,
                      batch=1, kv_len=4096, seed=1003),
 }
+
+# GLM-style pre-attention path (one layer's prologue before sparse MLA):
+# M token rows = n_seqs requests x rows_per_seq tokens, token t of request r at
+# cache position pos0 + t.  Column layout of the QKV-A output:
+# [q_lora | kv_lora | rope_dim]; each query head is head_dim = nope + rope_dim.
+GLM_CONFIGS = {
+    "glm_preattn": dict(arch="glm", hidden=6144, q_lora=1536, kv_lora=512, rope_dim=64, n_q_heads=64,
+                        head_dim=192, n_idx_heads=32, idx_head_dim=128, n_gate=64, n_seqs=2, rows_per_seq=8,
+                        pos0=8192, rms_eps=1e-5, rope_theta=1e4, seed=1004),
+    "glm_tiny": dict(arch="glm", hidden=512, q_lora=256, kv_lora=128, rope_dim=64, n_q_heads=4,
+                     head_dim=192, n_idx_heads=2, idx_head_dim=128, n_gate=16, n_seqs=2, rows_per_seq=3,
+                     pos0=100, rms_eps=1e-5, rope_theta=1e4, seed=1005),
+}
+CONFIGS.update(GLM_CONFIGS)
+# GLM weight slots, in this fixed order: norms bf16, linear weights fp8 [out, in]
+# with fp32 [ceil(out/128), in/128] block scales.
+GLM_SLOTS = ("attn_norm", "w_qkva", "s_qkva", "w_gate", "s_gate", "w_idxk", "s_idxk", "q_a_norm", "kv_a_norm",
+             "w_qb", "s_qb", "w_idxq", "s_idxq")
+TID_GLM = 30000
+
+
+def glm_dims(cfg):
+    """(M, N_qkva, N_qb, N_idxq) of a GLM config."""
+    M = cfg["n_seqs"] * cfg["rows_per_seq"]
+    return (M, cfg["q_lora"] + cfg["kv_lora"] + cfg["rope_dim"], cfg["n_q_heads"] * cfg["head_dim"],
+            cfg["n_idx_heads"] * cfg["idx_head_dim"])
+
+
+def glm_positions(cfg):
+    """cache position and request of each token row"""
+    M = cfg["n_seqs"] * cfg["rows_per_seq"]
+    m = np.arange(M)
+    return (cfg["pos0"] + m % cfg["rows_per_seq"]).astype(np.int32), (m // cfg["rows_per_seq"]).astype(np.int32)
+
+
+def glm_capacity(cfg):
+    return int((cfg["pos0"] + cfg["rows_per_seq"] + 15) // 16 * 16)
+
+
+def make_glm_inputs(name, norm_sigma=0.0, **overrides):
+    """All inputs of the GLM pre-attention step: dict(cfg, weights, x, r, pos, req,
+    kv_cache [n_seqs][cap][kv_lora + rope_dim], idx_cache [n_seqs][cap][idx_head_dim]).
+    x, r ~N(0,1) bf16 [M, hidden]; fp8 weights ~N(0, 0.02) quantized per block;
+    norm weights 1.0 (or ~N(1, norm_sigma)); both caches all NaN (the step
+    writes only the rows of its tokens)."""
+    cfg = config(name, **overrides)
+    seed, H, QL = cfg["seed"], cfg["hidden"], cfg["q_lora"]
+    M, Nqkva, Nqb, Niq = glm_dims(cfg)
+    shapes = {"w_qkva": (Nqkva, H), "w_gate": (cfg["n_gate"], H), "w_idxk": (cfg["idx_head_dim"], H),
+              "w_qb": (Nqb, QL), "w_idxq": (Niq, QL)}
+    norms = {"attn_norm": H, "q_a_norm": QL, "kv_a_norm": cfg["kv_lora"]}
+    w = {}
+    for i, s in enumerate(GLM_SLOTS):
+        if s in shapes:
+            w[s], w["s_" + s[2:]] = fp8_weights(seed, TID_GLM + i, *shapes[s])
+        elif s in norms:
+            w[s] = (np.full(norms[s], BF16_ONE, dtype=np.uint16) if norm_sigma == 0.0 else
+                    normal_bf16(seed, TID_GLM + i, (norms[s],), norm_sigma, mean=1.0))
+    x = normal_bf16(seed, TID_GLM + 100, (M, H), 1.0)
+    r = normal_bf16(seed, TID_GLM + 101, (M, H), 1.0)
+    pos, req = glm_positions(cfg)
+    cap = glm_capacity(cfg)
+    kvc = np.full((cfg["n_seqs"], cap, cfg["kv_lora"] + cfg["rope_dim"]), BF16_NAN, dtype=np.uint16)
+    idc = np.full((cfg["n_seqs"], cap, cfg["idx_head_dim"]), BF16_NAN, dtype=np.uint16)
+    return dict(cfg=cfg, weights=w, x=x, r=r, pos=pos, req=req, kv_cache=kvc, idx_cache=idc)
+
 
 # Per-layer weight slots, in this fixed order.  Shapes are [out, in] row-major.
 LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate", "w_up", "w_down")

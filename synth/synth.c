@@ -17,6 +17,11 @@
  *                 value = mean + sigma * z, rounded to fp32, then fp32 -> bf16
  *                 round-to-nearest-even on the bit pattern.
  *   uniform int : lo + word(k, i) mod (hi - lo + 1)
+ *   fp8 weights : w[n][k] = fp32(sigma * normal(n * K + k)); per 128 x 128
+ *                 block (row block n / 128, column block k / 128) the fp32 scale
+ *                 is amax / 448 (1 when the block is all zero) and the stored
+ *                 byte is the OCP FP8 E4M3 (e4m3fn) code of w / scale, rounded
+ *                 to nearest even and saturated to +-448.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -92,3 +97,52 @@ void synth_fill_u16(uint16_t v, uint64_t n, uint16_t* out) {
 
 uint64_t synth_mix(uint64_t x) { return mix(x); }
 uint16_t synth_f32_to_bf16(float f) { return f32_to_bf16_rne(f); }
+
+/* OCP FP8 E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * no infinities; S.1111.111 is NaN; largest finite 448 = 1.75 * 2^8; smallest
+ * normal 2^-6; subnormals m * 2^-9).  Round to nearest even, saturate. */
+static uint8_t e4m3_code(double v) {
+  if (isnan(v)) return 0x7F;
+  uint8_t sign = signbit(v) ? 0x80 : 0;
+  double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < 0x1.0p-6) { /* subnormal range: multiples of 2^-9 (8 * 2^-9 is the smallest normal) */
+    double m = nearbyint(a * 512.0);
+    return sign | (uint8_t)m;
+  }
+  int ex;
+  double f = frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1) */
+  int E = ex - 1;           /* a = (2f) * 2^E, 2f in [1, 2) */
+  double q = nearbyint((2.0 * f - 1.0) * 8.0);
+  if (q == 8.0) { q = 0.0; ++E; }
+  if (E > 8 || (E == 8 && q == 7.0)) return sign | 0x7E;
+  return sign | (uint8_t)(((E + 7) << 3) | (int)q);
+}
+
+/* [N, K] fp8 weights and [ceil(N / 128), K / 128] fp32 block scales (K % 128 == 0). */
+void synth_fp8_weights(uint64_t seed, uint64_t tid, double sigma, uint64_t N, uint64_t K,
+                       uint8_t* codes, float* scales) {
+  uint64_t k = key_of(seed, tid);
+  uint64_t NB = (N + 127) / 128, KB = K / 128;
+#pragma omp parallel for schedule(static)
+  for (int64_t bb = 0; bb < (int64_t)(NB * KB); ++bb) {
+    uint64_t nb = (uint64_t)bb / KB, kb = (uint64_t)bb % KB;
+    uint64_t n1 = (nb + 1) * 128 < N ? (nb + 1) * 128 : N;
+    float amax = 0.f;
+    for (uint64_t n = nb * 128; n < n1; ++n)
+      for (uint64_t c = kb * 128; c < kb * 128 + 128; ++c) {
+        float w = (float)(sigma * normal_at(k, n * K + c));
+        float aw = fabsf(w);
+        if (aw > amax) amax = aw;
+      }
+    float sc = amax > 0.f ? amax / 448.f : 1.f;
+    scales[bb] = sc;
+    for (uint64_t n = nb * 128; n < n1; ++n)
+      for (uint64_t c = kb * 128; c < kb * 128 + 128; ++c) {
+        float w = (float)(sigma * normal_at(k, n * K + c));
+        codes[n * K + c] = e4m3_code((double)(w / sc));
+      }
+  }
+}
+
+uint8_t synth_e4m3_code(double v) { return e4m3_code(v); }
