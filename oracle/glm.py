@@ -22,7 +22,11 @@ fp8 e4m3 weights with fp32 scales per 128 x 128 block.
 Readings where the pages leave a step open (each listed in the design notes):
   - RMSNorm: y = h / sqrt(mean(h^2) + eps) * w, in full precision.
   - Activation quantization: per (row, 128-column block), s = max(amax, 1e-4) / 448,
-    code = e4m3(y / s) rounded to nearest even and saturated at +-448.
+    code = e4m3(y / s) rounded to nearest even and saturated at +-448.  The
+    quotient is evaluated as 448 * u / max|u| with u = the row before its 1/rms
+    factor (h * w), which is the same number (the factor cancels) but exact for
+    bf16-derived u, so that exact ties -- frequent when u has few significant
+    bits -- resolve to the even code by definition, not by rounding noise.
   - Weights: W = e4m3 value * scale of the weight's 128 x 128 block.
   - QKV-A, indexer-K, QKV-B and indexer-Q take the dequantized fp8 activation
     (code value * scale); the head gate takes the unquantized norm output.
@@ -109,18 +113,41 @@ def bf16_decode(bits):
 # ---------------------------------------------------------------------------
 # operators
 # ---------------------------------------------------------------------------
+def rms_inv(h, eps):
+    """1 / sqrt(mean(h^2) + eps) per row."""
+    h = np.asarray(h, dtype=np.float64)
+    return 1.0 / np.sqrt(np.mean(h * h, axis=-1) + eps)
+
+
 def rmsnorm(h, w, eps):
     h = np.asarray(h, dtype=np.float64)
     return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps) * w
 
 
-def quantize_rows(y, floor=ACT_SCALE_FLOOR):
-    """Per (row, 128-column block): scale s = max(amax, floor) / 448 and codes
-    e4m3(y / s).  Returns (codes uint8 [M, K], scales fp64 [M, K / 128])."""
-    M, K = y.shape
-    yb = y.reshape(M, K // BLOCK, BLOCK)
-    s = np.maximum(np.max(np.abs(yb), axis=2), floor) / E4M3_MAX
-    codes = e4m3_encode(yb / s[:, :, None]).reshape(M, K)
+def norm_quant(h, w, eps):
+    """RMSNorm then quant: (norm output, codes, scales)."""
+    h = np.asarray(h, dtype=np.float64)
+    inv = rms_inv(h, eps)
+    u = h * w
+    codes, scales = quantize_rows(u, inv)
+    return u * inv[:, None], codes, scales
+
+
+def quantize_rows(u, inv=None, floor=ACT_SCALE_FLOOR):
+    """Quantize the rows n = u * inv (inv: one factor per row, default 1): per
+    (row, 128-column block) scale s = max(max|n|, floor) / 448 and codes
+    e4m3(n / s), the quotient taken as 448 * u / max|u| while the floor is not
+    active.  Returns (codes uint8 [M, K], scales fp64 [M, K / 128])."""
+    M, K = u.shape
+    inv = np.ones(M) if inv is None else np.asarray(inv, dtype=np.float64).reshape(M)
+    ub = u.reshape(M, K // BLOCK, BLOCK)
+    amu = np.max(np.abs(ub), axis=2)
+    amn = amu * inv[:, None]
+    s = np.maximum(amn, floor) / E4M3_MAX
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = np.where((amn >= floor)[:, :, None], E4M3_MAX * ub / amu[:, :, None],
+                     ub * inv[:, None, None] / s[:, :, None])
+    codes = e4m3_encode(q).reshape(M, K)
     return codes, s
 
 
@@ -167,8 +194,7 @@ def rope(v, pos, theta):
 def a0(x_bits, r_bits, norm_bits, eps):
     """Add + RMSNorm + quant: (r_out bf16 bits, norm output, codes, scales)."""
     h = bf16_decode(x_bits) + bf16_decode(r_bits)
-    n = rmsnorm(h, bf16_decode(norm_bits), eps)
-    codes, scales = quantize_rows(n)
+    n, codes, scales = norm_quant(h, bf16_decode(norm_bits), eps)
     return bf16_bits(h), n, codes, scales
 
 
@@ -192,8 +218,7 @@ def glm_step(inp):
     kidx = bf16_bits(block_gemm(a, w["w_idxk"], w["s_idxk"]))
     out["kidx"] = kidx
     # q path: RMSNorm + quant, then QKV-B (RoPE on each head's last RD dims) and indexer-Q
-    qn = rmsnorm(qkva[:, :QL], bf16_decode(w["q_a_norm"]), eps)
-    q8, q_s = quantize_rows(qn)
+    _, q8, q_s = norm_quant(qkva[:, :QL], bf16_decode(w["q_a_norm"]), eps)
     out.update(qa_codes=q8, qa_scales=q_s)
     qa = dequant_rows(q8, q_s)
     q = block_gemm(qa, w["w_qb"], w["s_qb"]).reshape(M, nh, hd)

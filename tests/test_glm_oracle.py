@@ -105,6 +105,33 @@ def test_bf16_round_matches_torch():
 # ---------------------------------------------------------------------------
 # operators, against brute force
 # ---------------------------------------------------------------------------
+def test_a0_exact_ties_resolve_to_even():
+    """With unit norm weights the quantizer's quotient 448 h / max|h| of
+    bf16-derived values often lands exactly on an e4m3 midpoint; exact rational
+    arithmetic and a nearest-code search with ties to the even code decide every
+    such element the way the oracle does."""
+    from fractions import Fraction
+    M, H, eps = 2, 512, 1e-5
+    x = synth.normal_bf16(13, 1, (M, H), 1.0)
+    r = synth.normal_bf16(13, 2, (M, H), 1.0)
+    w = np.full(H, synth.BF16_ONE, dtype=np.uint16)
+    _, _, codes, _ = G.a0(x, r, w, eps)
+    table = [(c, Fraction(G.e4m3_decode(np.array([c]))[0])) for c in range(0x7F)]
+    ties = 0
+    for m in range(M):
+        h = [Fraction(G.bf16_decode(x[m, k])) + Fraction(G.bf16_decode(r[m, k])) for k in range(H)]
+        for b in range(H // 128):
+            amax = max(abs(v) for v in h[b * 128:(b + 1) * 128])
+            for k in range(b * 128, (b + 1) * 128):
+                q = 448 * h[k] / amax
+                a = abs(q)
+                best = min(table, key=lambda cv: (abs(cv[1] - a), cv[0] & 1))
+                d = sorted(abs(v - a) for _, v in table)
+                ties += d[0] == d[1]
+                assert codes[m, k] == (best[0] | (0x80 if q < 0 else 0)), (m, k, q)
+    assert ties > 0  # the case this test is about does occur
+
+
 def test_a0_brute_force():
     M, H, eps = 2, 256, 1e-5
     x = synth.normal_bf16(11, 1, (M, H), 1.0)
@@ -215,8 +242,7 @@ def test_step_with_selection_weights():
     assert not np.array_equal(o["gate"], a[:, sel_g])
     assert np.array_equal(o["kidx"], G.bf16_bits(a[:, sel_k]))
     # the q path: RMSNorm of the q part, quantized, then selected
-    qn = G.rmsnorm(o["qkva"][:, :QL], G.bf16_decode(w["q_a_norm"]), cfg["rms_eps"])
-    qc, qs = G.quantize_rows(qn)
+    _, qc, qs = G.norm_quant(o["qkva"][:, :QL], G.bf16_decode(w["q_a_norm"]), cfg["rms_eps"])
     assert np.array_equal(qc, o["qa_codes"])
     qa = G.dequant_rows(qc, qs)
     qi = G.bf16_decode(o["qidx"].reshape(M, Niq))
