@@ -59,9 +59,29 @@ int mk_abi_version(void);
  * weight_dtype: MK_BF16 (row-major [out, in], PyTorch Linear layout).
  * max_kv_len: rows per sequence in the KV cache (capacity); kv_len[b] + 1 <= it.
  * RoPE is rotate-half with angle pos * rope_theta^(-2i/head_dim).
+ *
+ * MK_ARCH_GLM_PREATTN: the GLM-style path before sparse MLA (MegaRTP article,
+ * sections 1 and 4) for M = batch token rows (1..16), rows_per_seq rows per
+ * request (row m belongs to request m / rows_per_seq, kv_len[m] is its cache
+ * position): h = x + r, r_out = bf16(h); y = RMSNorm(h) * attn_norm; y is
+ * quantized to OCP E4M3 per (row, 128 columns) with scale max(amax, 1e-4) / 448;
+ * three independent branches: QKV-A (y8 -> q_lora + kv_lora + rope_dim), head
+ * gate (y -> n_gate, fp32 output) and indexer-K (y8 -> idx_head_dim, bf16 into
+ * the indexer cache); the q columns are RMSNorm'd (q_a_norm) and requantized,
+ * then QKV-B (-> n_q_heads x head_dim, rotate-half RoPE on each head's last
+ * rope_dim dims, bf16 output) and indexer-Q (-> n_idx_heads x idx_head_dim,
+ * bf16 output); the KV row [RMSNorm(kv) * kv_a_norm | RoPE(k_rope)] (bf16) is
+ * written at the row's position.  weight_dtype MK_FP8_E4M3_B128: linear
+ * weights are E4M3 codes [out, in] with fp32 scales [ceil(out/128)][in/128].
+ * Fields used: hidden, n_q_heads, head_dim, max_kv_len, rms_eps, rope_theta
+ * and the GLM fields below (n_layers must be 1; the Llama-only fields are ignored).
+ * Supported: hidden and q_lora multiples of 128, kv_lora a multiple of 8,
+ * head_dim - rope_dim and rope_dim positive multiples of 16 with each head's
+ * rope dims inside one 128-row scale block, n_gate, idx_head_dim and
+ * n_idx_heads * idx_head_dim multiples of 16 (64, 128, 4096 for the GLM shape).
  * ------------------------------------------------------------------------- */
-enum { MK_ARCH_LLAMA = 1, MK_ARCH_QWEN3 = 2 };
-enum { MK_BF16 = 0 };
+enum { MK_ARCH_LLAMA = 1, MK_ARCH_QWEN3 = 2, MK_ARCH_GLM_PREATTN = 3 };
+enum { MK_BF16 = 0, MK_FP8_E4M3_B128 = 1 };
 
 typedef struct {
   uint32_t abi_version; /* MK_ABI_VERSION */
@@ -73,6 +93,8 @@ typedef struct {
   int32_t weight_dtype; /* MK_BF16 */
   int32_t max_kv_len;   /* KV-cache capacity per sequence (rows) */
   float rms_eps, rope_theta;
+  /* MK_ARCH_GLM_PREATTN only (0 otherwise) */
+  int32_t q_lora, kv_lora, rope_dim, n_idx_heads, idx_head_dim, n_gate, rows_per_seq;
 } mk_model_desc;
 
 /* Planning options; pass NULL (or 0 in a field) for the defaults.
@@ -165,6 +187,11 @@ mk_status mk_plan_export(const mk_plan* plan, mk_plan_view* out);
  * w_gate, w_up, w_down); q_norm/k_norm may be NULL without qk_norm.  embed and
  * final_norm are required; lm_head is ignored when tied.  All bf16. */
 #define MK_LAYER_SLOTS 11
+/* MK_ARCH_GLM_PREATTN: layer_ptrs holds MK_GLM_SLOTS device pointers in slot
+ * order (attn_norm bf16 [hidden], w_qkva codes, s_qkva scales, w_gate, s_gate,
+ * w_idxk, s_idxk, q_a_norm bf16 [q_lora], kv_a_norm bf16 [kv_lora], w_qb, s_qb,
+ * w_idxq, s_idxq); embed, final_norm and lm_head are ignored. */
+#define MK_GLM_SLOTS 13
 typedef struct {
   const void* const* layer_ptrs;
   const void* embed;
@@ -179,6 +206,11 @@ typedef struct {
  *   are read, nothing else is touched, so repeated runs are idempotent.
  * tokens: device int32 [batch], input token ids (ids outside [0, vocab) are
  *   clamped into it on the device).
+ * MK_ARCH_GLM_PREATTN: tokens is device bf16 [2][batch][hidden] (x, then r);
+ *   kv_cache is device bf16, the KV cache [n_seq][max_kv_len][kv_lora +
+ *   rope_dim] followed by the indexer cache [n_seq][max_kv_len][idx_head_dim]
+ *   (n_seq = ceil(batch / rows_per_seq)); only row kv_len[m] of request
+ *   m / rows_per_seq is written in each.
  * Results stay in the plan (see mk_plan_output).  Only enqueues work; the
  * first call uploads the plan; pointer changes rewrite the operand table.
  * A device wait that exceeds the plan's bound makes the grid exit early and is
@@ -197,8 +229,19 @@ mk_status mk_run_layerwise(mk_plan* plan, const mk_weights* weights, void* kv_ca
  * MK_OUT_QKV fp32 [n_layers][batch][n_kv_heads][(n_q/n_kv + 2) * head_dim]
  *   (per kv head: its q heads, then k, then v, before RoPE);
  * MK_OUT_HIDDEN fp32 [n_layers][2][batch][hidden] (residual stream after the
- *   attention block and after the FFN block of each layer). */
+ *   attention block and after the FFN block of each layer).
+ * GLM: MK_OUT_GLM_R bf16 [M][hidden] (x + r); MK_OUT_GLM_Q bf16 [M][n_q_heads]
+ *   [head_dim]; MK_OUT_GLM_QIDX bf16 [M][n_idx_heads][idx_head_dim];
+ *   MK_OUT_GLM_GATE fp32 [M][n_gate]; and the intermediates MK_OUT_GLM_NORM fp32
+ *   [M][hidden], MK_OUT_GLM_ACT (E4M3 codes, uint8 [M][hidden]),
+ *   MK_OUT_GLM_ACT_SCALE fp32 [M][hidden/128], MK_OUT_GLM_QKVA fp32 [M][q_lora
+ *   + kv_lora + rope_dim], MK_OUT_GLM_QA uint8 [M][q_lora], MK_OUT_GLM_QA_SCALE
+ *   fp32 [M][q_lora/128]. */
 enum { MK_OUT_LOGITS = 0, MK_OUT_NEXT_TOKEN = 1, MK_OUT_QKV = 2, MK_OUT_HIDDEN = 3 };
+enum {
+  MK_OUT_GLM_R = 4, MK_OUT_GLM_Q = 5, MK_OUT_GLM_QIDX = 6, MK_OUT_GLM_GATE = 7, MK_OUT_GLM_NORM = 8,
+  MK_OUT_GLM_ACT = 9, MK_OUT_GLM_ACT_SCALE = 10, MK_OUT_GLM_QKVA = 11, MK_OUT_GLM_QA = 12, MK_OUT_GLM_QA_SCALE = 13
+};
 mk_status mk_plan_output(const mk_plan* plan, int32_t which, void** dev_ptr, size_t* bytes);
 /* Enqueue a device-to-device copy of output 'which' into dst (device, at least
  * 'bytes' = the output's size) on 'stream'. */

@@ -50,6 +50,9 @@ N_PAY = 10
 
 # opcodes of the Llama-family decode step
 NOOP, QKV, ATTN, COMBINE, OPROJ, GATEUP, DOWN, LMHEAD, ARGMAX = range(9)
+# opcodes of the GLM-style pre-attention path
+G_A0, G_QKVA, G_GATE, G_IDXK, G_QANORM, G_QKVB, G_IDXQ = range(9, 16)
+GLM_ROWS = 16  # weight rows per fp8 GEMM tile (the matrix-core M dimension)
 
 
 def lcm(a, b):
@@ -411,7 +414,55 @@ def split_range(pos, S, s):
     return lo, hi
 
 
+def glm_graph(desc, M):
+    """GLM-style pre-attention path (MegaRTP article, section 4, "OpGraph"/"TaskGraph":
+    A0 works one token row per tile; GEMMs are cut into output-row tiles; the
+    QKV-A, head-gate and indexer-K branches hang off A0 independently; the q path
+    (RMSNorm + requant of QKV-A's q columns, one row per tile) feeds QKV-B and
+    indexer-Q).  QKV-B tiles: per head, nope/16 plain 16-row tiles, then rope/16
+    tiles that pair 8 rows of the first half of the rope dims with the 8 rows
+    rope/2 further on, so one tile holds both members of its RoPE pairs.
+    Payload: A0 / q-norm (row); GEMMs (row0, nrows, second-segment row0 or -1)."""
+    H, QL, KL, RD = desc["hidden"], desc["q_lora"], desc["kv_lora"], desc["rope_dim"]
+    nh, hd = desc["n_q_heads"], desc["head_dim"]
+    NOPE, R = hd - RD, GLM_ROWS
+    Na = QL + KL + RD
+    Ng, Nk, Niq = desc["n_gate"], desc["idx_head_dim"], desc["n_idx_heads"] * desc["idx_head_dim"]
+    assert NOPE % R == 0 and RD % R == 0
+    ops, edges = [], []
+
+    def add(op):
+        ops.append(op)
+        return len(ops) - 1
+
+    def rows(N):
+        return lambda x, y, z: (x * R, min(R, N - x * R), -1)
+
+    def qb_rows(x, y, z):
+        if y < NOPE // R:
+            return (x * hd + y * R, R, -1)
+        j = y - NOPE // R
+        return (x * hd + NOPE + j * (R // 2), R // 2, x * hd + NOPE + RD // 2 + j * (R // 2))
+
+    a0 = add(Op("a0", G_A0, (M,), 0, 0, lambda x, y, z: (x,)))
+    qa = add(Op("qkva", G_QKVA, (ceil_div(Na, R),), 0, 0, rows(Na)))
+    ga = add(Op("gate", G_GATE, (ceil_div(Ng, R),), 0, 0, rows(Ng)))
+    ik = add(Op("idxk", G_IDXK, (ceil_div(Nk, R),), 0, 0, rows(Nk)))
+    qn = add(Op("qanorm", G_QANORM, (M,), 0, 0, lambda x, y, z: (x,)))
+    qb = add(Op("qkvb", G_QKVB, (nh, (NOPE + RD) // R), 0, 0, qb_rows))
+    iq = add(Op("idxq", G_IDXQ, (ceil_div(Niq, R),), 0, 0, rows(Niq)))
+    for c in (qa, ga, ik):
+        edges.append(Edge(a0, c, (0,), (), [M, H, 1, 1], [1, H, 1, 1], [M, H, 1, 1], "act"))
+    edges.append(Edge(qa, qn, (1,), (0,), [M, Na, 1, 1], [M, R, 1, 1], [1, Na, 1, 1], "qkva"))
+    for c in (qb, iq):
+        edges.append(Edge(qn, c, (0,), (), [M, QL, 1, 1], [1, QL, 1, 1], [M, QL, 1, 1], "qa"))
+    return ops, edges, dict(opts=dict(num_cus=0))
+
+
 def model_graph(desc, batch, kv_len, opts=None):
+    if desc.get("arch") == "glm":
+        ops, edges, info = glm_graph(desc, batch)
+        return ops, edges, info
     o = resolve_opts(desc, batch, kv_len, opts)
     H, nq, nkv, hd = desc["hidden"], desc["n_q_heads"], desc["n_kv_heads"], desc["head_dim"]
     F, V, L = desc["ffn"], desc["vocab"], desc["n_layers"]
@@ -457,7 +508,11 @@ def model_graph(desc, batch, kv_len, opts=None):
 
 
 def plan_model(desc, batch, kv_len, opts=None):
-    o = resolve_opts(desc, batch, kv_len, opts)
+    if desc.get("arch") == "glm":
+        o = dict(DEFAULT_OPTS)
+        o.update({k: v for k, v in (opts or {}).items() if v})
+    else:
+        o = resolve_opts(desc, batch, kv_len, opts)
     ops, edges, info = model_graph(desc, batch, kv_len, o)
     pl = plan_graph(ops, edges, o["num_cus"])
     pl.info = info

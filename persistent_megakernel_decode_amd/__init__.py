@@ -19,10 +19,20 @@ LIB_PATH = os.path.join(_HERE, "libmk.so")
 
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_TIMEOUT, MK_E_STATE = 0, -1, -2, -3, -4, -5, -6
 MK_ABI_VERSION = 1
-MK_ARCH_LLAMA, MK_ARCH_QWEN3 = 1, 2
-MK_BF16 = 0
+MK_ARCH_LLAMA, MK_ARCH_QWEN3, MK_ARCH_GLM_PREATTN = 1, 2, 3
+MK_BF16, MK_FP8_E4M3_B128 = 0, 1
 MK_LAYER_SLOTS = 11
+MK_GLM_SLOTS = 13
 MK_OUT_LOGITS, MK_OUT_NEXT_TOKEN, MK_OUT_QKV, MK_OUT_HIDDEN = 0, 1, 2, 3
+(MK_OUT_GLM_R, MK_OUT_GLM_Q, MK_OUT_GLM_QIDX, MK_OUT_GLM_GATE, MK_OUT_GLM_NORM, MK_OUT_GLM_ACT,
+ MK_OUT_GLM_ACT_SCALE, MK_OUT_GLM_QKVA, MK_OUT_GLM_QA, MK_OUT_GLM_QA_SCALE) = range(4, 14)
+# element type of each output: "f32", "i32", "bf16" (returned as int16 bit patterns) or "u8"
+OUTPUT_TYPES = {MK_OUT_LOGITS: "f32", MK_OUT_NEXT_TOKEN: "i32", MK_OUT_QKV: "f32", MK_OUT_HIDDEN: "f32",
+                MK_OUT_GLM_R: "bf16", MK_OUT_GLM_Q: "bf16", MK_OUT_GLM_QIDX: "bf16", MK_OUT_GLM_GATE: "f32",
+                MK_OUT_GLM_NORM: "f32", MK_OUT_GLM_ACT: "u8", MK_OUT_GLM_ACT_SCALE: "f32", MK_OUT_GLM_QKVA: "f32",
+                MK_OUT_GLM_QA: "u8", MK_OUT_GLM_QA_SCALE: "f32"}
+GLM_SLOTS = ("attn_norm", "w_qkva", "s_qkva", "w_gate", "s_gate", "w_idxk", "s_idxk", "q_a_norm", "kv_a_norm",
+             "w_qb", "s_qb", "w_idxq", "s_idxq")
 LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_plan_export", "mk_run",
             "mk_run_layerwise", "mk_plan_output", "mk_plan_copy_output", "mk_plan_check", "mk_plan_set_trace",
@@ -35,7 +45,8 @@ class ModelDesc(ctypes.Structure):
     _fields_ = [("abi_version", u32), ("struct_size", u32), ("arch", i32), ("n_layers", i32), ("hidden", i32),
                 ("n_q_heads", i32), ("n_kv_heads", i32), ("head_dim", i32), ("ffn", i32), ("vocab", i32),
                 ("tied_lm_head", i32), ("qk_norm", i32), ("weight_dtype", i32), ("max_kv_len", i32),
-                ("rms_eps", f32), ("rope_theta", f32)]
+                ("rms_eps", f32), ("rope_theta", f32), ("q_lora", i32), ("kv_lora", i32), ("rope_dim", i32),
+                ("n_idx_heads", i32), ("idx_head_dim", i32), ("n_gate", i32), ("rows_per_seq", i32)]
 
 
 class PlanOpts(ctypes.Structure):
@@ -114,6 +125,13 @@ def _check(st):
 
 def model_desc(cfg, max_kv_len):
     """mk_model_desc from a workload dict (synth.config format)."""
+    if cfg.get("arch") == "glm":
+        d = ModelDesc(MK_ABI_VERSION, ctypes.sizeof(ModelDesc), MK_ARCH_GLM_PREATTN, 1, cfg["hidden"],
+                      cfg["n_q_heads"], 0, cfg["head_dim"], 0, 0, 0, 0, MK_FP8_E4M3_B128, int(max_kv_len),
+                      cfg["rms_eps"], cfg["rope_theta"])
+        for k in ("q_lora", "kv_lora", "rope_dim", "n_idx_heads", "idx_head_dim", "n_gate", "rows_per_seq"):
+            setattr(d, k, int(cfg[k]))
+        return d
     return ModelDesc(MK_ABI_VERSION, ctypes.sizeof(ModelDesc),
                      MK_ARCH_QWEN3 if cfg.get("qk_norm") else MK_ARCH_LLAMA, cfg["n_layers"], cfg["hidden"],
                      cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn"], cfg["vocab"],
@@ -145,7 +163,7 @@ class Plan:
             setattr(o, k, int(v))
         h = vp()
         _check(lib().mk_plan_build(ctypes.byref(desc), int(batch), kv.ctypes.data, ctypes.byref(o), ctypes.byref(h)))
-        return cls(h.value, batch, cfg["vocab"])
+        return cls(h.value, batch, cfg.get("vocab"))
 
     @classmethod
     def graph(cls, ops, edges, num_cus):
@@ -183,7 +201,7 @@ class Plan:
                     edge_kept=_arr(v.edge_kept, v.num_edges, np.uint8))
 
     def run(self, weights, kv_cache, tokens, stream=None, layerwise=False):
-        w = weights.struct if isinstance(weights, DeviceWeights) else weights
+        w = weights.struct if isinstance(weights, (DeviceWeights, GlmDeviceWeights)) else weights
         s = vp(stream.cuda_stream if stream is not None else current_stream())
         fn = lib().mk_run_layerwise if layerwise else lib().mk_run
         _check(fn(self._h, ctypes.byref(w), vp(kv_cache.data_ptr()), vp(tokens.data_ptr()), s))
@@ -192,12 +210,14 @@ class Plan:
         self.run(weights, kv_cache, tokens, stream, layerwise=True)
 
     def output(self, which):
-        """Copy an output into a new torch tensor (on the current stream)."""
+        """Copy an output into a new flat torch tensor (on the current stream):
+        float32, int32, int16 (bf16 bit patterns) or uint8 (E4M3 codes)."""
         import torch
         p, n = vp(), sz()
         _check(lib().mk_plan_output(self._h, which, ctypes.byref(p), ctypes.byref(n)))
-        dt = torch.int32 if which == MK_OUT_NEXT_TOKEN else torch.float32
-        out = torch.empty(n.value // 4, dtype=dt, device="cuda")
+        dt, isz = {"f32": (torch.float32, 4), "i32": (torch.int32, 4), "bf16": (torch.int16, 2),
+                   "u8": (torch.uint8, 1)}[OUTPUT_TYPES[which]]
+        out = torch.empty(n.value // isz, dtype=dt, device="cuda")
         _check(lib().mk_plan_copy_output(self._h, which, vp(out.data_ptr()), n.value, vp(current_stream())))
         return out
 
@@ -271,3 +291,34 @@ def kv_to_device(kv_host):
 def tokens_to_device(tokens):
     import torch
     return torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to("cuda")
+
+
+class GlmDeviceWeights:
+    """Upload GLM pre-attention weights (synth.make_glm_inputs format: bf16 norm
+    bits, E4M3 codes, fp32 block scales) and hold the mk_weights table."""
+
+    def __init__(self, host_weights):
+        import torch
+        self.tensors = []
+        self.table = (vp * MK_GLM_SLOTS)()
+        for k, name in enumerate(GLM_SLOTS):
+            a = np.ascontiguousarray(host_weights[name])
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            t = torch.from_numpy(a).to("cuda")
+            self.tensors.append(t)
+            self.table[k] = t.data_ptr()
+        self.struct = Weights(ctypes.cast(self.table, vp), None, None, None)
+
+
+def glm_inputs_to_device(x, r):
+    """bf16 [2][M][hidden] device tensor (x, then r) from uint16 bit arrays."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(np.stack([x, r])).view(np.int16)).to("cuda")
+
+
+def glm_caches_to_device(kv_cache, idx_cache):
+    """One bf16 device buffer: the KV cache followed by the indexer cache."""
+    import torch
+    flat = np.concatenate([np.ascontiguousarray(kv_cache).ravel(), np.ascontiguousarray(idx_cache).ravel()])
+    return torch.from_numpy(flat.view(np.int16)).to("cuda")

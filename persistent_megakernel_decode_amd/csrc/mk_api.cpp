@@ -20,7 +20,7 @@
 namespace mk {
 hipError_t launch_megakernel(const mkd::KArgs& a, int num_cus, hipStream_t s);
 hipError_t launch_layer(const mkd::KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s);
-hipError_t megakernel_occupancy(int hd, int batch, int* blocks_per_cu);
+hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu);
 int ring_pages(int batch);
 }  // namespace mk
 
@@ -74,6 +74,12 @@ struct mk_plan {
   size_t off_qkv = 0, off_part = 0, off_ao = 0, off_hidden = 0, off_act = 0, off_logits = 0, off_lmmax = 0,
          off_next = 0;
   size_t sz_qkv = 0, sz_part = 0, sz_ao = 0, sz_act = 0;
+  // GLM pre-attention path: token rows' (position, request), workspace offsets
+  bool glm = false;
+  int n_seq = 0;
+  int* d_rows = nullptr;
+  size_t off_gn = 0, off_ga8 = 0, off_gas = 0, off_gqkva = 0, off_gqa8 = 0, off_gqs = 0, off_gr = 0, off_gq = 0,
+         off_gqidx = 0, off_ggate = 0;
 };
 
 extern "C" {
@@ -95,6 +101,114 @@ static mk_status finish_plan_common(mk_plan* p) {
   return MK_OK;
 }
 
+static mk_status resolve_cus(const mk_plan_opts* opts, int* num_cus, int* timeout_ms, int* dma_pages) {
+  *num_cus = opts ? opts->num_cus : 0;
+  if (opts && opts->timeout_ms > 0) *timeout_ms = opts->timeout_ms;
+  if (opts && (opts->dma_pages < 0 || opts->dma_pages > 3))
+    return fail(MK_E_INVALID, "dma_pages must be 0 (default), 1, 2 or 3");
+  if (opts && opts->dma_pages > 0) *dma_pages = opts->dma_pages;
+  if (*num_cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return fail(MK_E_INVALID, "num_cus not given and no device to query");
+    *num_cus = n;
+  }
+  return MK_OK;
+}
+
+// The GLM-style pre-attention path: fp8 weights, M <= 16 token rows.
+static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_len, const mk_plan_opts* opts,
+                           mk_plan** out) {
+  if (d.weight_dtype != MK_FP8_E4M3_B128)
+    return fail(MK_E_UNSUPPORTED, "the GLM path needs E4M3 weights with 128 x 128 block scales");
+  if (d.n_layers != 1) return fail(MK_E_INVALID, "the GLM path is one layer's prologue: n_layers must be 1");
+  if (M < 1 || M > mkd::kMB) return fail(MK_E_UNSUPPORTED, "batch (token rows) must be 1..16");
+  const int H = d.hidden, QL = d.q_lora, KL = d.kv_lora, RD = d.rope_dim, hd = d.head_dim, nh = d.n_q_heads;
+  const int nope = hd - RD, Niq = d.n_idx_heads * d.idx_head_dim;
+  if (d.rows_per_seq < 1 || nh < 1 || d.n_idx_heads < 1) return fail(MK_E_INVALID, "GLM sizes must be positive");
+  if (H < 128 || H % 128 || QL < 128 || QL % 128) return fail(MK_E_UNSUPPORTED, "hidden and q_lora must be multiples of 128");
+  if (KL < 8 || KL % 8) return fail(MK_E_UNSUPPORTED, "kv_lora must be a positive multiple of 8");
+  if (nope < 16 || nope % 16 || RD < 16 || RD % 16 || RD > 128)
+    return fail(MK_E_UNSUPPORTED, "head_dim - rope_dim and rope_dim (<= 128) must be positive multiples of 16");
+  if (d.n_gate < 16 || d.n_gate % 16 || d.idx_head_dim < 16 || d.idx_head_dim % 16 || Niq % 16)
+    return fail(MK_E_UNSUPPORTED, "n_gate, idx_head_dim and n_idx_heads * idx_head_dim must be multiples of 16");
+  if ((QL + KL + RD) % 4) return fail(MK_E_UNSUPPORTED, "q_lora + kv_lora + rope_dim must be a multiple of 4");
+  if (16L * H > (long)mk::ring_pages(2) * mkd::kPage || 16L * QL > (long)mk::ring_pages(2) * mkd::kPage)
+    return fail(MK_E_UNSUPPORTED, "a 16-row fp8 tile of hidden or q_lora columns does not fit the LDS ring (128 KiB)");
+  for (int h = 0; h < nh; ++h)
+    if ((h * hd + nope) / 128 != (h * hd + hd - 1) / 128)
+      return fail(MK_E_UNSUPPORTED, "each head's rope rows must lie in one 128-row scale block");
+  if (!(d.rms_eps > 0.f) || !(d.rope_theta > 0.f)) return fail(MK_E_INVALID, "rms_eps and rope_theta must be > 0");
+  const int n_seq = (M + d.rows_per_seq - 1) / d.rows_per_seq;
+  std::vector<int32_t> kl(kv_len, kv_len + M);
+  for (int m = 0; m < M; ++m) {
+    if (kl[m] < 0 || kl[m] >= d.max_kv_len) return fail(MK_E_UNSUPPORTED, "kv_len[m] must be in [0, max_kv_len)");
+    for (int j = 0; j < m; ++j)
+      if (j / d.rows_per_seq == m / d.rows_per_seq && kl[j] == kl[m])
+        return fail(MK_E_INVALID, "two token rows of one request write the same cache position");
+  }
+  auto* p = new mk_plan();
+  p->desc = d;
+  p->batch = M;
+  p->kv_len = kl;
+  p->glm = true;
+  p->n_seq = n_seq;
+  int timeout_ms = 200;
+  int ncu = 0;
+  mk_status st = resolve_cus(opts, &ncu, &timeout_ms, &p->dma_pages);
+  if (st != MK_OK) {
+    delete p;
+    return st;
+  }
+  p->opts.num_cus = ncu;
+  mk::GlmShape g{H, QL, KL, RD, nh, hd, d.n_idx_heads, d.idx_head_dim, d.n_gate};
+  std::vector<mk::GraphEdge> edges;
+  std::string err = mk::glm_graph(g, M, &p->ops, &edges);
+  if (err.empty()) err = mk::plan_graph(p->ops, edges, ncu, &p->kv_len, &p->P);
+  if (!err.empty()) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "planner: " + err);
+  }
+  finish_plan_common(p);
+  p->num_cus = ncu;
+  mkd::Consts& c = p->c;
+  c.glm = 1;
+  c.H = H;
+  c.B = M;
+  c.cap = d.max_kv_len;
+  c.nq = nh;
+  c.hd = 64;  // unused by the GLM kernels
+  c.eps = d.rms_eps;
+  c.ql = QL;
+  c.kl = KL;
+  c.rd = RD;
+  c.nope = nope;
+  c.na = QL + KL + RD;
+  c.ng = d.n_gate;
+  c.nik = d.idx_head_dim;
+  c.niq = Niq;
+  p->timeout_ticks = (unsigned long long)timeout_ms * 100000ull;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o2 = off;
+    off += (bytes + 255) / 256 * 256;
+    return o2;
+  };
+  p->off_gn = take((size_t)M * H * 4);
+  p->off_ga8 = take((size_t)M * H);
+  p->off_gas = take((size_t)M * (H / 128) * 4);
+  p->off_gqkva = take((size_t)M * c.na * 4);
+  p->off_gqa8 = take((size_t)M * QL);
+  p->off_gqs = take((size_t)M * (QL / 128) * 4);
+  p->off_gr = take((size_t)M * H * 2);
+  p->off_gq = take((size_t)M * nh * hd * 2);
+  p->off_gqidx = take((size_t)M * Niq * 2);
+  p->off_ggate = take((size_t)M * d.n_gate * 4);
+  p->ws_bytes = off;
+  *out = p;
+  return MK_OK;
+}
+
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* kv_len, const mk_plan_opts* opts,
                         mk_plan** out) {
   g_err.clear();
@@ -103,6 +217,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   if (desc->abi_version != MK_ABI_VERSION || desc->struct_size != sizeof(mk_model_desc))
     return fail(MK_E_INVALID, "mk_model_desc abi_version/struct_size mismatch");
   const mk_model_desc& d = *desc;
+  if (d.arch == MK_ARCH_GLM_PREATTN) return build_glm(d, batch, kv_len, opts, out);
   if (d.arch != MK_ARCH_LLAMA && d.arch != MK_ARCH_QWEN3) return fail(MK_E_UNSUPPORTED, "unknown arch");
   if (d.weight_dtype != MK_BF16) return fail(MK_E_UNSUPPORTED, "only bf16 weights are supported");
   if (d.n_layers < 1 || d.hidden < 32 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.ffn < 32 || d.vocab < 1)
@@ -323,7 +438,7 @@ static mk_status ensure_device(mk_plan* p) {
   int ncu = 0;
   HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, p->device), "hipDeviceGetAttribute");
   int occ = 0;
-  HIPCHK(mk::megakernel_occupancy(p->c.hd, p->batch, &occ), "occupancy");
+  HIPCHK(mk::megakernel_occupancy(p->c.hd, p->batch, p->c.glm != 0, &occ), "occupancy");
   if (p->num_cus > ncu || occ < 1)
     return fail(MK_E_UNSUPPORTED, "the persistent grid (" + std::to_string(p->num_cus) + " workgroups) cannot be co-resident on " +
                                       std::to_string(ncu) + " CUs");
@@ -332,28 +447,127 @@ static mk_status ensure_device(mk_plan* p) {
   HIPCHK(hipMalloc(&p->d_counters, ebytes), "hipMalloc counters");
   HIPCHK(hipMalloc(&p->d_err, 64), "hipMalloc err");
   HIPCHK(hipMalloc(&p->d_optab, p->ops.size() * 16 * 8), "hipMalloc optab");
-  HIPCHK(hipMalloc(&p->d_rope, (size_t)p->batch * p->c.hd * 4), "hipMalloc rope");
+  const int rope_w = p->glm ? p->c.rd : p->c.hd;  // (cos, sin) pairs per row
+  HIPCHK(hipMalloc(&p->d_rope, (size_t)p->batch * rope_w * 4), "hipMalloc rope");
   HIPCHK(hipMalloc(&p->d_ws, p->ws_bytes), "hipMalloc workspace");
   HIPCHK(hipMemcpy(p->d_queue, p->P.queue.data(), qbytes, hipMemcpyHostToDevice), "upload queue");
   HIPCHK(hipMemset(p->d_counters, 0, ebytes), "zero counters");
   HIPCHK(hipMemset(p->d_err, 0, 64), "zero err");
   HIPCHK(hipMemset(p->d_ws, 0xFF, p->ws_bytes), "poison workspace");  // NaN until written
-  // RoPE table (cos, sin) at each sequence's new position, computed in fp64
-  std::vector<float> rope((size_t)p->batch * p->c.hd);
-  const int half = p->c.hd / 2;
+  // RoPE table (cos, sin) at each sequence's (GLM: token row's) new position,
+  // computed in fp64; rotate-half over rope_w dims
+  std::vector<float> rope((size_t)p->batch * rope_w);
+  const int half = rope_w / 2;
   for (int b = 0; b < p->batch; ++b)
     for (int i = 0; i < half; ++i) {
-      double ang = (double)p->kv_len[b] * std::pow((double)p->desc.rope_theta, -2.0 * i / p->c.hd);
-      rope[(size_t)b * p->c.hd + 2 * i] = (float)std::cos(ang);
-      rope[(size_t)b * p->c.hd + 2 * i + 1] = (float)std::sin(ang);
+      double ang = (double)p->kv_len[b] * std::pow((double)p->desc.rope_theta, -2.0 * i / rope_w);
+      rope[(size_t)b * rope_w + 2 * i] = (float)std::cos(ang);
+      rope[(size_t)b * rope_w + 2 * i + 1] = (float)std::sin(ang);
     }
   HIPCHK(hipMemcpy(p->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice), "upload rope");
+  if (p->glm) {
+    // token rows: cache position, then request
+    std::vector<int32_t> rows(2 * (size_t)p->batch);
+    for (int m = 0; m < p->batch; ++m) {
+      rows[m] = p->kv_len[m];
+      rows[p->batch + m] = m / p->desc.rows_per_seq;
+    }
+    HIPCHK(hipMalloc(&p->d_rows, rows.size() * 4), "hipMalloc rows");
+    HIPCHK(hipMemcpy(p->d_rows, rows.data(), rows.size() * 4, hipMemcpyHostToDevice), "upload rows");
+  }
   p->uploaded = true;
   p->epoch = 0;
   return MK_OK;
 }
 
+static mk_status upload_optab(mk_plan* p, const std::vector<uint64_t>& t, hipStream_t s) {
+  if (t != p->h_optab) {
+    p->h_optab = t;
+    HIPCHK(hipMemcpyAsync(p->d_optab, p->h_optab.data(), t.size() * 8, hipMemcpyHostToDevice, s), "upload operand table");
+    HIPCHK(hipStreamSynchronize(s), "operand table sync");
+  }
+  return MK_OK;
+}
+
+static mk_status bind_glm(mk_plan* p, const mk_weights* w, void* kv, const void* xr, hipStream_t s) {
+  const mk_model_desc& d = p->desc;
+  if (!w || !w->layer_ptrs || !kv || !xr) return fail(MK_E_INVALID, "null weight, cache or input pointer");
+  for (int k = 0; k < MK_GLM_SLOTS; ++k)
+    if (!w->layer_ptrs[k]) return fail(MK_E_INVALID, "null GLM weight pointer");
+  const void* const* W = w->layer_ptrs;
+  auto u = [](const void* q) { return (uint64_t)(uintptr_t)q; };
+  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(p->d_ws + off); };
+  const size_t M = p->batch, H = d.hidden;
+  const uint64_t x = u(xr), r = u((const char*)xr + M * H * 2);
+  const uint64_t kvc = u(kv), idc = u((const char*)kv + (size_t)p->n_seq * d.max_kv_len * (d.kv_lora + d.rope_dim) * 2);
+  std::vector<uint64_t> t(p->ops.size() * 16, 0);
+  for (size_t o = 0; o < p->ops.size(); ++o) {
+    uint64_t* q = &t[o * 16];
+    switch (p->ops[o].opcode) {
+      case mk::kGA0:
+        q[mkd::GaX] = x;
+        q[mkd::GaR] = r;
+        q[mkd::GaNorm] = u(W[0]);
+        q[mkd::GaROut] = ws(p->off_gr);
+        q[mkd::GaN] = ws(p->off_gn);
+        q[mkd::GaA8] = ws(p->off_ga8);
+        q[mkd::GaAS] = ws(p->off_gas);
+        break;
+      case mk::kGQkva:
+        q[mkd::GmW] = u(W[1]);
+        q[mkd::GmS] = u(W[2]);
+        q[mkd::GmA8] = ws(p->off_ga8);
+        q[mkd::GmAS] = ws(p->off_gas);
+        q[mkd::GmOut] = ws(p->off_gqkva);
+        break;
+      case mk::kGGate:
+        q[mkd::GmW] = u(W[3]);
+        q[mkd::GmS] = u(W[4]);
+        q[mkd::GmAF] = ws(p->off_gn);
+        q[mkd::GmOut] = ws(p->off_ggate);
+        break;
+      case mk::kGIdxk:
+        q[mkd::GmW] = u(W[5]);
+        q[mkd::GmS] = u(W[6]);
+        q[mkd::GmA8] = ws(p->off_ga8);
+        q[mkd::GmAS] = ws(p->off_gas);
+        q[mkd::GmOut] = idc;
+        q[mkd::GmRows] = u(p->d_rows);
+        break;
+      case mk::kGQaNorm:
+        q[mkd::QnIn] = ws(p->off_gqkva);
+        q[mkd::QnNorm] = u(W[7]);
+        q[mkd::QnKvNorm] = u(W[8]);
+        q[mkd::QnA8] = ws(p->off_gqa8);
+        q[mkd::QnAS] = ws(p->off_gqs);
+        q[mkd::QnKv] = kvc;
+        q[mkd::QnRope] = u(p->d_rope);
+        q[mkd::QnRows] = u(p->d_rows);
+        break;
+      case mk::kGQkvb:
+        q[mkd::GmW] = u(W[9]);
+        q[mkd::GmS] = u(W[10]);
+        q[mkd::GmA8] = ws(p->off_gqa8);
+        q[mkd::GmAS] = ws(p->off_gqs);
+        q[mkd::GmOut] = ws(p->off_gq);
+        q[mkd::GmRope] = u(p->d_rope);
+        break;
+      case mk::kGIdxq:
+        q[mkd::GmW] = u(W[11]);
+        q[mkd::GmS] = u(W[12]);
+        q[mkd::GmA8] = ws(p->off_gqa8);
+        q[mkd::GmAS] = ws(p->off_gqs);
+        q[mkd::GmOut] = ws(p->off_gqidx);
+        break;
+      default:
+        break;
+    }
+  }
+  return upload_optab(p, t, s);
+}
+
 static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const void* tokens, hipStream_t s) {
+  if (p->glm) return bind_glm(p, w, kv, tokens, s);
   const mk_model_desc& d = p->desc;
   const int L = d.n_layers;
   if (!w || !w->layer_ptrs || !w->embed || !w->final_norm || !kv || !tokens)
@@ -438,12 +652,7 @@ static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const 
     }
   }
   (void)hpg;
-  if (t != p->h_optab) {
-    p->h_optab = t;
-    HIPCHK(hipMemcpyAsync(p->d_optab, p->h_optab.data(), t.size() * 8, hipMemcpyHostToDevice, s), "upload operand table");
-    HIPCHK(hipStreamSynchronize(s), "operand table sync");
-  }
-  return MK_OK;
+  return upload_optab(p, t, s);
 }
 
 static mkd::KArgs kargs(const mk_plan* p) {
@@ -504,6 +713,28 @@ mk_status mk_plan_output(const mk_plan* p, int32_t which, void** dev_ptr, size_t
   if (!p || !dev_ptr || !bytes) return fail(MK_E_INVALID, "null argument");
   if (p->graph_only || !p->uploaded) return fail(MK_E_STATE, "the plan has not run");
   const size_t B = p->batch;
+  if (p->glm) {
+    const mk_model_desc& d = p->desc;
+    const size_t H = d.hidden;
+    size_t off = 0, n = 0;
+    switch (which) {
+      case MK_OUT_GLM_R: off = p->off_gr; n = B * H * 2; break;
+      case MK_OUT_GLM_Q: off = p->off_gq; n = B * d.n_q_heads * d.head_dim * 2; break;
+      case MK_OUT_GLM_QIDX: off = p->off_gqidx; n = B * d.n_idx_heads * d.idx_head_dim * 2; break;
+      case MK_OUT_GLM_GATE: off = p->off_ggate; n = B * d.n_gate * 4; break;
+      case MK_OUT_GLM_NORM: off = p->off_gn; n = B * H * 4; break;
+      case MK_OUT_GLM_ACT: off = p->off_ga8; n = B * H; break;
+      case MK_OUT_GLM_ACT_SCALE: off = p->off_gas; n = B * (H / 128) * 4; break;
+      case MK_OUT_GLM_QKVA: off = p->off_gqkva; n = B * (size_t)p->c.na * 4; break;
+      case MK_OUT_GLM_QA: off = p->off_gqa8; n = B * d.q_lora; break;
+      case MK_OUT_GLM_QA_SCALE: off = p->off_gqs; n = B * (d.q_lora / 128) * 4; break;
+      default:
+        return fail(MK_E_INVALID, "unknown output for the GLM path");
+    }
+    *dev_ptr = p->d_ws + off;
+    *bytes = n;
+    return MK_OK;
+  }
   switch (which) {
     case MK_OUT_LOGITS:
       *dev_ptr = p->d_ws + p->off_logits;
@@ -603,6 +834,7 @@ void mk_plan_free(mk_plan* p) {
     (void)hipFree(p->d_optab);
     (void)hipFree(p->d_rope);
     (void)hipFree(p->d_ws);
+    if (p->d_rows) (void)hipFree(p->d_rows);
   }
   if (p->d_trace) (void)hipFree(p->d_trace);
   delete p;

@@ -29,6 +29,10 @@ enum : int {
   WSigInc = 8, WTask = 9, WLayer = 10, WGx = 11, WGy = 12, WGz = 13, WPay = 14
 };
 enum : int { OpNoop = 0, OpQkv = 1, OpAttn = 2, OpCombine = 3, OpOproj = 4, OpGateUp = 5, OpDown = 6, OpLmHead = 7, OpArgmax = 8 };
+// GLM-style pre-attention path: add + RMSNorm + fp8 quant (one token row per
+// task), fp8 GEMM tiles of 16 weight rows (QKV-A, head gate, indexer-K, QKV-B,
+// indexer-Q) and the q path's RMSNorm + requant with the KV-row write.
+enum : int { OpGA0 = 9, OpGQkva = 10, OpGGate = 11, OpGIdxk = 12, OpGQaNorm = 13, OpGQkvb = 14, OpGIdxq = 15 };
 
 // ---- operand table slots (one row of 16 u64 per op) --------------------------
 enum : int {
@@ -47,7 +51,14 @@ enum : int {
   // LMHEAD
   LmW = 0, LmNorm = 1, LmIn = 2, LmLogits = 3, LmMax = 4,
   // ARGMAX
-  AmMax = 0, AmOut = 1
+  AmMax = 0, AmOut = 1,
+  // GLM A0: inputs x, r (bf16), norm weight, outputs r_out (bf16), norm (fp32), codes, scales
+  GaX = 0, GaR = 1, GaNorm = 2, GaROut = 3, GaN = 4, GaA8 = 5, GaAS = 6,
+  // GLM fp8 GEMMs: weight codes and block scales, activation codes and scales
+  // (or the fp32 norm output for the gate), output, RoPE table, token rows info
+  GmW = 0, GmS = 1, GmA8 = 2, GmAS = 3, GmAF = 4, GmOut = 5, GmRope = 6, GmRows = 7,
+  // GLM q-path norm: QKV-A output, q / kv norm weights, q codes and scales, KV cache, RoPE, rows
+  QnIn = 0, QnNorm = 1, QnKvNorm = 2, QnA8 = 3, QnAS = 4, QnKv = 5, QnRope = 6, QnRows = 7
 };
 
 constexpr int kPage = 16384;  // bytes per LDS page
@@ -71,6 +82,9 @@ __host__ __device__ inline size_t ctr_word(int e, int k, int num_events) {
 struct Consts {
   int H, nq, nkv, hd, F, V, L, B, cap, hpg, RPG, S, T_v, qk_norm;
   float eps, inv_sqrt_hd;
+  // GLM path (glm != 0): q_lora, kv_lora, rope dims, nope dims per head, QKV-A
+  // outputs, gate outputs, indexer head dim, indexer-Q outputs
+  int glm, ql, kl, rd, nope, na, ng, nik, niq;
 };
 
 struct KArgs {
@@ -248,6 +262,23 @@ __device__ inline Tile tile_info(const M& m, const Consts& c) {
       t.p0 = (const GLB char*)m.q(LmW) + (size_t)m.w(WPay) * c.H * 2;
       t.len0 = m.w(WPay + 1) * c.H * 2;
       break;
+    case OpGQkva:
+    case OpGGate:
+    case OpGIdxk:
+    case OpGQkvb:
+    case OpGIdxq: {
+      // fp8 weight rows [row0, row0 + nrows) and, for a RoPE-pair tile, the
+      // same number of rows from row1 as the second segment
+      const int K = (op == OpGQkvb || op == OpGIdxq) ? c.ql : c.H;
+      const int row0 = m.w(WPay), nrows = m.w(WPay + 1), row1 = m.w(WPay + 2);
+      t.p0 = (const GLB char*)m.q(GmW) + (size_t)row0 * K;
+      t.len0 = nrows * K;
+      if (row1 >= 0) {
+        t.p1 = (const GLB char*)m.q(GmW) + (size_t)row1 * K;
+        t.len1 = nrows * K;
+      }
+      break;
+    }
     case OpAttn: {
       const int b = m.w(WGx), g = m.w(WGy), lo = m.w(WPay), hi = m.w(WPay + 1), pos = m.w(WPay + 2);
       int nk = (hi < pos ? hi : pos) - lo;

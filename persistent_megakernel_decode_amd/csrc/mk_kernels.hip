@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include "mk_device.hpp"
+#include "mk_glm.hpp"
 
 using namespace mkd;
 
@@ -48,9 +49,10 @@ struct CtrlT {
 constexpr int kMeta = 8;
 // Workgroup LDS.  MB: batched sequences (MFMA tiles) -- one page less in the
 // ring for the 16 x 16 partial blocks.
-template <bool MB_>
+template <bool MB_, bool GLM_ = false>
 struct __attribute__((aligned(16))) LdsT {
   static constexpr bool MB = MB_;
+  static constexpr bool GLM = GLM_;  // the GLM pre-attention interpreter (batched layout)
   static constexpr int NP = MB_ ? kNumPages - 1 : kNumPages;  // ring pages
   static constexpr int PW = MB_ ? kMB * kMB : kMaxRows;
   static constexpr int SW = MB_ ? kMB : 1;
@@ -235,7 +237,10 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
     if (op == OpNoop) break;
     const int sl = i & 3;
     const bool gemv = is_gemv(op);
-    if constexpr (LT::MB) {
+    if constexpr (LT::GLM) {
+      if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
+      if (glm_is_gemm(op)) glm_epilogue(m, a.c, &L->c.part[sl][0][0]);
+    } else if constexpr (LT::MB) {
       const f32x4 res = gemv_residual_mb(m, a.c);
       if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
       if (gemv)
@@ -443,8 +448,20 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
     src.off1 = (uint32_t)t.off1;
     src.wrap = (uint32_t)(LT::NP * kPage);
     const int sl = i & 3;
-    const bool gemv = is_gemv(op);
-    if (gemv && !LT::MB) {
+    const bool gemv = LT::GLM ? glm_is_gemm(op) : is_gemv(op);
+    if constexpr (LT::GLM) {
+      // weights (if any) are in the ring; activations follow the event
+      if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
+      if (cw == 0 && tr && lane == 0) tr[1] = now_ticks();
+      if (gemv) {
+        glm_gemm_wave(src, m, a.c, cw, &L->c.part[sl][cw][0]);
+      } else if (op == OpGA0) {
+        glm_a0_wave(m, a.c, cw);
+      } else if (op == OpGQaNorm) {
+        glm_qan_wave(m, a.c, cw);
+      }
+      release();
+    } else if (gemv && !LT::MB) {
       const GemvIn gi = gemv_input(m, a.c);
       bool live = true;
       auto pre = [&]() {
@@ -484,9 +501,9 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
   }
 }
 
-template <int HD, bool MB>
+template <int HD, bool MB, bool GLM = false>
 __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
-  typedef LdsT<MB> LT;
+  typedef LdsT<MB, GLM> LT;
   __shared__ LT Ls;
   LDS LT* L = (LDS LT*)&Ls;
   {
@@ -514,7 +531,7 @@ __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
 
 // ---------------------------------------------------------------------------
 // Layerwise: one launch per operator, one workgroup (4 waves) per tile.
-template <int HD, bool MB>
+template <int HD, bool MB, bool GLM = false>
 __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int first_task) {
   constexpr int PW = MB ? kMB * kMB : kMaxRows, SW = MB ? kMB : 1;
   __shared__ float part_s[kNW][PW];
@@ -539,6 +556,18 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   src.p0 = tl.p0;
   src.p1 = tl.p1 ? tl.p1 : tl.p0;
   const int op = m.w(WOpcode);
+  if constexpr (GLM) {
+    if (glm_is_gemm(op)) {
+      glm_gemm_wave(src, m, a.c, cw, part[cw]);
+      __syncthreads();
+      if (cw == 0) glm_epilogue(m, a.c, &part[0][0]);
+    } else if (op == OpGA0) {
+      glm_a0_wave(m, a.c, cw);
+    } else if (op == OpGQaNorm) {
+      glm_qan_wave(m, a.c, cw);
+    }
+    return;
+  }
   if (is_gemv(op)) {
     const GemvIn gi = gemv_input(m, a.c);
     if constexpr (MB) {
@@ -575,7 +604,9 @@ const void* megakernel_fn(int hd) {
 namespace mk {
 
 hipError_t launch_megakernel(const KArgs& a, int num_cus, hipStream_t s) {
-  if (a.c.B == 1) {
+  if (a.c.glm) {
+    hipLaunchKernelGGL((mk_megakernel<64, true, true>), dim3(num_cus), dim3(512), 0, s, a);
+  } else if (a.c.B == 1) {
     if (a.c.hd == 64)
       hipLaunchKernelGGL((mk_megakernel<64, false>), dim3(num_cus), dim3(512), 0, s, a);
     else
@@ -590,7 +621,9 @@ hipError_t launch_megakernel(const KArgs& a, int num_cus, hipStream_t s) {
 }
 
 hipError_t launch_layer(const KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s) {
-  if (a.c.B == 1) {
+  if (a.c.glm) {
+    hipLaunchKernelGGL((mk_layer_kernel<64, true, true>), dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
+  } else if (a.c.B == 1) {
     if (a.c.hd == 64)
       hipLaunchKernelGGL((mk_layer_kernel<64, false>), dim3(ntasks), dim3(256), 0, s, a, num_cus, first_task);
     else
@@ -604,9 +637,10 @@ hipError_t launch_layer(const KArgs& a, int num_cus, int first_task, int ntasks,
   return hipGetLastError();
 }
 
-hipError_t megakernel_occupancy(int hd, int batch, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      blocks_per_cu, batch == 1 ? megakernel_fn<false>(hd) : megakernel_fn<true>(hd), 512, 0);
+hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu) {
+  const void* f = glm ? (const void*)mk_megakernel<64, true, true>
+                      : (batch == 1 ? megakernel_fn<false>(hd) : megakernel_fn<true>(hd));
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, 512, 0);
 }
 
 int ring_pages(int batch) { return batch == 1 ? LdsT<false>::NP : LdsT<true>::NP; }

@@ -56,6 +56,32 @@ void payload(const GraphOp& op, int x, int y, int z, const std::vector<int32_t>*
     case kArgmax:  // p0 = LM-head tiles
       w[0] = p[0];
       break;
+    case kGA0:
+    case kGQaNorm:  // one token row per task
+      w[0] = x;
+      break;
+    case kGQkva:
+    case kGGate:
+    case kGIdxk:
+    case kGIdxq:  // p0 = output rows
+      w[0] = x * kGlmRows;
+      w[1] = std::min(kGlmRows, p[0] - x * kGlmRows);
+      w[2] = -1;
+      break;
+    case kGQkvb: {  // p0 = head_dim, p1 = nope dims, p2 = rope dims; x head, y tile
+      const int base = x * p[0];
+      if (y < p[1] / kGlmRows) {
+        w[0] = base + y * kGlmRows;
+        w[1] = kGlmRows;
+        w[2] = -1;
+      } else {
+        const int j = y - p[1] / kGlmRows, h = kGlmRows / 2;
+        w[0] = base + p[1] + j * h;
+        w[1] = h;
+        w[2] = base + p[1] + p[2] / 2 + j * h;
+      }
+      break;
+    }
     default:
       break;
   }
@@ -470,6 +496,58 @@ std::string model_graph(const ModelShape& m, int batch, const std::vector<int32_
   int am = add(kArgmax, {{B, 1, 1}}, L, 0, {{T_v}});
   edge(prev_down, lm, {{1, -1, -1}}, none, {{B, H, 1, 1}}, {{1, DR, 1, 1}}, {{1, H, 1, 1}});
   edge(lm, am, {{1, -1, -1}}, {{0, -1, -1}}, {{B, T_v, 1, 1}}, {{B, 1, 1, 1}}, {{1, T_v, 1, 1}});
+  return "";
+}
+
+}  // namespace mk
+
+namespace mk {
+
+// GLM-style pre-attention path (MegaRTP article, section 4): A0 and the q-path
+// norm work one token row per task; the fp8 GEMMs are cut into 16-row output
+// tiles; QKV-B's rope dims come in tiles that pair 8 rows of the first half with
+// the 8 rows half the rope width further on.
+std::string glm_graph(const GlmShape& g, int M, std::vector<GraphOp>* ops_out, std::vector<GraphEdge>* edges_out) {
+  const int R = kGlmRows, nope = g.head_dim - g.rope_dim;
+  const int Na = g.q_lora + g.kv_lora + g.rope_dim, Niq = g.n_idx_heads * g.idx_head_dim;
+  if (nope <= 0 || nope % R || g.rope_dim % R) return "nope and rope dims must be positive multiples of 16";
+  auto& ops = *ops_out;
+  auto& edges = *edges_out;
+  ops.clear();
+  edges.clear();
+  auto add = [&](int opcode, std::array<int, 3> grid, std::array<int, 8> p) {
+    GraphOp op;
+    op.opcode = opcode;
+    op.kind = opcode;
+    op.grid = grid;
+    op.p = p;
+    ops.push_back(op);
+    return (int)ops.size() - 1;
+  };
+  auto edge = [&](int p, int c, std::array<int, 3> om, std::array<int, 3> im, std::array<int, 4> ext,
+                  std::array<int, 4> pt, std::array<int, 4> ct) {
+    GraphEdge e;
+    e.prod = p;
+    e.cons = c;
+    e.out_map = om;
+    e.in_map = im;
+    e.has_extent = true;
+    e.extent = ext;
+    e.ptile = pt;
+    e.ctile = ct;
+    edges.push_back(e);
+  };
+  const std::array<int, 3> none{{-1, -1, -1}}, d0{{0, -1, -1}}, d1{{1, -1, -1}};
+  const int a0 = add(kGA0, {{M, 1, 1}}, {{}});
+  const int qa = add(kGQkva, {{ceil_div(Na, R), 1, 1}}, {{Na}});
+  const int ga = add(kGGate, {{ceil_div(g.n_gate, R), 1, 1}}, {{g.n_gate}});
+  const int ik = add(kGIdxk, {{ceil_div(g.idx_head_dim, R), 1, 1}}, {{g.idx_head_dim}});
+  const int qn = add(kGQaNorm, {{M, 1, 1}}, {{}});
+  const int qb = add(kGQkvb, {{g.n_heads, (nope + g.rope_dim) / R, 1}}, {{g.head_dim, nope, g.rope_dim}});
+  const int iq = add(kGIdxq, {{ceil_div(Niq, R), 1, 1}}, {{Niq}});
+  for (int c : {qa, ga, ik}) edge(a0, c, d0, none, {{M, g.hidden, 1, 1}}, {{1, g.hidden, 1, 1}}, {{M, g.hidden, 1, 1}});
+  edge(qa, qn, d1, d0, {{M, Na, 1, 1}}, {{M, R, 1, 1}}, {{1, Na, 1, 1}});
+  for (int c : {qb, iq}) edge(qn, c, d0, none, {{M, g.q_lora, 1, 1}}, {{1, g.q_lora, 1, 1}}, {{M, g.q_lora, 1, 1}});
   return "";
 }
 

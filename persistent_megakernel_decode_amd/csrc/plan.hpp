@@ -28,6 +28,9 @@ enum : int {
 
 // opcodes of the Llama-family decode step
 enum : int { kNoop = 0, kQkv = 1, kAttn = 2, kCombine = 3, kOproj = 4, kGateUp = 5, kDown = 6, kLmHead = 7, kArgmax = 8 };
+// opcodes of the GLM-style pre-attention path
+enum : int { kGA0 = 9, kGQkva = 10, kGGate = 11, kGIdxk = 12, kGQaNorm = 13, kGQkvb = 14, kGIdxq = 15 };
+constexpr int kGlmRows = 16;  // weight rows per fp8 GEMM tile
 
 struct GraphOp {
   int opcode = 0, spec = 0, layer = 0;
@@ -73,6 +76,12 @@ void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, Model
 // Operator DAG of one Llama-family decode step, in topological order.
 std::string model_graph(const ModelShape& m, int batch, const std::vector<int32_t>& kv_len, const ModelOpts& o,
                         std::vector<GraphOp>* ops, std::vector<GraphEdge>* edges);
+
+struct GlmShape {
+  int hidden, q_lora, kv_lora, rope_dim, n_heads, head_dim, n_idx_heads, idx_head_dim, n_gate;
+};
+// Operator DAG of the GLM-style pre-attention path for M token rows.
+std::string glm_graph(const GlmShape& g, int M, std::vector<GraphOp>* ops, std::vector<GraphEdge>* edges);
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 

@@ -66,6 +66,37 @@ def test_cpp_planner_matches_reference(name, overrides, num_cus, opts):
         plan.free()
 
 
+@pytest.mark.parametrize("name,num_cus", [("glm_preattn", 256), ("glm_preattn", 148), ("glm_tiny", 37),
+                                           ("glm_tiny", 7)])
+def test_cpp_planner_matches_reference_glm(name, num_cus):
+    cfg = synth.config(name)
+    pos, _ = synth.glm_positions(cfg)
+    ref = P.plan_model(cfg, len(pos), pos, dict(num_cus=num_cus))
+    plan = mk.Plan.build(cfg, len(pos), pos, synth.glm_capacity(cfg), num_cus=num_cus)
+    try:
+        _compare(plan, ref)
+    finally:
+        plan.free()
+
+
+def test_glm_plan_structure():
+    """A0 (16 rows) forks to QKV-A / gate / indexer-K through one event of 16
+    triggers; QKV-A's 132 tiles join into the q-path norm (one event, 132
+    triggers); the norm forks to QKV-B (64 heads x 12 tiles) and indexer-Q (256
+    tiles) through one event of 16 triggers: 1200 tasks in all."""
+    cfg = synth.config("glm_preattn")
+    pos, _ = synth.glm_positions(cfg)
+    ref = P.plan_model(cfg, len(pos), pos, dict(num_cus=256))
+    assert ref.num_tasks == 16 + 132 + 4 + 8 + 16 + 64 * 12 + 256 == 1200
+    assert list(ref.event_target) == [16, 132, 16] and ref.max_len == 5
+    # QKV-B payloads: plain tiles of 16 rows, then RoPE-pair tiles (8 rows + 8 rows 32 further on)
+    q = np.asarray(ref.queue).reshape(-1, 32)
+    qb = q[q[:, 0] == P.G_QKVB]
+    pays = sorted(tuple(r[14:17]) for r in qb if r[11] == 1)
+    assert pays[:8] == [(192 + 16 * y, 16, -1) for y in range(8)]
+    assert pays[8:] == [(192 + 128 + 8 * j, 8, 192 + 160 + 8 * j) for j in range(4)]
+
+
 def _graph_via_lib(ops, edges, num_cus):
     lops = [(op.opcode, op.grid, op.spec, op.layer) for op in ops]
     ledges = [(e.prod, e.cons, e.out_map, e.in_map, e.extent, e.ptile, e.ctile) for e in edges]
@@ -116,6 +147,24 @@ def test_plan_build_rejects_bad_arguments():
     assert mk.lib().mk_plan_build(ctypes.byref(d), 1, kv.ctypes.data, None, ctypes.byref(h)) == mk.MK_E_INVALID
     assert mk.lib().mk_plan_build(None, 1, kv.ctypes.data, None, ctypes.byref(h)) == mk.MK_E_INVALID
     assert b"null" in mk.lib().mk_last_error()
+    # GLM: bf16 weights, two rows of one request at one position, positions past the cache
+    g = synth.config("glm_tiny")
+    pos, _ = synth.glm_positions(g)
+    cap = synth.glm_capacity(g)
+    gd = mk.model_desc(g, cap)
+    gd.weight_dtype = mk.MK_BF16
+    assert mk.lib().mk_plan_build(ctypes.byref(gd), len(pos), pos.ctypes.data, None, ctypes.byref(h)) == mk.MK_E_UNSUPPORTED
+    dup = pos.copy()
+    dup[1] = dup[0]
+    with pytest.raises(mk.MKError) as e:
+        mk.Plan.build(g, len(pos), dup, cap, num_cus=8)
+    assert e.value.status == mk.MK_E_INVALID
+    with pytest.raises(mk.MKError) as e:
+        mk.Plan.build(g, len(pos), pos + cap, cap, num_cus=8)
+    assert e.value.status == mk.MK_E_UNSUPPORTED
+    with pytest.raises(mk.MKError) as e:
+        mk.Plan.build(dict(g, rope_dim=40), len(pos), pos, cap, num_cus=8)
+    assert e.value.status == mk.MK_E_UNSUPPORTED
     # a graph-only plan cannot run
     g = mk.Plan.graph([(1, (4,))], [], 4)
     w = mk.Weights()
