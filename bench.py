@@ -1,6 +1,7 @@
 """Benchmark of one decode step: persistent megakernel vs the layerwise baseline.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama1b]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama1b | llama1b_b16 | qwen3_8b |
+                                                           glm_preattn]
 
 Prints ONE JSON line.  ``value`` is the megakernel's decode-step latency (us,
 median over the timed steps, lower is better) on the Llama-3.2-1B-shaped
@@ -29,7 +30,8 @@ PEAK_GBPS = 8000.0
 SHAPES = {"tiny": "tiny Llama-style", "llama1b": "Llama-3.2-1B-shaped", "llama1b_b16": "Llama-3.2-1B-shaped",
           "qwen3_8b": "Qwen3-8B-shaped"}
 KERNEL_SOURCES = ["persistent_megakernel_decode_amd/csrc/mk_kernels.hip",
-                  "persistent_megakernel_decode_amd/csrc/mk_device.hpp"]
+                  "persistent_megakernel_decode_amd/csrc/mk_device.hpp",
+                  "persistent_megakernel_decode_amd/csrc/mk_glm.hpp"]
 
 
 def algorithmic_bytes(cfg, kv_len):
@@ -48,6 +50,18 @@ def algorithmic_bytes(cfg, kv_len):
     kv_write = 2 * L * nkv * hd * 2 * B
     logits = 4 * B * V
     return weights + emb + kv_read + kv_write + logits
+
+
+def glm_algorithmic_bytes(cfg, w):
+    """Bytes one GLM pre-attention step must move: every fp8 weight and its fp32
+    block scales once, the bf16 norm weights, x and r in, and out: r_out, q,
+    indexer q (bf16), the gate (fp32), the KV and indexer cache rows (bf16)."""
+    import synth
+    M, Na, Nqb, Niq = synth.glm_dims(cfg)
+    weights = sum(int(a.nbytes) for a in w.values())
+    io = 2 * M * cfg["hidden"] * 2 + M * cfg["hidden"] * 2
+    out = M * (Nqb + Niq) * 2 + M * cfg["n_gate"] * 4 + M * (cfg["kv_lora"] + cfg["rope_dim"] + cfg["idx_head_dim"]) * 2
+    return weights + io + out
 
 
 def sources_hash():
@@ -108,6 +122,87 @@ def cpu_baseline(inp, budget_s=20.0):
                 sample="%d whole decode step(s) of the same workload (fp64 C oracle, OpenMP over output rows)" % n)
 
 
+def bench_glm(args):
+    """The GLM-style pre-attention step (fp8 weights, 16 token rows).  Its 40 MB
+    of weights fit the 256 MiB MALL, so it is timed warm (one weight copy, as a
+    loop over one layer would see it) and cold (eight weight copies in turn, one
+    plan each, 315 MB per round: every step's weights come from HBM)."""
+    import torch
+    import synth
+    import persistent_megakernel_decode_amd as mk
+    torch.cuda.set_device(0)
+    name = args.workload
+    inp = synth.make_glm_inputs(name)
+    cfg = inp["cfg"]
+    M = len(inp["pos"])
+    cap = synth.glm_capacity(cfg)
+    xr = mk.glm_inputs_to_device(inp["x"], inp["r"])
+    caches = mk.glm_caches_to_device(inp["kv_cache"], inp["idx_cache"])
+    ncopy = 8
+    ws = [mk.GlmDeviceWeights(inp["weights"]) for _ in range(ncopy)]
+    plans = [mk.Plan.build(cfg, M, inp["pos"], cap) for _ in range(ncopy)]
+    stream = torch.cuda.current_stream()
+    nbytes = glm_algorithmic_bytes(cfg, inp["weights"])
+    res = {}
+    for key, lw in (("mk", False), ("lw", True)):
+        if args.only == "megakernel" and lw or args.only == "layerwise" and not lw:
+            continue
+        print("[bench] timing %s (warm, cold)" % ("layerwise" if lw else "megakernel"), file=sys.stderr, flush=True)
+        res[key + "_warm"] = time_launches(lambda: plans[0].run(ws[0], caches, xr, layerwise=lw), stream,
+                                           args.steps, args.warmup)
+        it = [0]
+
+        def cold():
+            k = it[0] % ncopy
+            it[0] += 1
+            plans[k].run(ws[k], caches, xr, layerwise=lw)
+        for p_, w_ in zip(plans, ws):  # bind every plan once (operand-table upload) before timing
+            p_.run(w_, caches, xr, layerwise=lw)
+        res[key + "_cold"] = time_launches(cold, stream, args.steps, args.warmup)
+        if not lw:
+            st, chk = plans[0].check()
+            if st != mk.MK_OK or not chk.counters_ok:
+                raise RuntimeError("megakernel check failed: %s" % mk.lib().mk_last_error().decode())
+    main_key = "mk_cold" if "mk_cold" in res else "lw_cold"
+    lat = res[main_key]["median"]
+    achieved = nbytes / (res[main_key]["mean"] * 1e-6) / 1e9
+    out = {
+        "metric": "GLM pre-attention step latency (µs), cold weights, + achieved HBM GB/s vs peak",
+        "value": round(lat, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res[main_key]["outer_us_per_step"] / 1e3, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 weights (fp32 128x128 block scales), fp8 activations, fp32 accumulate",
+        "data": "synthetic (seeded, random-init weights of the workload's shape)",
+        "config": {"workload": "%s: GLM-style pre-attention, M=%d (%d requests x %d tokens), hidden %d, fp8 weights, "
+                               "KV position %d" % (name, M, cfg["n_seqs"], cfg["rows_per_seq"], cfg["hidden"],
+                                                   cfg["pos0"]),
+                   "weight_copies_cold": ncopy,
+                   "persistent_grid": "%d workgroups x 512 threads" % plans[0].export()["num_cus"]},
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None},
+    }
+    for k, v in res.items():
+        out[k + "_us"] = {a: round(b, 2) for a, b in v.items()}
+    if "mk_cold" in res and "lw_cold" in res:
+        out["speedup_vs_layerwise_cold"] = round(res["lw_cold"]["median"] / res["mk_cold"]["median"], 3)
+        out["speedup_vs_layerwise_warm"] = round(res["lw_warm"]["median"] / res["mk_warm"]["median"], 3)
+    if not args.no_cpu_baseline:
+        from oracle import glm as G
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        n = 0
+        while n < 3 and (n == 0 or time.perf_counter() - t0 < 10.0):
+            G.glm_step(inp)
+            n += 1
+        out["cpu_baseline"] = dict(value=(time.perf_counter() - t0) / n * 1e6, unit="us",
+                                   cores=int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), kind="oracle",
+                                   sample="%d whole step(s) of the same workload (fp64 numpy oracle)" % n)
+    for p_ in plans:
+        p_.free()
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +219,8 @@ def main():
         print("bench.py runs on exactly one GPU: the decode megakernel is a single-GPU design here "
               "(no collectives); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("glm"):
+        return bench_glm(args)
     import torch
     import synth
     import persistent_megakernel_decode_amd as mk
