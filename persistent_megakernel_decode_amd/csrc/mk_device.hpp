@@ -172,6 +172,49 @@ __device__ __forceinline__ void st_agent(GLB float* p, float v) {
 __device__ __forceinline__ void st_agent(GLB int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Reads of data that other compute units wrote during the same step
+// (activations, residual stream, q/k/v, attention partials, LM tile maxima,
+// quantized activations and scales).  The producers store them agent-coherent
+// and count them only once the stores have completed; the consumer reads them
+// with sc1 buffer loads, served at the device's coherence point and never from a
+// line its own XCD's L2 may hold from before the write (lines can mix data of
+// different events).  So the event wait needs no acquire that invalidates the
+// L2 -- such an invalidate per instruction costs about 80 us per step and throws
+// away every other CU's cached lines on that XCD.  The descriptor's base must be
+// wave-uniform (per-lane parts go into the offset); the range check of the
+// buffer descriptor (2 GiB) is never reached.
+// The layerwise kernels read the same data across kernel boundaries (stream
+// order makes it visible), so their tile functions take POL = 0 (cached loads).
+constexpr int kCohPolicy = 16;  // sc1
+template <int POL>
+struct CohT {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ explicit CohT(const GLB void* base) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    r = __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, 0x7FFFFFFF,
+                                          0x00020000);
+  }
+  __device__ __forceinline__ f32x4 f4(uint32_t off) const {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL));
+  }
+  __device__ __forceinline__ u32x4 u4(uint32_t off) const {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL));
+  }
+  __device__ __forceinline__ f32x2 f2(uint32_t off) const {
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POL));
+  }
+  __device__ __forceinline__ float f1(uint32_t off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POL));
+  }
+  // per-lane offset plus a wave-uniform one (kept in a scalar register)
+  __device__ __forceinline__ float f1(uint32_t voff, uint32_t soff) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, POL));
+  }
+};
+using Coh = CohT<kCohPolicy>;
+
 // token id of sequence 0, clamped into [0, vocab) so that a bad id cannot index
 // outside the embedding
 __device__ __forceinline__ int token_of(const GLB int* tokens, int b, int V) {
@@ -370,7 +413,7 @@ struct Act {
 // fp32 input lands straight in a.x, so besides a the load holds only the norm
 // weights (and a bf16 input) in flight: it can run while a GEMV tile's weights
 // sit in registers.  MC: chunks per lane unrolled (at least a.nc).
-template <int MC>
+template <int MC, int POL = kCohPolicy>
 __device__ inline void load_act_t(Act& a, int K, int cw, const GLB float* xf, const GLB uint16_t* xb,
                                   const GLB uint16_t* nw) {
   const int lane = lane_id();
@@ -387,7 +430,8 @@ __device__ inline void load_act_t(Act& a, int K, int cw, const GLB float* xf, co
     const int k0 = (ok[j] ? base + ch : 0) * 8;
     if (j < a.nc) {
       if (xf) {
-        const f32x4 v0 = *(const GLB f32x4*)(xf + k0), v1 = *(const GLB f32x4*)(xf + k0 + 4);
+        const CohT<POL> cx(xf);
+        const f32x4 v0 = cx.f4(k0 * 4), v1 = cx.f4(k0 * 4 + 16);
         a.x[j][0] = v0.x; a.x[j][1] = v0.y; a.x[j][2] = v0.z; a.x[j][3] = v0.w;
         a.x[j][4] = v1.x; a.x[j][5] = v1.y; a.x[j][6] = v1.z; a.x[j][7] = v1.w;
       } else {
@@ -556,7 +600,7 @@ __device__ inline void gemv_chunked(const Src& src, const Act& a, const GemvGeom
 // tile of the same op left them in a): the weights never wait for the event.
 // Otherwise pre() runs first and rel() after the arithmetic.  The activation
 // load has one call site, so it is inlined once.
-template <class Src, class Rel, class Pre>
+template <int POL = kCohPolicy, class Src, class Rel, class Pre>
 __device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int cw, LDS float* part, const Rel& rel,
                                  const Pre& pre) {
   const GemvGeom g(gi, cw);
@@ -574,7 +618,7 @@ __device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int c
   // for it, paying the LDS latency once per row
   __builtin_amdgcn_sched_barrier(0);
   if (shape != 3) rel();
-  if (pre()) load_act_t<kMaxChunks>(a, gi.K, cw, gi.xf, gi.xb, gi.nw);
+  if (pre()) load_act_t<kMaxChunks, POL>(a, gi.K, cw, gi.xf, gi.xb, gi.nw);
   if (shape == 0)
     gemv_finish<16, 1>(a, wv, g.nrows, part);
   else if (shape == 1)
@@ -649,15 +693,16 @@ __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
 // Residual input of a GEMV tile's rows (O projection: the residual stream or,
 // in layer 0, the embedding row; down projection: the post-attention stream),
 // one value per lane < nrows; loaded ahead of the epilogue.
+template <int POL = kCohPolicy>
 __device__ inline float gemv_residual(const Meta& m, const Consts& c) {
   const int lane = lane_id();
   const int op = m.w(WOpcode);
   const int row0 = m.w(WPay), nr = m.w(WPay + 1);
   const int rr = row0 + (lane < nr ? lane : 0);
   if (op == OpOproj)
-    return m.q(OX) ? ((const GLB float*)m.q(OX))[rr]
+    return m.q(OX) ? CohT<POL>((const GLB float*)m.q(OX)).f1(rr * 4)
                     : bf16f(((const GLB uint16_t*)m.q(OEmbed))[(size_t)token0(m.q(OTokens), c.V) * c.H + rr]);
-  if (op == OpDown) return ((const GLB float*)m.q(DnRes))[rr];
+  if (op == OpDown) return CohT<POL>((const GLB float*)m.q(DnRes)).f1(rr * 4);
   return 0.f;
 }
 
@@ -739,7 +784,7 @@ __device__ __forceinline__ bool amax_better(float v, int i, float bv, int bi) {
 // within rounding.  Rows past nrows re-read the last row, sequences past B and
 // chunks past the wave's range read valid addresses and are zeroed.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-template <bool EMB, class Src, class Rel>
+template <bool EMB, int POL, class Src, class Rel>
 __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
                                     LDS float* ssp, const Rel& rel) {
   const int lane = lane_id();
@@ -751,12 +796,13 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
   const int arow = rr * K * 2;
   const int b = lane & 15;
   const bool bok = b < B;
-  const GLB float* xf = nullptr;
   const GLB uint16_t* xb = nullptr;
+  uint32_t xoff = 0;  // byte offset of sequence b's activation row
   if (EMB)
     xb = gi.emb + (size_t)token_of(gi.tok, bok ? b : 0, V) * K;
   else
-    xf = gi.xf + (size_t)(bok ? b : 0) * K;
+    xoff = (uint32_t)((bok ? b : 0) * K) * 4;
+  const CohT<POL> cx(EMB ? (const GLB void*)gi.emb : (const GLB void*)gi.xf);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
   constexpr int NB = 4;  // k-steps whose loads are issued together
@@ -774,8 +820,8 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
       if (EMB) {
         xr[u] = *(const GLB u32x4*)(xb + kk);
       } else {
-        x0[u] = *(const GLB f32x4*)(xf + kk);
-        x1[u] = *(const GLB f32x4*)(xf + kk + 4);
+        x0[u] = cx.f4(xoff + kk * 4);
+        x1[u] = cx.f4(xoff + kk * 4 + 16);
       }
       if (gi.nw) wn[u] = *(const GLB u32x4*)(gi.nw + kk);
     }
@@ -821,17 +867,18 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
   for (int i = 0; i < 4; ++i) part[(4 * q + i) * kMB + b] = acc[i];
 }
 
-template <class Src, class Rel>
+template <int POL = kCohPolicy, class Src, class Rel>
 __device__ inline void gemv_rows_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
                                     LDS float* ssp, const Rel& rel) {
   if (gi.xf)
-    gemv_tile_mb<false>(src, gi, B, V, cw, part, ssp, rel);
+    gemv_tile_mb<false, POL>(src, gi, B, V, cw, part, ssp, rel);
   else
-    gemv_tile_mb<true>(src, gi, B, V, cw, part, ssp, rel);
+    gemv_tile_mb<true, POL>(src, gi, B, V, cw, part, ssp, rel);
 }
 
 // Residual inputs of the four (row, sequence) outputs lane l owns in the batched
 // epilogue: index idx = l + 64 j, row idx / 16, sequence idx % 16 = l % 16.
+template <int POL = kCohPolicy>
 __device__ inline f32x4 gemv_residual_mb(const Meta& m, const Consts& c) {
   const int lane = lane_id();
   const int op = m.w(WOpcode);
@@ -844,11 +891,11 @@ __device__ inline f32x4 gemv_residual_mb(const Meta& m, const Consts& c) {
     const int row = (lane + 64 * j) >> 4;
     const int rr = row0 + (row < nr ? row : 0);
     if (op == OpOproj) {
-      r[j] = m.q(OX) ? ((const GLB float*)m.q(OX))[(size_t)bb * c.H + rr]
+      r[j] = m.q(OX) ? CohT<POL>((const GLB float*)m.q(OX)).f1((uint32_t)(bb * c.H + rr) * 4)
                      : bf16f(((const GLB uint16_t*)m.q(OEmbed))[(size_t)token_of((const GLB int*)m.q(OTokens), bb, c.V) *
                                                                   c.H + rr]);
     } else {
-      r[j] = ((const GLB float*)m.q(DnRes))[(size_t)bb * c.H + rr];
+      r[j] = CohT<POL>((const GLB float*)m.q(DnRes)).f1((uint32_t)(bb * c.H + rr) * 4);
     }
   }
   return r;
@@ -943,7 +990,7 @@ __device__ __forceinline__ bool is_gemv(int op) {
 // Every global input is loaded in one batch up front; the RoPE partner of
 // element d (d +- head_dim/2) is in the same lane for head_dim 128 and in
 // lane ^ 32 for head_dim 64.
-template <int HD, class Src>
+template <int HD, int POL = kCohPolicy, class Src>
 __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c, int cw,
                                  LDS float* scr, bool writer, unsigned long long* tr = nullptr) {
   const int lane = lane_id();
@@ -955,7 +1002,7 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   const bool active = cw < c.hpg;
   constexpr int HALF = HD / 2;
   constexpr int PER = HD / 64;  // head elements per lane: d = lane + 64 k
-  const GLB float* qkv = (const GLB float*)mt.q(AttnQkv) + ((size_t)b * c.nkv + g) * c.RPG;
+  const CohT<POL> cq((const GLB float*)mt.q(AttnQkv) + ((size_t)b * c.nkv + g) * c.RPG);
   const GLB float* rope = (const GLB float*)mt.q(AttnRope) + (size_t)b * HD;  // (cos, sin) pairs
   const GLB uint16_t* qn = c.qk_norm ? (const GLB uint16_t*)mt.q(AttnQn) : nullptr;
   const GLB uint16_t* knw = c.qk_norm ? (const GLB uint16_t*)mt.q(AttnKn) : nullptr;
@@ -970,9 +1017,9 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   for (int k = 0; k < PER; ++k) {
     const int d = lane + 64 * k;
     const int ii = d < HALF ? d : d - HALF;
-    qv[k] = qkv[qh * HD + d];
-    kv[k] = qkv[c.hpg * HD + d];
-    vv[k] = qkv[(c.hpg + 1) * HD + d];
+    qv[k] = cq.f1((uint32_t)(qh * HD + d) * 4);
+    kv[k] = cq.f1((uint32_t)(c.hpg * HD + d) * 4);
+    vv[k] = cq.f1((uint32_t)((c.hpg + 1) * HD + d) * 4);
     cs[k] = rope[2 * ii];
     sn[k] = rope[2 * ii + 1];
     wq[k] = qn ? bf16f(qn[d]) : 1.f;
@@ -1141,7 +1188,7 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
 // split s's (max, sum) and turns it into a weight; the weighted outputs are
 // read 16 splits per batch with clamped (branch-free) addresses so that each
 // batch's loads are issued together.
-template <int HD>
+template <int HD, int POL = kCohPolicy>
 __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
                                     unsigned long long* tr = nullptr) {
   if (cw >= c.hpg) return;
@@ -1152,7 +1199,8 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
   const size_t stride = (size_t)c.hpg * (HD + 2);
   const int S = c.S;  // <= 64 (checked at plan build)
   const int sl = lane < S ? lane : S - 1;
-  const float ms = part[sl * stride], ls = part[sl * stride + 1];
+  const CohT<POL> cp(part);
+  const float ms = cp.f1((uint32_t)(sl * stride) * 4), ls = cp.f1((uint32_t)(sl * stride + 1) * 4);
   const bool live = lane < S && ls > 0.f;
   const float M = wave_max(live ? ms : -INFINITY);
   const float wsp = live ? __expf(ms - M) : 0.f;
@@ -1167,7 +1215,7 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
     for (int u = 0; u < 16; ++u) {
       const int s = s0 + u < S ? s0 + u : S - 1;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) ov[u][k] = part[s * stride + 2 + lane + 64 * k];
+      for (int k = 0; k < PER; ++k) ov[u][k] = cp.f1((uint32_t)(2 + lane + 64 * k) * 4, (uint32_t)(s * stride) * 4);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1186,10 +1234,11 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
 // ties.  Compute wave cw scans the contiguous quarter cw of the T tile maxima,
 // 32 per lane per batch (every load of a batch issued before any is used), and
 // leaves its best (value, index) in out2[0..1]; argmax_final merges the quarters.
+template <int POL = kCohPolicy>
 __device__ inline void argmax_part(const Meta& m, const Consts& c, int cw, LDS float* out2) {
   const int lane = lane_id();
   const int b = m.w(WGx), T = m.w(WPay);
-  const GLB f32x2* mx = (const GLB f32x2*)m.q(AmMax) + (size_t)b * T;
+  const CohT<POL> mx((const GLB f32x2*)m.q(AmMax) + (size_t)b * T);
   const int per = (T + kNW - 1) / kNW;
   const int lo = cw * per, hi = lo + per < T ? lo + per : T;
   float bv = -INFINITY;
@@ -1200,7 +1249,7 @@ __device__ inline void argmax_part(const Meta& m, const Consts& c, int cw, LDS f
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * 64 + lane;
-      pr[u] = mx[t < hi ? t : lo];
+      pr[u] = mx.f2((uint32_t)(t < hi ? t : lo) * 8);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
 // operands (the same K positions, so the product sums over the whole block).
 // Rows past the tile re-read its last row and tokens past M re-read token 0;
 // those outputs are never stored.  Partial block: part[(4 g + i) * 16 + b].
-template <class Src>
+template <int POL = kCohPolicy, class Src>
 __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts& c, int cw, LDS float* part) {
   const int op = m.w(WOpcode);
   const int lane = lane_id();
@@ -74,7 +74,8 @@ __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts
     // the gate reads the unquantized fp32 norm output: bf16 high and low parts
     // against the exactly converted weights, 4 k-steps of 8 per lane per block
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-    const GLB float* xf = (const GLB float*)m.q(GmAF) + (size_t)bb * K;
+    const CohT<POL> cx((const GLB float*)m.q(GmAF));
+    const uint32_t xo = (uint32_t)(bb * K) * 4;
     for (int kb = kb0; kb < kb1; ++kb) {
       const int ko = kb * 128 + g * 32;
       const uint4 w0 = src.ld16(seg, rr * K + ko), w1 = src.ld16(seg, rr * K + ko + 16);
@@ -82,8 +83,8 @@ __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts
       f32x4 blk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const f32x4 x0 = *(const GLB f32x4*)(xf + ko + ks * 8);
-        const f32x4 x1 = *(const GLB f32x4*)(xf + ko + ks * 8 + 4);
+        const f32x4 x0 = cx.f4(xo + (uint32_t)(ko + ks * 8) * 4);
+        const f32x4 x1 = cx.f4(xo + (uint32_t)(ko + ks * 8 + 4) * 4);
         const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         bf16x8 av, hi, lo;
 #pragma unroll
@@ -102,8 +103,8 @@ __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(blk[i], sc, acc[i]);
     }
   } else {
-    const GLB uint8_t* act = (const GLB uint8_t*)m.q(GmA8) + (size_t)bb * K;
-    const GLB float* as = (const GLB float*)m.q(GmAS) + (size_t)bb * nkb;
+    const CohT<POL> ca((const GLB uint8_t*)m.q(GmA8)), cs((const GLB float*)m.q(GmAS));
+    const uint32_t ao = (uint32_t)(bb * K), so = (uint32_t)(bb * nkb) * 4;
     constexpr int U = 4;  // blocks whose loads are issued together
     for (int kq = kb0; kq < kb1; kq += U) {
       v8i A[U], X[U];
@@ -113,10 +114,10 @@ __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts
         const int kb = kq + u < kb1 ? kq + u : kb0;
         const int ko = kb * 128 + g * 32;
         const uint4 w0 = src.ld16(seg, rr * K + ko), w1 = src.ld16(seg, rr * K + ko + 16);
-        const u32x4 x0 = *(const GLB u32x4*)(act + ko), x1 = *(const GLB u32x4*)(act + ko + 16);
+        const u32x4 x0 = ca.u4(ao + ko), x1 = ca.u4(ao + ko + 16);
         A[u] = v8i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
         X[u] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sc[u] = kq + u < kb1 ? ws[kb] * as[kb] : 0.f;
+        sc[u] = kq + u < kb1 ? ws[kb] * cs.f1(so + kb * 4) : 0.f;
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -245,19 +246,20 @@ __device__ inline void glm_a0_wave(const Meta& m, const Consts& c, int cw) {
 // Waves 0..2 share the q blocks (each sums the squares of all q columns); wave 3
 // normalizes the kv columns, rotates the k_rope columns and writes the bf16 row
 // [kv | k_rope] at the token's position of its request's cache.
+template <int POL = kCohPolicy>
 __device__ inline void glm_qan_wave(const Meta& m, const Consts& c, int cw) {
   const int lane = lane_id(), row = m.w(WPay);
-  const GLB float* in = (const GLB float*)m.q(QnIn) + (size_t)row * c.na;
-  auto sumsq = [&](const GLB float* p, int n) {  // n a multiple of 4
+  const CohT<POL> ci((const GLB float*)m.q(QnIn) + (size_t)row * c.na);  // the row's QKV-A output
+  auto sumsq = [&](int e0, int n) {  // elements e0 .. e0 + n - 1, n a multiple of 4
     float ss = 0.f;
     for (int j = lane; j < n / 4; j += 64) {
-      const f32x4 v = *(const GLB f32x4*)(p + 4 * j);
+      const f32x4 v = ci.f4((uint32_t)(e0 + 4 * j) * 4);
       ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
     }
     return wave_sum(ss);
   };
   if (cw < 3) {
-    const float inv = 1.f / sqrtf(sumsq(in, c.ql) / (float)c.ql + c.eps);
+    const float inv = 1.f / sqrtf(sumsq(0, c.ql) / (float)c.ql + c.eps);
     const int nb = c.ql / 128, per = (nb + 2) / 3;
     const int b0 = cw * per, b1 = b0 + per < nb ? b0 + per : nb;
     const GLB uint16_t* w = (const GLB uint16_t*)m.q(QnNorm);
@@ -267,7 +269,7 @@ __device__ inline void glm_qan_wave(const Meta& m, const Consts& c, int cw) {
       const int blk = bq + (lane >> 4);
       const bool live = blk < b1;
       const int k0 = (live ? blk : b0) * 128 + (lane & 15) * 8;
-      const f32x4 x0 = *(const GLB f32x4*)(in + k0), x1 = *(const GLB f32x4*)(in + k0 + 4);
+      const f32x4 x0 = ci.f4((uint32_t)k0 * 4), x1 = ci.f4((uint32_t)(k0 + 4) * 4);
       const u32x4 wv = *(const GLB u32x4*)(w + k0);
       const float u[8] = {x0.x * bf16lo(wv.x), x0.y * bf16hi(wv.x), x0.z * bf16lo(wv.y), x0.w * bf16hi(wv.y),
                           x1.x * bf16lo(wv.z), x1.y * bf16hi(wv.z), x1.z * bf16lo(wv.w), x1.w * bf16hi(wv.w)};
@@ -279,18 +281,18 @@ __device__ inline void glm_qan_wave(const Meta& m, const Consts& c, int cw) {
       }
     }
   } else {
-    const GLB float* kv = in + c.ql;
-    const float inv = 1.f / sqrtf(sumsq(kv, c.kl) / (float)c.kl + c.eps);
+    const float inv = 1.f / sqrtf(sumsq(c.ql, c.kl) / (float)c.kl + c.eps);
     const GLB int* rows = (const GLB int*)m.q(QnRows);
     const int pos = rows[row], req = rows[c.B + row];
     GLB uint16_t* out = (GLB uint16_t*)m.q(QnKv) + ((size_t)req * c.cap + pos) * (c.kl + c.rd);
     const GLB uint16_t* w = (const GLB uint16_t*)m.q(QnKvNorm);
-    for (int j = lane; j < c.kl; j += 64) out[j] = f2bf(kv[j] * inv * bf16f(w[j]));
+    for (int j = lane; j < c.kl; j += 64) out[j] = f2bf(ci.f1((uint32_t)(c.ql + j) * 4) * inv * bf16f(w[j]));
     const int half = c.rd / 2;
     if (lane < half) {
-      const GLB float* kr = kv + c.kl;
       const GLB float* rope = (const GLB float*)m.q(QnRope) + ((size_t)row * half + lane) * 2;
-      const float cs = rope[0], sn = rope[1], x0 = kr[lane], x1 = kr[lane + half];
+      const int kr = c.ql + c.kl;  // first k_rope column
+      const float cs = rope[0], sn = rope[1];
+      const float x0 = ci.f1((uint32_t)(kr + lane) * 4), x1 = ci.f1((uint32_t)(kr + lane + half) * 4);
       out[c.kl + lane] = f2bf(x0 * cs - x1 * sn);
       out[c.kl + lane + half] = f2bf(x1 * cs + x0 * sn);
     }

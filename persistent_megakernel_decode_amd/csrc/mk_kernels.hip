@@ -208,7 +208,8 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
           }
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // no agent-scope acquire (an L2 invalidate): every read of data another CU
+      // wrote in this step is a coherent load issued after this point (Coh)
       seen_ev = m.w(WWaitEv);
       seen_val = v;
     }
@@ -558,35 +559,35 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   const int op = m.w(WOpcode);
   if constexpr (GLM) {
     if (glm_is_gemm(op)) {
-      glm_gemm_wave(src, m, a.c, cw, part[cw]);
+      glm_gemm_wave<0>(src, m, a.c, cw, part[cw]);
       __syncthreads();
       if (cw == 0) glm_epilogue(m, a.c, &part[0][0]);
     } else if (op == OpGA0) {
       glm_a0_wave(m, a.c, cw);
     } else if (op == OpGQaNorm) {
-      glm_qan_wave(m, a.c, cw);
+      glm_qan_wave<0>(m, a.c, cw);
     }
     return;
   }
   if (is_gemv(op)) {
     const GemvIn gi = gemv_input(m, a.c);
     if constexpr (MB) {
-      gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {});
+      gemv_rows_mb<0>(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {});
       __syncthreads();
-      if (cw == 0) gemv_epilogue_mb(m, a.c, &part[0][0], &ssp[0][0], gemv_residual_mb(m, a.c));
+      if (cw == 0) gemv_epilogue_mb(m, a.c, &part[0][0], &ssp[0][0], gemv_residual_mb<0>(m, a.c));
     } else {
       Act act;
-      gemv_rows(src, act, gi, cw, part[cw], [] {}, [] { return true; });
+      gemv_rows<0>(src, act, gi, cw, part[cw], [] {}, [] { return true; });
       if (lane == 0) ssp[cw][0] = act.ssw;
       __syncthreads();
-      if (cw == 0) gemv_epilogue(m, a.c, part, &ssp[0][0], gemv_residual(m, a.c));
+      if (cw == 0) gemv_epilogue(m, a.c, part, &ssp[0][0], gemv_residual<0>(m, a.c));
     }
   } else if (op == OpAttn) {
-    attn_wave<HD>(src, m, a.c, cw, scr[cw], cw == 0);
+    attn_wave<HD, 0>(src, m, a.c, cw, scr[cw], cw == 0);
   } else if (op == OpCombine) {
-    combine_wave<HD>(m, a.c, cw);
+    combine_wave<HD, 0>(m, a.c, cw);
   } else if (op == OpArgmax) {
-    argmax_part(m, a.c, cw, part[cw]);
+    argmax_part<0>(m, a.c, cw, part[cw]);
     __syncthreads();
     if (cw == 0) argmax_final(m, &part[0][0], PW);
   }
