@@ -54,7 +54,7 @@ struct mk_plan {
   mkd::Consts c{};
   int num_cus = 0;
   unsigned long long timeout_ticks = 0;
-  int dma_pages = 2;
+  int dma_pages = 1;
   // device state
   int device = -1;
   bool uploaded = false;

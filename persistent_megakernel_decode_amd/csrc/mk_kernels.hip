@@ -193,8 +193,7 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
       if ((int)(v - tgt) < 0) {
         const unsigned long long t0 = now_ticks();
         for (unsigned it = 0;; ++it) {
-          __builtin_amdgcn_s_sleep(4);
-          v = count();
+          v = count();  // each poll is a memory round trip: no sleep between them
           if ((int)(v - tgt) >= 0) break;
           if ((it & 15) == 15) {
             if (aborted(L) || __hip_atomic_load(&a.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
