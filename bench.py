@@ -107,6 +107,23 @@ def time_launches(fn, stream, steps, warmup):
                 wall_us_per_step=wall * 1e6 / steps)
 
 
+def capture(run):
+    """Capture run(stream) (one step's launches) in a graph; returns its replay.
+    The run is made once eagerly first so that the plan has bound its operand
+    table (the capture then records kernel launches only, no copies or fills)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(s)
+    torch.cuda.synchronize()
+    return g.replay
+
+
 def cpu_baseline(inp, budget_s=20.0):
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -159,6 +176,11 @@ def bench_glm(args):
         for p_, w_ in zip(plans, ws):  # bind every plan once (operand-table upload) before timing
             p_.run(w_, caches, xr, layerwise=lw)
         res[key + "_cold"] = time_launches(cold, stream, args.steps, args.warmup)
+        if lw and not args.no_graph:
+            print("[bench] timing layerwise as a captured graph", file=sys.stderr, flush=True)
+            res["lw_graph_warm"] = time_launches(
+                capture(lambda s: plans[0].run(ws[0], caches, xr, stream=s, layerwise=True)), stream,
+                args.steps, args.warmup)
         if not lw:
             st, chk = plans[0].check()
             if st != mk.MK_OK or not chk.counters_ok:
@@ -187,6 +209,8 @@ def bench_glm(args):
     if "mk_cold" in res and "lw_cold" in res:
         out["speedup_vs_layerwise_cold"] = round(res["lw_cold"]["median"] / res["mk_cold"]["median"], 3)
         out["speedup_vs_layerwise_warm"] = round(res["lw_warm"]["median"] / res["mk_warm"]["median"], 3)
+    if "mk_warm" in res and "lw_graph_warm" in res:
+        out["speedup_vs_layerwise_graph_warm"] = round(res["lw_graph_warm"]["median"] / res["mk_warm"]["median"], 3)
     if not args.no_cpu_baseline:
         from oracle import glm as G
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -210,6 +234,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured layerwise baseline")
     ap.add_argument("--only", choices=["megakernel", "layerwise", "both"], default="both")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first launch one device-to-device copy of 256 MiB (read 256 MiB, write 256 MiB), so that "
@@ -252,6 +277,12 @@ def main():
     if args.only in ("layerwise", "both"):
         print("[bench] timing layerwise", file=sys.stderr, flush=True)
         res["lw"] = time_launches(lambda: plan.run_layerwise(w, kv, tok), stream, args.steps, args.warmup)
+        if not args.no_graph:
+            # the stronger baseline: the same launches captured once in a HIP graph
+            # and replayed (no per-launch host cost)
+            print("[bench] timing layerwise as a captured graph", file=sys.stderr, flush=True)
+            res["lw_graph"] = time_launches(capture(lambda s: plan.run_layerwise(w, kv, tok, stream=s)), stream,
+                                            args.steps, args.warmup)
     torch.cuda.synchronize()
     main_key = "mk" if "mk" in res else "lw"
     lat = res[main_key]["median"]
@@ -292,6 +323,10 @@ def main():
         out["layerwise_achieved_GBps"] = round(nbytes / (lwl * 1e-6) / 1e9, 1)
         if "mk" in res:
             out["speedup_vs_layerwise"] = round(lwl / lat, 3)
+    if "lw_graph" in res:
+        out["layerwise_graph_us"] = {k: round(v, 2) for k, v in res["lw_graph"].items()}
+        if "mk" in res:
+            out["speedup_vs_layerwise_graph"] = round(res["lw_graph"]["median"] / lat, 3)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp)

@@ -205,3 +205,36 @@ def test_gpu_llama1b_batch16_full_size():
         del c
         gc.collect()
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(300)
+def test_gpu_layerwise_graph_replay_matches_eager():
+    """The layerwise launches captured in a HIP graph (the stronger baseline the
+    benchmark reports) give the eager result on every replay, with eager work
+    (a megakernel step and torch ops) and synchronizations between replays."""
+    mk = _mk()
+    case = Case("tiny")
+    kv = case.fresh_kv()
+    case.plan.run(case.w, kv, case.tokens, layerwise=True)
+    torch.cuda.synchronize()
+    want = case.plan.output(mk.MK_OUT_LOGITS).cpu().numpy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        case.plan.run(case.w, kv, case.tokens, stream=s, layerwise=True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("  capture layerwise tiny", flush=True)
+    with torch.cuda.graph(g, stream=s):
+        case.plan.run(case.w, kv, case.tokens, stream=s, layerwise=True)
+    torch.cuda.synchronize()
+    for k in range(4):
+        print("  replay %d" % k, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        got = case.plan.output(mk.MK_OUT_LOGITS).cpu().numpy()
+        assert np.array_equal(got, want), k
+        # eager work between replays
+        case.plan.run(case.w, case.fresh_kv(), case.tokens)
+        torch.ones(1 << 20, device="cuda").sum().item()
+        torch.cuda.synchronize()
