@@ -73,7 +73,7 @@ struct mk_plan {
   // workspace offsets (bytes)
   size_t off_qkv = 0, off_part = 0, off_ao = 0, off_hidden = 0, off_act = 0, off_logits = 0, off_lmmax = 0,
          off_next = 0;
-  size_t sz_qkv = 0, sz_part = 0, sz_ao = 0, sz_act = 0;
+  size_t sz_qkv = 0, sz_part = 0, sz_ao = 0, sz_act = 0, sz_hid = 0;
   // GLM pre-attention path: token rows' (position, request), workspace offsets
   bool glm = false;
   int n_seq = 0;
@@ -341,14 +341,18 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     off += (bytes + 255) / 256 * 256;
     return o2;
   };
-  p->sz_qkv = B * c.nkv * c.RPG * 4;
-  p->sz_part = B * c.nkv * c.S * hpg * (c.hd + 2) * 4;
-  p->sz_ao = B * c.nq * c.hd * 4;
-  p->sz_act = B * c.F * 4;
+  // per-layer slices start on 256-byte boundaries: no cache line holds data
+  // of two layers (written under different events)
+  auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
+  p->sz_qkv = r256(B * c.nkv * c.RPG * 4);
+  p->sz_part = r256(B * c.nkv * c.S * hpg * (c.hd + 2) * 4);
+  p->sz_ao = r256(B * c.nq * c.hd * 4);
+  p->sz_act = r256(B * c.F * 4);
+  p->sz_hid = r256(B * c.H * 4);
   p->off_qkv = take(p->sz_qkv * L);
   p->off_part = take(p->sz_part * L);
   p->off_ao = take(p->sz_ao * L);
-  p->off_hidden = take(B * c.H * 4 * 2 * L);
+  p->off_hidden = take(p->sz_hid * 2 * L);
   p->off_act = take(p->sz_act * L);
   p->off_logits = take(B * c.V * 4);
   p->off_lmmax = take(B * c.T_v * 8);
@@ -581,7 +585,7 @@ static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const 
   const size_t B = p->batch, hpg = p->c.hpg;
   auto u = [](const void* q) { return (uint64_t)(uintptr_t)q; };
   auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(p->d_ws + off); };
-  const size_t hid = B * p->c.H * 4;
+  const size_t hid = p->sz_hid;
   auto xa = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l) * hid); };
   auto xb = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l + 1) * hid); };
   const size_t kvlayer = (size_t)2 * B * d.n_kv_heads * d.max_kv_len * d.head_dim * 2;
@@ -750,7 +754,7 @@ mk_status mk_plan_output(const mk_plan* p, int32_t which, void** dev_ptr, size_t
       return MK_OK;
     case MK_OUT_HIDDEN:
       *dev_ptr = p->d_ws + p->off_hidden;
-      *bytes = B * p->c.H * 4 * 2 * p->c.L;
+      *bytes = p->sz_hid * 2 * p->c.L;
       return MK_OK;
     default:
       return fail(MK_E_INVALID, "unknown output");

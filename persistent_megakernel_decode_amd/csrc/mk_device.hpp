@@ -175,16 +175,19 @@ __device__ __forceinline__ void st_agent(GLB int* p, int v) {
 // Reads of data that other compute units wrote during the same step
 // (activations, residual stream, q/k/v, attention partials, LM tile maxima,
 // quantized activations and scales).  The producers store them agent-coherent
-// and count them only once the stores have completed; the consumer reads them
-// with sc1 buffer loads, served at the device's coherence point and never from a
-// line its own XCD's L2 may hold from before the write (lines can mix data of
-// different events).  So the event wait needs no acquire that invalidates the
-// L2 -- such an invalidate per instruction costs about 80 us per step and throws
-// away every other CU's cached lines on that XCD.  The descriptor's base must be
-// wave-uniform (per-lane parts go into the offset); the range check of the
-// buffer descriptor (2 GiB) is never reached.
-// The layerwise kernels read the same data across kernel boundaries (stream
-// order makes it visible), so their tile functions take POL = 0 (cached loads).
+// and count them only once the stores have completed, and the interpreter waits
+// for an event without an acquire that would invalidate the L2 (one per
+// instruction costs about 80 us per step and throws away every other CU's
+// cached lines on that XCD).  A consumer may then read through the caches
+// (POL = 0) only data that cannot sit stale in them: the interpreter
+// invalidates its L1 / L2 once when it starts, and such a buffer is written
+// once per step, read only after the event that counts all of its producers,
+// and shares no cache line with data of another event (per-layer slices start
+// on 256-byte boundaries).  Data that fails the last condition -- the attention
+// partials, whose (sequence, kv head) blocks are not line-aligned and complete
+// under different events -- is read with sc1 loads (POL = kCohPolicy), served
+// at the device's coherence point.  The descriptor's base must be wave-uniform
+// (per-lane parts go into the offset); its 2 GiB range is never reached.
 constexpr int kCohPolicy = 16;  // sc1
 template <int POL>
 struct CohT {
@@ -213,7 +216,6 @@ struct CohT {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, POL));
   }
 };
-using Coh = CohT<kCohPolicy>;
 
 // token id of sequence 0, clamped into [0, vocab) so that a bad id cannot index
 // outside the embedding
@@ -413,7 +415,7 @@ struct Act {
 // fp32 input lands straight in a.x, so besides a the load holds only the norm
 // weights (and a bf16 input) in flight: it can run while a GEMV tile's weights
 // sit in registers.  MC: chunks per lane unrolled (at least a.nc).
-template <int MC, int POL = kCohPolicy>
+template <int MC, int POL = 0>
 __device__ inline void load_act_t(Act& a, int K, int cw, const GLB float* xf, const GLB uint16_t* xb,
                                   const GLB uint16_t* nw) {
   const int lane = lane_id();
@@ -600,7 +602,7 @@ __device__ inline void gemv_chunked(const Src& src, const Act& a, const GemvGeom
 // tile of the same op left them in a): the weights never wait for the event.
 // Otherwise pre() runs first and rel() after the arithmetic.  The activation
 // load has one call site, so it is inlined once.
-template <int POL = kCohPolicy, class Src, class Rel, class Pre>
+template <int POL = 0, class Src, class Rel, class Pre>
 __device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int cw, LDS float* part, const Rel& rel,
                                  const Pre& pre) {
   const GemvGeom g(gi, cw);
@@ -693,7 +695,7 @@ __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
 // Residual input of a GEMV tile's rows (O projection: the residual stream or,
 // in layer 0, the embedding row; down projection: the post-attention stream),
 // one value per lane < nrows; loaded ahead of the epilogue.
-template <int POL = kCohPolicy>
+template <int POL = 0>
 __device__ inline float gemv_residual(const Meta& m, const Consts& c) {
   const int lane = lane_id();
   const int op = m.w(WOpcode);
@@ -867,7 +869,7 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
   for (int i = 0; i < 4; ++i) part[(4 * q + i) * kMB + b] = acc[i];
 }
 
-template <int POL = kCohPolicy, class Src, class Rel>
+template <int POL = 0, class Src, class Rel>
 __device__ inline void gemv_rows_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
                                     LDS float* ssp, const Rel& rel) {
   if (gi.xf)
@@ -878,7 +880,7 @@ __device__ inline void gemv_rows_mb(const Src& src, const GemvIn& gi, int B, int
 
 // Residual inputs of the four (row, sequence) outputs lane l owns in the batched
 // epilogue: index idx = l + 64 j, row idx / 16, sequence idx % 16 = l % 16.
-template <int POL = kCohPolicy>
+template <int POL = 0>
 __device__ inline f32x4 gemv_residual_mb(const Meta& m, const Consts& c) {
   const int lane = lane_id();
   const int op = m.w(WOpcode);
@@ -990,7 +992,7 @@ __device__ __forceinline__ bool is_gemv(int op) {
 // Every global input is loaded in one batch up front; the RoPE partner of
 // element d (d +- head_dim/2) is in the same lane for head_dim 128 and in
 // lane ^ 32 for head_dim 64.
-template <int HD, int POL = kCohPolicy, class Src>
+template <int HD, int POL = 0, class Src>
 __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c, int cw,
                                  LDS float* scr, bool writer, unsigned long long* tr = nullptr) {
   const int lane = lane_id();
@@ -1188,7 +1190,7 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
 // split s's (max, sum) and turns it into a weight; the weighted outputs are
 // read 16 splits per batch with clamped (branch-free) addresses so that each
 // batch's loads are issued together.
-template <int HD, int POL = kCohPolicy>
+template <int HD, int POL = 0>
 __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
                                     unsigned long long* tr = nullptr) {
   if (cw >= c.hpg) return;
@@ -1199,7 +1201,7 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
   const size_t stride = (size_t)c.hpg * (HD + 2);
   const int S = c.S;  // <= 64 (checked at plan build)
   const int sl = lane < S ? lane : S - 1;
-  const CohT<POL> cp(part);
+  const CohT<kCohPolicy> cp(part);  // blocks of different events share lines
   const float ms = cp.f1((uint32_t)(sl * stride) * 4), ls = cp.f1((uint32_t)(sl * stride + 1) * 4);
   const bool live = lane < S && ls > 0.f;
   const float M = wave_max(live ? ms : -INFINITY);
@@ -1234,7 +1236,7 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
 // ties.  Compute wave cw scans the contiguous quarter cw of the T tile maxima,
 // 32 per lane per batch (every load of a batch issued before any is used), and
 // leaves its best (value, index) in out2[0..1]; argmax_final merges the quarters.
-template <int POL = kCohPolicy>
+template <int POL = 0>
 __device__ inline void argmax_part(const Meta& m, const Consts& c, int cw, LDS float* out2) {
   const int lane = lane_id();
   const int b = m.w(WGx), T = m.w(WPay);

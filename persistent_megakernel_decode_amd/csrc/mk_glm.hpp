@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
 // operands (the same K positions, so the product sums over the whole block).
 // Rows past the tile re-read its last row and tokens past M re-read token 0;
 // those outputs are never stored.  Partial block: part[(4 g + i) * 16 + b].
-template <int POL = kCohPolicy, class Src>
+template <int POL = 0, class Src>
 __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts& c, int cw, LDS float* part) {
   const int op = m.w(WOpcode);
   const int lane = lane_id();
@@ -246,7 +246,7 @@ __device__ inline void glm_a0_wave(const Meta& m, const Consts& c, int cw) {
 // Waves 0..2 share the q blocks (each sums the squares of all q columns); wave 3
 // normalizes the kv columns, rotates the k_rope columns and writes the bf16 row
 // [kv | k_rope] at the token's position of its request's cache.
-template <int POL = kCohPolicy>
+template <int POL = 0>
 __device__ inline void glm_qan_wave(const Meta& m, const Consts& c, int cw) {
   const int lane = lane_id(), row = m.w(WPay);
   const CohT<POL> ci((const GLB float*)m.q(QnIn) + (size_t)row * c.na);  // the row's QKV-A output

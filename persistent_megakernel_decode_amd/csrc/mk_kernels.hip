@@ -207,8 +207,8 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
           }
         }
       }
-      // no agent-scope acquire (an L2 invalidate): every read of data another CU
-      // wrote in this step is a coherent load issued after this point (Coh)
+      // no agent-scope acquire (an L2 invalidate) here: see CohT for why the
+      // reads that follow need none
       seen_ev = m.w(WWaitEv);
       seen_val = v;
     }
@@ -511,6 +511,10 @@ __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
     const int n = (int)(sizeof(L->c) / 4);
     for (int k = threadIdx.x; k < n; k += blockDim.x) c[k] = 0;
   }
+  // drop every line this CU's L1 and its XCD's L2 hold from before this launch,
+  // so that the cached reads of this step's data (see CohT) cannot see a stale
+  // copy; within the step no such line can appear
+  if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   // issue priority: compute and storer waves (the dependency chain) ahead of
   // the controller, the controller ahead of the loaders

@@ -161,6 +161,28 @@ def test_gpu_consecutive_runs_new_tokens(key, name):
         assert int(c.plan.output(mk.MK_OUT_NEXT_TOKEN).cpu()[0]) == int(ref["next"][0])
 
 
+def test_gpu_consecutive_runs_batched():
+    """Batch 16 (matrix-core tiles): three consecutive runs on one plan with
+    different token ids each match their own oracle result, so no run reads a
+    cached line of an earlier run's intermediates."""
+    mk = _mk()
+    c = case("tiny_b16_seq", "tiny", norm_sigma=0.1, batch=16, kv_len=(0, 300), seed=21)
+    V, B = c.cfg["vocab"], c.cfg["batch"]
+    for trial in range(3):
+        tok = ((c.inp["tokens"].astype(np.int64) + 1 + 977 * trial) % V).astype(np.int32)
+        inp = dict(c.inp, tokens=tok)
+        ref = oracle.decode_step(inp)
+        c.plan.run(c.w, c.fresh_kv(), mk.tokens_to_device(tok))
+        torch.cuda.synchronize()
+        st, chk = c.plan.check()
+        assert st == mk.MK_OK and chk.counters_ok == 1
+        logits = c.plan.output(mk.MK_OUT_LOGITS).cpu().numpy().reshape(B, -1)
+        rel = np.linalg.norm(logits - ref["logits"]) / np.linalg.norm(ref["logits"])
+        print("  trial %d rel-L2 %.3g" % (trial, rel), flush=True)
+        assert rel <= LOGIT_TOL
+        assert np.array_equal(c.plan.output(mk.MK_OUT_NEXT_TOKEN).cpu().numpy(), ref["next"])
+
+
 @pytest.mark.timeout(900)
 def test_gpu_qwen3_8b_full_size():
     """Qwen3-8B shape (36 layers, hidden 4096, head_dim 128, q/k RMSNorm, FFN
