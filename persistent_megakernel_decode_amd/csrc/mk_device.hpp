@@ -26,7 +26,10 @@ namespace mkd {
 // ---- instruction words (same layout as the host planner) -------------------
 enum : int {
   WOpcode = 0, WSpec = 1, WOpRow = 2, WWaitCnt = 3, WWaitEv = 4, WWaitTgt = 5, WSigCnt = 6, WSigEv = 7,
-  WSigInc = 8, WTask = 9, WLayer = 10, WGx = 11, WGy = 12, WGz = 13, WPay = 14
+  WSigInc = 8, WTask = 9, WLayer = 10, WGx = 11, WGy = 12, WGz = 13, WPay = 14,
+  // LDS copy only (the queue holds zero there): sequence number of the
+  // instruction's first ring page, written by the controller as it stages it
+  WFirstPage = 31
 };
 enum : int { OpNoop = 0, OpQkv = 1, OpAttn = 2, OpCombine = 3, OpOproj = 4, OpGateUp = 5, OpDown = 6, OpLmHead = 7, OpArgmax = 8 };
 // GLM-style pre-attention path: add + RMSNorm + fp8 quant (one token row per
@@ -67,7 +70,7 @@ constexpr int kNW = 4;        // compute waves per workgroup (K split / one q he
 constexpr int kMaxRows = 16;  // weight rows per GEMV tile
 constexpr int kMB = 16;       // sequences per batched GEMV tile (the MFMA N dimension)
 constexpr int kMaxChunks = 6; // 16-byte activation chunks per lane (K / (8 * kNW * 64))
-constexpr int kScratch = 512; // floats of per-compute-wave scratch
+constexpr int kScratch = 384; // floats of per-compute-wave scratch (attention: 3 head vectors)
 constexpr int kTraceWords = 16; // timestamps per traced instruction
 constexpr int kCtrStride = 64;  // u32 words between event counters: one 256-byte line each
 // Each event is counted in kCtrSub sub-counters (a producer on compute unit c
@@ -95,7 +98,7 @@ struct KArgs {
   unsigned* err;              // watchdog record [8]
   unsigned long long* trace;  // [C][max_len][kTraceWords] or null
   int max_len;
-  int dma_pages;  // pages in flight per loader wave (1 or 2)
+  int dma_pages;  // pages in flight per loader wave (1 to 3; batch-1 interpreter)
   unsigned epoch;
   unsigned long long timeout_ticks;
   Consts c;

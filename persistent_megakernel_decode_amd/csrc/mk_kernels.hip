@@ -32,8 +32,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // PW / SW: partial-sum and sum-of-squares floats per compute wave per slot
 // (one value per tile row for batch 1; a 16 x 16 block of rows x sequences and
-// one value per sequence for the batched path)
-template <int PW, int SW>
+// one value per sequence for the batched path); NWT: compute waves in all
+template <int PW, int SW, int NWT>
 struct CtrlT {
   int ready_seq, done_seq, abort_flag, meta_seq;  // meta_seq: meta records staged (instructions 0 .. meta_seq-1)
   int slot_full[16];   // generation + 1 of the data in each ring slot (loaders -> compute)
@@ -42,13 +42,17 @@ struct CtrlT {
   int rel_sink[64];    // target of the zero adds of lanes that release no page
   float part[4][kNW][PW];
   float ssp[4][kNW][SW];
-  float scratch[kNW][kScratch];
+  float scratch[NWT][kScratch];
 };
 // Copies of the instructions in flight (instruction i in slot i % kMeta) and of
 // their operand-table rows, staged by the controller.
 constexpr int kMeta = 8;
 // Workgroup LDS.  MB: batched sequences (MFMA tiles) -- one page less in the
-// ring for the 16 x 16 partial blocks.
+// ring for the 16 x 16 partial blocks.  SETS: groups of kNW compute waves; with
+// two, consecutive instructions alternate between the groups, so that one
+// tile's activation loads and matrix-core work overlap the next one's (the
+// batched path: its tiles are bound by the latency of those loads, and its
+// registers leave room for a third wave per SIMD).
 template <bool MB_, bool GLM_ = false>
 struct __attribute__((aligned(16))) LdsT {
   static constexpr bool MB = MB_;
@@ -56,10 +60,15 @@ struct __attribute__((aligned(16))) LdsT {
   static constexpr int NP = MB_ ? kNumPages - 1 : kNumPages;  // ring pages
   static constexpr int PW = MB_ ? kMB * kMB : kMaxRows;
   static constexpr int SW = MB_ ? kMB : 1;
+  static constexpr int SETS = (MB_ && !GLM_) ? 2 : 1;
+  static constexpr int THREADS = (4 + kNW * SETS) * 64;
   char ring[NP][kPage];
   uint32_t meta[kMeta][64];
-  CtrlT<PW, SW> c;
+  CtrlT<PW, SW, kNW * SETS> c;
 };
+static_assert(sizeof(LdsT<true>) <= 160 * 1024 && sizeof(LdsT<false>) <= 160 * 1024 &&
+                  sizeof(LdsT<true, true>) <= 160 * 1024,
+              "workgroup LDS above 160 KiB");
 
 template <class T>
 __device__ __forceinline__ uint32_t lds_addr(LDS T* p) {
@@ -133,9 +142,12 @@ __device__ __forceinline__ const CST uint64_t* oprow(const KArgs& a, int row) {
 }
 
 // Copy instruction j and its operand row into meta record j % kMeta (scalar
-// loads; lane 0 writes).  Past the end of the queue the record is a NoOp.
+// loads; lane 0 writes).  With two compute groups the record also carries the
+// sequence number of the instruction's first ring page (pages: pages of
+// instructions 0 .. j-1; instructions are staged in order); a single group
+// counts them itself.  Past the end of the queue the record is a NoOp.
 template <class LT>
-__device__ void stage(const KArgs& a, LDS LT* L, int j) {
+__device__ void stage(const KArgs& a, LDS LT* L, int j, int& pages) {
   LDS uint32_t* rec = L->meta[j % kMeta];
   if (j >= a.max_len) {
     if (lane_id() == 0) rec[WOpcode] = OpNoop;
@@ -147,7 +159,13 @@ __device__ void stage(const KArgs& a, LDS LT* L, int j) {
   for (int k = 0; k < 32; ++k) w[k] = g[k];
   if (lane_id() == 0) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) rec[k] = w[k];
+    for (int k = 0; k < 32; ++k) rec[k] = k == WFirstPage ? (uint32_t)pages : w[k];
+  }
+  if (LT::SETS > 1 && (int)w[WOpcode] != OpNoop) {
+    GMeta gm;
+    gm.ins = (const CST int*)g;
+    gm.row = oprow(a, (int)w[WOpRow]);
+    pages += tile_info(gm, a.c).npages;
   }
   const CST uint32_t* gr = (const CST uint32_t*)oprow(a, (int)w[WOpRow]);
 #pragma unroll
@@ -166,19 +184,27 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
   // event for a target within that count needs neither a poll nor an acquire
   int seen_ev = -1;
   unsigned seen_val = 0;
-  stage(a, L, 0);
+  int pages = 0;
+  stage(a, L, 0, pages);
   if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, 1);
   for (int i = 0; i < a.max_len; ++i) {
     const Meta m = load_meta(L->meta[i % kMeta]);
     if (m.w(WOpcode) == OpNoop) {
-      // let the other waves read the NoOp and leave their loops
+      // let the other waves read the NoOp and leave their loops; with two
+      // compute groups the one whose next instruction is i + 1 reads that (a
+      // NoOp too: a queue ends at its first NoOp)
+      if (LT::SETS > 1) {
+        if (i + 2 > kMeta && !wait_lds_ge(a, L, &L->c.done_seq, i + 2 - kMeta, ErrDrain, i)) return;
+        stage(a, L, i + 1, pages);
+        if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, i + 2);
+      }
       if (lane_id() == 0) lds_store_rel(&L->c.ready_seq, i + 1);
       break;
     }
     // slot (i + 1) % kMeta last held instruction i + 1 - kMeta; the storer reads
     // the slots of the instruction it is on and of the next one
     if (i + 2 > kMeta && !wait_lds_ge(a, L, &L->c.done_seq, i + 2 - kMeta, ErrDrain, i)) return;
-    stage(a, L, i + 1);
+    stage(a, L, i + 1, pages);
     if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, i + 2);
     if (m.w(WWaitCnt) && !(m.w(WWaitEv) == seen_ev && (int)(seen_val - a.epoch * (unsigned)m.w(WWaitTgt)) >= 0)) {
       const unsigned tgt = a.epoch * (unsigned)m.w(WWaitTgt);
@@ -307,6 +333,11 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
     if (npend > 3) publish(q3, l3);
     npend = 0;
   };
+  // the batched interpreters keep 8 to 16 KiB in flight per loader wave (their
+  // tiles are bound by the latency of activation loads that queue behind the
+  // DMA); the batch-1 interpreter keeps dma_pages pages (its larger models are
+  // bound by bandwidth)
+  constexpr bool half = LT::MB;
   int seq = 0;
   for (int i = 0; i < a.max_len; ++i) {
     const CST int* ins = instr(a, i);
@@ -346,11 +377,27 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
         whole = t.p0 + pofs;
       else if (t.len1 && pofs >= t.off1 && pofs + kPage <= t.off1 + t.len1)
         whole = t.p1 + (pofs - t.off1);
+      // batched interpreters: after each 8 KiB half of a page, wait for the
+      // previous half; the wait after a page's first half completes every
+      // earlier page (at most one is pending then)
+      auto half_wait = [&](int j) {
+        if constexpr (half) {
+          if (j == 7 || j == 15) {
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            if (j == 7 && npend) {
+              publish(q0, l0);
+              npend = 0;
+            }
+          }
+        }
+      };
       if (whole) {
         const GLB char* src = whole + lane * 16;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < 16; ++j) {
           __builtin_amdgcn_global_load_lds((const GLB void*)(src + j * 1024), (lds_void*)(dst + j * 1024), 16, 0, kDmaNT);
+          half_wait(j);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -361,9 +408,16 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
           else if (toff >= t.off1 && toff < t.off1 + t.len1)
             src = t.p1 + (toff - t.off1);
           __builtin_amdgcn_global_load_lds((const GLB void*)src, (lds_void*)(dst + j * 1024), 16, 0, kDmaNT);
+          half_wait(j);
         }
       }
       const int last_of = pg == t.npages - 1 ? i : -1;
+      if constexpr (half) {
+        q0 = seq;
+        l0 = last_of;
+        npend = 1;
+        continue;
+      }
       if (npend == 0) {
         q0 = seq;
         l0 = last_of;
@@ -409,21 +463,27 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
 // its share into registers and hands the pages back, and only then waits for
 // the instruction's event (controller "ready") and loads the activations.
 // Other ops wait for "ready" first.
+// set: this wave's compute group; group g takes instructions g, g + SETS, ...
+// (it reads only their records, each before its arrival, so the controller
+// cannot have reused the slot).
 template <int HD, class LT>
-__device__ void compute(const KArgs& a, LDS LT* L, int cw) {
+__device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
   const int lane = lane_id();
-  int seq = 0;
   int act_row = -1;
+  int seq = 0;  // one group: ring pages of the instructions before i
   Act act;
-  for (int i = 0; i < a.max_len; ++i) {
+  for (int i = set; i < a.max_len; i += LT::SETS) {
     if (!wait_lds_ge(a, L, &L->c.meta_seq, i + 1, ErrReady, i)) return;
     const Meta m = load_meta(L->meta[i % kMeta]);
     const int op = m.w(WOpcode);
     if (op == OpNoop) break;
     const Tile t = tile_info(m, a.c);
     unsigned long long* tr = a.trace ? a.trace + ((size_t)blockIdx.x * a.max_len + i) * kTraceWords : nullptr;
-    const int first = seq;
-    seq += t.npages;
+    int first = seq;
+    if constexpr (LT::SETS > 1)
+      first = m.w(WFirstPage);
+    else
+      seq += t.npages;
     // the partial-sum slot i % 4 was last used by instruction i - 4
     if (!wait_lds_ge(a, L, &L->c.done_seq, i - 3, ErrDrain, i)) return;
     for (int pg = 0; pg < t.npages; ++pg) {
@@ -485,7 +545,7 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
         const GemvIn gi = gemv_input(m, a.c);
         gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, &L->c.part[sl][cw][0], &L->c.ssp[sl][cw][0], release);
       } else if (op == OpAttn) {
-        attn_wave<HD>(src, m, a.c, cw, L->c.scratch[cw], cw == 0, cw == 0 ? tr : nullptr);
+        attn_wave<HD>(src, m, a.c, cw, L->c.scratch[set * kNW + cw], cw == 0, cw == 0 ? tr : nullptr);
       } else if (op == OpCombine) {
         combine_wave<HD>(m, a.c, cw, cw == 0 ? tr : nullptr);
       } else if (op == OpArgmax) {
@@ -502,7 +562,7 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw) {
 }
 
 template <int HD, bool MB, bool GLM = false>
-__global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
+__global__ void __launch_bounds__((LdsT<MB, GLM>::THREADS), 1) mk_megakernel(KArgs a) {
   typedef LdsT<MB, GLM> LT;
   __shared__ LT Ls;
   LDS LT* L = (LDS LT*)&Ls;
@@ -529,7 +589,7 @@ __global__ void __launch_bounds__(512, 1) mk_megakernel(KArgs a) {
     loader(a, L, w - 2);
   } else {
     __builtin_amdgcn_s_setprio(2);
-    compute<HD, LT>(a, L, w - 4);
+    compute<HD, LT>(a, L, (w - 4) % kNW, LT::SETS > 1 ? (w - 4) / kNW : 0);
   }
 }
 
@@ -609,17 +669,19 @@ namespace mk {
 
 hipError_t launch_megakernel(const KArgs& a, int num_cus, hipStream_t s) {
   if (a.c.glm) {
-    hipLaunchKernelGGL((mk_megakernel<64, true, true>), dim3(num_cus), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((mk_megakernel<64, true, true>), dim3(num_cus), dim3(LdsT<true, true>::THREADS), 0, s, a);
   } else if (a.c.B == 1) {
+    constexpr int T = LdsT<false>::THREADS;
     if (a.c.hd == 64)
-      hipLaunchKernelGGL((mk_megakernel<64, false>), dim3(num_cus), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((mk_megakernel<64, false>), dim3(num_cus), dim3(T), 0, s, a);
     else
-      hipLaunchKernelGGL((mk_megakernel<128, false>), dim3(num_cus), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((mk_megakernel<128, false>), dim3(num_cus), dim3(T), 0, s, a);
   } else {
+    constexpr int T = LdsT<true>::THREADS;
     if (a.c.hd == 64)
-      hipLaunchKernelGGL((mk_megakernel<64, true>), dim3(num_cus), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((mk_megakernel<64, true>), dim3(num_cus), dim3(T), 0, s, a);
     else
-      hipLaunchKernelGGL((mk_megakernel<128, true>), dim3(num_cus), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((mk_megakernel<128, true>), dim3(num_cus), dim3(T), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -644,7 +706,8 @@ hipError_t launch_layer(const KArgs& a, int num_cus, int first_task, int ntasks,
 hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu) {
   const void* f = glm ? (const void*)mk_megakernel<64, true, true>
                       : (batch == 1 ? megakernel_fn<false>(hd) : megakernel_fn<true>(hd));
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, 512, 0);
+  const int threads = glm ? LdsT<true, true>::THREADS : (batch == 1 ? LdsT<false>::THREADS : LdsT<true>::THREADS);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, threads, 0);
 }
 
 int ring_pages(int batch) { return batch == 1 ? LdsT<false>::NP : LdsT<true>::NP; }
