@@ -208,12 +208,20 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
     if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, i + 2);
     if (m.w(WWaitCnt) && !(m.w(WWaitEv) == seen_ev && (int)(seen_val - a.epoch * (unsigned)m.w(WWaitTgt)) >= 0)) {
       const unsigned tgt = a.epoch * (unsigned)m.w(WWaitTgt);
-      // lane k < kCtrSub reads sub-counter k; the event's count is their sum
-      const int k = lane_id() < kCtrSub ? lane_id() : 0;
+      // lane l reads sub-counters l, l + 64, ... (below kCtrSub); the event's
+      // count is their sum
+      const int lane = lane_id();
+      const int k = lane < kCtrSub ? lane : 0;
       unsigned* ctr = a.counters + ctr_word(m.w(WWaitEv), k, a.num_events);
+      const size_t step = ctr_word(0, 64, a.num_events);  // words from sub-counter k to k + 64
       auto count = [&]() {
-        const unsigned x = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return row0_sum_u32(lane_id() < kCtrSub ? x : 0u);
+        unsigned x[kCtrPer];
+#pragma unroll
+        for (int j = 0; j < kCtrPer; ++j) x[j] = __hip_atomic_load(ctr + j * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned s = 0;
+#pragma unroll
+        for (int j = 0; j < kCtrPer; ++j) s += x[j];
+        return ctr_sum_u32(lane < kCtrSub ? s : 0u);
       };
       unsigned v = count();
       if ((int)(v - tgt) < 0) {
