@@ -78,12 +78,15 @@ constexpr int kCtrStride = 64;  // u32 words between event counters: one 256-byt
 // adds of one event's many producers do not serialize on one line: the adds of
 // one line are applied one after another at the memory side, and the waiters'
 // polls queue behind them (Llama-1B batch 1: 16 lines 883 us, 32 845, 64 828).
-// Sub-counter k of event e is word ctr_word(e, k, E) of the counter buffer.
+// Sub-counter k of event e is word ctr_word(e, k, E) of the counter buffer: an
+// event's lines are contiguous (one 16 KiB block), so a poll touches one small
+// range (Llama-1B 830 -> 807 us against the lines of one k being contiguous).
 constexpr int kCtrSub = 64;
 constexpr int kCtrPer = kCtrSub > 64 ? kCtrSub / 64 : 1;  // sub-counters a polling lane reads
 static_assert(kCtrSub <= 64 || kCtrSub % 64 == 0, "sub-counters: up to 64, or a multiple of 64");
 __host__ __device__ inline size_t ctr_word(int e, int k, int num_events) {
-  return ((size_t)k * num_events + e) * kCtrStride;
+  (void)num_events;
+  return ((size_t)e * kCtrSub + k) * kCtrStride;
 }
 
 struct Consts {
@@ -97,7 +100,7 @@ struct Consts {
 struct KArgs {
   const int* queue;           // [C][max_len][32]
   const uint64_t* optab;      // [num_ops][16]
-  unsigned* counters;         // [kCtrSub][num_events] lines (ctr_word)
+  unsigned* counters;         // [num_events][kCtrSub] lines (ctr_word)
   int num_events;
   unsigned* err;              // watchdog record [8]
   unsigned long long* trace;  // [C][max_len][kTraceWords] or null
