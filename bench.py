@@ -308,7 +308,8 @@ def main():
                       str(int(inp["kv_len"][0])) if cfg["batch"] == 1 else "%d..%d" % (min(inp["kv_len"]), max(inp["kv_len"])),
                       cfg["n_layers"], cfg["hidden"]),
                    "batch": int(cfg["batch"]), "kv_len": [int(k) for k in inp["kv_len"]],
-                   "persistent_grid": "%d workgroups x 512 threads" % plan.export()["num_cus"]},
+                   "persistent_grid": "%d workgroups x %d threads" % (plan.export()["num_cus"],
+                                                                      512 if cfg["batch"] == 1 else 768)},
         "algorithmic_bytes": nbytes,
         "achieved_GBps": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
