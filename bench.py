@@ -181,6 +181,14 @@ def bench_glm(args):
             res["lw_graph_warm"] = time_launches(
                 capture(lambda s: plans[0].run(ws[0], caches, xr, stream=s, layerwise=True)), stream,
                 args.steps, args.warmup)
+            # the pages' strongest baseline: graph + the independent branches on
+            # streams of their own (QKV-A / gate / indexer-K; QKV-B / indexer-Q)
+            print("[bench] timing layerwise as a captured graph with branch streams", file=sys.stderr, flush=True)
+            pms = mk.Plan.build(cfg, M, inp["pos"], cap, lw_streams=3)
+            res["lw_graph_ms_warm"] = time_launches(
+                capture(lambda s: pms.run(ws[0], caches, xr, stream=s, layerwise=True)), stream,
+                args.steps, args.warmup)
+            pms.free()
         if not lw:
             st, chk = plans[0].check()
             if st != mk.MK_OK or not chk.counters_ok:
@@ -211,6 +219,9 @@ def bench_glm(args):
         out["speedup_vs_layerwise_warm"] = round(res["lw_warm"]["median"] / res["mk_warm"]["median"], 3)
     if "mk_warm" in res and "lw_graph_warm" in res:
         out["speedup_vs_layerwise_graph_warm"] = round(res["lw_graph_warm"]["median"] / res["mk_warm"]["median"], 3)
+    if "mk_warm" in res and "lw_graph_ms_warm" in res:
+        out["speedup_vs_layerwise_graph_branches_warm"] = round(
+            res["lw_graph_ms_warm"]["median"] / res["mk_warm"]["median"], 3)
     if not args.no_cpu_baseline:
         from oracle import glm as G
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -113,12 +113,21 @@ typedef struct {
  *   (1 to 3, default 1): the event polls and activation reads that carry the
  *   dependency chain share the compute unit's vector-memory queue with the page
  *   DMA, so a shallow DMA backlog is faster (Llama-1B 886 / 895 / 915 us at 1 /
- *   2 / 3).  Does not change the plan's schedule metadata. */
+ *   2 / 3).  Does not change the plan's schedule metadata.
+ * lw_streams: streams of mk_run_layerwise (0 or 1: every launch on the caller's
+ *   stream; 2 or 3: independent branches of the op graph -- the GLM path's QKV-A,
+ *   head gate and indexer-K after A0, QKV-B and indexer-Q after the q-path norm --
+ *   on streams of their own, forked from and joined back into the caller's stream
+ *   with events, also under stream capture; a chain, like the Llama-family
+ *   graph, stays on one stream).  Eager GLM steps are slower with branches (the
+ *   event hand-offs cost more than the branches overlap); captured in a graph
+ *   they time the same as one stream. */
 typedef struct {
   int32_t num_cus, gemv_rows, gateup_outs, down_rows, lm_rows, attn_splits;
   int32_t timeout_ms;
   int32_t dma_pages;
-  int32_t reserved[4];
+  int32_t lw_streams;
+  int32_t reserved[3];
 } mk_plan_opts;
 
 /* Build the static tile plan of one decode step (host-only arithmetic; uploads

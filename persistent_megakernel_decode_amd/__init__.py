@@ -51,7 +51,7 @@ class ModelDesc(ctypes.Structure):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", i32), ("gemv_rows", i32), ("gateup_outs", i32), ("down_rows", i32), ("lm_rows", i32),
-                ("attn_splits", i32), ("timeout_ms", i32), ("dma_pages", i32), ("reserved", i32 * 4)]
+                ("attn_splits", i32), ("timeout_ms", i32), ("dma_pages", i32), ("lw_streams", i32), ("reserved", i32 * 3)]
 
 
 class GraphOp(ctypes.Structure):

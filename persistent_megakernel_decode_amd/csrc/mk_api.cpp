@@ -51,6 +51,14 @@ struct mk_plan {
   mk::ModelOpts opts{};
   std::vector<mk::GraphOp> ops;
   std::vector<int> op_first, op_count;
+  // layerwise baseline: an op's producers, and the stream it is launched on
+  // (0: the caller's; branches of the op graph get streams of their own)
+  std::vector<std::vector<int>> op_prod;
+  std::vector<int> op_stream;
+  int n_streams = 1;
+  std::vector<hipStream_t> xs;      // [n_streams], xs[0] unused (the caller's stream)
+  std::vector<hipEvent_t> op_done;  // one per op
+  hipEvent_t ev_fork = nullptr;
   mkd::Consts c{};
   int num_cus = 0;
   unsigned long long timeout_ticks = 0;
@@ -101,12 +109,54 @@ static mk_status finish_plan_common(mk_plan* p) {
   return MK_OK;
 }
 
+// Streams of the layerwise baseline: an op continues the stream whose last op is
+// one of its producers; otherwise it opens another stream (up to 3), so the
+// independent branches of the op graph (the GLM path's QKV-A / gate / indexer-K
+// after A0, QKV-B / indexer-Q after the q-path norm) run concurrently.  A plain
+// chain (the Llama-family graph) stays on the caller's stream.
+static void assign_streams(mk_plan* p, const std::vector<mk::GraphEdge>& edges, int max_streams) {
+  const int n = (int)p->ops.size();
+  const int kMaxStreams = std::max(1, std::min(3, max_streams));
+  p->op_prod.assign(n, {});
+  for (const auto& e : edges) {
+    auto& v = p->op_prod[e.cons];
+    if (std::find(v.begin(), v.end(), e.prod) == v.end()) v.push_back(e.prod);
+  }
+  p->op_stream.assign(n, 0);
+  std::vector<int> tail(3, -1);
+  int used = 1;
+  for (int o = 0; o < n; ++o) {
+    int st = -1;
+    for (int q : p->op_prod[o])
+      if (tail[p->op_stream[q]] == q) {
+        st = p->op_stream[q];
+        break;
+      }
+    if (st < 0) {
+      if (p->op_prod[o].empty() || used == kMaxStreams) {
+        // no producer (the first op), or all streams taken: the stream whose
+        // last op finished earliest in program order
+        st = 0;
+        for (int k = 1; k < used; ++k)
+          if (tail[k] < tail[st]) st = k;
+        if (p->op_prod[o].empty() && tail[0] < 0) st = 0;
+      } else {
+        st = used++;
+      }
+    }
+    p->op_stream[o] = st;
+    tail[st] = o;
+  }
+  p->n_streams = used;
+}
+
 static mk_status resolve_cus(const mk_plan_opts* opts, int* num_cus, int* timeout_ms, int* dma_pages) {
   *num_cus = opts ? opts->num_cus : 0;
   if (opts && opts->timeout_ms > 0) *timeout_ms = opts->timeout_ms;
   if (opts && (opts->dma_pages < 0 || opts->dma_pages > 3))
     return fail(MK_E_INVALID, "dma_pages must be 0 (default), 1, 2 or 3");
   if (opts && opts->dma_pages > 0) *dma_pages = opts->dma_pages;
+  if (opts && (opts->lw_streams < 0 || opts->lw_streams > 3)) return fail(MK_E_INVALID, "lw_streams must be 0..3");
   if (*num_cus <= 0) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -170,6 +220,7 @@ static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_
     return fail(MK_E_UNSUPPORTED, "planner: " + err);
   }
   finish_plan_common(p);
+  assign_streams(p, edges, opts ? opts->lw_streams : 1);
   p->num_cus = ncu;
   mkd::Consts& c = p->c;
   c.glm = 1;
@@ -256,6 +307,10 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
       return fail(MK_E_INVALID, "dma_pages must be 0 (default), 1, 2 or 3");
     }
     if (opts->dma_pages > 0) p->dma_pages = opts->dma_pages;
+    if (opts->lw_streams < 0 || opts->lw_streams > 3) {
+      delete p;
+      return fail(MK_E_INVALID, "lw_streams must be 0..3");
+    }
   }
   if (o.num_cus <= 0) {
     int dev = 0, n = 0;
@@ -308,6 +363,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     return fail(MK_E_UNSUPPORTED, "planner: " + err);
   }
   finish_plan_common(p);
+  assign_streams(p, edges, opts ? opts->lw_streams : 1);
   for (size_t k = 0; k < p->ops.size(); ++k)
     if (p->op_first[k] < 0) {
       delete p;
@@ -707,8 +763,36 @@ mk_status mk_run_layerwise(mk_plan* p, const mk_weights* w, void* kv_cache, cons
   if (st != MK_OK) return st;
   mkd::KArgs a = kargs(p);
   a.trace = nullptr;
-  for (size_t o = 0; o < p->ops.size(); ++o)
-    HIPCHK(mk::launch_layer(a, p->num_cus, p->op_first[o], p->op_count[o], s), "layer launch");
+  if (p->n_streams == 1) {
+    for (size_t o = 0; o < p->ops.size(); ++o)
+      HIPCHK(mk::launch_layer(a, p->num_cus, p->op_first[o], p->op_count[o], s), "layer launch");
+    return MK_OK;
+  }
+  // branches on streams of their own: fork from the caller's stream, wait on
+  // each producer launched elsewhere, join every stream back at the end (the
+  // same pattern is valid under stream capture)
+  if (p->xs.empty()) {
+    p->xs.assign(p->n_streams, nullptr);
+    for (int k = 1; k < p->n_streams; ++k) HIPCHK(hipStreamCreateWithFlags(&p->xs[k], hipStreamNonBlocking), "stream");
+    p->op_done.assign(p->ops.size(), nullptr);
+    for (auto& e : p->op_done) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming), "event");
+    HIPCHK(hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming), "event");
+  }
+  auto stream_of = [&](int k) { return k == 0 ? s : p->xs[k]; };
+  HIPCHK(hipEventRecord(p->ev_fork, s), "fork");
+  for (int k = 1; k < p->n_streams; ++k) HIPCHK(hipStreamWaitEvent(p->xs[k], p->ev_fork, 0), "fork wait");
+  std::vector<int> tail(p->n_streams, -1);
+  for (size_t o = 0; o < p->ops.size(); ++o) {
+    const int k = p->op_stream[o];
+    hipStream_t so = stream_of(k);
+    for (int q : p->op_prod[o])
+      if (p->op_stream[q] != k) HIPCHK(hipStreamWaitEvent(so, p->op_done[q], 0), "wait producer");
+    HIPCHK(mk::launch_layer(a, p->num_cus, p->op_first[o], p->op_count[o], so), "layer launch");
+    HIPCHK(hipEventRecord(p->op_done[o], so), "op done");
+    tail[k] = (int)o;
+  }
+  for (int k = 1; k < p->n_streams; ++k)
+    if (tail[k] >= 0) HIPCHK(hipStreamWaitEvent(s, p->op_done[tail[k]], 0), "join");
   return MK_OK;
 }
 
@@ -841,6 +925,11 @@ void mk_plan_free(mk_plan* p) {
     if (p->d_rows) (void)hipFree(p->d_rows);
   }
   if (p->d_trace) (void)hipFree(p->d_trace);
+  for (size_t k = 1; k < p->xs.size(); ++k)
+    if (p->xs[k]) (void)hipStreamDestroy(p->xs[k]);
+  for (auto e : p->op_done)
+    if (e) (void)hipEventDestroy(e);
+  if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
   delete p;
 }
 

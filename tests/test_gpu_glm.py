@@ -48,7 +48,7 @@ def codes_match(g_codes, o_codes, quotient):
 
 
 class GlmCase:
-    def __init__(self, name, norm_sigma=0.1):
+    def __init__(self, name, norm_sigma=0.1, **opts):
         mk = _mk()
         self.inp = synth.make_glm_inputs(name, norm_sigma=norm_sigma)
         self.cfg = cfg = self.inp["cfg"]
@@ -57,7 +57,7 @@ class GlmCase:
         self.M = len(self.inp["pos"])
         self.w = mk.GlmDeviceWeights(self.inp["weights"])
         self.xr = mk.glm_inputs_to_device(self.inp["x"], self.inp["r"])
-        self.plan = mk.Plan.build(cfg, self.M, self.inp["pos"], self.cap)
+        self.plan = mk.Plan.build(cfg, self.M, self.inp["pos"], self.cap, **opts)
 
     def run(self, layerwise=False):
         mk = _mk()
@@ -180,3 +180,40 @@ def test_gpu_glm_full_size():
         assert chk.counters_ok == 1
         for k in ("q", "qidx", "gate", "kv_cache", "idx_cache"):
             assert np.array_equal(g[k], g2[k]), k
+
+
+@pytest.mark.timeout(600)
+def test_gpu_glm_layerwise_branches_graph_replay():
+    """The layerwise baseline runs the graph's independent branches (QKV-A /
+    gate / indexer-K, then QKV-B / indexer-Q) on streams of their own, forked
+    from and joined back into the caller's stream: eager and captured-graph
+    replays (with eager work in between) match the eager layerwise result bit for
+    bit on every output."""
+    mk = _mk()
+    case = GlmCase("glm_tiny", lw_streams=3)
+    st, chk, ref = case.run(layerwise=True)
+    case.assert_parity(st, chk, ref, layerwise=True)
+    tiny = case
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    caches = mk.glm_caches_to_device(tiny.inp["kv_cache"], tiny.inp["idx_cache"])
+    with torch.cuda.stream(s):
+        tiny.plan.run(tiny.w, caches, tiny.xr, stream=s, layerwise=True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("  capture GLM layerwise", flush=True)
+    with torch.cuda.graph(g, stream=s):
+        tiny.plan.run(tiny.w, caches, tiny.xr, stream=s, layerwise=True)
+    torch.cuda.synchronize()
+    for k in range(3):
+        print("  replay %d" % k, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for key, which in (("q", mk.MK_OUT_GLM_Q), ("qidx", mk.MK_OUT_GLM_QIDX), ("gate", mk.MK_OUT_GLM_GATE),
+                           ("qkva", mk.MK_OUT_GLM_QKVA)):
+            t = tiny.plan.output(which).cpu().numpy()
+            got = t.view(np.uint16) if t.dtype == np.int16 else t
+            assert np.array_equal(got, ref[key]), (k, key)
+        tiny.run()  # eager megakernel work between replays
+        torch.ones(1 << 20, device="cuda").sum().item()
+        torch.cuda.synchronize()
