@@ -234,6 +234,32 @@ mk_status mk_run(mk_plan* plan, const mk_weights* weights, void* kv_cache, const
 mk_status mk_run_layerwise(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens,
                            void* stream);
 
+/* Move a Llama-family plan to new sequence lengths (the next decode step)
+ * without replanning (MegaRTP article, §三/§四: a plan is regenerated only when
+ * tile counts or thresholds change).  Only the attention tasks' payloads (split
+ * ranges and the new position) and the RoPE table depend on the lengths; the
+ * queue's shape, events and targets do not, and counters stay epoch-based.
+ * kv_len: host int32 [batch], each kv_len[b] + 1 <= max_kv_len.  If the plan has
+ * run, the patch is enqueued on stream (a copy from pinned host memory and a
+ * small kernel that rewrites the words in the device queue) before any later
+ * work on that stream; otherwise the first run uploads the patched plan.
+ * mk_plan_export shows the new payloads.  Errors: MK_E_INVALID (null),
+ * MK_E_STATE (graph-only plan), MK_E_UNSUPPORTED (GLM plan, a length past the
+ * capacity, or an attention split that no longer fits the LDS page ring:
+ * build a new plan), MK_E_HIP. */
+mk_status mk_plan_set_kv_len(mk_plan* plan, const int32_t* kv_len, void* stream);
+
+/* n_steps decode steps back to back on stream: step k runs at lengths
+ * kv_len + k (kv_len: the plan's current lengths), writes its K/V rows at those
+ * positions, and reads as its tokens those of step k - 1's argmax (step 0:
+ * tokens, device int32 [batch]; the plan keeps its own copy).  out_tokens
+ * (device int32 [n_steps][batch], or null) receives every step's next tokens.
+ * layerwise != 0 runs each step as mk_run_layerwise does.  Afterwards the plan
+ * is at the last step's lengths and its outputs are the last step's.
+ * Errors: as mk_run and mk_plan_set_kv_len; MK_E_INVALID for n_steps < 1. */
+mk_status mk_run_steps(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens,
+                       int32_t n_steps, void* out_tokens, int32_t layerwise, void* stream);
+
 /* Device pointer and size of a plan output:
  * MK_OUT_LOGITS fp32 [batch][vocab]; MK_OUT_NEXT_TOKEN int32 [batch];
  * MK_OUT_QKV fp32 [n_layers] slices of [batch][n_kv_heads][(n_q/n_kv + 2) *

@@ -36,7 +36,7 @@ GLM_SLOTS = ("attn_norm", "w_qkva", "s_qkva", "w_gate", "s_gate", "w_idxk", "s_i
 LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_plan_export", "mk_run",
             "mk_run_layerwise", "mk_plan_output", "mk_plan_copy_output", "mk_plan_check", "mk_plan_set_trace",
-            "mk_plan_trace", "mk_plan_free")
+            "mk_plan_trace", "mk_plan_free", "mk_plan_set_kv_len", "mk_run_steps")
 
 i32, u32, f32, vp, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -102,6 +102,8 @@ def lib():
         L.mk_plan_export.argtypes = [vp, P(PlanView)]
         L.mk_run.argtypes = [vp, P(Weights), vp, vp, vp]
         L.mk_run_layerwise.argtypes = [vp, P(Weights), vp, vp, vp]
+        L.mk_plan_set_kv_len.argtypes = [vp, vp, vp]
+        L.mk_run_steps.argtypes = [vp, P(Weights), vp, vp, i32, vp, i32, vp]
         L.mk_plan_output.argtypes = [vp, i32, P(vp), P(sz)]
         L.mk_plan_copy_output.argtypes = [vp, i32, vp, sz, vp]
         L.mk_plan_check.argtypes = [vp, vp, P(Check)]
@@ -208,6 +210,25 @@ class Plan:
 
     def run_layerwise(self, weights, kv_cache, tokens, stream=None):
         self.run(weights, kv_cache, tokens, stream, layerwise=True)
+
+    def set_kv_len(self, kv_len, stream=None):
+        """mk_plan_set_kv_len: the next step's sequence lengths, without replanning."""
+        import torch
+        kv = np.ascontiguousarray(kv_len, dtype=np.int32)
+        if stream is not None:
+            s = vp(stream.cuda_stream)
+        else:  # a plan that has not run needs no stream (host-side patch only)
+            s = vp(current_stream() if torch.cuda.is_available() else 0)
+        _check(lib().mk_plan_set_kv_len(self._h, kv.ctypes.data, s))
+
+    def run_steps(self, weights, kv_cache, tokens, n_steps, out_tokens=None, stream=None, layerwise=False):
+        """mk_run_steps: n_steps decode steps, each fed the previous step's argmax;
+        out_tokens: a device int32 tensor of n_steps * batch elements, or None."""
+        w = weights.struct if isinstance(weights, (DeviceWeights, GlmDeviceWeights)) else weights
+        s = vp(stream.cuda_stream if stream is not None else current_stream())
+        o = vp(out_tokens.data_ptr()) if out_tokens is not None else vp(0)
+        _check(lib().mk_run_steps(self._h, ctypes.byref(w), vp(kv_cache.data_ptr()), vp(tokens.data_ptr()),
+                                  int(n_steps), o, 1 if layerwise else 0, s))
 
     def output(self, which):
         """Copy an output into a new flat torch tensor (on the current stream):

@@ -22,6 +22,7 @@ hipError_t launch_megakernel(const mkd::KArgs& a, int num_cus, hipStream_t s);
 hipError_t launch_layer(const mkd::KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s);
 hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu);
 int ring_pages(int batch);
+hipError_t launch_patch_queue(int* queue, const void* patches, int n, hipStream_t s);
 }  // namespace mk
 
 namespace {
@@ -78,6 +79,19 @@ struct mk_plan {
   unsigned epoch = 0;
   bool need_reset = false;
   std::vector<uint64_t> h_optab;
+  // new sequence lengths without replanning: the attention tasks' first words
+  // in the queue, their payload patches (device and host staging) and the
+  // host RoPE table
+  std::vector<int> attn_words;
+  int* d_patch = nullptr;
+  std::vector<float> h_rope;
+  // staging of a run of steps: pinned host buffer and its device copy, per step
+  // the attention patches then the RoPE table; an event marks the last upload
+  char* h_steps = nullptr;
+  char* d_steps = nullptr;
+  size_t steps_cap = 0;
+  hipEvent_t ev_steps = nullptr;
+  int32_t* d_tok = nullptr;  // tokens of a run of steps (the previous step's next tokens)
   // workspace offsets (bytes)
   size_t off_qkv = 0, off_part = 0, off_ao = 0, off_hidden = 0, off_act = 0, off_logits = 0, off_lmmax = 0,
          off_next = 0;
@@ -364,6 +378,8 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   }
   finish_plan_common(p);
   assign_streams(p, edges, opts ? opts->lw_streams : 1);
+  for (size_t t = 0; t * 32 < p->P.queue.size(); ++t)
+    if (p->P.queue[t * 32 + mkd::WOpcode] == mkd::OpAttn) p->attn_words.push_back((int)(t * 32));
   for (size_t k = 0; k < p->ops.size(); ++k)
     if (p->op_first[k] < 0) {
       delete p;
@@ -487,6 +503,20 @@ static size_t counter_bytes(const mk_plan* p) {
   return (size_t)mkd::kCtrSub * std::max(1, p->P.num_events) * mkd::kCtrStride * 4;
 }
 
+// RoPE table (cos, sin) at each sequence's (GLM: token row's) new position,
+// computed in fp64; rotate-half over the rope width
+static void rope_table(mk_plan* p) {
+  const int rope_w = p->glm ? p->c.rd : p->c.hd;
+  p->h_rope.assign((size_t)p->batch * rope_w, 0.f);
+  const int half = rope_w / 2;
+  for (int b = 0; b < p->batch; ++b)
+    for (int i = 0; i < half; ++i) {
+      double ang = (double)p->kv_len[b] * std::pow((double)p->desc.rope_theta, -2.0 * i / rope_w);
+      p->h_rope[(size_t)b * rope_w + 2 * i] = (float)std::cos(ang);
+      p->h_rope[(size_t)b * rope_w + 2 * i + 1] = (float)std::sin(ang);
+    }
+}
+
 static mk_status ensure_device(mk_plan* p) {
   if (p->uploaded) {
     int dev = -1;
@@ -514,17 +544,11 @@ static mk_status ensure_device(mk_plan* p) {
   HIPCHK(hipMemset(p->d_counters, 0, ebytes), "zero counters");
   HIPCHK(hipMemset(p->d_err, 0, 64), "zero err");
   HIPCHK(hipMemset(p->d_ws, 0xFF, p->ws_bytes), "poison workspace");  // NaN until written
-  // RoPE table (cos, sin) at each sequence's (GLM: token row's) new position,
-  // computed in fp64; rotate-half over rope_w dims
-  std::vector<float> rope((size_t)p->batch * rope_w);
-  const int half = rope_w / 2;
-  for (int b = 0; b < p->batch; ++b)
-    for (int i = 0; i < half; ++i) {
-      double ang = (double)p->kv_len[b] * std::pow((double)p->desc.rope_theta, -2.0 * i / rope_w);
-      rope[(size_t)b * rope_w + 2 * i] = (float)std::cos(ang);
-      rope[(size_t)b * rope_w + 2 * i + 1] = (float)std::sin(ang);
-    }
-  HIPCHK(hipMemcpy(p->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice), "upload rope");
+  rope_table(p);
+  HIPCHK(hipMemcpy(p->d_rope, p->h_rope.data(), p->h_rope.size() * 4, hipMemcpyHostToDevice), "upload rope");
+  if (!p->glm) {
+    HIPCHK(hipMalloc(&p->d_patch, std::max<size_t>(1, p->attn_words.size()) * 16), "hipMalloc patches");
+  }
   if (p->glm) {
     // token rows: cache position, then request
     std::vector<int32_t> rows(2 * (size_t)p->batch);
@@ -715,6 +739,9 @@ static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const 
   return upload_optab(p, t, s);
 }
 
+static mk_status launch_step(mk_plan* p, hipStream_t s);
+static mk_status launch_layerwise(mk_plan* p, hipStream_t s);
+
 static mkd::KArgs kargs(const mk_plan* p) {
   mkd::KArgs a{};
   a.queue = p->d_queue;
@@ -740,6 +767,10 @@ mk_status mk_run(mk_plan* p, const mk_weights* w, void* kv_cache, const void* to
   if (st != MK_OK) return st;
   st = bind_operands(p, w, kv_cache, tokens, s);
   if (st != MK_OK) return st;
+  return launch_step(p, s);
+}
+
+static mk_status launch_step(mk_plan* p, hipStream_t s) {
   if (p->need_reset) {
     HIPCHK(hipMemsetAsync(p->d_counters, 0, counter_bytes(p), s), "reset counters");
     p->epoch = 0;
@@ -761,6 +792,10 @@ mk_status mk_run_layerwise(mk_plan* p, const mk_weights* w, void* kv_cache, cons
   if (st != MK_OK) return st;
   st = bind_operands(p, w, kv_cache, tokens, s);
   if (st != MK_OK) return st;
+  return launch_layerwise(p, s);
+}
+
+static mk_status launch_layerwise(mk_plan* p, hipStream_t s) {
   mkd::KArgs a = kargs(p);
   a.trace = nullptr;
   if (p->n_streams == 1) {
@@ -795,6 +830,143 @@ mk_status mk_run_layerwise(mk_plan* p, const mk_weights* w, void* kv_cache, cons
     if (tail[k] >= 0) HIPCHK(hipStreamWaitEvent(s, p->op_done[tail[k]], 0), "join");
   return MK_OK;
 }
+
+// ---- new sequence lengths without replanning; runs of steps -------------------
+// A step at lengths kv differs from the planned one only in the attention
+// tasks' payloads (split ranges and position) and the RoPE table: the queue's
+// shape, events and targets do not depend on the lengths.
+static mk_status check_lengths(const mk_plan* p, const std::vector<int32_t>& kv) {
+  if (p->graph_only) return fail(MK_E_STATE, "graph-only plans have no sequence lengths");
+  if (p->glm) return fail(MK_E_UNSUPPORTED, "the GLM path's token positions are fixed by its plan");
+  const mk_model_desc& d = p->desc;
+  int maxpos = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    if (kv[b] < 0 || kv[b] + 1 > d.max_kv_len) return fail(MK_E_UNSUPPORTED, "kv_len[b] + 1 must be <= max_kv_len");
+    maxpos = std::max(maxpos, kv[b] + 1);
+  }
+  const long ring = (long)mk::ring_pages(p->batch) * mkd::kPage;
+  const long rows = mk::ceil_div(maxpos, p->opts.attn_splits);
+  if ((rows * d.head_dim * 2 + 1023) / 1024 * 1024 * 2 > ring)
+    return fail(MK_E_UNSUPPORTED, "an attention split no longer fits the LDS page ring: build a new plan");
+  return MK_OK;
+}
+
+// Host side: patch the queue copy and the RoPE table for lengths kv; write the
+// attention patches (word index, lo, hi, pos) to out (4 int32 each) if given.
+static void apply_lengths(mk_plan* p, const std::vector<int32_t>& kv, int32_t* out) {
+  p->kv_len = kv;
+  const int S = p->opts.attn_splits;
+  for (size_t j = 0; j < p->attn_words.size(); ++j) {
+    int32_t* w = &p->P.queue[p->attn_words[j]];
+    const int b = w[mkd::WGx], sp = w[mkd::WGz], pos = kv[b];
+    int lo = 0, hi = 0;
+    mk::split_range(pos, S, sp, &lo, &hi);
+    w[mkd::WPay] = lo;
+    w[mkd::WPay + 1] = hi;
+    w[mkd::WPay + 2] = pos;
+    if (out) {
+      out[4 * j] = p->attn_words[j] + mkd::WPay;
+      out[4 * j + 1] = lo;
+      out[4 * j + 2] = hi;
+      out[4 * j + 3] = pos;
+    }
+  }
+  rope_table(p);
+}
+
+// Stage n steps at lengths kv + k (k = 0 .. n-1) in pinned host memory and copy
+// them to the device on stream s; the host state ends at the last step's lengths.
+static mk_status stage_steps(mk_plan* p, const std::vector<int32_t>& kv, int n, hipStream_t s, size_t* step_bytes) {
+  const size_t pbytes = p->attn_words.size() * 16, rbytes = p->h_rope.size() * 4;
+  const size_t per = (pbytes + rbytes + 255) / 256 * 256;
+  *step_bytes = per;
+  if (p->ev_steps) HIPCHK(hipEventSynchronize(p->ev_steps), "previous staging");  // host buffer reuse
+  if ((size_t)n * per > p->steps_cap) {
+    if (p->h_steps) HIPCHK(hipHostFree(p->h_steps), "hipHostFree");
+    if (p->d_steps) HIPCHK(hipFree(p->d_steps), "hipFree");
+    p->h_steps = nullptr;
+    p->d_steps = nullptr;
+    p->steps_cap = 0;
+    HIPCHK(hipHostMalloc((void**)&p->h_steps, (size_t)n * per, hipHostMallocDefault), "hipHostMalloc steps");
+    HIPCHK(hipMalloc((void**)&p->d_steps, (size_t)n * per), "hipMalloc steps");
+    p->steps_cap = (size_t)n * per;
+  }
+  if (!p->ev_steps) HIPCHK(hipEventCreateWithFlags(&p->ev_steps, hipEventDisableTiming), "event");
+  std::vector<int32_t> k_kv(kv);
+  for (int k = 0; k < n; ++k) {
+    for (int b = 0; b < p->batch; ++b) k_kv[b] = kv[b] + k;
+    char* h = p->h_steps + (size_t)k * per;
+    apply_lengths(p, k_kv, (int32_t*)h);
+    std::memcpy(h + pbytes, p->h_rope.data(), rbytes);
+  }
+  HIPCHK(hipMemcpyAsync(p->d_steps, p->h_steps, (size_t)n * per, hipMemcpyHostToDevice, s), "upload steps");
+  HIPCHK(hipEventRecord(p->ev_steps, s), "staging event");
+  return MK_OK;
+}
+
+// Step k of a staged run: patch the queue and install its RoPE table.
+static mk_status install_step(mk_plan* p, int k, size_t per, hipStream_t s) {
+  const char* d = p->d_steps + (size_t)k * per;
+  HIPCHK(mk::launch_patch_queue(p->d_queue, d, (int)p->attn_words.size(), s), "patch queue");
+  HIPCHK(hipMemcpyAsync(p->d_rope, d + p->attn_words.size() * 16, p->h_rope.size() * 4, hipMemcpyDeviceToDevice, s),
+         "install rope");
+  return MK_OK;
+}
+
+mk_status mk_plan_set_kv_len(mk_plan* p, const int32_t* kv_len, void* stream) {
+  g_err.clear();
+  if (!p || !kv_len) return fail(MK_E_INVALID, "null argument");
+  std::vector<int32_t> kv(kv_len, kv_len + std::max(0, p->batch));
+  mk_status st = check_lengths(p, kv);
+  if (st != MK_OK) return st;
+  if (!p->uploaded) {  // the first run uploads the patched queue and table
+    apply_lengths(p, kv, nullptr);
+    return MK_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  size_t per = 0;
+  st = stage_steps(p, kv, 1, s, &per);
+  if (st != MK_OK) return st;
+  return install_step(p, 0, per, s);
+}
+
+mk_status mk_run_steps(mk_plan* p, const mk_weights* w, void* kv_cache, const void* tokens, int32_t n_steps,
+                       void* out_tokens, int32_t layerwise, void* stream) {
+  g_err.clear();
+  if (!p) return fail(MK_E_INVALID, "null plan");
+  if (n_steps < 1) return fail(MK_E_INVALID, "n_steps must be >= 1");
+  std::vector<int32_t> last(p->kv_len);
+  for (auto& v : last) v += n_steps - 1;
+  mk_status st = check_lengths(p, last);
+  if (st != MK_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = ensure_device(p);
+  if (st != MK_OK) return st;
+  if (!p->d_tok) HIPCHK(hipMalloc((void**)&p->d_tok, (size_t)p->batch * 4), "hipMalloc tokens");
+  if (!tokens) return fail(MK_E_INVALID, "null token pointer");
+  HIPCHK(hipMemcpyAsync(p->d_tok, tokens, (size_t)p->batch * 4, hipMemcpyDeviceToDevice, s), "first tokens");
+  st = bind_operands(p, w, kv_cache, p->d_tok, s);
+  if (st != MK_OK) return st;
+  const std::vector<int32_t> first(p->kv_len);
+  size_t per = 0;
+  st = stage_steps(p, first, n_steps, s, &per);
+  if (st != MK_OK) return st;
+  const char* next = p->d_ws + p->off_next;
+  for (int k = 0; k < n_steps; ++k) {
+    if (k > 0) {
+      st = install_step(p, k, per, s);
+      if (st != MK_OK) return st;
+      HIPCHK(hipMemcpyAsync(p->d_tok, next, (size_t)p->batch * 4, hipMemcpyDeviceToDevice, s), "feed next tokens");
+    }
+    st = layerwise ? launch_layerwise(p, s) : launch_step(p, s);
+    if (st != MK_OK) return st;
+    if (out_tokens)
+      HIPCHK(hipMemcpyAsync((char*)out_tokens + (size_t)k * p->batch * 4, next, (size_t)p->batch * 4,
+                            hipMemcpyDeviceToDevice, s), "copy out tokens");
+  }
+  return MK_OK;
+}
+
 
 mk_status mk_plan_output(const mk_plan* p, int32_t which, void** dev_ptr, size_t* bytes) {
   g_err.clear();
@@ -923,6 +1095,9 @@ void mk_plan_free(mk_plan* p) {
     (void)hipFree(p->d_rope);
     (void)hipFree(p->d_ws);
     if (p->d_rows) (void)hipFree(p->d_rows);
+    if (p->d_patch) (void)hipFree(p->d_patch);
+    if (p->d_steps) (void)hipFree(p->d_steps);
+    if (p->d_tok) (void)hipFree(p->d_tok);
   }
   if (p->d_trace) (void)hipFree(p->d_trace);
   for (size_t k = 1; k < p->xs.size(); ++k)
@@ -930,6 +1105,8 @@ void mk_plan_free(mk_plan* p) {
   for (auto e : p->op_done)
     if (e) (void)hipEventDestroy(e);
   if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+  if (p->ev_steps) (void)hipEventDestroy(p->ev_steps);
+  if (p->h_steps) (void)hipHostFree(p->h_steps);
   delete p;
 }
 

@@ -720,4 +720,22 @@ hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu)
 
 int ring_pages(int batch) { return batch == 1 ? LdsT<false>::NP : LdsT<true>::NP; }
 
+// Rewrites the payload words of queued instructions in place: patch i =
+// (word index, three values) stores the values at queue[index .. index + 2].
+__global__ void mk_patch_queue(int* queue, const int4* patches, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const int4 p = patches[i];
+    queue[p.x] = p.y;
+    queue[p.x + 1] = p.z;
+    queue[p.x + 2] = p.w;
+  }
+}
+
+hipError_t launch_patch_queue(int* queue, const void* patches, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mk_patch_queue, dim3((n + 255) / 256), dim3(256), 0, s, queue, (const int4*)patches, n);
+  return hipGetLastError();
+}
+
 }  // namespace mk

@@ -260,3 +260,67 @@ def test_gpu_layerwise_graph_replay_matches_eager():
         case.plan.run(case.w, case.fresh_kv(), case.tokens)
         torch.ones(1 << 20, device="cuda").sum().item()
         torch.cuda.synchronize()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n", [("tiny", 5), ("llama1b", 3)])
+def test_gpu_run_steps_match_oracle_step_by_step(name, n):
+    """mk_run_steps: n decode steps back to back, each fed the previous step's
+    argmax, without replanning.  Every step's next token equals the oracle's
+    (the oracle run step by step on the same token sequence, with its own KV
+    cache), the last step's logits are within the bar, every new K/V row was
+    written and nothing else; the layerwise run of the same steps gives the same
+    tokens; afterwards the plan reports the last step's lengths."""
+    mk = _mk()
+    inp = synth.make_inputs(name, norm_sigma=0.0 if name == "llama1b" else 0.1)
+    cfg = inp["cfg"]
+    B, kv0 = cfg["batch"], inp["kv_len"]
+    cache = inp["kv_cache"]
+    assert cache.shape[4] >= int(kv0.max()) + n
+    w = mk.DeviceWeights(inp["weights"], cfg)
+    tok = mk.tokens_to_device(inp["tokens"])
+    plan = mk.Plan.build(cfg, B, kv0, cache.shape[4])
+    try:
+        got = {}
+        for lw in (False, True):
+            kv = mk.kv_to_device(cache)
+            plan.set_kv_len(kv0)
+            out = torch.empty(n * B, dtype=torch.int32, device="cuda")
+            print("  %s: %d steps, layerwise=%s" % (name, n, lw), flush=True)
+            plan.run_steps(w, kv, tok, n, out_tokens=out, layerwise=lw)
+            torch.cuda.synchronize()
+            if not lw:
+                st, chk = plan.check()
+                assert st == mk.MK_OK and chk.counters_ok == 1 and chk.err_kind == 0
+            got[lw] = dict(tokens=out.cpu().numpy().reshape(n, B),
+                           logits=plan.output(mk.MK_OUT_LOGITS).cpu().numpy().reshape(B, -1),
+                           kv=kv.cpu().view(torch.int16).numpy().view(np.uint16))
+        assert np.array_equal(got[False]["tokens"], got[True]["tokens"])
+        ex = plan.export()
+        att = ex["queue"].reshape(-1, 32)
+        att = att[att[:, 0] == 2]
+        assert set(att[:, 16].tolist()) <= set((kv0 + n - 1).tolist())  # attention payload: the new position
+        # the oracle, step by step on the GPU's token sequence
+        ocache = cache.copy()
+        toks = inp["tokens"]
+        for k in range(n):
+            ref = oracle.decode_step(dict(inp, kv_len=kv0 + k, tokens=toks), kv_cache=ocache)
+            print("  step %d: gpu %s oracle %s" % (k, got[False]["tokens"][k], ref["next"]), flush=True)
+            assert np.array_equal(got[False]["tokens"][k], ref["next"]), k
+            toks = got[False]["tokens"][k].astype(np.int32)
+        rel = np.linalg.norm(got[False]["logits"] - ref["logits"]) / np.linalg.norm(ref["logits"])
+        print("  last-step logits rel-L2 %.3g" % rel, flush=True)
+        assert rel <= LOGIT_TOL
+        # cache: rows kv0 .. kv0 + n - 1 written (within one bf16 step of the
+        # oracle's), every other byte untouched
+        mask = np.zeros(cache.shape, dtype=bool)
+        for b in range(B):
+            mask[:, :, b, :, int(kv0[b]):int(kv0[b]) + n, :] = True
+        g = got[False]["kv"]
+        assert np.array_equal(g[~mask], cache[~mask])
+        gv = oracle.bf16_to_f64(g[mask]).reshape(-1, cache.shape[-1])
+        ov = oracle.bf16_to_f64(ocache[mask]).reshape(-1, cache.shape[-1])
+        rms = np.sqrt(np.mean(ov * ov, axis=1, keepdims=True))
+        assert (np.abs(gv - ov) <= np.abs(ov) * 2.0 ** -7 + 1e-4 * rms).all()
+    finally:
+        plan.free()

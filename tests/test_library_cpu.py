@@ -173,3 +173,58 @@ def test_plan_build_rejects_bad_arguments():
     # an edge that goes backwards is rejected
     with pytest.raises(mk.MKError):
         mk.Plan.graph([(1, (4,)), (2, (4,))], [(1, 0, (0,), (0,), None, None, None)], 4)
+
+
+@pytest.mark.parametrize("name,num_cus,splits,shift", [("tiny", 37, 5, 3), ("llama1b_b16", 256, 4, 7),
+                                                        ("tiny", 256, 0, 9)])
+def test_set_kv_len_patches_match_a_fresh_plan(name, num_cus, splits, shift):
+    """Moving a plan to new sequence lengths (no device needed before its first
+    run) gives exactly the queue the planner builds for those lengths with the
+    same attention split count: only the attention payloads change."""
+    cfg = synth.config(name)
+    kv0 = synth.kv_lengths(cfg)
+    kv1 = kv0 + shift
+    cap = synth.kv_capacity(kv1)
+    plan = mk.Plan.build(cfg, cfg["batch"], kv0, cap, num_cus=num_cus, attn_splits=splits)
+    try:
+        ref0 = P.plan_model(cfg, cfg["batch"], kv0, dict(num_cus=num_cus, attn_splits=splits))
+        S = ref0.info["S"]
+        ref1 = P.plan_model(cfg, cfg["batch"], kv1, dict(num_cus=num_cus, attn_splits=S))
+        before = plan.export()["queue"].copy()
+        plan.set_kv_len(kv1)
+        after = plan.export()["queue"]
+        assert np.array_equal(after, np.asarray(ref1.queue, dtype=np.int32))
+        changed = np.nonzero((before != after).any(axis=2))
+        assert set(before[changed][:, 0]) <= {P.ATTN}
+    finally:
+        plan.free()
+
+
+def test_set_kv_len_rejections():
+    cfg = synth.config("tiny")
+    kv = synth.kv_lengths(cfg)
+    cap = synth.kv_capacity(kv)
+    plan = mk.Plan.build(cfg, 1, kv, cap, num_cus=8)
+    try:
+        with pytest.raises(mk.MKError) as e:
+            plan.set_kv_len(np.array([cap], np.int32))  # kv_len + 1 > capacity
+        assert e.value.status == mk.MK_E_UNSUPPORTED
+        with pytest.raises(mk.MKError) as e:  # a split past the ring: replan
+            small = mk.Plan.build(cfg, 1, [10], 100000, num_cus=8, attn_splits=1)
+            try:
+                small.set_kv_len(np.array([99000], np.int32))
+            finally:
+                small.free()
+        assert e.value.status == mk.MK_E_UNSUPPORTED and b"ring" in mk.lib().mk_last_error()
+        assert mk.lib().mk_plan_set_kv_len(plan._h, None, None) == mk.MK_E_INVALID
+    finally:
+        plan.free()
+    g = synth.config("glm_tiny")
+    pos, _ = synth.glm_positions(g)
+    gp = mk.Plan.build(g, len(pos), pos, synth.glm_capacity(g), num_cus=8)
+    try:
+        with pytest.raises(mk.MKError) as e:
+            gp.set_kv_len(pos + 1)
+        assert e.value.status == mk.MK_E_UNSUPPORTED
+    finally:
+        gp.free()
