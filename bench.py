@@ -285,6 +285,18 @@ def main():
         st, chk = plan.check()
         if st != mk.MK_OK or not chk.counters_ok:
             raise RuntimeError("megakernel check failed: %s" % mk.lib().mk_last_error().decode())
+        # a decode loop: 8 steps per call (mk_run_steps), each step's argmax fed to
+        # the next, the plan moved to each step's lengths without replanning
+        print("[bench] timing an 8-step decode loop", file=sys.stderr, flush=True)
+        kv_loop = mk.kv_to_device(inp["kv_cache"])
+        kv0 = inp["kv_len"]
+
+        def loop():
+            plan.set_kv_len(kv0)
+            plan.run_steps(w, kv_loop, tok, 8)
+        r = time_launches(loop, stream, max(2, args.steps // 8), 2)
+        res["mk_loop"] = {k: v / 8 for k, v in r.items()}
+        plan.set_kv_len(kv0)
     if args.only in ("layerwise", "both"):
         print("[bench] timing layerwise", file=sys.stderr, flush=True)
         res["lw"] = time_launches(lambda: plan.run_layerwise(w, kv, tok), stream, args.steps, args.warmup)
@@ -329,6 +341,10 @@ def main():
     }
     if "mk" in res:
         out["megakernel_us"] = {k: round(v, 2) for k, v in res["mk"].items()}
+    if "mk_loop" in res:
+        # per step of an 8-step mk_run_steps call (includes each step's queue
+        # patch, RoPE copy and token hand-over; per-step percentiles are of calls / 8)
+        out["decode_loop_us_per_step"] = {k: round(v, 2) for k, v in res["mk_loop"].items()}
     if "lw" in res:
         out["layerwise_us"] = {k: round(v, 2) for k, v in res["lw"].items()}
         lwl = res["lw"]["median"]

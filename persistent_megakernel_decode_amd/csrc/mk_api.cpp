@@ -22,7 +22,8 @@ hipError_t launch_megakernel(const mkd::KArgs& a, int num_cus, hipStream_t s);
 hipError_t launch_layer(const mkd::KArgs& a, int num_cus, int first_task, int ntasks, hipStream_t s);
 hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu);
 int ring_pages(int batch);
-hipError_t launch_patch_queue(int* queue, const void* patches, int n, hipStream_t s);
+hipError_t launch_step_setup(int* queue, const void* patches, int n, float* rope, const float* rope_src, int nr,
+                             int* tok, const int* next, int* out, int nt, hipStream_t s);
 }  // namespace mk
 
 namespace {
@@ -904,12 +905,15 @@ static mk_status stage_steps(mk_plan* p, const std::vector<int32_t>& kv, int n, 
   return MK_OK;
 }
 
-// Step k of a staged run: patch the queue and install its RoPE table.
-static mk_status install_step(mk_plan* p, int k, size_t per, hipStream_t s) {
+// Step k of a staged run: patch the queue and install its RoPE table; with
+// ntok > 0 also hand the previous step's next tokens to the token buffer (and
+// to out, if given) -- one launch.
+static mk_status install_step(mk_plan* p, int k, size_t per, hipStream_t s, int ntok = 0, int* out = nullptr) {
   const char* d = p->d_steps + (size_t)k * per;
-  HIPCHK(mk::launch_patch_queue(p->d_queue, d, (int)p->attn_words.size(), s), "patch queue");
-  HIPCHK(hipMemcpyAsync(p->d_rope, d + p->attn_words.size() * 16, p->h_rope.size() * 4, hipMemcpyDeviceToDevice, s),
-         "install rope");
+  HIPCHK(mk::launch_step_setup(p->d_queue, d, (int)p->attn_words.size(), p->d_rope,
+                               (const float*)(d + p->attn_words.size() * 16), (int)p->h_rope.size(), p->d_tok,
+                               (const int*)(p->d_ws + p->off_next), out, ntok, s),
+         "step set-up");
   return MK_OK;
 }
 
@@ -953,17 +957,17 @@ mk_status mk_run_steps(mk_plan* p, const mk_weights* w, void* kv_cache, const vo
   if (st != MK_OK) return st;
   const char* next = p->d_ws + p->off_next;
   for (int k = 0; k < n_steps; ++k) {
-    if (k > 0) {
-      st = install_step(p, k, per, s);
+    if (k > 0) {  // step k's lengths and RoPE; step k - 1's next tokens in, and out
+      int* out = out_tokens ? (int*)out_tokens + (size_t)(k - 1) * p->batch : nullptr;
+      st = install_step(p, k, per, s, p->batch, out);
       if (st != MK_OK) return st;
-      HIPCHK(hipMemcpyAsync(p->d_tok, next, (size_t)p->batch * 4, hipMemcpyDeviceToDevice, s), "feed next tokens");
     }
     st = layerwise ? launch_layerwise(p, s) : launch_step(p, s);
     if (st != MK_OK) return st;
-    if (out_tokens)
-      HIPCHK(hipMemcpyAsync((char*)out_tokens + (size_t)k * p->batch * 4, next, (size_t)p->batch * 4,
-                            hipMemcpyDeviceToDevice, s), "copy out tokens");
   }
+  if (out_tokens)
+    HIPCHK(hipMemcpyAsync((char*)out_tokens + (size_t)(n_steps - 1) * p->batch * 4, next, (size_t)p->batch * 4,
+                          hipMemcpyDeviceToDevice, s), "copy out tokens");
   return MK_OK;
 }
 

@@ -720,9 +720,13 @@ hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu)
 
 int ring_pages(int batch) { return batch == 1 ? LdsT<false>::NP : LdsT<true>::NP; }
 
-// Rewrites the payload words of queued instructions in place: patch i =
-// (word index, three values) stores the values at queue[index .. index + 2].
-__global__ void mk_patch_queue(int* queue, const int4* patches, int n) {
+// Set-up of a decode step at new lengths, one launch: rewrites the payload
+// words of queued instructions in place (patch i = (word index, three values)
+// stores the values at queue[index .. index + 2]), installs the step's RoPE
+// table (nr floats), and hands the previous step's next tokens (nt int32) to
+// the token buffer and, if given, to the caller's output row.
+__global__ void mk_step_setup(int* queue, const int4* patches, int n, float* rope, const float* rope_src, int nr,
+                              int* tok, const int* next, int* out, int nt) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
     const int4 p = patches[i];
@@ -730,11 +734,20 @@ __global__ void mk_patch_queue(int* queue, const int4* patches, int n) {
     queue[p.x + 1] = p.z;
     queue[p.x + 2] = p.w;
   }
+  if (i < nr) rope[i] = rope_src[i];
+  if (i < nt) {
+    const int t = next[i];
+    tok[i] = t;
+    if (out) out[i] = t;
+  }
 }
 
-hipError_t launch_patch_queue(int* queue, const void* patches, int n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mk_patch_queue, dim3((n + 255) / 256), dim3(256), 0, s, queue, (const int4*)patches, n);
+hipError_t launch_step_setup(int* queue, const void* patches, int n, float* rope, const float* rope_src, int nr,
+                             int* tok, const int* next, int* out, int nt, hipStream_t s) {
+  const int m = n > nr ? (n > nt ? n : nt) : (nr > nt ? nr : nt);
+  if (m <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mk_step_setup, dim3((m + 255) / 256), dim3(256), 0, s, queue, (const int4*)patches, n, rope,
+                     rope_src, nr, tok, next, out, nt);
   return hipGetLastError();
 }
 
