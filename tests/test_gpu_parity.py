@@ -263,8 +263,10 @@ def test_gpu_layerwise_graph_replay_matches_eager():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,n", [("tiny", 5), ("llama1b", 3)])
-def test_gpu_run_steps_match_oracle_step_by_step(name, n):
+@pytest.mark.parametrize("name,n,overrides", [("tiny", 5, {}), ("llama1b", 3, {}),
+                                               ("tiny", 4, dict(batch=3, kv_len=(0, 200), seed=12)),
+                                               ("llama1b_b16", 2, {})])
+def test_gpu_run_steps_match_oracle_step_by_step(name, n, overrides):
     """mk_run_steps: n decode steps back to back, each fed the previous step's
     argmax, without replanning.  Every step's next token equals the oracle's
     (the oracle run step by step on the same token sequence, with its own KV
@@ -272,7 +274,7 @@ def test_gpu_run_steps_match_oracle_step_by_step(name, n):
     written and nothing else; the layerwise run of the same steps gives the same
     tokens; afterwards the plan reports the last step's lengths."""
     mk = _mk()
-    inp = synth.make_inputs(name, norm_sigma=0.0 if name == "llama1b" else 0.1)
+    inp = synth.make_inputs(name, norm_sigma=0.0 if name.startswith("llama1b") else 0.1, **overrides)
     cfg = inp["cfg"]
     B, kv0 = cfg["batch"], inp["kv_len"]
     cache = inp["kv_cache"]
