@@ -228,3 +228,22 @@ def test_set_kv_len_rejections():
         assert e.value.status == mk.MK_E_UNSUPPORTED
     finally:
         gp.free()
+
+
+def test_set_kv_len_random_lengths_match_fresh_plans():
+    """Property check over random mixed lengths (batch 5, fixed split count):
+    moving one plan through a sequence of lengths always leaves exactly the
+    queue a fresh plan for those lengths has."""
+    rng = np.random.default_rng(2024)
+    cfg = synth.config("tiny", batch=5, kv_len=(0, 300), seed=21)
+    kv0 = synth.kv_lengths(cfg)
+    cap = 400
+    plan = mk.Plan.build(cfg, 5, kv0, cap, num_cus=29, attn_splits=6)
+    try:
+        for _ in range(6):
+            kv = rng.integers(0, cap - 1, size=5).astype(np.int32)
+            plan.set_kv_len(kv)
+            ref = P.plan_model(cfg, 5, kv, dict(num_cus=29, attn_splits=6))
+            assert np.array_equal(plan.export()["queue"], np.asarray(ref.queue, dtype=np.int32))
+    finally:
+        plan.free()
