@@ -1202,8 +1202,9 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
 
 // Merge the S split partials of one query head (log-sum-exp).  Lane s reads
 // split s's (max, sum) and turns it into a weight; the weighted outputs are
-// read 16 splits per batch with clamped (branch-free) addresses so that each
-// batch's loads are issued together.
+// read 32 splits per batch with clamped (branch-free) addresses.  The first
+// batch is issued right behind the (max, sum) loads, before the weights are
+// formed, so up to 32 splits cost one memory round trip.
 template <int HD, int POL = 0>
 __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
                                     unsigned long long* tr = nullptr) {
@@ -1211,32 +1212,36 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
   const int lane = lane_id();
   const int b = m.w(WGx), g = m.w(WGy);
   constexpr int PER = HD / 64;
+  constexpr int UB = 32;  // splits per batch of loads
   const GLB float* part = (const GLB float*)m.q(CombPart) + (((size_t)b * c.nkv + g) * c.S * c.hpg + cw) * (HD + 2);
   const size_t stride = (size_t)c.hpg * (HD + 2);
   const int S = c.S;  // <= 64 (checked at plan build)
   const int sl = lane < S ? lane : S - 1;
   const CohT<kCohPolicy> cp(part);  // blocks of different events share lines
   const float ms = cp.f1((uint32_t)(sl * stride) * 4), ls = cp.f1((uint32_t)(sl * stride + 1) * 4);
-  const bool live = lane < S && ls > 0.f;
-  const float M = wave_max(live ? ms : -INFINITY);
-  const float wsp = live ? __expf(ms - M) : 0.f;
-  const float L = wave_sum(wsp * (live ? ls : 0.f));
-  if (tr && lane == 0) tr[6] = now_ticks();
+  float M = 0.f, wsp = 0.f, L = 0.f;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 16) {
-    float ov[16][PER];
+  for (int s0 = 0; s0 < S; s0 += UB) {
+    float ov[UB][PER];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < UB; ++u) {
       const int s = s0 + u < S ? s0 + u : S - 1;
 #pragma unroll
       for (int k = 0; k < PER; ++k) ov[u][k] = cp.f1((uint32_t)(2 + lane + 64 * k) * 4, (uint32_t)(s * stride) * 4);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (s0 == 0) {  // the (max, sum) loads were issued first: no wait for the batch
+      const bool live = lane < S && ls > 0.f;
+      M = wave_max(live ? ms : -INFINITY);
+      wsp = live ? __expf(ms - M) : 0.f;
+      L = wave_sum(wsp * (live ? ls : 0.f));
+      if (tr && lane == 0) tr[6] = now_ticks();
+    }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float w = __shfl(wsp, s0 + u < 64 ? s0 + u : 63, 64);  // 0 for splits >= S
+    for (int u = 0; u < UB; ++u) {
+      const float w = readlane_f(wsp, s0 + u < 64 ? s0 + u : 63);  // 0 for splits >= S
 #pragma unroll
       for (int k = 0; k < PER; ++k) o[k] = fmaf(s0 + u < S ? w : 0.f, ov[u][k], o[k]);
     }
