@@ -383,7 +383,11 @@ def resolve_opts(desc, batch, kv_len, opts=None):
     attn_splits = clamp(ceil((max kv + 1) / 64), 1, 32), lowered to
     max(1, ceil(2 * num_cus / (batch * n_kv_heads))) if that is smaller (about two
     attention tasks per compute unit), then raised until one split's K and V rows
-    (2 * rows * head_dim * 2 bytes) fit in 64 KiB."""
+    (2 * rows * head_dim * 2 bytes) fit in 64 KiB -- or in half the interpreter's
+    page ring (72 KiB at batch 1, 64 KiB above) while the attention tasks still
+    fit on the compute units at one each, since one more split would then put a
+    second task on some units.  (A tuning rule of this implementation, not of the
+    pages.)"""
     o = dict(DEFAULT_OPTS)
     o.update({k: v for k, v in (opts or {}).items() if v})
     H, F, hd = desc["hidden"], desc["ffn"], desc["head_dim"]
@@ -399,7 +403,11 @@ def resolve_opts(desc, batch, kv_len, opts=None):
         n = int(max(kv_len)) + 1
         S = max(1, min(32, ceil_div(n, 64)))
         S = min(S, max(1, ceil_div(2 * o["num_cus"], len(kv_len) * desc["n_kv_heads"])))
-        while ceil_div(n, S) * hd * 4 > 65536:
+        pairs = len(kv_len) * desc["n_kv_heads"]
+        cap = 65536
+        if pairs * S <= o["num_cus"]:
+            cap = (9 if len(kv_len) == 1 else 8) * 16384 // 2
+        while ceil_div(n, S) * hd * 4 > cap:
             S += 1
         o["attn_splits"] = S
     return o
