@@ -102,12 +102,14 @@ typedef struct {
  *   count; the plan can be built without a GPU when it is given).
  * gemv_rows: weight rows per QKV / O / LM-head tile (default 32768 / hidden,
  *   clamped to [4, 16]); gateup_outs: FFN outputs per gate/up tile (default
- *   gemv_rows / 2); down_rows: rows per down tile (default 32768 / ffn,
- *   clamped to [1, 16]); lm_rows: LM-head rows per tile (default gemv_rows);
+ *   gemv_rows / 2); down_rows: rows per down tile (default 32768 / ffn at
+ *   batch 1, 65536 / ffn above, clamped to [1, 16]); lm_rows: LM-head rows per
+ *   tile (default gemv_rows);
  * attn_splits: KV splits per (sequence, kv head) (default from the longest
  *   sequence: ceil((kv+1)/64) clamped to [1, 32], lowered to
  *   ceil(2 num_cus / (batch n_kv_heads)) when that is smaller, then raised
- *   until one split's K and V rows fit in 64 KiB);
+ *   until one split's K and V rows fit in 64 KiB, or in half the page ring
+ *   while batch n_kv_heads splits still fit on num_cus at one each);
  * timeout_ms: bound of every device-side wait (default 200);
  * dma_pages: 16 KiB pages each of the two weight-loader waves keeps in flight
  *   (1 to 3, default 1): the event polls and activation reads that carry the
@@ -140,10 +142,10 @@ typedef struct {
  * t / num_cus.  Deterministic: equal inputs give bit-identical plans.
  * Errors: MK_E_INVALID (null/size/abi mismatch), MK_E_UNSUPPORTED (head_dim not
  * 64 or 128, hidden or ffn not a multiple of 8 or above 12288, more than 4 query
- * heads per kv head, kv_len[b] + 1 > max_kv_len, batch outside 1..16, GEMV
- * tiles with more rows than their K allows (16 up to K 2048, 8 up to 4096, 4
- * beyond), tiles that do not fit the LDS page ring: 144 KiB at batch 1, 128 KiB
- * at batch 2..16).  Batch 1 runs fp32 vector GEMV tiles; batch 2..16 runs the
+ * heads per kv head, kv_len[b] + 1 > max_kv_len, batch outside 1..16, batch-1
+ * GEMV tiles with more rows than their K allows (16 up to K 2048, 8 up to 4096,
+ * 4 beyond), tiles that do not fit the LDS page ring: 144 KiB at batch 1, 128
+ * KiB at batch 2..16).  Batch 1 runs fp32 vector GEMV tiles; batch 2..16 runs the
  * same tiles on the matrix cores (16 weight rows x 16 sequences per MFMA block,
  * activations entered as bf16 high and low parts). */
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* kv_len,

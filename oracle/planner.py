@@ -379,7 +379,10 @@ DEFAULT_OPTS = dict(num_cus=256, gemv_rows=0, gateup_outs=0, down_rows=0, lm_row
 def resolve_opts(desc, batch, kv_len, opts=None):
     """Fill the 0 (default) fields: tiles of about 64 KiB of bf16 weights.
     gemv_rows = clamp(32768 // hidden, 4, 16); gateup_outs = gemv_rows // 2;
-    down_rows = clamp(32768 // ffn, 1, 16); lm_rows = gemv_rows;
+    down_rows = clamp(32768 // ffn, 1, 16) at batch 1 (the batch-1 GEMV holds a tile
+    in registers), clamp(131072 // (2 * ffn), 1, 16) above (a batched tile is read
+    from the 128 KiB page ring and may fill it: fewer re-reads of the sequences'
+    activations per weight row); lm_rows = gemv_rows;
     attn_splits = clamp(ceil((max kv + 1) / 64), 1, 32), lowered to
     max(1, ceil(2 * num_cus / (batch * n_kv_heads))) if that is smaller (about two
     attention tasks per compute unit), then raised until one split's K and V rows
@@ -396,7 +399,7 @@ def resolve_opts(desc, batch, kv_len, opts=None):
     if not o["gateup_outs"]:
         o["gateup_outs"] = max(1, o["gemv_rows"] // 2)
     if not o["down_rows"]:
-        o["down_rows"] = max(1, min(16, 32768 // F))
+        o["down_rows"] = max(1, min(16, (32768 if len(kv_len) == 1 else 131072 // 2) // F))
     if not o["lm_rows"]:
         o["lm_rows"] = o["gemv_rows"]
     if not o["attn_splits"]:

@@ -342,8 +342,10 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
     delete p;
     return fail(MK_E_UNSUPPORTED, "tile rows must be <= 16");
   }
-  // the GEMV tile shapes the kernels instantiate (rows per tile by K)
-  {
+  // the GEMV tile shapes the batch-1 kernels instantiate (rows per tile by K:
+  // each compute wave holds its share of a tile in registers); the batched
+  // tiles read their weights from the ring, limited only by its size below
+  if (batch == 1) {
     const int K_h = d.hidden, K_o = d.n_q_heads * d.head_dim, K_f = d.ffn;
     if (o.gemv_rows > mkd::gemv_max_rows(K_h) || o.gemv_rows > mkd::gemv_max_rows(K_o) ||
         2 * o.gateup_outs > mkd::gemv_max_rows(K_h) || o.down_rows > mkd::gemv_max_rows(K_f) ||

@@ -420,7 +420,10 @@ std::string plan_graph(const std::vector<GraphOp>& ops, const std::vector<GraphE
 void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, ModelOpts* o) {
   if (!o->gemv_rows) o->gemv_rows = std::max(4, std::min(16, 32768 / m.hidden));
   if (!o->gateup_outs) o->gateup_outs = std::max(1, o->gemv_rows / 2);
-  if (!o->down_rows) o->down_rows = std::max(1, std::min(16, 32768 / m.ffn));
+  // batch 1: a down tile is held in the compute waves' registers (64 KiB of
+  // weights); batched: read from the 128 KiB page ring, which it may fill (more
+  // rows per tile, fewer re-reads of the sequences' activations)
+  if (!o->down_rows) o->down_rows = std::max(1, std::min(16, (kv_len.size() == 1 ? 32768 : 65536) / m.ffn));
   if (!o->lm_rows) o->lm_rows = o->gemv_rows;
   if (!o->attn_splits) {
     int n = *std::max_element(kv_len.begin(), kv_len.end()) + 1;

@@ -204,10 +204,12 @@ def test_gpu_qwen3_8b_full_size():
     ("b3", "tiny", dict(batch=3, kv_len=(0, 200), seed=11)),
     ("b16", "tiny", dict(batch=16, kv_len=(100, 300), seed=12)),
     ("b5_qwen", "tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128, batch=5, kv_len=(1, 90), seed=13)),
+    ("b6_ragged", "tiny", dict(batch=6, kv_len=(1, 120), seed=15, opts=dict(down_rows=6, gateup_outs=3))),
 ])
 def test_gpu_batched(key, name, overrides):
     """Batch 2..16 (matrix-core GEMV tiles, per-sequence attention lengths):
-    megakernel and layerwise against the oracle, every sequence's argmax."""
+    megakernel and layerwise against the oracle, every sequence's argmax.
+    b6_ragged: down and gate/up tiles whose row counts leave a short last tile."""
     c = case(key, name, **overrides)
     c.assert_parity(c.run())
     c.assert_parity(c.run(layerwise=True), layerwise=True)

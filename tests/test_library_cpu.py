@@ -53,6 +53,8 @@ def _compare(lib_plan, ref):
     ("llama1b_b16", {}, 256, {}),
     ("llama1b", {}, 148, dict(gemv_rows=8, down_rows=2)),
     ("qwen3_8b", {}, 256, {}),
+    ("qwen3_8b", dict(batch=4, kv_len=(100, 3000), seed=3), 256, {}),  # batched default down tiles, F 12288
+    ("tiny", dict(batch=6, kv_len=(1, 120), seed=15), 64, dict(down_rows=6, gateup_outs=3)),
 ])
 def test_cpp_planner_matches_reference(name, overrides, num_cus, opts):
     cfg = synth.config(name, **overrides)
@@ -247,3 +249,14 @@ def test_set_kv_len_random_lengths_match_fresh_plans():
             assert np.array_equal(plan.export()["queue"], np.asarray(ref.queue, dtype=np.int32))
     finally:
         plan.free()
+
+
+def test_default_down_tiles_by_batch():
+    """Batch 1 keeps a down tile within the compute waves' registers (64 KiB of
+    weights); batched plans fill up to the 128 KiB page ring."""
+    for name, batch, want in (("llama1b", 1, 4), ("llama1b_b16", 16, 8), ("qwen3_8b", 1, 2)):
+        cfg = synth.config(name)
+        kv = synth.kv_lengths(cfg)
+        assert P.resolve_opts(cfg, batch, kv, dict(num_cus=256))["down_rows"] == want
+    cfg = synth.config("qwen3_8b", batch=4, kv_len=(100, 3000), seed=3)
+    assert P.resolve_opts(cfg, 4, synth.kv_lengths(cfg), dict(num_cus=256))["down_rows"] == 5
