@@ -257,7 +257,10 @@ mk_status mk_plan_set_kv_len(mk_plan* plan, const int32_t* kv_len, void* stream)
  * tokens, device int32 [batch]; the plan keeps its own copy).  out_tokens
  * (device int32 [n_steps][batch], or null) receives every step's next tokens.
  * layerwise != 0 runs each step as mk_run_layerwise does.  Afterwards the plan
- * is at the last step's lengths and its outputs are the last step's.
+ * is at the last step's lengths and its outputs are the last step's.  Only
+ * enqueues work (the host waits at most for the upload of the call before the
+ * previous one); calls on one plan must be ordered on one stream, as its runs
+ * share the plan's queue and workspace.
  * Errors: as mk_run and mk_plan_set_kv_len; MK_E_INVALID for n_steps < 1. */
 mk_status mk_run_steps(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens,
                        int32_t n_steps, void* out_tokens, int32_t layerwise, void* stream);

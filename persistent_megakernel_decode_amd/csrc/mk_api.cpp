@@ -87,11 +87,16 @@ struct mk_plan {
   int* d_patch = nullptr;
   std::vector<float> h_rope;
   // staging of a run of steps: pinned host buffer and its device copy, per step
-  // the attention patches then the RoPE table; an event marks the last upload
-  char* h_steps = nullptr;
-  char* d_steps = nullptr;
-  size_t steps_cap = 0;
-  hipEvent_t ev_steps = nullptr;
+  // the attention patches then the RoPE table; an event marks the upload.  Two
+  // of them, used in turn, so that staging a call never waits for the steps the
+  // previous call queued (only for the upload of the call before that)
+  struct Staging {
+    char* h = nullptr;
+    char* d = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+  } stg[2];
+  int stg_next = 0;
   int32_t* d_tok = nullptr;  // tokens of a run of steps (the previous step's next tokens)
   // workspace offsets (bytes)
   size_t off_qkv = 0, off_part = 0, off_ao = 0, off_hidden = 0, off_act = 0, off_logits = 0, off_lmmax = 0,
@@ -878,40 +883,47 @@ static void apply_lengths(mk_plan* p, const std::vector<int32_t>& kv, int32_t* o
 }
 
 // Stage n steps at lengths kv + k (k = 0 .. n-1) in pinned host memory and copy
-// them to the device on stream s; the host state ends at the last step's lengths.
-static mk_status stage_steps(mk_plan* p, const std::vector<int32_t>& kv, int n, hipStream_t s, size_t* step_bytes) {
+// them to the device on stream s (*dev: the device copy); the host state ends at
+// the last step's lengths.
+static mk_status stage_steps(mk_plan* p, const std::vector<int32_t>& kv, int n, hipStream_t s, size_t* step_bytes,
+                             const char** dev) {
   const size_t pbytes = p->attn_words.size() * 16, rbytes = p->h_rope.size() * 4;
   const size_t per = (pbytes + rbytes + 255) / 256 * 256;
   *step_bytes = per;
-  if (p->ev_steps) HIPCHK(hipEventSynchronize(p->ev_steps), "previous staging");  // host buffer reuse
-  if ((size_t)n * per > p->steps_cap) {
-    if (p->h_steps) HIPCHK(hipHostFree(p->h_steps), "hipHostFree");
-    if (p->d_steps) HIPCHK(hipFree(p->d_steps), "hipFree");
-    p->h_steps = nullptr;
-    p->d_steps = nullptr;
-    p->steps_cap = 0;
-    HIPCHK(hipHostMalloc((void**)&p->h_steps, (size_t)n * per, hipHostMallocDefault), "hipHostMalloc steps");
-    HIPCHK(hipMalloc((void**)&p->d_steps, (size_t)n * per), "hipMalloc steps");
-    p->steps_cap = (size_t)n * per;
+  mk_plan::Staging& g = p->stg[p->stg_next];
+  p->stg_next ^= 1;
+  if (g.ev) HIPCHK(hipEventSynchronize(g.ev), "earlier staging");  // host buffer reuse
+  if ((size_t)n * per > g.cap) {
+    // hipFree waits for the device, so no queued set-up kernel still reads g.d
+    if (g.h) HIPCHK(hipHostFree(g.h), "hipHostFree");
+    if (g.d) HIPCHK(hipFree(g.d), "hipFree");
+    g.h = nullptr;
+    g.d = nullptr;
+    g.cap = 0;
+    HIPCHK(hipHostMalloc((void**)&g.h, (size_t)n * per, hipHostMallocDefault), "hipHostMalloc steps");
+    HIPCHK(hipMalloc((void**)&g.d, (size_t)n * per), "hipMalloc steps");
+    g.cap = (size_t)n * per;
   }
-  if (!p->ev_steps) HIPCHK(hipEventCreateWithFlags(&p->ev_steps, hipEventDisableTiming), "event");
+  if (!g.ev) HIPCHK(hipEventCreateWithFlags(&g.ev, hipEventDisableTiming), "event");
   std::vector<int32_t> k_kv(kv);
   for (int k = 0; k < n; ++k) {
     for (int b = 0; b < p->batch; ++b) k_kv[b] = kv[b] + k;
-    char* h = p->h_steps + (size_t)k * per;
+    char* h = g.h + (size_t)k * per;
     apply_lengths(p, k_kv, (int32_t*)h);
     std::memcpy(h + pbytes, p->h_rope.data(), rbytes);
   }
-  HIPCHK(hipMemcpyAsync(p->d_steps, p->h_steps, (size_t)n * per, hipMemcpyHostToDevice, s), "upload steps");
-  HIPCHK(hipEventRecord(p->ev_steps, s), "staging event");
+  HIPCHK(hipMemcpyAsync(g.d, g.h, (size_t)n * per, hipMemcpyHostToDevice, s), "upload steps");
+  HIPCHK(hipEventRecord(g.ev, s), "staging event");
+  *dev = g.d;
   return MK_OK;
 }
 
 // Step k of a staged run: patch the queue and install its RoPE table; with
 // ntok > 0 also hand the previous step's next tokens to the token buffer (and
 // to out, if given) -- one launch.
-static mk_status install_step(mk_plan* p, int k, size_t per, hipStream_t s, int ntok = 0, int* out = nullptr) {
-  const char* d = p->d_steps + (size_t)k * per;
+static mk_status install_step(mk_plan* p, const char* staged, int k, size_t per, hipStream_t s, int ntok = 0,
+                              int* out = nullptr) {
+  const char* d = staged + (size_t)k * per;
   HIPCHK(mk::launch_step_setup(p->d_queue, d, (int)p->attn_words.size(), p->d_rope,
                                (const float*)(d + p->attn_words.size() * 16), (int)p->h_rope.size(), p->d_tok,
                                (const int*)(p->d_ws + p->off_next), out, ntok, s),
@@ -931,9 +943,10 @@ mk_status mk_plan_set_kv_len(mk_plan* p, const int32_t* kv_len, void* stream) {
   }
   hipStream_t s = (hipStream_t)stream;
   size_t per = 0;
-  st = stage_steps(p, kv, 1, s, &per);
+  const char* staged = nullptr;
+  st = stage_steps(p, kv, 1, s, &per, &staged);
   if (st != MK_OK) return st;
-  return install_step(p, 0, per, s);
+  return install_step(p, staged, 0, per, s);
 }
 
 mk_status mk_run_steps(mk_plan* p, const mk_weights* w, void* kv_cache, const void* tokens, int32_t n_steps,
@@ -955,13 +968,14 @@ mk_status mk_run_steps(mk_plan* p, const mk_weights* w, void* kv_cache, const vo
   if (st != MK_OK) return st;
   const std::vector<int32_t> first(p->kv_len);
   size_t per = 0;
-  st = stage_steps(p, first, n_steps, s, &per);
+  const char* staged = nullptr;
+  st = stage_steps(p, first, n_steps, s, &per, &staged);
   if (st != MK_OK) return st;
   const char* next = p->d_ws + p->off_next;
   for (int k = 0; k < n_steps; ++k) {
     if (k > 0) {  // step k's lengths and RoPE; step k - 1's next tokens in, and out
       int* out = out_tokens ? (int*)out_tokens + (size_t)(k - 1) * p->batch : nullptr;
-      st = install_step(p, k, per, s, p->batch, out);
+      st = install_step(p, staged, k, per, s, p->batch, out);
       if (st != MK_OK) return st;
     }
     st = layerwise ? launch_layerwise(p, s) : launch_step(p, s);
@@ -1102,7 +1116,8 @@ void mk_plan_free(mk_plan* p) {
     (void)hipFree(p->d_ws);
     if (p->d_rows) (void)hipFree(p->d_rows);
     if (p->d_patch) (void)hipFree(p->d_patch);
-    if (p->d_steps) (void)hipFree(p->d_steps);
+    for (auto& g : p->stg)
+      if (g.d) (void)hipFree(g.d);
     if (p->d_tok) (void)hipFree(p->d_tok);
   }
   if (p->d_trace) (void)hipFree(p->d_trace);
@@ -1111,8 +1126,10 @@ void mk_plan_free(mk_plan* p) {
   for (auto e : p->op_done)
     if (e) (void)hipEventDestroy(e);
   if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
-  if (p->ev_steps) (void)hipEventDestroy(p->ev_steps);
-  if (p->h_steps) (void)hipHostFree(p->h_steps);
+  for (auto& g : p->stg) {
+    if (g.ev) (void)hipEventDestroy(g.ev);
+    if (g.h) (void)hipHostFree(g.h);
+  }
   delete p;
 }
 
