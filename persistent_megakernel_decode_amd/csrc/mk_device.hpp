@@ -1137,41 +1137,55 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // the batch's LDS reads stay in flight together
+    // the U scores first, then one rescale of the running sums per pass: the
+    // exponentials of a pass do not wait on one another
+    float sc[U];
+    float mx = m;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * PPP + gi;
-      float kf[8], vf[8];
+      float d = 0.f;
       if (j < nk) {
-        kf[0] = bf16lo(ku[u].x); kf[1] = bf16hi(ku[u].x); kf[2] = bf16lo(ku[u].y); kf[3] = bf16hi(ku[u].y);
-        kf[4] = bf16lo(ku[u].z); kf[5] = bf16hi(ku[u].z); kf[6] = bf16lo(ku[u].w); kf[7] = bf16hi(ku[u].w);
-        vf[0] = bf16lo(vu[u].x); vf[1] = bf16hi(vu[u].x); vf[2] = bf16lo(vu[u].y); vf[3] = bf16hi(vu[u].y);
-        vf[4] = bf16lo(vu[u].z); vf[5] = bf16hi(vu[u].z); vf[6] = bf16lo(vu[u].w); vf[7] = bf16hi(vu[u].w);
+        d = fmaf(bf16lo(ku[u].x), qc[0], d); d = fmaf(bf16hi(ku[u].x), qc[1], d);
+        d = fmaf(bf16lo(ku[u].y), qc[2], d); d = fmaf(bf16hi(ku[u].y), qc[3], d);
+        d = fmaf(bf16lo(ku[u].z), qc[4], d); d = fmaf(bf16hi(ku[u].z), qc[5], d);
+        d = fmaf(bf16lo(ku[u].w), qc[6], d); d = fmaf(bf16hi(ku[u].w), qc[7], d);
       } else {  // the new row (j == nk) or past the end (masked below)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kf[e] = kn[cidx * 8 + e];
-          vf[e] = vn[cidx * 8 + e];
-        }
+        for (int e = 0; e < 8; ++e) d = fmaf(kn[cidx * 8 + e], qc[e], d);
       }
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(kf[e], qc[e], d);
       // sum over the LPP lanes of this position (8: half a DPP row, 16: a row)
       d += dppf<DppXor1>(d);
       d += dppf<DppXor2>(d);
       d += dppf<DppHalfMirror>(d);
       if (LPP == 16) d += dppf<DppRor8>(d);
-      if (j < n) {
-        const float sj = d * c.inv_sqrt_hd;
-        const float mn = fmaxf(m, sj);
-        const float al = __expf(m - mn);  // 0 when m = -inf
-        const float pj = __expf(sj - mn);
-        l = l * al + pj;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(pj, vf[e], o[e] * al);
-        m = mn;
-      }
+      sc[u] = j < n ? d * c.inv_sqrt_hd : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
     }
+    // a finite base while no position of this lane group is valid yet (then
+    // every term below is zero and the sums stay empty)
+    const float mb = mx == -INFINITY ? 0.f : mx;
+    const float al = __expf(m - mb);  // 0 when m = -inf
+    l *= al;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= al;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * PPP + gi;
+      const float pj = __expf(sc[u] - mb);  // 0 for masked positions
+      float vf[8];
+      if (j < nk) {
+        vf[0] = bf16lo(vu[u].x); vf[1] = bf16hi(vu[u].x); vf[2] = bf16lo(vu[u].y); vf[3] = bf16hi(vu[u].y);
+        vf[4] = bf16lo(vu[u].z); vf[5] = bf16hi(vu[u].z); vf[6] = bf16lo(vu[u].w); vf[7] = bf16hi(vu[u].w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = vn[cidx * 8 + e];
+      }
+      l += pj;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(pj, vf[e], o[e]);
+    }
+    m = mx;
   }
   // merge the PPP position groups
 #pragma unroll
