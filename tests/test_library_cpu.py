@@ -260,3 +260,22 @@ def test_default_down_tiles_by_batch():
         assert P.resolve_opts(cfg, batch, kv, dict(num_cus=256))["down_rows"] == want
     cfg = synth.config("qwen3_8b", batch=4, kv_len=(100, 3000), seed=3)
     assert P.resolve_opts(cfg, 4, synth.kv_lengths(cfg), dict(num_cus=256))["down_rows"] == 5
+
+
+def test_split_rule_one_task_per_cu():
+    """The per-split byte cap is half the page ring while the attention tasks
+    fit on the compute units at one each, 64 KiB otherwise: Qwen3-8B at KV 4096
+    (8 kv heads, 4097 positions, 512 bytes per position) takes 32 splits of 129
+    positions (66,048 bytes) on 256 CUs, and 33 on 200 CUs, where 32 splits
+    would already need 256 tasks."""
+    cfg = synth.config("qwen3_8b")
+    kv = synth.kv_lengths(cfg)
+    assert P.resolve_opts(cfg, 1, kv, dict(num_cus=256))["attn_splits"] == 32
+    assert P.resolve_opts(cfg, 1, kv, dict(num_cus=200))["attn_splits"] == 33
+    for cus in (256, 200):
+        plan = mk.Plan.build(cfg, 1, kv, synth.kv_capacity(kv), num_cus=cus)
+        try:
+            ref = P.plan_model(cfg, 1, kv, dict(num_cus=cus))
+            assert np.array_equal(plan.export()["queue"], np.asarray(ref.queue, dtype=np.int32))
+        finally:
+            plan.free()
