@@ -584,8 +584,8 @@ __global__ void __launch_bounds__((LdsT<MB, GLM>::THREADS), 1) mk_megakernel(KAr
   // copy; within the step no such line can appear
   if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
-  // issue priority: compute and storer waves (the dependency chain) ahead of
-  // the controller, the controller ahead of the loaders
+  // issue priority: the compute waves first, then the storer (the dependency
+  // chain), the controller, and the loaders last
   const int w = threadIdx.x >> 6;
   if (w == 0) {
     __builtin_amdgcn_s_setprio(1);
@@ -596,7 +596,7 @@ __global__ void __launch_bounds__((LdsT<MB, GLM>::THREADS), 1) mk_megakernel(KAr
   } else if (w < 4) {
     loader(a, L, w - 2);
   } else {
-    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_s_setprio(3);
     compute<HD, LT>(a, L, (w - 4) % kNW, LT::SETS > 1 ? (w - 4) / kNW : 0);
   }
 }
