@@ -211,8 +211,12 @@ def test_gpu_batched(key, name, overrides):
     megakernel and layerwise against the oracle, every sequence's argmax.
     b6_ragged: down and gate/up tiles whose row counts leave a short last tile."""
     c = case(key, name, **overrides)
-    c.assert_parity(c.run())
-    c.assert_parity(c.run(layerwise=True), layerwise=True)
+    r = c.run()
+    c.assert_parity(r)
+    lw = c.run(layerwise=True)
+    c.assert_parity(lw, layerwise=True)
+    # the layerwise kernels run the same tile functions in the same order
+    assert np.array_equal(lw["logits"], r["logits"])
 
 
 @pytest.mark.timeout(900)
