@@ -133,8 +133,11 @@ def test_gpu_llama1b_full_size():
     """Llama-3.2-1B shape, batch 1, KV 1024, in the launch configuration the
     benchmark times (256 workgroups, default tiles)."""
     c = case("llama1b", "llama1b", norm_sigma=0.0)
-    c.assert_parity(c.run())
-    c.assert_parity(c.run(layerwise=True), layerwise=True)
+    r = c.run()
+    c.assert_parity(r)
+    lw = c.run(layerwise=True)
+    c.assert_parity(lw, layerwise=True)
+    assert np.array_equal(lw["logits"], r["logits"])  # same tile functions, same order
 
 
 @pytest.mark.parametrize("key,name", [("tiny", "tiny"), ("llama1b", "llama1b")])
@@ -191,8 +194,11 @@ def test_gpu_qwen3_8b_full_size():
     import gc
     c = Case("qwen3_8b", norm_sigma=0.0)
     try:
-        c.assert_parity(c.run())
-        c.assert_parity(c.run(layerwise=True), layerwise=True)
+        r = c.run()
+        c.assert_parity(r)
+        lw = c.run(layerwise=True)
+        c.assert_parity(lw, layerwise=True)
+        assert np.array_equal(lw["logits"], r["logits"])  # same tile functions, same order
     finally:
         c.plan.free()
         del c
@@ -226,8 +232,11 @@ def test_gpu_llama1b_batch16_full_size():
     import gc
     c = Case("llama1b_b16", norm_sigma=0.0)
     try:
-        c.assert_parity(c.run())
-        c.assert_parity(c.run(layerwise=True), layerwise=True)
+        r = c.run()
+        c.assert_parity(r)
+        lw = c.run(layerwise=True)
+        c.assert_parity(lw, layerwise=True)
+        assert np.array_equal(lw["logits"], r["logits"])  # same tile functions, same order
     finally:
         c.plan.free()
         del c
