@@ -114,8 +114,8 @@ typedef struct {
  * dma_pages: 16 KiB pages each of the two weight-loader waves keeps in flight
  *   (1 to 3, default 1): the event polls and activation reads that carry the
  *   dependency chain share the compute unit's vector-memory queue with the page
- *   DMA, so a shallow DMA backlog is faster (Llama-1B 886 / 895 / 915 us at 1 /
- *   2 / 3).  Does not change the plan's schedule metadata.
+ *   DMA, so a shallow DMA backlog is the default.  Does not change the plan's
+ *   schedule metadata.
  * lw_streams: streams of mk_run_layerwise (0 or 1: every launch on the caller's
  *   stream; 2 or 3: independent branches of the op graph -- the GLM path's QKV-A,
  *   head gate and indexer-K after A0, QKV-B and indexer-Q after the q-path norm --
@@ -133,7 +133,14 @@ typedef struct {
 } mk_plan_opts;
 
 /* Build the static tile plan of one decode step (host-only arithmetic; uploads
- * nothing until the first run).  kv_len: host int32[batch], prior rows per
+ * nothing until the first run).  Defined by: MegaRTP article, section 4
+ * ("TaskGraph": tiles to counter events; "KernelPlan": round-robin queues of
+ * 32-word instructions padded with NoOps; the operand pointer table); MPK
+ * internals notes, "fine-grained pipeline" (per-dimension gcd of the producer
+ * and consumer partitions), "handling fork producer" / "handling join
+ * consumer" (lcm normalization) and "building the SM-level DAG"
+ * (linearization); CMU 15-779 lecture 7 notes, section 6 (per-layer task
+ * partition of the decode step).  kv_len: host int32[batch], prior rows per
  * sequence; the step writes row kv_len[b] and attends rows 0..kv_len[b].  The
  * planner cuts every operator into tiles, derives events by gcd partition of
  * each producer/consumer edge (lcm-normalized at forks and joins), drops
@@ -152,7 +159,8 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
                         const mk_plan_opts* opts, mk_plan** out);
 
 /* Plan an arbitrary operator graph with the same rules (no payloads; the result
- * can be exported but not run: mk_run returns MK_E_STATE).  ops[i].grid holds
+ * can be exported but not run: mk_run returns MK_E_STATE).  Defined by the MPK
+ * internals notes' worked examples (fork producer, join consumer, gcd table).  ops[i].grid holds
  * up to three axis extents; edges must go from a lower to a higher op index;
  * out_map / in_map give, per grid axis, the tensor dimension (0..3) it
  * partitions or -1; when has_extent is set, extent/ptile/ctile (elements) let
@@ -171,7 +179,9 @@ typedef struct {
 mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_edge* edges, int32_t n_edges,
                         int32_t num_cus, mk_plan** out);
 
-/* Host views of the plan's schedule metadata, valid until mk_plan_free.
+/* Host views of the plan's schedule metadata, valid until mk_plan_free
+ * (MegaRTP article, section 4 "KernelPlan": the [num_CUs, max_len, 32] int32
+ * instruction tensor, per-event thresholds).
  * queue: int32 [num_cus][max_len][32] (word layout: 0 opcode, 1 spec_id,
  *   2 operand row, 3 wait count, 4 wait event, 5 wait target per run, 6 signal
  *   count, 7 signal event, 8 signal increment, 9 task id, 10 layer, 11-13 grid
@@ -212,12 +222,18 @@ typedef struct {
 } mk_weights;
 
 /* Run one decode step as the persistent megakernel: ONE launch of 'num_cus'
- * workgroups on 'stream' (a hipStream_t; NULL = default stream).
+ * workgroups on 'stream' (a hipStream_t; NULL = default stream).  Defined by:
+ * CMU 15-779 lecture 7 notes, section 4.1 (the worker loop: fetch, prefetch
+ * weights before waiting, wait for counters, compute, signal) and section 6
+ * (the decode step's operator chain); MegaRTP article, section 4 ("Device-side
+ * execution": controller / loader / consumer / storer roles, shared-memory
+ * pages recycled across instructions, global event counters).
  * kv_cache: device bf16 [n_layers][2][batch][n_kv_heads][max_kv_len][head_dim];
  *   row kv_len[b] of every (layer, K|V, b, head) is written, rows < kv_len[b]
  *   are read, nothing else is touched, so repeated runs are idempotent.
- * tokens: device int32 [batch], input token ids (ids outside [0, vocab) are
- *   clamped into it on the device).
+ * tokens: device int32 [batch], input token ids in [0, vocab).  An id outside
+ *   it fails the run: the step computes on the id clamped into range (no access
+ *   leaves the embedding) and mk_plan_check returns MK_E_INVALID.
  * MK_ARCH_GLM_PREATTN: tokens is device bf16 [2][batch][hidden] (x, then r);
  *   kv_cache is device bf16, the KV cache [n_seq][max_kv_len][kv_lora +
  *   rope_dim] followed by the indexer cache [n_seq][max_kv_len][idx_head_dim]
@@ -226,13 +242,20 @@ typedef struct {
  * Results stay in the plan (see mk_plan_output).  Only enqueues work; the
  * first call uploads the plan; pointer changes rewrite the operand table.
  * A device wait that exceeds the plan's bound makes the grid exit early and is
- * reported by mk_plan_check.  Errors: MK_E_INVALID, MK_E_STATE (graph-only
- * plan), MK_E_HIP. */
+ * reported by mk_plan_check.  The launch carries the run's epoch, so it must not
+ * be captured into a graph: under stream capture mk_run returns
+ * MK_E_UNSUPPORTED (capture mk_run_layerwise instead).  Errors: MK_E_INVALID,
+ * MK_E_STATE (graph-only plan), MK_E_UNSUPPORTED (capture; the grid cannot be
+ * co-resident on the device), MK_E_HIP. */
 mk_status mk_run(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens, void* stream);
 
 /* The same step with one kernel launch per operator (stream order replaces the
  * event counters; same tiles and tile arithmetic, weights read straight from
- * memory).  The baseline the megakernel is measured against. */
+ * memory).  The baseline the megakernel is measured against: CMU 15-779 lecture
+ * 7 notes, section 2 (one kernel per operator: launch gaps, latency, tails);
+ * MegaRTP article, sections 1 and 5 (fused per-op kernels on one stream; graph
+ * + multistream).  It may be captured into a graph (the launch arguments
+ * carry nothing that changes between runs). */
 mk_status mk_run_layerwise(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens,
                            void* stream);
 
@@ -261,11 +284,16 @@ mk_status mk_plan_set_kv_len(mk_plan* plan, const int32_t* kv_len, void* stream)
  * enqueues work (the host waits at most for the upload of the call before the
  * previous one); calls on one plan must be ordered on one stream, as its runs
  * share the plan's queue and workspace.
+ * Not capturable (MK_E_UNSUPPORTED under stream capture), as mk_run.
+ * Defined by: CMU 15-779 lecture 7 notes, section 4.1 (the decode loop);
+ * MegaRTP article, section 4 (a plan is rebuilt only when tile counts or
+ * thresholds change).
  * Errors: as mk_run and mk_plan_set_kv_len; MK_E_INVALID for n_steps < 1. */
 mk_status mk_run_steps(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens,
                        int32_t n_steps, void* out_tokens, int32_t layerwise, void* stream);
 
-/* Device pointer and size of a plan output:
+/* Device pointer and size of a plan output (the tensors the pages' decode step
+ * produces: CMU 15-779 lecture 7 notes, section 6; MegaRTP article, section 1):
  * MK_OUT_LOGITS fp32 [batch][vocab]; MK_OUT_NEXT_TOKEN int32 [batch];
  * MK_OUT_QKV fp32 [n_layers] slices of [batch][n_kv_heads][(n_q/n_kv + 2) *
  *   head_dim] (per kv head: its q heads, then k, then v, before RoPE);
@@ -290,10 +318,15 @@ mk_status mk_plan_output(const mk_plan* plan, int32_t which, void** dev_ptr, siz
  * 'bytes' = the output's size) on 'stream'. */
 mk_status mk_plan_copy_output(const mk_plan* plan, int32_t which, void* dst, size_t bytes, void* stream);
 
-/* Synchronize the stream, then read back the device state of the last run:
+/* Synchronize the stream, then read back the device state of the last run
+ * (MegaRTP article, section 4: every counter reaches its threshold):
  * counters_ok = 1 when every event counter equals epoch * target; err_* is the
  * watchdog record (err_kind 0 = none, 1 = event wait, 2 = page wait, 3 = ready
- * wait, 4 = drain wait).  Returns MK_E_TIMEOUT when the record is set. */
+ * wait, 4 = drain wait, 5 = free-page wait).  Returns MK_E_TIMEOUT when the
+ * record is set (the next run then clears the counters and restarts at epoch
+ * 1), MK_E_INVALID when the last run's input tokens held an id outside [0,
+ * vocab).  Counters are cleared the same way when they disagree with their
+ * targets, and before the epoch would wrap. */
 typedef struct {
   uint32_t epoch;
   int32_t counters_ok;
@@ -304,15 +337,28 @@ typedef struct {
 mk_status mk_plan_check(mk_plan* plan, void* stream, mk_check* out);
 
 /* Per-instruction timestamps of the next mk_run calls (enable=1) or none
- * (enable=0).  mk_plan_trace copies the last run's trace to host memory:
+ * (enable=0), for the active-CU fraction and bubble analysis of the MegaRTP
+ * article, sections 1 and 6.  mk_plan_trace copies the last run's trace to host memory:
  * uint64 [num_cus][max_len][16] = (event satisfied, compute start, compute end,
  * signalled, first page DMA issued, last page landed in LDS, compute wave 0
  * activation ready, 0, then per compute wave 0..3 its start and its
- * pages-released time), in ticks of 'ticks_per_us'. */
+ * pages-released time), in ticks of the device's constant clock, whose rate
+ * (hipDeviceAttributeWallClockRate) is returned in ticks_per_us. */
 mk_status mk_plan_set_trace(mk_plan* plan, int32_t enable);
 mk_status mk_plan_trace(mk_plan* plan, void* stream, uint64_t* host_out, size_t bytes, double* ticks_per_us);
 
 void mk_plan_free(mk_plan* plan);
+
+/* Fill the plan's workspace (every intermediate and output) with 0xFF bytes
+ * (NaN as fp32) on the stream, so that a run that read data no task of it wrote
+ * shows NaN.  Errors: MK_E_STATE before the plan's first run. */
+mk_status mk_plan_poison_workspace(mk_plan* plan, void* stream);
+
+/* For tests of the watchdog: add delta to the wait threshold of every
+ * instruction that waits on 'event' (re-uploaded at once if the plan has run).
+ * A threshold above the event's producer count makes its waiters time out: the
+ * grid drains and exits normally and mk_plan_check reports MK_E_TIMEOUT. */
+mk_status mk_plan_debug_raise_wait(mk_plan* plan, int32_t event, int32_t delta);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,8 @@ GLM_SLOTS = ("attn_norm", "w_qkva", "s_qkva", "w_gate", "s_gate", "w_idxk", "s_i
 LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_plan_export", "mk_run",
             "mk_run_layerwise", "mk_plan_output", "mk_plan_copy_output", "mk_plan_check", "mk_plan_set_trace",
-            "mk_plan_trace", "mk_plan_free", "mk_plan_set_kv_len", "mk_run_steps")
+            "mk_plan_trace", "mk_plan_free", "mk_plan_set_kv_len", "mk_run_steps", "mk_plan_debug_raise_wait",
+            "mk_plan_poison_workspace")
 
 i32, u32, f32, vp, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -109,6 +110,8 @@ def lib():
         L.mk_plan_check.argtypes = [vp, vp, P(Check)]
         L.mk_plan_set_trace.argtypes = [vp, i32]
         L.mk_plan_trace.argtypes = [vp, vp, vp, sz, P(ctypes.c_double)]
+        L.mk_plan_debug_raise_wait.argtypes = [vp, i32, i32]
+        L.mk_plan_poison_workspace.argtypes = [vp, vp]
         L.mk_plan_free.argtypes = [vp]
         L.mk_plan_free.restype = None
         for n in EXPORTED:
@@ -210,6 +213,15 @@ class Plan:
 
     def run_layerwise(self, weights, kv_cache, tokens, stream=None):
         self.run(weights, kv_cache, tokens, stream, layerwise=True)
+
+    def poison_workspace(self, stream=None):
+        """mk_plan_poison_workspace: every intermediate and output to NaN."""
+        _check(lib().mk_plan_poison_workspace(self._h, vp(stream.cuda_stream if stream is not None
+                                                            else current_stream())))
+
+    def debug_raise_wait(self, event, delta):
+        """mk_plan_debug_raise_wait (tests of the watchdog)."""
+        _check(lib().mk_plan_debug_raise_wait(self._h, int(event), int(delta)))
 
     def set_kv_len(self, kv_len, stream=None):
         """mk_plan_set_kv_len: the next step's sequence lengths, without replanning."""

@@ -63,7 +63,9 @@ struct mk_plan {
   hipEvent_t ev_fork = nullptr;
   mkd::Consts c{};
   int num_cus = 0;
-  unsigned long long timeout_ticks = 0;
+  int timeout_ms = 200;
+  unsigned long long timeout_ticks = 0;  // timeout_ms in ticks of the device's constant clock
+  double ticks_per_us = 100.0;           // that clock's rate (queried at upload)
   int dma_pages = 1;
   // device state
   int device = -1;
@@ -78,6 +80,7 @@ struct mk_plan {
   unsigned long long* d_trace = nullptr;
   bool trace_on = false;
   unsigned epoch = 0;
+  unsigned run_seq = 0;  // runs of either path; a bad token id is flagged with the run's number
   bool need_reset = false;
   std::vector<uint64_t> h_optab;
   // new sequence lengths without replanning: the attention tasks' first words
@@ -258,7 +261,7 @@ static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_
   c.ng = d.n_gate;
   c.nik = d.idx_head_dim;
   c.niq = Niq;
-  p->timeout_ticks = (unsigned long long)timeout_ms * 100000ull;
+  p->timeout_ms = timeout_ms;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o2 = off;
@@ -412,7 +415,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   c.qk_norm = d.qk_norm;
   c.eps = d.rms_eps;
   c.inv_sqrt_hd = (float)(1.0 / std::sqrt((double)d.head_dim));
-  p->timeout_ticks = (unsigned long long)timeout_ms * 100000ull;  // 100 MHz constant clock
+  p->timeout_ms = timeout_ms;
   // workspace layout (fp32 everywhere)
   const size_t B = batch, L = d.n_layers;
   size_t off = 0;
@@ -434,8 +437,9 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   p->off_ao = take(p->sz_ao * L);
   p->off_hidden = take(p->sz_hid * 2 * L);
   p->off_act = take(p->sz_act * L);
-  p->off_logits = take(B * c.V * 4);
   p->off_lmmax = take(B * c.T_v * 8);
+  // the step's outputs last
+  p->off_logits = take(B * c.V * 4);
   p->off_next = take(B * 4);
   p->ws_bytes = off;
   *out = p;
@@ -533,6 +537,13 @@ static mk_status ensure_device(mk_plan* p) {
     return MK_OK;
   }
   HIPCHK(hipGetDevice(&p->device), "hipGetDevice");
+  // the device's constant-rate clock (s_memrealtime), in kHz: trace ticks and
+  // the watchdog bound are counted in it
+  int clk_khz = 0;
+  HIPCHK(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, p->device), "hipDeviceGetAttribute clock");
+  if (clk_khz <= 0) return fail(MK_E_HIP, "the device reports no constant clock rate");
+  p->ticks_per_us = clk_khz / 1000.0;
+  p->timeout_ticks = (unsigned long long)p->timeout_ms * (unsigned long long)clk_khz;
   int ncu = 0;
   HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, p->device), "hipDeviceGetAttribute");
   int occ = 0;
@@ -572,23 +583,39 @@ static mk_status ensure_device(mk_plan* p) {
   return MK_OK;
 }
 
-static mk_status upload_optab(mk_plan* p, const std::vector<uint64_t>& t, hipStream_t s) {
-  if (t != p->h_optab) {
-    p->h_optab = t;
-    HIPCHK(hipMemcpyAsync(p->d_optab, p->h_optab.data(), t.size() * 8, hipMemcpyHostToDevice, s), "upload operand table");
+// Where a run's plan-owned device data lives: the plan's own buffers (mk_run,
+// mk_run_layerwise) or the library's static buffer (mk_run_noalloc).  cache is
+// the host copy of what the device operand table holds.
+struct Bind {
+  char* ws;
+  float* rope;
+  float* logits;
+  int* next;
+  uint64_t* optab;
+  std::vector<uint64_t>* cache;
+};
+static Bind own_bind(mk_plan* p) {
+  return Bind{p->d_ws, p->d_rope, (float*)(p->d_ws + p->off_logits), (int*)(p->d_ws + p->off_next), p->d_optab,
+              &p->h_optab};
+}
+
+static mk_status upload_optab(const Bind& b, const std::vector<uint64_t>& t, hipStream_t s) {
+  if (t != *b.cache) {
+    *b.cache = t;
+    HIPCHK(hipMemcpyAsync(b.optab, b.cache->data(), t.size() * 8, hipMemcpyHostToDevice, s), "upload operand table");
     HIPCHK(hipStreamSynchronize(s), "operand table sync");
   }
   return MK_OK;
 }
 
-static mk_status bind_glm(mk_plan* p, const mk_weights* w, void* kv, const void* xr, hipStream_t s) {
+static mk_status bind_glm(mk_plan* p, const mk_weights* w, void* kv, const void* xr, hipStream_t s, const Bind& b) {
   const mk_model_desc& d = p->desc;
   if (!w || !w->layer_ptrs || !kv || !xr) return fail(MK_E_INVALID, "null weight, cache or input pointer");
   for (int k = 0; k < MK_GLM_SLOTS; ++k)
     if (!w->layer_ptrs[k]) return fail(MK_E_INVALID, "null GLM weight pointer");
   const void* const* W = w->layer_ptrs;
   auto u = [](const void* q) { return (uint64_t)(uintptr_t)q; };
-  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(p->d_ws + off); };
+  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(b.ws + off); };
   const size_t M = p->batch, H = d.hidden;
   const uint64_t x = u(xr), r = u((const char*)xr + M * H * 2);
   const uint64_t kvc = u(kv), idc = u((const char*)kv + (size_t)p->n_seq * d.max_kv_len * (d.kv_lora + d.rope_dim) * 2);
@@ -633,7 +660,7 @@ static mk_status bind_glm(mk_plan* p, const mk_weights* w, void* kv, const void*
         q[mkd::QnA8] = ws(p->off_gqa8);
         q[mkd::QnAS] = ws(p->off_gqs);
         q[mkd::QnKv] = kvc;
-        q[mkd::QnRope] = u(p->d_rope);
+        q[mkd::QnRope] = u(b.rope);
         q[mkd::QnRows] = u(p->d_rows);
         break;
       case mk::kGQkvb:
@@ -642,7 +669,7 @@ static mk_status bind_glm(mk_plan* p, const mk_weights* w, void* kv, const void*
         q[mkd::GmA8] = ws(p->off_gqa8);
         q[mkd::GmAS] = ws(p->off_gqs);
         q[mkd::GmOut] = ws(p->off_gq);
-        q[mkd::GmRope] = u(p->d_rope);
+        q[mkd::GmRope] = u(b.rope);
         break;
       case mk::kGIdxq:
         q[mkd::GmW] = u(W[11]);
@@ -655,11 +682,12 @@ static mk_status bind_glm(mk_plan* p, const mk_weights* w, void* kv, const void*
         break;
     }
   }
-  return upload_optab(p, t, s);
+  return upload_optab(b, t, s);
 }
 
-static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const void* tokens, hipStream_t s) {
-  if (p->glm) return bind_glm(p, w, kv, tokens, s);
+static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const void* tokens, hipStream_t s,
+                               const Bind& b) {
+  if (p->glm) return bind_glm(p, w, kv, tokens, s, b);
   const mk_model_desc& d = p->desc;
   const int L = d.n_layers;
   if (!w || !w->layer_ptrs || !w->embed || !w->final_norm || !kv || !tokens)
@@ -672,7 +700,7 @@ static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const 
     }
   const size_t B = p->batch, hpg = p->c.hpg;
   auto u = [](const void* q) { return (uint64_t)(uintptr_t)q; };
-  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(p->d_ws + off); };
+  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(b.ws + off); };
   const size_t hid = p->sz_hid;
   auto xa = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l) * hid); };
   auto xb = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l + 1) * hid); };
@@ -698,7 +726,7 @@ static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const 
         r[mkd::AttnQkv] = ws(p->off_qkv + l * p->sz_qkv);
         r[mkd::AttnK] = u((const char*)kv + l * kvlayer);
         r[mkd::AttnV] = u((const char*)kv + l * kvlayer + kvlayer / 2);
-        r[mkd::AttnRope] = u(p->d_rope);
+        r[mkd::AttnRope] = u(b.rope);
         r[mkd::AttnOut] = ws(p->off_part + l * p->sz_part);
         r[mkd::AttnQn] = d.qk_norm ? u(W[4]) : 0;
         r[mkd::AttnKn] = d.qk_norm ? u(W[5]) : 0;
@@ -732,38 +760,52 @@ static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const 
         r[mkd::LmW] = u(d.tied_lm_head ? w->embed : w->lm_head);
         r[mkd::LmNorm] = u(w->final_norm);
         r[mkd::LmIn] = xb(L - 1);
-        r[mkd::LmLogits] = ws(p->off_logits);
+        r[mkd::LmLogits] = u(b.logits);
         r[mkd::LmMax] = ws(p->off_lmmax);
         break;
       case mk::kArgmax:
         r[mkd::AmMax] = ws(p->off_lmmax);
-        r[mkd::AmOut] = ws(p->off_next);
+        r[mkd::AmOut] = u(b.next);
         break;
       default:
         break;
     }
   }
   (void)hpg;
-  return upload_optab(p, t, s);
+  return upload_optab(b, t, s);
 }
 
 static mk_status launch_step(mk_plan* p, hipStream_t s);
 static mk_status launch_layerwise(mk_plan* p, hipStream_t s);
 
-static mkd::KArgs kargs(const mk_plan* p) {
+static mkd::KArgs kargs(const mk_plan* p, const int* queue, const uint64_t* optab, unsigned* counters, unsigned* err) {
   mkd::KArgs a{};
-  a.queue = p->d_queue;
-  a.optab = p->d_optab;
-  a.counters = p->d_counters;
+  a.queue = queue;
+  a.optab = optab;
+  a.counters = counters;
   a.num_events = std::max(1, p->P.num_events);
-  a.err = p->d_err;
+  a.err = err;
   a.trace = p->trace_on ? p->d_trace : nullptr;
   a.max_len = p->P.max_len;
   a.dma_pages = p->dma_pages;
   a.epoch = p->epoch;
+  a.run_id = p->run_seq;
   a.timeout_ticks = p->timeout_ticks;
   a.c = p->c;
   return a;
+}
+static mkd::KArgs kargs(const mk_plan* p) { return kargs(p, p->d_queue, p->d_optab, p->d_counters, p->d_err); }
+
+// The megakernel's launch arguments carry the run's epoch (its event waits
+// compare counters with epoch * target), so a captured launch would replay a
+// stale epoch: the persistent path refuses stream capture.
+static mk_status refuse_capture(hipStream_t s, const char* what) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIPCHK(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(MK_E_UNSUPPORTED, std::string(what) + " cannot be captured into a graph (each run's epoch is a launch "
+                                                      "argument); capture mk_run_layerwise instead");
+  return MK_OK;
 }
 
 mk_status mk_run(mk_plan* p, const mk_weights* w, void* kv_cache, const void* tokens, void* stream) {
@@ -771,21 +813,26 @@ mk_status mk_run(mk_plan* p, const mk_weights* w, void* kv_cache, const void* to
   if (!p) return fail(MK_E_INVALID, "null plan");
   if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
   hipStream_t s = (hipStream_t)stream;
-  mk_status st = ensure_device(p);
+  mk_status st = refuse_capture(s, "mk_run");
   if (st != MK_OK) return st;
-  st = bind_operands(p, w, kv_cache, tokens, s);
+  st = ensure_device(p);
+  if (st != MK_OK) return st;
+  st = bind_operands(p, w, kv_cache, tokens, s, own_bind(p));
   if (st != MK_OK) return st;
   return launch_step(p, s);
 }
 
 static mk_status launch_step(mk_plan* p, hipStream_t s) {
-  if (p->need_reset) {
+  // counters restart from zero after a failed run (some events stopped short of
+  // their targets) and before the epoch would wrap to 0, which marks "no error"
+  // in the watchdog record
+  if (p->need_reset || p->epoch == 0xFFFFFFFFu) {
     HIPCHK(hipMemsetAsync(p->d_counters, 0, counter_bytes(p), s), "reset counters");
     p->epoch = 0;
     p->need_reset = false;
   }
   p->epoch += 1;
-  if (p->epoch == 0) p->epoch = 1;  // 0 marks "no error" in the watchdog record
+  p->run_seq += 1;
   if (p->trace_on) HIPCHK(hipMemsetAsync(p->d_trace, 0, (size_t)p->num_cus * p->P.max_len * mkd::kTraceWords * 8, s), "clear trace");
   HIPCHK(mk::launch_megakernel(kargs(p), p->num_cus, s), "megakernel launch");
   return MK_OK;
@@ -798,12 +845,13 @@ mk_status mk_run_layerwise(mk_plan* p, const mk_weights* w, void* kv_cache, cons
   hipStream_t s = (hipStream_t)stream;
   mk_status st = ensure_device(p);
   if (st != MK_OK) return st;
-  st = bind_operands(p, w, kv_cache, tokens, s);
+  st = bind_operands(p, w, kv_cache, tokens, s, own_bind(p));
   if (st != MK_OK) return st;
   return launch_layerwise(p, s);
 }
 
 static mk_status launch_layerwise(mk_plan* p, hipStream_t s) {
+  p->run_seq += 1;
   mkd::KArgs a = kargs(p);
   a.trace = nullptr;
   if (p->n_streams == 1) {
@@ -959,12 +1007,14 @@ mk_status mk_run_steps(mk_plan* p, const mk_weights* w, void* kv_cache, const vo
   mk_status st = check_lengths(p, last);
   if (st != MK_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  st = refuse_capture(s, "mk_run_steps");
+  if (st != MK_OK) return st;
   st = ensure_device(p);
   if (st != MK_OK) return st;
   if (!p->d_tok) HIPCHK(hipMalloc((void**)&p->d_tok, (size_t)p->batch * 4), "hipMalloc tokens");
   if (!tokens) return fail(MK_E_INVALID, "null token pointer");
   HIPCHK(hipMemcpyAsync(p->d_tok, tokens, (size_t)p->batch * 4, hipMemcpyDeviceToDevice, s), "first tokens");
-  st = bind_operands(p, w, kv_cache, p->d_tok, s);
+  st = bind_operands(p, w, kv_cache, p->d_tok, s, own_bind(p));
   if (st != MK_OK) return st;
   const std::vector<int32_t> first(p->kv_len);
   size_t per = 0;
@@ -1078,6 +1128,8 @@ mk_status mk_plan_check(mk_plan* p, void* stream, mk_check* out) {
                                   ", slot " + std::to_string(err[3]) + ")");
   }
   if (bad) p->need_reset = true;
+  if (p->run_seq != 0 && err[7] == p->run_seq)
+    return fail(MK_E_INVALID, "an input token id was outside [0, vocab) (the step ran on the clamped id)");
   return MK_OK;
 }
 
@@ -1100,7 +1152,29 @@ mk_status mk_plan_trace(mk_plan* p, void* stream, uint64_t* host_out, size_t byt
   if (bytes < need) return fail(MK_E_INVALID, "host buffer too small");
   HIPCHK(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
   HIPCHK(hipMemcpy(host_out, p->d_trace, need, hipMemcpyDeviceToHost), "read trace");
-  *ticks_per_us = 100.0;
+  *ticks_per_us = p->ticks_per_us;
+  return MK_OK;
+}
+
+mk_status mk_plan_poison_workspace(mk_plan* p, void* stream) {
+  g_err.clear();
+  if (!p) return fail(MK_E_INVALID, "null plan");
+  if (p->graph_only || !p->uploaded) return fail(MK_E_STATE, "the plan has not run");
+  HIPCHK(hipMemsetAsync(p->d_ws, 0xFF, p->ws_bytes, (hipStream_t)stream), "poison workspace");
+  return MK_OK;
+}
+
+mk_status mk_plan_debug_raise_wait(mk_plan* p, int32_t event, int32_t delta) {
+  g_err.clear();
+  if (!p) return fail(MK_E_INVALID, "null plan");
+  if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
+  if (event < 0 || event >= p->P.num_events) return fail(MK_E_INVALID, "event out of range");
+  for (size_t t = 0; t * 32 < p->P.queue.size(); ++t) {
+    int32_t* w = &p->P.queue[t * 32];
+    if (w[mkd::WOpcode] != mkd::OpNoop && w[mkd::WWaitCnt] && w[mkd::WWaitEv] == event) w[mkd::WWaitTgt] += delta;
+  }
+  if (p->uploaded)
+    HIPCHK(hipMemcpy(p->d_queue, p->P.queue.data(), p->P.queue.size() * 4, hipMemcpyHostToDevice), "upload queue");
   return MK_OK;
 }
 

@@ -107,6 +107,7 @@ struct KArgs {
   int max_len;
   int dma_pages;  // pages in flight per loader wave (1 to 3; batch-1 interpreter)
   unsigned epoch;
+  unsigned run_id;  // sequence number of the run (megakernel or layerwise), for err[7]
   unsigned long long timeout_ticks;
   Consts c;
 };
@@ -232,7 +233,7 @@ struct CohT {
 };
 
 // token id of sequence 0, clamped into [0, vocab) so that a bad id cannot index
-// outside the embedding
+// outside the embedding (the run is flagged as failed: see check_tokens)
 __device__ __forceinline__ int token_of(const GLB int* tokens, int b, int V) {
   const int t = tokens[b];
   return t < 0 ? 0 : (t >= V ? V - 1 : t);

@@ -7,10 +7,12 @@
 // trigger counter), split over wavefront roles as in the MegaRTP article,
 // section 3 (controller / loader / consumer / storer warps) and section 4
 // ("Device-side execution", "shared-memory paging"):
-//   wave 0    controller: waits for each instruction's event counter
-//             (agent-scope acquire) and publishes "ready" in LDS;
-//   wave 1    storer: after the compute waves finish an instruction, an
-//             agent-scope release and one atomic add on its trigger counter;
+//   wave 0    controller: stages each instruction's record in LDS, waits
+//             for its event counter and publishes "ready" in LDS (the reads
+//             that follow need no acquire: see CohT in mk_device.hpp);
+//   wave 1    storer: after the compute waves finish an instruction, runs
+//             the epilogue, waits for the outputs' stores to complete and
+//             adds to the trigger counter (relaxed, agent scope);
 //   waves 2-3 weight loaders: stream every instruction's weight (or K/V) bytes
 //             HBM -> LDS with LDS-DMA (global_load_lds_dwordx4), alternating
 //             16 KiB pages of a 9-page ring; they never wait on events, only on
@@ -132,6 +134,17 @@ __device__ bool wait_lds_ge(const KArgs& a, LDS LT* L, LDS int* p, int v, int ki
       }
     }
   }
+}
+
+// Input token ids outside [0, vocab): the tiles read a clamped id (no access
+// leaves the embedding), and the run is flagged in err[7] (= the run's id), so
+// that mk_plan_check reports it.  Done by the layer-0 QKV tiles, which are the
+// first to read the tokens.
+__device__ __forceinline__ void check_tokens(const KArgs& a, const Meta& m) {
+  if (m.w(WOpcode) != OpQkv || m.w(WLayer) != 0 || m.q(QkvX) != 0) return;
+  const int lane = lane_id();
+  const int t = lane < a.c.B ? ((const GLB int*)m.q(QkvTokens))[lane] : 0;
+  if (t < 0 || t >= a.c.V) __hip_atomic_store(&a.err[7], a.run_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ const CST int* instr(const KArgs& a, int i) {
@@ -271,6 +284,7 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
     if (op == OpNoop) break;
     const int sl = i & 3;
     const bool gemv = is_gemv(op);
+    if constexpr (!LT::GLM) check_tokens(a, m);
     if constexpr (LT::GLM) {
       if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
       if (glm_is_gemm(op)) glm_epilogue(m, a.c, &L->c.part[sl][0][0]);
@@ -300,8 +314,9 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
       const Meta nx = load_meta(L->meta[(i + 1) % kMeta]);
       const bool same_next = nx.w(WOpcode) != OpNoop && nx.w(WSigCnt) && nx.w(WSigEv) == m.w(WSigEv);
       if (!same_next) {
-        // every output of the run was stored agent-coherent (by this wave or
-        // by the compute waves before they arrived): wait for completion, then count
+        // every output of the run was stored agent-coherent, by this wave or by
+        // the compute waves, which waited for their stores before arriving:
+        // wait for this wave's stores, then count
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (lane == 0)
           __hip_atomic_fetch_add(a.counters + ctr_word(m.w(WSigEv), blockIdx.x % kCtrSub, a.num_events), pending,
@@ -367,9 +382,15 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
           __builtin_amdgcn_s_sleep(1);
           if (lds_ld_asm(rel_base + 4 * slot) >= kNW * gen) break;
           if ((it & 31) == 31) {
-            if (aborted(L)) return;
+            // leave only once this wave's page DMA has landed (the workgroup's
+            // LDS must not be written after its waves have ended)
+            if (aborted(L)) {
+              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+              return;
+            }
             if (now_ticks() - t0 > a.timeout_ticks) {
               record_error(a, L, ErrFree, i, slot, 0, gen);
+              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
               return;
             }
           }
@@ -562,9 +583,13 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
       if (!gemv) release();
     }
     if (tr && lane == 0) tr[12 + cw] = now_ticks();
-    // arrival: GEMV partials are in LDS; other ops wrote global memory, which
-    // must be complete before the storer signals (workgroup release = vmcnt(0))
-    if (!gemv) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // arrival: GEMV partials are in LDS; other ops stored their results to
+    // global memory themselves, and the storer's counter add must not overtake
+    // those stores.  A workgroup-scope release does not wait for them on this
+    // target (the workgroup shares one CU, so it orders only LDS), and the
+    // storer's own vmcnt wait covers only its own stores: each compute wave
+    // waits for its stores to complete before it arrives.
+    if (!gemv) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0) __hip_atomic_fetch_add(&L->c.arrive[sl], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
@@ -640,6 +665,7 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
     }
     return;
   }
+  if (cw == 0) check_tokens(a, m);
   if (is_gemv(op)) {
     const GemvIn gi = gemv_input(m, a.c);
     if constexpr (MB) {
