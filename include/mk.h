@@ -360,6 +360,27 @@ mk_status mk_plan_poison_workspace(mk_plan* plan, void* stream);
  * grid drains and exits normally and mk_plan_check reports MK_E_TIMEOUT. */
 mk_status mk_plan_debug_raise_wait(mk_plan* plan, int32_t event, int32_t delta);
 
+/* mk_run for callers that cannot allocate device memory (code under graph
+ * capture elsewhere in the process, tight serving loops, harnesses that forbid
+ * hipMalloc): the plan's queue, counters, watchdog record, operand table, RoPE
+ * table and workspace live in one static device buffer of the library (64 MiB
+ * per GPU, held from first use until the process ends), and the step's outputs
+ * go to the caller's buffers: logits device fp32 [batch][vocab], next_tokens
+ * device int32 [batch].  It never calls hipMalloc or hipFree.  Llama-family
+ * plans only; a plan whose state exceeds the buffer (see mk_noalloc_bytes) gets
+ * MK_E_UNSUPPORTED.  Every call on one GPU shares that buffer and leaves its
+ * contents there: the queue and RoPE table are copied in when another plan (or
+ * another state of this plan) used it last, and the counters and watchdog
+ * record are cleared on the stream at every call.  Calls that overlap on one
+ * GPU (on different streams, or from different threads without ordering) race
+ * on the buffer and give undefined results.  mk_plan_check and mk_plan_output
+ * do not see these runs.  Not capturable (MK_E_UNSUPPORTED under capture). */
+mk_status mk_run_noalloc(mk_plan* plan, const mk_weights* weights, void* kv_cache, const void* tokens, void* logits,
+                         void* next_tokens, void* stream);
+/* Bytes of the static buffer a plan needs (0 for plans mk_run_noalloc does not
+ * run), and the buffer's size. */
+mk_status mk_noalloc_bytes(const mk_plan* plan, size_t* need, size_t* limit);
+
 #ifdef __cplusplus
 }
 #endif

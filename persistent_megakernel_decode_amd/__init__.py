@@ -37,7 +37,7 @@ LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_nor
 EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_plan_export", "mk_run",
             "mk_run_layerwise", "mk_plan_output", "mk_plan_copy_output", "mk_plan_check", "mk_plan_set_trace",
             "mk_plan_trace", "mk_plan_free", "mk_plan_set_kv_len", "mk_run_steps", "mk_plan_debug_raise_wait",
-            "mk_plan_poison_workspace")
+            "mk_run_noalloc", "mk_noalloc_bytes", "mk_plan_poison_workspace")
 
 i32, u32, f32, vp, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -112,6 +112,8 @@ def lib():
         L.mk_plan_trace.argtypes = [vp, vp, vp, sz, P(ctypes.c_double)]
         L.mk_plan_debug_raise_wait.argtypes = [vp, i32, i32]
         L.mk_plan_poison_workspace.argtypes = [vp, vp]
+        L.mk_run_noalloc.argtypes = [vp, P(Weights), vp, vp, vp, vp, vp]
+        L.mk_noalloc_bytes.argtypes = [vp, P(sz), P(sz)]
         L.mk_plan_free.argtypes = [vp]
         L.mk_plan_free.restype = None
         for n in EXPORTED:
@@ -213,6 +215,21 @@ class Plan:
 
     def run_layerwise(self, weights, kv_cache, tokens, stream=None):
         self.run(weights, kv_cache, tokens, stream, layerwise=True)
+
+    def run_noalloc(self, weights, kv_cache, tokens, logits, next_tokens, stream=None):
+        """mk_run_noalloc: the step with the plan's device state in the library's
+        static buffer; logits (float32 [batch * vocab]) and next_tokens (int32
+        [batch]) are the caller's device tensors."""
+        w = weights.struct if isinstance(weights, DeviceWeights) else weights
+        s = vp(stream.cuda_stream if stream is not None else current_stream())
+        _check(lib().mk_run_noalloc(self._h, ctypes.byref(w), vp(kv_cache.data_ptr()), vp(tokens.data_ptr()),
+                                    vp(logits.data_ptr()), vp(next_tokens.data_ptr()), s))
+
+    def noalloc_bytes(self):
+        """(bytes of the static buffer this plan needs, the buffer's size)"""
+        need, limit = sz(), sz()
+        _check(lib().mk_noalloc_bytes(self._h, ctypes.byref(need), ctypes.byref(limit)))
+        return need.value, limit.value
 
     def poison_workspace(self, stream=None):
         """mk_plan_poison_workspace: every intermediate and output to NaN."""

@@ -8,14 +8,24 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "mk.h"
 #include "mk_device.hpp"
 #include "plan.hpp"
+
+// Device memory of the allocation-free entry point (mk_run_noalloc): one
+// static buffer per GPU, held from the library's load on that GPU until the
+// process ends.  In host code 'scratch' names a host-side stand-in, never the
+// device address: that is taken once per device with hipGetSymbolAddress
+// (scratch_base) and only that address is handed to kernels and copies.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace mk {
 hipError_t launch_megakernel(const mkd::KArgs& a, int num_cus, hipStream_t s);
@@ -46,6 +56,9 @@ mk_status hip_fail(hipError_t e, const char* what) {
 
 struct mk_plan {
   bool graph_only = false;
+  // identity of the plan's host state (queue words, RoPE table): uid is unique
+  // per plan, version changes whenever that state is patched
+  uint64_t uid = 0, version = 0;
   mk::Plan P;
   mk_model_desc desc{};
   int batch = 0;
@@ -112,6 +125,13 @@ struct mk_plan {
   size_t off_gn = 0, off_ga8 = 0, off_gas = 0, off_gqkva = 0, off_gqa8 = 0, off_gqs = 0, off_gr = 0, off_gq = 0,
          off_gqidx = 0, off_ggate = 0;
 };
+
+static std::atomic<uint64_t> g_plan_uid{0};
+static mk_plan* new_plan() {
+  auto* p = new mk_plan();
+  p->uid = ++g_plan_uid;
+  return p;
+}
 
 extern "C" {
 
@@ -220,7 +240,7 @@ static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_
       if (j / d.rows_per_seq == m / d.rows_per_seq && kl[j] == kl[m])
         return fail(MK_E_INVALID, "two token rows of one request write the same cache position");
   }
-  auto* p = new mk_plan();
+  auto* p = new_plan();
   p->desc = d;
   p->batch = M;
   p->kv_len = kl;
@@ -311,7 +331,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   for (int b = 0; b < batch; ++b)
     if (kl[b] < 0 || kl[b] + 1 > d.max_kv_len) return fail(MK_E_UNSUPPORTED, "kv_len[b] + 1 must be <= max_kv_len");
 
-  auto* p = new mk_plan();
+  auto* p = new_plan();
   p->desc = d;
   p->batch = batch;
   p->kv_len = kl;
@@ -438,7 +458,8 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   p->off_hidden = take(p->sz_hid * 2 * L);
   p->off_act = take(p->sz_act * L);
   p->off_lmmax = take(B * c.T_v * 8);
-  // the step's outputs last
+  // the step's outputs last: the allocation-free entry point keeps everything
+  // before them in its static buffer and writes the outputs to the caller's
   p->off_logits = take(B * c.V * 4);
   p->off_next = take(B * 4);
   p->ws_bytes = off;
@@ -452,7 +473,7 @@ mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_ed
   if (!out || (n_ops > 0 && !ops) || (n_edges > 0 && !edges) || n_ops < 0 || n_edges < 0)
     return fail(MK_E_INVALID, "null argument");
   *out = nullptr;
-  auto* p = new mk_plan();
+  auto* p = new_plan();
   p->graph_only = true;
   std::vector<mk::GraphEdge> ge;
   for (int i = 0; i < n_ops; ++i) {
@@ -911,6 +932,7 @@ static mk_status check_lengths(const mk_plan* p, const std::vector<int32_t>& kv)
 // attention patches (word index, lo, hi, pos) to out (4 int32 each) if given.
 static void apply_lengths(mk_plan* p, const std::vector<int32_t>& kv, int32_t* out) {
   p->kv_len = kv;
+  p->version += 1;
   const int S = p->opts.attn_splits;
   for (size_t j = 0; j < p->attn_words.size(); ++j) {
     int32_t* w = &p->P.queue[p->attn_words[j]];
@@ -1156,6 +1178,110 @@ mk_status mk_plan_trace(mk_plan* p, void* stream, uint64_t* host_out, size_t byt
   return MK_OK;
 }
 
+// ---- the allocation-free entry point -----------------------------------------
+// Per device: the address of the static buffer, and which plan state it holds.
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchDev {
+  void* base = nullptr;                 // device address of 'scratch' on this device
+  uint64_t owner_uid = 0, owner_ver = 0;  // plan whose queue and RoPE table it holds
+  std::vector<uint64_t> optab;          // host copy of its operand table
+};
+std::mutex g_scratch_mu;
+ScratchDev g_scratch[kMaxDevices];
+
+size_t r256(size_t v) { return (v + 255) / 256 * 256; }
+
+// The buffer's layout for plan p: queue, counters, watchdog record, operand
+// table, RoPE table, then the workspace up to (not including) the outputs.
+struct ScratchLayout {
+  size_t queue, counters, err, optab, rope, ws, total;
+};
+ScratchLayout scratch_layout(const mk_plan* p) {
+  ScratchLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += r256(bytes);
+    return o;
+  };
+  l.queue = take(p->P.queue.size() * 4);
+  l.counters = take((size_t)mkd::kCtrSub * std::max(1, p->P.num_events) * mkd::kCtrStride * 4);
+  l.err = take(64);
+  l.optab = take(p->ops.size() * 16 * 8);
+  l.rope = take((size_t)p->batch * p->c.hd * 4);
+  l.ws = take(p->off_logits);
+  l.total = off;
+  return l;
+}
+}  // namespace
+
+mk_status mk_run_noalloc(mk_plan* p, const mk_weights* w, void* kv_cache, const void* tokens, void* logits,
+                         void* next_tokens, void* stream) {
+  g_err.clear();
+  if (!p || !logits || !next_tokens) return fail(MK_E_INVALID, "null plan or output pointer");
+  if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
+  if (p->glm) return fail(MK_E_UNSUPPORTED, "mk_run_noalloc runs Llama-family plans only");
+  hipStream_t s = (hipStream_t)stream;
+  mk_status st = refuse_capture(s, "mk_run_noalloc");
+  if (st != MK_OK) return st;
+  int dev = -1;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MK_E_UNSUPPORTED, "device index out of range");
+  const ScratchLayout lay = scratch_layout(p);
+  if (lay.total > kScratchBytes)
+    return fail(MK_E_UNSUPPORTED, "the plan needs " + std::to_string(lay.total) + " bytes of device scratch; mk_run_noalloc "
+                                  "holds at most " + std::to_string(kScratchBytes) + " (use mk_run)");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchDev& sd = g_scratch[dev];
+  if (!sd.base) {
+    // once per device, with that device current
+    void* ptr = nullptr;
+    HIPCHK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(MK_E_HIP, "hipGetSymbolAddress(scratch) returned null");
+    sd.base = ptr;
+  }
+  // the grid must be co-resident (queries only, no allocation)
+  int ncu = 0, occ = 0;
+  HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+  HIPCHK(mk::megakernel_occupancy(p->c.hd, p->batch, false, &occ), "occupancy");
+  if (p->num_cus > ncu || occ < 1) return fail(MK_E_UNSUPPORTED, "the persistent grid cannot be co-resident");
+  int clk_khz = 0;
+  HIPCHK(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, dev), "hipDeviceGetAttribute clock");
+  if (clk_khz <= 0) return fail(MK_E_HIP, "the device reports no constant clock rate");
+  char* base = (char*)sd.base;
+  int* queue = (int*)(base + lay.queue);
+  unsigned* counters = (unsigned*)(base + lay.counters);
+  unsigned* err = (unsigned*)(base + lay.err);
+  uint64_t* optab = (uint64_t*)(base + lay.optab);
+  float* rope = (float*)(base + lay.rope);
+  char* ws = base + lay.ws;
+  // the buffer keeps the last call's contents: the queue and RoPE table are
+  // copied in when another plan (or another state of this one) used it last
+  if (sd.owner_uid != p->uid || sd.owner_ver != p->version) {
+    if (p->h_rope.empty()) rope_table(p);
+    HIPCHK(hipMemcpyAsync(queue, p->P.queue.data(), p->P.queue.size() * 4, hipMemcpyHostToDevice, s), "upload queue");
+    HIPCHK(hipMemcpyAsync(rope, p->h_rope.data(), p->h_rope.size() * 4, hipMemcpyHostToDevice, s), "upload rope");
+    sd.optab.clear();  // the table sits elsewhere in the new layout
+    sd.owner_uid = p->uid;
+    sd.owner_ver = p->version;
+  }
+  Bind b{ws, rope, (float*)logits, (int*)next_tokens, optab, &sd.optab};
+  st = bind_operands(p, w, kv_cache, tokens, s, b);
+  if (st != MK_OK) return st;
+  // every call starts its counters and watchdog record from zero, at epoch 1
+  HIPCHK(hipMemsetAsync(counters, 0, (size_t)mkd::kCtrSub * std::max(1, p->P.num_events) * mkd::kCtrStride * 4, s),
+         "clear counters");
+  HIPCHK(hipMemsetAsync(err, 0, 64, s), "clear watchdog record");
+  mkd::KArgs a = kargs(p, queue, optab, counters, err);
+  a.epoch = 1;
+  a.run_id = 1;
+  a.trace = nullptr;
+  a.timeout_ticks = (unsigned long long)p->timeout_ms * (unsigned long long)clk_khz;
+  HIPCHK(mk::launch_megakernel(a, p->num_cus, s), "megakernel launch");
+  return MK_OK;
+}
+
 mk_status mk_plan_poison_workspace(mk_plan* p, void* stream) {
   g_err.clear();
   if (!p) return fail(MK_E_INVALID, "null plan");
@@ -1173,8 +1299,17 @@ mk_status mk_plan_debug_raise_wait(mk_plan* p, int32_t event, int32_t delta) {
     int32_t* w = &p->P.queue[t * 32];
     if (w[mkd::WOpcode] != mkd::OpNoop && w[mkd::WWaitCnt] && w[mkd::WWaitEv] == event) w[mkd::WWaitTgt] += delta;
   }
+  p->version += 1;
   if (p->uploaded)
     HIPCHK(hipMemcpy(p->d_queue, p->P.queue.data(), p->P.queue.size() * 4, hipMemcpyHostToDevice), "upload queue");
+  return MK_OK;
+}
+
+mk_status mk_noalloc_bytes(const mk_plan* p, size_t* need, size_t* limit) {
+  g_err.clear();
+  if (!p || !need || !limit) return fail(MK_E_INVALID, "null argument");
+  *need = (p->graph_only || p->glm) ? 0 : scratch_layout(p).total;
+  *limit = kScratchBytes;
   return MK_OK;
 }
 
