@@ -190,7 +190,32 @@ mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_ed
  *   task-id range of its successors.  task_trigger/task_wait: per task, the
  *   event it triggers / waits on, or -1.  op_table: int32 [num_ops][8] rows
  *   (opcode, spec, layer, grid x, y, z, tasks, 0).  edge_kept: per input edge, 0
- *   when dropped as residual. */
+ *   when dropped as residual.
+ *   tile_opts: the tile options the plan was built with, defaults resolved:
+ *   num_cus, gemv_rows, gateup_outs, down_rows, lm_rows, attn_splits (zeros
+ *   for GLM and graph plans).  op_slots: the operand table's layout, int32
+ *   [num_ops][16]: the kind (MK_SLOT_*) of the tensor each slot of an op's row
+ *   points at, 0 for an unused slot (the row itself holds the addresses; one
+ *   row per op, shared by all of its tile instructions: MegaRTP article,
+ *   section 4, "OperandPtrTable"). */
+enum {
+  MK_SLOT_NONE = 0,
+  /* weights (Llama family) */
+  MK_SLOT_ATTN_NORM = 1, MK_SLOT_WQ, MK_SLOT_WK, MK_SLOT_WV, MK_SLOT_Q_NORM, MK_SLOT_K_NORM, MK_SLOT_WO,
+  MK_SLOT_FFN_NORM, MK_SLOT_W_GATE, MK_SLOT_W_UP, MK_SLOT_W_DOWN, MK_SLOT_EMBED, MK_SLOT_FINAL_NORM,
+  MK_SLOT_LM_HEAD,
+  /* caller inputs and caches */
+  MK_SLOT_TOKENS = 20, MK_SLOT_K_CACHE, MK_SLOT_V_CACHE,
+  /* plan-owned data */
+  MK_SLOT_ROPE = 30, MK_SLOT_QKV, MK_SLOT_ATTN_PART, MK_SLOT_ATTN_OUT, MK_SLOT_HIDDEN_ATTN, MK_SLOT_HIDDEN_FFN,
+  MK_SLOT_FFN_ACT, MK_SLOT_LOGITS, MK_SLOT_LM_MAX, MK_SLOT_NEXT_TOKEN,
+  /* the GLM pre-attention path: inputs, weights (codes, scales), caches,
+     intermediates and outputs */
+  MK_SLOT_G_X = 50, MK_SLOT_G_R, MK_SLOT_G_ATTN_NORM, MK_SLOT_G_W, MK_SLOT_G_W_SCALE, MK_SLOT_G_Q_A_NORM,
+  MK_SLOT_G_KV_A_NORM, MK_SLOT_G_KV_CACHE, MK_SLOT_G_IDX_CACHE, MK_SLOT_G_ROWS, MK_SLOT_G_R_OUT, MK_SLOT_G_NORM,
+  MK_SLOT_G_ACT, MK_SLOT_G_ACT_SCALE, MK_SLOT_G_QKVA, MK_SLOT_G_QA, MK_SLOT_G_QA_SCALE, MK_SLOT_G_Q,
+  MK_SLOT_G_QIDX, MK_SLOT_G_GATE
+};
 typedef struct {
   int32_t num_cus, max_len, num_tasks, num_events, num_ops, num_edges;
   const int32_t* queue;
@@ -201,6 +226,8 @@ typedef struct {
   const int32_t* task_wait;
   const int32_t* op_table;
   const uint8_t* edge_kept;
+  int32_t tile_opts[6];
+  const int32_t* op_slots;
 } mk_plan_view;
 mk_status mk_plan_export(const mk_plan* plan, mk_plan_view* out);
 

@@ -55,6 +55,8 @@ def lib(precision="f64"):
         vp, ci, cd = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         L.oracle_decode_step.argtypes = [ctypes.POINTER(_Model), vp, ci, vp, vp, vp, vp, vp]
         L.oracle_decode_step.restype = ci
+        L.oracle_decode_step_ex.argtypes = [ctypes.POINTER(_Model), vp, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_decode_step_ex.restype = ci
         L.oracle_rmsnorm.argtypes = [ci, vp, vp, cd, vp]
         L.oracle_matvec.argtypes = [ci, ci, vp, vp, vp]
         L.oracle_rope.argtypes = [ci, ci, cd, vp]
@@ -125,12 +127,15 @@ def argmax(v, precision="f64"):
     return int(lib(precision).oracle_argmax(v.size, _p(v)))
 
 
-def decode_step(inputs, precision="f64", round_new_kv=True, kv_cache=None):
+def decode_step(inputs, precision="f64", round_new_kv=True, kv_cache=None, intermediates=False):
     """Run one decode step on the host.
 
     ``inputs`` is the dict made by ``synth.make_inputs``.  The KV cache is
     copied (or ``kv_cache`` is updated in place when given).  Returns
-    dict(logits [B, V], next [B] int32, kv_cache).
+    dict(logits [B, V], next [B] int32, kv_cache), and with ``intermediates``
+    also hidden [L, 2, B, H] (residual stream after each layer's attention and
+    FFN blocks) and qkv [L, B, n_q + 2 n_kv, head_dim] (projections before the
+    q/k norm and RoPE).
     """
     cfg, w = inputs["cfg"], inputs["weights"]
     L, B = cfg["n_layers"], cfg["batch"]
@@ -157,8 +162,18 @@ def decode_step(inputs, precision="f64", round_new_kv=True, kv_cache=None):
     tokens = np.ascontiguousarray(inputs["tokens"], dtype=np.int32)
     logits = np.empty((B, cfg["vocab"]), dtype=_dt(precision))
     nxt = np.empty(B, dtype=np.int32)
-    rc = lib(precision).oracle_decode_step(ctypes.byref(m), ctypes.cast(table, ctypes.c_void_p), B,
-                                           _p(kv_len), _p(tokens), _p(kv), _p(logits), _p(nxt))
+    hid = qkv = None
+    if intermediates:
+        nh = cfg["n_q_heads"] + 2 * cfg["n_kv_heads"]
+        hid = np.empty((L, 2, B, cfg["hidden"]), dtype=_dt(precision))
+        qkv = np.empty((L, B, nh, cfg["head_dim"]), dtype=_dt(precision))
+    rc = lib(precision).oracle_decode_step_ex(ctypes.byref(m), ctypes.cast(table, ctypes.c_void_p), B,
+                                              _p(kv_len), _p(tokens), _p(kv), _p(logits), _p(nxt),
+                                              _p(hid) if hid is not None else None,
+                                              _p(qkv) if qkv is not None else None)
     if rc != 0:
         raise ValueError("oracle_decode_step rejected its arguments")
-    return dict(logits=logits, next=nxt, kv_cache=kv)
+    out = dict(logits=logits, next=nxt, kv_cache=kv)
+    if intermediates:
+        out.update(hidden=hid, qkv=qkv)
+    return out

@@ -166,10 +166,14 @@ int oracle_argmax(int n, const real* v) {
  * [n_layers * N_SLOTS + 0/1/2] (lm_head may be NULL when tied).
  * kv_cache: bf16 [L][2][B][n_kv][kv_capacity][head_dim]; row kv_len[b] of
  * every (layer, K|V, b, head) is written.  logits: [B][vocab].
+ * Optional intermediates (NULL to skip): hidden_out [L][2][B][hidden], the
+ * residual stream after each layer's attention block and after its FFN block;
+ * qkv_out [L][B][(n_q + 2 n_kv) head_dim], each layer's q, k, v projections
+ * (q heads, then k heads, then v heads) before the q/k norm and RoPE.
  * Returns 0, or -1 on an invalid argument. */
-int oracle_decode_step(const oracle_model* m, const uint16_t* const* weights, int batch,
-                       const int32_t* kv_len, const int32_t* tokens, uint16_t* kv_cache,
-                       real* logits, int32_t* next_tokens) {
+int oracle_decode_step_ex(const oracle_model* m, const uint16_t* const* weights, int batch,
+                          const int32_t* kv_len, const int32_t* tokens, uint16_t* kv_cache,
+                          real* logits, int32_t* next_tokens, real* hidden_out, real* qkv_out) {
   const int H = m->hidden, nq = m->n_q_heads, nkv = m->n_kv_heads, d = m->head_dim, F = m->ffn;
   const int V = m->vocab, L = m->n_layers, cap = m->kv_capacity;
   if (nkv <= 0 || nq % nkv || d % 2 || batch <= 0) return -1;
@@ -203,6 +207,12 @@ int oracle_decode_step(const oracle_model* m, const uint16_t* const* weights, in
       oracle_matvec(nq * d, H, W[SLOT_WQ], y, q);
       oracle_matvec(nkv * d, H, W[SLOT_WK], y, k);
       oracle_matvec(nkv * d, H, W[SLOT_WV], y, v);
+      if (qkv_out) {
+        real* dst = qkv_out + ((size_t)l * batch + b) * (size_t)(nq + 2 * nkv) * d;
+        memcpy(dst, q, sizeof(real) * nq * d);
+        memcpy(dst + (size_t)nq * d, k, sizeof(real) * nkv * d);
+        memcpy(dst + (size_t)(nq + nkv) * d, v, sizeof(real) * nkv * d);
+      }
       if (m->qk_norm) {
         for (int h = 0; h < nq; ++h) {
           oracle_rmsnorm(d, q + h * d, W[SLOT_Q_NORM], m->rms_eps, t);
@@ -233,6 +243,7 @@ int oracle_decode_step(const oracle_model* m, const uint16_t* const* weights, in
       }
       oracle_matvec(H, nq * d, W[SLOT_WO], o, t);
       for (int i = 0; i < H; ++i) x[i] += t[i];
+      if (hidden_out) memcpy(hidden_out + (((size_t)l * 2 + 0) * batch + b) * H, x, sizeof(real) * H);
       /* feed-forward block */
       oracle_rmsnorm(H, x, W[SLOT_FFN_NORM], m->rms_eps, y);
       oracle_matvec(F, H, W[SLOT_W_GATE], y, g);
@@ -240,6 +251,7 @@ int oracle_decode_step(const oracle_model* m, const uint16_t* const* weights, in
       for (int i = 0; i < F; ++i) g[i] = oracle_silu(g[i]) * u[i];
       oracle_matvec(H, F, W[SLOT_W_DOWN], g, t);
       for (int i = 0; i < H; ++i) x[i] += t[i];
+      if (hidden_out) memcpy(hidden_out + (((size_t)l * 2 + 1) * batch + b) * H, x, sizeof(real) * H);
     }
     oracle_rmsnorm(H, x, final_norm, m->rms_eps, y);
     oracle_matvec(V, H, lm, y, logits + (size_t)b * V);
@@ -247,4 +259,10 @@ int oracle_decode_step(const oracle_model* m, const uint16_t* const* weights, in
   }
   free(x); free(y); free(q); free(k); free(v); free(kr); free(vr); free(o); free(t); free(g); free(u);
   return 0;
+}
+
+int oracle_decode_step(const oracle_model* m, const uint16_t* const* weights, int batch,
+                       const int32_t* kv_len, const int32_t* tokens, uint16_t* kv_cache,
+                       real* logits, int32_t* next_tokens) {
+  return oracle_decode_step_ex(m, weights, batch, kv_len, tokens, kv_cache, logits, next_tokens, NULL, NULL);
 }

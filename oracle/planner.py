@@ -373,47 +373,19 @@ def plan_graph(ops, edges, num_cus):
 # ---------------------------------------------------------------------------
 # Llama-family decode step as an operator DAG
 # ---------------------------------------------------------------------------
-DEFAULT_OPTS = dict(num_cus=256, gemv_rows=0, gateup_outs=0, down_rows=0, lm_rows=0, attn_splits=0)
+# The pages fix no tile size and no split count (the CMU 15-779 lecture 7 notes,
+# section 5.1, use 16-row tiles and 16 KV splits as one example), so the
+# reference planner takes all of them as inputs; the library chooses its own
+# and both are fed the same values.
+MODEL_OPTS = ("num_cus", "gemv_rows", "gateup_outs", "down_rows", "lm_rows", "attn_splits")
 
 
-def resolve_opts(desc, batch, kv_len, opts=None):
-    """Fill the 0 (default) fields: tiles of about 64 KiB of bf16 weights.
-    gemv_rows = clamp(32768 // hidden, 4, 16); gateup_outs = gemv_rows // 2;
-    down_rows = clamp(32768 // ffn, 1, 16) at batch 1 (the batch-1 GEMV holds a tile
-    in registers), clamp(131072 // (2 * ffn), 1, 16) above (a batched tile is read
-    from the 128 KiB page ring and may fill it: fewer re-reads of the sequences'
-    activations per weight row); lm_rows = gemv_rows;
-    attn_splits = clamp(ceil((max kv + 1) / 64), 1, 32), lowered to
-    max(1, ceil(2 * num_cus / (batch * n_kv_heads))) if that is smaller (about two
-    attention tasks per compute unit), then raised until one split's K and V rows
-    (2 * rows * head_dim * 2 bytes) fit in 64 KiB -- or in half the interpreter's
-    page ring (72 KiB at batch 1, 64 KiB above) while the attention tasks still
-    fit on the compute units at one each, since one more split would then put a
-    second task on some units.  (A tuning rule of this implementation, not of the
-    pages.)"""
-    o = dict(DEFAULT_OPTS)
-    o.update({k: v for k, v in (opts or {}).items() if v})
-    H, F, hd = desc["hidden"], desc["ffn"], desc["head_dim"]
-    if not o["gemv_rows"]:
-        o["gemv_rows"] = max(4, min(16, 32768 // H))
-    if not o["gateup_outs"]:
-        o["gateup_outs"] = max(1, o["gemv_rows"] // 2)
-    if not o["down_rows"]:
-        o["down_rows"] = max(1, min(16, (32768 if len(kv_len) == 1 else 131072 // 2) // F))
-    if not o["lm_rows"]:
-        o["lm_rows"] = o["gemv_rows"]
-    if not o["attn_splits"]:
-        n = int(max(kv_len)) + 1
-        S = max(1, min(32, ceil_div(n, 64)))
-        S = min(S, max(1, ceil_div(2 * o["num_cus"], len(kv_len) * desc["n_kv_heads"])))
-        pairs = len(kv_len) * desc["n_kv_heads"]
-        cap = 65536
-        if pairs * S <= o["num_cus"]:
-            cap = (9 if len(kv_len) == 1 else 8) * 16384 // 2
-        while ceil_div(n, S) * hd * 4 > cap:
-            S += 1
-        o["attn_splits"] = S
-    return o
+def check_opts(opts):
+    """Every entry of MODEL_OPTS must be given, as a positive int."""
+    missing = [k for k in MODEL_OPTS if not (opts or {}).get(k)]
+    if missing:
+        raise ValueError("the reference planner needs every tile option given explicitly; missing %s" % missing)
+    return {k: int(opts[k]) for k in MODEL_OPTS}
 
 
 def split_range(pos, S, s):
@@ -470,11 +442,16 @@ def glm_graph(desc, M):
     return ops, edges, dict(opts=dict(num_cus=0))
 
 
-def model_graph(desc, batch, kv_len, opts=None):
+def model_graph(desc, batch, kv_len, opts):
+    """The decode step's operators per layer -- QKV (RMSNorm fused), attention
+    (RoPE, KV write, split-KV partials), combine, O projection (+ residual),
+    gate/up (RMSNorm and SiLU fused), down (+ residual) -- then the LM head
+    (final RMSNorm fused) and argmax: the chain of the CMU 15-779 lecture 7
+    notes, sections 2 and 5.1.  opts: MODEL_OPTS, all explicit."""
     if desc.get("arch") == "glm":
         ops, edges, info = glm_graph(desc, batch)
         return ops, edges, info
-    o = resolve_opts(desc, batch, kv_len, opts)
+    o = check_opts(opts)
     H, nq, nkv, hd = desc["hidden"], desc["n_q_heads"], desc["n_kv_heads"], desc["head_dim"]
     F, V, L = desc["ffn"], desc["vocab"], desc["n_layers"]
     B = batch
@@ -518,12 +495,14 @@ def model_graph(desc, batch, kv_len, opts=None):
     return ops, edges, dict(S=S, T_qkv=T_qkv, T_o=T_o, T_f=T_f, T_d=T_d, T_v=T_v, spec=spec, opts=o)
 
 
-def plan_model(desc, batch, kv_len, opts=None):
+def plan_model(desc, batch, kv_len, opts):
+    """opts: num_cus (GLM path), or every entry of MODEL_OPTS (Llama family)."""
     if desc.get("arch") == "glm":
-        o = dict(DEFAULT_OPTS)
-        o.update({k: v for k, v in (opts or {}).items() if v})
+        if not (opts or {}).get("num_cus"):
+            raise ValueError("num_cus must be given")
+        o = dict(num_cus=int(opts["num_cus"]))
     else:
-        o = resolve_opts(desc, batch, kv_len, opts)
+        o = check_opts(opts)
     ops, edges, info = model_graph(desc, batch, kv_len, o)
     pl = plan_graph(ops, edges, o["num_cus"])
     pl.info = info

@@ -39,6 +39,58 @@ EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan",
             "mk_plan_trace", "mk_plan_free", "mk_plan_set_kv_len", "mk_run_steps", "mk_plan_debug_raise_wait",
             "mk_run_noalloc", "mk_noalloc_bytes", "mk_plan_poison_workspace")
 
+# operand-table slot kinds (mk.h MK_SLOT_*)
+MK_SLOT_NONE = 0
+MK_SLOT_ATTN_NORM = 1
+MK_SLOT_WQ = 2
+MK_SLOT_WK = 3
+MK_SLOT_WV = 4
+MK_SLOT_Q_NORM = 5
+MK_SLOT_K_NORM = 6
+MK_SLOT_WO = 7
+MK_SLOT_FFN_NORM = 8
+MK_SLOT_W_GATE = 9
+MK_SLOT_W_UP = 10
+MK_SLOT_W_DOWN = 11
+MK_SLOT_EMBED = 12
+MK_SLOT_FINAL_NORM = 13
+MK_SLOT_LM_HEAD = 14
+MK_SLOT_TOKENS = 20
+MK_SLOT_K_CACHE = 21
+MK_SLOT_V_CACHE = 22
+MK_SLOT_ROPE = 30
+MK_SLOT_QKV = 31
+MK_SLOT_ATTN_PART = 32
+MK_SLOT_ATTN_OUT = 33
+MK_SLOT_HIDDEN_ATTN = 34
+MK_SLOT_HIDDEN_FFN = 35
+MK_SLOT_FFN_ACT = 36
+MK_SLOT_LOGITS = 37
+MK_SLOT_LM_MAX = 38
+MK_SLOT_NEXT_TOKEN = 39
+MK_SLOT_G_X = 50
+MK_SLOT_G_R = 51
+MK_SLOT_G_ATTN_NORM = 52
+MK_SLOT_G_W = 53
+MK_SLOT_G_W_SCALE = 54
+MK_SLOT_G_Q_A_NORM = 55
+MK_SLOT_G_KV_A_NORM = 56
+MK_SLOT_G_KV_CACHE = 57
+MK_SLOT_G_IDX_CACHE = 58
+MK_SLOT_G_ROWS = 59
+MK_SLOT_G_R_OUT = 60
+MK_SLOT_G_NORM = 61
+MK_SLOT_G_ACT = 62
+MK_SLOT_G_ACT_SCALE = 63
+MK_SLOT_G_QKVA = 64
+MK_SLOT_G_QA = 65
+MK_SLOT_G_QA_SCALE = 66
+MK_SLOT_G_Q = 67
+MK_SLOT_G_QIDX = 68
+MK_SLOT_G_GATE = 69
+# mk_plan_view.tile_opts, in order
+TILE_OPTS = ("num_cus", "gemv_rows", "gateup_outs", "down_rows", "lm_rows", "attn_splits")
+
 i32, u32, f32, vp, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
 
@@ -67,7 +119,8 @@ class GraphEdge(ctypes.Structure):
 class PlanView(ctypes.Structure):
     _fields_ = [("num_cus", i32), ("max_len", i32), ("num_tasks", i32), ("num_events", i32), ("num_ops", i32),
                 ("num_edges", i32), ("queue", vp), ("event_target", vp), ("event_first", vp), ("event_last", vp),
-                ("task_trigger", vp), ("task_wait", vp), ("op_table", vp), ("edge_kept", vp)]
+                ("task_trigger", vp), ("task_wait", vp), ("op_table", vp), ("edge_kept", vp),
+                ("tile_opts", i32 * 6), ("op_slots", vp)]
 
 
 class Weights(ctypes.Structure):
@@ -205,7 +258,9 @@ class Plan:
                     event_last=_arr(v.event_last, E, np.int32), task_trigger=_arr(v.task_trigger, T, np.int32),
                     task_wait=_arr(v.task_wait, T, np.int32),
                     op_table=_arr(v.op_table, v.num_ops * 8, np.int32).reshape(v.num_ops, 8),
-                    edge_kept=_arr(v.edge_kept, v.num_edges, np.uint8))
+                    edge_kept=_arr(v.edge_kept, v.num_edges, np.uint8),
+                    tile_opts=dict(zip(TILE_OPTS, list(v.tile_opts))),
+                    op_slots=_arr(v.op_slots, v.num_ops * 16, np.int32).reshape(v.num_ops, 16))
 
     def run(self, weights, kv_cache, tokens, stream=None, layerwise=False):
         w = weights.struct if isinstance(weights, (DeviceWeights, GlmDeviceWeights)) else weights

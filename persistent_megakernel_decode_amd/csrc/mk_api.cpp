@@ -96,6 +96,7 @@ struct mk_plan {
   unsigned run_seq = 0;  // runs of either path; a bad token id is flagged with the run's number
   bool need_reset = false;
   std::vector<uint64_t> h_optab;
+  mutable std::vector<int32_t> op_slots;  // operand-table layout (MK_SLOT_* per slot), made on first export
   // new sequence lengths without replanning: the attention tasks' first words
   // in the queue, their payload patches (device and host staging) and the
   // host RoPE table
@@ -511,26 +512,6 @@ mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_ed
   return MK_OK;
 }
 
-mk_status mk_plan_export(const mk_plan* p, mk_plan_view* v) {
-  g_err.clear();
-  if (!p || !v) return fail(MK_E_INVALID, "null argument");
-  v->num_cus = p->P.num_cus;
-  v->max_len = p->P.max_len;
-  v->num_tasks = p->P.num_tasks;
-  v->num_events = p->P.num_events;
-  v->num_ops = (int32_t)p->ops.size();
-  v->num_edges = (int32_t)p->P.edge_kept.size();
-  v->queue = p->P.queue.data();
-  v->event_target = p->P.event_target.data();
-  v->event_first = p->P.event_first.data();
-  v->event_last = p->P.event_last.data();
-  v->task_trigger = p->P.task_trigger.data();
-  v->task_wait = p->P.task_wait.data();
-  v->op_table = p->P.op_table.data();
-  v->edge_kept = p->P.edge_kept.data();
-  return MK_OK;
-}
-
 // kCtrSub sub-counter lines per event
 static size_t counter_bytes(const mk_plan* p) {
   return (size_t)mkd::kCtrSub * std::max(1, p->P.num_events) * mkd::kCtrStride * 4;
@@ -629,171 +610,246 @@ static mk_status upload_optab(const Bind& b, const std::vector<uint64_t>& t, hip
   return MK_OK;
 }
 
-static mk_status bind_glm(mk_plan* p, const mk_weights* w, void* kv, const void* xr, hipStream_t s, const Bind& b) {
-  const mk_model_desc& d = p->desc;
-  if (!w || !w->layer_ptrs || !kv || !xr) return fail(MK_E_INVALID, "null weight, cache or input pointer");
-  for (int k = 0; k < MK_GLM_SLOTS; ++k)
-    if (!w->layer_ptrs[k]) return fail(MK_E_INVALID, "null GLM weight pointer");
-  const void* const* W = w->layer_ptrs;
-  auto u = [](const void* q) { return (uint64_t)(uintptr_t)q; };
-  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(b.ws + off); };
-  const size_t M = p->batch, H = d.hidden;
-  const uint64_t x = u(xr), r = u((const char*)xr + M * H * 2);
-  const uint64_t kvc = u(kv), idc = u((const char*)kv + (size_t)p->n_seq * d.max_kv_len * (d.kv_lora + d.rope_dim) * 2);
-  std::vector<uint64_t> t(p->ops.size() * 16, 0);
-  for (size_t o = 0; o < p->ops.size(); ++o) {
-    uint64_t* q = &t[o * 16];
-    switch (p->ops[o].opcode) {
-      case mk::kGA0:
-        q[mkd::GaX] = x;
-        q[mkd::GaR] = r;
-        q[mkd::GaNorm] = u(W[0]);
-        q[mkd::GaROut] = ws(p->off_gr);
-        q[mkd::GaN] = ws(p->off_gn);
-        q[mkd::GaA8] = ws(p->off_ga8);
-        q[mkd::GaAS] = ws(p->off_gas);
-        break;
-      case mk::kGQkva:
-        q[mkd::GmW] = u(W[1]);
-        q[mkd::GmS] = u(W[2]);
-        q[mkd::GmA8] = ws(p->off_ga8);
-        q[mkd::GmAS] = ws(p->off_gas);
-        q[mkd::GmOut] = ws(p->off_gqkva);
-        break;
-      case mk::kGGate:
-        q[mkd::GmW] = u(W[3]);
-        q[mkd::GmS] = u(W[4]);
-        q[mkd::GmAF] = ws(p->off_gn);
-        q[mkd::GmOut] = ws(p->off_ggate);
-        break;
-      case mk::kGIdxk:
-        q[mkd::GmW] = u(W[5]);
-        q[mkd::GmS] = u(W[6]);
-        q[mkd::GmA8] = ws(p->off_ga8);
-        q[mkd::GmAS] = ws(p->off_gas);
-        q[mkd::GmOut] = idc;
-        q[mkd::GmRows] = u(p->d_rows);
-        break;
-      case mk::kGQaNorm:
-        q[mkd::QnIn] = ws(p->off_gqkva);
-        q[mkd::QnNorm] = u(W[7]);
-        q[mkd::QnKvNorm] = u(W[8]);
-        q[mkd::QnA8] = ws(p->off_gqa8);
-        q[mkd::QnAS] = ws(p->off_gqs);
-        q[mkd::QnKv] = kvc;
-        q[mkd::QnRope] = u(b.rope);
-        q[mkd::QnRows] = u(p->d_rows);
-        break;
-      case mk::kGQkvb:
-        q[mkd::GmW] = u(W[9]);
-        q[mkd::GmS] = u(W[10]);
-        q[mkd::GmA8] = ws(p->off_gqa8);
-        q[mkd::GmAS] = ws(p->off_gqs);
-        q[mkd::GmOut] = ws(p->off_gq);
-        q[mkd::GmRope] = u(b.rope);
-        break;
-      case mk::kGIdxq:
-        q[mkd::GmW] = u(W[11]);
-        q[mkd::GmS] = u(W[12]);
-        q[mkd::GmA8] = ws(p->off_gqa8);
-        q[mkd::GmAS] = ws(p->off_gqs);
-        q[mkd::GmOut] = ws(p->off_gqidx);
-        break;
-      default:
-        break;
-    }
-  }
-  return upload_optab(b, t, s);
-}
+// Everything an operand row can point at.  Fields may be null when only the
+// table's layout (the slot kinds) is wanted.
+struct Src {
+  const void* const* layer_ptrs = nullptr;
+  const void* embed = nullptr;
+  const void* final_norm = nullptr;
+  const void* lm_head = nullptr;
+  const void* kv = nullptr;
+  const void* tokens = nullptr;
+  Bind b{};
+};
 
-static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const void* tokens, hipStream_t s,
-                               const Bind& b) {
-  if (p->glm) return bind_glm(p, w, kv, tokens, s, b);
+// The operand table: one row of 16 slots per op (MegaRTP article, section 4,
+// "OperandPtrTable"); vals gets the addresses, kinds the MK_SLOT_* of each
+// slot (0 where unused).
+static void fill_rows(const mk_plan* p, const Src& src, uint64_t* vals, int32_t* kinds) {
   const mk_model_desc& d = p->desc;
-  const int L = d.n_layers;
-  if (!w || !w->layer_ptrs || !w->embed || !w->final_norm || !kv || !tokens)
-    return fail(MK_E_INVALID, "null weight, KV-cache or token pointer");
-  if (!d.tied_lm_head && !w->lm_head) return fail(MK_E_INVALID, "lm_head is required when not tied");
-  for (int l = 0; l < L; ++l)
-    for (int sidx = 0; sidx < MK_LAYER_SLOTS; ++sidx) {
-      bool need = !(sidx == 4 || sidx == 5) || d.qk_norm;
-      if (need && !w->layer_ptrs[l * MK_LAYER_SLOTS + sidx]) return fail(MK_E_INVALID, "null layer weight pointer");
-    }
-  const size_t B = p->batch, hpg = p->c.hpg;
   auto u = [](const void* q) { return (uint64_t)(uintptr_t)q; };
-  auto ws = [&](size_t off) { return (uint64_t)(uintptr_t)(b.ws + off); };
+  auto ws = [&](size_t off) { return src.b.ws ? (uint64_t)(uintptr_t)(src.b.ws + off) : (uint64_t)0; };
+  auto put = [&](size_t o, int slot, uint64_t v, int kind) {
+    vals[o * 16 + slot] = v;
+    kinds[o * 16 + slot] = kind;
+  };
+  std::fill(vals, vals + p->ops.size() * 16, (uint64_t)0);
+  std::fill(kinds, kinds + p->ops.size() * 16, 0);
+  if (p->glm) {
+    const void* const* W = src.layer_ptrs;
+    auto w = [&](int k) { return W ? u(W[k]) : (uint64_t)0; };
+    const size_t M = p->batch, H = d.hidden;
+    const uint64_t x = u(src.tokens), r = src.tokens ? u((const char*)src.tokens + M * H * 2) : 0;
+    const uint64_t kvc = u(src.kv);
+    const uint64_t idc =
+        src.kv ? u((const char*)src.kv + (size_t)p->n_seq * d.max_kv_len * (d.kv_lora + d.rope_dim) * 2) : 0;
+    for (size_t o = 0; o < p->ops.size(); ++o) {
+      switch (p->ops[o].opcode) {
+        case mk::kGA0:
+          put(o, mkd::GaX, x, MK_SLOT_G_X);
+          put(o, mkd::GaR, r, MK_SLOT_G_R);
+          put(o, mkd::GaNorm, w(0), MK_SLOT_G_ATTN_NORM);
+          put(o, mkd::GaROut, ws(p->off_gr), MK_SLOT_G_R_OUT);
+          put(o, mkd::GaN, ws(p->off_gn), MK_SLOT_G_NORM);
+          put(o, mkd::GaA8, ws(p->off_ga8), MK_SLOT_G_ACT);
+          put(o, mkd::GaAS, ws(p->off_gas), MK_SLOT_G_ACT_SCALE);
+          break;
+        case mk::kGQkva:
+          put(o, mkd::GmW, w(1), MK_SLOT_G_W);
+          put(o, mkd::GmS, w(2), MK_SLOT_G_W_SCALE);
+          put(o, mkd::GmA8, ws(p->off_ga8), MK_SLOT_G_ACT);
+          put(o, mkd::GmAS, ws(p->off_gas), MK_SLOT_G_ACT_SCALE);
+          put(o, mkd::GmOut, ws(p->off_gqkva), MK_SLOT_G_QKVA);
+          break;
+        case mk::kGGate:
+          put(o, mkd::GmW, w(3), MK_SLOT_G_W);
+          put(o, mkd::GmS, w(4), MK_SLOT_G_W_SCALE);
+          put(o, mkd::GmAF, ws(p->off_gn), MK_SLOT_G_NORM);
+          put(o, mkd::GmOut, ws(p->off_ggate), MK_SLOT_G_GATE);
+          break;
+        case mk::kGIdxk:
+          put(o, mkd::GmW, w(5), MK_SLOT_G_W);
+          put(o, mkd::GmS, w(6), MK_SLOT_G_W_SCALE);
+          put(o, mkd::GmA8, ws(p->off_ga8), MK_SLOT_G_ACT);
+          put(o, mkd::GmAS, ws(p->off_gas), MK_SLOT_G_ACT_SCALE);
+          put(o, mkd::GmOut, idc, MK_SLOT_G_IDX_CACHE);
+          put(o, mkd::GmRows, u(p->d_rows), MK_SLOT_G_ROWS);
+          break;
+        case mk::kGQaNorm:
+          put(o, mkd::QnIn, ws(p->off_gqkva), MK_SLOT_G_QKVA);
+          put(o, mkd::QnNorm, w(7), MK_SLOT_G_Q_A_NORM);
+          put(o, mkd::QnKvNorm, w(8), MK_SLOT_G_KV_A_NORM);
+          put(o, mkd::QnA8, ws(p->off_gqa8), MK_SLOT_G_QA);
+          put(o, mkd::QnAS, ws(p->off_gqs), MK_SLOT_G_QA_SCALE);
+          put(o, mkd::QnKv, kvc, MK_SLOT_G_KV_CACHE);
+          put(o, mkd::QnRope, u(src.b.rope), MK_SLOT_ROPE);
+          put(o, mkd::QnRows, u(p->d_rows), MK_SLOT_G_ROWS);
+          break;
+        case mk::kGQkvb:
+          put(o, mkd::GmW, w(9), MK_SLOT_G_W);
+          put(o, mkd::GmS, w(10), MK_SLOT_G_W_SCALE);
+          put(o, mkd::GmA8, ws(p->off_gqa8), MK_SLOT_G_QA);
+          put(o, mkd::GmAS, ws(p->off_gqs), MK_SLOT_G_QA_SCALE);
+          put(o, mkd::GmOut, ws(p->off_gq), MK_SLOT_G_Q);
+          put(o, mkd::GmRope, u(src.b.rope), MK_SLOT_ROPE);
+          break;
+        case mk::kGIdxq:
+          put(o, mkd::GmW, w(11), MK_SLOT_G_W);
+          put(o, mkd::GmS, w(12), MK_SLOT_G_W_SCALE);
+          put(o, mkd::GmA8, ws(p->off_gqa8), MK_SLOT_G_QA);
+          put(o, mkd::GmAS, ws(p->off_gqs), MK_SLOT_G_QA_SCALE);
+          put(o, mkd::GmOut, ws(p->off_gqidx), MK_SLOT_G_QIDX);
+          break;
+        default:
+          break;
+      }
+    }
+    return;
+  }
+  const int L = d.n_layers;
+  const size_t B = p->batch;
   const size_t hid = p->sz_hid;
   auto xa = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l) * hid); };
   auto xb = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l + 1) * hid); };
   const size_t kvlayer = (size_t)2 * B * d.n_kv_heads * d.max_kv_len * d.head_dim * 2;
-  std::vector<uint64_t> t(p->ops.size() * 16, 0);
+  auto kvp = [&](int l, int half) {
+    return src.kv ? u((const char*)src.kv + l * kvlayer + half * (kvlayer / 2)) : (uint64_t)0;
+  };
   for (size_t o = 0; o < p->ops.size(); ++o) {
     const auto& op = p->ops[o];
-    uint64_t* r = &t[o * 16];
     const int l = op.layer;
-    const void* const* W = l < L ? w->layer_ptrs + (size_t)l * MK_LAYER_SLOTS : nullptr;
+    auto w = [&](int k) {
+      return (src.layer_ptrs && l < L) ? u(src.layer_ptrs[(size_t)l * MK_LAYER_SLOTS + k]) : (uint64_t)0;
+    };
     switch (op.opcode) {
       case mk::kQkv:
-        r[mkd::QkvWq] = u(W[1]);
-        r[mkd::QkvWk] = u(W[2]);
-        r[mkd::QkvWv] = u(W[3]);
-        r[mkd::QkvNorm] = u(W[0]);
-        r[mkd::QkvX] = l ? xb(l - 1) : 0;
-        r[mkd::QkvEmbed] = u(w->embed);
-        r[mkd::QkvTokens] = u(tokens);
-        r[mkd::QkvOut] = ws(p->off_qkv + l * p->sz_qkv);
+        put(o, mkd::QkvWq, w(1), MK_SLOT_WQ);
+        put(o, mkd::QkvWk, w(2), MK_SLOT_WK);
+        put(o, mkd::QkvWv, w(3), MK_SLOT_WV);
+        put(o, mkd::QkvNorm, w(0), MK_SLOT_ATTN_NORM);
+        if (l) put(o, mkd::QkvX, xb(l - 1), MK_SLOT_HIDDEN_FFN);  // layer 0 reads the embedding row
+        put(o, mkd::QkvEmbed, u(src.embed), MK_SLOT_EMBED);
+        put(o, mkd::QkvTokens, u(src.tokens), MK_SLOT_TOKENS);
+        put(o, mkd::QkvOut, ws(p->off_qkv + l * p->sz_qkv), MK_SLOT_QKV);
         break;
       case mk::kAttn:
-        r[mkd::AttnQkv] = ws(p->off_qkv + l * p->sz_qkv);
-        r[mkd::AttnK] = u((const char*)kv + l * kvlayer);
-        r[mkd::AttnV] = u((const char*)kv + l * kvlayer + kvlayer / 2);
-        r[mkd::AttnRope] = u(b.rope);
-        r[mkd::AttnOut] = ws(p->off_part + l * p->sz_part);
-        r[mkd::AttnQn] = d.qk_norm ? u(W[4]) : 0;
-        r[mkd::AttnKn] = d.qk_norm ? u(W[5]) : 0;
+        put(o, mkd::AttnQkv, ws(p->off_qkv + l * p->sz_qkv), MK_SLOT_QKV);
+        put(o, mkd::AttnK, kvp(l, 0), MK_SLOT_K_CACHE);
+        put(o, mkd::AttnV, kvp(l, 1), MK_SLOT_V_CACHE);
+        put(o, mkd::AttnRope, u(src.b.rope), MK_SLOT_ROPE);
+        put(o, mkd::AttnOut, ws(p->off_part + l * p->sz_part), MK_SLOT_ATTN_PART);
+        if (d.qk_norm) {
+          put(o, mkd::AttnQn, w(4), MK_SLOT_Q_NORM);
+          put(o, mkd::AttnKn, w(5), MK_SLOT_K_NORM);
+        }
         break;
       case mk::kCombine:
-        r[mkd::CombPart] = ws(p->off_part + l * p->sz_part);
-        r[mkd::CombOut] = ws(p->off_ao + l * p->sz_ao);
+        put(o, mkd::CombPart, ws(p->off_part + l * p->sz_part), MK_SLOT_ATTN_PART);
+        put(o, mkd::CombOut, ws(p->off_ao + l * p->sz_ao), MK_SLOT_ATTN_OUT);
         break;
       case mk::kOproj:
-        r[mkd::OWo] = u(W[6]);
-        r[mkd::OIn] = ws(p->off_ao + l * p->sz_ao);
-        r[mkd::OX] = l ? xb(l - 1) : 0;
-        r[mkd::OEmbed] = u(w->embed);
-        r[mkd::OTokens] = u(tokens);
-        r[mkd::OOut] = xa(l);
+        put(o, mkd::OWo, w(6), MK_SLOT_WO);
+        put(o, mkd::OIn, ws(p->off_ao + l * p->sz_ao), MK_SLOT_ATTN_OUT);
+        if (l) put(o, mkd::OX, xb(l - 1), MK_SLOT_HIDDEN_FFN);  // layer 0: the embedding row is the residual
+        put(o, mkd::OEmbed, u(src.embed), MK_SLOT_EMBED);
+        put(o, mkd::OTokens, u(src.tokens), MK_SLOT_TOKENS);
+        put(o, mkd::OOut, xa(l), MK_SLOT_HIDDEN_ATTN);
         break;
       case mk::kGateUp:
-        r[mkd::GuWg] = u(W[8]);
-        r[mkd::GuWu] = u(W[9]);
-        r[mkd::GuNorm] = u(W[7]);
-        r[mkd::GuIn] = xa(l);
-        r[mkd::GuOut] = ws(p->off_act + l * p->sz_act);
+        put(o, mkd::GuWg, w(8), MK_SLOT_W_GATE);
+        put(o, mkd::GuWu, w(9), MK_SLOT_W_UP);
+        put(o, mkd::GuNorm, w(7), MK_SLOT_FFN_NORM);
+        put(o, mkd::GuIn, xa(l), MK_SLOT_HIDDEN_ATTN);
+        put(o, mkd::GuOut, ws(p->off_act + l * p->sz_act), MK_SLOT_FFN_ACT);
         break;
       case mk::kDown:
-        r[mkd::DnW] = u(W[10]);
-        r[mkd::DnIn] = ws(p->off_act + l * p->sz_act);
-        r[mkd::DnRes] = xa(l);
-        r[mkd::DnOut] = xb(l);
+        put(o, mkd::DnW, w(10), MK_SLOT_W_DOWN);
+        put(o, mkd::DnIn, ws(p->off_act + l * p->sz_act), MK_SLOT_FFN_ACT);
+        put(o, mkd::DnRes, xa(l), MK_SLOT_HIDDEN_ATTN);
+        put(o, mkd::DnOut, xb(l), MK_SLOT_HIDDEN_FFN);
         break;
       case mk::kLmHead:
-        r[mkd::LmW] = u(d.tied_lm_head ? w->embed : w->lm_head);
-        r[mkd::LmNorm] = u(w->final_norm);
-        r[mkd::LmIn] = xb(L - 1);
-        r[mkd::LmLogits] = u(b.logits);
-        r[mkd::LmMax] = ws(p->off_lmmax);
+        if (d.tied_lm_head)
+          put(o, mkd::LmW, u(src.embed), MK_SLOT_EMBED);
+        else
+          put(o, mkd::LmW, u(src.lm_head), MK_SLOT_LM_HEAD);
+        put(o, mkd::LmNorm, u(src.final_norm), MK_SLOT_FINAL_NORM);
+        put(o, mkd::LmIn, xb(L - 1), MK_SLOT_HIDDEN_FFN);
+        put(o, mkd::LmLogits, u(src.b.logits), MK_SLOT_LOGITS);
+        put(o, mkd::LmMax, ws(p->off_lmmax), MK_SLOT_LM_MAX);
         break;
       case mk::kArgmax:
-        r[mkd::AmMax] = ws(p->off_lmmax);
-        r[mkd::AmOut] = u(b.next);
+        put(o, mkd::AmMax, ws(p->off_lmmax), MK_SLOT_LM_MAX);
+        put(o, mkd::AmOut, u(src.b.next), MK_SLOT_NEXT_TOKEN);
         break;
       default:
         break;
     }
   }
-  (void)hpg;
+}
+
+static mk_status bind_operands(mk_plan* p, const mk_weights* w, void* kv, const void* tokens, hipStream_t s,
+                               const Bind& b) {
+  const mk_model_desc& d = p->desc;
+  Src src;
+  src.b = b;
+  src.kv = kv;
+  src.tokens = tokens;
+  if (p->glm) {
+    if (!w || !w->layer_ptrs || !kv || !tokens) return fail(MK_E_INVALID, "null weight, cache or input pointer");
+    for (int k = 0; k < MK_GLM_SLOTS; ++k)
+      if (!w->layer_ptrs[k]) return fail(MK_E_INVALID, "null GLM weight pointer");
+    src.layer_ptrs = w->layer_ptrs;
+  } else {
+    if (!w || !w->layer_ptrs || !w->embed || !w->final_norm || !kv || !tokens)
+      return fail(MK_E_INVALID, "null weight, KV-cache or token pointer");
+    if (!d.tied_lm_head && !w->lm_head) return fail(MK_E_INVALID, "lm_head is required when not tied");
+    for (int l = 0; l < d.n_layers; ++l)
+      for (int sidx = 0; sidx < MK_LAYER_SLOTS; ++sidx) {
+        bool need = !(sidx == 4 || sidx == 5) || d.qk_norm;
+        if (need && !w->layer_ptrs[l * MK_LAYER_SLOTS + sidx]) return fail(MK_E_INVALID, "null layer weight pointer");
+      }
+    src.layer_ptrs = w->layer_ptrs;
+    src.embed = w->embed;
+    src.final_norm = w->final_norm;
+    src.lm_head = w->lm_head;
+  }
+  std::vector<uint64_t> t(p->ops.size() * 16, 0);
+  std::vector<int32_t> kinds(p->ops.size() * 16, 0);
+  fill_rows(p, src, t.data(), kinds.data());
   return upload_optab(b, t, s);
+}
+
+mk_status mk_plan_export(const mk_plan* p, mk_plan_view* v) {
+  g_err.clear();
+  if (!p || !v) return fail(MK_E_INVALID, "null argument");
+  v->num_cus = p->P.num_cus;
+  v->max_len = p->P.max_len;
+  v->num_tasks = p->P.num_tasks;
+  v->num_events = p->P.num_events;
+  v->num_ops = (int32_t)p->ops.size();
+  v->num_edges = (int32_t)p->P.edge_kept.size();
+  v->queue = p->P.queue.data();
+  v->event_target = p->P.event_target.data();
+  v->event_first = p->P.event_first.data();
+  v->event_last = p->P.event_last.data();
+  v->task_trigger = p->P.task_trigger.data();
+  v->task_wait = p->P.task_wait.data();
+  v->op_table = p->P.op_table.data();
+  v->edge_kept = p->P.edge_kept.data();
+  std::fill(v->tile_opts, v->tile_opts + 6, 0);
+  if (!p->graph_only && !p->glm) {
+    const mk::ModelOpts& o = p->opts;
+    const int32_t t[6] = {o.num_cus, o.gemv_rows, o.gateup_outs, o.down_rows, o.lm_rows, o.attn_splits};
+    std::copy(t, t + 6, v->tile_opts);
+  }
+  if (p->op_slots.size() != p->ops.size() * 16) {
+    std::vector<uint64_t> vals(p->ops.size() * 16);
+    p->op_slots.assign(p->ops.size() * 16, 0);
+    if (!p->graph_only) fill_rows(p, Src{}, vals.data(), p->op_slots.data());
+  }
+  v->op_slots = p->op_slots.data();
+  return MK_OK;
 }
 
 static mk_status launch_step(mk_plan* p, hipStream_t s);

@@ -10,6 +10,7 @@ import pytest
 
 import synth
 from oracle import planner as P
+from tests.lib_defaults import documented_defaults
 
 mk = pytest.importorskip("persistent_megakernel_decode_amd")
 
@@ -57,13 +58,40 @@ def _compare(lib_plan, ref):
     ("tiny", dict(batch=6, kv_len=(1, 120), seed=15), 64, dict(down_rows=6, gateup_outs=3)),
 ])
 def test_cpp_planner_matches_reference(name, overrides, num_cus, opts):
+    """Both planners get the same explicit tile options (every field given)."""
     cfg = synth.config(name, **overrides)
     kv = synth.kv_lengths(cfg)
     cap = synth.kv_capacity(kv)
-    ref = P.plan_model(cfg, cfg["batch"], kv, dict(num_cus=num_cus, **opts))
-    plan = mk.Plan.build(cfg, cfg["batch"], kv, cap, num_cus=num_cus, **opts)
+    o = documented_defaults(cfg, cfg["batch"], kv, num_cus, **opts)
+    ref = P.plan_model(cfg, cfg["batch"], kv, o)
+    plan = mk.Plan.build(cfg, cfg["batch"], kv, cap, **o)
     try:
-        _compare(plan, ref)
+        ex = _compare(plan, ref)
+        assert ex["tile_opts"] == o
+    finally:
+        plan.free()
+
+
+@pytest.mark.parametrize("name,overrides,num_cus,opts", [
+    ("tiny", {}, 256, {}),
+    ("tiny", dict(kv_len=0), 64, {}),
+    ("tiny", dict(ffn=688 + 32, vocab=4100, kv_len=999), 100, {}),
+    ("llama1b", {}, 256, {}),
+    ("llama1b", {}, 148, dict(gemv_rows=8, down_rows=2)),
+    ("llama1b_b16", {}, 256, {}),
+    ("qwen3_8b", {}, 256, {}),
+    ("qwen3_8b", {}, 200, {}),
+    ("qwen3_8b", dict(batch=4, kv_len=(100, 3000), seed=3), 256, {}),
+    ("tiny", dict(batch=3, kv_len=(0, 200), seed=11), 37, {}),
+])
+def test_library_defaults_follow_the_documented_rule(name, overrides, num_cus, opts):
+    """With fields left at 0 the library resolves each by the rule its header
+    documents (tested here against that documentation, not the oracle)."""
+    cfg = synth.config(name, **overrides)
+    kv = synth.kv_lengths(cfg)
+    plan = mk.Plan.build(cfg, cfg["batch"], kv, synth.kv_capacity(kv), num_cus=num_cus, **opts)
+    try:
+        assert plan.export()["tile_opts"] == documented_defaults(cfg, cfg["batch"], kv, num_cus, **opts)
     finally:
         plan.free()
 
@@ -189,9 +217,8 @@ def test_set_kv_len_patches_match_a_fresh_plan(name, num_cus, splits, shift):
     cap = synth.kv_capacity(kv1)
     plan = mk.Plan.build(cfg, cfg["batch"], kv0, cap, num_cus=num_cus, attn_splits=splits)
     try:
-        ref0 = P.plan_model(cfg, cfg["batch"], kv0, dict(num_cus=num_cus, attn_splits=splits))
-        S = ref0.info["S"]
-        ref1 = P.plan_model(cfg, cfg["batch"], kv1, dict(num_cus=num_cus, attn_splits=S))
+        o = plan.export()["tile_opts"]
+        ref1 = P.plan_model(cfg, cfg["batch"], kv1, o)
         before = plan.export()["queue"].copy()
         plan.set_kv_len(kv1)
         after = plan.export()["queue"]
@@ -245,7 +272,7 @@ def test_set_kv_len_random_lengths_match_fresh_plans():
         for _ in range(6):
             kv = rng.integers(0, cap - 1, size=5).astype(np.int32)
             plan.set_kv_len(kv)
-            ref = P.plan_model(cfg, 5, kv, dict(num_cus=29, attn_splits=6))
+            ref = P.plan_model(cfg, 5, kv, documented_defaults(cfg, 5, kv0, 29, attn_splits=6))
             assert np.array_equal(plan.export()["queue"], np.asarray(ref.queue, dtype=np.int32))
     finally:
         plan.free()
@@ -254,12 +281,15 @@ def test_set_kv_len_random_lengths_match_fresh_plans():
 def test_default_down_tiles_by_batch():
     """Batch 1 keeps a down tile within the compute waves' registers (64 KiB of
     weights); batched plans fill up to the 128 KiB page ring."""
-    for name, batch, want in (("llama1b", 1, 4), ("llama1b_b16", 16, 8), ("qwen3_8b", 1, 2)):
-        cfg = synth.config(name)
+    for name, overrides, want in (("llama1b", {}, 4), ("llama1b_b16", {}, 8), ("qwen3_8b", {}, 2),
+                                  ("qwen3_8b", dict(batch=4, kv_len=(100, 3000), seed=3), 5)):
+        cfg = synth.config(name, **overrides)
         kv = synth.kv_lengths(cfg)
-        assert P.resolve_opts(cfg, batch, kv, dict(num_cus=256))["down_rows"] == want
-    cfg = synth.config("qwen3_8b", batch=4, kv_len=(100, 3000), seed=3)
-    assert P.resolve_opts(cfg, 4, synth.kv_lengths(cfg), dict(num_cus=256))["down_rows"] == 5
+        plan = mk.Plan.build(cfg, cfg["batch"], kv, synth.kv_capacity(kv), num_cus=256)
+        try:
+            assert plan.export()["tile_opts"]["down_rows"] == want
+        finally:
+            plan.free()
 
 
 def test_split_rule_one_task_per_cu():
@@ -270,12 +300,68 @@ def test_split_rule_one_task_per_cu():
     would already need 256 tasks."""
     cfg = synth.config("qwen3_8b")
     kv = synth.kv_lengths(cfg)
-    assert P.resolve_opts(cfg, 1, kv, dict(num_cus=256))["attn_splits"] == 32
-    assert P.resolve_opts(cfg, 1, kv, dict(num_cus=200))["attn_splits"] == 33
-    for cus in (256, 200):
+    for cus, want in ((256, 32), (200, 33)):
         plan = mk.Plan.build(cfg, 1, kv, synth.kv_capacity(kv), num_cus=cus)
         try:
-            ref = P.plan_model(cfg, 1, kv, dict(num_cus=cus))
-            assert np.array_equal(plan.export()["queue"], np.asarray(ref.queue, dtype=np.int32))
+            assert plan.export()["tile_opts"]["attn_splits"] == want
         finally:
             plan.free()
+
+
+def test_operand_table_layout():
+    """The operand table has one row of 16 slots per op, shared by all of its
+    tile instructions; the exported layout names the tensor kind of each slot
+    (0 for unused ones), so it compares exactly: MegaRTP article, section 4
+    ("OperandPtrTable")."""
+    S = mk
+    want = {
+        P.QKV: [S.MK_SLOT_WQ, S.MK_SLOT_WK, S.MK_SLOT_WV, S.MK_SLOT_ATTN_NORM, "x", S.MK_SLOT_EMBED, S.MK_SLOT_TOKENS,
+                S.MK_SLOT_QKV],
+        P.ATTN: [S.MK_SLOT_QKV, S.MK_SLOT_K_CACHE, S.MK_SLOT_V_CACHE, S.MK_SLOT_ROPE, S.MK_SLOT_ATTN_PART],
+        P.COMBINE: [S.MK_SLOT_ATTN_PART, S.MK_SLOT_ATTN_OUT],
+        P.OPROJ: [S.MK_SLOT_WO, S.MK_SLOT_ATTN_OUT, "x", S.MK_SLOT_EMBED, S.MK_SLOT_TOKENS, S.MK_SLOT_HIDDEN_ATTN],
+        P.GATEUP: [S.MK_SLOT_W_GATE, S.MK_SLOT_W_UP, S.MK_SLOT_FFN_NORM, S.MK_SLOT_HIDDEN_ATTN, S.MK_SLOT_FFN_ACT],
+        P.DOWN: [S.MK_SLOT_W_DOWN, S.MK_SLOT_FFN_ACT, S.MK_SLOT_HIDDEN_ATTN, S.MK_SLOT_HIDDEN_FFN],
+        P.LMHEAD: [S.MK_SLOT_EMBED, S.MK_SLOT_FINAL_NORM, S.MK_SLOT_HIDDEN_FFN, S.MK_SLOT_LOGITS, S.MK_SLOT_LM_MAX],
+        P.ARGMAX: [S.MK_SLOT_LM_MAX, S.MK_SLOT_NEXT_TOKEN],
+    }
+    cfg = synth.config("tiny")
+    kv = synth.kv_lengths(cfg)
+    plan = mk.Plan.build(cfg, 1, kv, synth.kv_capacity(kv), num_cus=64)
+    try:
+        ex = plan.export()
+        slots = ex["op_slots"]
+        assert slots.shape == (len(ex["op_table"]), 16)
+        for o, row in enumerate(ex["op_table"]):
+            opcode, layer = int(row[0]), int(row[2])
+            w = [(S.MK_SLOT_HIDDEN_FFN if layer else 0) if k == "x" else k for k in want[opcode]]
+            assert slots[o].tolist() == w + [0] * (16 - len(w)), (o, opcode)
+    finally:
+        plan.free()
+    # Qwen3-style: the attention row also holds the q/k norm weights; untied LM head
+    cfg = synth.config("tiny", arch="qwen3", qk_norm=1, tied=0, head_dim=128)
+    plan = mk.Plan.build(cfg, 1, kv, synth.kv_capacity(kv), num_cus=64)
+    try:
+        ex = plan.export()
+        for o, row in enumerate(ex["op_table"]):
+            if row[0] == P.ATTN:
+                assert ex["op_slots"][o, 5:7].tolist() == [S.MK_SLOT_Q_NORM, S.MK_SLOT_K_NORM]
+            if row[0] == P.LMHEAD:
+                assert ex["op_slots"][o, 0] == S.MK_SLOT_LM_HEAD
+    finally:
+        plan.free()
+    # GLM path: every op's weight slots are (codes, block scales); caches and row info
+    g = synth.config("glm_tiny")
+    pos, _ = synth.glm_positions(g)
+    plan = mk.Plan.build(g, len(pos), pos, synth.glm_capacity(g), num_cus=8)
+    try:
+        ex = plan.export()
+        kinds = {int(r[0]): ex["op_slots"][o].tolist() for o, r in enumerate(ex["op_table"])}
+        assert kinds[P.G_A0][:7] == [S.MK_SLOT_G_X, S.MK_SLOT_G_R, S.MK_SLOT_G_ATTN_NORM, S.MK_SLOT_G_R_OUT,
+                                     S.MK_SLOT_G_NORM, S.MK_SLOT_G_ACT, S.MK_SLOT_G_ACT_SCALE]
+        for op in (P.G_QKVA, P.G_GATE, P.G_IDXK, P.G_QKVB, P.G_IDXQ):
+            assert kinds[op][:2] == [S.MK_SLOT_G_W, S.MK_SLOT_G_W_SCALE]
+        assert kinds[P.G_GATE][4] == S.MK_SLOT_G_NORM and kinds[P.G_GATE][2:4] == [0, 0]
+        assert S.MK_SLOT_G_KV_CACHE in kinds[P.G_QANORM] and S.MK_SLOT_G_IDX_CACHE in kinds[P.G_IDXK]
+    finally:
+        plan.free()

@@ -270,3 +270,91 @@ def test_bf16_rounding_all_exponents_and_tie_patterns():
     assert oracle.to_bf16(-(tie + 2.0 ** -40)) == 0xBF81
     assert oracle.to_bf16(float("nan")) == 0x7FC0
     assert oracle.to_bf16(3.5e38) == 0x7F80
+
+
+def test_new_k_row_is_rounded_before_it_is_attended():
+    """Reading A5 (the new K and V rows are rounded to bf16 before they are
+    attended), its K half, by a closed form at kv_len = 1.  One layer, one head;
+    the normed input is exactly all ones (embedding row of ones, eps 1e-30), so
+    q, k and v are chosen columns of Wq, Wk, Wv.  The prior cache row is set to
+    bf16(RoPE(k)) -- the row the step itself writes -- with V = 0, and Wo is the
+    identity with a zero FFN.  Attending the rounded new k gives two equal
+    scores, weights exactly 1/2, so the post-attention stream is exactly
+    1 + v / 2; attending the unrounded k gives the logistic weight of the score
+    gap instead (the rotated q is chosen along the rounding error, so the gap
+    is positive).  RoPE and bf16 rounding, pinned on their own above, build the
+    prior row."""
+    d, V, t = 64, 8, 3
+    cfg = synth.config("tiny", n_layers=1, hidden=d, n_q_heads=1, n_kv_heads=1, head_dim=d, ffn=16, vocab=V,
+                       kv_len=1, rms_eps=1e-30, seed=91)
+    one = 0x3F80
+    kappa = synth.normal_bf16(91, 1, (d,), 1.0)
+    z = bf16_to_f64(synth.normal_bf16(91, 2, (d,), 1.0))
+    nu = _bf16_vec(np.sign(z) * np.clip(np.round(np.abs(z) * 8), 1, 16) / 16)  # nonzero multiples of 1/16
+    k_rot = oracle.rope(bf16_to_f64(kappa), 1, cfg["rope_theta"])
+    K0 = _bf16_vec(k_rot)
+    err = k_rot - bf16_to_f64(K0)
+    assert np.count_nonzero(err) > d // 2
+    # q is rotated too: pick the sign that makes the rotated q's gap positive
+    q = _bf16_vec(64.0 * np.sign(err))
+    if oracle.rope(bf16_to_f64(q), 1, cfg["rope_theta"]) @ err < 0:
+        q = _bf16_vec(-64.0 * np.sign(err))
+
+    def col0(v):
+        W = np.zeros((d, d), dtype=np.uint16)
+        W[:, 0] = v
+        return W
+    zeros = lambda shp: np.zeros(shp, dtype=np.uint16)
+    layer = dict(attn_norm=np.full(d, one, np.uint16), wq=col0(q), wk=col0(kappa), wv=col0(nu),
+                 wo=np.diag(np.full(d, one, np.uint16)).astype(np.uint16), ffn_norm=np.full(d, one, np.uint16),
+                 w_gate=zeros((16, d)), w_up=zeros((16, d)), w_down=zeros((d, 16)))
+    embed = zeros((V, d))
+    embed[t] = one
+    w = dict(embed=embed, final_norm=np.full(d, one, np.uint16), layers=[layer])
+    cap = 16
+    kv = np.full((1, 2, 1, 1, cap, d), 0x7FC0, dtype=np.uint16)
+    kv[0, 0, 0, 0, 0] = K0
+    kv[0, 1, 0, 0, 0] = 0
+    inp = dict(cfg=cfg, weights=w, kv_len=np.array([1], np.int32), kv_cache=kv, tokens=np.array([t], np.int32))
+    r = oracle.decode_step(inp, intermediates=True)
+    nuf = bf16_to_f64(nu)
+    assert np.array_equal(r["kv_cache"][0, 0, 0, 0, 1], K0)  # the step writes bf16(RoPE(k)) at row 1
+    assert np.array_equal(r["kv_cache"][0, 1, 0, 0, 1], nu)
+    assert np.array_equal(r["hidden"][0, 0, 0], 1.0 + nuf / 2)  # exact: weights 1/2 each
+    # the other reading (the new k unrounded) moves the weight by the score gap
+    u = oracle.decode_step(inp, round_new_kv=False, intermediates=True)
+    gap = float(oracle.rope(bf16_to_f64(q), 1, cfg["rope_theta"]) @ err) / np.sqrt(d)
+    assert gap > 0
+    want = 1.0 + nuf / (1.0 + np.exp(-gap))
+    assert np.allclose(u["hidden"][0, 0, 0], want, rtol=1e-14, atol=1e-14)
+    assert not np.array_equal(u["hidden"][0, 0, 0], r["hidden"][0, 0, 0])
+
+
+def test_intermediates_are_the_steps_own_values():
+    """The per-layer intermediates the oracle reports are the values its step
+    uses: the last layer's FFN output is the input of the final norm (logits by
+    numpy from it), layer 0's q/k/v are the projections of the normed embedding
+    row, and each layer's attention output feeds its FFN block."""
+    inp = synth.make_inputs("tiny", norm_sigma=0.1, batch=2, kv_len=(3, 60), seed=44)
+    cfg, w = inp["cfg"], inp["weights"]
+    r = oracle.decode_step(inp, intermediates=True)
+    plain = oracle.decode_step(inp)
+    assert np.array_equal(r["logits"], plain["logits"])
+    E = bf16_to_f64(w["embed"])
+    for b in range(cfg["batch"]):
+        xf = r["hidden"][-1, 1, b]
+        yf = xf / np.sqrt(np.mean(xf * xf) + cfg["rms_eps"]) * bf16_to_f64(w["final_norm"])
+        assert _rel(r["logits"][b], E @ yf) < 1e-12
+        x0 = E[int(inp["tokens"][b])]
+        d0 = w["layers"][0]
+        y0 = x0 / np.sqrt(np.mean(x0 * x0) + cfg["rms_eps"]) * bf16_to_f64(d0["attn_norm"])
+        proj = np.concatenate([bf16_to_f64(d0[k]) @ y0 for k in ("wq", "wk", "wv")])
+        assert _rel(r["qkv"][0, b].ravel(), proj) < 1e-12
+        for l in range(cfg["n_layers"]):
+            dl = w["layers"][l]
+            x1 = r["hidden"][l, 0, b]
+            y2 = x1 / np.sqrt(np.mean(x1 * x1) + cfg["rms_eps"]) * bf16_to_f64(dl["ffn_norm"])
+            g, u = bf16_to_f64(dl["w_gate"]) @ y2, bf16_to_f64(dl["w_up"]) @ y2
+            from scipy.special import expit
+            x2 = x1 + bf16_to_f64(dl["w_down"]) @ (g * expit(g) * u)
+            assert _rel(r["hidden"][l, 1, b], x2) < 1e-12

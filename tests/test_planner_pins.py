@@ -203,7 +203,8 @@ TINY = dict(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=
 
 @pytest.mark.parametrize("batch,kv", [(1, [128]), (3, [0, 7, 300])])
 def test_model_plan_invariants_and_happens_before(batch, kv):
-    pl = P.plan_model(TINY, batch, kv, dict(num_cus=37))
+    pl = P.plan_model(TINY, batch, kv, dict(num_cus=37, gemv_rows=16, gateup_outs=8, down_rows=16, lm_rows=16,
+                                            attn_splits=3))
     q = np.array(pl.queue)
     C, L = q.shape[:2]
     T = pl.num_tasks
