@@ -124,9 +124,160 @@ def capture(run):
     return g.replay
 
 
+OP_NAMES = {1: "qkv", 2: "attn", 3: "combine", 4: "oproj", 5: "gateup", 6: "down", 7: "lmhead", 8: "argmax",
+            9: "glm_a0", 10: "glm_qkva", 11: "glm_gate", 12: "glm_idxk", 13: "glm_qanorm", 14: "glm_qkvb",
+            15: "glm_idxq", 16: "glm_gate_red"}
+
+
+def trace_report(tr, tpu, queue):
+    """Decode one step's per-instruction trace (mk_plan_trace) into the
+    measures of the MegaRTP article, sections 1 and 6: the active-CU fraction
+    (time the compute units spend inside an instruction, from its input being
+    ready to its outputs stored, over CUs x the step's span), the bubbles
+    between consecutive instructions of a CU (median and share of the span),
+    and per event the hand-off: the tail of its producers (last signal minus
+    median signal) and its detection (median consumer start minus last signal).
+    Times in us from the first stamp."""
+    live = queue[:, :, 0] != 0
+    C = queue.shape[0]
+    ready, done, sig = tr[:, :, 1].astype(np.float64), tr[:, :, 2].astype(np.float64), tr[:, :, 3].astype(np.float64)
+    evs = tr[:, :, 0].astype(np.float64)
+    t0 = min(evs[live].min(), ready[live & (ready > 0)].min())
+    us = lambda t: (t - t0) / tpu
+    start = np.where(ready > 0, ready, evs)  # instructions without a compute stamp start at their event
+    span = us(sig[live].max())
+    busy, gaps = 0.0, []
+    for c in range(C):
+        n = int(live[c].sum())
+        if n == 0:
+            continue
+        st, en = us(start[c, :n]), us(done[c, :n])
+        # union of the CU's busy intervals (with two compute groups consecutive
+        # instructions overlap); the gaps between them are its bubbles
+        order = np.argsort(st, kind="stable")
+        cur_s, cur_e = st[order[0]], en[order[0]]
+        for k in order[1:]:
+            if st[k] <= cur_e:
+                cur_e = max(cur_e, en[k])
+            else:
+                busy += cur_e - cur_s
+                gaps.append(st[k] - cur_e)
+                cur_s, cur_e = st[k], en[k]
+        busy += cur_e - cur_s
+    gaps = np.array(gaps) if gaps else np.zeros(1)
+    ops = {}
+    hop_tail, hop_detect = [], []
+    wait_ev, sig_ev = queue[:, :, 4], queue[:, :, 7]
+    has_wait, has_sig = queue[:, :, 3] != 0, queue[:, :, 6] != 0
+    E = int(max(wait_ev[live & has_wait].max(initial=-1), sig_ev[live & has_sig].max(initial=-1))) + 1
+    for e in range(E):
+        prod = live & has_sig & (sig_ev == e)
+        cons = live & has_wait & (wait_ev == e)
+        if not prod.any() or not cons.any():
+            continue
+        ps = us(sig[prod])
+        hop_tail.append(float(ps.max() - np.median(ps)))
+        hop_detect.append(float(np.median(us(evs[cons])) - ps.max()))
+    for c in range(C):
+        for i in range(int(live[c].sum())):
+            key = (int(queue[c, i, 10]), OP_NAMES.get(int(queue[c, i, 0]), str(int(queue[c, i, 0]))))
+            o = ops.setdefault(key, dict(first=1e30, last=0.0, dur=[]))
+            o["first"] = min(o["first"], us(start[c, i]))
+            o["last"] = max(o["last"], us(sig[c, i]))
+            o["dur"].append(us(done[c, i]) - us(start[c, i]))
+    per_op = {}
+    for (layer, name), o in ops.items():
+        a = per_op.setdefault(name, dict(tasks=0, task_us=[], span_us=[]))
+        a["tasks"] += len(o["dur"])
+        a["task_us"].append(float(np.median(o["dur"])))
+        a["span_us"].append(o["last"] - o["first"])
+    per_op = {k: dict(tasks=v["tasks"], median_task_us=round(float(np.median(v["task_us"])), 3),
+                      median_span_us=round(float(np.median(v["span_us"])), 3)) for k, v in per_op.items()}
+    span, busy = float(span), float(busy)
+    return dict(traced_step_us=round(span, 2), active_cu_frac=round(busy / (C * span), 4),
+                bubble_median_us=round(float(np.median(gaps)), 3),
+                bubble_share=round(float(gaps.sum()) / (C * span), 4),
+                hop_tail_median_us=round(float(np.median(hop_tail)), 3) if hop_tail else None,
+                hop_detect_median_us=round(float(np.median(hop_detect)), 3) if hop_detect else None,
+                events=len(hop_tail), per_op=per_op)
+
+
+def traced_step(plan, run, dump=None):
+    """One traced run of the megakernel after the timed ones (the trace stamps
+    cost a few percent, so the timed steps run untraced); its decoded report.
+    dump: a path to save the raw trace and queue (npz) to."""
+    import torch
+    plan.set_trace(True)
+    run()
+    torch.cuda.synchronize()
+    tr, tpu = plan.trace()
+    plan.set_trace(False)
+    q = plan.export()["queue"]
+    if dump:
+        np.savez_compressed(dump, trace=tr, ticks_per_us=tpu, queue=q)
+    return trace_report(tr, tpu, q)
+
+
+def stream_ceiling(full=False, gib=2):
+    """Streaming-read ceiling of the device (mk_stream_probe over a 2 GiB buffer,
+    8x the memory-side cache): GB/s per configuration (median of 5 reads) and
+    the best.  The default set covers the megakernel's own loader layout (2
+    waves, 1 page in flight, LDS-DMA) and the best layouts of the full sweep."""
+    import torch
+    import persistent_megakernel_decode_amd as mk
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    if full:
+        cfgs = [(1, 256, w, d) for w in (1, 2, 4, 8) for d in (1, 2, 3, 4) if w * d <= 8]
+        cfgs += [(1, 512, 4, d) for d in (1, 2)] + [(0, g, w, d) for g in (256, 512, 1024) for w in (4, 8) for d in (1, 2)]
+    else:
+        cfgs = [(1, 256, 2, 1), (1, 256, 4, 2), (1, 256, 8, 1), (0, 256, 8, 2), (0, 1024, 8, 1)]
+    stream = torch.cuda.current_stream()
+    out = []
+    for lds, g, w, d in cfgs:
+        ts = []
+        for k in range(7):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            mk.stream_probe(buf, lds, g, w, d, sink)
+            b.record(stream)
+            b.synchronize()
+            if k >= 2:
+                ts.append(a.elapsed_time(b) * 1e-3)
+        gbps = buf.numel() / float(np.median(ts)) / 1e9
+        out.append(dict(mode="lds_dma" if lds else "registers", workgroups=g, waves=w, depth=d, GBps=round(gbps, 1)))
+    del buf
+    best = max(out, key=lambda r: r["GBps"])
+    return dict(best_GBps=best["GBps"], best=best, configs=out)
+
+
+def cpu_model():
+    """The host CPU's model name (what lscpu reports), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _omp():
+    """The OpenMP runtime the CPU oracle runs on (libgomp, loaded with it)."""
+    import ctypes
+    g = ctypes.CDLL("libgomp.so.1")
+    g.omp_get_max_threads.restype = ctypes.c_int
+    g.omp_set_num_threads.argtypes = [ctypes.c_int]
+    return g
+
+
 def cpu_baseline(inp, budget_s=20.0):
+    """The fp64 C oracle on this host's cores: whole decode steps with every
+    OpenMP thread (the reported value), then one step on one thread."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    oracle.lib()
+    omp = _omp()
+    threads = int(omp.omp_get_max_threads())
     t0 = time.perf_counter()
     n = 0
     while True:
@@ -135,8 +286,17 @@ def cpu_baseline(inp, budget_s=20.0):
         if time.perf_counter() - t0 > budget_s * 0.5 or n >= 3:
             break
     dt = (time.perf_counter() - t0) / n
+    omp.omp_set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.decode_step(inp)
+        one = time.perf_counter() - t1
+    finally:
+        omp.omp_set_num_threads(threads)
     return dict(value=dt * 1e6, unit="us", cores=threads, kind="oracle",
-                sample="%d whole decode step(s) of the same workload (fp64 C oracle, OpenMP over output rows)" % n)
+                sample="%d whole decode step(s) of the same workload (fp64 C oracle, OpenMP over output rows), "
+                       "then 1 step on 1 thread" % n,
+                cpu_model=cpu_model(), one_thread_us=round(one * 1e6, 1))
 
 
 def bench_glm(args):
@@ -193,6 +353,8 @@ def bench_glm(args):
             st, chk = plans[0].check()
             if st != mk.MK_OK or not chk.counters_ok:
                 raise RuntimeError("megakernel check failed: %s" % mk.lib().mk_last_error().decode())
+            print("[bench] one traced megakernel step", file=sys.stderr, flush=True)
+            res_trace = traced_step(plans[0], lambda: plans[0].run(ws[0], caches, xr), args.trace_dump)
     main_key = "mk_cold" if "mk_cold" in res else "lw_cold"
     lat = res[main_key]["median"]
     achieved = nbytes / (res[main_key]["mean"] * 1e-6) / 1e9
@@ -214,6 +376,8 @@ def bench_glm(args):
     }
     for k, v in res.items():
         out[k + "_us"] = {a: round(b, 2) for a, b in v.items()}
+    if args.only != "layerwise":
+        out["trace"] = res_trace
     if "mk_cold" in res and "lw_cold" in res:
         out["speedup_vs_layerwise_cold"] = round(res["lw_cold"]["median"] / res["mk_cold"]["median"], 3)
         out["speedup_vs_layerwise_warm"] = round(res["lw_warm"]["median"] / res["mk_warm"]["median"], 3)
@@ -232,7 +396,8 @@ def bench_glm(args):
             n += 1
         out["cpu_baseline"] = dict(value=(time.perf_counter() - t0) / n * 1e6, unit="us",
                                    cores=int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), kind="oracle",
-                                   sample="%d whole step(s) of the same workload (fp64 numpy oracle)" % n)
+                                   sample="%d whole step(s) of the same workload (fp64 numpy oracle)" % n,
+                                   cpu_model=cpu_model())
     for p_ in plans:
         p_.free()
     print(json.dumps(out))
@@ -247,6 +412,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured layerwise baseline")
     ap.add_argument("--only", choices=["megakernel", "layerwise", "both"], default="both")
+    ap.add_argument("--trace-dump", default=None, help="save the traced step's raw trace and queue (npz) here")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only sweep the streaming-read probe (mk_stream_probe) and print its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first launch one device-to-device copy of 256 MiB (read 256 MiB, write 256 MiB), so that "
                          "a profiler run can scale its HBM byte counters by a kernel of known traffic")
@@ -255,6 +423,11 @@ def main():
         print("bench.py runs on exactly one GPU: the decode megakernel is a single-GPU design here "
               "(no collectives); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.stream_ceiling:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(stream_ceiling(full=True)))
+        return
     if args.workload.startswith("glm"):
         return bench_glm(args)
     import torch
@@ -285,6 +458,8 @@ def main():
         st, chk = plan.check()
         if st != mk.MK_OK or not chk.counters_ok:
             raise RuntimeError("megakernel check failed: %s" % mk.lib().mk_last_error().decode())
+        print("[bench] one traced megakernel step", file=sys.stderr, flush=True)
+        res["trace"] = traced_step(plan, lambda: plan.run(w, kv, tok), args.trace_dump)
         # a decode loop: 8 steps per call (mk_run_steps), each step's argmax fed to
         # the next, the plan moved to each step's lengths without replanning
         print("[bench] timing an 8-step decode loop", file=sys.stderr, flush=True)
@@ -307,6 +482,8 @@ def main():
             res["lw_graph"] = time_launches(capture(lambda s: plan.run_layerwise(w, kv, tok, stream=s)), stream,
                                             args.steps, args.warmup)
     torch.cuda.synchronize()
+    print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
+    ceil = stream_ceiling()
     main_key = "mk" if "mk" in res else "lw"
     lat = res[main_key]["median"]
     # roofline: algorithmic bytes per launch over the kernel's average launch
@@ -338,9 +515,15 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic},
+        # second denominator: the best plain streaming read measured on this device
+        "stream_ceiling": {"GBps": ceil["best_GBps"], "config": ceil["best"],
+                           "loader_layout_GBps": ceil["configs"][0]["GBps"],
+                           "frac_of_ceiling": round(achieved / ceil["best_GBps"], 4)},
     }
     if "mk" in res:
         out["megakernel_us"] = {k: round(v, 2) for k, v in res["mk"].items()}
+    if "trace" in res:
+        out["trace"] = res["trace"]
     if "mk_loop" in res:
         # per step of an 8-step mk_run_steps call (includes each step's queue
         # patch, RoPE copy and token hand-over; per-step percentiles are of calls / 8)

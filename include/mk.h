@@ -75,10 +75,13 @@ int mk_abi_version(void);
  * weights are E4M3 codes [out, in] with fp32 scales [ceil(out/128)][in/128].
  * Fields used: hidden, n_q_heads, head_dim, max_kv_len, rms_eps, rope_theta
  * and the GLM fields below (n_layers must be 1; the Llama-only fields are ignored).
- * Supported: hidden and q_lora multiples of 128, kv_lora a multiple of 8,
- * head_dim - rope_dim and rope_dim positive multiples of 16 with each head's
- * rope dims inside one 128-row scale block, n_gate, idx_head_dim and
- * n_idx_heads * idx_head_dim multiples of 16 (64, 128, 4096 for the GLM shape).
+ * Supported: hidden (<= 8192) and q_lora (<= 3072) multiples of 128, kv_lora
+ * (<= 1024) a multiple of 8 with kv_lora + rope_dim a multiple of 8, head_dim -
+ * rope_dim and rope_dim positive multiples of 16 with each head's rope dims
+ * inside one 128-row scale block, n_gate, idx_head_dim and n_idx_heads *
+ * idx_head_dim multiples of 16 (64, 128, 4096 for the GLM shape).  The head
+ * gate is planned as K-split tiles (4 blocks of 128 columns each) and a reduce
+ * op that adds their partials in split order.
  * ------------------------------------------------------------------------- */
 enum { MK_ARCH_LLAMA = 1, MK_ARCH_QWEN3 = 2, MK_ARCH_GLM_PREATTN = 3 };
 enum { MK_BF16 = 0, MK_FP8_E4M3_B128 = 1 };
@@ -214,7 +217,7 @@ enum {
   MK_SLOT_G_X = 50, MK_SLOT_G_R, MK_SLOT_G_ATTN_NORM, MK_SLOT_G_W, MK_SLOT_G_W_SCALE, MK_SLOT_G_Q_A_NORM,
   MK_SLOT_G_KV_A_NORM, MK_SLOT_G_KV_CACHE, MK_SLOT_G_IDX_CACHE, MK_SLOT_G_ROWS, MK_SLOT_G_R_OUT, MK_SLOT_G_NORM,
   MK_SLOT_G_ACT, MK_SLOT_G_ACT_SCALE, MK_SLOT_G_QKVA, MK_SLOT_G_QA, MK_SLOT_G_QA_SCALE, MK_SLOT_G_Q,
-  MK_SLOT_G_QIDX, MK_SLOT_G_GATE
+  MK_SLOT_G_QIDX, MK_SLOT_G_GATE, MK_SLOT_G_GATE_PART
 };
 typedef struct {
   int32_t num_cus, max_len, num_tasks, num_events, num_ops, num_edges;
@@ -386,6 +389,16 @@ mk_status mk_plan_poison_workspace(mk_plan* plan, void* stream);
  * A threshold above the event's producer count makes its waiters time out: the
  * grid drains and exits normally and mk_plan_check reports MK_E_TIMEOUT. */
 mk_status mk_plan_debug_raise_wait(mk_plan* plan, int32_t event, int32_t delta);
+
+/* Measurement: one streaming read of 'bytes' (a multiple of 16 KiB) at src
+ * (device), the ceiling a weight stream can reach on this device: 16 KiB pages
+ * dealt round-robin to 'waves' waves (1..8) of each of 'workgroups' workgroups,
+ * read with LDS-DMA into an LDS ring (lds_dma = 1, as the megakernel's loaders
+ * do; depth 1..4 pages in flight per wave) or with 16-byte register loads
+ * (lds_dma = 0; depth 1..2).  sink: device, at least workgroups * waves uint32
+ * (written so the register loads are kept).  Only enqueues. */
+mk_status mk_stream_probe(const void* src, size_t bytes, int32_t lds_dma, int32_t workgroups, int32_t waves,
+                          int32_t depth, void* sink, void* stream);
 
 /* mk_run for callers that cannot allocate device memory (code under graph
  * capture elsewhere in the process, tight serving loops, harnesses that forbid

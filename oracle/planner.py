@@ -51,8 +51,9 @@ N_PAY = 10
 # opcodes of the Llama-family decode step
 NOOP, QKV, ATTN, COMBINE, OPROJ, GATEUP, DOWN, LMHEAD, ARGMAX = range(9)
 # opcodes of the GLM-style pre-attention path
-G_A0, G_QKVA, G_GATE, G_IDXK, G_QANORM, G_QKVB, G_IDXQ = range(9, 16)
+G_A0, G_QKVA, G_GATE, G_IDXK, G_QANORM, G_QKVB, G_IDXQ, G_GATE_RED = range(9, 17)
 GLM_ROWS = 16  # weight rows per fp8 GEMM tile (the matrix-core M dimension)
+GATE_BLOCKS = 4  # 128-column blocks per head-gate K-split tile
 
 
 def lcm(a, b):
@@ -427,15 +428,23 @@ def glm_graph(desc, M):
         j = y - NOPE // R
         return (x * hd + NOPE + j * (R // 2), R // 2, x * hd + NOPE + RD // 2 + j * (R // 2))
 
+    # the head gate is cut along K too (GATE_BLOCKS blocks of 128 columns per
+    # task) and a reduce op adds each row tile's partials: the tile_reduce
+    # pairing of the MegaRTP article, section 4 ("TaskGraph")
+    nkb = H // 128
+    GS, Tg = ceil_div(nkb, GATE_BLOCKS), ceil_div(Ng, R)
     a0 = add(Op("a0", G_A0, (M,), 0, 0, lambda x, y, z: (x,)))
     qa = add(Op("qkva", G_QKVA, (ceil_div(Na, R),), 0, 0, rows(Na)))
-    ga = add(Op("gate", G_GATE, (ceil_div(Ng, R),), 0, 0, rows(Ng)))
+    ga = add(Op("gate", G_GATE, (Tg, GS), 0, 0,
+                lambda x, y, z: (x * R, min(R, Ng - x * R), -1, y * GATE_BLOCKS, min(GATE_BLOCKS, nkb - y * GATE_BLOCKS))))
     ik = add(Op("idxk", G_IDXK, (ceil_div(Nk, R),), 0, 0, rows(Nk)))
+    gr = add(Op("gate_red", G_GATE_RED, (Tg,), 0, 0, lambda x, y, z: (x * R, min(R, Ng - x * R), GS)))
     qn = add(Op("qanorm", G_QANORM, (M,), 0, 0, lambda x, y, z: (x,)))
     qb = add(Op("qkvb", G_QKVB, (nh, (NOPE + RD) // R), 0, 0, qb_rows))
     iq = add(Op("idxq", G_IDXQ, (ceil_div(Niq, R),), 0, 0, rows(Niq)))
     for c in (qa, ga, ik):
         edges.append(Edge(a0, c, (0,), (), [M, H, 1, 1], [1, H, 1, 1], [M, H, 1, 1], "act"))
+    edges.append(Edge(ga, gr, (1,), (1,), [M, Ng, 1, 1], [M, R, 1, 1], [M, R, 1, 1], "gate_part"))
     edges.append(Edge(qa, qn, (1,), (0,), [M, Na, 1, 1], [M, R, 1, 1], [1, Na, 1, 1], "qkva"))
     for c in (qb, iq):
         edges.append(Edge(qn, c, (0,), (), [M, QL, 1, 1], [1, QL, 1, 1], [M, QL, 1, 1], "qa"))

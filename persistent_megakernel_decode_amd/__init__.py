@@ -37,7 +37,7 @@ LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_nor
 EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_plan_export", "mk_run",
             "mk_run_layerwise", "mk_plan_output", "mk_plan_copy_output", "mk_plan_check", "mk_plan_set_trace",
             "mk_plan_trace", "mk_plan_free", "mk_plan_set_kv_len", "mk_run_steps", "mk_plan_debug_raise_wait",
-            "mk_run_noalloc", "mk_noalloc_bytes", "mk_plan_poison_workspace")
+            "mk_run_noalloc", "mk_noalloc_bytes", "mk_plan_poison_workspace", "mk_stream_probe")
 
 # operand-table slot kinds (mk.h MK_SLOT_*)
 MK_SLOT_NONE = 0
@@ -88,6 +88,7 @@ MK_SLOT_G_QA_SCALE = 66
 MK_SLOT_G_Q = 67
 MK_SLOT_G_QIDX = 68
 MK_SLOT_G_GATE = 69
+MK_SLOT_G_GATE_PART = 70
 # mk_plan_view.tile_opts, in order
 TILE_OPTS = ("num_cus", "gemv_rows", "gateup_outs", "down_rows", "lm_rows", "attn_splits")
 
@@ -165,6 +166,7 @@ def lib():
         L.mk_plan_trace.argtypes = [vp, vp, vp, sz, P(ctypes.c_double)]
         L.mk_plan_debug_raise_wait.argtypes = [vp, i32, i32]
         L.mk_plan_poison_workspace.argtypes = [vp, vp]
+        L.mk_stream_probe.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp]
         L.mk_run_noalloc.argtypes = [vp, P(Weights), vp, vp, vp, vp, vp]
         L.mk_noalloc_bytes.argtypes = [vp, P(sz), P(sz)]
         L.mk_plan_free.argtypes = [vp]
@@ -427,3 +429,10 @@ def glm_caches_to_device(kv_cache, idx_cache):
     import torch
     flat = np.concatenate([np.ascontiguousarray(kv_cache).ravel(), np.ascontiguousarray(idx_cache).ravel()])
     return torch.from_numpy(flat.view(np.int16)).to("cuda")
+
+
+def stream_probe(buf, lds_dma, workgroups, waves, depth, sink, stream=None):
+    """mk_stream_probe: one streaming read of the device tensor buf."""
+    s = vp(stream.cuda_stream if stream is not None else current_stream())
+    _check(lib().mk_stream_probe(vp(buf.data_ptr()), buf.numel() * buf.element_size(), int(lds_dma),
+                                 int(workgroups), int(waves), int(depth), vp(sink.data_ptr()), s))

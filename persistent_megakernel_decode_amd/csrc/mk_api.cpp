@@ -17,6 +17,7 @@
 
 #include "mk.h"
 #include "mk_device.hpp"
+#include "mk_glm.hpp"
 #include "plan.hpp"
 
 // Device memory of the allocation-free entry point (mk_run_noalloc): one
@@ -34,6 +35,8 @@ hipError_t megakernel_occupancy(int hd, int batch, bool glm, int* blocks_per_cu)
 int ring_pages(int batch);
 hipError_t launch_step_setup(int* queue, const void* patches, int n, float* rope, const float* rope_src, int nr,
                              int* tok, const int* next, int* out, int nt, hipStream_t s);
+hipError_t launch_stream_probe(const void* src, long npages, int lds_dma, int workgroups, int waves, int depth,
+                               unsigned* sink, hipStream_t s);
 }  // namespace mk
 
 namespace {
@@ -124,7 +127,7 @@ struct mk_plan {
   int n_seq = 0;
   int* d_rows = nullptr;
   size_t off_gn = 0, off_ga8 = 0, off_gas = 0, off_gqkva = 0, off_gqa8 = 0, off_gqs = 0, off_gr = 0, off_gq = 0,
-         off_gqidx = 0, off_ggate = 0;
+         off_gqidx = 0, off_ggate = 0, off_ggpart = 0;
 };
 
 static std::atomic<uint64_t> g_plan_uid{0};
@@ -222,6 +225,14 @@ static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_
   if (d.rows_per_seq < 1 || nh < 1 || d.n_idx_heads < 1) return fail(MK_E_INVALID, "GLM sizes must be positive");
   if (H < 128 || H % 128 || QL < 128 || QL % 128) return fail(MK_E_UNSUPPORTED, "hidden and q_lora must be multiples of 128");
   if (KL < 8 || KL % 8) return fail(MK_E_UNSUPPORTED, "kv_lora must be a positive multiple of 8");
+  // the row ops keep a wave's share of a row in registers (hidden: 16 blocks of
+  // 128 per wave; q_lora: 8 blocks per wave over three waves; kv_lora: 2 chunks
+  // of 8 per lane), and the cache rows are stored 16 bytes at a time
+  if (H > mkd::kNW * 4 * mkd::kA0Groups * 128 || QL > 3 * 4 * mkd::kQaGroups * 128 || KL > 8 * 64 * mkd::kKvChunks ||
+      mk::ceil_div(H / 128, mk::kGateBlocks) > mkd::kMaxGateSplits ||
+      (KL + RD) % 8)
+    return fail(MK_E_UNSUPPORTED, "hidden <= 8192, q_lora <= 3072, kv_lora <= 1024 and kv_lora + rope_dim a "
+                                  "multiple of 8");
   if (nope < 16 || nope % 16 || RD < 16 || RD % 16 || RD > 128)
     return fail(MK_E_UNSUPPORTED, "head_dim - rope_dim and rope_dim (<= 128) must be positive multiples of 16");
   if (d.n_gate < 16 || d.n_gate % 16 || d.idx_head_dim < 16 || d.idx_head_dim % 16 || Niq % 16)
@@ -299,6 +310,9 @@ static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_
   p->off_gq = take((size_t)M * nh * hd * 2);
   p->off_gqidx = take((size_t)M * Niq * 2);
   p->off_ggate = take((size_t)M * d.n_gate * 4);
+  // head-gate K-split partials: [split][row tile][16 tokens][16 rows] fp32
+  const int gsplits = mk::ceil_div(H / 128, mk::kGateBlocks);
+  p->off_ggpart = take((size_t)gsplits * mk::ceil_div(d.n_gate, mkd::kMB) * mkd::kMB * mkd::kMB * 4);
   p->ws_bytes = off;
   *out = p;
   return MK_OK;
@@ -665,7 +679,11 @@ static void fill_rows(const mk_plan* p, const Src& src, uint64_t* vals, int32_t*
           put(o, mkd::GmW, w(3), MK_SLOT_G_W);
           put(o, mkd::GmS, w(4), MK_SLOT_G_W_SCALE);
           put(o, mkd::GmAF, ws(p->off_gn), MK_SLOT_G_NORM);
-          put(o, mkd::GmOut, ws(p->off_ggate), MK_SLOT_G_GATE);
+          put(o, mkd::GmOut, ws(p->off_ggpart), MK_SLOT_G_GATE_PART);
+          break;
+        case mk::kGGateRed:
+          put(o, mkd::GrPart, ws(p->off_ggpart), MK_SLOT_G_GATE_PART);
+          put(o, mkd::GrOut, ws(p->off_ggate), MK_SLOT_G_GATE);
           break;
         case mk::kGIdxk:
           put(o, mkd::GmW, w(5), MK_SLOT_G_W);
@@ -1358,6 +1376,19 @@ mk_status mk_plan_debug_raise_wait(mk_plan* p, int32_t event, int32_t delta) {
   p->version += 1;
   if (p->uploaded)
     HIPCHK(hipMemcpy(p->d_queue, p->P.queue.data(), p->P.queue.size() * 4, hipMemcpyHostToDevice), "upload queue");
+  return MK_OK;
+}
+
+mk_status mk_stream_probe(const void* src, size_t bytes, int32_t lds_dma, int32_t workgroups, int32_t waves,
+                          int32_t depth, void* sink, void* stream) {
+  g_err.clear();
+  if (!src || !sink) return fail(MK_E_INVALID, "null buffer");
+  if (bytes == 0 || bytes % mkd::kPage) return fail(MK_E_INVALID, "bytes must be a positive multiple of 16 KiB");
+  if (workgroups < 1 || waves < 1 || waves > 8 || depth < 1 || depth > (lds_dma ? 4 : 2))
+    return fail(MK_E_INVALID, "workgroups >= 1, waves 1..8, depth 1..4 (LDS-DMA) or 1..2 (register loads)");
+  HIPCHK(mk::launch_stream_probe(src, (long)(bytes / mkd::kPage), lds_dma, workgroups, waves, depth, (unsigned*)sink,
+                                 (hipStream_t)stream),
+         "stream probe launch");
   return MK_OK;
 }
 

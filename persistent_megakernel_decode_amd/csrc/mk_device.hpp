@@ -35,7 +35,8 @@ enum : int { OpNoop = 0, OpQkv = 1, OpAttn = 2, OpCombine = 3, OpOproj = 4, OpGa
 // GLM-style pre-attention path: add + RMSNorm + fp8 quant (one token row per
 // task), fp8 GEMM tiles of 16 weight rows (QKV-A, head gate, indexer-K, QKV-B,
 // indexer-Q) and the q path's RMSNorm + requant with the KV-row write.
-enum : int { OpGA0 = 9, OpGQkva = 10, OpGGate = 11, OpGIdxk = 12, OpGQaNorm = 13, OpGQkvb = 14, OpGIdxq = 15 };
+enum : int { OpGA0 = 9, OpGQkva = 10, OpGGate = 11, OpGIdxk = 12, OpGQaNorm = 13, OpGQkvb = 14, OpGIdxq = 15,
+             OpGGateRed = 16 };
 
 // ---- operand table slots (one row of 16 u64 per op) --------------------------
 enum : int {
@@ -61,7 +62,9 @@ enum : int {
   // (or the fp32 norm output for the gate), output, RoPE table, token rows info
   GmW = 0, GmS = 1, GmA8 = 2, GmAS = 3, GmAF = 4, GmOut = 5, GmRope = 6, GmRows = 7,
   // GLM q-path norm: QKV-A output, q / kv norm weights, q codes and scales, KV cache, RoPE, rows
-  QnIn = 0, QnNorm = 1, QnKvNorm = 2, QnA8 = 3, QnAS = 4, QnKv = 5, QnRope = 6, QnRows = 7
+  QnIn = 0, QnNorm = 1, QnKvNorm = 2, QnA8 = 3, QnAS = 4, QnKv = 5, QnRope = 6, QnRows = 7,
+  // GLM head-gate reduce: the K-split partials, the gate output
+  GrPart = 0, GrOut = 1
 };
 
 constexpr int kPage = 16384;  // bytes per LDS page
@@ -187,6 +190,18 @@ __device__ __forceinline__ void st_agent(GLB float* p, float v) {
 __device__ __forceinline__ void st_agent(GLB int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes per lane at base + off (base wave-uniform, off per lane, 16-byte
+// aligned), with the cache policy of st_agent (sc1: written through to the
+// device's coherence point): one store instruction instead of four scattered
+// ones, for lanes that own four consecutive fp32 outputs.
+__device__ __forceinline__ void st_agent16(const GLB void* base, uint32_t off, f32x4 v) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 16 /* sc1 */);
+}
 // Reads of data that other compute units wrote during the same step
 // (activations, residual stream, q/k/v, attention partials, LM tile maxima,
 // quantized activations and scales).  The producers store them agent-coherent
@@ -281,6 +296,9 @@ struct Tile {
   const GLB char* p1;
   int len0, off1, len1;
   int bytes, npages;
+  // segment 0 as rows of seglen bytes, stride bytes apart in memory (packed
+  // densely in the tile); stride 0: one contiguous run
+  int seglen, stride;
 };
 
 __device__ __forceinline__ int round1k(int v) { return (v + 1023) & ~1023; }
@@ -291,6 +309,7 @@ __device__ inline Tile tile_info(const M& m, const Consts& c) {
   t.p0 = nullptr;
   t.p1 = nullptr;
   t.len0 = t.off1 = t.len1 = 0;
+  t.seglen = t.stride = 0;
   const int op = m.w(WOpcode);
   switch (op) {
     case OpQkv: {
@@ -322,8 +341,17 @@ __device__ inline Tile tile_info(const M& m, const Consts& c) {
       t.p0 = (const GLB char*)m.q(LmW) + (size_t)m.w(WPay) * c.H * 2;
       t.len0 = m.w(WPay + 1) * c.H * 2;
       break;
+    case OpGGate: {
+      // a K-split of 16 rows: blocks [kb0, kb0 + nkb) of 128 columns, each row's
+      // part contiguous (nkb * 128 bytes), the rows c.H bytes apart
+      const int row0 = m.w(WPay), nrows = m.w(WPay + 1), kb0 = m.w(WPay + 3), nkb = m.w(WPay + 4);
+      t.p0 = (const GLB char*)m.q(GmW) + (size_t)row0 * c.H + kb0 * 128;
+      t.seglen = nkb * 128;
+      t.stride = c.H;
+      t.len0 = nrows * t.seglen;
+      break;
+    }
     case OpGQkva:
-    case OpGGate:
     case OpGIdxk:
     case OpGQkvb:
     case OpGIdxq: {
@@ -365,6 +393,7 @@ __device__ inline Tile tile_info(const M& m, const Consts& c) {
 // subtraction: min over unsigned of x and x - ring size (the second wraps to a
 // huge value while x is below the ring size).  The uniform part of x is scalar.
 struct LdsSrc {
+  static constexpr bool kLds = true;  // tiles packed densely (strided rows become rows of their own length)
   uint32_t ring;   // LDS byte address of ring slot 0
   uint32_t first;  // first * kPage
   uint32_t off1;   // tile offset of segment 1
@@ -381,6 +410,9 @@ struct LdsSrc {
   __device__ __forceinline__ uint16_t ld2(int seg, int o) const {
     return *(const LDS uint16_t*)(uintptr_t)addr(seg, (uint32_t)o);
   }
+  __device__ __forceinline__ uint32_t ld4(int seg, int o) const {
+    return *(const LDS uint32_t*)(uintptr_t)addr(seg, (uint32_t)o);
+  }
 };
 // A tile whose pages do not wrap around the ring end: plain offsets.
 struct LdsLin {
@@ -393,6 +425,7 @@ struct LdsLin {
 };
 // Straight from device memory (layerwise kernels).
 struct GlbSrc {
+  static constexpr bool kLds = false;  // tiles read in place (row stride of the weight matrix)
   const GLB char* p0;
   const GLB char* p1;
   __device__ __forceinline__ uint4 ld16(int seg, int o) const {
@@ -400,6 +433,7 @@ struct GlbSrc {
     return make_uint4(v.x, v.y, v.z, v.w);
   }
   __device__ __forceinline__ uint16_t ld2(int seg, int o) const { return *(const GLB uint16_t*)((seg ? p1 : p0) + o); }
+  __device__ __forceinline__ uint32_t ld4(int seg, int o) const { return *(const GLB uint32_t*)((seg ? p1 : p0) + o); }
 };
 
 // Which activation and norm a GEMV op reads, and its K.

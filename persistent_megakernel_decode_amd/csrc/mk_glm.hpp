@@ -21,6 +21,8 @@ namespace mkd {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
+// a GEMM tile: 16 weight rows, partials of the four compute waves summed by the
+// storer (the head gate's K-split tiles included; its reduce op is a row op)
 __device__ __forceinline__ bool glm_is_gemm(int op) {
   return op == OpGQkva || op == OpGGate || op == OpGIdxk || op == OpGQkvb || op == OpGIdxq;
 }
@@ -53,7 +55,8 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
 // Rows past the tile re-read its last row and tokens past M re-read token 0;
 // those outputs are never stored.  Partial block: part[(4 g + i) * 16 + b].
 template <int POL = 0, class Src>
-__device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts& c, int cw, LDS float* part) {
+__device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts& c, int cw, LDS float* part,
+                                     unsigned long long* tr = nullptr) {
   const int op = m.w(WOpcode);
   const int lane = lane_id();
   const int K = (op == OpGQkvb || op == OpGIdxq) ? c.ql : c.H;
@@ -71,36 +74,63 @@ __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts
   const GLB float* ws = (const GLB float*)m.q(GmS) + (size_t)(row0 / 128) * nkb;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (op == OpGGate) {
-    // the gate reads the unquantized fp32 norm output: bf16 high and low parts
-    // against the exactly converted weights, 4 k-steps of 8 per lane per block
+    // a K-split tile: blocks [gkb0, gkb0 + gnkb), one per compute wave; its rows
+    // sit gnkb * 128 bytes apart in the LDS tile (in memory: K bytes apart).
+    // The gate reads the unquantized fp32 norm output: bf16 high and low parts
+    // against the exactly converted weights, 4 k-steps of 8 per lane per block.
+    // The k order within a block is permuted (the same way for both operands,
+    // so the block's sum is unchanged): load t of lane (token, g) takes the 4
+    // activations at 16 t + 4 g, so the four g lanes of a token read 64
+    // contiguous bytes; k-step ks uses loads 2 ks and 2 ks + 1, and the weight
+    // bytes at the same positions.
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     const CohT<POL> cx((const GLB float*)m.q(GmAF));
     const uint32_t xo = (uint32_t)(bb * K) * 4;
-    for (int kb = kb0; kb < kb1; ++kb) {
-      const int ko = kb * 128 + g * 32;
-      const uint4 w0 = src.ld16(seg, rr * K + ko), w1 = src.ld16(seg, rr * K + ko + 16);
-      const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      f32x4 blk = {0.f, 0.f, 0.f, 0.f};
+    const int gkb0 = m.w(WPay + 3), gnkb = m.w(WPay + 4);
+    const int lrow = Src::kLds ? gnkb * 128 : K;  // bytes between the tile's rows in src
+    constexpr int UG = 1;  // blocks whose weight and activation loads are issued together
+    for (int kq = gkb0 + cw; kq < gkb0 + gnkb; kq += kNW * UG) {
+      uint32_t wd[UG][8];
+      f32x4 xa[UG][8];
+      float sc[UG];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f32x4 x0 = cx.f4(xo + (uint32_t)(ko + ks * 8) * 4);
-        const f32x4 x1 = cx.f4(xo + (uint32_t)(ko + ks * 8 + 4) * 4);
-        const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        bf16x8 av, hi, lo;
+      for (int u = 0; u < UG; ++u) {
+        const int kb = kq + u * kNW < gkb0 + gnkb ? kq + u * kNW : kq;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t code = (wd[2 * ks + e / 4] >> (8 * (e & 3))) & 0xFFu;
-          av[e] = __builtin_bit_cast(__bf16, (uint16_t)e4m3_to_bf16(code));
-          const __bf16 h = (__bf16)v[e];
-          hi[e] = h;
-          lo[e] = (__bf16)(v[e] - (float)h);
+        for (int t = 0; t < 8; ++t) {
+          const int kl = 16 * t + 4 * g;
+          wd[u][t] = src.ld4(seg, rr * lrow + (kb - gkb0) * 128 + kl);
+          xa[u][t] = cx.f4(xo + (uint32_t)(kb * 128 + kl) * 4);
         }
-        blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hi, blk, 0, 0, 0);
-        blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lo, blk, 0, 0, 0);
+        sc[u] = kq + u * kNW < gkb0 + gnkb ? ws[kb] : 0.f;
       }
-      const float sc = ws[kb];
+      __builtin_amdgcn_sched_barrier(0);  // one memory latency per group of blocks
+      if (tr && kq == gkb0 + cw && lane == 0) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        tr[6] = now_ticks();
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(blk[i], sc, acc[i]);
+      for (int u = 0; u < UG; ++u) {
+        f32x4 blk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const f32x4 x0 = xa[u][2 * ks], x1 = xa[u][2 * ks + 1];
+          const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          bf16x8 av, hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t code = (wd[u][2 * ks + e / 4] >> (8 * (e & 3))) & 0xFFu;
+            av[e] = __builtin_bit_cast(__bf16, (uint16_t)e4m3_to_bf16(code));
+            const __bf16 h = (__bf16)v[e];
+            hi[e] = h;
+            lo[e] = (__bf16)(v[e] - (float)h);
+          }
+          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hi, blk, 0, 0, 0);
+          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lo, blk, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(blk[i], sc[u], acc[i]);
+      }
     }
   } else {
     const CohT<POL> ca((const GLB uint8_t*)m.q(GmA8)), cs((const GLB float*)m.q(GmAS));
@@ -130,6 +160,7 @@ __device__ inline void glm_gemm_wave(const Src& src, const Meta& m, const Consts
       }
     }
   }
+  if (tr && lane == 0) tr[7] = now_ticks();
 #pragma unroll
   for (int i = 0; i < 4; ++i) part[(4 * g + i) * kMB + b] = acc[i];
 }
@@ -167,134 +198,198 @@ __device__ __forceinline__ void st_agent_u64(GLB void* p, uint2 v) {
 }
 
 // ---- A0: add + RMSNorm + fp8 quant of token row m.WPay ------------------------
-// Every wave sums the squares of the whole row (the row is 2 x hidden bf16, read
-// once from memory and then from the cache); wave cw then finishes its quarter
-// of the 128-column blocks: 16 lanes per block, 8 elements per lane.  Outputs
-// the residual sum in bf16, the norm output in fp32 (the gate's input) and the
-// codes and scales (the other GEMMs' input).
-__device__ inline void glm_a0_wave(const Meta& m, const Consts& c, int cw) {
+// Wave cw owns a quarter of the row's 128-column blocks: 16 lanes per block, 8
+// elements per lane, up to GRP groups of four blocks per wave.  Every load of
+// the wave's share (x, r and the norm weight) is issued at once; the wave's
+// sum of squares goes through xsum, which returns the sum over the four waves
+// (the same value, added in wave order, on every wave), and the codes are then
+// formed from the values still in registers.  Outputs the residual sum in bf16,
+// the norm output in fp32 (the gate's input) and the codes and scales (the
+// other GEMMs' input).
+constexpr int kA0Groups = 4;  // 16 blocks per wave: hidden up to 8192
+template <class XSum>
+__device__ inline void glm_a0_wave(const Meta& m, const Consts& c, int cw, const XSum& xsum,
+                                   unsigned long long* tr = nullptr) {
   const int lane = lane_id(), row = m.w(WPay), H = c.H;
   const GLB uint16_t* x = (const GLB uint16_t*)m.q(GaX) + (size_t)row * H;
   const GLB uint16_t* r = (const GLB uint16_t*)m.q(GaR) + (size_t)row * H;
-  const int nch = H / 8;
-  float ss = 0.f;
-  for (int j0 = 0; j0 < nch; j0 += 4 * 64) {
-    u32x4 xv[4], rv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * 64 + lane;
-      const int jj = j < nch ? j : 0;
-      xv[u] = *(const GLB u32x4*)(x + jj * 8);
-      rv[u] = *(const GLB u32x4*)(r + jj * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (j0 + u * 64 + lane < nch) {
-        const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w}, rw[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float h0 = bf16lo(xw[e]) + bf16lo(rw[e]), h1 = bf16hi(xw[e]) + bf16hi(rw[e]);
-          ss = fmaf(h0, h0, ss);
-          ss = fmaf(h1, h1, ss);
-        }
-      }
-    }
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.f / sqrtf(ss / (float)H + c.eps);
+  const GLB uint16_t* w = (const GLB uint16_t*)m.q(GaNorm);
   const int nb = H / 128, per = (nb + kNW - 1) / kNW;
   const int b0 = cw * per, b1 = b0 + per < nb ? b0 + per : nb;
-  const GLB uint16_t* w = (const GLB uint16_t*)m.q(GaNorm);
+  u32x4 xv[kA0Groups], rv[kA0Groups], wv[kA0Groups];
+  bool live[kA0Groups];
+  int k0[kA0Groups];
+#pragma unroll
+  for (int gq = 0; gq < kA0Groups; ++gq) {
+    const int blk = b0 + 4 * gq + (lane >> 4);
+    live[gq] = blk < b1;
+    k0[gq] = (live[gq] ? blk : 0) * 128 + (lane & 15) * 8;
+    if (b0 + 4 * gq < b1) {
+      xv[gq] = *(const GLB u32x4*)(x + k0[gq]);
+      rv[gq] = *(const GLB u32x4*)(r + k0[gq]);
+      wv[gq] = *(const GLB u32x4*)(w + k0[gq]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // one memory latency for all of them
+  float h[kA0Groups][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int gq = 0; gq < kA0Groups; ++gq) {
+    if (b0 + 4 * gq >= b1) continue;
+    const uint32_t xw[4] = {xv[gq].x, xv[gq].y, xv[gq].z, xv[gq].w};
+    const uint32_t rw[4] = {rv[gq].x, rv[gq].y, rv[gq].z, rv[gq].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[gq][2 * e] = bf16lo(xw[e]) + bf16lo(rw[e]);
+      h[gq][2 * e + 1] = bf16hi(xw[e]) + bf16hi(rw[e]);
+    }
+    if (live[gq]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(h[gq][e], h[gq][e], ss);
+    }
+  }
+  if (tr && lane == 0) tr[6] = now_ticks();
+  const float inv = 1.f / sqrtf(xsum(wave_sum(ss)) / (float)H + c.eps);
+  if (tr && lane == 0) tr[7] = now_ticks();
   GLB uint16_t* rout = (GLB uint16_t*)m.q(GaROut) + (size_t)row * H;
   GLB float* nout = (GLB float*)m.q(GaN) + (size_t)row * H;
   GLB uint8_t* codes = (GLB uint8_t*)m.q(GaA8) + (size_t)row * H;
   GLB float* scales = (GLB float*)m.q(GaAS) + (size_t)row * nb;
-  for (int bq = b0; bq < b1; bq += 4) {
-    const int blk = bq + (lane >> 4);
-    const bool live = blk < b1;
-    const int k0 = (live ? blk : b0) * 128 + (lane & 15) * 8;
-    const u32x4 xv = *(const GLB u32x4*)(x + k0), rv = *(const GLB u32x4*)(r + k0), wv = *(const GLB u32x4*)(w + k0);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
-    float h[8], u[8], n[8];
+#pragma unroll
+  for (int gq = 0; gq < kA0Groups; ++gq) {
+    if (b0 + 4 * gq >= b1) continue;
+    const uint32_t ww[4] = {wv[gq].x, wv[gq].y, wv[gq].z, wv[gq].w};
+    float u[8], n[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      h[2 * e] = bf16lo(xw[e]) + bf16lo(rw[e]);
-      h[2 * e + 1] = bf16hi(xw[e]) + bf16hi(rw[e]);
-      u[2 * e] = h[2 * e] * bf16lo(ww[e]);
-      u[2 * e + 1] = h[2 * e + 1] * bf16hi(ww[e]);
+      u[2 * e] = h[gq][2 * e] * bf16lo(ww[e]);
+      u[2 * e + 1] = h[gq][2 * e + 1] * bf16hi(ww[e]);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) n[e] = u[e] * inv;
     float sc;
     const uint2 q = glm_quant8(u, inv, &sc);
-    if (live) {
+    if (live[gq]) {
       u32x4 hb;
-      hb.x = (uint32_t)f2bf(h[0]) | ((uint32_t)f2bf(h[1]) << 16);
-      hb.y = (uint32_t)f2bf(h[2]) | ((uint32_t)f2bf(h[3]) << 16);
-      hb.z = (uint32_t)f2bf(h[4]) | ((uint32_t)f2bf(h[5]) << 16);
-      hb.w = (uint32_t)f2bf(h[6]) | ((uint32_t)f2bf(h[7]) << 16);
-      *(GLB u32x4*)(rout + k0) = hb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st_agent(nout + k0 + e, n[e]);
-      st_agent_u64(codes + k0, q);
-      if ((lane & 15) == 0) st_agent(scales + blk, sc);
+      hb.x = (uint32_t)f2bf(h[gq][0]) | ((uint32_t)f2bf(h[gq][1]) << 16);
+      hb.y = (uint32_t)f2bf(h[gq][2]) | ((uint32_t)f2bf(h[gq][3]) << 16);
+      hb.z = (uint32_t)f2bf(h[gq][4]) | ((uint32_t)f2bf(h[gq][5]) << 16);
+      hb.w = (uint32_t)f2bf(h[gq][6]) | ((uint32_t)f2bf(h[gq][7]) << 16);
+      *(GLB u32x4*)(rout + k0[gq]) = hb;
+      st_agent16(nout, (uint32_t)k0[gq] * 4, f32x4{n[0], n[1], n[2], n[3]});
+      st_agent16(nout, (uint32_t)(k0[gq] + 4) * 4, f32x4{n[4], n[5], n[6], n[7]});
+      st_agent_u64(codes + k0[gq], q);
+      if ((lane & 15) == 0) st_agent(scales + (k0[gq] >> 7), sc);
     }
   }
 }
 
 // ---- q path: RMSNorm + requant of QKV-A's q columns, KV row ----------------------
-// Waves 0..2 share the q blocks (each sums the squares of all q columns); wave 3
+// Waves 0..2 own a third of the q blocks each (up to QG groups of four blocks;
+// their sums of squares are added through xsum, wave 3 adding zero); wave 3
 // normalizes the kv columns, rotates the k_rope columns and writes the bf16 row
-// [kv | k_rope] at the token's position of its request's cache.
-template <int POL = 0>
-__device__ inline void glm_qan_wave(const Meta& m, const Consts& c, int cw) {
+// [kv | k_rope] at the token's position of its request's cache.  Every load of a
+// wave is issued before any is used.
+constexpr int kQaGroups = 2;  // 8 blocks per wave: q_lora up to 3072
+constexpr int kKvChunks = 2;  // 16-byte kv chunks per lane of wave 3: kv_lora up to 1024
+template <int POL = 0, class XSum>
+__device__ inline void glm_qan_wave(const Meta& m, const Consts& c, int cw, const XSum& xsum) {
   const int lane = lane_id(), row = m.w(WPay);
   const CohT<POL> ci((const GLB float*)m.q(QnIn) + (size_t)row * c.na);  // the row's QKV-A output
-  auto sumsq = [&](int e0, int n) {  // elements e0 .. e0 + n - 1, n a multiple of 4
-    float ss = 0.f;
-    for (int j = lane; j < n / 4; j += 64) {
-      const f32x4 v = ci.f4((uint32_t)(e0 + 4 * j) * 4);
-      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
-    }
-    return wave_sum(ss);
-  };
   if (cw < 3) {
-    const float inv = 1.f / sqrtf(sumsq(0, c.ql) / (float)c.ql + c.eps);
     const int nb = c.ql / 128, per = (nb + 2) / 3;
     const int b0 = cw * per, b1 = b0 + per < nb ? b0 + per : nb;
     const GLB uint16_t* w = (const GLB uint16_t*)m.q(QnNorm);
+    f32x4 x0[kQaGroups], x1[kQaGroups];
+    u32x4 wv[kQaGroups];
+    bool live[kQaGroups];
+    int k0[kQaGroups];
+#pragma unroll
+    for (int gq = 0; gq < kQaGroups; ++gq) {
+      const int blk = b0 + 4 * gq + (lane >> 4);
+      live[gq] = blk < b1;
+      k0[gq] = (live[gq] ? blk : 0) * 128 + (lane & 15) * 8;
+      if (b0 + 4 * gq < b1) {
+        x0[gq] = ci.f4((uint32_t)k0[gq] * 4);
+        x1[gq] = ci.f4((uint32_t)(k0[gq] + 4) * 4);
+        wv[gq] = *(const GLB u32x4*)(w + k0[gq]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float ss = 0.f;
+#pragma unroll
+    for (int gq = 0; gq < kQaGroups; ++gq) {
+      if (b0 + 4 * gq < b1 && live[gq]) {
+        ss = fmaf(x0[gq].x, x0[gq].x, fmaf(x0[gq].y, x0[gq].y, fmaf(x0[gq].z, x0[gq].z, fmaf(x0[gq].w, x0[gq].w, ss))));
+        ss = fmaf(x1[gq].x, x1[gq].x, fmaf(x1[gq].y, x1[gq].y, fmaf(x1[gq].z, x1[gq].z, fmaf(x1[gq].w, x1[gq].w, ss))));
+      }
+    }
+    const float inv = 1.f / sqrtf(xsum(wave_sum(ss)) / (float)c.ql + c.eps);
     GLB uint8_t* codes = (GLB uint8_t*)m.q(QnA8) + (size_t)row * c.ql;
     GLB float* scales = (GLB float*)m.q(QnAS) + (size_t)row * nb;
-    for (int bq = b0; bq < b1; bq += 4) {
-      const int blk = bq + (lane >> 4);
-      const bool live = blk < b1;
-      const int k0 = (live ? blk : b0) * 128 + (lane & 15) * 8;
-      const f32x4 x0 = ci.f4((uint32_t)k0 * 4), x1 = ci.f4((uint32_t)(k0 + 4) * 4);
-      const u32x4 wv = *(const GLB u32x4*)(w + k0);
-      const float u[8] = {x0.x * bf16lo(wv.x), x0.y * bf16hi(wv.x), x0.z * bf16lo(wv.y), x0.w * bf16hi(wv.y),
-                          x1.x * bf16lo(wv.z), x1.y * bf16hi(wv.z), x1.z * bf16lo(wv.w), x1.w * bf16hi(wv.w)};
+#pragma unroll
+    for (int gq = 0; gq < kQaGroups; ++gq) {
+      if (b0 + 4 * gq >= b1) continue;
+      const float u[8] = {x0[gq].x * bf16lo(wv[gq].x), x0[gq].y * bf16hi(wv[gq].x), x0[gq].z * bf16lo(wv[gq].y),
+                          x0[gq].w * bf16hi(wv[gq].y), x1[gq].x * bf16lo(wv[gq].z), x1[gq].y * bf16hi(wv[gq].z),
+                          x1[gq].z * bf16lo(wv[gq].w), x1[gq].w * bf16hi(wv[gq].w)};
       float sc;
       const uint2 q = glm_quant8(u, inv, &sc);
-      if (live) {
-        st_agent_u64(codes + k0, q);
-        if ((lane & 15) == 0) st_agent(scales + blk, sc);
+      if (live[gq]) {
+        st_agent_u64(codes + k0[gq], q);
+        if ((lane & 15) == 0) st_agent(scales + (k0[gq] >> 7), sc);
       }
     }
   } else {
-    const float inv = 1.f / sqrtf(sumsq(c.ql, c.kl) / (float)c.kl + c.eps);
+    (void)xsum(0.f);  // wave 3 takes part in the exchange with nothing to add
     const GLB int* rows = (const GLB int*)m.q(QnRows);
-    const int pos = rows[row], req = rows[c.B + row];
-    GLB uint16_t* out = (GLB uint16_t*)m.q(QnKv) + ((size_t)req * c.cap + pos) * (c.kl + c.rd);
     const GLB uint16_t* w = (const GLB uint16_t*)m.q(QnKvNorm);
-    for (int j = lane; j < c.kl; j += 64) out[j] = f2bf(ci.f1((uint32_t)(c.ql + j) * 4) * inv * bf16f(w[j]));
-    const int half = c.rd / 2;
+    const int half = c.rd / 2, kr = c.ql + c.kl;  // kr: first k_rope column
+    const int nch = c.kl / 8;                      // 8-element chunks of the kv columns
+    f32x4 v0[kKvChunks], v1[kKvChunks];
+    u32x4 wv[kKvChunks];
+#pragma unroll
+    for (int j = 0; j < kKvChunks; ++j) {
+      const int ch = lane + 64 * j < nch ? lane + 64 * j : 0;
+      v0[j] = ci.f4((uint32_t)(c.ql + ch * 8) * 4);
+      v1[j] = ci.f4((uint32_t)(c.ql + ch * 8 + 4) * 4);
+      wv[j] = *(const GLB u32x4*)(w + ch * 8);
+    }
+    const int pl = lane < half ? lane : 0;
+    const float r0 = ci.f1((uint32_t)(kr + pl) * 4), r1 = ci.f1((uint32_t)(kr + pl + half) * 4);
+    const GLB float* rope = (const GLB float*)m.q(QnRope) + ((size_t)row * half + pl) * 2;
+    const float cs = rope[0], sn = rope[1];
+    const int pos = rows[row], req = rows[c.B + row];
+    __builtin_amdgcn_sched_barrier(0);
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kKvChunks; ++j) {
+      if (lane + 64 * j < nch) {
+        ss = fmaf(v0[j].x, v0[j].x, fmaf(v0[j].y, v0[j].y, fmaf(v0[j].z, v0[j].z, fmaf(v0[j].w, v0[j].w, ss))));
+        ss = fmaf(v1[j].x, v1[j].x, fmaf(v1[j].y, v1[j].y, fmaf(v1[j].z, v1[j].z, fmaf(v1[j].w, v1[j].w, ss))));
+      }
+    }
+    const float inv = 1.f / sqrtf(wave_sum(ss) / (float)c.kl + c.eps);
+    GLB uint16_t* out = (GLB uint16_t*)m.q(QnKv) + ((size_t)req * c.cap + pos) * (c.kl + c.rd);
+#pragma unroll
+    for (int j = 0; j < kKvChunks; ++j) {
+      if (lane + 64 * j < nch) {
+        const int e0 = (lane + 64 * j) * 8;
+        const float n8[8] = {v0[j].x * inv * bf16lo(wv[j].x), v0[j].y * inv * bf16hi(wv[j].x),
+                             v0[j].z * inv * bf16lo(wv[j].y), v0[j].w * inv * bf16hi(wv[j].y),
+                             v1[j].x * inv * bf16lo(wv[j].z), v1[j].y * inv * bf16hi(wv[j].z),
+                             v1[j].z * inv * bf16lo(wv[j].w), v1[j].w * inv * bf16hi(wv[j].w)};
+        u32x4 o;  // rows are (kv_lora + rope_dim) bf16 long, 16-byte aligned (checked on the host)
+        o.x = (uint32_t)f2bf(n8[0]) | ((uint32_t)f2bf(n8[1]) << 16);
+        o.y = (uint32_t)f2bf(n8[2]) | ((uint32_t)f2bf(n8[3]) << 16);
+        o.z = (uint32_t)f2bf(n8[4]) | ((uint32_t)f2bf(n8[5]) << 16);
+        o.w = (uint32_t)f2bf(n8[6]) | ((uint32_t)f2bf(n8[7]) << 16);
+        *(GLB u32x4*)(out + e0) = o;
+      }
+    }
     if (lane < half) {
-      const GLB float* rope = (const GLB float*)m.q(QnRope) + ((size_t)row * half + lane) * 2;
-      const int kr = c.ql + c.kl;  // first k_rope column
-      const float cs = rope[0], sn = rope[1];
-      const float x0 = ci.f1((uint32_t)(kr + lane) * 4), x1 = ci.f1((uint32_t)(kr + lane + half) * 4);
-      out[c.kl + lane] = f2bf(x0 * cs - x1 * sn);
-      out[c.kl + lane + half] = f2bf(x1 * cs + x0 * sn);
+      out[c.kl + lane] = f2bf(r0 * cs - r1 * sn);
+      out[c.kl + lane + half] = f2bf(r1 * cs + r0 * sn);
     }
   }
 }
@@ -336,6 +431,20 @@ __device__ inline void glm_epilogue(const Meta& m, const Consts& c, const LDS fl
     return;
   }
   if (!bok) return;
+  if (op == OpGGate) {
+    // the K-split's partial block: [split][row tile][token][16 rows], four
+    // consecutive rows of token b per lane (the reduce op adds the splits)
+    const int Tg = (c.ng + kMB - 1) / kMB;
+    const uint32_t at = (uint32_t)(((m.w(WGy) * Tg + m.w(WGx)) * kMB + b) * kMB + 4 * q) * 4;
+    st_agent16((const GLB float*)m.q(GmOut), at, f32x4{v[0], v[1], v[2], v[3]});
+    return;
+  }
+  if (op == OpGQkva && 4 * q + 3 < nrows) {
+    // four consecutive outputs of token b in one 16-byte store (rows of
+    // q_lora + kv_lora + rope_dim floats, a multiple of 4: checked on the host)
+    st_agent16((const GLB float*)m.q(GmOut), (uint32_t)(b * c.na + row0 + 4 * q) * 4, f32x4{v[0], v[1], v[2], v[3]});
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tr = 4 * q + i;
@@ -344,9 +453,6 @@ __device__ inline void glm_epilogue(const Meta& m, const Consts& c, const LDS fl
     switch (op) {
       case OpGQkva:
         st_agent((GLB float*)m.q(GmOut) + (size_t)b * c.na + n, v[i]);
-        break;
-      case OpGGate:
-        ((GLB float*)m.q(GmOut))[(size_t)b * c.ng + n] = v[i];
         break;
       case OpGIdxk: {
         const GLB int* rows = (const GLB int*)m.q(GmRows);
@@ -362,6 +468,34 @@ __device__ inline void glm_epilogue(const Meta& m, const Consts& c, const LDS fl
         break;
     }
   }
+}
+
+// ---- head-gate reduce: the K-split partials of one row tile, in split order --------
+// One wave: lane l holds token l % 16, rows 4 (l / 16) .. + 3; the splits'
+// partials are loaded in batches of kGateRedBatch (one memory latency each)
+// and added in split order.
+constexpr int kMaxGateSplits = 16;
+constexpr int kGateRedBatch = 4;
+template <int POL = 0>
+__device__ inline void glm_gate_red_wave(const Meta& m, const Consts& c, int cw) {
+  if (cw != 0) return;
+  const int lane = lane_id(), b = lane & 15, q = lane >> 4;
+  const int row0 = m.w(WPay), GS = m.w(WPay + 2), x = m.w(WGx);
+  const int Tg = (c.ng + kMB - 1) / kMB;
+  const CohT<POL> cp((const GLB float*)m.q(GrPart));
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < GS; z0 += kGateRedBatch) {
+    f32x4 pv[kGateRedBatch];
+#pragma unroll
+    for (int u = 0; u < kGateRedBatch; ++u) {
+      const int z = z0 + u < GS ? z0 + u : z0;
+      pv[u] = cp.f4((uint32_t)(((z * Tg + x) * kMB + b) * kMB + 4 * q) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < kGateRedBatch; ++u)
+      if (z0 + u < GS) acc += pv[u];
+  }
+  if (b < c.B) *(GLB f32x4*)((GLB float*)m.q(GrOut) + (size_t)b * c.ng + row0 + 4 * q) = acc;
 }
 
 }  // namespace mkd

@@ -41,6 +41,7 @@ struct CtrlT {
   int slot_full[16];   // generation + 1 of the data in each ring slot (loaders -> compute)
   int slot_rel[16];    // compute-wave releases of each slot, cumulative (kNW per use)
   int arrive[4];       // compute waves done with instruction i (slot i % 4)
+  int xch[4];          // compute waves that posted a partial sum for instruction i (slot i % 4)
   int rel_sink[64];    // target of the zero adds of lanes that release no page
   float part[4][kNW][PW];
   float ssp[4][kNW][SW];
@@ -305,6 +306,7 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
     }
     if (lane == 0) {
       __hip_atomic_store(&L->c.arrive[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&L->c.xch[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       lds_store_rel(&L->c.done_seq, i + 1);
     }
     if (a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 2] = now_ticks();
@@ -402,7 +404,7 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
       // 16-byte chunk picks its segment (chunks past the tile re-read a valid one)
       const int pofs = pg * kPage;
       const GLB char* whole = nullptr;
-      if (pofs + kPage <= t.len0)
+      if (pofs + kPage <= t.len0 && !t.stride)
         whole = t.p0 + pofs;
       else if (t.len1 && pofs >= t.off1 && pofs + kPage <= t.off1 + t.len1)
         whole = t.p1 + (pofs - t.off1);
@@ -432,8 +434,8 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
         for (int j = 0; j < 16; ++j) {
           const int toff = pofs + j * 1024 + lane * 16;
           const GLB char* src = dummy;
-          if (toff < t.len0)
-            src = t.p0 + toff;
+          if (toff < t.len0)  // a strided segment's rows are multiples of 16 bytes long
+            src = t.stride ? t.p0 + (size_t)(toff / t.seglen) * t.stride + toff % t.seglen : t.p0 + toff;
           else if (toff >= t.off1 && toff < t.off1 + t.len1)
             src = t.p1 + (toff - t.off1);
           __builtin_amdgcn_global_load_lds((const GLB void*)src, (lds_void*)(dst + j * 1024), 16, 0, kDmaNT);
@@ -542,12 +544,25 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
       // weights (if any) are in the ring; activations follow the event
       if (!wait_lds_ge(a, L, &L->c.ready_seq, i + 1, ErrReady, i)) return;
       if (cw == 0 && tr && lane == 0) tr[1] = now_ticks();
+      // the row ops' sum of squares over the four compute waves: each posts its
+      // partial in its slot of the instruction and counts itself in, then all add
+      // the four in wave order
+      auto xsum = [&](float v) {
+        if (lane == 0) {
+          L->c.ssp[sl][cw][0] = v;
+          __hip_atomic_fetch_add(&L->c.xch[sl], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        if (!wait_lds_ge(a, L, &L->c.xch[sl], kNW, ErrReady, i)) return v;  // aborting
+        return ((L->c.ssp[sl][0][0] + L->c.ssp[sl][1][0]) + L->c.ssp[sl][2][0]) + L->c.ssp[sl][3][0];
+      };
       if (gemv) {
-        glm_gemm_wave(src, m, a.c, cw, &L->c.part[sl][cw][0]);
+        glm_gemm_wave(src, m, a.c, cw, &L->c.part[sl][cw][0], cw == 0 ? tr : nullptr);
       } else if (op == OpGA0) {
-        glm_a0_wave(m, a.c, cw);
+        glm_a0_wave(m, a.c, cw, xsum, cw == 0 ? tr : nullptr);
       } else if (op == OpGQaNorm) {
-        glm_qan_wave(m, a.c, cw);
+        glm_qan_wave(m, a.c, cw, xsum);
+      } else if (op == OpGGateRed) {
+        glm_gate_red_wave(m, a.c, cw);
       }
       release();
     } else if (gemv && !LT::MB) {
@@ -658,10 +673,19 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
       glm_gemm_wave<0>(src, m, a.c, cw, part[cw]);
       __syncthreads();
       if (cw == 0) glm_epilogue(m, a.c, &part[0][0]);
-    } else if (op == OpGA0) {
-      glm_a0_wave(m, a.c, cw);
-    } else if (op == OpGQaNorm) {
-      glm_qan_wave<0>(m, a.c, cw);
+    } else {
+      // sum of squares over the four waves of the block, added in wave order
+      auto xsum = [&](float v) {
+        if (lane == 0) ssp[cw][0] = v;
+        __syncthreads();
+        return ((ssp[0][0] + ssp[1][0]) + ssp[2][0]) + ssp[3][0];
+      };
+      if (op == OpGA0)
+        glm_a0_wave(m, a.c, cw, xsum);
+      else if (op == OpGQaNorm)
+        glm_qan_wave<0>(m, a.c, cw, xsum);
+      else if (op == OpGGateRed)
+        glm_gate_red_wave<0>(m, a.c, cw);
     }
     return;
   }
@@ -777,4 +801,79 @@ hipError_t launch_step_setup(int* queue, const void* patches, int n, float* rope
   return hipGetLastError();
 }
 
+}  // namespace mk
+
+namespace {
+// ---- streaming-read probe ----------------------------------------------------
+// The ceiling of a plain weight stream on this device, the second denominator of
+// the roofline: pages of 16 KiB are dealt round-robin to (workgroup, wave), and
+// each wave reads its pages either with LDS-DMA into an LDS ring (as the
+// megakernel's loaders do) or with 16-byte loads into registers, keeping DEPTH
+// pages in flight.  Nothing is computed on the data; an XOR of the register
+// loads goes to sink so that they are not removed.
+template <int DEPTH>
+__global__ void __launch_bounds__(512, 1) mk_stream_lds(const char* __restrict__ src, long npages, unsigned* sink) {
+  __shared__ __attribute__((aligned(16))) char ring[8][kPage];
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+  const long stride = (long)gridDim.x * nw;
+  int k = 0;
+  for (long p = (long)blockIdx.x * nw + w; p < npages; p += stride, ++k) {
+    const GLB char* g = (const GLB char*)src + p * kPage + lane * 16;
+    LDS char* dst = (LDS char*)ring[(w * DEPTH + k % DEPTH) & 7];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      __builtin_amdgcn_global_load_lds((const GLB void*)(g + j * 1024), (lds_void*)(dst + j * 1024), 16, 0, kDmaNT);
+    if (DEPTH == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (DEPTH == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    if (DEPTH == 3) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    if (DEPTH == 4) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane == 0 && k == -1) sink[0] = 0;
+}
+
+template <int DEPTH>
+__global__ void __launch_bounds__(512, 1) mk_stream_vgpr(const char* __restrict__ src, long npages, unsigned* sink) {
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+  const long stride = (long)gridDim.x * nw;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (long p0 = (long)blockIdx.x * nw + w; p0 < npages; p0 += stride * DEPTH) {
+    u32x4 v[DEPTH][16];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const long p = p0 + d * stride < npages ? p0 + d * stride : p0;
+      const GLB u32x4* g = (const GLB u32x4*)((const GLB char*)src + p * kPage) + lane;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[d][j] = __builtin_nontemporal_load(g + j * 64);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc ^= v[d][j];
+  }
+  sink[(size_t)blockIdx.x * nw + w] = (acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u ? 1u : 0u;
+}
+
+}  // namespace
+
+namespace mk {
+hipError_t launch_stream_probe(const void* src, long npages, int lds_dma, int workgroups, int waves, int depth,
+                               unsigned* sink, hipStream_t s) {
+  const dim3 g(workgroups), b(64 * waves);
+  const char* p = (const char*)src;
+  if (lds_dma) {
+    switch (depth) {
+      case 1: hipLaunchKernelGGL(mk_stream_lds<1>, g, b, 0, s, p, npages, sink); break;
+      case 2: hipLaunchKernelGGL(mk_stream_lds<2>, g, b, 0, s, p, npages, sink); break;
+      case 3: hipLaunchKernelGGL(mk_stream_lds<3>, g, b, 0, s, p, npages, sink); break;
+      default: hipLaunchKernelGGL(mk_stream_lds<4>, g, b, 0, s, p, npages, sink); break;
+    }
+  } else {
+    switch (depth) {
+      case 1: hipLaunchKernelGGL(mk_stream_vgpr<1>, g, b, 0, s, p, npages, sink); break;
+      default: hipLaunchKernelGGL(mk_stream_vgpr<2>, g, b, 0, s, p, npages, sink); break;
+    }
+  }
+  return hipGetLastError();
+}
 }  // namespace mk

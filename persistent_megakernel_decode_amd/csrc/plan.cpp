@@ -61,12 +61,23 @@ void payload(const GraphOp& op, int x, int y, int z, const std::vector<int32_t>*
       w[0] = x;
       break;
     case kGQkva:
-    case kGGate:
     case kGIdxk:
     case kGIdxq:  // p0 = output rows
       w[0] = x * kGlmRows;
       w[1] = std::min(kGlmRows, p[0] - x * kGlmRows);
       w[2] = -1;
+      break;
+    case kGGate:  // p0 = output rows, p1 = 128-column blocks of K; x row tile, y K-split
+      w[0] = x * kGlmRows;
+      w[1] = std::min(kGlmRows, p[0] - x * kGlmRows);
+      w[2] = -1;
+      w[3] = y * kGateBlocks;
+      w[4] = std::min(kGateBlocks, p[1] - y * kGateBlocks);
+      break;
+    case kGGateRed:  // p0 = output rows, p1 = K-splits
+      w[0] = x * kGlmRows;
+      w[1] = std::min(kGlmRows, p[0] - x * kGlmRows);
+      w[2] = p[1];
       break;
     case kGQkvb: {  // p0 = head_dim, p1 = nope dims, p2 = rope dims; x head, y tile
       const int base = x * p[0];
@@ -550,12 +561,18 @@ std::string glm_graph(const GlmShape& g, int M, std::vector<GraphOp>* ops_out, s
   const std::array<int, 3> none{{-1, -1, -1}}, d0{{0, -1, -1}}, d1{{1, -1, -1}};
   const int a0 = add(kGA0, {{M, 1, 1}}, {{}});
   const int qa = add(kGQkva, {{ceil_div(Na, R), 1, 1}}, {{Na}});
-  const int ga = add(kGGate, {{ceil_div(g.n_gate, R), 1, 1}}, {{g.n_gate}});
+  // the head gate as K-split partial tiles (one 128-column block per compute
+  // wave) and a reduce op that adds the partials of each row tile in split
+  // order: the MegaRTP article's tile_reduce pairing (section 4, "TaskGraph")
+  const int nkb = g.hidden / 128, gsplits = ceil_div(nkb, kGateBlocks), Tg = ceil_div(g.n_gate, R);
+  const int ga = add(kGGate, {{Tg, gsplits, 1}}, {{g.n_gate, nkb}});
   const int ik = add(kGIdxk, {{ceil_div(g.idx_head_dim, R), 1, 1}}, {{g.idx_head_dim}});
+  const int gr = add(kGGateRed, {{Tg, 1, 1}}, {{g.n_gate, gsplits}});
   const int qn = add(kGQaNorm, {{M, 1, 1}}, {{}});
   const int qb = add(kGQkvb, {{g.n_heads, (nope + g.rope_dim) / R, 1}}, {{g.head_dim, nope, g.rope_dim}});
   const int iq = add(kGIdxq, {{ceil_div(Niq, R), 1, 1}}, {{Niq}});
   for (int c : {qa, ga, ik}) edge(a0, c, d0, none, {{M, g.hidden, 1, 1}}, {{1, g.hidden, 1, 1}}, {{M, g.hidden, 1, 1}});
+  edge(ga, gr, d1, d1, {{M, g.n_gate, 1, 1}}, {{M, R, 1, 1}}, {{M, R, 1, 1}});
   edge(qa, qn, d1, d0, {{M, Na, 1, 1}}, {{M, R, 1, 1}}, {{1, Na, 1, 1}});
   for (int c : {qb, iq}) edge(qn, c, d0, none, {{M, g.q_lora, 1, 1}}, {{1, g.q_lora, 1, 1}}, {{M, g.q_lora, 1, 1}});
   return "";

@@ -29,8 +29,9 @@ enum : int {
 // opcodes of the Llama-family decode step
 enum : int { kNoop = 0, kQkv = 1, kAttn = 2, kCombine = 3, kOproj = 4, kGateUp = 5, kDown = 6, kLmHead = 7, kArgmax = 8 };
 // opcodes of the GLM-style pre-attention path
-enum : int { kGA0 = 9, kGQkva = 10, kGGate = 11, kGIdxk = 12, kGQaNorm = 13, kGQkvb = 14, kGIdxq = 15 };
-constexpr int kGlmRows = 16;  // weight rows per fp8 GEMM tile
+enum : int { kGA0 = 9, kGQkva = 10, kGGate = 11, kGIdxk = 12, kGQaNorm = 13, kGQkvb = 14, kGIdxq = 15, kGGateRed = 16 };
+constexpr int kGlmRows = 16;    // weight rows per fp8 GEMM tile
+constexpr int kGateBlocks = 4;  // 128-column blocks per head-gate K-split tile (one per compute wave)
 
 struct GraphOp {
   int opcode = 0, spec = 0, layer = 0;

@@ -111,14 +111,20 @@ def test_cpp_planner_matches_reference_glm(name, num_cus):
 
 def test_glm_plan_structure():
     """A0 (16 rows) forks to QKV-A / gate / indexer-K through one event of 16
-    triggers; QKV-A's 132 tiles join into the q-path norm (one event, 132
+    triggers; the gate's 4 row tiles x 12 K-splits (4 blocks of 128 columns
+    each) reach the gate reduce through one event per row tile (tile_reduce, 12
+    triggers); QKV-A's 132 tiles join into the q-path norm (one event, 132
     triggers); the norm forks to QKV-B (64 heads x 12 tiles) and indexer-Q (256
-    tiles) through one event of 16 triggers: 1200 tasks in all."""
+    tiles) through one event of 16 triggers: 1248 tasks in all."""
     cfg = synth.config("glm_preattn")
     pos, _ = synth.glm_positions(cfg)
     ref = P.plan_model(cfg, len(pos), pos, dict(num_cus=256))
-    assert ref.num_tasks == 16 + 132 + 4 + 8 + 16 + 64 * 12 + 256 == 1200
-    assert list(ref.event_target) == [16, 132, 16] and ref.max_len == 5
+    assert ref.num_tasks == 16 + 132 + 4 * 12 + 8 + 4 + 16 + 64 * 12 + 256 == 1248
+    assert list(ref.event_target) == [16, 12, 12, 12, 12, 132, 16] and ref.max_len == 5
+    q = np.asarray(ref.queue).reshape(-1, 32)
+    gate = q[q[:, 0] == P.G_GATE]
+    # split y covers blocks 4y .. 4y + 3 of the 48
+    assert sorted({(r[12], r[17], r[18]) for r in gate}) == [(y, 4 * y, 4) for y in range(12)]
     # QKV-B payloads: plain tiles of 16 rows, then RoPE-pair tiles (8 rows + 8 rows 32 further on)
     q = np.asarray(ref.queue).reshape(-1, 32)
     qb = q[q[:, 0] == P.G_QKVB]
