@@ -413,6 +413,11 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured layerwise baseline")
     ap.add_argument("--only", choices=["megakernel", "layerwise", "both"], default="both")
     ap.add_argument("--trace-dump", default=None, help="save the traced step's raw trace and queue (npz) here")
+    ap.add_argument("--pairing", type=int, default=0, choices=[0, 1],
+                    help="plan with the pairing strategies (mk_plan_opts.pairing) instead of the gcd/lcm rules")
+    ap.add_argument("--attn-order", type=int, default=0, choices=[-1, 0, 1],
+                    help="attention placement (mk_plan_opts.attn_order): 1 longest first, -1 plan order, "
+                         "0 the default (longest first at batch > 1)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only sweep the streaming-read probe (mk_stream_probe) and print its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -441,7 +446,8 @@ def main():
     w = mk.DeviceWeights(inp["weights"], cfg)
     kv = mk.kv_to_device(inp["kv_cache"])
     tok = mk.tokens_to_device(inp["tokens"])
-    plan = mk.Plan.build(cfg, cfg["batch"], inp["kv_len"], inp["kv_cache"].shape[4])
+    plan = mk.Plan.build(cfg, cfg["batch"], inp["kv_len"], inp["kv_cache"].shape[4], pairing=args.pairing,
+                         attn_order=args.attn_order)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -509,7 +515,8 @@ def main():
                       cfg["n_layers"], cfg["hidden"]),
                    "batch": int(cfg["batch"]), "kv_len": [int(k) for k in inp["kv_len"]],
                    "persistent_grid": "%d workgroups x %d threads" % (plan.export()["num_cus"],
-                                                                      512 if cfg["batch"] == 1 else 768)},
+                                                                      512 if cfg["batch"] == 1 else 768),
+                   "plan": {"pairing": args.pairing, "attn_order": plan.export()["attn_order"]}},
         "algorithmic_bytes": nbytes,
         "achieved_GBps": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",

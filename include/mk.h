@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 
 typedef enum {
   MK_OK = 0,
@@ -126,13 +126,31 @@ typedef struct {
  *   with events, also under stream capture; a chain, like the Llama-family
  *   graph, stays on one stream).  Eager GLM steps are slower with branches (the
  *   event hand-offs cost more than the branches overlap); captured in a graph
- *   they time the same as one stream. */
+ *   they time the same as one stream.
+ * pairing (Llama family): 0 (default) derives events with the gcd/lcm rules
+ *   below; 1 plans with the pairing strategies of mk_pair_plan instead (MegaRTP
+ *   article, section 4, "TaskGraph"): QKV tiles cover their kv head's rows,
+ *   attention splits are partials reduced by combine, every other input is read
+ *   whole, and the residual inputs stay explicit, so O waits on combine and on
+ *   the previous layer's down, and down on gate/up and on O (two waits per
+ *   instruction).  Tasks op by op in grid order.
+ * attn_order (Llama family): 1 places attention tasks longest first (CMU
+ *   15-779 lecture 7 notes, section 6.4, variable-length tasks): within each
+ *   run of consecutive attention tasks that wait on the same events, tasks are
+ *   taken in decreasing KV rows (ties in task order), each on the free position
+ *   of the run whose queue holds the least attention rows of that layer so far
+ *   (ties: lowest position); it moves tasks only within such runs, so the events
+ *   and their thresholds are unchanged.  -1 leaves them in plan order.  0
+ *   (default): longest first at batch 2..16 (sequences of different lengths),
+ *   plan order at batch 1. */
 typedef struct {
   int32_t num_cus, gemv_rows, gateup_outs, down_rows, lm_rows, attn_splits;
   int32_t timeout_ms;
   int32_t dma_pages;
   int32_t lw_streams;
-  int32_t reserved[3];
+  int32_t pairing;
+  int32_t attn_order;
+  int32_t reserved;
 } mk_plan_opts;
 
 /* Build the static tile plan of one decode step (host-only arithmetic; uploads
@@ -182,16 +200,54 @@ typedef struct {
 mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_edge* edges, int32_t n_edges,
                         int32_t num_cus, mk_plan** out);
 
+/* Plan an operator graph under the pairing strategies (MegaRTP article,
+ * section 4, "TaskGraph" and "KernelPlan"; graph only, like mk_graph_plan).  An
+ * op publishes outputs (mk_pair_pub); an edge reads one publication of an
+ * earlier op under a strategy.  The region of producer tile c along region dim
+ * r is c[map[r]] / div[r] (0 where map[r] is -1); tile c publishes only where
+ * c[a] == sel[a] for every axis a with sel[a] >= 0 (e.g. the last split of a
+ * split-K op, which finishes the output tile).  A consumer tile c reads region
+ * c[map[r]] / div[r] of the edge's publication.  Every region some consumer
+ * reads becomes one event; each publishing tile adds 1; the threshold is the
+ * number of publishing tiles.  Strategies (host checks only; the device sees
+ * counters): MK_PAIR_WHOLE needs one region published by every tile;
+ * MK_PAIR_TILE one publishing tile per region; MK_PAIR_TILE_COVER several
+ * disjoint tiles covering a region; MK_PAIR_TILE_REDUCE several partials of a
+ * region, the same count in every region the edge reads.  An instruction
+ * waits on at most two events and signals at most two (one per publication).
+ * Tasks are listed op by op in row-major grid order (last axis fastest),
+ * events numbered in the order consumers first wait on them, and task t goes
+ * to queue t % num_cus at slot t / num_cus.  event_first/last span each
+ * event's waiting tasks (not contiguous in general).  Errors: MK_E_INVALID for
+ * null/out-of-range arguments, an edge reading a later op, a strategy whose
+ * check fails, a region without publishing tiles, more than two waits or
+ * signals on one task (mk_last_error names the edge or task). */
+enum { MK_PAIR_WHOLE = 0, MK_PAIR_TILE = 1, MK_PAIR_TILE_COVER = 2, MK_PAIR_TILE_REDUCE = 3 };
+typedef struct {
+  int32_t op;
+  int32_t map[3], div[3], sel[3];
+} mk_pair_pub;
+typedef struct {
+  int32_t pub, cons, strategy;
+  int32_t map[3], div[3];
+} mk_pair_edge;
+mk_status mk_pair_plan(const mk_graph_op* ops, int32_t n_ops, const mk_pair_pub* pubs, int32_t n_pubs,
+                       const mk_pair_edge* edges, int32_t n_edges, int32_t num_cus, mk_plan** out);
+
 /* Host views of the plan's schedule metadata, valid until mk_plan_free
  * (MegaRTP article, section 4 "KernelPlan": the [num_CUs, max_len, 32] int32
  * instruction tensor, per-event thresholds).
  * queue: int32 [num_cus][max_len][32] (word layout: 0 opcode, 1 spec_id,
  *   2 operand row, 3 wait count, 4 wait event, 5 wait target per run, 6 signal
  *   count, 7 signal event, 8 signal increment, 9 task id, 10 layer, 11-13 grid
- *   coordinates, 14-23 op payload, 24-31 zero; NoOp rows are all zero).
+ *   coordinates, 14-23 op payload, 24/25 second wait event and target,
+ *   26/27 second signal event and increment, 28/29 publication of signal 1/2
+ *   (pairing plans; the device does not read them), 30-31 zero; word 3 / 6
+ *   count the waits / signals (0..2); NoOp rows are all zero).
  * event_target/first/last: per event, triggers per run and the [first, last)
  *   task-id range of its successors.  task_trigger/task_wait: per task, the
- *   event it triggers / waits on, or -1.  op_table: int32 [num_ops][8] rows
+ *   event it triggers / waits on, or -1; task_trigger2/task_wait2 the second
+ *   ones (pairing plans), or -1.  op_table: int32 [num_ops][8] rows
  *   (opcode, spec, layer, grid x, y, z, tasks, 0).  edge_kept: per input edge, 0
  *   when dropped as residual.
  *   tile_opts: the tile options the plan was built with, defaults resolved:
@@ -200,7 +256,9 @@ mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_ed
  *   [num_ops][16]: the kind (MK_SLOT_*) of the tensor each slot of an op's row
  *   points at, 0 for an unused slot (the row itself holds the addresses; one
  *   row per op, shared by all of its tile instructions: MegaRTP article,
- *   section 4, "OperandPtrTable"). */
+ *   section 4, "OperandPtrTable").  pairing, attn_order: the planner choices
+ *   the plan was built with, defaults resolved (pairing 0/1; attn_order 1
+ *   longest first, 0 plan order; 1 and 0 for mk_pair_plan plans). */
 enum {
   MK_SLOT_NONE = 0,
   /* weights (Llama family) */
@@ -231,6 +289,9 @@ typedef struct {
   const uint8_t* edge_kept;
   int32_t tile_opts[6];
   const int32_t* op_slots;
+  const int32_t* task_trigger2;
+  const int32_t* task_wait2;
+  int32_t pairing, attn_order;
 } mk_plan_view;
 mk_status mk_plan_export(const mk_plan* plan, mk_plan_view* out);
 
@@ -293,7 +354,10 @@ mk_status mk_run_layerwise(mk_plan* plan, const mk_weights* weights, void* kv_ca
  * without replanning (MegaRTP article, §三/§四: a plan is regenerated only when
  * tile counts or thresholds change).  Only the attention tasks' payloads (split
  * ranges and the new position) and the RoPE table depend on the lengths; the
- * queue's shape, events and targets do not, and counters stay epoch-based.
+ * queue's shape, events and targets do not, and counters stay epoch-based.  The
+ * placement of the attention tasks is kept (with attn_order longest first, the
+ * order chosen for the lengths the plan was built with; any placement within
+ * a run of equal waits keeps every dependency).
  * kv_len: host int32 [batch], each kv_len[b] + 1 <= max_kv_len.  If the plan has
  * run, the patch is enqueued on stream (a copy from pinned host memory and a
  * small kernel that rewrites the words in the device queue) before any later
@@ -384,11 +448,14 @@ void mk_plan_free(mk_plan* plan);
  * shows NaN.  Errors: MK_E_STATE before the plan's first run. */
 mk_status mk_plan_poison_workspace(mk_plan* plan, void* stream);
 
-/* For tests of the watchdog: add delta to the wait threshold of every
- * instruction that waits on 'event' (re-uploaded at once if the plan has run).
- * A threshold above the event's producer count makes its waiters time out: the
- * grid drains and exits normally and mk_plan_check reports MK_E_TIMEOUT. */
-mk_status mk_plan_debug_raise_wait(mk_plan* plan, int32_t event, int32_t delta);
+/* For tests of the watchdog: add delta to the wait threshold of the
+ * instructions that wait on 'event' (re-uploaded at once if the plan has run):
+ * slot 0 raises every such wait, 1 only those in an instruction's first wait,
+ * 2 only those in its second wait (pairing plans).  A threshold above the
+ * event's producer count makes its waiters time out: the grid drains and exits
+ * normally and mk_plan_check reports MK_E_TIMEOUT.  Errors: MK_E_INVALID for an
+ * event or slot out of range, MK_E_STATE for graph-only plans. */
+mk_status mk_plan_debug_raise_wait(mk_plan* plan, int32_t event, int32_t delta, int32_t slot);
 
 /* Measurement: one streaming read of 'bytes' (a multiple of 16 KiB) at src
  * (device), the ceiling a weight stream can reach on this device: 16 KiB pages

@@ -47,6 +47,8 @@ MAX_DIMS = 4
 W_OPCODE, W_SPEC, W_OPROW, W_WAIT_CNT, W_WAIT_EV, W_WAIT_TGT = 0, 1, 2, 3, 4, 5
 W_SIG_CNT, W_SIG_EV, W_SIG_INC, W_TASK, W_LAYER, W_GX, W_GY, W_GZ, W_PAY = 6, 7, 8, 9, 10, 11, 12, 13, 14
 N_PAY = 10
+# second wait and second signal, and the publication of each signal (pairing plans)
+W_WAIT2_EV, W_WAIT2_TGT, W_SIG2_EV, W_SIG2_INC, W_SIG_PUB, W_SIG2_PUB = 24, 25, 26, 27, 28, 29
 
 # opcodes of the Llama-family decode step
 NOOP, QKV, ATTN, COMBINE, OPROJ, GATEUP, DOWN, LMHEAD, ARGMAX = range(9)
@@ -338,37 +340,207 @@ def plan_graph(ops, edges, num_cus):
 
     # --- 6. placement and encoding -------------------------------------------
     T = len(tasks)
-    max_len = max(1, ceil_div(T, num_cus))
-    queue = np.zeros((num_cus, max_len, WORDS), dtype=np.int32)
-    for t, (o, x, y, z) in enumerate(tasks):
-        op = ops[o]
-        w = queue[t % num_cus, t // num_cus]
-        w[W_OPCODE] = op.opcode
-        w[W_SPEC] = op.spec
-        w[W_OPROW] = o
-        if wait[t] >= 0:
-            w[W_WAIT_CNT], w[W_WAIT_EV], w[W_WAIT_TGT] = 1, wait[t], ev_ntrig[wait[t]]
-        if trig[t] >= 0:
-            w[W_SIG_CNT], w[W_SIG_EV], w[W_SIG_INC] = 1, trig[t], 1
-        w[W_TASK] = t
-        w[W_LAYER] = op.layer
-        w[W_GX], w[W_GY], w[W_GZ] = x, y, z
-        pay = tuple(op.payload(x, y, z))
-        assert len(pay) <= N_PAY
-        for j, v in enumerate(pay):
-            w[W_PAY + j] = int(v)
-
     pl = Plan()
-    pl.num_cus, pl.max_len, pl.num_tasks, pl.num_events = num_cus, max_len, T, len(ev_first)
-    pl.queue = queue
+    pl.num_cus, pl.num_tasks, pl.num_events = num_cus, T, len(ev_first)
     pl.tasks, pl.trigger, pl.wait = tasks, trig, wait
+    pl.trigger2, pl.wait2 = [-1] * T, [-1] * T
     pl.event_first, pl.event_last, pl.event_target = ev_first, ev_last, ev_ntrig
     pl.kept = kept
     pl.evd = evd
     pl.kind = {tuple(sorted(es)): kind[r] for r, es in comps.items()}
     pl.ops = ops
     pl.edges = edges
+    encode(pl)
     return pl
+
+
+# ---------------------------------------------------------------------------
+# Pairing strategies (MegaRTP article, section 4, "TaskGraph")
+# ---------------------------------------------------------------------------
+# An op publishes one or more outputs ("publications"); an edge reads one
+# publication of an earlier op under one of four pairing strategies.  A
+# publication's output is cut into regions: the region of a producer tile is
+# its grid coordinates mapped and divided per region dimension, and only the
+# tiles a publication selects publish (a split-K op whose last split writes the
+# final tile publishes from that split only).  Each region that some consumer
+# reads becomes one counter event; every publishing tile adds one; the event's
+# threshold is the number of its publishing tiles.  The strategies differ only
+# in what the host checks (the device sees counters and thresholds alone):
+#   whole       -- one region, every producer tile publishes: the consumer
+#                  waits for the whole producer;
+#   tile        -- one producer tile per region (threshold 1);
+#   tile_cover  -- several disjoint producer tiles make up the region;
+#   tile_reduce -- several partials of one region (the same count for every
+#                  region the edge reads).
+# An instruction waits on up to two events (the page's D1 waits on two, a
+# join) and signals up to two (its A0 publishes two outputs).  Tasks are
+# listed op by op, each op's grid in row-major order (last axis fastest), and
+# events are numbered in the order consumers first wait on them; placement is
+# round-robin as in ``plan_graph``.  Readings (where the page leaves a step
+# open): the region map (divide the mapped coordinate), the publisher selection
+# (a fixed index per axis) and the numbering orders above.
+WHOLE, TILE, TILE_COVER, TILE_REDUCE = range(4)
+PAIR_NAMES = ("whole", "tile", "tile_cover", "tile_reduce")
+
+
+def _pad3(v, fill):
+    v = tuple(v)
+    return v + (fill,) * (3 - len(v))
+
+
+class Pub:
+    """Publication of op ``op``.  Region dim r of producer tile c is
+    c[map[r]] // div[r] (0 where map[r] is -1); tile c publishes only if
+    c[a] == sel[a] for every axis a with sel[a] >= 0."""
+
+    def __init__(self, op, map=(), div=(), sel=(), name=""):
+        self.op, self.name = op, name
+        self.map, self.div, self.sel = _pad3(map, -1), _pad3(div, 1), _pad3(sel, -1)
+
+
+class PairEdge:
+    """Consumer ``cons`` reads publication ``pub``; the region a consumer tile c
+    waits on has dim r = c[map[r]] // div[r] (0 where map[r] is -1)."""
+
+    def __init__(self, pub, cons, strategy, map=(), div=(), name=""):
+        self.pub, self.cons, self.strategy, self.name = pub, cons, strategy, name
+        self.map, self.div = _pad3(map, -1), _pad3(div, 1)
+
+
+def _region(coord, amap, div):
+    return tuple(coord[amap[r]] // div[r] if amap[r] >= 0 else 0 for r in range(3))
+
+
+def pair_plan(ops, pubs, edges, num_cus):
+    """Plan an op graph whose edges carry pairing strategies (see above)."""
+    n_ops = len(ops)
+    for p in pubs:
+        if not 0 <= p.op < n_ops:
+            raise ValueError("publication of an unknown op")
+        for r in range(3):
+            if p.map[r] >= 3 or p.div[r] < 1 or (p.sel[r] >= 0 and p.sel[r] >= ops[p.op].grid[r]):
+                raise ValueError("publication map/div/sel out of range")
+    for e in edges:
+        if not 0 <= e.pub < len(pubs) or not pubs[e.pub].op < e.cons < n_ops:
+            raise ValueError("an edge must read a publication of an earlier op")
+        if e.strategy not in (WHOLE, TILE, TILE_COVER, TILE_REDUCE):
+            raise ValueError("unknown pairing strategy")
+        if any(e.map[r] >= 3 or e.div[r] < 1 for r in range(3)):
+            raise ValueError("edge map/div out of range")
+
+    def nregions(p):
+        g = ops[p.op].grid
+        return tuple(ceil_div(g[p.map[r]], p.div[r]) if p.map[r] >= 0 else 1 for r in range(3))
+
+    def pub_region(p, c):
+        if any(p.sel[a] >= 0 and c[a] != p.sel[a] for a in range(3)):
+            return None
+        return _region(c, p.map, p.div)
+
+    # publishing tiles per (publication, region)
+    count = [{} for _ in pubs]
+    for k, p in enumerate(pubs):
+        for c in product(*(range(v) for v in ops[p.op].grid)):
+            r = pub_region(p, c)
+            if r is not None:
+                count[k][r] = count[k].get(r, 0) + 1
+
+    tasks = [(o,) + c for o in range(n_ops) for c in product(*(range(v) for v in ops[o].grid))]
+    in_edges = [[] for _ in range(n_ops)]
+    for i, e in enumerate(edges):
+        in_edges[e.cons].append(i)
+    ev_of, ev_target, ev_pub, ev_tasks = {}, [], [], []
+    reduce_n = {}
+    waits = []
+    for t, (o, x, y, z) in enumerate(tasks):
+        w = []
+        for i in in_edges[o]:
+            e = edges[i]
+            p = pubs[e.pub]
+            r = _region((x, y, z), e.map, e.div)
+            if any(r[d] >= nregions(p)[d] for d in range(3)):
+                raise ValueError("edge %d: consumer tile %s reads region %s outside the publication" % (i, (x, y, z), r))
+            n = count[e.pub].get(r, 0)
+            if n == 0:
+                raise ValueError("edge %d: region %s has no publishing tile" % (i, r))
+            if e.strategy == WHOLE and (nregions(p) != (1, 1, 1) or any(s >= 0 for s in p.sel)):
+                raise ValueError("edge %d: 'whole' needs one region that every producer tile publishes" % i)
+            if e.strategy == TILE and n != 1:
+                raise ValueError("edge %d: 'tile' needs one producer tile per region" % i)
+            if e.strategy == TILE_REDUCE and reduce_n.setdefault(i, n) != n:
+                raise ValueError("edge %d: 'tile_reduce' regions must have equal partial counts" % i)
+            key = (e.pub, r)
+            if key not in ev_of:
+                ev_of[key] = len(ev_target)
+                ev_target.append(n)
+                ev_pub.append(e.pub)
+                ev_tasks.append([])
+            ev = ev_of[key]
+            if ev not in w:
+                w.append(ev)
+                ev_tasks[ev].append(t)
+        if len(w) > 2:
+            raise ValueError("task %s waits on more than two events" % ((o, x, y, z),))
+        waits.append(w)
+    pubs_of = [[k for k, p in enumerate(pubs) if p.op == o] for o in range(n_ops)]
+    sigs = []
+    for (o, x, y, z) in tasks:
+        s = []
+        for k in pubs_of[o]:
+            r = pub_region(pubs[k], (x, y, z))
+            if r is not None and (k, r) in ev_of:
+                s.append((ev_of[(k, r)], k))
+        if len(s) > 2:
+            raise ValueError("task %s signals more than two events" % ((o, x, y, z),))
+        sigs.append(s)
+
+    pl = Plan()
+    T = len(tasks)
+    pl.num_cus, pl.num_tasks, pl.num_events = num_cus, T, len(ev_target)
+    pl.tasks = tasks
+    pl.wait = [w[0] if w else -1 for w in waits]
+    pl.wait2 = [w[1] if len(w) > 1 else -1 for w in waits]
+    pl.trigger = [s[0][0] if s else -1 for s in sigs]
+    pl.trigger2 = [s[1][0] if len(s) > 1 else -1 for s in sigs]
+    pl.sig_pub = [[k for _, k in s] for s in sigs]
+    pl.event_target, pl.event_pub = ev_target, ev_pub
+    # successors of a pairing event need not be contiguous: [first, last) spans them
+    pl.event_first = [ts[0] for ts in ev_tasks]
+    pl.event_last = [ts[-1] + 1 for ts in ev_tasks]
+    pl.ops, pl.pubs, pl.edges = ops, pubs, edges
+    pl.kept = [True] * len(edges)
+    encode(pl)
+    return pl
+
+
+def encode(pl):
+    """Place task t in queue t mod C at slot t div C and write its 32 words."""
+    T, C = pl.num_tasks, pl.num_cus
+    pl.max_len = max(1, ceil_div(T, C))
+    queue = np.zeros((C, pl.max_len, WORDS), dtype=np.int32)
+    sig_pub = getattr(pl, "sig_pub", None)
+    for t, (o, x, y, z) in enumerate(pl.tasks):
+        op = pl.ops[o]
+        w = queue[t % C, t // C]
+        w[W_OPCODE], w[W_SPEC], w[W_OPROW] = op.opcode, op.spec, o
+        if pl.wait[t] >= 0:
+            w[W_WAIT_CNT], w[W_WAIT_EV], w[W_WAIT_TGT] = 1, pl.wait[t], pl.event_target[pl.wait[t]]
+            if pl.wait2[t] >= 0:
+                w[W_WAIT_CNT], w[W_WAIT2_EV], w[W_WAIT2_TGT] = 2, pl.wait2[t], pl.event_target[pl.wait2[t]]
+        if pl.trigger[t] >= 0:
+            w[W_SIG_CNT], w[W_SIG_EV], w[W_SIG_INC] = 1, pl.trigger[t], 1
+            if sig_pub is not None:
+                w[W_SIG_PUB] = sig_pub[t][0]
+            if pl.trigger2[t] >= 0:
+                w[W_SIG_CNT], w[W_SIG2_EV], w[W_SIG2_INC], w[W_SIG2_PUB] = 2, pl.trigger2[t], 1, sig_pub[t][1]
+        w[W_TASK], w[W_LAYER] = t, op.layer
+        w[W_GX], w[W_GY], w[W_GZ] = x, y, z
+        pay = tuple(op.payload(x, y, z))
+        assert len(pay) <= N_PAY
+        for j, v in enumerate(pay):
+            w[W_PAY + j] = int(v)
+    pl.queue = queue
+    return queue
 
 
 # ---------------------------------------------------------------------------
@@ -504,16 +676,109 @@ def model_graph(desc, batch, kv_len, opts):
     return ops, edges, dict(S=S, T_qkv=T_qkv, T_o=T_o, T_f=T_f, T_d=T_d, T_v=T_v, spec=spec, opts=o)
 
 
+def model_pairs(ops):
+    """Publications and pairing edges of the Llama-family decode step over the
+    ops of ``model_graph`` (six per layer -- QKV, attention, combine, O, gate/up,
+    down -- then LM head and argmax).  QKV tiles cover their kv head's q/k/v
+    rows (one region per kv head); attention splits are partials of their
+    (sequence, kv head) region, reduced by combine; every other input is read
+    whole.  The residual inputs stay explicit: O waits on combine and on the
+    previous layer's down, down on gate/up and on O (two waits each)."""
+    L = (len(ops) - 2) // 6
+    pubs, edges = [], []
+
+    def pub(op, **kw):
+        pubs.append(Pub(op, **kw))
+        return len(pubs) - 1
+
+    prev_d = None
+    for l in range(L):
+        q, a, c, o, g, d = range(6 * l, 6 * l + 6)
+        pq = pub(q, map=(0,), name="qkv%d" % l)
+        pa = pub(a, map=(0, 1), name="part%d" % l)
+        pc = pub(c, name="ao%d" % l)
+        po = pub(o, name="xa%d" % l)
+        pg = pub(g, name="act%d" % l)
+        if prev_d is not None:
+            edges.append(PairEdge(prev_d, q, WHOLE, name="xb"))
+        edges.append(PairEdge(pq, a, TILE_COVER, map=(1,), name="qkv"))
+        edges.append(PairEdge(pa, c, TILE_REDUCE, map=(0, 1), name="part"))
+        edges.append(PairEdge(pc, o, WHOLE, name="ao"))
+        if prev_d is not None:
+            edges.append(PairEdge(prev_d, o, WHOLE, name="xb_res"))
+        edges.append(PairEdge(po, g, WHOLE, name="xa"))
+        edges.append(PairEdge(pg, d, WHOLE, name="act"))
+        edges.append(PairEdge(po, d, WHOLE, name="xa_res"))
+        prev_d = pub(d, name="xb%d" % l)
+    lm, am = 6 * L, 6 * L + 1
+    edges.append(PairEdge(prev_d, lm, WHOLE, name="xb"))
+    edges.append(PairEdge(pub(lm, name="lmmax"), am, WHOLE, name="lmmax"))
+    return pubs, edges
+
+
+def balance_attention(pl, kv_len, S):
+    """Longest-first placement of the attention tasks (CMU 15-779 lecture 7
+    notes, section 6.4: variable-length tasks placed longest first).  Within
+    each run of consecutive attention tasks with identical waits (one event's
+    consumers: any order within the run keeps every dependency), the tasks are
+    taken longest first (KV rows of their split; ties in task order) and each
+    is put on the free position of the run whose compute unit holds the least
+    attention work of that op so far (ties: the lowest position).  Positions
+    keep their compute unit (t mod C), so only which task lands where changes."""
+    C, T = pl.num_cus, pl.num_tasks
+    ops = pl.ops
+    rows = lambda t: (lambda lo_hi: lo_hi[1] - lo_hi[0])(split_range(int(kv_len[pl.tasks[t][1]]), S, pl.tasks[t][3]))
+    load = {}
+    t = 0
+    while t < T:
+        o = pl.tasks[t][0]
+        if ops[o].opcode != ATTN:
+            t += 1
+            continue
+        e = t + 1
+        while e < T and pl.tasks[e][0] == o and (pl.wait[e], pl.wait2[e]) == (pl.wait[t], pl.wait2[t]):
+            e += 1
+        ld = load.setdefault(o, [0] * C)
+        run = list(range(t, e))
+        order = sorted(run, key=lambda u: (-rows(u), u))
+        free = list(run)
+        new_at = {}
+        for u in order:
+            pos = min(free, key=lambda v: (ld[v % C], v))
+            free.remove(pos)
+            new_at[pos] = u
+            ld[pos % C] += rows(u)
+        old = [(pl.tasks[u], pl.trigger[u], pl.trigger2[u]) for u in run]
+        for pos in run:
+            pl.tasks[pos], pl.trigger[pos], pl.trigger2[pos] = old[new_at[pos] - t]
+        if getattr(pl, "sig_pub", None) is not None:
+            sp = [pl.sig_pub[u] for u in run]
+            for pos in run:
+                pl.sig_pub[pos] = sp[new_at[pos] - t]
+        t = e
+
+
 def plan_model(desc, batch, kv_len, opts):
-    """opts: num_cus (GLM path), or every entry of MODEL_OPTS (Llama family)."""
+    """opts: num_cus (GLM path), or every entry of MODEL_OPTS (Llama family);
+    optionally ``pairing`` (1: plan with the pairing strategies of
+    ``model_pairs`` instead of the gcd/lcm rules) and ``attn_order`` (1:
+    longest-first attention placement, ``balance_attention``)."""
     if desc.get("arch") == "glm":
         if not (opts or {}).get("num_cus"):
             raise ValueError("num_cus must be given")
         o = dict(num_cus=int(opts["num_cus"]))
     else:
         o = check_opts(opts)
+    pairing, attn_order = int((opts or {}).get("pairing", 0)), int((opts or {}).get("attn_order", 0))
     ops, edges, info = model_graph(desc, batch, kv_len, o)
-    pl = plan_graph(ops, edges, o["num_cus"])
+    if pairing and desc.get("arch") != "glm":
+        pubs, pedges = model_pairs(ops)
+        pl = pair_plan(ops, pubs, pedges, o["num_cus"])
+    else:
+        pl = plan_graph(ops, edges, o["num_cus"])
+    if attn_order and desc.get("arch") != "glm":
+        balance_attention(pl, kv_len, o["attn_splits"])
+        encode(pl)
     pl.info = info
     return pl
 

@@ -3,8 +3,8 @@ tests, the smoke check and the benchmark's CPU leg use it).
 
 Models the persistent interpreter the way the CMU 15-779 lecture 7 notes do in
 section 6.5: each worker walks its own queue in order; a task may start only
-when the counter of the event it waits on has reached its target; finishing a
-task adds one to the counter of the event it triggers.  ``order="random"``
+when the counters of the events it waits on (one or two) have reached their
+targets; finishing a task adds its increments to the events it signals.  ``order="random"``
 picks a random runnable worker at each step (uneven worker speeds);
 ``order="serial"`` always takes the smallest runnable task id.  A state where
 unfinished work remains but no worker can start raises ``Deadlock`` with the
@@ -15,10 +15,17 @@ import random
 import numpy as np
 
 from .planner import W_OPCODE, W_TASK, W_WAIT_CNT, W_WAIT_EV, W_WAIT_TGT, W_SIG_CNT, W_SIG_EV, W_SIG_INC
+from .planner import W_WAIT2_EV, W_WAIT2_TGT, W_SIG2_EV, W_SIG2_INC
 
 
 class Deadlock(RuntimeError):
     pass
+
+
+# (event, target) and (event, increment) word pairs of an instruction's up to
+# two waits and two signals
+WAITS = ((W_WAIT_EV, W_WAIT_TGT), (W_WAIT2_EV, W_WAIT2_TGT))
+SIGNALS = ((W_SIG_EV, W_SIG_INC), (W_SIG2_EV, W_SIG2_INC))
 
 
 def replay(queue, num_events, execute, order="serial", seed=0, workers=None):
@@ -46,7 +53,7 @@ def replay(queue, num_events, execute, order="serial", seed=0, workers=None):
         for w, q in enumerate(queues):
             if head[w] < len(q):
                 r = q[head[w]]
-                if not r[W_WAIT_CNT] or ctr[r[W_WAIT_EV]] >= r[W_WAIT_TGT]:
+                if all(ctr[r[ev]] >= r[tg] for ev, tg in WAITS[:r[W_WAIT_CNT]]):
                     runnable.append(w)
         if not runnable:
             stuck = [(w, queues[w][head[w]][W_TASK], queues[w][head[w]][W_WAIT_EV]) for w in range(len(queues))
@@ -58,8 +65,8 @@ def replay(queue, num_events, execute, order="serial", seed=0, workers=None):
             w = min(runnable, key=lambda i: queues[i][head[i]][W_TASK])
         r = queues[w][head[w]]
         execute(r)
-        if r[W_SIG_CNT]:
-            ctr[r[W_SIG_EV]] += r[W_SIG_INC]
+        for ev, inc in SIGNALS[:r[W_SIG_CNT]]:
+            ctr[r[ev]] += r[inc]
         head[w] += 1
         done.append(r[W_TASK])
         remaining -= 1

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_TIMEOUT, MK_E_STATE = 0, -1, -2, -3, -4, -5, -6
-MK_ABI_VERSION = 1
+MK_ABI_VERSION = 2
 MK_ARCH_LLAMA, MK_ARCH_QWEN3, MK_ARCH_GLM_PREATTN = 1, 2, 3
 MK_BF16, MK_FP8_E4M3_B128 = 0, 1
 MK_LAYER_SLOTS = 11
@@ -34,7 +34,8 @@ OUTPUT_TYPES = {MK_OUT_LOGITS: "f32", MK_OUT_NEXT_TOKEN: "i32", MK_OUT_QKV: "f32
 GLM_SLOTS = ("attn_norm", "w_qkva", "s_qkva", "w_gate", "s_gate", "w_idxk", "s_idxk", "q_a_norm", "kv_a_norm",
              "w_qb", "s_qb", "w_idxq", "s_idxq")
 LAYER_SLOTS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
-EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_plan_export", "mk_run",
+EXPORTED = ("mk_last_error", "mk_abi_version", "mk_plan_build", "mk_graph_plan", "mk_pair_plan", "mk_plan_export",
+            "mk_run",
             "mk_run_layerwise", "mk_plan_output", "mk_plan_copy_output", "mk_plan_check", "mk_plan_set_trace",
             "mk_plan_trace", "mk_plan_free", "mk_plan_set_kv_len", "mk_run_steps", "mk_plan_debug_raise_wait",
             "mk_run_noalloc", "mk_noalloc_bytes", "mk_plan_poison_workspace", "mk_stream_probe")
@@ -105,7 +106,8 @@ class ModelDesc(ctypes.Structure):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", i32), ("gemv_rows", i32), ("gateup_outs", i32), ("down_rows", i32), ("lm_rows", i32),
-                ("attn_splits", i32), ("timeout_ms", i32), ("dma_pages", i32), ("lw_streams", i32), ("reserved", i32 * 3)]
+                ("attn_splits", i32), ("timeout_ms", i32), ("dma_pages", i32), ("lw_streams", i32), ("pairing", i32),
+                ("attn_order", i32), ("reserved", i32)]
 
 
 class GraphOp(ctypes.Structure):
@@ -117,11 +119,24 @@ class GraphEdge(ctypes.Structure):
                 ("extent", i32 * 4), ("ptile", i32 * 4), ("ctile", i32 * 4)]
 
 
+# pairing strategies (mk.h MK_PAIR_*)
+MK_PAIR_WHOLE, MK_PAIR_TILE, MK_PAIR_TILE_COVER, MK_PAIR_TILE_REDUCE = range(4)
+
+
+class PairPub(ctypes.Structure):
+    _fields_ = [("op", i32), ("map", i32 * 3), ("div", i32 * 3), ("sel", i32 * 3)]
+
+
+class PairEdge(ctypes.Structure):
+    _fields_ = [("pub", i32), ("cons", i32), ("strategy", i32), ("map", i32 * 3), ("div", i32 * 3)]
+
+
 class PlanView(ctypes.Structure):
     _fields_ = [("num_cus", i32), ("max_len", i32), ("num_tasks", i32), ("num_events", i32), ("num_ops", i32),
                 ("num_edges", i32), ("queue", vp), ("event_target", vp), ("event_first", vp), ("event_last", vp),
                 ("task_trigger", vp), ("task_wait", vp), ("op_table", vp), ("edge_kept", vp),
-                ("tile_opts", i32 * 6), ("op_slots", vp)]
+                ("tile_opts", i32 * 6), ("op_slots", vp), ("task_trigger2", vp), ("task_wait2", vp),
+                ("pairing", i32), ("attn_order", i32)]
 
 
 class Weights(ctypes.Structure):
@@ -154,6 +169,7 @@ def lib():
         L.mk_abi_version.restype = ctypes.c_int
         L.mk_plan_build.argtypes = [P(ModelDesc), i32, vp, P(PlanOpts), P(vp)]
         L.mk_graph_plan.argtypes = [vp, i32, vp, i32, i32, P(vp)]
+        L.mk_pair_plan.argtypes = [vp, i32, vp, i32, vp, i32, i32, P(vp)]
         L.mk_plan_export.argtypes = [vp, P(PlanView)]
         L.mk_run.argtypes = [vp, P(Weights), vp, vp, vp]
         L.mk_run_layerwise.argtypes = [vp, P(Weights), vp, vp, vp]
@@ -164,7 +180,7 @@ def lib():
         L.mk_plan_check.argtypes = [vp, vp, P(Check)]
         L.mk_plan_set_trace.argtypes = [vp, i32]
         L.mk_plan_trace.argtypes = [vp, vp, vp, sz, P(ctypes.c_double)]
-        L.mk_plan_debug_raise_wait.argtypes = [vp, i32, i32]
+        L.mk_plan_debug_raise_wait.argtypes = [vp, i32, i32, i32]
         L.mk_plan_poison_workspace.argtypes = [vp, vp]
         L.mk_stream_probe.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp]
         L.mk_run_noalloc.argtypes = [vp, P(Weights), vp, vp, vp, vp, vp]
@@ -250,6 +266,25 @@ class Plan:
         _check(lib().mk_graph_plan(OA, len(ops), EA, len(edges), num_cus, ctypes.byref(h)))
         return cls(h.value)
 
+    @classmethod
+    def pairs(cls, ops, pubs, edges, num_cus):
+        """mk_pair_plan.  ops: [(opcode, grid)], pubs: [(op, map, div, sel)],
+        edges: [(pub, cons, strategy, map, div)]; short tuples are padded (map
+        and sel with -1, div with 1)."""
+        pad = lambda v, f: tuple(v) + (f,) * (3 - len(v))
+        OA = (GraphOp * max(1, len(ops)))()
+        for i, (opcode, grid) in enumerate(ops):
+            OA[i] = GraphOp(opcode, 0, 0, (i32 * 3)(*pad(grid, 1)))
+        PA = (PairPub * max(1, len(pubs)))()
+        for i, (op, mp, dv, sl) in enumerate(pubs):
+            PA[i] = PairPub(op, (i32 * 3)(*pad(mp, -1)), (i32 * 3)(*pad(dv, 1)), (i32 * 3)(*pad(sl, -1)))
+        EA = (PairEdge * max(1, len(edges)))()
+        for i, (pb, c, st, mp, dv) in enumerate(edges):
+            EA[i] = PairEdge(pb, c, st, (i32 * 3)(*pad(mp, -1)), (i32 * 3)(*pad(dv, 1)))
+        h = vp()
+        _check(lib().mk_pair_plan(OA, len(ops), PA, len(pubs), EA, len(edges), num_cus, ctypes.byref(h)))
+        return cls(h.value)
+
     def export(self):
         v = PlanView()
         _check(lib().mk_plan_export(self._h, ctypes.byref(v)))
@@ -262,7 +297,9 @@ class Plan:
                     op_table=_arr(v.op_table, v.num_ops * 8, np.int32).reshape(v.num_ops, 8),
                     edge_kept=_arr(v.edge_kept, v.num_edges, np.uint8),
                     tile_opts=dict(zip(TILE_OPTS, list(v.tile_opts))),
-                    op_slots=_arr(v.op_slots, v.num_ops * 16, np.int32).reshape(v.num_ops, 16))
+                    op_slots=_arr(v.op_slots, v.num_ops * 16, np.int32).reshape(v.num_ops, 16),
+                    task_trigger2=_arr(v.task_trigger2, T, np.int32), task_wait2=_arr(v.task_wait2, T, np.int32),
+                    pairing=v.pairing, attn_order=v.attn_order)
 
     def run(self, weights, kv_cache, tokens, stream=None, layerwise=False):
         w = weights.struct if isinstance(weights, (DeviceWeights, GlmDeviceWeights)) else weights
@@ -293,9 +330,10 @@ class Plan:
         _check(lib().mk_plan_poison_workspace(self._h, vp(stream.cuda_stream if stream is not None
                                                             else current_stream())))
 
-    def debug_raise_wait(self, event, delta):
-        """mk_plan_debug_raise_wait (tests of the watchdog)."""
-        _check(lib().mk_plan_debug_raise_wait(self._h, int(event), int(delta)))
+    def debug_raise_wait(self, event, delta, slot=0):
+        """mk_plan_debug_raise_wait (tests of the watchdog); slot 0 every wait on
+        the event, 1 first waits only, 2 second waits only."""
+        _check(lib().mk_plan_debug_raise_wait(self._h, int(event), int(delta), int(slot)))
 
     def set_kv_len(self, kv_len, stream=None):
         """mk_plan_set_kv_len: the next step's sequence lengths, without replanning."""

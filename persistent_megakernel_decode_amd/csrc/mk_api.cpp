@@ -59,6 +59,7 @@ mk_status hip_fail(hipError_t e, const char* what) {
 
 struct mk_plan {
   bool graph_only = false;
+  int pairing = 0, attn_order = 0;  // planner choices of mk_plan_opts
   // identity of the plan's host state (queue words, RoPE table): uid is unique
   // per plan, version changes whenever that state is patched
   uint64_t uid = 0, version = 0;
@@ -266,6 +267,10 @@ static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_
     return st;
   }
   p->opts.num_cus = ncu;
+  if (opts && (opts->pairing || opts->attn_order)) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "pairing and attn_order apply to the Llama family only");
+  }
   mk::GlmShape g{H, QL, KL, RD, nh, hd, d.n_idx_heads, d.idx_head_dim, d.n_gate};
   std::vector<mk::GraphEdge> edges;
   std::string err = mk::glm_graph(g, M, &p->ops, &edges);
@@ -369,7 +374,15 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
       delete p;
       return fail(MK_E_INVALID, "lw_streams must be 0..3");
     }
+    if (opts->pairing < 0 || opts->pairing > 1 || opts->attn_order < -1 || opts->attn_order > 1) {
+      delete p;
+      return fail(MK_E_INVALID, "pairing must be 0 or 1 and attn_order -1, 0 or 1");
+    }
+    p->pairing = opts->pairing;
   }
+  // longest-first attention by default where sequences differ in length
+  const int ao = opts ? opts->attn_order : 0;
+  p->attn_order = ao == 0 ? (batch > 1 ? 1 : 0) : (ao > 0 ? 1 : 0);
   if (o.num_cus <= 0) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
@@ -417,7 +430,15 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   p->opts = o;
   std::vector<mk::GraphEdge> edges;
   std::string err = mk::model_graph(ms, batch, kl, o, &p->ops, &edges);
-  if (err.empty()) err = mk::plan_graph(p->ops, edges, o.num_cus, &p->kv_len, &p->P);
+  if (err.empty() && p->pairing) {
+    std::vector<mk::PairPub> pubs;
+    std::vector<mk::PairEdge> pedges;
+    mk::model_pairs(p->ops, &pubs, &pedges);
+    err = mk::plan_pairs(p->ops, pubs, pedges, o.num_cus, &p->kv_len, &p->P);
+  } else if (err.empty()) {
+    err = mk::plan_graph(p->ops, edges, o.num_cus, &p->kv_len, &p->P);
+  }
+  if (err.empty() && p->attn_order) mk::balance_attention(p->ops, p->kv_len, o.attn_splits, &p->P);
   if (!err.empty()) {
     delete p;
     return fail(MK_E_UNSUPPORTED, "planner: " + err);
@@ -516,6 +537,54 @@ mk_status mk_graph_plan(const mk_graph_op* ops, int32_t n_ops, const mk_graph_ed
     ge.push_back(e);
   }
   std::string err = mk::plan_graph(p->ops, ge, num_cus, nullptr, &p->P);
+  if (!err.empty()) {
+    delete p;
+    return fail(MK_E_INVALID, "planner: " + err);
+  }
+  finish_plan_common(p);
+  p->num_cus = num_cus;
+  *out = p;
+  return MK_OK;
+}
+
+mk_status mk_pair_plan(const mk_graph_op* ops, int32_t n_ops, const mk_pair_pub* pubs, int32_t n_pubs,
+                       const mk_pair_edge* edges, int32_t n_edges, int32_t num_cus, mk_plan** out) {
+  g_err.clear();
+  if (!out || (n_ops > 0 && !ops) || (n_pubs > 0 && !pubs) || (n_edges > 0 && !edges) || n_ops < 0 || n_pubs < 0 ||
+      n_edges < 0)
+    return fail(MK_E_INVALID, "null argument");
+  *out = nullptr;
+  auto* p = new_plan();
+  p->graph_only = true;
+  p->pairing = 1;
+  for (int i = 0; i < n_ops; ++i) {
+    mk::GraphOp op;
+    op.opcode = ops[i].opcode;
+    op.spec = ops[i].spec;
+    op.layer = ops[i].layer;
+    op.grid = {{ops[i].grid[0], ops[i].grid[1], ops[i].grid[2]}};
+    p->ops.push_back(op);
+  }
+  std::vector<mk::PairPub> pp(n_pubs);
+  for (int i = 0; i < n_pubs; ++i) {
+    pp[i].op = pubs[i].op;
+    for (int r = 0; r < 3; ++r) {
+      pp[i].map[r] = pubs[i].map[r];
+      pp[i].div[r] = pubs[i].div[r];
+      pp[i].sel[r] = pubs[i].sel[r];
+    }
+  }
+  std::vector<mk::PairEdge> pe(n_edges);
+  for (int i = 0; i < n_edges; ++i) {
+    pe[i].pub = edges[i].pub;
+    pe[i].cons = edges[i].cons;
+    pe[i].strategy = edges[i].strategy;
+    for (int r = 0; r < 3; ++r) {
+      pe[i].map[r] = edges[i].map[r];
+      pe[i].div[r] = edges[i].div[r];
+    }
+  }
+  std::string err = mk::plan_pairs(p->ops, pp, pe, num_cus, nullptr, &p->P);
   if (!err.empty()) {
     delete p;
     return fail(MK_E_INVALID, "planner: " + err);
@@ -867,6 +936,10 @@ mk_status mk_plan_export(const mk_plan* p, mk_plan_view* v) {
     if (!p->graph_only) fill_rows(p, Src{}, vals.data(), p->op_slots.data());
   }
   v->op_slots = p->op_slots.data();
+  v->task_trigger2 = p->P.task_trigger2.data();
+  v->task_wait2 = p->P.task_wait2.data();
+  v->pairing = p->pairing;
+  v->attn_order = p->attn_order;
   return MK_OK;
 }
 
@@ -1364,14 +1437,17 @@ mk_status mk_plan_poison_workspace(mk_plan* p, void* stream) {
   return MK_OK;
 }
 
-mk_status mk_plan_debug_raise_wait(mk_plan* p, int32_t event, int32_t delta) {
+mk_status mk_plan_debug_raise_wait(mk_plan* p, int32_t event, int32_t delta, int32_t slot) {
   g_err.clear();
   if (!p) return fail(MK_E_INVALID, "null plan");
   if (p->graph_only) return fail(MK_E_STATE, "graph-only plans cannot run");
   if (event < 0 || event >= p->P.num_events) return fail(MK_E_INVALID, "event out of range");
+  if (slot < 0 || slot > 2) return fail(MK_E_INVALID, "slot must be 0, 1 or 2");
   for (size_t t = 0; t * 32 < p->P.queue.size(); ++t) {
     int32_t* w = &p->P.queue[t * 32];
-    if (w[mkd::WOpcode] != mkd::OpNoop && w[mkd::WWaitCnt] && w[mkd::WWaitEv] == event) w[mkd::WWaitTgt] += delta;
+    if (w[mkd::WOpcode] == mkd::OpNoop) continue;
+    if (slot != 2 && w[mkd::WWaitCnt] >= 1 && w[mkd::WWaitEv] == event) w[mkd::WWaitTgt] += delta;
+    if (slot != 1 && w[mkd::WWaitCnt] == 2 && w[mkd::WWait2Ev] == event) w[mkd::WWait2Tgt] += delta;
   }
   p->version += 1;
   if (p->uploaded)

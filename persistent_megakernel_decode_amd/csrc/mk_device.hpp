@@ -27,6 +27,9 @@ namespace mkd {
 enum : int {
   WOpcode = 0, WSpec = 1, WOpRow = 2, WWaitCnt = 3, WWaitEv = 4, WWaitTgt = 5, WSigCnt = 6, WSigEv = 7,
   WSigInc = 8, WTask = 9, WLayer = 10, WGx = 11, WGy = 12, WGz = 13, WPay = 14,
+  // second wait (event, target) and second signal (event, increment): word 3 /
+  // word 6 count the waits / signals, 0..2
+  WWait2Ev = 24, WWait2Tgt = 25, WSig2Ev = 26, WSig2Inc = 27,
   // LDS copy only (the queue holds zero there): sequence number of the
   // instruction's first ring page, written by the controller as it stages it
   WFirstPage = 31

@@ -193,11 +193,12 @@ __device__ void stage(const KArgs& a, LDS LT* L, int j, int& pages) {
 // ---------------------------------------------------------------------------
 template <class LT>
 __device__ void controller(const KArgs& a, LDS LT* L) {
-  // the last event this wave saw at or past a target, and the count it read:
-  // counters only grow within a run, so a later instruction waiting on the same
-  // event for a target within that count needs neither a poll nor an acquire
-  int seen_ev = -1;
-  unsigned seen_val = 0;
+  // per wait slot, the last event this wave saw at or past a target and the
+  // count it read: counters only grow within a run, so a later instruction
+  // waiting on the same event for a target within that count needs neither a
+  // poll nor an acquire
+  int seen_ev[2] = {-1, -1};
+  unsigned seen_val[2] = {0u, 0u};
   int pages = 0;
   stage(a, L, 0, pages);
   if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, 1);
@@ -220,22 +221,29 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
     if (i + 2 > kMeta && !wait_lds_ge(a, L, &L->c.done_seq, i + 2 - kMeta, ErrDrain, i)) return;
     stage(a, L, i + 1, pages);
     if (lane_id() == 0) lds_store_rel(&L->c.meta_seq, i + 2);
-    if (m.w(WWaitCnt) && !(m.w(WWaitEv) == seen_ev && (int)(seen_val - a.epoch * (unsigned)m.w(WWaitTgt)) >= 0)) {
-      const unsigned tgt = a.epoch * (unsigned)m.w(WWaitTgt);
+    // one or two waits (a join waits on both of its producers' events)
+    const int nwait = m.w(WWaitCnt);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k >= nwait) break;
+      const int ev = m.w(k ? WWait2Ev : WWaitEv);
+      const unsigned tgt = a.epoch * (unsigned)m.w(k ? WWait2Tgt : WWaitTgt);
+      if ((ev == seen_ev[0] && (int)(seen_val[0] - tgt) >= 0) || (ev == seen_ev[1] && (int)(seen_val[1] - tgt) >= 0))
+        continue;
       // lane l reads sub-counters l, l + 64, ... (below kCtrSub); the event's
       // count is their sum
       const int lane = lane_id();
-      const int k = lane < kCtrSub ? lane : 0;
-      unsigned* ctr = a.counters + ctr_word(m.w(WWaitEv), k, a.num_events);
+      const int kk = lane < kCtrSub ? lane : 0;
+      unsigned* ctr = a.counters + ctr_word(ev, kk, a.num_events);
       const size_t step = ctr_word(0, 64, a.num_events);  // words from sub-counter k to k + 64
       auto count = [&]() {
         unsigned x[kCtrPer];
 #pragma unroll
         for (int j = 0; j < kCtrPer; ++j) x[j] = __hip_atomic_load(ctr + j * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        unsigned s = 0;
+        unsigned sum = 0;
 #pragma unroll
-        for (int j = 0; j < kCtrPer; ++j) s += x[j];
-        return ctr_sum_u32(lane < kCtrSub ? s : 0u);
+        for (int j = 0; j < kCtrPer; ++j) sum += x[j];
+        return ctr_sum_u32(lane < kCtrSub ? sum : 0u);
       };
       unsigned v = count();
       if ((int)(v - tgt) < 0) {
@@ -249,7 +257,7 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
               return;
             }
             if (now_ticks() - t0 > a.timeout_ticks) {
-              record_error(a, L, ErrEvent, i, m.w(WWaitEv), v, tgt);
+              record_error(a, L, ErrEvent, i, ev, v, tgt);
               return;
             }
           }
@@ -257,8 +265,8 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
       }
       // no agent-scope acquire (an L2 invalidate) here: see CohT for why the
       // reads that follow need none
-      seen_ev = m.w(WWaitEv);
-      seen_val = v;
+      seen_ev[k] = ev;
+      seen_val[k] = v;
     }
     if (a.trace && lane_id() == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 0] = now_ticks();
     if (lane_id() == 0) lds_store_rel(&L->c.ready_seq, i + 1);
@@ -312,17 +320,23 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
     if (a.trace && lane == 0) a.trace[((size_t)blockIdx.x * a.max_len + i) * kTraceWords + 2] = now_ticks();
     if (m.w(WSigCnt)) {
       pending += (unsigned)m.w(WSigInc);
-      // the next instruction was staged before this one was published
+      // the next instruction was staged before this one was published; runs
+      // are merged only between single-signal instructions
       const Meta nx = load_meta(L->meta[(i + 1) % kMeta]);
-      const bool same_next = nx.w(WOpcode) != OpNoop && nx.w(WSigCnt) && nx.w(WSigEv) == m.w(WSigEv);
+      const bool same_next = m.w(WSigCnt) == 1 && nx.w(WOpcode) != OpNoop && nx.w(WSigCnt) == 1 &&
+                             nx.w(WSigEv) == m.w(WSigEv);
       if (!same_next) {
         // every output of the run was stored agent-coherent, by this wave or by
         // the compute waves, which waited for their stores before arriving:
         // wait for this wave's stores, then count
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (lane == 0)
+        if (lane == 0) {
           __hip_atomic_fetch_add(a.counters + ctr_word(m.w(WSigEv), blockIdx.x % kCtrSub, a.num_events), pending,
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (m.w(WSigCnt) == 2)
+            __hip_atomic_fetch_add(a.counters + ctr_word(m.w(WSig2Ev), blockIdx.x % kCtrSub, a.num_events),
+                                   (unsigned)m.w(WSig2Inc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         pending = 0;
       }
     }

@@ -98,6 +98,63 @@ void payload(const GraphOp& op, int x, int y, int z, const std::vector<int32_t>*
   }
 }
 
+// Place task t in queue t % num_cus at slot t / num_cus and write its words
+// (MegaRTP article, section 4 "KernelPlan"); fills the op table too.
+void encode(const std::vector<GraphOp>& ops, const std::vector<int32_t>* kv_len, Plan* out) {
+  Plan& P = *out;
+  const int num_cus = P.num_cus;
+  P.max_len = std::max(1, ceil_div(P.num_tasks, num_cus));
+  P.queue.assign((size_t)num_cus * P.max_len * kWords, 0);
+  for (int t = 0; t < P.num_tasks; ++t) {
+    const auto& tk = P.tasks[t];
+    const GraphOp& op = ops[tk[0]];
+    int32_t* w = &P.queue[((size_t)(t % num_cus) * P.max_len + t / num_cus) * kWords];
+    w[kWOpcode] = op.opcode;
+    w[kWSpec] = op.spec;
+    w[kWOpRow] = tk[0];
+    if (P.task_wait[t] >= 0) {
+      w[kWWaitCnt] = 1;
+      w[kWWaitEv] = P.task_wait[t];
+      w[kWWaitTgt] = (int32_t)P.event_target[P.task_wait[t]];
+      if (P.task_wait2[t] >= 0) {
+        w[kWWaitCnt] = 2;
+        w[kWWait2Ev] = P.task_wait2[t];
+        w[kWWait2Tgt] = (int32_t)P.event_target[P.task_wait2[t]];
+      }
+    }
+    if (P.task_trigger[t] >= 0) {
+      w[kWSigCnt] = 1;
+      w[kWSigEv] = P.task_trigger[t];
+      w[kWSigInc] = 1;
+      if (!P.sig_pub.empty()) w[kWSigPub] = P.sig_pub[t][0];
+      if (P.task_trigger2[t] >= 0) {
+        w[kWSigCnt] = 2;
+        w[kWSig2Ev] = P.task_trigger2[t];
+        w[kWSig2Inc] = 1;
+        w[kWSig2Pub] = P.sig_pub[t][1];
+      }
+    }
+    w[kWTask] = t;
+    w[kWLayer] = op.layer;
+    w[kWGx] = tk[1];
+    w[kWGy] = tk[2];
+    w[kWGz] = tk[3];
+    payload(op, tk[1], tk[2], tk[3], kv_len, w + kWPay);
+  }
+  const int n_ops = (int)ops.size();
+  P.op_table.assign((size_t)n_ops * 8, 0);
+  for (int o = 0; o < n_ops; ++o) {
+    int32_t* r = &P.op_table[(size_t)o * 8];
+    r[0] = ops[o].opcode;
+    r[1] = ops[o].spec;
+    r[2] = ops[o].layer;
+    r[3] = ops[o].grid[0];
+    r[4] = ops[o].grid[1];
+    r[5] = ops[o].grid[2];
+    r[6] = ops[o].grid[0] * ops[o].grid[1] * ops[o].grid[2];
+  }
+}
+
 }  // namespace
 
 std::string plan_graph(const std::vector<GraphOp>& ops, const std::vector<GraphEdge>& edges, int num_cus,
@@ -387,45 +444,233 @@ std::string plan_graph(const std::vector<GraphOp>& ops, const std::vector<GraphE
   P.num_cus = num_cus;
   P.num_tasks = (int)P.tasks.size();
   P.num_events = (int)P.event_first.size();
-  P.max_len = std::max(1, ceil_div(P.num_tasks, num_cus));
-  P.queue.assign((size_t)num_cus * P.max_len * kWords, 0);
-  for (int t = 0; t < P.num_tasks; ++t) {
-    const auto& tk = P.tasks[t];
-    const GraphOp& op = ops[tk[0]];
-    int32_t* w = &P.queue[((size_t)(t % num_cus) * P.max_len + t / num_cus) * kWords];
-    w[kWOpcode] = op.opcode;
-    w[kWSpec] = op.spec;
-    w[kWOpRow] = tk[0];
-    if (P.task_wait[t] >= 0) {
-      w[kWWaitCnt] = 1;
-      w[kWWaitEv] = P.task_wait[t];
-      w[kWWaitTgt] = (int32_t)P.event_target[P.task_wait[t]];
-    }
-    if (P.task_trigger[t] >= 0) {
-      w[kWSigCnt] = 1;
-      w[kWSigEv] = P.task_trigger[t];
-      w[kWSigInc] = 1;
-    }
-    w[kWTask] = t;
-    w[kWLayer] = op.layer;
-    w[kWGx] = tk[1];
-    w[kWGy] = tk[2];
-    w[kWGz] = tk[3];
-    payload(op, tk[1], tk[2], tk[3], kv_len, w + kWPay);
-  }
-  P.op_table.assign((size_t)n_ops * 8, 0);
-  for (int o = 0; o < n_ops; ++o) {
-    int32_t* r = &P.op_table[(size_t)o * 8];
-    r[0] = ops[o].opcode;
-    r[1] = ops[o].spec;
-    r[2] = ops[o].layer;
-    r[3] = ops[o].grid[0];
-    r[4] = ops[o].grid[1];
-    r[5] = ops[o].grid[2];
-    r[6] = ops[o].grid[0] * ops[o].grid[1] * ops[o].grid[2];
-  }
+  P.task_wait2.assign(P.num_tasks, -1);
+  P.task_trigger2.assign(P.num_tasks, -1);
+  encode(ops, kv_len, &P);
   P.edge_kept = kept;
   return "";
+}
+
+std::string plan_pairs(const std::vector<GraphOp>& ops, const std::vector<PairPub>& pubs,
+                       const std::vector<PairEdge>& edges, int num_cus, const std::vector<int32_t>* kv_len, Plan* out) {
+  const int n_ops = (int)ops.size(), n_pubs = (int)pubs.size();
+  if (num_cus <= 0) return "num_cus must be positive";
+  for (const auto& op : ops)
+    for (int a = 0; a < 3; ++a)
+      if (op.grid[a] < 1) return "grid extents must be >= 1";
+  for (const auto& p : pubs) {
+    if (p.op < 0 || p.op >= n_ops) return "publication of an unknown op";
+    for (int r = 0; r < 3; ++r)
+      if (p.map[r] < -1 || p.map[r] >= 3 || p.div[r] < 1 || p.sel[r] < -1 || (p.sel[r] >= 0 && p.sel[r] >= ops[p.op].grid[r]))
+        return "publication map/div/sel out of range";
+  }
+  for (const auto& e : edges) {
+    if (e.pub < 0 || e.pub >= n_pubs || e.cons >= n_ops || !(pubs[e.pub].op < e.cons))
+      return "an edge must read a publication of an earlier op";
+    if (e.strategy < kPairWhole || e.strategy > kPairTileReduce) return "unknown pairing strategy";
+    for (int r = 0; r < 3; ++r)
+      if (e.map[r] < -1 || e.map[r] >= 3 || e.div[r] < 1) return "edge map/div out of range";
+  }
+  auto nregions = [&](const PairPub& p) {
+    std::array<int, 3> n{{1, 1, 1}};
+    for (int r = 0; r < 3; ++r)
+      if (p.map[r] >= 0) n[r] = ceil_div(ops[p.op].grid[p.map[r]], p.div[r]);
+    return n;
+  };
+  auto region = [](const std::array<int, 3>& c, const std::array<int, 3>& map, const std::array<int, 3>& div) {
+    std::array<int, 3> r{{0, 0, 0}};
+    for (int d = 0; d < 3; ++d)
+      if (map[d] >= 0) r[d] = c[map[d]] / div[d];
+    return r;
+  };
+  auto publishes = [](const PairPub& p, const std::array<int, 3>& c) {
+    for (int a = 0; a < 3; ++a)
+      if (p.sel[a] >= 0 && c[a] != p.sel[a]) return false;
+    return true;
+  };
+  // publishing tiles per (publication, region)
+  std::vector<std::map<std::array<int, 3>, int>> count(n_pubs);
+  for (int k = 0; k < n_pubs; ++k) {
+    const auto& g = ops[pubs[k].op].grid;
+    for (int x = 0; x < g[0]; ++x)
+      for (int y = 0; y < g[1]; ++y)
+        for (int z = 0; z < g[2]; ++z) {
+          std::array<int, 3> c{{x, y, z}};
+          if (publishes(pubs[k], c)) ++count[k][region(c, pubs[k].map, pubs[k].div)];
+        }
+  }
+  Plan& P = *out;
+  P = Plan();
+  for (int o = 0; o < n_ops; ++o)
+    for (int x = 0; x < ops[o].grid[0]; ++x)
+      for (int y = 0; y < ops[o].grid[1]; ++y)
+        for (int z = 0; z < ops[o].grid[2]; ++z) P.tasks.push_back({{o, x, y, z}});
+  const int T = (int)P.tasks.size();
+  std::vector<std::vector<int>> in_edges(n_ops);
+  for (int i = 0; i < (int)edges.size(); ++i) in_edges[edges[i].cons].push_back(i);
+  std::map<std::pair<int, std::array<int, 3>>, int> ev_of;
+  std::map<int, int> reduce_n;
+  std::vector<std::vector<int>> ev_tasks;
+  P.task_wait.assign(T, -1);
+  P.task_wait2.assign(T, -1);
+  for (int t = 0; t < T; ++t) {
+    const auto& tk = P.tasks[t];
+    const std::array<int, 3> c{{tk[1], tk[2], tk[3]}};
+    int w[3], nw = 0;
+    for (int i : in_edges[tk[0]]) {
+      const PairEdge& e = edges[i];
+      const PairPub& p = pubs[e.pub];
+      const auto r = region(c, e.map, e.div);
+      const auto nr = nregions(p);
+      for (int d = 0; d < 3; ++d)
+        if (r[d] >= nr[d]) return "edge " + std::to_string(i) + ": a consumer tile reads a region outside the publication";
+      auto it = count[e.pub].find(r);
+      const int n = it == count[e.pub].end() ? 0 : it->second;
+      if (n == 0) return "edge " + std::to_string(i) + ": a region has no publishing tile";
+      if (e.strategy == kPairWhole && (nr != std::array<int, 3>{{1, 1, 1}} || p.sel != std::array<int, 3>{{-1, -1, -1}}))
+        return "edge " + std::to_string(i) + ": 'whole' needs one region that every producer tile publishes";
+      if (e.strategy == kPairTile && n != 1) return "edge " + std::to_string(i) + ": 'tile' needs one producer tile per region";
+      if (e.strategy == kPairTileReduce && reduce_n.emplace(i, n).first->second != n)
+        return "edge " + std::to_string(i) + ": 'tile_reduce' regions must have equal partial counts";
+      const auto key = std::make_pair(e.pub, r);
+      auto ev = ev_of.find(key);
+      if (ev == ev_of.end()) {
+        ev = ev_of.emplace(key, (int)P.event_target.size()).first;
+        P.event_target.push_back((uint32_t)n);
+        ev_tasks.emplace_back();
+      }
+      bool dup = false;
+      for (int j = 0; j < nw; ++j) dup |= w[j] == ev->second;
+      if (dup) continue;
+      if (nw == 2) return "a task waits on more than two events";
+      w[nw++] = ev->second;
+      ev_tasks[ev->second].push_back(t);
+    }
+    if (nw > 0) P.task_wait[t] = w[0];
+    if (nw > 1) P.task_wait2[t] = w[1];
+  }
+  std::vector<std::vector<int>> pubs_of(n_ops);
+  for (int k = 0; k < n_pubs; ++k) pubs_of[pubs[k].op].push_back(k);
+  P.task_trigger.assign(T, -1);
+  P.task_trigger2.assign(T, -1);
+  P.sig_pub.assign(T, {{0, 0}});
+  for (int t = 0; t < T; ++t) {
+    const auto& tk = P.tasks[t];
+    const std::array<int, 3> c{{tk[1], tk[2], tk[3]}};
+    int ns = 0;
+    for (int k : pubs_of[tk[0]]) {
+      if (!publishes(pubs[k], c)) continue;
+      auto ev = ev_of.find(std::make_pair(k, region(c, pubs[k].map, pubs[k].div)));
+      if (ev == ev_of.end()) continue;
+      if (ns == 2) return "a task signals more than two events";
+      (ns == 0 ? P.task_trigger[t] : P.task_trigger2[t]) = ev->second;
+      P.sig_pub[t][ns++] = k;
+    }
+  }
+  P.num_cus = num_cus;
+  P.num_tasks = T;
+  P.num_events = (int)P.event_target.size();
+  for (const auto& ts : ev_tasks) {
+    P.event_first.push_back(ts.front());
+    P.event_last.push_back(ts.back() + 1);
+  }
+  encode(ops, kv_len, &P);
+  P.edge_kept.assign(edges.size(), 1);
+  return "";
+}
+
+void model_pairs(const std::vector<GraphOp>& ops, std::vector<PairPub>* pubs_out, std::vector<PairEdge>* edges_out) {
+  auto& pubs = *pubs_out;
+  auto& edges = *edges_out;
+  pubs.clear();
+  edges.clear();
+  auto pub = [&](int op, std::array<int, 3> map) {
+    PairPub p;
+    p.op = op;
+    p.map = map;
+    pubs.push_back(p);
+    return (int)pubs.size() - 1;
+  };
+  auto edge = [&](int p, int c, int strategy, std::array<int, 3> map) {
+    PairEdge e;
+    e.pub = p;
+    e.cons = c;
+    e.strategy = strategy;
+    e.map = map;
+    edges.push_back(e);
+  };
+  const std::array<int, 3> none{{-1, -1, -1}};
+  const int L = ((int)ops.size() - 2) / 6;
+  int prev_d = -1;
+  for (int l = 0; l < L; ++l) {
+    const int q = 6 * l, a = q + 1, c = q + 2, o = q + 3, g = q + 4, d = q + 5;
+    const int pq = pub(q, {{0, -1, -1}}), pa = pub(a, {{0, 1, -1}}), pc = pub(c, none), po = pub(o, none),
+              pg = pub(g, none);
+    if (prev_d >= 0) edge(prev_d, q, kPairWhole, none);
+    edge(pq, a, kPairTileCover, {{1, -1, -1}});
+    edge(pa, c, kPairTileReduce, {{0, 1, -1}});
+    edge(pc, o, kPairWhole, none);
+    if (prev_d >= 0) edge(prev_d, o, kPairWhole, none);
+    edge(po, g, kPairWhole, none);
+    edge(pg, d, kPairWhole, none);
+    edge(po, d, kPairWhole, none);
+    prev_d = pub(d, none);
+  }
+  const int lm = 6 * L, am = lm + 1;
+  edge(prev_d, lm, kPairWhole, none);
+  edge(pub(lm, none), am, kPairWhole, none);
+}
+
+void balance_attention(const std::vector<GraphOp>& ops, const std::vector<int32_t>& kv_len, int splits, Plan* out) {
+  Plan& P = *out;
+  const int C = P.num_cus, T = P.num_tasks;
+  auto rows = [&](int t) {
+    int lo, hi;
+    split_range(kv_len[P.tasks[t][1]], splits, P.tasks[t][3], &lo, &hi);
+    return hi - lo;
+  };
+  std::map<int, std::vector<long>> load;
+  for (int t = 0; t < T;) {
+    const int o = P.tasks[t][0];
+    if (ops[o].opcode != kAttn) {
+      ++t;
+      continue;
+    }
+    int e = t + 1;
+    while (e < T && P.tasks[e][0] == o && P.task_wait[e] == P.task_wait[t] && P.task_wait2[e] == P.task_wait2[t]) ++e;
+    auto& ld = load[o];
+    if (ld.empty()) ld.assign(C, 0);
+    std::vector<int> order;
+    for (int u = t; u < e; ++u) order.push_back(u);
+    std::stable_sort(order.begin(), order.end(), [&](int u, int v) { return rows(u) > rows(v); });
+    std::vector<int> free_pos(order.size()), from(e - t);
+    for (int k = 0; k < e - t; ++k) free_pos[k] = t + k;
+    for (int u : order) {
+      size_t best = 0;
+      for (size_t k = 1; k < free_pos.size(); ++k) {
+        const int v = free_pos[k], b = free_pos[best];
+        if (ld[v % C] < ld[b % C] || (ld[v % C] == ld[b % C] && v < b)) best = k;
+      }
+      const int pos = free_pos[best];
+      free_pos.erase(free_pos.begin() + best);
+      from[pos - t] = u;
+      ld[pos % C] += rows(u);
+    }
+    std::vector<std::array<int, 4>> tk(P.tasks.begin() + t, P.tasks.begin() + e);
+    std::vector<int32_t> tr(P.task_trigger.begin() + t, P.task_trigger.begin() + e),
+        tr2(P.task_trigger2.begin() + t, P.task_trigger2.begin() + e);
+    std::vector<std::array<int32_t, 2>> sp;
+    if (!P.sig_pub.empty()) sp.assign(P.sig_pub.begin() + t, P.sig_pub.begin() + e);
+    for (int pos = t; pos < e; ++pos) {
+      const int k = from[pos - t] - t;
+      P.tasks[pos] = tk[k];
+      P.task_trigger[pos] = tr[k];
+      P.task_trigger2[pos] = tr2[k];
+      if (!sp.empty()) P.sig_pub[pos] = sp[k];
+    }
+    t = e;
+  }
+  encode(ops, &kv_len, &P);
 }
 
 void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, ModelOpts* o) {

@@ -23,7 +23,10 @@ constexpr int kMaxDims = 4;
 enum : int {
   kWOpcode = 0, kWSpec = 1, kWOpRow = 2, kWWaitCnt = 3, kWWaitEv = 4, kWWaitTgt = 5,
   kWSigCnt = 6, kWSigEv = 7, kWSigInc = 8, kWTask = 9, kWLayer = 10, kWGx = 11, kWGy = 12, kWGz = 13,
-  kWPay = 14, kNPay = 10
+  kWPay = 14, kNPay = 10,
+  // second wait and second signal, and the publication of each signal
+  // (pairing plans); word 31 stays free
+  kWWait2Ev = 24, kWWait2Tgt = 25, kWSig2Ev = 26, kWSig2Inc = 27, kWSigPub = 28, kWSig2Pub = 29
 };
 
 // opcodes of the Llama-family decode step
@@ -53,7 +56,9 @@ struct Plan {
   std::vector<int32_t> queue;  // [num_cus][max_len][32]
   std::vector<uint32_t> event_target;
   std::vector<int32_t> event_first, event_last;
-  std::vector<int32_t> task_trigger, task_wait;
+  std::vector<int32_t> task_trigger, task_wait;    // first signal / wait per task, or -1
+  std::vector<int32_t> task_trigger2, task_wait2;  // second signal / wait per task, or -1
+  std::vector<std::array<int32_t, 2>> sig_pub;     // publication of each signal (pairing plans)
   std::vector<std::array<int, 4>> tasks;  // (op, x, y, z)
   std::vector<int32_t> op_table;          // [num_ops][8]
   std::vector<uint8_t> edge_kept;
@@ -83,6 +88,36 @@ struct GlmShape {
 };
 // Operator DAG of the GLM-style pre-attention path for M token rows.
 std::string glm_graph(const GlmShape& g, int M, std::vector<GraphOp>* ops, std::vector<GraphEdge>* edges);
+
+// Pairing strategies (MegaRTP article, section 4, "TaskGraph").  An op
+// publishes outputs; an edge reads one publication of an earlier op.  Region
+// dim r of producer tile c is c[map[r]] / div[r] (0 where map[r] is -1); tile c
+// publishes only if c[a] == sel[a] wherever sel[a] >= 0.  Each region some
+// consumer reads is one event whose threshold is its number of publishing
+// tiles.  whole: one region published by every tile; tile: one publishing tile
+// per region; tile_cover: several disjoint tiles; tile_reduce: several partials,
+// the same count in every region the edge reads.  At most two waits and two
+// signals per instruction.  Tasks op by op in row-major grid order; events
+// numbered in the order consumers first wait on them; round-robin placement.
+enum : int { kPairWhole = 0, kPairTile = 1, kPairTileCover = 2, kPairTileReduce = 3 };
+struct PairPub {
+  int op = 0;
+  std::array<int, 3> map{{-1, -1, -1}}, div{{1, 1, 1}}, sel{{-1, -1, -1}};
+};
+struct PairEdge {
+  int pub = 0, cons = 0, strategy = kPairWhole;
+  std::array<int, 3> map{{-1, -1, -1}}, div{{1, 1, 1}};
+};
+std::string plan_pairs(const std::vector<GraphOp>& ops, const std::vector<PairPub>& pubs,
+                       const std::vector<PairEdge>& edges, int num_cus, const std::vector<int32_t>* kv_len, Plan* out);
+
+// Publications and pairing edges of the Llama-family decode step over the ops
+// model_graph lists (residual inputs kept as second waits of O and down).
+void model_pairs(const std::vector<GraphOp>& ops, std::vector<PairPub>* pubs, std::vector<PairEdge>* edges);
+
+// Longest-first placement of attention tasks within each run of consecutive
+// attention tasks that wait on the same events, then re-encode the queues.
+void balance_attention(const std::vector<GraphOp>& ops, const std::vector<int32_t>& kv_len, int splits, Plan* P);
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 

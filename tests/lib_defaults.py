@@ -31,3 +31,12 @@ def documented_defaults(cfg, batch, kv_len, num_cus, **given):
             S += 1
     o["attn_splits"] = S
     return o
+
+
+def documented_choices(batch, **given):
+    """Planner choices of a Llama-family plan by the rules mk.h states: the
+    gcd/lcm events (pairing 0) and longest-first attention at batch > 1
+    (attn_order 0 resolves to 1 there, to 0 at batch 1; -1 is plan order),
+    in the reference planner's terms (attn_order 1 or 0)."""
+    ao = given.get("attn_order", 0)
+    return dict(pairing=int(given.get("pairing", 0)), attn_order=(1 if batch > 1 else 0) if ao == 0 else int(ao > 0))

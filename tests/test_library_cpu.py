@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from oracle import planner as P
-from tests.lib_defaults import documented_defaults
+from tests.lib_defaults import documented_choices, documented_defaults
 
 mk = pytest.importorskip("persistent_megakernel_decode_amd")
 
@@ -38,6 +38,8 @@ def _compare(lib_plan, ref):
     assert ex["event_last"].tolist() == list(ref.event_last)
     assert ex["task_trigger"].tolist() == list(ref.trigger)
     assert ex["task_wait"].tolist() == list(ref.wait)
+    assert ex["task_trigger2"].tolist() == list(ref.trigger2)
+    assert ex["task_wait2"].tolist() == list(ref.wait2)
     assert ex["edge_kept"].astype(bool).tolist() == list(ref.kept)
     assert ex["op_table"].tolist() == P.op_table(ref)
     return ex
@@ -63,7 +65,7 @@ def test_cpp_planner_matches_reference(name, overrides, num_cus, opts):
     kv = synth.kv_lengths(cfg)
     cap = synth.kv_capacity(kv)
     o = documented_defaults(cfg, cfg["batch"], kv, num_cus, **opts)
-    ref = P.plan_model(cfg, cfg["batch"], kv, o)
+    ref = P.plan_model(cfg, cfg["batch"], kv, dict(o, **documented_choices(cfg["batch"])))
     plan = mk.Plan.build(cfg, cfg["batch"], kv, cap, **o)
     try:
         ex = _compare(plan, ref)
@@ -201,6 +203,15 @@ def test_plan_build_rejects_bad_arguments():
     with pytest.raises(mk.MKError) as e:
         mk.Plan.build(dict(g, rope_dim=40), len(pos), pos, cap, num_cus=8)
     assert e.value.status == mk.MK_E_UNSUPPORTED
+    # planner choices: out of range, or on the GLM path
+    for bad in (dict(pairing=2), dict(pairing=-1), dict(attn_order=2), dict(attn_order=-2)):
+        with pytest.raises(mk.MKError) as e:
+            mk.Plan.build(cfg, 1, [10], 100, num_cus=8, **bad)
+        assert e.value.status == mk.MK_E_INVALID, bad
+    for bad in (dict(pairing=1), dict(attn_order=1)):
+        with pytest.raises(mk.MKError) as e:
+            mk.Plan.build(g, len(pos), pos, cap, num_cus=8, **bad)
+        assert e.value.status == mk.MK_E_UNSUPPORTED, bad
     # a graph-only plan cannot run
     g = mk.Plan.graph([(1, (4,))], [], 4)
     w = mk.Weights()
@@ -221,18 +232,26 @@ def test_set_kv_len_patches_match_a_fresh_plan(name, num_cus, splits, shift):
     kv0 = synth.kv_lengths(cfg)
     kv1 = kv0 + shift
     cap = synth.kv_capacity(kv1)
-    plan = mk.Plan.build(cfg, cfg["batch"], kv0, cap, num_cus=num_cus, attn_splits=splits)
-    try:
-        o = plan.export()["tile_opts"]
-        ref1 = P.plan_model(cfg, cfg["batch"], kv1, o)
-        before = plan.export()["queue"].copy()
-        plan.set_kv_len(kv1)
-        after = plan.export()["queue"]
-        assert np.array_equal(after, np.asarray(ref1.queue, dtype=np.int32))
-        changed = np.nonzero((before != after).any(axis=2))
-        assert set(before[changed][:, 0]) <= {P.ATTN}
-    finally:
-        plan.free()
+    for order in (-1, 0):
+        plan = mk.Plan.build(cfg, cfg["batch"], kv0, cap, num_cus=num_cus, attn_splits=splits, attn_order=order)
+        try:
+            ex = plan.export()
+            o = ex["tile_opts"]
+            # the reference: the plan for kv0 (its placement) with kv1's payloads
+            ref1 = P.plan_model(cfg, cfg["batch"], kv0, dict(o, attn_order=ex["attn_order"]))
+            ref1.ops = P.model_graph(cfg, cfg["batch"], kv1, o)[0]
+            P.encode(ref1)
+            if ex["attn_order"] == 0:  # plan order does not depend on the lengths
+                fresh = P.plan_model(cfg, cfg["batch"], kv1, o)
+                assert np.array_equal(fresh.queue, ref1.queue)
+            before = ex["queue"].copy()
+            plan.set_kv_len(kv1)
+            after = plan.export()["queue"]
+            assert np.array_equal(after, np.asarray(ref1.queue, dtype=np.int32))
+            changed = np.nonzero((before != after).any(axis=2))
+            assert set(before[changed][:, 0]) <= {P.ATTN}
+        finally:
+            plan.free()
 
 
 def test_set_kv_len_rejections():
@@ -273,7 +292,7 @@ def test_set_kv_len_random_lengths_match_fresh_plans():
     cfg = synth.config("tiny", batch=5, kv_len=(0, 300), seed=21)
     kv0 = synth.kv_lengths(cfg)
     cap = 400
-    plan = mk.Plan.build(cfg, 5, kv0, cap, num_cus=29, attn_splits=6)
+    plan = mk.Plan.build(cfg, 5, kv0, cap, num_cus=29, attn_splits=6, attn_order=-1)
     try:
         for _ in range(6):
             kv = rng.integers(0, cap - 1, size=5).astype(np.int32)
@@ -371,3 +390,80 @@ def test_operand_table_layout():
         assert S.MK_SLOT_G_KV_CACHE in kinds[P.G_QANORM] and S.MK_SLOT_G_IDX_CACHE in kinds[P.G_IDXK]
     finally:
         plan.free()
+
+
+@pytest.mark.parametrize("name,overrides,num_cus,extra", [
+    ("tiny", {}, 37, dict(pairing=1)),
+    ("tiny", dict(batch=3, kv_len=(0, 200), seed=11), 37, dict(pairing=1, attn_order=1)),
+    ("tiny", dict(batch=6, kv_len=(1, 120), seed=15), 64, dict(attn_order=1)),
+    ("tiny", dict(batch=6, kv_len=(1, 120), seed=15), 64, dict(attn_order=-1)),
+    ("llama1b", {}, 256, dict(pairing=1)),
+    ("llama1b", {}, 256, dict(attn_order=1)),
+    ("llama1b_b16", {}, 256, dict(attn_order=1)),
+    ("llama1b_b16", {}, 256, dict(pairing=1, attn_order=1)),
+    ("qwen3_8b", dict(batch=4, kv_len=(100, 3000), seed=3), 256, dict(pairing=1, attn_order=1)),
+])
+def test_cpp_pairing_and_longest_first_match_reference(name, overrides, num_cus, extra):
+    """The pairing-strategy plan (two waits on O and down) and the
+    longest-first attention placement: bit-exact with the reference planner."""
+    cfg = synth.config(name, **overrides)
+    kv = synth.kv_lengths(cfg)
+    o = documented_defaults(cfg, cfg["batch"], kv, num_cus)
+    ref = P.plan_model(cfg, cfg["batch"], kv, dict(o, **documented_choices(cfg["batch"], **extra)))
+    plan = mk.Plan.build(cfg, cfg["batch"], kv, synth.kv_capacity(kv), **o, **extra)
+    try:
+        ex = _compare(plan, ref)
+        assert ex["pairing"] == extra.get("pairing", 0)
+        assert ex["attn_order"] == documented_choices(cfg["batch"], **extra)["attn_order"]
+        if extra.get("pairing"):
+            assert (ex["queue"][:, :, P.W_WAIT_CNT] == 2).any()
+    finally:
+        plan.free()
+
+
+def test_longest_first_lowers_the_attention_load_per_queue():
+    """Variable sequence lengths at batch 16: the largest per-queue attention
+    work (KV rows) of a layer drops with longest-first placement, the plan's
+    events and thresholds stay the same, and tasks move only within runs of
+    identical waits."""
+    cfg = synth.config("llama1b_b16")
+    kv = synth.kv_lengths(cfg)
+    o = documented_defaults(cfg, cfg["batch"], kv, 256)
+    base = P.plan_model(cfg, cfg["batch"], kv, o)
+    lf = P.plan_model(cfg, cfg["batch"], kv, dict(o, attn_order=1))
+    assert lf.event_target == base.event_target and lf.event_first == base.event_first
+    assert lf.wait == base.wait and lf.wait2 == base.wait2
+
+    def max_load(pl):
+        ld = np.zeros(pl.num_cus, dtype=np.int64)
+        for t, (op, x, y, z) in enumerate(pl.tasks):
+            if pl.ops[op].opcode == P.ATTN and pl.ops[op].layer == 0:
+                lo, hi = P.split_range(int(kv[x]), o["attn_splits"], z)
+                ld[t % pl.num_cus] += hi - lo
+        return ld.max(), ld.sum()
+
+    (mb, sb), (ml, sl) = max_load(base), max_load(lf)
+    assert sb == sl and ml < mb
+    print("  max KV rows per queue, layer 0: %d -> %d (mean %.1f)" % (mb, ml, sl / base.num_cus))
+    assert sorted(base.tasks) == sorted(lf.tasks)
+
+
+def test_cpp_pair_plan_matches_reference_on_the_megartp_graph():
+    from tests.test_planner_pins import megartp_graph
+    ops, pubs, edges, _ = megartp_graph()
+    ref = P.pair_plan(ops, pubs, edges, num_cus=148)
+    plan = mk.Plan.pairs([(op.opcode, op.grid) for op in ops], [(p.op, p.map, p.div, p.sel) for p in pubs],
+                         [(e.pub, e.cons, e.strategy, e.map, e.div) for e in edges], 148)
+    try:
+        ex = _compare(plan, ref)
+        assert ex["pairing"] == 1 and list(ex["queue"].shape) == [148, 5, 32]
+    finally:
+        plan.free()
+    # the host checks of the strategies, through the library
+    bad = [((1, (4,)), (2, (2,))), [(0, (), (), ())], [(0, 1, mk.MK_PAIR_TILE, (), ())]]
+    with pytest.raises(mk.MKError, match="tile") as e:
+        mk.Plan.pairs(*bad, 8)
+    assert e.value.status == mk.MK_E_INVALID
+    with pytest.raises(mk.MKError, match="more than two"):
+        mk.Plan.pairs([(1, (1,)), (2, (1,)), (3, (1,)), (4, (1,))], [(k, (), (), ()) for k in range(3)],
+                      [(k, 3, mk.MK_PAIR_TILE, (), ()) for k in range(3)], 8)

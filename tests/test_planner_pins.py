@@ -298,3 +298,133 @@ def test_replay_reports_deadlock():
                 r[P.W_WAIT_TGT] += 1  # a target that can never be reached
     with pytest.raises(Deadlock):
         replay(bad.queue, bad.num_events, lambda r: None)
+
+
+# ---------------------------------------------------------------------------
+# MegaRTP article, section 4: the plan of the GLM pre-attention subgraph at
+# M=16, KV=8192 under the pairing strategies.  Graph only (no arithmetic): the
+# op grids are the page's tile counts; the publications and edges are our
+# reading of its event list -- A0 publishes the hidden fp8/scale rows and the
+# norm rows; B0 and D1 finish split-K tiles in their last split, and only B0's
+# first 16 N tiles (the Q/scale tiles that make up D0's K=2048 input) are read
+# downstream; B1 signals once, from the tile that completes the cache write;
+# D0 publishes one region per head (its two N tiles), which D2's four tiles of
+# that head read.
+def megartp_graph():
+    G = GOLD["megartp_plan"]
+    names = G["ops_in_page_order"]
+    ops = [P.Op(n, 100 + i, tuple(G["tiles"][n])) for i, n in enumerate(names)]
+    ix = {n: i for i, n in enumerate(names)}
+    pubs = [
+        P.Pub(ix["A0"], name="hidden"), P.Pub(ix["A0"], name="norm"),
+        P.Pub(ix["B0"], map=(1,), div=(16,), sel=(-1, -1, 3), name="q"),
+        P.Pub(ix["C0"], name="gate_partial"),
+        P.Pub(ix["B1"], sel=(-1, 7), name="kcache"),
+        P.Pub(ix["D1"], sel=(-1, -1, 3), name="idx_q"),
+        P.Pub(ix["D0"], map=(1,), name="q_b"),
+    ]
+    pix = {p.name: k for k, p in enumerate(pubs)}
+    E = P.PairEdge
+    edges = [
+        E(pix["hidden"], ix["B0"], P.TILE_COVER), E(pix["norm"], ix["C0"], P.TILE_COVER),
+        E(pix["hidden"], ix["B1"], P.TILE_COVER),
+        E(pix["q"], ix["D1"], P.TILE_COVER), E(pix["gate_partial"], ix["D1"], P.TILE_REDUCE),
+        E(pix["q"], ix["D0"], P.TILE_COVER),
+        E(pix["q_b"], ix["D2"], P.TILE_COVER, map=(1,)),
+        E(pix["idx_q"], ix["E1"], P.TILE_COVER), E(pix["kcache"], ix["E1"], P.TILE),
+    ]
+    return ops, pubs, edges, ix
+
+
+def test_megartp_page_plan():
+    G = GOLD["megartp_plan"]
+    ops, pubs, edges, ix = megartp_graph()
+    pl = P.pair_plan(ops, pubs, edges, num_cus=G["queue_shape"][0])
+    assert pl.num_tasks == G["tasks"] and pl.num_events == G["events"]
+    th = G["thresholds"]
+    want = [th["event0"], th["event1"], th["event2"], th["event3"]] + [th["events4_67"]] * 64 + \
+        [th["event68"], th["event69"]]
+    assert pl.event_target == want
+    assert list(pl.queue.shape) == G["queue_shape"]
+    live = (pl.queue[:, :, P.W_OPCODE] != 0).sum(axis=1)
+    assert (live == 5).sum() == G["queues_with_5"] and (live == 4).sum() == G["queues_with_4"]
+    rows = pl.queue.reshape(-1, P.WORDS)
+    rows = rows[rows[:, P.W_OPCODE] != 0]
+    by_op = {n: rows[rows[:, P.W_OPROW] == i] for n, i in ix.items()}
+
+    def waits(r):
+        w = [(r[P.W_WAIT_EV], r[P.W_WAIT_TGT])] if r[P.W_WAIT_CNT] >= 1 else []
+        if r[P.W_WAIT_CNT] == 2:
+            w.append((r[P.W_WAIT2_EV], r[P.W_WAIT2_TGT]))
+        return [tuple(map(int, v)) for v in w]
+
+    for n, wl in G["waits"].items():
+        for r in by_op[n]:
+            assert waits(r) == [tuple(v) for v in wl], n
+    d0 = G["d0_head_events"]
+    for r in by_op["D2"]:
+        assert waits(r) == [(d0["first"] + int(r[P.W_GY]), d0["threshold"])]
+    assert (by_op["A0"][:, P.W_WAIT_CNT] == 0).all()
+    # signals: A0 publishes two outputs; split-K ops from their final split
+    for r in by_op["A0"]:
+        assert r[P.W_SIG_CNT] == 2 and [r[P.W_SIG_EV], r[P.W_SIG2_EV]] == G["a0_signals"]
+        assert [r[P.W_SIG_PUB], r[P.W_SIG2_PUB]] == [0, 1]
+    sig = lambda n: by_op[n][by_op[n][:, P.W_SIG_CNT] > 0]
+    assert len(sig("B0")) == th["event2"] and set(sig("B0")[:, P.W_GZ]) == {3}
+    assert len(sig("C0")) == th["event3"] and len(sig("D1")) == th["event68"] and len(sig("B1")) == th["event69"]
+    assert len(sig("D0")) == 128 and len(sig("D2")) == 0 and len(sig("E1")) == 0
+    for r in sig("D0"):
+        assert r[P.W_SIG_EV] == d0["first"] + r[P.W_GY]
+    assert set(by_op["E1"][:, P.W_OPROW]) == {G["e1_operand_row"]}
+    # every wait's threshold equals the number of signals to its event
+    n_sig = np.zeros(pl.num_events, dtype=int)
+    for r in rows:
+        for k in range(r[P.W_SIG_CNT]):
+            n_sig[r[(P.W_SIG_EV, P.W_SIG2_EV)[k]]] += 1
+    assert list(n_sig) == want
+
+
+def test_pairing_strategies_are_checked():
+    ops = [P.Op("P", 1, (4,)), P.Op("C", 2, (2,))]
+    # 'tile' needs one producer tile per region
+    with pytest.raises(ValueError, match="tile"):
+        P.pair_plan(ops, [P.Pub(0)], [P.PairEdge(0, 1, P.TILE)], 8)
+    # 'whole' needs one region published by every tile
+    with pytest.raises(ValueError, match="whole"):
+        P.pair_plan(ops, [P.Pub(0, map=(0,), div=(2,))], [P.PairEdge(0, 1, P.WHOLE)], 8)
+    with pytest.raises(ValueError, match="whole"):
+        P.pair_plan(ops, [P.Pub(0, sel=(3,))], [P.PairEdge(0, 1, P.WHOLE)], 8)
+    # regions of a tile_reduce edge hold equal partial counts
+    ops3 = [P.Op("P", 1, (3,)), P.Op("C", 2, (2,))]
+    with pytest.raises(ValueError, match="tile_reduce"):
+        P.pair_plan(ops3, [P.Pub(0, map=(0,), div=(2,))], [P.PairEdge(0, 1, P.TILE_REDUCE, map=(0,))], 8)
+    pl = P.pair_plan(ops3, [P.Pub(0, map=(0,), div=(2,))], [P.PairEdge(0, 1, P.TILE_COVER, map=(0,))], 8)
+    assert pl.event_target == [2, 1]
+    # a consumer region outside the publication, and three waits
+    with pytest.raises(ValueError, match="outside"):
+        P.pair_plan(ops, [P.Pub(0, map=(0,), div=(4,))], [P.PairEdge(0, 1, P.TILE_COVER, map=(0,))], 8)
+    ops4 = [P.Op("A", 1, (1,)), P.Op("B", 2, (1,)), P.Op("C", 3, (1,)), P.Op("D", 4, (1,))]
+    with pytest.raises(ValueError, match="more than two"):
+        P.pair_plan(ops4, [P.Pub(0), P.Pub(1), P.Pub(2)], [P.PairEdge(k, 3, P.TILE) for k in range(3)], 8)
+    # an op publishing three read outputs signals three events
+    with pytest.raises(ValueError, match="more than two"):
+        P.pair_plan(ops4, [P.Pub(0), P.Pub(0), P.Pub(0)], [P.PairEdge(k, 1 + k, P.TILE) for k in range(3)], 8)
+
+
+def test_megartp_page_plan_replays_under_random_interleavings():
+    """The page plan executed by the CPU replay (two waits, two signals): no
+    deadlock in 20 random worker interleavings, every consumer starts only
+    after all producer tiles of its regions finished."""
+    from oracle.replay import replay
+    ops, pubs, edges, ix = megartp_graph()
+    pl = P.pair_plan(ops, pubs, edges, num_cus=148)
+    pos = {}
+    for seed in range(20):
+        ctr, done = replay(pl.queue, pl.num_events, lambda r: None, order="random", seed=seed)
+        assert ctr == pl.event_target and sorted(done) == list(range(pl.num_tasks))
+        at = {t: i for i, t in enumerate(done)}
+        for t in range(pl.num_tasks):
+            for ev in (pl.wait[t], pl.wait2[t]):
+                if ev >= 0:
+                    prods = [u for u in range(pl.num_tasks) if ev in (pl.trigger[u], pl.trigger2[u])]
+                    assert max(at[u] for u in prods) < at[t]

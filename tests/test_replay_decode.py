@@ -33,6 +33,10 @@ def _rel(a, b):
     ("tiny", dict(batch=3, kv_len=(0, 200), seed=11), dict(OPTS, attn_splits=5, num_cus=7)),
     ("tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128, ffn=720, vocab=4100, seed=8),
      dict(OPTS, down_rows=6, gateup_outs=5, lm_rows=12)),
+    # the pairing-strategy plan (two waits on O and down) and longest-first attention
+    ("tiny", {}, dict(OPTS, pairing=1)),
+    ("tiny", dict(batch=3, kv_len=(0, 200), seed=11), dict(OPTS, attn_splits=5, num_cus=7, pairing=1, attn_order=1)),
+    ("tiny", dict(batch=4, kv_len=(10, 300), seed=5), dict(OPTS, attn_splits=4, num_cus=9, attn_order=1)),
 ])
 def test_replay_of_the_decode_plan_matches_the_oracle(name, overrides, opts):
     inp = synth.make_inputs(name, norm_sigma=0.1, **overrides)
@@ -46,7 +50,7 @@ def test_replay_of_the_decode_plan_matches_the_oracle(name, overrides, opts):
     assert _rel(ex.logits, ref["logits"]) < 1e-12
     assert np.array_equal(ex.next, ref["next"])
     assert np.array_equal(ex.kv, ref["kv_cache"])  # the new rows, and nothing else
-    for seed in range(20 if name == "tiny" and not overrides else 4):
+    for seed in range(20 if name == "tiny" and not overrides and len(opts) == len(OPTS) else 4):
         ex2, ctr2, done2 = _run(inp, pl, "random", seed)
         assert list(ctr2) == list(pl.event_target)
         assert sorted(done2) == list(range(pl.num_tasks))
