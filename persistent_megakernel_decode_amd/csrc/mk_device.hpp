@@ -1061,9 +1061,9 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   const GLB float* rope = (const GLB float*)mt.q(AttnRope) + (size_t)b * HD;  // (cos, sin) pairs
   const GLB uint16_t* qn = c.qk_norm ? (const GLB uint16_t*)mt.q(AttnQn) : nullptr;
   const GLB uint16_t* knw = c.qk_norm ? (const GLB uint16_t*)mt.q(AttnKn) : nullptr;
-  LDS float* qs = scr;            // rotated q, HD floats
-  LDS float* kn = scr + HD;       // new k (bf16-rounded), HD
-  LDS float* vn = scr + 2 * HD;   // new v (bf16-rounded), HD
+  LDS float* qs = scr;                                   // rotated q, HD floats
+  LDS uint16_t* kn = (LDS uint16_t*)(scr + HD);          // new k row as the cache holds it (bf16), HD
+  LDS uint16_t* vn = (LDS uint16_t*)(scr + 2 * HD);      // new v row (bf16), HD
 
   // ---- one batch of global loads
   float qv[PER], kv[PER], vv[PER], cs[PER], sn[PER], wq[PER], wk[PER];
@@ -1117,8 +1117,8 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
     for (int k = 0; k < PER; ++k) {
       kb[k] = f2bf(kv[k]);
       vb[k] = f2bf(vv[k]);
-      kn[lane + 64 * k] = bf16f(kb[k]);
-      vn[lane + 64 * k] = bf16f(vb[k]);
+      kn[lane + 64 * k] = kb[k];
+      vn[lane + 64 * k] = vb[k];
     }
     if (writer) {
       const size_t row = (((size_t)b * c.nkv + g) * c.cap + pos) * HD;
@@ -1151,7 +1151,8 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   // a 16-byte K chunk and a 16-byte V chunk per pass; the LPP lanes of a
   // position sum their partial dot products; every lane keeps a running
   // (max, sum, weighted V) for its positions, and the PPP groups are merged by
-  // log-sum-exp at the end.
+  // log-sum-exp at the end.  The new row takes part like a cached one (its
+  // chunk is selected in registers), so the pass has no divergent branch.
   constexpr int LPP = HD / 8;
   constexpr int PPP = 64 / LPP;
   constexpr int U = 4;  // passes whose loads are issued together
@@ -1159,6 +1160,12 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   float qc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qc[e] = qs[cidx * 8 + e];
+  uint4 knq = make_uint4(0u, 0u, 0u, 0u), vnq = knq;
+  if (has_new) {
+    const u32x4 a4 = ((const LDS u32x4*)kn)[cidx], b4 = ((const LDS u32x4*)vn)[cidx];
+    knq = make_uint4(a4.x, a4.y, a4.z, a4.w);
+    vnq = make_uint4(b4.x, b4.y, b4.z, b4.w);
+  }
   // head_dim 64: q as bf16 high and low parts, so that a K chunk's dot products
   // run on v_dot2 (bf16 pairs, exact products, fp32 accumulate) without
   // converting K (Llama-1B -7 us, batch 16 -17 us; the head_dim 128 build lost
@@ -1175,16 +1182,17 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
   for (int j0 = 0; j0 < n; j0 += U * PPP) {
     uint4 ku[U], vu[U];
+    if (nk > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int j = j0 + u * PPP + gi;
-      j = j < nk ? j : (nk > 0 ? nk - 1 : 0);
-      if (nk > 0) {
+      for (int u = 0; u < U; ++u) {
+        int j = j0 + u * PPP + gi;
+        j = j < nk ? j : nk - 1;
         ku[u] = src.ld16(0, j * HD * 2 + cidx * 16);
         vu[u] = src.ld16(1, j * HD * 2 + cidx * 16);
-      } else {
-        ku[u] = vu[u] = make_uint4(0, 0, 0, 0);
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) ku[u] = vu[u] = knq;
     }
     __builtin_amdgcn_sched_barrier(0);  // the batch's LDS reads stay in flight together
     // the U scores first, then one rescale of the running sums per pass: the
@@ -1194,10 +1202,14 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * PPP + gi;
+      // the new row (j == nk) or past the end (masked below): the new row's chunk
+      const bool cached = j < nk;
+      const uint4 k4 = make_uint4(cached ? ku[u].x : knq.x, cached ? ku[u].y : knq.y, cached ? ku[u].z : knq.z,
+                                  cached ? ku[u].w : knq.w);
       float d = 0.f;
-      if (HD == 64 && j < nk) {
-        const bf16x2 k0 = __builtin_bit_cast(bf16x2, ku[u].x), k1 = __builtin_bit_cast(bf16x2, ku[u].y);
-        const bf16x2 k2 = __builtin_bit_cast(bf16x2, ku[u].z), k3 = __builtin_bit_cast(bf16x2, ku[u].w);
+      if (HD == 64) {
+        const bf16x2 k0 = __builtin_bit_cast(bf16x2, k4.x), k1 = __builtin_bit_cast(bf16x2, k4.y);
+        const bf16x2 k2 = __builtin_bit_cast(bf16x2, k4.z), k3 = __builtin_bit_cast(bf16x2, k4.w);
         d = __builtin_amdgcn_fdot2_f32_bf16(k0, qhi[0], d, false);
         d = __builtin_amdgcn_fdot2_f32_bf16(k1, qhi[1], d, false);
         d = __builtin_amdgcn_fdot2_f32_bf16(k2, qhi[2], d, false);
@@ -1206,14 +1218,11 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
         d = __builtin_amdgcn_fdot2_f32_bf16(k1, qlo[1], d, false);
         d = __builtin_amdgcn_fdot2_f32_bf16(k2, qlo[2], d, false);
         d = __builtin_amdgcn_fdot2_f32_bf16(k3, qlo[3], d, false);
-      } else if (j < nk) {
-        d = fmaf(bf16lo(ku[u].x), qc[0], d); d = fmaf(bf16hi(ku[u].x), qc[1], d);
-        d = fmaf(bf16lo(ku[u].y), qc[2], d); d = fmaf(bf16hi(ku[u].y), qc[3], d);
-        d = fmaf(bf16lo(ku[u].z), qc[4], d); d = fmaf(bf16hi(ku[u].z), qc[5], d);
-        d = fmaf(bf16lo(ku[u].w), qc[6], d); d = fmaf(bf16hi(ku[u].w), qc[7], d);
-      } else {  // the new row (j == nk) or past the end (masked below)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(kn[cidx * 8 + e], qc[e], d);
+      } else {
+        d = fmaf(bf16lo(k4.x), qc[0], d); d = fmaf(bf16hi(k4.x), qc[1], d);
+        d = fmaf(bf16lo(k4.y), qc[2], d); d = fmaf(bf16hi(k4.y), qc[3], d);
+        d = fmaf(bf16lo(k4.z), qc[4], d); d = fmaf(bf16hi(k4.z), qc[5], d);
+        d = fmaf(bf16lo(k4.w), qc[6], d); d = fmaf(bf16hi(k4.w), qc[7], d);
       }
       // sum over the LPP lanes of this position (8: half a DPP row, 16: a row)
       d += dppf<DppXor1>(d);
@@ -1234,28 +1243,35 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * PPP + gi;
       const float pj = __expf(sc[u] - mb);  // 0 for masked positions
-      float vf[8];
-      if (j < nk) {
-        vf[0] = bf16lo(vu[u].x); vf[1] = bf16hi(vu[u].x); vf[2] = bf16lo(vu[u].y); vf[3] = bf16hi(vu[u].y);
-        vf[4] = bf16lo(vu[u].z); vf[5] = bf16hi(vu[u].z); vf[6] = bf16lo(vu[u].w); vf[7] = bf16hi(vu[u].w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = vn[cidx * 8 + e];
-      }
+      const bool cached = j < nk;
+      const uint4 v4 = make_uint4(cached ? vu[u].x : vnq.x, cached ? vu[u].y : vnq.y, cached ? vu[u].z : vnq.z,
+                                  cached ? vu[u].w : vnq.w);
+      const float vf[8] = {bf16lo(v4.x), bf16hi(v4.x), bf16lo(v4.y), bf16hi(v4.y),
+                           bf16lo(v4.z), bf16hi(v4.z), bf16lo(v4.w), bf16hi(v4.w)};
       l += pj;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = fmaf(pj, vf[e], o[e]);
     }
     m = mx;
   }
-  // merge the PPP position groups
+  // merge the PPP position groups: lane l with lane l ^ mm, by DPP within a
+  // 16-lane row (mm = 8) and the gfx950 row/half swaps across rows (16, 32)
 #pragma unroll
   for (int mm = LPP; mm < 64; mm <<= 1) {
-    const float m2 = __shfl_xor(m, mm, 64);
-    const float l2 = __shfl_xor(l, mm, 64);
+    auto other = [&](float v) {
+      if (mm == 8) return dppf<DppRor8>(v);
+      if (mm == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+      }
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    };
+    const float m2 = other(m);
+    const float l2 = other(l);
     float o2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[e], mm, 64);
+    for (int e = 0; e < 8; ++e) o2[e] = other(o[e]);
     const float M = fmaxf(m, m2);
     const float a1 = m == -INFINITY ? 0.f : __expf(m - M);
     const float a2 = m2 == -INFINITY ? 0.f : __expf(m2 - M);
