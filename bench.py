@@ -415,6 +415,8 @@ def main():
     ap.add_argument("--trace-dump", default=None, help="save the traced step's raw trace and queue (npz) here")
     ap.add_argument("--pairing", type=int, default=0, choices=[0, 1],
                     help="plan with the pairing strategies (mk_plan_opts.pairing) instead of the gcd/lcm rules")
+    ap.add_argument("--dma-pages", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="weight pages each loader wave keeps in flight (mk_plan_opts.dma_pages; 0: default)")
     ap.add_argument("--attn-order", type=int, default=0, choices=[-1, 0, 1],
                     help="attention placement (mk_plan_opts.attn_order): 1 longest first, -1 plan order, "
                          "0 the default (longest first at batch > 1)")
@@ -447,7 +449,7 @@ def main():
     kv = mk.kv_to_device(inp["kv_cache"])
     tok = mk.tokens_to_device(inp["tokens"])
     plan = mk.Plan.build(cfg, cfg["batch"], inp["kv_len"], inp["kv_cache"].shape[4], pairing=args.pairing,
-                         attn_order=args.attn_order)
+                         attn_order=args.attn_order, dma_pages=args.dma_pages)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
