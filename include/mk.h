@@ -114,10 +114,11 @@ typedef struct {
  *   until one split's K and V rows fit in 64 KiB, or in half the page ring
  *   while batch n_kv_heads splits still fit on num_cus at one each);
  * timeout_ms: bound of every device-side wait (default 200);
- * dma_pages: 16 KiB pages each of the two weight-loader waves keeps in flight
- *   (1 to 3, default 1): the event polls and activation reads that carry the
- *   dependency chain share the compute unit's vector-memory queue with the page
- *   DMA, so a shallow DMA backlog is the default.  Does not change the plan's
+ * dma_pages: 16 KiB pages each of the two weight-loader waves may leave in
+ *   flight behind the one it is issuing (1 to 3, default 1): the event polls and
+ *   activation reads that carry the dependency chain queue behind the page DMA,
+ *   and more bytes in flight lengthen those queues without raising the stream
+ *   rate, so a shallow backlog is the default.  Does not change the plan's
  *   schedule metadata.
  * lw_streams: streams of mk_run_layerwise (0 or 1: every launch on the caller's
  *   stream; 2 or 3: independent branches of the op graph -- the GLM path's QKV-A,

@@ -215,6 +215,8 @@ static mk_status resolve_cus(const mk_plan_opts* opts, int* num_cus, int* timeou
 }
 
 // The GLM-style pre-attention path: fp8 weights, M <= 16 token rows.
+static std::string check_cached_layout(const mk_plan* p);
+
 static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_len, const mk_plan_opts* opts,
                            mk_plan** out) {
   if (d.weight_dtype != MK_FP8_E4M3_B128)
@@ -319,8 +321,40 @@ static mk_status build_glm(const mk_model_desc& d, int32_t M, const int32_t* kv_
   const int gsplits = mk::ceil_div(H / 128, mk::kGateBlocks);
   p->off_ggpart = take((size_t)gsplits * mk::ceil_div(d.n_gate, mkd::kMB) * mkd::kMB * mkd::kMB * 4);
   p->ws_bytes = off;
+  const std::string lay = check_cached_layout(p);
+  if (!lay.empty()) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "workspace layout: " + lay);
+  }
   *out = p;
   return MK_OK;
+}
+
+// The cached-read protocol (CohT in mk_device.hpp) reads a buffer through the
+// caches only when no cache line of it holds data completed under two
+// different events.  The workspace layout is built that way; this checks it
+// for every buffer so read, per event slice: 256-byte aligned offsets and
+// sizes (the attention partials, whose blocks are not aligned, are read with
+// coherent loads and are exempt).  Returns "" or what breaks the invariant.
+static std::string check_cached_layout(const mk_plan* p) {
+  auto al = [](size_t v) { return v % 256 == 0; };
+  if (p->glm) {
+    const size_t offs[] = {p->off_gn, p->off_ga8, p->off_gas, p->off_gqkva, p->off_gqa8, p->off_gqs,
+                           p->off_gr, p->off_gq, p->off_gqidx, p->off_ggate, p->off_ggpart};
+    for (size_t o : offs)
+      if (!al(o)) return "a GLM buffer does not start on a 256-byte boundary";
+    // gate partials: one 16 x 16 fp32 block (1 KiB) per (split, row tile), each its own event
+    if ((size_t)mkd::kMB * mkd::kMB * 4 % 256) return "gate partial blocks are not 256-byte multiples";
+    return "";
+  }
+  const mkd::Consts& c = p->c;
+  const size_t offs[] = {p->off_qkv, p->off_ao, p->off_hidden, p->off_act, p->off_lmmax,
+                         p->sz_qkv, p->sz_ao, p->sz_hid, p->sz_act};
+  for (size_t o : offs)
+    if (!al(o)) return "a per-layer slice does not start on a 256-byte boundary";
+  // q/k/v output: one event per kv head; its (sequence, kv head) blocks
+  if (!al((size_t)c.RPG * 4)) return "a (sequence, kv head) block of the q/k/v output is not a 256-byte multiple";
+  return "";
 }
 
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* kv_len, const mk_plan_opts* opts,
@@ -499,6 +533,11 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   p->off_logits = take(B * c.V * 4);
   p->off_next = take(B * 4);
   p->ws_bytes = off;
+  const std::string lay = check_cached_layout(p);
+  if (!lay.empty()) {
+    delete p;
+    return fail(MK_E_UNSUPPORTED, "workspace layout: " + lay);
+  }
   *out = p;
   return MK_OK;
 }

@@ -467,3 +467,22 @@ def test_cpp_pair_plan_matches_reference_on_the_megartp_graph():
     with pytest.raises(mk.MKError, match="more than two"):
         mk.Plan.pairs([(1, (1,)), (2, (1,)), (3, (1,)), (4, (1,))], [(k, (), (), ()) for k in range(3)],
                       [(k, 3, mk.MK_PAIR_TILE, (), ()) for k in range(3)], 8)
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("tiny", {}), ("tiny", dict(batch=3, kv_len=(0, 200), seed=11)), ("tiny", dict(ffn=720, vocab=4100, kv_len=999)),
+    ("tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128)), ("llama1b_b16", {}), ("glm_tiny", {}),
+])
+def test_plans_satisfy_the_cached_read_layout(name, overrides):
+    """Every plan's workspace passes the library's check of the cached-read
+    layout (each buffer read through the caches starts its per-event slices on
+    256-byte boundaries; a plan that broke it would fail to build)."""
+    cfg = synth.config(name, **overrides)
+    if cfg.get("arch") == "glm":
+        pos, _ = synth.glm_positions(cfg)
+        plan = mk.Plan.build(cfg, len(pos), pos, synth.glm_capacity(cfg), num_cus=37)
+    else:
+        kv = synth.kv_lengths(cfg)
+        plan = mk.Plan.build(cfg, cfg["batch"], kv, synth.kv_capacity(kv), num_cus=37)
+    plan.free()
+    assert mk.lib().mk_last_error() == b""
