@@ -392,10 +392,11 @@ mk_status mk_run_steps(mk_plan* plan, const mk_weights* weights, void* kv_cache,
  * MK_OUT_LOGITS fp32 [batch][vocab]; MK_OUT_NEXT_TOKEN int32 [batch];
  * MK_OUT_QKV fp32 [n_layers] slices of [batch][n_kv_heads][(n_q/n_kv + 2) *
  *   head_dim] (per kv head: its q heads, then k, then v, before RoPE);
- * MK_OUT_HIDDEN fp32 [n_layers][2] slices of [batch][hidden] (residual stream
- *   after the attention block and after the FFN block of each layer);
- *   each slice of these two starts at a multiple of 256 bytes (slice stride =
- *   its size rounded up to 256 bytes).
+ * MK_OUT_HIDDEN fp32 [n_layers][2] slices of [hidden / 8][batch][8] (residual
+ *   stream after the attention block and after the FFN block of each layer;
+ *   element (b, k) at ((k / 8) * batch + b) * 8 + k % 8, which at batch 1 is
+ *   the plain vector); each slice of these two starts at a multiple of 256
+ *   bytes (slice stride = its size rounded up to 256 bytes).
  * GLM: MK_OUT_GLM_R bf16 [M][hidden] (x + r); MK_OUT_GLM_Q bf16 [M][n_q_heads]
  *   [head_dim]; MK_OUT_GLM_QIDX bf16 [M][n_idx_heads][idx_head_dim];
  *   MK_OUT_GLM_GATE fp32 [M][n_gate]; and the intermediates MK_OUT_GLM_NORM fp32

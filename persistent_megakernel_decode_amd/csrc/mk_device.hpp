@@ -125,6 +125,15 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// Element (b, k) of a [B][K] activation of this step (the residual stream,
+// the attention output, the FFN activation): laid out as [K / 8][B][8], so
+// that the 16 sequences' 32-byte chunks of one k range are contiguous and a
+// batched tile's loads of a k-step cover one 2 KiB run instead of B lines a
+// power-of-two row length apart.  At B = 1 this is the plain vector.
+__device__ __forceinline__ size_t act_ix(int b, int k, int B) {
+  return ((size_t)(k >> 3) * B + b) * 8 + (k & 7);
+}
+
 // fp32 -> bf16, round to nearest even (NaN stays NaN)
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
@@ -855,11 +864,16 @@ __device__ __forceinline__ bool amax_better(float v, int i, float bv, int bi) {
 // products keep about 16 bits of the activation, as the fp32 path does to
 // within rounding.  Rows past nrows re-read the last row, sequences past B and
 // chunks past the wave's range read valid addresses and are zeroed.
+// kpart / nparts: the tile's K range is cut into nparts equal parts (K / 8 a
+// multiple of nparts) and this call runs part kpart; a part after the first
+// adds its sums to the ones already in part / ssp (the earlier parts', written
+// by this wave or, in the megakernel, by the owning group's wave cw), so the
+// result is (part 0 + part 1) in that order wherever the tile runs.
 template <bool EMB, int POL, class Src, class Rel>
 __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
-                                    LDS float* ssp, const Rel& rel) {
+                                    LDS float* ssp, const Rel& rel, int kpart, int nparts) {
   const int lane = lane_id();
-  const int K = gi.K, nch = K / 8, cpw = (nch + kNW - 1) / kNW, base = cw * cpw;
+  const int K = gi.K, nch = K / 8 / nparts, c0 = kpart * nch, cpw = (nch + kNW - 1) / kNW, base = c0 + cw * cpw;
   const int nks = (cpw + 3) / 4;  // k-steps of 4 chunks
   const int r = lane & 15, q = lane >> 4;
   const int rc = r < gi.nrows ? r : gi.nrows - 1;
@@ -868,11 +882,8 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
   const int b = lane & 15;
   const bool bok = b < B;
   const GLB uint16_t* xb = nullptr;
-  uint32_t xoff = 0;  // byte offset of sequence b's activation row
-  if (EMB)
-    xb = gi.emb + (size_t)token_of(gi.tok, bok ? b : 0, V) * K;
-  else
-    xoff = (uint32_t)((bok ? b : 0) * K) * 4;
+  if (EMB) xb = gi.emb + (size_t)token_of(gi.tok, bok ? b : 0, V) * K;
+  const int bb = bok ? b : 0;
   const CohT<POL> cx(EMB ? (const GLB void*)gi.emb : (const GLB void*)gi.xf);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
@@ -884,15 +895,16 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int ks = ks0 + u, ch = ks * 4 + q;
-      ok[u] = ks < nks && ch < cpw && base + ch < nch;
+      ok[u] = ks < nks && ch < cpw && base + ch < c0 + nch;
       const int kk = (ok[u] ? base + ch : 0) * 8;
       const uint4 w = src.ld16(seg, arow + kk * 2);
       A[u] = u32x4{w.x, w.y, w.z, w.w};
       if (EMB) {
         xr[u] = *(const GLB u32x4*)(xb + kk);
       } else {
-        x0[u] = cx.f4(xoff + kk * 4);
-        x1[u] = cx.f4(xoff + kk * 4 + 16);
+        const uint32_t xo = (uint32_t)act_ix(bb, kk, B) * 4;  // chunk kk of sequence b (act_ix)
+        x0[u] = cx.f4(xo);
+        x1[u] = cx.f4(xo + 16);
       }
       if (gi.nw) wn[u] = *(const GLB u32x4*)(gi.nw + kk);
     }
@@ -933,18 +945,35 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
   // sequence b's sum of squares over the wave's range: lanes b, b+16, b+32, b+48
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
-  if (lane < kMB) ssp[lane] = ss;
+  if (kpart == 0) {
+    if (lane < kMB) ssp[lane] = ss;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[(4 * q + i) * kMB + b] = acc[i];
+    for (int i = 0; i < 4; ++i) part[(4 * q + i) * kMB + b] = acc[i];
+  } else {
+    if (lane < kMB) ssp[lane] = ssp[lane] + ss;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[(4 * q + i) * kMB + b] = part[(4 * q + i) * kMB + b] + acc[i];
+  }
 }
 
 template <int POL = 0, class Src, class Rel>
 __device__ inline void gemv_rows_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
-                                    LDS float* ssp, const Rel& rel) {
+                                    LDS float* ssp, const Rel& rel, int kpart = 0, int nparts = 1) {
   if (gi.xf)
-    gemv_tile_mb<false, POL>(src, gi, B, V, cw, part, ssp, rel);
+    gemv_tile_mb<false, POL>(src, gi, B, V, cw, part, ssp, rel, kpart, nparts);
   else
-    gemv_tile_mb<true, POL>(src, gi, B, V, cw, part, ssp, rel);
+    gemv_tile_mb<true, POL>(src, gi, B, V, cw, part, ssp, rel, kpart, nparts);
+}
+
+// Batched QKV, O-projection and down tiles run their K range in two halves:
+// in the megakernel the instruction's own compute group takes the first half
+// and the other group, otherwise idle through these ops (at most one tile of
+// them per compute unit), the second; the layer-by-layer kernel runs both
+// halves in turn.  The sums are added in the same order either way.
+__device__ __forceinline__ bool gemv_k_halves(int op, const Consts& c) {
+  if (c.B <= 1 || c.glm) return false;
+  const int K = op == OpQkv ? c.H : op == OpOproj ? c.nq * c.hd : op == OpDown ? c.F : 0;
+  return K > 0 && K % 16 == 0;
 }
 
 // Residual inputs of the four (row, sequence) outputs lane l owns in the batched
@@ -962,11 +991,11 @@ __device__ inline f32x4 gemv_residual_mb(const Meta& m, const Consts& c) {
     const int row = (lane + 64 * j) >> 4;
     const int rr = row0 + (row < nr ? row : 0);
     if (op == OpOproj) {
-      r[j] = m.q(OX) ? CohT<POL>((const GLB float*)m.q(OX)).f1((uint32_t)(bb * c.H + rr) * 4)
+      r[j] = m.q(OX) ? CohT<POL>((const GLB float*)m.q(OX)).f1((uint32_t)act_ix(bb, rr, c.B) * 4)
                      : bf16f(((const GLB uint16_t*)m.q(OEmbed))[(size_t)token_of((const GLB int*)m.q(OTokens), bb, c.V) *
                                                                   c.H + rr]);
     } else {
-      r[j] = CohT<POL>((const GLB float*)m.q(DnRes)).f1((uint32_t)(bb * c.H + rr) * 4);
+      r[j] = CohT<POL>((const GLB float*)m.q(DnRes)).f1((uint32_t)act_ix(bb, rr, c.B) * 4);
     }
   }
   return r;
@@ -1006,16 +1035,16 @@ __device__ inline void gemv_epilogue_mb(const Meta& m, const Consts& c, const LD
         if (live) st_agent((GLB float*)m.q(QkvOut) + ((size_t)b * c.nkv + m.w(WGx)) * c.RPG + row0 + row, val(row));
         break;
       case OpOproj:
-        if (live) st_agent((GLB float*)m.q(OOut) + (size_t)b * c.H + row0 + row, res[j] + val(row));
+        if (live) st_agent((GLB float*)m.q(OOut) + act_ix(b, row0 + row, c.B), res[j] + val(row));
         break;
       case OpGateUp:
         if (live) {
           const float gt = val(row), up = val(nr + row);  // up row j sits at tile row nr + j
-          st_agent((GLB float*)m.q(GuOut) + (size_t)b * c.F + row0 + row, gt / (1.f + __expf(-gt)) * up);
+          st_agent((GLB float*)m.q(GuOut) + act_ix(b, row0 + row, c.B), gt / (1.f + __expf(-gt)) * up);
         }
         break;
       case OpDown:
-        if (live) st_agent((GLB float*)m.q(DnOut) + (size_t)b * c.H + row0 + row, res[j] + val(row));
+        if (live) st_agent((GLB float*)m.q(DnOut) + act_ix(b, row0 + row, c.B), res[j] + val(row));
         break;
       case OpLmHead:
         if (live) {
@@ -1353,9 +1382,10 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
       for (int k = 0; k < PER; ++k) o[k] = fmaf(s0 + u < S ? w : 0.f, ov[u][k], o[k]);
     }
   }
-  GLB float* out = (GLB float*)m.q(CombOut) + (size_t)b * c.nq * HD + (size_t)(g * c.hpg + cw) * HD;
+  GLB float* out = (GLB float*)m.q(CombOut);
+  const int k0 = (g * c.hpg + cw) * HD;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) st_agent(out + lane + 64 * k, o[k] / L);
+  for (int k = 0; k < PER; ++k) st_agent(out + act_ix(b, k0 + lane + 64 * k, c.B), o[k] / L);
 }
 
 // Reduce the LM-head tile maxima of sequence b in tile order, lowest index on

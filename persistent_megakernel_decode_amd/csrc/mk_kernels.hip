@@ -299,7 +299,9 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
       if (glm_is_gemm(op)) glm_epilogue(m, a.c, &L->c.part[sl][0][0]);
     } else if constexpr (LT::MB) {
       const f32x4 res = gemv_residual_mb(m, a.c);
-      if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
+      // a K-halved tile is complete once both groups have arrived
+      const int arrivals = (LT::SETS > 1 && gemv_k_halves(op, a.c)) ? 2 * kNW : kNW;
+      if (!wait_lds_ge(a, L, &L->c.arrive[sl], arrivals, ErrDrain, i)) return;
       if (gemv)
         gemv_epilogue_mb(m, a.c, &L->c.part[sl][0][0], &L->c.ssp[sl][0][0], res);
       else if (op == OpArgmax)
@@ -509,15 +511,29 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
 // the instruction's event (controller "ready") and loads the activations.
 // Other ops wait for "ready" first.
 // set: this wave's compute group; group g takes instructions g, g + SETS, ...
-// (it reads only their records, each before its arrival, so the controller
-// cannot have reused the slot).
+// and, with two groups, the second K-half of the other group's K-halved GEMV
+// tiles (it reads only these records, each before its arrival, so the
+// controller cannot have reused the slot).
 template <int HD, class LT>
 __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
   const int lane = lane_id();
   int act_row = -1;
   int seq = 0;  // one group: ring pages of the instructions before i
   Act act;
-  for (int i = set; i < a.max_len; i += LT::SETS) {
+  for (int i = LT::SETS > 1 ? 0 : set; i < a.max_len; i += LT::SETS > 1 ? 1 : LT::SETS) {
+    // two groups: besides its own instructions (i mod 2 = set) a group helps
+    // with the other group's K-halved tiles; it tells them from the queue's
+    // opcode word (the queue does not change during a run), and reads such a
+    // record before arriving on it, so that the slot is still that record's
+    bool own = true;
+    if constexpr (LT::SETS > 1) {
+      own = (i & 1) == set;
+      if (!own) {
+        const int opg = instr(a, i)[WOpcode];
+        if (opg == OpNoop) break;
+        if (!gemv_k_halves(opg, a.c)) continue;
+      }
+    }
     if (!wait_lds_ge(a, L, &L->c.meta_seq, i + 1, ErrReady, i)) return;
     const Meta m = load_meta(L->meta[i % kMeta]);
     const int op = m.w(WOpcode);
@@ -601,7 +617,30 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
       if (cw == 0 && tr && lane == 0) tr[1] = now_ticks();
       if (gemv) {
         const GemvIn gi = gemv_input(m, a.c);
-        gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, &L->c.part[sl][cw][0], &L->c.ssp[sl][cw][0], release);
+        LDS float* pw = &L->c.part[sl][cw][0];
+        LDS float* sw = &L->c.ssp[sl][cw][0];
+        if (LT::SETS > 1 && gemv_k_halves(op, a.c)) {
+          if (own) {
+            // first half; the helping group hands the pages back
+            gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, pw, sw, [] {}, 0, 2);
+          } else {
+            // second half: once the owning group has arrived (its partial
+            // sums are in the slot and it has finished reading the pages),
+            // release the pages and add to its sums
+            bool live = true;
+            auto rel2 = [&]() {
+              if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) {
+                live = false;
+                return;
+              }
+              release();
+            };
+            gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, pw, sw, rel2, 1, 2);
+            if (!live) return;
+          }
+        } else {
+          gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, pw, sw, release);
+        }
       } else if (op == OpAttn) {
         attn_wave<HD>(src, m, a.c, cw, L->c.scratch[set * kNW + cw], cw == 0, cw == 0 ? tr : nullptr);
       } else if (op == OpCombine) {
@@ -707,7 +746,12 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
   if (is_gemv(op)) {
     const GemvIn gi = gemv_input(m, a.c);
     if constexpr (MB) {
-      gemv_rows_mb<0>(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {});
+      if (gemv_k_halves(op, a.c)) {
+        gemv_rows_mb<0>(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {}, 0, 2);
+        gemv_rows_mb<0>(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {}, 1, 2);
+      } else {
+        gemv_rows_mb<0>(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {});
+      }
       __syncthreads();
       if (cw == 0) gemv_epilogue_mb(m, a.c, &part[0][0], &ssp[0][0], gemv_residual_mb<0>(m, a.c));
     } else {

@@ -74,7 +74,9 @@ class Case:
         nq, nkv = cfg["n_q_heads"], cfg["n_kv_heads"]
         hpg = nq // nkv
         pad = lambda n: (n * 4 + 255) // 256 * 64  # floats per slice, padded to 256 bytes
-        hs = r["hidden"].reshape(L * 2, pad(B * H))[:, :B * H].reshape(L, 2, B, H)
+        # element (b, k) of a slice at ((k / 8) * B + b) * 8 + k % 8
+        hs = r["hidden"].reshape(L * 2, pad(B * H))[:, :B * H].reshape(L, 2, H // 8, B, 8)
+        hs = hs.transpose(0, 1, 3, 2, 4).reshape(L, 2, B, H)
         RPG = (hpg + 2) * hd
         qs = r["qkv"].reshape(L, pad(B * nkv * RPG))[:, :B * nkv * RPG].reshape(L, B, nkv, hpg + 2, hd)
         nat = np.concatenate([qs[:, :, :, :hpg].reshape(L, B, nq, hd), qs[:, :, :, hpg], qs[:, :, :, hpg + 1]],
