@@ -259,7 +259,15 @@ mk_status mk_pair_plan(const mk_graph_op* ops, int32_t n_ops, const mk_pair_pub*
  *   row per op, shared by all of its tile instructions: MegaRTP article,
  *   section 4, "OperandPtrTable").  pairing, attn_order: the planner choices
  *   the plan was built with, defaults resolved (pairing 0/1; attn_order 1
- *   longest first, 0 plan order; 1 and 0 for mk_pair_plan plans). */
+ *   longest first, 0 plan order; 1 and 0 for mk_pair_plan plans).
+ *   At batch > 1 the matrix-core tiles read their inputs pre-split: per
+ *   8-element chunk and sequence 32 bytes, the chunk's bf16 parts h = bf16(v)
+ *   then bf16(v - h) (MK_SLOT_ATTN_OUT and MK_SLOT_FFN_ACT hold only this
+ *   form then); the O projection and down also store the next op's normed
+ *   input in this form (MK_SLOT_SPLIT_FFN: x times the FFN norm weight;
+ *   MK_SLOT_SPLIT_ATTN: x times the next layer's attention norm weight, or
+ *   the final norm weight for the LM head) with the sums of squares of x per
+ *   chunk, fp32 [chunks][batch] (MK_SLOT_SUMSQ_*). */
 enum {
   MK_SLOT_NONE = 0,
   /* weights (Llama family) */
@@ -270,7 +278,8 @@ enum {
   MK_SLOT_TOKENS = 20, MK_SLOT_K_CACHE, MK_SLOT_V_CACHE,
   /* plan-owned data */
   MK_SLOT_ROPE = 30, MK_SLOT_QKV, MK_SLOT_ATTN_PART, MK_SLOT_ATTN_OUT, MK_SLOT_HIDDEN_ATTN, MK_SLOT_HIDDEN_FFN,
-  MK_SLOT_FFN_ACT, MK_SLOT_LOGITS, MK_SLOT_LM_MAX, MK_SLOT_NEXT_TOKEN,
+  MK_SLOT_FFN_ACT, MK_SLOT_LOGITS, MK_SLOT_LM_MAX, MK_SLOT_NEXT_TOKEN, MK_SLOT_SPLIT_ATTN, MK_SLOT_SPLIT_FFN,
+  MK_SLOT_SUMSQ_ATTN, MK_SLOT_SUMSQ_FFN,
   /* the GLM pre-attention path: inputs, weights (codes, scales), caches,
      intermediates and outputs */
   MK_SLOT_G_X = 50, MK_SLOT_G_R, MK_SLOT_G_ATTN_NORM, MK_SLOT_G_W, MK_SLOT_G_W_SCALE, MK_SLOT_G_Q_A_NORM,

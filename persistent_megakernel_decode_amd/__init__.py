@@ -69,6 +69,7 @@ MK_SLOT_FFN_ACT = 36
 MK_SLOT_LOGITS = 37
 MK_SLOT_LM_MAX = 38
 MK_SLOT_NEXT_TOKEN = 39
+MK_SLOT_SPLIT_ATTN, MK_SLOT_SPLIT_FFN, MK_SLOT_SUMSQ_ATTN, MK_SLOT_SUMSQ_FFN = 40, 41, 42, 43
 MK_SLOT_G_X = 50
 MK_SLOT_G_R = 51
 MK_SLOT_G_ATTN_NORM = 52

@@ -123,6 +123,10 @@ struct mk_plan {
   size_t off_qkv = 0, off_part = 0, off_ao = 0, off_hidden = 0, off_act = 0, off_logits = 0, off_lmmax = 0,
          off_next = 0;
   size_t sz_qkv = 0, sz_part = 0, sz_ao = 0, sz_act = 0, sz_hid = 0;
+  // batch > 1: the normed GEMV inputs in pre-split form and their chunk sums of
+  // squares -- QKV of layers 1..L-1 and the LM head (slices 1..L, written by
+  // down), gate/up of each layer (written by O)
+  size_t off_xpa = 0, off_xpf = 0, off_ssa = 0, off_ssf = 0, sz_ssc = 0;
   // GLM pre-attention path: token rows' (position, request), workspace offsets
   bool glm = false;
   int n_seq = 0;
@@ -348,8 +352,8 @@ static std::string check_cached_layout(const mk_plan* p) {
     return "";
   }
   const mkd::Consts& c = p->c;
-  const size_t offs[] = {p->off_qkv, p->off_ao, p->off_hidden, p->off_act, p->off_lmmax,
-                         p->sz_qkv, p->sz_ao, p->sz_hid, p->sz_act};
+  const size_t offs[] = {p->off_qkv, p->off_ao, p->off_hidden, p->off_act, p->off_lmmax, p->off_xpa, p->off_xpf,
+                         p->off_ssa, p->off_ssf, p->sz_qkv, p->sz_ao, p->sz_hid, p->sz_act, p->sz_ssc};
   for (size_t o : offs)
     if (!al(o)) return "a per-layer slice does not start on a 256-byte boundary";
   // q/k/v output: one event per kv head; its (sequence, kv head) blocks
@@ -505,6 +509,11 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   c.qk_norm = d.qk_norm;
   c.eps = d.rms_eps;
   c.inv_sqrt_hd = (float)(1.0 / std::sqrt((double)d.head_dim));
+  // rows per stored sum of squares: the largest of 8, 4, 2, 1 that divides the
+  // producing tiles' rows (down for the QKV / LM-head input, O for gate/up's)
+  auto sum_rows = [](int rows) { return rows % 8 == 0 ? 8 : rows % 4 == 0 ? 4 : rows % 2 == 0 ? 2 : 1; };
+  c.ssg_a = sum_rows(o.down_rows);
+  c.ssg_f = sum_rows(o.gemv_rows);
   p->timeout_ms = timeout_ms;
   // workspace layout (fp32 everywhere)
   const size_t B = batch, L = d.n_layers;
@@ -527,6 +536,13 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   p->off_ao = take(p->sz_ao * L);
   p->off_hidden = take(p->sz_hid * 2 * L);
   p->off_act = take(p->sz_act * L);
+  if (B > 1) {
+    p->sz_ssc = r256((size_t)c.H * B * 4);  // up to one sum per row (rows per sum: ssg_a, ssg_f)
+    p->off_xpa = take(p->sz_hid * (L + 1));
+    p->off_xpf = take(p->sz_hid * L);
+    p->off_ssa = take(p->sz_ssc * (L + 1));
+    p->off_ssf = take(p->sz_ssc * L);
+  }
   p->off_lmmax = take(B * c.T_v * 8);
   // the step's outputs last: the allocation-free entry point keeps everything
   // before them in its static buffer and writes the outputs to the caller's
@@ -837,6 +853,15 @@ static void fill_rows(const mk_plan* p, const Src& src, uint64_t* vals, int32_t*
   const size_t hid = p->sz_hid;
   auto xa = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l) * hid); };
   auto xb = [&](int l) { return ws(p->off_hidden + (size_t)(2 * l + 1) * hid); };
+  const bool split = B > 1;  // pre-split GEMV inputs (batched tiles)
+  auto xpa = [&](int l) { return ws(p->off_xpa + (size_t)l * hid); };
+  auto xpf = [&](int l) { return ws(p->off_xpf + (size_t)l * hid); };
+  auto ssa = [&](int l) { return ws(p->off_ssa + (size_t)l * p->sz_ssc); };
+  auto ssf = [&](int l) { return ws(p->off_ssf + (size_t)l * p->sz_ssc); };
+  auto attn_norm = [&](int l) {  // layer l's attention RMSNorm weight; the final norm past the last layer
+    if (l >= L) return u(src.final_norm);
+    return src.layer_ptrs ? u(src.layer_ptrs[(size_t)l * MK_LAYER_SLOTS + 0]) : (uint64_t)0;
+  };
   const size_t kvlayer = (size_t)2 * B * d.n_kv_heads * d.max_kv_len * d.head_dim * 2;
   auto kvp = [&](int l, int half) {
     return src.kv ? u((const char*)src.kv + l * kvlayer + half * (kvlayer / 2)) : (uint64_t)0;
@@ -857,6 +882,10 @@ static void fill_rows(const mk_plan* p, const Src& src, uint64_t* vals, int32_t*
         put(o, mkd::QkvEmbed, u(src.embed), MK_SLOT_EMBED);
         put(o, mkd::QkvTokens, u(src.tokens), MK_SLOT_TOKENS);
         put(o, mkd::QkvOut, ws(p->off_qkv + l * p->sz_qkv), MK_SLOT_QKV);
+        if (split && l) {
+          put(o, mkd::QkvPrep, xpa(l), MK_SLOT_SPLIT_ATTN);
+          put(o, mkd::QkvSs, ssa(l), MK_SLOT_SUMSQ_ATTN);
+        }
         break;
       case mk::kAttn:
         put(o, mkd::AttnQkv, ws(p->off_qkv + l * p->sz_qkv), MK_SLOT_QKV);
@@ -880,6 +909,11 @@ static void fill_rows(const mk_plan* p, const Src& src, uint64_t* vals, int32_t*
         put(o, mkd::OEmbed, u(src.embed), MK_SLOT_EMBED);
         put(o, mkd::OTokens, u(src.tokens), MK_SLOT_TOKENS);
         put(o, mkd::OOut, xa(l), MK_SLOT_HIDDEN_ATTN);
+        if (split) {
+          put(o, mkd::OPrepW, w(7), MK_SLOT_FFN_NORM);
+          put(o, mkd::OPrep, xpf(l), MK_SLOT_SPLIT_FFN);
+          put(o, mkd::OSs, ssf(l), MK_SLOT_SUMSQ_FFN);
+        }
         break;
       case mk::kGateUp:
         put(o, mkd::GuWg, w(8), MK_SLOT_W_GATE);
@@ -887,12 +921,21 @@ static void fill_rows(const mk_plan* p, const Src& src, uint64_t* vals, int32_t*
         put(o, mkd::GuNorm, w(7), MK_SLOT_FFN_NORM);
         put(o, mkd::GuIn, xa(l), MK_SLOT_HIDDEN_ATTN);
         put(o, mkd::GuOut, ws(p->off_act + l * p->sz_act), MK_SLOT_FFN_ACT);
+        if (split) {
+          put(o, mkd::GuPrep, xpf(l), MK_SLOT_SPLIT_FFN);
+          put(o, mkd::GuSs, ssf(l), MK_SLOT_SUMSQ_FFN);
+        }
         break;
       case mk::kDown:
         put(o, mkd::DnW, w(10), MK_SLOT_W_DOWN);
         put(o, mkd::DnIn, ws(p->off_act + l * p->sz_act), MK_SLOT_FFN_ACT);
         put(o, mkd::DnRes, xa(l), MK_SLOT_HIDDEN_ATTN);
         put(o, mkd::DnOut, xb(l), MK_SLOT_HIDDEN_FFN);
+        if (split) {
+          put(o, mkd::DnPrepW, attn_norm(l + 1), l + 1 < L ? MK_SLOT_ATTN_NORM : MK_SLOT_FINAL_NORM);
+          put(o, mkd::DnPrep, xpa(l + 1), MK_SLOT_SPLIT_ATTN);
+          put(o, mkd::DnSs, ssa(l + 1), MK_SLOT_SUMSQ_ATTN);
+        }
         break;
       case mk::kLmHead:
         if (d.tied_lm_head)
@@ -903,6 +946,10 @@ static void fill_rows(const mk_plan* p, const Src& src, uint64_t* vals, int32_t*
         put(o, mkd::LmIn, xb(L - 1), MK_SLOT_HIDDEN_FFN);
         put(o, mkd::LmLogits, u(src.b.logits), MK_SLOT_LOGITS);
         put(o, mkd::LmMax, ws(p->off_lmmax), MK_SLOT_LM_MAX);
+        if (split) {
+          put(o, mkd::LmPrep, xpa(L), MK_SLOT_SPLIT_ATTN);
+          put(o, mkd::LmSs, ssa(L), MK_SLOT_SUMSQ_ATTN);
+        }
         break;
       case mk::kArgmax:
         put(o, mkd::AmMax, ws(p->off_lmmax), MK_SLOT_LM_MAX);

@@ -45,20 +45,27 @@ enum : int { OpGA0 = 9, OpGQkva = 10, OpGGate = 11, OpGIdxk = 12, OpGQaNorm = 13
 
 // ---- operand table slots (one row of 16 u64 per op) --------------------------
 enum : int {
+  // Batch > 1: the GEMV activations are stored pre-split (see act_split):
+  // the producer of a normed input also stores it times the consumer's
+  // RMSNorm weight (QkvPrep, GuPrep, LmPrep) and per-chunk sums of squares
+  // (QkvSs, GuSs, LmSs); the attention output and the FFN activation are
+  // stored only in that form (OIn, DnIn).
   // QKV
-  QkvWq = 0, QkvWk = 1, QkvWv = 2, QkvNorm = 3, QkvX = 4, QkvEmbed = 5, QkvTokens = 6, QkvOut = 7,
+  QkvWq = 0, QkvWk = 1, QkvWv = 2, QkvNorm = 3, QkvX = 4, QkvEmbed = 5, QkvTokens = 6, QkvOut = 7, QkvPrep = 8,
+  QkvSs = 9,
   // ATTN
   AttnQkv = 0, AttnK = 1, AttnV = 2, AttnRope = 3, AttnOut = 4, AttnQn = 5, AttnKn = 6,
   // COMBINE
   CombPart = 0, CombOut = 1,
-  // OPROJ
-  OWo = 0, OIn = 1, OX = 2, OEmbed = 3, OTokens = 4, OOut = 5,
+  // OPROJ (OPrepW / OPrep / OSs: the gate/up input's norm weight, pre-split
+  // copy and chunk sums of squares, batch > 1)
+  OWo = 0, OIn = 1, OX = 2, OEmbed = 3, OTokens = 4, OOut = 5, OPrepW = 6, OPrep = 7, OSs = 8,
   // GATEUP
-  GuWg = 0, GuWu = 1, GuNorm = 2, GuIn = 3, GuOut = 4,
-  // DOWN
-  DnW = 0, DnIn = 1, DnRes = 2, DnOut = 3,
+  GuWg = 0, GuWu = 1, GuNorm = 2, GuIn = 3, GuOut = 4, GuPrep = 5, GuSs = 6,
+  // DOWN (DnPrepW / DnPrep / DnSs: the same for the next QKV or the LM head)
+  DnW = 0, DnIn = 1, DnRes = 2, DnOut = 3, DnPrepW = 4, DnPrep = 5, DnSs = 6,
   // LMHEAD
-  LmW = 0, LmNorm = 1, LmIn = 2, LmLogits = 3, LmMax = 4,
+  LmW = 0, LmNorm = 1, LmIn = 2, LmLogits = 3, LmMax = 4, LmPrep = 5, LmSs = 6,
   // ARGMAX
   AmMax = 0, AmOut = 1,
   // GLM A0: inputs x, r (bf16), norm weight, outputs r_out (bf16), norm (fp32), codes, scales
@@ -103,6 +110,10 @@ struct Consts {
   // GLM path (glm != 0): q_lora, kv_lora, rope dims, nope dims per head, QKV-A
   // outputs, gate outputs, indexer head dim, indexer-Q outputs
   int glm, ql, kl, rd, nope, na, ng, nik, niq;
+  // batch > 1: rows per stored sum of squares of the residual stream (8, 4, 2
+  // or 1; stored [K / 8][B][8 / rows]) for the QKV / LM-head input (written by
+  // down) and for gate/up's (written by O)
+  int ssg_a, ssg_f;
 };
 
 struct KArgs {
@@ -132,6 +143,28 @@ __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uin
 // power-of-two row length apart.  At B = 1 this is the plain vector.
 __device__ __forceinline__ size_t act_ix(int b, int k, int B) {
   return ((size_t)(k >> 3) * B + b) * 8 + (k & 7);
+}
+// The pre-split form of such an activation (batch > 1): per 8-element chunk
+// and sequence 32 bytes, the chunk's bf16 high parts h = bf16(v) then its low
+// parts bf16(v - h) -- the two matrix-core operands of a batched tile, so that
+// the tiles that read it convert nothing.  Byte offset of element (b, k)'s
+// high part; its low part sits 16 bytes further.
+__device__ __forceinline__ uint32_t split_off(int b, int k, int B) {
+  return (uint32_t)((((k >> 3) * B + b) * 32) + (k & 7) * 2);
+}
+// Store v in that form (16-bit stores written through to the device's
+// coherence point, like st_agent).
+__device__ __forceinline__ void st_split(const GLB void* base, int b, int k, int B, float v) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, 0x7FFFFFFF, 0x00020000);
+  const __bf16 h = (__bf16)v;
+  const __bf16 l = (__bf16)(v - (float)h);
+  const uint32_t o = split_off(b, k, B);
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), r, (int)o, 0, 16 /* sc1 */);
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, l), r, (int)o + 16, 0, 16);
 }
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN)
@@ -457,8 +490,12 @@ struct GemvIn {
   const GLB uint16_t* nw;
   const GLB uint16_t* emb;  // embedding table when the input is the token's row (xf null)
   const GLB int* tok;       // token ids [B]
+  const GLB char* xs;    // batch > 1: the input in pre-split form (act_split)
+  const GLB float* ssc;  // with xs and a fused norm: sums of squares [K / 8][B][8 / ssg]
+  int ssg;               // rows per sum
   int K;
   int n0, nrows;  // rows in segment 0, total rows
+  int norm;       // the op fuses an RMSNorm (scale applied in the epilogue)
 };
 
 // ---- activations of a GEMV tile ---------------------------------------------
@@ -723,6 +760,9 @@ __host__ __device__ inline int gemv_max_rows(int K) {
   return nc <= 1 ? 16 : nc == 2 ? 8 : 4;
 }
 
+__device__ __forceinline__ int op_sum_rows(int op, const Consts& c) {
+  return op == OpGateUp || op == OpOproj ? c.ssg_f : c.ssg_a;
+}
 __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
   GemvIn g;
   g.xf = nullptr;
@@ -730,14 +770,26 @@ __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
   g.nw = nullptr;
   g.emb = nullptr;
   g.tok = nullptr;
+  g.xs = nullptr;
+  g.ssc = nullptr;
+  g.ssg = op_sum_rows(m.w(WOpcode), c);
+  g.norm = 0;
+  const bool split = c.B > 1;  // batch > 1: inputs in pre-split form (act_split)
   const int op = m.w(WOpcode);
   switch (op) {
     case OpQkv:
       g.K = c.H;
-      g.nw = (const GLB uint16_t*)m.q(QkvNorm);
+      g.norm = 1;
       if (m.q(QkvX)) {
-        g.xf = (const GLB float*)m.q(QkvX);
+        if (split) {
+          g.xs = (const GLB char*)m.q(QkvPrep);
+          g.ssc = (const GLB float*)m.q(QkvSs);
+        } else {
+          g.xf = (const GLB float*)m.q(QkvX);
+          g.nw = (const GLB uint16_t*)m.q(QkvNorm);
+        }
       } else {
+        g.nw = (const GLB uint16_t*)m.q(QkvNorm);
         g.emb = (const GLB uint16_t*)m.q(QkvEmbed);
         g.tok = (const GLB int*)m.q(QkvTokens);
         if (c.B == 1) g.xb = g.emb + (size_t)token0(m.q(QkvTokens), c.V) * c.H;
@@ -746,25 +798,43 @@ __device__ inline GemvIn gemv_input(const Meta& m, const Consts& c) {
       break;
     case OpOproj:
       g.K = c.nq * c.hd;
-      g.xf = (const GLB float*)m.q(OIn);
+      if (split)
+        g.xs = (const GLB char*)m.q(OIn);
+      else
+        g.xf = (const GLB float*)m.q(OIn);
       g.n0 = g.nrows = m.w(WPay + 1);
       break;
     case OpGateUp:
       g.K = c.H;
-      g.nw = (const GLB uint16_t*)m.q(GuNorm);
-      g.xf = (const GLB float*)m.q(GuIn);
+      g.norm = 1;
+      if (split) {
+        g.xs = (const GLB char*)m.q(GuPrep);
+        g.ssc = (const GLB float*)m.q(GuSs);
+      } else {
+        g.nw = (const GLB uint16_t*)m.q(GuNorm);
+        g.xf = (const GLB float*)m.q(GuIn);
+      }
       g.n0 = m.w(WPay + 1);
       g.nrows = 2 * m.w(WPay + 1);
       break;
     case OpDown:
       g.K = c.F;
-      g.xf = (const GLB float*)m.q(DnIn);
+      if (split)
+        g.xs = (const GLB char*)m.q(DnIn);
+      else
+        g.xf = (const GLB float*)m.q(DnIn);
       g.n0 = g.nrows = m.w(WPay + 1);
       break;
     default:  // OpLmHead
       g.K = c.H;
-      g.nw = (const GLB uint16_t*)m.q(LmNorm);
-      g.xf = (const GLB float*)m.q(LmIn);
+      g.norm = 1;
+      if (split) {
+        g.xs = (const GLB char*)m.q(LmPrep);
+        g.ssc = (const GLB float*)m.q(LmSs);
+      } else {
+        g.nw = (const GLB uint16_t*)m.q(LmNorm);
+        g.xf = (const GLB float*)m.q(LmIn);
+      }
       g.n0 = g.nrows = m.w(WPay + 1);
       break;
   }
@@ -795,7 +865,7 @@ __device__ inline void gemv_epilogue(const Meta& m, const Consts& c,
   const int op = m.w(WOpcode);
   const GemvIn g = gemv_input(m, c);
   float scale = 1.f;
-  if (g.nw) {
+  if (g.norm) {
     float ss = 0.f;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) ss += ssp[w];
@@ -862,8 +932,13 @@ __device__ __forceinline__ bool amax_better(float v, int i, float bv, int bi) {
 // fp32 activations (times the RMSNorm weight) enter as two bf16 parts, hi =
 // bf16(x) and lo = bf16(x - hi), one MFMA each: the weight x activation
 // products keep about 16 bits of the activation, as the fp32 path does to
-// within rounding.  Rows past nrows re-read the last row, sequences past B and
-// chunks past the wave's range read valid addresses and are zeroed.
+// within rounding.  The producers store the activations already split
+// (act_split), so a k-step is two 16-byte loads straight into the MFMA
+// operands, and the fused norm's sums of squares come with the residual
+// (gemv_sumsq_mb); only layer 0's QKV, whose input is the token's bf16
+// embedding row, splits and squares in the tile.  Rows
+// past nrows re-read the last row; sequences past B and chunks past the
+// wave's range read valid addresses and are zeroed.
 // kpart / nparts: the tile's K range is cut into nparts equal parts (K / 8 a
 // multiple of nparts) and this call runs part kpart; a part after the first
 // adds its sums to the ones already in part / ssp (the earlier parts', written
@@ -881,45 +956,47 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
   const int arow = rr * K * 2;
   const int b = lane & 15;
   const bool bok = b < B;
-  const GLB uint16_t* xb = nullptr;
-  if (EMB) xb = gi.emb + (size_t)token_of(gi.tok, bok ? b : 0, V) * K;
   const int bb = bok ? b : 0;
-  const CohT<POL> cx(EMB ? (const GLB void*)gi.emb : (const GLB void*)gi.xf);
+  const GLB uint16_t* xb = nullptr;
+  if (EMB) xb = gi.emb + (size_t)token_of(gi.tok, bb, V) * K;
+  const CohT<POL> cx(EMB ? (const GLB void*)gi.emb : (const GLB void*)gi.xs);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
   constexpr int NB = 4;  // k-steps whose loads are issued together
   for (int ks0 = 0; ks0 < nks; ks0 += NB) {
-    u32x4 A[NB], xr[NB], wn[NB];
-    f32x4 x0[NB], x1[NB];
+    u32x4 A[NB], xr[NB], wn[NB], xh[NB], xl[NB];
     bool ok[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int ks = ks0 + u, ch = ks * 4 + q;
       ok[u] = ks < nks && ch < cpw && base + ch < c0 + nch;
-      const int kk = (ok[u] ? base + ch : 0) * 8;
+      const int chunk = ok[u] ? base + ch : 0, kk = chunk * 8;
       const uint4 w = src.ld16(seg, arow + kk * 2);
       A[u] = u32x4{w.x, w.y, w.z, w.w};
       if (EMB) {
         xr[u] = *(const GLB u32x4*)(xb + kk);
+        if (gi.nw) wn[u] = *(const GLB u32x4*)(gi.nw + kk);
       } else {
-        const uint32_t xo = (uint32_t)act_ix(bb, kk, B) * 4;  // chunk kk of sequence b (act_ix)
-        x0[u] = cx.f4(xo);
-        x1[u] = cx.f4(xo + 16);
+        const uint32_t xo = (uint32_t)((chunk * B + bb) * 32);  // split_off(bb, kk, B)
+        xh[u] = cx.u4(xo);
+        xl[u] = cx.u4(xo + 16);
+
       }
-      if (gi.nw) wn[u] = *(const GLB u32x4*)(gi.nw + kk);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      float v[8];
-      if (EMB) {
-        v[0] = bf16lo(xr[u].x); v[1] = bf16hi(xr[u].x); v[2] = bf16lo(xr[u].y); v[3] = bf16hi(xr[u].y);
-        v[4] = bf16lo(xr[u].z); v[5] = bf16hi(xr[u].z); v[6] = bf16lo(xr[u].w); v[7] = bf16hi(xr[u].w);
-      } else {
-        v[0] = x0[u].x; v[1] = x0[u].y; v[2] = x0[u].z; v[3] = x0[u].w;
-        v[4] = x1[u].x; v[5] = x1[u].y; v[6] = x1[u].z; v[7] = x1[u].w;
-      }
       const bool live = ok[u] && bok;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, A[u]);
+      if (!EMB) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, live ? xh[u] : z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, live ? xl[u] : z), acc, 0, 0, 0);
+        continue;
+      }
+      float v[8];
+      v[0] = bf16lo(xr[u].x); v[1] = bf16hi(xr[u].x); v[2] = bf16lo(xr[u].y); v[3] = bf16hi(xr[u].y);
+      v[4] = bf16lo(xr[u].z); v[5] = bf16hi(xr[u].z); v[6] = bf16lo(xr[u].w); v[7] = bf16hi(xr[u].w);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         v[e] = live ? v[e] : 0.f;
@@ -936,7 +1013,6 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
         hi[e] = h;
         lo[e] = (__bf16)(v[e] - (float)h);
       }
-      const bf16x8 av = __builtin_bit_cast(bf16x8, A[u]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hi, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lo, acc, 0, 0, 0);
     }
@@ -959,7 +1035,7 @@ __device__ inline void gemv_tile_mb(const Src& src, const GemvIn& gi, int B, int
 template <int POL = 0, class Src, class Rel>
 __device__ inline void gemv_rows_mb(const Src& src, const GemvIn& gi, int B, int V, int cw, LDS float* part,
                                     LDS float* ssp, const Rel& rel, int kpart = 0, int nparts = 1) {
-  if (gi.xf)
+  if (gi.xs)
     gemv_tile_mb<false, POL>(src, gi, B, V, cw, part, ssp, rel, kpart, nparts);
   else
     gemv_tile_mb<true, POL>(src, gi, B, V, cw, part, ssp, rel, kpart, nparts);
@@ -976,45 +1052,132 @@ __device__ __forceinline__ bool gemv_k_halves(int op, const Consts& c) {
   return K > 0 && K % 16 == 0;
 }
 
-// Residual inputs of the four (row, sequence) outputs lane l owns in the batched
-// epilogue: index idx = l + 64 j, row idx / 16, sequence idx % 16 = l % 16.
+// Batched O-projection, gate/up and down tiles whose output rows are whole
+// 8-row chunks (row0 and the row count multiples of 8) run a chunk-wise
+// epilogue: lane (chunk l / 16, sequence l % 16) owns the chunk's 8 outputs, so
+// the residual, the stored residual stream, the norm weight and the split
+// copy move as 16-byte vectors.  Other tiles (row counts not a multiple of 8)
+// keep the element-wise one.
+__device__ __forceinline__ bool mb_chunk_tile(const Meta& m, const Consts& c) {
+  const int op = m.w(WOpcode);
+  // (O and down keep their sums of squares per chunk only when every tile of
+  // the op has whole chunks)
+  return (op == OpGateUp || ((op == OpOproj || op == OpDown) && op_sum_rows(op, c) == 8)) && (m.w(WPay) & 7) == 0 &&
+         (m.w(WPay + 1) & 7) == 0;
+}
+struct ResMB {
+  f32x4 r0, r1;  // chunk-wise: the chunk's 8 residuals; element-wise: r0 = the lane's 4
+  float ss;      // pre-split input with a fused norm: sequence lane % 16's sum of squares
+};
+// Residual inputs of the batched epilogue, loaded before the tile's partial
+// sums are in (element-wise: lane l owns index idx = l + 64 j, row idx / 16,
+// sequence idx % 16 = l % 16).
 template <int POL = 0>
-__device__ inline f32x4 gemv_residual_mb(const Meta& m, const Consts& c) {
+__device__ inline ResMB gemv_residual_mb(const Meta& m, const Consts& c) {
   const int lane = lane_id();
   const int op = m.w(WOpcode);
-  f32x4 r = {0.f, 0.f, 0.f, 0.f};
+  ResMB r;
+  r.r0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  r.r1 = r.r0;
+  r.ss = 0.f;
   if (op != OpOproj && op != OpDown) return r;
   const int row0 = m.w(WPay), nr = m.w(WPay + 1);
   const int b = lane & 15, bb = b < c.B ? b : 0;
+  if (mb_chunk_tile(m, c)) {
+    const int cl = (lane >> 4) < (nr >> 3) ? (lane >> 4) : 0;
+    const int k = row0 + 8 * cl;
+    if (op == OpOproj && !m.q(OX)) {
+      const u32x4 e = *(const GLB u32x4*)((const GLB uint16_t*)m.q(OEmbed) +
+                                          (size_t)token_of((const GLB int*)m.q(OTokens), bb, c.V) * c.H + k);
+      r.r0 = f32x4{bf16lo(e.x), bf16hi(e.x), bf16lo(e.y), bf16hi(e.y)};
+      r.r1 = f32x4{bf16lo(e.z), bf16hi(e.z), bf16lo(e.w), bf16hi(e.w)};
+    } else {
+      const CohT<POL> cx((const GLB float*)m.q(op == OpOproj ? OX : DnRes));
+      const uint32_t o = (uint32_t)act_ix(bb, k, c.B) * 4;
+      r.r0 = cx.f4(o);
+      r.r1 = cx.f4(o + 16);
+    }
+    return r;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = (lane + 64 * j) >> 4;
     const int rr = row0 + (row < nr ? row : 0);
     if (op == OpOproj) {
-      r[j] = m.q(OX) ? CohT<POL>((const GLB float*)m.q(OX)).f1((uint32_t)act_ix(bb, rr, c.B) * 4)
-                     : bf16f(((const GLB uint16_t*)m.q(OEmbed))[(size_t)token_of((const GLB int*)m.q(OTokens), bb, c.V) *
-                                                                  c.H + rr]);
+      r.r0[j] = m.q(OX) ? CohT<POL>((const GLB float*)m.q(OX)).f1((uint32_t)act_ix(bb, rr, c.B) * 4)
+                        : bf16f(((const GLB uint16_t*)m.q(OEmbed))[(size_t)token_of((const GLB int*)m.q(OTokens), bb,
+                                                                                     c.V) * c.H + rr]);
     } else {
-      r[j] = CohT<POL>((const GLB float*)m.q(DnRes)).f1((uint32_t)act_ix(bb, rr, c.B) * 4);
+      r.r0[j] = CohT<POL>((const GLB float*)m.q(DnRes)).f1((uint32_t)act_ix(bb, rr, c.B) * 4);
     }
   }
   return r;
 }
 
+// Batch > 1, a fused norm over a pre-split input: the input's sum of squares
+// for sequence lane % 16, from the producers' sums over groups of ssg rows
+// ([b][H / ssg]).  Lane (b, p = lane / 16) adds the p-th quarter in order,
+// then the quarters are added (fixed order, the same in every kernel).
+// Returns 0 for other ops.
+template <int POL = 0>
+__device__ inline float gemv_sumsq_mb(const Meta& m, const Consts& c) {
+  const GemvIn g = gemv_input(m, c);
+  if (!g.norm || !g.xs) return 0.f;
+  const int lane = lane_id();
+  const int b = lane & 15, bb = b < c.B ? b : 0, p = lane >> 4;
+  const int n = c.H / g.ssg, per = (n + 3) / 4;  // sums per sequence, per lane
+  const CohT<POL> cs((const GLB void*)g.ssc);
+  float t = 0.f;
+  const int i0 = p * per;
+  if (n % 16 == 0) {  // quarters of whole 16-byte runs, eight loads in flight
+    for (int i = 0; i < per; i += 32) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = i + 4 * u < per ? cs.f4((uint32_t)(bb * n + i0 + i + 4 * u) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t += ((v[u].x + v[u].y) + (v[u].z + v[u].w));
+    }
+  } else {
+    for (int i = 0; i < per && i0 + i < n; ++i) t += cs.f1((uint32_t)(bb * n + i0 + i) * 4);
+  }
+  t += __shfl_xor(t, 16, 64);
+  t += __shfl_xor(t, 32, 64);
+  return t;
+}
+
+// 16 bytes from 8 floats' bf16 high parts (hi) or low parts (lo = bf16(v - h))
+__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 t = (__bf16)v[e];
+    h[e] = t;
+    l[e] = (__bf16)(v[e] - (float)t);
+  }
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, l);
+}
+
 // Epilogue of a batched GEMV tile: part[w * 256 + row * 16 + b] are wave w's
 // partial sums, ssp[w * 16 + b] its sums of squares of sequence b.
 __device__ inline void gemv_epilogue_mb(const Meta& m, const Consts& c, const LDS float* part, const LDS float* ssp,
-                                        f32x4 res) {
+                                        ResMB rs) {
+  const f32x4 res = rs.r0;
   const int lane = lane_id();
   const int op = m.w(WOpcode);
   const GemvIn g = gemv_input(m, c);
   const int b = lane & 15;
   const bool bok = b < c.B;
   float scale = 1.f;
-  if (g.nw) {
+  if (g.norm) {
     float ss = 0.f;
+    if (g.xs) {
+      ss = rs.ss;  // from the producers' sums (gemv_sumsq_mb)
+    } else {
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) ss += ssp[w * kMB + b];
+      for (int w = 0; w < kNW; ++w) ss += ssp[w * kMB + b];
+    }
     scale = 1.f / sqrtf(ss / (float)g.K + c.eps);
   }
   const int row0 = m.w(WPay), nr = m.w(WPay + 1);
@@ -1024,27 +1187,86 @@ __device__ inline void gemv_epilogue_mb(const Meta& m, const Consts& c, const LD
     for (int w = 0; w < kNW; ++w) v += part[w * kMB * kMB + row * kMB + b];
     return v * scale;
   };
+  if (mb_chunk_tile(m, c)) {
+    // lane (chunk cl, sequence b); stores through buffer resources with
+    // sc1 (st_agent16), everything 16 bytes per lane
+    const int cl = lane >> 4;
+    if (cl >= (nr >> 3) || !bok) return;
+    const int r0 = 8 * cl, k = row0 + r0;
+    const uint32_t so = split_off(b, k, c.B);
+    float x[8];
+    if (op == OpGateUp) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gt = val(r0 + e), up = val(nr + r0 + e);  // up row j sits at tile row nr + j
+        x[e] = gt / (1.f + __expf(-gt)) * up;
+      }
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      st_agent16((const GLB void*)m.q(GuOut), so, __builtin_bit_cast(f32x4, hi));
+      st_agent16((const GLB void*)m.q(GuOut), so + 16, __builtin_bit_cast(f32x4, lo));
+      return;
+    }
+    // O projection / down: x = residual + W a, stored as is; x times the next
+    // op's norm weight, split; the chunk's sum of squares of x
+    const u32x4 wq = *(const GLB u32x4*)((const GLB uint16_t*)m.q(op == OpOproj ? OPrepW : DnPrepW) + k);
+    const float w8[8] = {bf16lo(wq.x), bf16hi(wq.x), bf16lo(wq.y), bf16hi(wq.y),
+                         bf16lo(wq.z), bf16hi(wq.z), bf16lo(wq.w), bf16hi(wq.w)};
+    const float rv[8] = {rs.r0.x, rs.r0.y, rs.r0.z, rs.r0.w, rs.r1.x, rs.r1.y, rs.r1.z, rs.r1.w};
+    float y[8], sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = rv[e] + val(r0 + e);
+      y[e] = x[e] * w8[e];
+      sq = fmaf(x[e], x[e], sq);
+    }
+    const uint32_t xo = (uint32_t)act_ix(b, k, c.B) * 4;
+    const GLB void* xout = (const GLB void*)m.q(op == OpOproj ? OOut : DnOut);
+    st_agent16(xout, xo, f32x4{x[0], x[1], x[2], x[3]});
+    st_agent16(xout, xo + 16, f32x4{x[4], x[5], x[6], x[7]});
+    u32x4 hi, lo;
+    split8(y, hi, lo);
+    const GLB void* xs = (const GLB void*)m.q(op == OpOproj ? OPrep : DnPrep);
+    st_agent16(xs, so, __builtin_bit_cast(f32x4, hi));
+    st_agent16(xs, so + 16, __builtin_bit_cast(f32x4, lo));
+    // one sum per chunk (the row counts are multiples of 8, so the sums are
+    // kept per chunk: [B][H / 8])
+    st_agent((GLB float*)m.q(op == OpOproj ? OSs : DnSs) + (size_t)b * (c.H / 8) + (k >> 3), sq);
+    return;
+  }
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
+  // O projection and down: the residual stream x is stored as is, and again
+  // split and times the next op's RMSNorm weight (gate/up's; the next layer's
+  // QKV or the LM head's) with its sums of squares over groups of rows, which
+  // the next op's tiles add instead of squaring x themselves.
+  const bool resid = op == OpOproj || op == OpDown;
+  const GLB uint16_t* wnext = resid ? (const GLB uint16_t*)m.q(op == OpOproj ? OPrepW : DnPrepW) : nullptr;
+  const GLB void* xsplit = resid ? (const GLB void*)m.q(op == OpOproj ? OPrep : DnPrep) : nullptr;
+  float sq[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = (lane + 64 * j) >> 4;
     const bool live = bok && row < nr;
+    sq[j] = 0.f;
     switch (op) {
       case OpQkv:
         if (live) st_agent((GLB float*)m.q(QkvOut) + ((size_t)b * c.nkv + m.w(WGx)) * c.RPG + row0 + row, val(row));
         break;
       case OpOproj:
-        if (live) st_agent((GLB float*)m.q(OOut) + act_ix(b, row0 + row, c.B), res[j] + val(row));
+      case OpDown:
+        if (live) {
+          const float x = res[j] + val(row);
+          st_agent((GLB float*)m.q(op == OpOproj ? OOut : DnOut) + act_ix(b, row0 + row, c.B), x);
+          st_split(xsplit, b, row0 + row, c.B, x * bf16f(wnext[row0 + row]));
+          sq[j] = x * x;
+        }
         break;
       case OpGateUp:
         if (live) {
           const float gt = val(row), up = val(nr + row);  // up row j sits at tile row nr + j
-          st_agent((GLB float*)m.q(GuOut) + act_ix(b, row0 + row, c.B), gt / (1.f + __expf(-gt)) * up);
+          st_split((const GLB void*)m.q(GuOut), b, row0 + row, c.B, gt / (1.f + __expf(-gt)) * up);
         }
-        break;
-      case OpDown:
-        if (live) st_agent((GLB float*)m.q(DnOut) + act_ix(b, row0 + row, c.B), res[j] + val(row));
         break;
       case OpLmHead:
         if (live) {
@@ -1058,6 +1280,47 @@ __device__ inline void gemv_epilogue_mb(const Meta& m, const Consts& c, const LD
         break;
       default:
         break;
+    }
+  }
+  if (resid) {
+    // sums of squares of x over groups of g rows (g divides the tile rows, so
+    // row0 starts a group), stored [b][H / g].  Lane
+    // (b, q = lane / 16) holds rows q + 4 j; lanes b, b+16, b+32, b+48 hold
+    // sequence b's rows.
+    const int g = op_sum_rows(op, c);
+    GLB float* ssc = (GLB float*)m.q(op == OpOproj ? OSs : DnSs);
+    const int q = lane >> 4;
+    auto put = [&](int grp, float v) {  // grp: the group's first row within the tile
+      st_agent(ssc + (size_t)b * (c.H / g) + (row0 + grp) / g, v);
+    };
+    if (g == 8) {
+      float p0 = sq[0] + sq[1], p1 = sq[2] + sq[3];  // rows 0..7, 8..15
+      p0 += __shfl_xor(p0, 16, 64);
+      p1 += __shfl_xor(p1, 16, 64);
+      p0 += __shfl_xor(p0, 32, 64);
+      p1 += __shfl_xor(p1, 32, 64);
+      if (q == 0 && bok) {
+        put(0, p0);
+        if (nr > 8) put(8, p1);
+      }
+    } else if (g == 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // rows 4 j .. 4 j + 3
+        float t = sq[j];
+        t += __shfl_xor(t, 16, 64);
+        t += __shfl_xor(t, 32, 64);
+        if (q == 0 && bok && 4 * j < nr) put(4 * j, t);
+      }
+    } else if (g == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // rows q + 4 j and q + 1 + 4 j, q even
+        const float t = sq[j] + __shfl_xor(sq[j], 16, 64);
+        if ((q & 1) == 0 && bok && q + 4 * j < nr) put(q + 4 * j, t);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (bok && q + 4 * j < nr) put(q + 4 * j, sq[j]);
     }
   }
   if (op == OpLmHead) {
@@ -1384,8 +1647,32 @@ __device__ inline void combine_wave(const Meta& m, const Consts& c, int cw,
   }
   GLB float* out = (GLB float*)m.q(CombOut);
   const int k0 = (g * c.hpg + cw) * HD;
+  if (c.B == 1) {
 #pragma unroll
-  for (int k = 0; k < PER; ++k) st_agent(out + act_ix(b, k0 + lane + 64 * k, c.B), o[k] / L);
+    for (int k = 0; k < PER; ++k) st_agent(out + k0 + lane + 64 * k, o[k] / L);
+    return;
+  }
+  // batch > 1: split for the O projection's tiles; lane ch < HD / 8 gathers
+  // chunk ch (elements 8 ch .. 8 ch + 7, held by lanes 8 ch % 64 + e of o[8 ch / 64])
+  float v[8];
+  const int ch = lane < HD / 8 ? lane : 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const float s2 = __shfl(o[k], (8 * ch) % 64 + e, 64);
+      if ((8 * ch) / 64 == k) t = s2;
+    }
+    v[e] = t / L;
+  }
+  if (lane < HD / 8) {
+    u32x4 hi, lo;
+    split8(v, hi, lo);
+    const uint32_t so = split_off(b, k0 + 8 * ch, c.B);
+    st_agent16((const GLB void*)out, so, __builtin_bit_cast(f32x4, hi));
+    st_agent16((const GLB void*)out, so + 16, __builtin_bit_cast(f32x4, lo));
+  }
 }
 
 // Reduce the LM-head tile maxima of sequence b in tile order, lowest index on

@@ -284,6 +284,8 @@ template <class LT>
 __device__ void storer(const KArgs& a, LDS LT* L) {
   const int lane = lane_id();
   unsigned pending = 0;
+  int ss_row = -1;     // batched: operand row whose sums of squares ss_val holds
+  float ss_val = 0.f;
   for (int i = 0; i < a.max_len; ++i) {
     // the residual may be read only once the instruction's event has been
     // acquired (the controller publishes "ready" after its acquire)
@@ -298,7 +300,16 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
       if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
       if (glm_is_gemm(op)) glm_epilogue(m, a.c, &L->c.part[sl][0][0]);
     } else if constexpr (LT::MB) {
-      const f32x4 res = gemv_residual_mb(m, a.c);
+      ResMB res = gemv_residual_mb(m, a.c);
+      // the fused norm's sum of squares: the same for every tile of an op
+      // (consecutive tiles of the LM head, gate/up, ... reuse it)
+      if (gemv) {
+        if (m.w(WOpRow) != ss_row) {
+          ss_val = gemv_sumsq_mb(m, a.c);
+          ss_row = m.w(WOpRow);
+        }
+        res.ss = ss_val;
+      }
       // a K-halved tile is complete once both groups have arrived
       const int arrivals = (LT::SETS > 1 && gemv_k_halves(op, a.c)) ? 2 * kNW : kNW;
       if (!wait_lds_ge(a, L, &L->c.arrive[sl], arrivals, ErrDrain, i)) return;
@@ -753,7 +764,11 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
         gemv_rows_mb<0>(src, gi, a.c.B, a.c.V, cw, part[cw], ssp[cw], [] {});
       }
       __syncthreads();
-      if (cw == 0) gemv_epilogue_mb(m, a.c, &part[0][0], &ssp[0][0], gemv_residual_mb<0>(m, a.c));
+      if (cw == 0) {
+        ResMB res = gemv_residual_mb<0>(m, a.c);
+        res.ss = gemv_sumsq_mb<0>(m, a.c);
+        gemv_epilogue_mb(m, a.c, &part[0][0], &ssp[0][0], res);
+      }
     } else {
       Act act;
       gemv_rows<0>(src, act, gi, cw, part[cw], [] {}, [] { return true; });
