@@ -263,11 +263,14 @@ def test_gpu_qwen3_8b_full_size():
     ("b16", "tiny", dict(batch=16, kv_len=(100, 300), seed=12)),
     ("b5_qwen", "tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128, batch=5, kv_len=(1, 90), seed=13)),
     ("b6_ragged", "tiny", dict(batch=6, kv_len=(1, 120), seed=15, opts=dict(down_rows=6, gateup_outs=3))),
+    ("b4_odd", "tiny", dict(batch=4, kv_len=(3, 77), seed=17, opts=dict(gemv_rows=4, down_rows=5, gateup_outs=3))),
 ])
 def test_gpu_batched(key, name, overrides):
     """Batch 2..16 (matrix-core GEMV tiles, per-sequence attention lengths):
     megakernel and layerwise against the oracle, every sequence's argmax.
-    b6_ragged: down and gate/up tiles whose row counts leave a short last tile."""
+    b6_ragged: down and gate/up tiles whose row counts leave a short last tile
+    (the residual stream's sums of squares kept per 2 rows); b4_odd: O and down
+    tiles of 4 and 5 rows (sums per 4 rows and per row, element-wise epilogues)."""
     c = case(key, name, **overrides)
     r = c.run()
     c.assert_parity(r)
