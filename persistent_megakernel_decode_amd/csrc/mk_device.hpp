@@ -21,6 +21,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 namespace mkd {
@@ -1353,9 +1354,16 @@ __device__ __forceinline__ bool is_gemv(int op) {
 // Every global input is loaded in one batch up front; the RoPE partner of
 // element d (d +- head_dim/2) is in the same lane for head_dim 128 and in
 // lane ^ 32 for head_dim 64.
-template <int HD, int POL = 0, class Src>
-__device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c, int cw,
-                                 LDS float* scr, bool writer, unsigned long long* tr = nullptr) {
+// The attention task's prologue, the same for every attention kernel: the
+// wave's q head (cw; head 0 for waves past the group's heads) rotated into
+// scr[0, HD), the new K/V row (when the split holds it) as bf16 in scr after
+// it, written to the cache by the writer wave.  Returns the task's positions.
+struct AttnTask {
+  int b, g, s, lo, hi, pos, nk;
+  bool has_new, active;
+};
+template <int HD, int POL = 0>
+__device__ inline AttnTask attn_prologue(const Meta& mt, const Consts& c, int cw, LDS float* scr, bool writer) {
   const int lane = lane_id();
   const int b = mt.w(WGx), g = mt.w(WGy), s = mt.w(WGz);
   const int lo = mt.w(WPay), hi = mt.w(WPay + 1), pos = mt.w(WPay + 2);
@@ -1441,6 +1449,20 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  return AttnTask{b, g, s, lo, hi, pos, nk, has_new, active};
+}
+
+template <int HD, int POL = 0, class Src>
+__device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c, int cw,
+                                 LDS float* scr, bool writer, unsigned long long* tr = nullptr) {
+  const int lane = lane_id();
+  const AttnTask at = attn_prologue<HD, POL>(mt, c, cw, scr, writer);
+  const int b = at.b, g = at.g, s = at.s, nk = at.nk;
+  const bool has_new = at.has_new, active = at.active;
+  LDS float* qs = scr;                               // rotated q, HD floats
+  LDS uint16_t* kn = (LDS uint16_t*)(scr + HD);      // new k row (bf16), HD
+  LDS uint16_t* vn = (LDS uint16_t*)(scr + 2 * HD);  // new v row (bf16), HD
+  constexpr int PER = HD / 64;
   if (tr && lane == 0) tr[6] = now_ticks();
   if (!active) return;
   const int n = nk + (has_new ? 1 : 0);
@@ -1595,6 +1617,230 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   if (gi == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) st_agent(outp + 2 + cidx * 8 + e, o[e]);
+  }
+  if (tr && lane == 0) tr[7] = now_ticks();
+}
+
+// Batched attention, head_dim 64, on the matrix cores: the four compute waves
+// of the group take a quarter of the split's positions each, for every query
+// head of the kv group at once, in steps of 32 positions:
+//   scores  S = K q^T with v_mfma_f32_16x16x32_bf16 per 16 positions: A = the
+//           K rows (lane l: position l % 16, dims 8 (l / 16) .. +7, one 16-byte
+//           LDS read), B = q^T (lane l: head l % 16, the same dims; heads past
+//           the group's are zero; q as bf16 high and low parts, two MFMAs), so
+//           lane (head h = l % 16, g = l / 16) holds h's scores of positions
+//           4 g .. 4 g + 3;
+//   softmax online per head (running max and sum; the four lanes of a head
+//           combine by row swaps);
+//   P V     O += P V per 16 head dims: A = P (lane l: head l % 16, positions
+//           8 (l / 16) .. +7: the score layout of two 16-position blocks
+//           regrouped by one permlane32 and one permlane16 swap; P as bf16
+//           high and low parts, two MFMAs), B = V (lane l: dim l % 16, the same
+//           positions, two ds_read_b64_tr_b16 of the position-major V rows).
+// The new K/V row (scratch of each wave) is read instead of the ring for its
+// position.  The waves then exchange their per-head (max, sum, O) through the
+// instruction's partial-sum slot (xarea, 12 x 66 floats: wave w's partials of
+// heads h != w) and wave h merges head h's four and stores the split partial.
+// sync(k): the group's k-th rendezvous (all four waves past it).
+template <int POL = 0, class Src, class Sync>
+__device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts& c, int cw, LDS float* gscr,
+                                   LDS float* xarea, bool writer, const Sync& sync,
+                                   unsigned long long* tr = nullptr) {
+  constexpr int HD = 64;
+  const int lane = lane_id();
+  LDS float* scr = gscr + cw * kScratch;
+  const AttnTask at = attn_prologue<HD, POL>(mt, c, cw, scr, writer);
+  const int nk = at.nk, hpg = c.hpg;
+  const int n = nk + (at.has_new ? 1 : 0);
+  const LDS uint16_t* kn = (const LDS uint16_t*)(scr + HD);
+  const LDS uint16_t* vn = (const LDS uint16_t*)(scr + 2 * HD);
+  sync(1);  // every wave's rotated q is in its scratch
+  if (tr && lane == 0) tr[6] = now_ticks();
+  const int hq = lane & 15, gq = lane >> 4;
+  // B operands of the scores: q^T, head hq, dims 32 kb + 8 gq .. +7
+  bf16x8 qh[2], ql[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = hq < hpg ? gscr[hq * kScratch + 32 * kb + 8 * gq + e] : 0.f;
+      const __bf16 h = (__bf16)v;
+      qh[kb][e] = h;
+      ql[kb][e] = (__bf16)(v - (float)h);
+    }
+  }
+  // this wave's positions [p0, p1): quarters rounded up to 16
+  const int q4 = ((n + 3) / 4 + 15) & ~15;
+  const int p0 = cw * q4, p1 = n < p0 + q4 ? n : p0 + q4;
+  float m_run = -INFINITY, l_run = 0.f;  // head hq's, in lanes (hq, any gq)
+  f32x4 O[4];                            // O[db]: lane l: dim 16 db + l % 16, heads 4 (l / 16) + j
+#pragma unroll
+  for (int db = 0; db < 4; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto other16 = [&](float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  };
+  auto other32 = [&](float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  };
+  // the position whose K / V row a lane reads: cached rows from the ring, the
+  // new row from the scratch, anything past the split's end clamped to a row
+  // that holds finite values (its weight is zero)
+  const int last = nk > 0 ? nk - 1 : 0;
+  for (int s0 = p0; s0 < p1; s0 += 32) {
+    f32x4 S[2];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      const int pp = s0 + 16 * bk + hq;  // A row: position
+      const bool newrow = at.has_new && pp == nk;
+      const int pr = pp < nk ? pp : last;
+      S[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 kr = src.ld16(0, pr * HD * 2 + (32 * kb + 8 * gq) * 2);
+        const u32x4 kw = *(const LDS u32x4*)(kn + 32 * kb + 8 * gq);
+        const u32x4 ka = newrow || nk == 0 ? kw : u32x4{kr.x, kr.y, kr.z, kr.w};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ka);
+        S[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kb], S[bk], 0, 0, 0);
+        S[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kb], S[bk], 0, 0, 0);
+      }
+    }
+    // scores of lane (hq, gq): positions s0 + 16 bk + 4 gq + j
+    float sc[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pp = s0 + 16 * bk + 4 * gq + j;
+        sc[bk][j] = pp < p1 ? S[bk][j] * c.inv_sqrt_hd : -INFINITY;
+        mx = fmaxf(mx, sc[bk][j]);
+      }
+    mx = fmaxf(mx, other16(mx));
+    mx = fmaxf(mx, other32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float base = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __expf(m_run - base);  // 0 when m_run = -inf
+    float P[2][4], rs = 0.f;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        P[bk][j] = __expf(sc[bk][j] - base);  // 0 for masked positions
+        rs += P[bk][j];
+      }
+    rs += other16(rs);
+    rs += other32(rs);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    // rescale O: row j of every block holds head 4 (l / 16) + j; head j's
+    // factor sits in lane j (head j, group 0)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float aj = readlane_f(alpha, j);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) O[db][j] *= aj;
+    }
+    // regroup P into the A layout: lane (h, g) gets positions 8 g .. 8 g + 7
+    float pa[4], pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(P[0][j]), __float_as_uint(P[1][j]), false, false);
+      const auto r16 = __builtin_amdgcn_permlane16_swap(r32[0], r32[1], false, false);
+      pa[j] = __uint_as_float(r16[0]);
+      pb[j] = __uint_as_float(r16[1]);
+    }
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = e < 4 ? pa[e] : pb[e - 4];
+      const __bf16 h = (__bf16)v;
+      ph[e] = h;
+      pl[e] = (__bf16)(v - (float)h);
+    }
+    // V: lane L = 16 g + 4 r + cc addresses row s0 + 8 g + 4 half + r, dims
+    // 16 db + 4 cc .. +3; the transposed read hands lane (g, q) the 4 rows'
+    // dim 16 db + q
+    const int rg = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      bf16x4 vh[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int pp = s0 + 8 * rg + 4 * half + rr;
+        const bool newrow = at.has_new && pp == nk;
+        const int pr = pp < nk ? pp : last;
+        const uint32_t ring = src.addr(1, (uint32_t)(pr * HD * 2 + (16 * db + 4 * cc) * 2));
+        const uint32_t own = (uint32_t)(uintptr_t)(vn + 16 * db + 4 * cc);
+        const uint32_t ad = newrow || nk == 0 ? own : ring;
+        vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(uintptr_t)ad);
+      }
+      bf16x8 vb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vb[e] = vh[0][e];
+        vb[4 + e] = vh[1][e];
+      }
+      O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, O[db], 0, 0, 0);
+      O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, O[db], 0, 0, 0);
+    }
+  }
+  // exchange: wave w's (max, sum, O) of head h != w at slot w * 3 + (h < w ? h : h - 1)
+  auto slot = [&](int w, int h) { return xarea + (w * 3 + (h < w ? h : h - 1)) * (HD + 2); };
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if (h >= hpg || h == cw) continue;
+    LDS float* xs = slot(cw, h);
+    const float mh = readlane_f(m_run, h), lh = readlane_f(l_run, h);
+    if (lane == 0) {
+      xs[0] = mh;
+      xs[1] = lh;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) xs[2 + 16 * db + lane] = O[db][h];
+    }
+  }
+  sync(2);  // every wave's partials are in the slot
+  if (cw >= hpg) return;
+  // head cw: merge the four quarters (own registers + three slots), then store
+  const float mo = readlane_f(m_run, cw), lo_ = readlane_f(l_run, cw);
+  float mw[4], lw[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w == cw) {
+      mw[w] = mo;
+      lw[w] = lo_;
+    } else {
+      const LDS float* xs = slot(w, cw);
+      mw[w] = xs[0];
+      lw[w] = xs[1];
+    }
+  }
+  const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+  float aw[4], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    aw[w] = (mw[w] == -INFINITY) ? 0.f : __expf(mw[w] - M);
+    L += aw[w] * lw[w];
+  }
+  GLB float* outp = (GLB float*)mt.q(AttnOut) + ((((size_t)at.b * c.nkv + at.g) * c.S + at.s) * c.hpg + cw) * (HD + 2);
+  if (lane == 0) {
+    st_agent(outp, M);
+    st_agent(outp + 1, L);
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float ow = (w == cw) ? O[db][cw] : slot(w, cw)[2 + 16 * db + lane];
+        o += aw[w] * ow;
+      }
+      st_agent(outp + 2 + 16 * db + lane, o);
+    }
   }
   if (tr && lane == 0) tr[7] = now_ticks();
 }

@@ -653,7 +653,19 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
           gemv_rows_mb(src, gi, a.c.B, a.c.V, cw, pw, sw, release);
         }
       } else if (op == OpAttn) {
-        attn_wave<HD>(src, m, a.c, cw, L->c.scratch[set * kNW + cw], cw == 0, cw == 0 ? tr : nullptr);
+        if constexpr (LT::MB && HD == 64) {
+          // the group's rendezvous: all four compute waves past point k
+          bool live = true;
+          auto sync = [&](int k) {
+            if (lane == 0) __hip_atomic_fetch_add(&L->c.xch[sl], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (!wait_lds_ge(a, L, &L->c.xch[sl], k * kNW, ErrReady, i)) live = false;
+          };
+          attn_mfma64(src, m, a.c, cw, &L->c.scratch[set * kNW][0], &L->c.part[sl][0][0], cw == 0, sync,
+                      cw == 0 ? tr : nullptr);
+          if (!live) return;
+        } else {
+          attn_wave<HD>(src, m, a.c, cw, L->c.scratch[set * kNW + cw], cw == 0, cw == 0 ? tr : nullptr);
+        }
       } else if (op == OpCombine) {
         combine_wave<HD>(m, a.c, cw, cw == 0 ? tr : nullptr);
       } else if (op == OpArgmax) {
@@ -777,6 +789,8 @@ __global__ void __launch_bounds__(256) mk_layer_kernel(KArgs a, int num_cus, int
       if (cw == 0) gemv_epilogue(m, a.c, part, &ssp[0][0], gemv_residual<0>(m, a.c));
     }
   } else if (op == OpAttn) {
+    // (the batched megakernel runs its attention on the matrix cores; here the
+    // vector form, which suits tasks read in place from device memory)
     attn_wave<HD, 0>(src, m, a.c, cw, scr[cw], cw == 0);
   } else if (op == OpCombine) {
     combine_wave<HD, 0>(m, a.c, cw);

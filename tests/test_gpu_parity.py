@@ -134,6 +134,23 @@ class Case:
 _cases = {}
 
 
+def assert_layerwise_consistent(cfg, lw, r):
+    """The layer-by-layer kernels run the megakernel's tile functions in the
+    same order, so their logits are bit-identical -- except at batch > 1 with
+    head_dim 64, where the megakernel's attention runs on the matrix cores
+    (the same mathematics, another rounding order) and the layerwise kernel's
+    on the vector units: there the two agree to well inside the parity bar,
+    with the same argmax (both are also checked against the oracle)."""
+    if cfg["batch"] == 1 or cfg["head_dim"] != 64:
+        assert np.array_equal(lw["logits"], r["logits"])
+        return
+    g, o = lw["logits"], r["logits"]
+    rel = np.linalg.norm(g - o) / np.linalg.norm(o)
+    print("  layerwise vs megakernel logits rel-L2 %.3g" % rel, flush=True)
+    assert rel <= 1e-4
+    assert np.array_equal(np.argmax(g, axis=1), np.argmax(o, axis=1))
+
+
 def case(key, *a, **k):
     if key not in _cases:
         _cases[key] = Case(*a, **k)
@@ -164,8 +181,7 @@ def test_gpu_tiny_repeated_runs_identical():
     assert np.array_equal(first["logits"], again["logits"])
     assert np.array_equal(first["kv"], again["kv"])
     lw = c.run(layerwise=True)
-    # layerwise runs the same tile arithmetic in the same order
-    assert np.array_equal(lw["logits"], first["logits"])
+    assert_layerwise_consistent(c.cfg, lw, first)
 
 
 @pytest.mark.parametrize("key,name,overrides,opts", [
@@ -189,7 +205,7 @@ def test_gpu_llama1b_full_size():
     c.assert_parity(r)
     lw = c.run(layerwise=True)
     c.assert_parity(lw, layerwise=True)
-    assert np.array_equal(lw["logits"], r["logits"])  # same tile functions, same order
+    assert_layerwise_consistent(c.cfg, lw, r)
 
 
 @pytest.mark.parametrize("key,name", [("tiny", "tiny"), ("llama1b", "llama1b")])
@@ -250,7 +266,7 @@ def test_gpu_qwen3_8b_full_size():
         c.assert_parity(r)
         lw = c.run(layerwise=True)
         c.assert_parity(lw, layerwise=True)
-        assert np.array_equal(lw["logits"], r["logits"])  # same tile functions, same order
+        assert_layerwise_consistent(c.cfg, lw, r)
     finally:
         c.plan.free()
         del c
@@ -276,8 +292,7 @@ def test_gpu_batched(key, name, overrides):
     c.assert_parity(r)
     lw = c.run(layerwise=True)
     c.assert_parity(lw, layerwise=True)
-    # the layerwise kernels run the same tile functions in the same order
-    assert np.array_equal(lw["logits"], r["logits"])
+    assert_layerwise_consistent(c.cfg, lw, r)
 
 
 @pytest.mark.timeout(900)
@@ -291,7 +306,7 @@ def test_gpu_llama1b_batch16_full_size():
         c.assert_parity(r)
         lw = c.run(layerwise=True)
         c.assert_parity(lw, layerwise=True)
-        assert np.array_equal(lw["logits"], r["logits"])  # same tile functions, same order
+        assert_layerwise_consistent(c.cfg, lw, r)
     finally:
         c.plan.free()
         del c

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from tests.lib_defaults import documented_choices
-from tests.test_gpu_parity import Case
+from tests.test_gpu_parity import Case, assert_layerwise_consistent
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -57,7 +57,7 @@ def test_gpu_plan_variant_matches_oracle_and_default_plan(name, overrides, extra
         assert np.array_equal(r["logits"], r0["logits"])
         assert np.array_equal(r["kv"], r0["kv"])
         lw = var.run(layerwise=True)
-        assert np.array_equal(lw["logits"], r["logits"])
+        assert_layerwise_consistent(var.cfg, lw, r)
     finally:
         _free(base, var)
 
