@@ -112,7 +112,8 @@ typedef struct {
  *   sequence: ceil((kv+1)/64) clamped to [1, 32], lowered to
  *   ceil(2 num_cus / (batch n_kv_heads)) when that is smaller, then raised
  *   until one split's K and V rows fit in 64 KiB, or in half the page ring
- *   while batch n_kv_heads splits still fit on num_cus at one each);
+ *   while batch n_kv_heads splits still fit on num_cus at one each; batched
+ *   head_dim-64 tasks stream their rows through the ring and skip the raise);
  * timeout_ms: bound of every device-side wait (default 200);
  * dma_pages: 16 KiB pages each of the two weight-loader waves may leave in
  *   flight behind the one it is issuing (1 to 3, default 1): the event polls and
@@ -174,7 +175,8 @@ typedef struct {
  * heads per kv head, kv_len[b] + 1 > max_kv_len, batch outside 1..16, batch-1
  * GEMV tiles with more rows than their K allows (16 up to K 2048, 8 up to 4096,
  * 4 beyond), tiles that do not fit the LDS page ring: 144 KiB at batch 1, 128
- * KiB at batch 2..16).  Batch 1 runs fp32 vector GEMV tiles; batch 2..16 runs the
+ * KiB at batch 2..16; batched head_dim-64 attention tasks stream their K/V rows
+ * through the ring in chunks of 32 positions and may be longer).  Batch 1 runs fp32 vector GEMV tiles; batch 2..16 runs the
  * same tiles on the matrix cores (16 weight rows x 16 sequences per MFMA block,
  * activations entered as bf16 high and low parts). */
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* kv_len,

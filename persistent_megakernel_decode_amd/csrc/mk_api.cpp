@@ -449,15 +449,17 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
                                     "4 beyond)");
     }
   }
-  // every tile's weight bytes must fit the LDS page ring
+  // every tile's weight bytes must fit the LDS page ring; the batched
+  // head_dim-64 attention streams its K/V rows through the ring (any length)
   auto r1k = [](long v) { return (v + 1023) / 1024 * 1024; };
   const long ring = (long)mk::ring_pages(batch) * mkd::kPage;
   const int Smax = o.attn_splits;
   const int maxpos = *std::max_element(kl.begin(), kl.end()) + 1;
   const long attn_rows = mk::ceil_div(maxpos, Smax);
+  const bool attn_streams = batch > 1 && d.head_dim == 64;
   if ((long)o.gemv_rows * d.hidden * 2 > ring || r1k((long)o.gateup_outs * d.hidden * 2) * 2 > ring ||
       (long)o.down_rows * d.ffn * 2 > ring || (long)o.gemv_rows * d.n_q_heads * d.head_dim * 2 > ring ||
-      (long)o.lm_rows * d.hidden * 2 > ring || r1k(attn_rows * d.head_dim * 2) * 2 > ring) {
+      (long)o.lm_rows * d.hidden * 2 > ring || (!attn_streams && r1k(attn_rows * d.head_dim * 2) * 2 > ring)) {
     delete p;
     return fail(MK_E_UNSUPPORTED, "a tile does not fit the LDS page ring (144 KiB, 128 KiB for batch > 1); use smaller tiles");
   }

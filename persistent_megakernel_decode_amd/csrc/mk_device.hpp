@@ -347,6 +347,11 @@ struct Tile {
   // segment 0 as rows of seglen bytes, stride bytes apart in memory (packed
   // densely in the tile); stride 0: one contiguous run
   int seglen, stride;
+  // batched head_dim-64 attention: the K and V rows interleaved in chunks of
+  // 32 positions (4 KiB of K rows, then the same positions' 4 KiB of V rows),
+  // so that the task can consume and hand back its pages in position order
+  // and may be longer than the ring (attn_mfma64)
+  int ilv;
 };
 
 __device__ __forceinline__ int round1k(int v) { return (v + 1023) & ~1023; }
@@ -358,6 +363,7 @@ __device__ inline Tile tile_info(const M& m, const Consts& c) {
   t.p1 = nullptr;
   t.len0 = t.off1 = t.len1 = 0;
   t.seglen = t.stride = 0;
+  t.ilv = 0;
   const int op = m.w(WOpcode);
   switch (op) {
     case OpQkv: {
@@ -423,13 +429,14 @@ __device__ inline Tile tile_info(const M& m, const Consts& c) {
       t.p0 = (const GLB char*)m.q(AttnK) + base;
       t.p1 = (const GLB char*)m.q(AttnV) + base;
       t.len0 = t.len1 = nk * c.hd * 2;
+      t.ilv = c.B > 1 && c.hd == 64;
       break;
     }
     default:
       break;
   }
   t.off1 = round1k(t.len0);
-  t.bytes = t.len1 ? t.off1 + t.len1 : t.len0;
+  t.bytes = t.ilv ? ((t.len0 + 4095) >> 12) * 8192 : t.len1 ? t.off1 + t.len1 : t.len0;
   t.npages = (t.bytes + kPage - 1) / kPage;
   return t;
 }
@@ -460,6 +467,22 @@ struct LdsSrc {
   }
   __device__ __forceinline__ uint32_t ld4(int seg, int o) const {
     return *(const LDS uint32_t*)(uintptr_t)addr(seg, (uint32_t)o);
+  }
+};
+// The interleaved attention tile (Tile::ilv) in a power-of-two ring: row byte o
+// of segment s (0 K, 1 V) sits at tile offset o + ((o >> 12) + s) * 4096, and
+// the tile may be longer than the ring (its pages are handed back as the task
+// moves on), so the ring offset is taken modulo the ring size.
+struct LdsAttnSrc {
+  uint32_t ring;   // LDS byte address of ring slot 0
+  uint32_t first;  // first * kPage
+  uint32_t mask;   // ring size in bytes - 1
+  __device__ __forceinline__ uint32_t addr(int seg, uint32_t o) const {
+    return ring + ((first + o + (((o >> 12) + (uint32_t)seg) << 12)) & mask);
+  }
+  __device__ __forceinline__ uint4 ld16(int seg, int o) const {
+    const u32x4 v = *(const LDS u32x4*)(uintptr_t)addr(seg, (uint32_t)o);
+    return make_uint4(v.x, v.y, v.z, v.w);
   }
 };
 // A tile whose pages do not wrap around the ring end: plain offsets.
@@ -1622,8 +1645,8 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
 }
 
 // Batched attention, head_dim 64, on the matrix cores: the four compute waves
-// of the group take a quarter of the split's positions each, for every query
-// head of the kv group at once, in steps of 32 positions:
+// of the group take the split's chunks of 32 positions in turn (wave w chunks
+// w, w + 4, ...), for every query head of the kv group at once:
 //   scores  S = K q^T with v_mfma_f32_16x16x32_bf16 per 16 positions: A = the
 //           K rows (lane l: position l % 16, dims 8 (l / 16) .. +7, one 16-byte
 //           LDS read), B = q^T (lane l: head l % 16, the same dims; heads past
@@ -1637,14 +1660,21 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
 //           regrouped by one permlane32 and one permlane16 swap; P as bf16
 //           high and low parts, two MFMAs), B = V (lane l: dim l % 16, the same
 //           positions, two ds_read_b64_tr_b16 of the position-major V rows).
-// The new K/V row (scratch of each wave) is read instead of the ring for its
-// position.  The waves then exchange their per-head (max, sum, O) through the
-// instruction's partial-sum slot (xarea, 12 x 66 floats: wave w's partials of
-// heads h != w) and wave h merges head h's four and stores the split partial.
-// sync(k): the group's k-th rendezvous (all four waves past it).
-template <int POL = 0, class Src, class Sync>
+// The cached rows arrive in the interleaved tile layout (Tile::ilv: chunk j's
+// K and V rows in ring page j / 2): a wave waits for its chunk's page, and
+// after each round of four chunks every wave hands back that round's two pages
+// (pages.wait(p), pages.release(p0, p1)), so the loaders refill the ring while
+// the task runs.  The new K/V row (scratch of each wave) is read instead of
+// the ring for its position, and so are the masked positions of a chunk that
+// holds no cached row (any other masked position reads its chunk's first row:
+// finite values whose weight is zero).  The waves then exchange their
+// per-head (max, sum, O) through the instruction's partial-sum slot (xarea, 12
+// x 66 floats: wave w's partials of heads h != w) and wave h merges head h's
+// four and stores the split partial.  sync(k): the group's k-th rendezvous
+// (all four waves past it).
+template <int POL = 0, class Src, class Sync, class Pages>
 __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts& c, int cw, LDS float* gscr,
-                                   LDS float* xarea, bool writer, const Sync& sync,
+                                   LDS float* xarea, bool writer, const Sync& sync, const Pages& pages,
                                    unsigned long long* tr = nullptr) {
   constexpr int HD = 64;
   const int lane = lane_id();
@@ -1669,9 +1699,8 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
       ql[kb][e] = (__bf16)(v - (float)h);
     }
   }
-  // this wave's positions [p0, p1): quarters rounded up to 16
-  const int q4 = ((n + 3) / 4 + 15) & ~15;
-  const int p0 = cw * q4, p1 = n < p0 + q4 ? n : p0 + q4;
+  const int nch = (n + 31) >> 5;                      // chunks of the split
+  const int npg = (((nk + 31) >> 5) + 1) >> 1;        // ring pages of its cached rows
   float m_run = -INFINITY, l_run = 0.f;  // head hq's, in lanes (hq, any gq)
   f32x4 O[4];                            // O[db]: lane l: dim 16 db + l % 16, heads 4 (l / 16) + j
 #pragma unroll
@@ -1684,23 +1713,29 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float((lane & 32) ? r[0] : r[1]);
   };
-  // the position whose K / V row a lane reads: cached rows from the ring, the
-  // new row from the scratch, anything past the split's end clamped to a row
-  // that holds finite values (its weight is zero)
-  const int last = nk > 0 ? nk - 1 : 0;
-  for (int s0 = p0; s0 < p1; s0 += 32) {
+  for (int rd = 0; 4 * rd < nch; ++rd) {
+    const int s0 = 32 * (4 * rd + cw);
+    if (s0 >= n) {
+      pages.release(2 * rd, 2 * rd + 2 < npg ? 2 * rd + 2 : npg);
+      continue;
+    }
+    if (s0 < nk && !pages.wait(s0 >> 6)) return;
+    // the row a lane reads for position pp: its own while cached, else the
+    // chunk's first row while that is cached, else the scratch row
+    auto ring_row = [&](int pp) { return pp < nk || (s0 < nk && !(at.has_new && pp == nk)); };
+    auto row_of = [&](int pp) { return pp < nk ? pp : s0; };
     f32x4 S[2];
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk) {
       const int pp = s0 + 16 * bk + hq;  // A row: position
-      const bool newrow = at.has_new && pp == nk;
-      const int pr = pp < nk ? pp : last;
+      const bool rr_ = ring_row(pp);
+      const int pr = row_of(pp);
       S[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const uint4 kr = src.ld16(0, pr * HD * 2 + (32 * kb + 8 * gq) * 2);
         const u32x4 kw = *(const LDS u32x4*)(kn + 32 * kb + 8 * gq);
-        const u32x4 ka = newrow || nk == 0 ? kw : u32x4{kr.x, kr.y, kr.z, kr.w};
+        const u32x4 ka = rr_ ? u32x4{kr.x, kr.y, kr.z, kr.w} : kw;
         const bf16x8 a = __builtin_bit_cast(bf16x8, ka);
         S[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kb], S[bk], 0, 0, 0);
         S[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kb], S[bk], 0, 0, 0);
@@ -1714,7 +1749,7 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int pp = s0 + 16 * bk + 4 * gq + j;
-        sc[bk][j] = pp < p1 ? S[bk][j] * c.inv_sqrt_hd : -INFINITY;
+        sc[bk][j] = pp < n ? S[bk][j] * c.inv_sqrt_hd : -INFINITY;
         mx = fmaxf(mx, sc[bk][j]);
       }
     mx = fmaxf(mx, other16(mx));
@@ -1769,11 +1804,9 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int pp = s0 + 8 * rg + 4 * half + rr;
-        const bool newrow = at.has_new && pp == nk;
-        const int pr = pp < nk ? pp : last;
-        const uint32_t ring = src.addr(1, (uint32_t)(pr * HD * 2 + (16 * db + 4 * cc) * 2));
+        const uint32_t ring = src.addr(1, (uint32_t)(row_of(pp) * HD * 2 + (16 * db + 4 * cc) * 2));
         const uint32_t own = (uint32_t)(uintptr_t)(vn + 16 * db + 4 * cc);
-        const uint32_t ad = newrow || nk == 0 ? own : ring;
+        const uint32_t ad = ring_row(pp) ? ring : own;
         vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(uintptr_t)ad);
       }
       bf16x8 vb;
@@ -1785,6 +1818,9 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
       O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, O[db], 0, 0, 0);
       O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, O[db], 0, 0, 0);
     }
+    // this round's pages: every wave has read its chunk (release waits for the
+    // LDS reads to return)
+    pages.release(2 * rd, 2 * rd + 2 < npg ? 2 * rd + 2 : npg);
   }
   // exchange: wave w's (max, sum, O) of head h != w at slot w * 3 + (h < w ? h : h - 1)
   auto slot = [&](int w, int h) { return xarea + (w * 3 + (h < w ? h : h - 1)) * (HD + 2); };

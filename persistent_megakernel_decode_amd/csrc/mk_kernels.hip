@@ -192,7 +192,7 @@ __device__ void stage(const KArgs& a, LDS LT* L, int j, int& pages) {
 
 // ---------------------------------------------------------------------------
 template <class LT>
-__device__ void controller(const KArgs& a, LDS LT* L) {
+__device__ __forceinline__ void controller(const KArgs& a, LDS LT* L) {
   // per wait slot, the last event this wave saw at or past a target and the
   // count it read: counters only grow within a run, so a later instruction
   // waiting on the same event for a target within that count needs neither a
@@ -281,7 +281,7 @@ __device__ void controller(const KArgs& a, LDS LT* L) {
 // its end, with the summed increment: a producer never depends on its own
 // trigger event, so deferring within the run cannot delay the event.
 template <class LT>
-__device__ void storer(const KArgs& a, LDS LT* L) {
+__device__ __forceinline__ void storer(const KArgs& a, LDS LT* L) {
   const int lane = lane_id();
   unsigned pending = 0;
   int ss_row = -1;     // batched: operand row whose sums of squares ss_val holds
@@ -364,7 +364,7 @@ __device__ void storer(const KArgs& a, LDS LT* L) {
 constexpr int kDmaNT = 2;
 
 template <class LT>
-__device__ void loader(const KArgs& a, LDS LT* L, int parity) {
+__device__ __forceinline__ void loader(const KArgs& a, LDS LT* L, int parity) {
   const int lane = lane_id();
   const uint32_t full_base = lds_addr(&L->c.slot_full[0]);
   const uint32_t rel_base = lds_addr(&L->c.slot_rel[0]);
@@ -431,9 +431,9 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
       // 16-byte chunk picks its segment (chunks past the tile re-read a valid one)
       const int pofs = pg * kPage;
       const GLB char* whole = nullptr;
-      if (pofs + kPage <= t.len0 && !t.stride)
+      if (!t.ilv && pofs + kPage <= t.len0 && !t.stride)
         whole = t.p0 + pofs;
-      else if (t.len1 && pofs >= t.off1 && pofs + kPage <= t.off1 + t.len1)
+      else if (!t.ilv && t.len1 && pofs >= t.off1 && pofs + kPage <= t.off1 + t.len1)
         whole = t.p1 + (pofs - t.off1);
       // batched interpreters: after each 8 KiB half of a page, wait for the
       // previous half; the wait after a page's first half completes every
@@ -461,7 +461,10 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
         for (int j = 0; j < 16; ++j) {
           const int toff = pofs + j * 1024 + lane * 16;
           const GLB char* src = dummy;
-          if (toff < t.len0)  // a strided segment's rows are multiples of 16 bytes long
+          if (t.ilv) {  // chunk toff / 8 KiB: 4 KiB of K rows, then 4 KiB of V rows
+            const int o = ((toff >> 13) << 12) + (toff & 4095);
+            if (o < t.len0) src = ((toff >> 12) & 1 ? t.p1 : t.p0) + o;
+          } else if (toff < t.len0)  // a strided segment's rows are multiples of 16 bytes long
             src = t.stride ? t.p0 + (size_t)(toff / t.seglen) * t.stride + toff % t.seglen : t.p0 + toff;
           else if (toff >= t.off1 && toff < t.off1 + t.len1)
             src = t.p1 + (toff - t.off1);
@@ -526,7 +529,7 @@ __device__ void loader(const KArgs& a, LDS LT* L, int parity) {
 // tiles (it reads only these records, each before its arrival, so the
 // controller cannot have reused the slot).
 template <int HD, class LT>
-__device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
+__device__ __forceinline__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
   const int lane = lane_id();
   int act_row = -1;
   int seq = 0;  // one group: ring pages of the instructions before i
@@ -558,7 +561,8 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
       seq += t.npages;
     // the partial-sum slot i % 4 was last used by instruction i - 4
     if (!wait_lds_ge(a, L, &L->c.done_seq, i - 3, ErrDrain, i)) return;
-    for (int pg = 0; pg < t.npages; ++pg) {
+    // the interleaved attention tile waits for its pages one by one (t.ilv)
+    for (int pg = 0; pg < (t.ilv ? 0 : t.npages); ++pg) {
       const int sq = first + pg;
       if (!wait_lds_ge(a, L, &L->c.slot_full[sq % LT::NP], sq / LT::NP + 1, ErrPage, i)) return;
     }
@@ -654,13 +658,36 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
         }
       } else if (op == OpAttn) {
         if constexpr (LT::MB && HD == 64) {
+          static_assert((LT::NP & (LT::NP - 1)) == 0, "the interleaved attention tile needs a power-of-two ring");
           // the group's rendezvous: all four compute waves past point k
           bool live = true;
           auto sync = [&](int k) {
             if (lane == 0) __hip_atomic_fetch_add(&L->c.xch[sl], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (!wait_lds_ge(a, L, &L->c.xch[sl], k * kNW, ErrReady, i)) live = false;
           };
-          attn_mfma64(src, m, a.c, cw, &L->c.scratch[set * kNW][0], &L->c.part[sl][0][0], cw == 0, sync,
+          // the task's pages, waited for and handed back round by round
+          struct Pages {
+            const KArgs& a;
+            LDS LT* L;
+            int first, i, lane;
+            bool& live;
+            __device__ bool wait(int p) const {
+              const int sq = first + p;
+              if (!wait_lds_ge(a, L, &L->c.slot_full[sq % LT::NP], sq / LT::NP + 1, ErrPage, i)) live = false;
+              return live;
+            }
+            __device__ void release(int p0, int p1) const {
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+              const bool mine = p0 + lane < p1;
+              LDS int* p = mine ? &L->c.slot_rel[(first + p0 + lane) % LT::NP] : &L->c.rel_sink[lane];
+              __hip_atomic_fetch_add(p, mine ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+          } pages{a, L, first, i, lane, live};
+          LdsAttnSrc asrc;
+          asrc.ring = src.ring;
+          asrc.first = src.first;
+          asrc.mask = (uint32_t)(LT::NP * kPage - 1);
+          attn_mfma64(asrc, m, a.c, cw, &L->c.scratch[set * kNW][0], &L->c.part[sl][0][0], cw == 0, sync, pages,
                       cw == 0 ? tr : nullptr);
           if (!live) return;
         } else {
@@ -671,7 +698,7 @@ __device__ void compute(const KArgs& a, LDS LT* L, int cw, int set) {
       } else if (op == OpArgmax) {
         argmax_part(m, a.c, cw, &L->c.part[sl][cw][0]);
       }
-      if (!gemv) release();
+      if (!gemv && !t.ilv) release();
     }
     if (tr && lane == 0) tr[12 + cw] = now_ticks();
     // arrival: GEMV partials are in LDS; other ops stored their results to

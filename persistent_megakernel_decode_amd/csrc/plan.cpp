@@ -692,10 +692,12 @@ void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, Model
     // compute units at one each, within half the page ring instead (9 pages of
     // 16 KiB at batch 1, 8 above): one more split would put a second attention
     // task on some units, which costs the chain more than a larger tile costs
-    // the ring
+    // the ring.  Batched head_dim-64 tasks stream their rows through the ring
+    // and take no cap.
+    const bool streams = kv_len.size() > 1 && m.head_dim == 64;
     long cap = 65536;
     if ((long)pairs * S <= o->num_cus) cap = (kv_len.size() == 1 ? 9L : 8L) * 16384 / 2;
-    while ((long)ceil_div(n, S) * m.head_dim * 4 > cap) ++S;
+    while (!streams && (long)ceil_div(n, S) * m.head_dim * 4 > cap) ++S;
     o->attn_splits = S;
   }
 }

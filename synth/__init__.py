@@ -234,6 +234,9 @@ def kv_lengths(cfg):
     kl = cfg["kv_len"]
     if isinstance(kl, tuple):
         return uniform_i32(cfg["seed"], TID_KV_LEN, kl[0], kl[1], cfg["batch"])
+    if isinstance(kl, list):  # explicit per-sequence lengths
+        assert len(kl) == cfg["batch"]
+        return np.array(kl, dtype=np.int32)
     return np.full(cfg["batch"], kl, dtype=np.int32)
 
 

@@ -27,7 +27,8 @@ def documented_defaults(cfg, batch, kv_len, num_cus, **given):
         cap = 65536
         if pairs * S <= num_cus:
             cap = (9 if batch == 1 else 8) * 16384 // 2
-        while ceil_div(n, S) * hd * 2 * 2 > cap:
+        streams = batch > 1 and hd == 64
+        while not streams and ceil_div(n, S) * hd * 2 * 2 > cap:
             S += 1
     o["attn_splits"] = S
     return o

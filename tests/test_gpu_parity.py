@@ -280,13 +280,21 @@ def test_gpu_qwen3_8b_full_size():
     ("b5_qwen", "tiny", dict(arch="qwen3", qk_norm=1, tied=0, head_dim=128, batch=5, kv_len=(1, 90), seed=13)),
     ("b6_ragged", "tiny", dict(batch=6, kv_len=(1, 120), seed=15, opts=dict(down_rows=6, gateup_outs=3))),
     ("b4_odd", "tiny", dict(batch=4, kv_len=(3, 77), seed=17, opts=dict(gemv_rows=4, down_rows=5, gateup_outs=3))),
+    ("b2_stream", "tiny", dict(batch=2, kv_len=(1100, 2040), seed=19, opts=dict(attn_splits=1))),
+    ("b4_chunks", "tiny", dict(batch=4, kv_len=[0, 63, 64, 95], seed=21, opts=dict(attn_splits=1))),
+    ("b3_splits", "tiny", dict(batch=3, kv_len=[200, 517, 1023], seed=23, opts=dict(attn_splits=3))),
 ])
 def test_gpu_batched(key, name, overrides):
     """Batch 2..16 (matrix-core GEMV tiles, per-sequence attention lengths):
     megakernel and layerwise against the oracle, every sequence's argmax.
     b6_ragged: down and gate/up tiles whose row counts leave a short last tile
     (the residual stream's sums of squares kept per 2 rows); b4_odd: O and down
-    tiles of 4 and 5 rows (sums per 4 rows and per row, element-wise epilogues)."""
+    tiles of 4 and 5 rows (sums per 4 rows and per row, element-wise epilogues).
+    The head_dim-64 attention tasks stream their K/V rows through the page ring
+    in chunks of 32 positions: b2_stream has tasks of 1100..2040 rows (up to
+    four times the ring), b4_chunks puts the new row alone in a chunk (64
+    cached rows), last in a chunk (63, 95) and alone in the task (0), b3_splits
+    cuts three lengths into three splits each."""
     c = case(key, name, **overrides)
     r = c.run()
     c.assert_parity(r)

@@ -333,6 +333,32 @@ def test_split_rule_one_task_per_cu():
             plan.free()
 
 
+def test_split_rule_streamed_attention():
+    """Batched head_dim-64 attention streams its K/V rows through the page
+    ring, so no byte cap raises the split count: Llama-1B at batch 16 (16 x 8
+    (sequence, kv head) pairs, longest KV 2016) keeps ceil(2 * 256 / 128) = 4
+    splits of up to 505 positions (129,280 bytes, more than the 128 KiB ring),
+    while head_dim 128 at batch 16 is still raised until a split fits 64 KiB."""
+    cfg = synth.config("llama1b_b16")
+    kv = synth.kv_lengths(cfg)
+    assert int(kv.max()) == 2016
+    plan = mk.Plan.build(cfg, 16, kv, synth.kv_capacity(kv), num_cus=256)
+    try:
+        assert plan.export()["tile_opts"]["attn_splits"] == 4
+    finally:
+        plan.free()
+    q = dict(cfg, head_dim=128)
+    n = int(kv.max()) + 1
+    want = 4
+    while -(-n // want) * 128 * 4 > 65536:
+        want += 1
+    plan = mk.Plan.build(q, 16, kv, synth.kv_capacity(kv), num_cus=256)
+    try:
+        assert plan.export()["tile_opts"]["attn_splits"] == want
+    finally:
+        plan.free()
+
+
 def test_operand_table_layout():
     """The operand table has one row of 16 slots per op, shared by all of its
     tile instructions; the exported layout names the tensor kind of each slot
