@@ -301,6 +301,10 @@ __device__ __forceinline__ void storer(const KArgs& a, LDS LT* L) {
       if (glm_is_gemm(op)) glm_epilogue(m, a.c, &L->c.part[sl][0][0]);
     } else if constexpr (LT::MB) {
       ResMB res = gemv_residual_mb(m, a.c);
+      // take the residual into registers here: left pending, its load would
+      // make the compiler wait for all of this wave's memory operations
+      // (earlier tiles' stores included) wherever those registers are reused
+      asm volatile("" : "+v"(res.r0), "+v"(res.r1));
       // the fused norm's sum of squares: the same for every tile of an op
       // (consecutive tiles of the LM head, gate/up, ... reuse it)
       if (gemv) {
@@ -318,7 +322,8 @@ __device__ __forceinline__ void storer(const KArgs& a, LDS LT* L) {
       else if (op == OpArgmax)
         argmax_final(m, &L->c.part[sl][0][0], LT::PW);
     } else {
-      const float res = (op == OpOproj || op == OpDown) ? gemv_residual(m, a.c) : 0.f;
+      float res = (op == OpOproj || op == OpDown) ? gemv_residual(m, a.c) : 0.f;
+      asm volatile("" : "+v"(res));  // in registers now (see the batched branch)
       if (!wait_lds_ge(a, L, &L->c.arrive[sl], kNW, ErrDrain, i)) return;
       if (gemv)
         gemv_epilogue(m, a.c, L->c.part[sl], &L->c.ssp[sl][0][0], res);
