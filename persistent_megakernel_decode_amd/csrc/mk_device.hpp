@@ -719,6 +719,16 @@ __device__ __forceinline__ void gemv_finish(const Act& a, const uint4 (&wv)[16],
   for (int j = 0; j < NC; ++j) gemv_fma_chunk<NR>(a, j, &wv[j * NR], acc);
   gemv_reduce<NR>(acc, nrows, part);
 }
+// two rows of up to kMaxChunks chunks (the whole share in 2 x NC registers),
+// reduced as a 4-row block whose last two rows are zero
+template <int NC>
+__device__ __forceinline__ void gemv_finish2(const Act& a, const uint4 (&wv)[16], int nrows, LDS float* part) {
+  float acc2[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NC; ++j) gemv_fma_chunk<2>(a, j, &wv[j * 2], acc2);
+  const float acc[4] = {acc2[0], acc2[1], 0.f, 0.f};
+  gemv_reduce<4>(acc, nrows, part);
+}
 // any K, 4 rows, chunk by chunk (the activations are already loaded)
 template <class Src>
 __device__ inline void gemv_chunked(const Src& src, const Act& a, const GemvGeom& g, LDS float* part) {
@@ -747,7 +757,7 @@ __device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int c
                                  const Pre& pre) {
   const GemvGeom g(gi, cw);
   const int nc = gemv_chunks(gi.K);
-  const int shape = nc == 1 ? 0 : nc == 2 ? 1 : nc <= 4 ? 2 : 3;
+  const int shape = nc == 1 ? 0 : nc == 2 ? 1 : nc <= 4 ? 2 : (nc <= kMaxChunks && g.nrows <= 2) ? 4 : 3;
   uint4 wv[16];
   if (shape == 0)
     gemv_pull<16, 1>(src, g, wv);
@@ -755,6 +765,8 @@ __device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int c
     gemv_pull<8, 2>(src, g, wv);
   else if (shape == 2)
     gemv_pull<4, 4>(src, g, wv);
+  else if (shape == 4)
+    gemv_pull<2, kMaxChunks>(src, g, wv);
   // keep every LDS read of the share in flight at once: without this boundary
   // the scheduler interleaves each read with the previous row's FMAs and waits
   // for it, paying the LDS latency once per row
@@ -767,6 +779,8 @@ __device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int c
     gemv_finish<8, 2>(a, wv, g.nrows, part);
   else if (shape == 2)
     gemv_finish<4, 4>(a, wv, g.nrows, part);
+  else if (shape == 4)
+    gemv_finish2<kMaxChunks>(a, wv, g.nrows, part);
   else {
     gemv_chunked(src, a, g, part);
     rel();
@@ -776,9 +790,10 @@ __device__ inline void gemv_rows(const Src& src, Act& a, const GemvIn& gi, int c
 
 // Tile shapes, by 16-byte chunks per lane nc = ceil(K / 2048): nc = 1 -> up to
 // 16 rows, nc = 2 -> up to 8, nc = 3..4 -> up to 4 (the wave's share, at most
-// 16 x 16 bytes per lane, is read whole); larger K -> up to 4 rows, chunk by
-// chunk.  Few shapes keep the interpreter's code within the instruction cache;
-// the plan builder rejects tiles with more rows (gemv_max_rows).
+// 16 x 16 bytes per lane, is read whole); larger K -> up to 2 rows read whole,
+// or up to 4 rows chunk by chunk (their pages held until the arithmetic ends).
+// Few shapes keep the interpreter's code within the instruction cache; the plan
+// builder rejects tiles with more rows (gemv_max_rows).
 __host__ __device__ inline int gemv_max_rows(int K) {
   const int nc = (K + 2047) / 2048;
   return nc <= 1 ? 16 : nc == 2 ? 8 : 4;
