@@ -1523,7 +1523,7 @@ __device__ inline void attn_wave(const Src& src, const Meta& mt, const Consts& c
   // chunk is selected in registers), so the pass has no divergent branch.
   constexpr int LPP = HD / 8;
   constexpr int PPP = 64 / LPP;
-  constexpr int U = 4;  // passes whose loads are issued together
+  constexpr int U = HD == 128 ? 8 : 4;  // passes whose loads are issued together
   const int gi = lane / LPP, cidx = lane % LPP;
   float qc[8];
 #pragma unroll
