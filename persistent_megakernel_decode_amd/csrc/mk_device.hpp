@@ -1728,6 +1728,8 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float((lane & 32) ? r[0] : r[1]);
   };
+  // the new row's K chunks of this lane (loop-invariant)
+  const u32x4 kw0 = *(const LDS u32x4*)(kn + 8 * gq), kw1 = *(const LDS u32x4*)(kn + 32 + 8 * gq);
   for (int rd = 0; 4 * rd < nch; ++rd) {
     const int s0 = 32 * (4 * rd + cw);
     if (s0 >= n) {
@@ -1746,11 +1748,12 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
       const bool rr_ = ring_row(pp);
       const int pr = row_of(pp);
       S[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // a 128-byte row never straddles a 4 KiB block or the ring's end
+      const uint32_t krow = src.addr(0, (uint32_t)(pr * HD * 2)) + (uint32_t)(16 * gq);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kr = src.ld16(0, pr * HD * 2 + (32 * kb + 8 * gq) * 2);
-        const u32x4 kw = *(const LDS u32x4*)(kn + 32 * kb + 8 * gq);
-        const u32x4 ka = rr_ ? u32x4{kr.x, kr.y, kr.z, kr.w} : kw;
+        const u32x4 kr = *(const LDS u32x4*)(uintptr_t)(krow + 64 * kb);
+        const u32x4 ka = rr_ ? kr : (kb ? kw1 : kw0);
         const bf16x8 a = __builtin_bit_cast(bf16x8, ka);
         S[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kb], S[bk], 0, 0, 0);
         S[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kb], S[bk], 0, 0, 0);
@@ -1813,17 +1816,20 @@ __device__ inline void attn_mfma64(const Src& src, const Meta& mt, const Consts&
     // 16 db + 4 cc .. +3; the transposed read hands lane (g, q) the 4 rows'
     // dim 16 db + q
     const int rg = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+    // each half's V row address once (a row never straddles a 4 KiB block or
+    // the ring's end), the 16-dim blocks as offsets from it
+    uint32_t vrow[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int pp = s0 + 8 * rg + 4 * half + rr;
+      vrow[half] = ring_row(pp) ? src.addr(1, (uint32_t)(row_of(pp) * HD * 2)) : (uint32_t)(uintptr_t)vn;
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       bf16x4 vh[2];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int pp = s0 + 8 * rg + 4 * half + rr;
-        const uint32_t ring = src.addr(1, (uint32_t)(row_of(pp) * HD * 2 + (16 * db + 4 * cc) * 2));
-        const uint32_t own = (uint32_t)(uintptr_t)(vn + 16 * db + 4 * cc);
-        const uint32_t ad = ring_row(pp) ? ring : own;
-        vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(uintptr_t)ad);
-      }
+      for (int half = 0; half < 2; ++half)
+        vh[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(uintptr_t)(vrow[half] + (16 * db + 4 * cc) * 2));
       bf16x8 vb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
