@@ -333,6 +333,21 @@ def test_split_rule_one_task_per_cu():
             plan.free()
 
 
+def test_streamed_attention_tasks_may_exceed_the_ring():
+    """Batched head_dim-64 attention tasks stream their K/V rows through the
+    page ring, so a split may be longer than the 128 KiB ring (one split of
+    2041 rows = 510 KiB here); the head_dim-128 path reads its split whole and
+    still rejects it, as batch 1 does."""
+    cfg = synth.config("tiny")
+    kv = [2040, 1100]
+    plan = mk.Plan.build(dict(cfg, batch=2), 2, kv, 2080, num_cus=16, attn_splits=1)
+    plan.free()
+    for c, b, k in ((dict(cfg, head_dim=128, batch=2), 2, kv), (cfg, 1, [2040])):
+        with pytest.raises(mk.MKError) as e:
+            mk.Plan.build(c, b, k, 2080, num_cus=16, attn_splits=1)
+        assert e.value.status == mk.MK_E_UNSUPPORTED and b"ring" in mk.lib().mk_last_error()
+
+
 def test_split_rule_streamed_attention():
     """Batched head_dim-64 attention streams its K/V rows through the page
     ring, so no byte cap raises the split count: Llama-1B at batch 16 (16 x 8
