@@ -283,6 +283,7 @@ def test_gpu_qwen3_8b_full_size():
     ("b2_stream", "tiny", dict(batch=2, kv_len=(1100, 2040), seed=19, opts=dict(attn_splits=1))),
     ("b4_chunks", "tiny", dict(batch=4, kv_len=[0, 63, 64, 95], seed=21, opts=dict(attn_splits=1))),
     ("b3_splits", "tiny", dict(batch=3, kv_len=[200, 517, 1023], seed=23, opts=dict(attn_splits=3))),
+    ("b2_pages", "tiny", dict(batch=2, kv_len=[127, 128], seed=25, opts=dict(attn_splits=1))),
 ])
 def test_gpu_batched(key, name, overrides):
     """Batch 2..16 (matrix-core GEMV tiles, per-sequence attention lengths):
@@ -294,7 +295,8 @@ def test_gpu_batched(key, name, overrides):
     in chunks of 32 positions: b2_stream has tasks of 1100..2040 rows (up to
     four times the ring), b4_chunks puts the new row alone in a chunk (64
     cached rows), last in a chunk (63, 95) and alone in the task (0), b3_splits
-    cuts three lengths into three splits each."""
+    cuts three lengths into three splits each, b2_pages ends the cached rows one
+    row before and exactly at a page boundary (two chunks per page)."""
     c = case(key, name, **overrides)
     r = c.run()
     c.assert_parity(r)
