@@ -107,6 +107,27 @@ def time_launches(fn, stream, steps, warmup):
                 wall_us_per_step=wall * 1e6 / steps)
 
 
+def time_cold(fn, flush, stream, steps, warmup):
+    """Like time_launches, with flush() (reads and writes a buffer larger
+    than the L2s and the memory-side cache) issued before each timed launch,
+    outside its events: every step then finds its weights and caches in HBM."""
+    import torch
+    for _ in range(warmup):
+        flush()
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, e in ev:
+        flush()
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([s.elapsed_time(e) * 1e3 for s, e in ev])  # us
+    return dict(median=float(np.median(per)), p10=float(np.percentile(per, 10)), p90=float(np.percentile(per, 90)),
+                mean=float(per.mean()))
+
+
 def capture(run):
     """Capture run(stream) (one step's launches) in a graph; returns its replay.
     The run is made once eagerly first so that the plan has bound its operand
@@ -500,6 +521,18 @@ def main():
             print("[bench] timing layerwise as a captured graph", file=sys.stderr, flush=True)
             res["lw_graph"] = time_launches(capture(lambda s: lw_plan.run_layerwise(w, kv, tok, stream=s)), stream,
                                             args.steps, args.warmup)
+    if args.workload == "tiny":
+        # the tiny model (2.4 MB of weights) stays in the caches between steps;
+        # it is also timed cold, every step after a 512 MiB cache flush
+        big = torch.empty(256 << 20, dtype=torch.float16, device="cuda")
+        flush = lambda: big.add_(1)
+        for key, lwf in (("mk_cold", False), ("lw_cold", True)):
+            if args.only == "megakernel" and lwf or args.only == "layerwise" and not lwf:
+                continue
+            print("[bench] timing %s cold" % ("layerwise" if lwf else "megakernel"), file=sys.stderr, flush=True)
+            run = (lambda: plan.run_layerwise(w, kv, tok)) if lwf else (lambda: plan.run(w, kv, tok))
+            res[key] = time_cold(run, flush, stream, args.steps, args.warmup)
+        del big
     torch.cuda.synchronize()
     print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
     ceil = stream_ceiling()
@@ -555,6 +588,12 @@ def main():
         out["layerwise_achieved_GBps"] = round(nbytes / (lwl * 1e-6) / 1e9, 1)
         if "mk" in res:
             out["speedup_vs_layerwise"] = round(lwl / lat, 3)
+    if "mk_cold" in res:
+        out["megakernel_cold_us"] = {k: round(v, 2) for k, v in res["mk_cold"].items()}
+    if "lw_cold" in res:
+        out["layerwise_cold_us"] = {k: round(v, 2) for k, v in res["lw_cold"].items()}
+        if "mk_cold" in res:
+            out["speedup_vs_layerwise_cold"] = round(res["lw_cold"]["median"] / res["mk_cold"]["median"], 3)
     if "lw_graph" in res:
         out["layerwise_graph_us"] = {k: round(v, 2) for k, v in res["lw_graph"].items()}
         if "mk" in res:
