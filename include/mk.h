@@ -376,8 +376,9 @@ mk_status mk_run_layerwise(mk_plan* plan, const mk_weights* weights, void* kv_ca
  * work on that stream; otherwise the first run uploads the patched plan.
  * mk_plan_export shows the new payloads.  Errors: MK_E_INVALID (null),
  * MK_E_STATE (graph-only plan), MK_E_UNSUPPORTED (GLM plan, a length past the
- * capacity, or an attention split that no longer fits the LDS page ring:
- * build a new plan), MK_E_HIP. */
+ * capacity, or an attention split that no longer fits the LDS page ring --
+ * never for batched head_dim-64 plans, whose attention streams through the
+ * ring: build a new plan), MK_E_HIP. */
 mk_status mk_plan_set_kv_len(mk_plan* plan, const int32_t* kv_len, void* stream);
 
 /* n_steps decode steps back to back on stream: step k runs at lengths

@@ -1156,9 +1156,11 @@ static mk_status check_lengths(const mk_plan* p, const std::vector<int32_t>& kv)
     if (kv[b] < 0 || kv[b] + 1 > d.max_kv_len) return fail(MK_E_UNSUPPORTED, "kv_len[b] + 1 must be <= max_kv_len");
     maxpos = std::max(maxpos, kv[b] + 1);
   }
+  // (batched head_dim-64 attention streams its rows through the ring: any length)
   const long ring = (long)mk::ring_pages(p->batch) * mkd::kPage;
   const long rows = mk::ceil_div(maxpos, p->opts.attn_splits);
-  if ((rows * d.head_dim * 2 + 1023) / 1024 * 1024 * 2 > ring)
+  const bool streams = p->batch > 1 && d.head_dim == 64;
+  if (!streams && (rows * d.head_dim * 2 + 1023) / 1024 * 1024 * 2 > ring)
     return fail(MK_E_UNSUPPORTED, "an attention split no longer fits the LDS page ring: build a new plan");
   return MK_OK;
 }

@@ -360,6 +360,8 @@ def test_gpu_layerwise_graph_replay_matches_eager():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,n,overrides", [("tiny", 5, {}), ("llama1b", 3, {}),
                                                ("tiny", 4, dict(batch=3, kv_len=(0, 200), seed=12)),
+                                               ("tiny", 3, dict(batch=2, kv_len=[1790, 2046], seed=27,
+                                                                opts=dict(attn_splits=1))),
                                                ("llama1b_b16", 2, {})])
 def test_gpu_run_steps_match_oracle_step_by_step(name, n, overrides):
     """mk_run_steps: n decode steps back to back, each fed the previous step's
@@ -367,8 +369,13 @@ def test_gpu_run_steps_match_oracle_step_by_step(name, n, overrides):
     (the oracle run step by step on the same token sequence, with its own KV
     cache), the last step's logits are within the bar, every new K/V row was
     written and nothing else; the layerwise run of the same steps gives the same
-    tokens; afterwards the plan reports the last step's lengths."""
+    tokens; afterwards the plan reports the last step's lengths.  The one-split
+    batch-2 case streams attention tasks of up to four times the page ring; its
+    longer sequence has 2046, 2047 and 2048 cached rows in the three steps, the
+    last exactly 32 pages of 64 rows (the new row alone in the next chunk)."""
     mk = _mk()
+    overrides = dict(overrides)
+    opts = overrides.pop("opts", {})
     inp = synth.make_inputs(name, norm_sigma=0.0 if name.startswith("llama1b") else 0.1, **overrides)
     cfg = inp["cfg"]
     B, kv0 = cfg["batch"], inp["kv_len"]
@@ -376,7 +383,7 @@ def test_gpu_run_steps_match_oracle_step_by_step(name, n, overrides):
     assert cache.shape[4] >= int(kv0.max()) + n
     w = mk.DeviceWeights(inp["weights"], cfg)
     tok = mk.tokens_to_device(inp["tokens"])
-    plan = mk.Plan.build(cfg, B, kv0, cache.shape[4])
+    plan = mk.Plan.build(cfg, B, kv0, cache.shape[4], **opts)
     try:
         got = {}
         for lw in (False, True):

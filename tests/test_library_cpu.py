@@ -346,6 +346,19 @@ def test_streamed_attention_tasks_may_exceed_the_ring():
         with pytest.raises(mk.MKError) as e:
             mk.Plan.build(c, b, k, 2080, num_cus=16, attn_splits=1)
         assert e.value.status == mk.MK_E_UNSUPPORTED and b"ring" in mk.lib().mk_last_error()
+    # moving a plan to longer lengths follows the same rule
+    plan = mk.Plan.build(dict(cfg, batch=2), 2, [100, 50], 2080, num_cus=16, attn_splits=1)
+    try:
+        plan.set_kv_len(np.array(kv, dtype=np.int32))
+    finally:
+        plan.free()
+    plan = mk.Plan.build(dict(cfg, head_dim=128, batch=2), 2, [100, 50], 2080, num_cus=16, attn_splits=1)
+    try:
+        with pytest.raises(mk.MKError) as e:
+            plan.set_kv_len(np.array(kv, dtype=np.int32))
+        assert e.value.status == mk.MK_E_UNSUPPORTED and b"ring" in mk.lib().mk_last_error()
+    finally:
+        plan.free()
 
 
 def test_split_rule_streamed_attention():
