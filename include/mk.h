@@ -110,10 +110,12 @@ typedef struct {
  *   tile (default gemv_rows);
  * attn_splits: KV splits per (sequence, kv head) (default from the longest
  *   sequence: ceil((kv+1)/64) clamped to [1, 32], lowered to
- *   ceil(2 num_cus / (batch n_kv_heads)) when that is smaller, then raised
- *   until one split's K and V rows fit in 64 KiB, or in half the page ring
- *   while batch n_kv_heads splits still fit on num_cus at one each; batched
- *   head_dim-64 tasks stream their rows through the ring and skip the raise);
+ *   ceil(2 num_cus / (batch n_kv_heads)) when that is smaller; while the
+ *   batch n_kv_heads S tasks still fit on num_cus at one each, lowered until
+ *   they fit on 7/8 of them; then raised until one split's K and V rows fit in
+ *   64 KiB, or in the page ring less 64 KiB while the tasks fit on num_cus at
+ *   one each; batched head_dim-64 tasks stream their rows through the ring and
+ *   skip the raise);
  * timeout_ms: bound of every device-side wait (default 200);
  * dma_pages: 16 KiB pages each of the two weight-loader waves may leave in
  *   flight behind the one it is issuing (1 to 3, default 1): the event polls and

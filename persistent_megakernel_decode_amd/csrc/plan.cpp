@@ -688,15 +688,20 @@ void resolve_opts(const ModelShape& m, const std::vector<int32_t>& kv_len, Model
     // (sequence, kv head) pairs: every split pays its own q/k/v loads
     const int pairs = (int)kv_len.size() * m.n_kv_heads;
     S = std::min(S, std::max(1, ceil_div(2L * o->num_cus, pairs)));
-    // one split's K and V rows within 64 KiB; while the tasks still fit on the
-    // compute units at one each, within half the page ring instead (9 pages of
-    // 16 KiB at batch 1, 8 above): one more split would put a second attention
-    // task on some units, which costs the chain more than a larger tile costs
-    // the ring.  Batched head_dim-64 tasks stream their rows through the ring
-    // and take no cap.
+    // one split's K and V rows within 64 KiB.  While the tasks still fit on the
+    // compute units at one each, an eighth of the units are left without one
+    // (their rings prefetch the FFN weights through the attention chain), and
+    // a split may take the page ring less one 64 KiB tile (9 pages of 16 KiB
+    // at batch 1, 8 above): one more split would put a second attention task
+    // on some units, which costs the chain more than a larger tile costs the
+    // ring.  Batched head_dim-64 tasks stream their rows through the ring and
+    // take no cap.
     const bool streams = kv_len.size() > 1 && m.head_dim == 64;
     long cap = 65536;
-    if ((long)pairs * S <= o->num_cus) cap = (kv_len.size() == 1 ? 9L : 8L) * 16384 / 2;
+    if ((long)pairs * S <= o->num_cus) {
+      while (S > 1 && (long)pairs * S * 8 > 7L * o->num_cus) --S;
+      cap = (kv_len.size() == 1 ? 9L : 8L) * 16384 - 65536;
+    }
     while (!streams && (long)ceil_div(n, S) * m.head_dim * 4 > cap) ++S;
     o->attn_splits = S;
   }

@@ -26,7 +26,9 @@ def documented_defaults(cfg, batch, kv_len, num_cus, **given):
         S = min(S, max(1, ceil_div(2 * num_cus, pairs)))
         cap = 65536
         if pairs * S <= num_cus:
-            cap = (9 if batch == 1 else 8) * 16384 // 2
+            while S > 1 and pairs * S * 8 > 7 * num_cus:
+                S -= 1
+            cap = (9 if batch == 1 else 8) * 16384 - 65536
         streams = batch > 1 and hd == 64
         while not streams and ceil_div(n, S) * hd * 2 * 2 > cap:
             S += 1

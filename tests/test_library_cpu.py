@@ -318,14 +318,15 @@ def test_default_down_tiles_by_batch():
 
 
 def test_split_rule_one_task_per_cu():
-    """The per-split byte cap is half the page ring while the attention tasks
-    fit on the compute units at one each, 64 KiB otherwise: Qwen3-8B at KV 4096
-    (8 kv heads, 4097 positions, 512 bytes per position) takes 32 splits of 129
-    positions (66,048 bytes) on 256 CUs, and 33 on 200 CUs, where 32 splits
+    """While the attention tasks fit on the compute units at one each, the
+    split count is lowered until they fit on 7/8 of them and the per-split byte
+    cap is the page ring less 64 KiB; 64 KiB otherwise.  Qwen3-8B at KV 4096
+    (8 kv heads, 4097 positions, 512 bytes per position) takes 28 splits of 147
+    positions (75,264 bytes) on 256 CUs, and 33 on 200 CUs, where 32 splits
     would already need 256 tasks."""
     cfg = synth.config("qwen3_8b")
     kv = synth.kv_lengths(cfg)
-    for cus, want in ((256, 32), (200, 33)):
+    for cus, want in ((256, 28), (200, 33)):
         plan = mk.Plan.build(cfg, 1, kv, synth.kv_capacity(kv), num_cus=cus)
         try:
             assert plan.export()["tile_opts"]["attn_splits"] == want
